@@ -1,0 +1,295 @@
+"""Benchmark of the cartridge-attention hot path on one MI355X.
+
+A step is one pass of the training hot path over one layer batch: RoPE on
+the real-token Q/K at positions p + i, the forward, the backward (into the
+token tensors and the f32 cartridge-row gradients, frozen row 0) and the
+RoPE adjoint on dQ and dK. The headline `value` is its algorithmic fwd+bwd
+TFLOP/s (visible pairs only: 4*d*V_pairs forward, 8*d*V_pairs backward;
+RoPE time is inside the step time). The serving half of the path -- writing
+the cartridge into a paged bf16 cache and decoding behind it -- is measured
+on the serving-decode workload and reported in `decode` (GB/s of K/V read).
+
+Inputs are seeded N(0, 1) tensors resident in HBM before timing starts.
+The CPU float64 oracle is timed beside it on a bounded sample (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|5]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+PEAK_HBM_GBPS = 8000.0
+METRIC = "cartridge attn fwd+bwd TFLOP/s and decode GB/s, as % of MI355X roofline"
+
+
+def _progress(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def _events_ms(fn, n):
+    import torch
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(n):
+        fn()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1)
+
+
+def train_bench(C, W, shape, steps, warmup):
+    import torch
+    dev = torch.device("cuda")
+    layers = shape.layers
+    _progress(f"{shape.name}: generating inputs ({layers} layer(s))")
+    L = []
+    for l in range(layers):
+        x = W.train_inputs(shape, seed=shape.seed + l)
+        g = {k: v.to(dev) for k, v in x.items()}
+        q, kt = g["q"], g["k_tok"]
+        B, n, Hq, d = q.shape
+        shp = C.attn_shape(q, kt, shape.p, shape.frozen_rows, 0.0, g["k_cart"].dtype)
+        st = dict(g=g, shp=shp,
+                  o=torch.empty_like(q),
+                  lse=torch.empty(B, Hq, n, dtype=torch.float32, device=dev),
+                  dq=torch.empty_like(q), dkt=torch.empty_like(kt),
+                  dvt=torch.empty_like(g["v_tok"]),
+                  dkc=torch.empty(g["k_cart"].shape, dtype=torch.float32, device=dev),
+                  dvc=torch.empty(g["v_cart"].shape, dtype=torch.float32, device=dev),
+                  wsf=C.workspace(C.cart_attn_workspace_size(shp, False), dev),
+                  wsb=C.workspace(C.cart_attn_workspace_size(shp, True), dev))
+        L.append(st)
+        del x
+    p = shape.p
+
+    def step():
+        # forward over every layer, then backward in reverse (training order)
+        for s in L:
+            g = s["g"]
+            C.cart_rope_tokens(g["q"], g["k_tok"], pos_base=p, theta=W.THETA)
+            C.cart_attn_fwd(s["shp"], g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"],
+                            s["o"], s["lse"], s["wsf"])
+        for s in reversed(L):
+            g = s["g"]
+            C.cart_attn_bwd(s["shp"], g["q"], g["k_tok"], g["v_tok"], g["k_cart"],
+                            g["v_cart"], s["o"], s["lse"], g["dout"], s["dq"], s["dkt"],
+                            s["dvt"], s["dkc"], s["dvc"], False, s["wsb"])
+            C.cart_rope_tokens(s["dq"], s["dkt"], pos_base=p, theta=W.THETA, inverse=True)
+
+    _progress(f"{shape.name}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    _progress(f"{shape.name}: timing {steps} steps")
+    C.timing_enable(True)
+    total_ms = _events_ms(step, steps)
+    kern = {}
+    for name in ("rope", "attn_fwd", "attn_fwd_combine", "bwd_preprocess", "attn_bwd",
+                 "bwd_dq_finalize", "bwd_cart_reduce"):
+        ms, cnt = C.timing_query(name)
+        if cnt:
+            kern[name] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms)
+    C.timing_enable(False)
+    _progress(f"{shape.name}: {total_ms / steps:.3f} ms/step")
+    return total_ms / steps, kern
+
+
+def decode_bench(C, W, shape, steps, warmup):
+    import torch
+    dev = torch.device("cuda")
+    _progress(f"{shape.name}: generating inputs")
+    di = W.decode_inputs(shape)
+    S, Hq, Hkv, d = shape.n_seqs, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    bt = di.page_perm.view(S, di.max_pages_per_seq)
+    cache = C.PagedCache(S, Hkv, d, di.max_pages_per_seq, di.n_pages, bt, dev)
+    kc, vc = di.k_cart.to(dev), di.v_cart.to(dev)
+    gens = [(di.k_gen[s].to(dev), di.v_gen[s].to(dev)) for s in range(S)]
+    q = di.q.to(dev)
+    torch.cuda.synchronize()
+    _progress(f"{shape.name}: writing {S} prefixes of {shape.p} rows")
+
+    C.timing_enable(True)
+    wr_ms = _events_ms(lambda: [cache.write(s, kc, vc) for s in range(S)], 1)
+    ms_app, n_app = C.timing_query("cache_append")
+    C.timing_enable(False)
+    for s in range(S):
+        if di.generated[s]:
+            cache.append(s, *gens[s])
+    lens = [cache.seq_len(s) for s in range(S)]
+    ws = C.workspace(cache.decode_workspace_size(Hq), dev)
+    out = torch.empty(S, Hq, d, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        cache.decode(q, out, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    C.timing_enable(True)
+    total_ms = _events_ms(step, steps)
+    kern = {}
+    for name in ("decode", "decode_merge"):
+        ms, cnt = C.timing_query(name)
+        if cnt:
+            kern[name] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms)
+    C.timing_enable(False)
+    kv_bytes = sum(lens) * Hkv * d * 2 * 2
+    wr_bytes = S * shape.p * Hkv * d * 2 * (4 + 2)      # f32 read + bf16 write, K and V
+    cache.close()
+    return dict(ms=total_ms / steps, kv_bytes=kv_bytes, lens=lens, kern=kern,
+                write_ms=wr_ms, write_kernel_ms=ms_app, write_bytes=wr_bytes)
+
+
+def cpu_baseline(W, shape):
+    """The oracle (numpy float64) timed on a bounded sample of the layer: the
+    first kv heads of sequence 0 (their GQA q-heads, all queries, all keys),
+    forward + backward, repeated until about 10 s of CPU time (at most 30)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import cartattn_oracle as O
+
+    x = W.train_inputs(shape)
+    g = shape.n_q_heads // shape.n_kv_heads
+    n, p, d = shape.q_seq, shape.p, shape.head_dim
+    pairs_per_head = n * p + n * (n + 1) // 2
+    # kv heads in the sample: keep one fwd+bwd under ~0.4 TFLOP of f64 work
+    kvh = max(1, min(shape.n_kv_heads, int(4e11 // (12.0 * d * pairs_per_head * g))))
+    f = lambda t: t.double().numpy()
+    q = f(x["q"][:1, :, :g * kvh])
+    kt, vt = f(x["k_tok"][:1, :, :kvh]), f(x["v_tok"][:1, :, :kvh])
+    kc, vc = f(x["k_cart"][:, :kvh]), f(x["v_cart"][:, :kvh])
+    do = f(x["dout"][:1, :, :g * kvh])
+    del x
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.attn_fwd(q, kt, vt, kc, vc)
+        O.attn_bwd(q, kt, vt, kc, vc, do, frozen_rows=shape.frozen_rows)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or dt * (reps + 1) / reps > 30.0:
+            break
+    flop = reps * 12.0 * d * pairs_per_head * g * kvh
+    threads = sum(i.get("num_threads", 0) for i in threadpool_info()
+                  if i.get("user_api") == "blas") or os.cpu_count()
+    return {"value": round(flop / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{shape.name}: sequence 0, kv heads 0..{kvh - 1} ({g * kvh} q-heads), "
+                      f"all {n} queries x {p}+{n} rows, fwd+bwd in float64 numpy, "
+                      f"{reps} rep(s) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU design is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_kv_amd import cartattn as C
+    from long_context_kv_amd import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    shape = W.SHAPES[args.config]
+    ms, kern = train_bench(C, W, shape, args.steps, args.warmup)
+    flop = shape.fwd_flop() + shape.bwd_flop()
+    value = flop / (ms * 1e-3) / 1e12
+
+    # roofline of the dominant kernel (largest share of the step's time)
+    per_launch_flop = {"attn_fwd": 4.0 * shape.head_dim * shape.visible_pairs,
+                       "attn_bwd": 8.0 * shape.head_dim * shape.visible_pairs}
+    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    roof = None
+    if dom in per_launch_flop:
+        ach = per_launch_flop[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    kernels = {}
+    for k, v in kern.items():
+        e = {"avg_ms": round(v["avg_ms"], 5), "launches": v["launches"]}
+        if k in per_launch_flop:
+            t = per_launch_flop[k] / (v["avg_ms"] * 1e-3) / 1e12
+            e.update(tflops=round(t, 2), frac=round(t / PEAK_BF16_TFLOPS, 4))
+        kernels[k] = e
+    attn_ms = sum(kern[k]["total_ms"] for k in kern if k != "rope") / args.steps
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: B={shape.batch} Hq={shape.n_q_heads} "
+                               f"Hkv={shape.n_kv_heads} d={shape.head_dim} p={shape.p} "
+                               f"n={shape.q_seq} layers={shape.layers}, rope+fwd+bwd+rope^T",
+                   "batch": shape.batch, "q_seq": shape.q_seq, "p": shape.p,
+                   "n_q_heads": shape.n_q_heads, "n_kv_heads": shape.n_kv_heads,
+                   "head_dim": shape.head_dim, "layers": shape.layers,
+                   "frozen_rows": shape.frozen_rows, "parallelism": "none (1 GPU)"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "attn_only_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_decode:
+        dec = decode_bench(C, W, W.DECODE, args.steps, args.warmup)
+        gbps = dec["kv_bytes"] / (dec["ms"] * 1e-3) / 1e9
+        dk = dec["kern"].get("decode")
+        droof = None
+        if dk:
+            ach = dec["kv_bytes"] / (dk["avg_ms"] * 1e-3) / 1e9
+            droof = {"kernel": "decode", "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None}
+        result["decode"] = {
+            "workload": f"{W.DECODE.name}: {W.DECODE.n_seqs} seqs, p={W.DECODE.p} + "
+                        f"U{{0..{W.DECODE.max_generated}}} generated, Hq={W.DECODE.n_q_heads} "
+                        f"Hkv={W.DECODE.n_kv_heads} d={W.DECODE.head_dim}, bf16 pages of 16",
+            "value": round(gbps, 1), "unit": "GB/s", "ms_per_step": round(dec["ms"], 4),
+            "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4), "kv_bytes": dec["kv_bytes"],
+            "roofline": droof,
+            "kernels": {k: {"avg_ms": round(v["avg_ms"], 5), "launches": v["launches"]}
+                        for k, v in dec["kern"].items()},
+            "write_cache": {"ms": round(dec["write_ms"], 3),
+                            "kernel_ms": round(dec["write_kernel_ms"], 3),
+                            "GB/s": round(dec["write_bytes"] / (dec["write_kernel_ms"] * 1e-3)
+                                          / 1e9, 1) if dec["write_kernel_ms"] else None},
+        }
+    if not args.no_cpu_baseline:
+        _progress("cpu baseline (oracle sample)")
+        result["cpu_baseline"] = cpu_baseline(W, shape)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+/*
+ * libcartattn: the cartridge-attention hot path for AMD MI355X (gfx950).
+ *
+ * A cartridge is a trained KV prefix: per layer, p key/value rows of shape
+ * [p, n_kv_heads, head_dim] living in the space of KV-cache rows. Keys are
+ * already rotated (RoPE at positions 0..p-1) and are never rotated again;
+ * real tokens sit at RoPE positions p, p+1, ...; row 0 is a frozen "sink".
+ * Attention runs over concat(sink, trainable rows, real tokens) with the
+ * end-aligned causal mask, source_offset = kv_seq - q_seq = p, so every
+ * query sees the whole cartridge and is causal over real tokens. Gradients
+ * flow through the concat into the trainable rows; serving writes the prefix
+ * into an empty KV cache and decodes behind it.
+ *   Source: "Cartridges: trained KV-prefix corpus compression" (Fucina
+ *   guide), section "Semantics (pinned to the reference implementation)".
+ *
+ * Conventions for every call below
+ *   - Pointers are caller-owned DEVICE pointers unless marked (host).
+ *   - Layouts are dense row-major: Q, O, dO, dQ [batch, q_seq, n_q_heads,
+ *     head_dim]; token K/V and their gradients [batch, q_seq, n_kv_heads,
+ *     head_dim]; cartridge K/V and their gradients [p, n_kv_heads, head_dim];
+ *     LSE [batch, n_q_heads, q_seq] float32 (natural log).
+ *   - q-head h reads kv-head h / (n_q_heads / n_kv_heads).
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the default stream), never synchronizes, never allocates
+ *     device memory and keeps no pointer after it returns.
+ *   - All argument checks run on the host before any HIP call, so every
+ *     error is reported without touching the GPU. A failed check launches
+ *     nothing. A launch failure returns CART_ERR_HIP; the HIP message is in
+ *     cart_last_error(). Faults inside kernels surface at the caller's next
+ *     synchronization (set CARTATTN_SYNC=1 to synchronize after each call).
+ *   - Device pointers must be 16-byte aligned (CART_ERR_ALIGNMENT).
+ *   - Calls are thread-safe except on the same cart_cache, which the caller
+ *     must serialize.
+ */
+#ifndef CARTATTN_H
+#define CARTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CART_OK = 0,
+  CART_ERR_INVALID_ARG = 1,     /* null pointer, bad size or count */
+  CART_ERR_UNSUPPORTED = 2,     /* valid but not built: head_dim, dtype mix */
+  CART_ERR_ALIGNMENT = 3,       /* a device pointer is not 16-byte aligned */
+  CART_ERR_WORKSPACE = 4,       /* workspace missing or too small */
+  CART_ERR_CACHE_NOT_EMPTY = 5, /* cart_write_cache into a non-empty seq */
+  CART_ERR_CACHE_FULL = 6,      /* rows would exceed the sequence's pages */
+  CART_ERR_GEOMETRY = 7,        /* cache and cartridge disagree on heads/dim */
+  CART_ERR_HIP = 8              /* a HIP launch or runtime call failed */
+} cart_status;
+
+typedef enum { CART_F32 = 0, CART_BF16 = 1 } cart_dtype;
+
+/* Shape of one attention layer of a cartridge training step. */
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t q_seq;        /* n >= 1 real tokens per sequence */
+  int32_t p;            /* cartridge rows, p >= 0 (p = 0: plain causal) */
+  int32_t frozen_rows;  /* 0 <= frozen_rows <= p; the pages' default is 1 */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;     /* d in {64, 128} */
+  float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  cart_dtype tok_dtype; /* Q, token K/V, O, dO, dQ, token dK/dV */
+  cart_dtype row_dtype; /* cartridge K/V storage (f32 master rows or bf16) */
+} cart_attn_shape;
+/* Supported dtype pairs: (tok F32, rows F32) is the float32 reference mode
+   (all arithmetic in f32); (tok BF16, rows F32 or BF16) is the bf16 mode:
+   MFMA operands are bf16 (f32 rows are rounded to nearest-even on load),
+   accumulation and softmax are f32. Anything else: CART_ERR_UNSUPPORTED. */
+
+/*
+ * cart_rope_tokens -- rotate the real-token queries and keys in place.
+ *   Source: Cartridges guide, "Semantics": real tokens sit at RoPE positions
+ *   p, p+1, ...; cartridge keys are never rotated again (so they are never
+ *   passed here). RIG cartridge-injection hand-off, section 5: a shifted
+ *   base position silently corrupts attention.
+ *
+ * q [batch, seq, n_q_heads, head_dim] and k [batch, seq, n_kv_heads,
+ * head_dim] (k may be NULL) of dtype `dt`. Token (b, i) is at position
+ *   pos = pos_base + (pos_offsets ? pos_offsets[b] : 0) + i,
+ * pos_offsets being a DEVICE int32 array [batch] or NULL. Element k and
+ * k + d/2 form a pair rotated by angle pos * theta^(-2k/d) (angle computed in
+ * double precision, rotation in f32, result rounded to `dt`):
+ *   x'[k] = x[k] cos - x[k+d/2] sin,   x'[k+d/2] = x[k+d/2] cos + x[k] sin.
+ * inverse != 0 rotates by -angle: the transpose of the forward rotation,
+ * which carries dQ and dK_tok back through RoPE in the backward pass.
+ * For a training step pos_base = p; for a decode step pos_base = 0 and
+ * pos_offsets = the cache's seq_lens (the new token sits at seq_len).
+ */
+int cart_rope_tokens(void* q, void* k, cart_dtype dt, int32_t batch, int32_t seq,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     int32_t pos_base, const int32_t* pos_offsets, double theta,
+                     int32_t inverse, void* stream);
+
+/*
+ * Workspace bytes that cart_attn_fwd (for_backward = 0) or cart_attn_bwd
+ * (for_backward = 1) needs for shape `s` (host pointer). Returns 0 for an
+ * invalid shape. The workspace is caller-owned device memory, 256-byte
+ * aligned, with no required contents; its contents are undefined afterwards.
+ */
+size_t cart_attn_workspace_size(const cart_attn_shape* s, int32_t for_backward);
+
+/*
+ * cart_attn_fwd -- end-aligned causal GQA over concat(cartridge, tokens).
+ *   Source: Cartridges guide, "Semantics" (attention paragraph) and
+ *   "Evidence" (kv_seq > q_seq with GQA).
+ *
+ * For query i of (b, h) and concatenated row j in [0, p + q_seq):
+ *   key_j = k_cart[j, h/g] if j < p else k_tok[b, j - p, h/g] (same for V);
+ *   row j is visible iff j <= i + p;
+ *   out[b,i,h] = sum_j softmax_j(scale * q[b,i,h] . key_j) v_j;
+ *   lse[b,h,i] = log sum_j exp(scale * q[b,i,h] . key_j)   (visible j).
+ * The concat is virtual: the two row sources are read in place.
+ * q, k_tok, v_tok, out: tok_dtype; k_cart, v_cart: row_dtype (may be NULL
+ * when p = 0); lse: float32, required (the backward reads it).
+ */
+int cart_attn_fwd(const cart_attn_shape* s, const void* q, const void* k_tok,
+                  const void* v_tok, const void* k_cart, const void* v_cart,
+                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * cart_attn_bwd -- gradients of the forward above, through the concat.
+ *   Source: Cartridges guide, "Semantics": the f32-KV backward routes
+ *   gradients through the concat into the trainable rows; row 0 is frozen.
+ *
+ * Inputs as for cart_attn_fwd plus `out` and `lse` from it and `dout`.
+ * With D_i = dout_i . out_i, P_ij = exp(scale q_i.key_j - lse_i) on visible
+ * pairs and dS_ij = P_ij (dout_i . v_j - D_i):
+ *   dq_i   = scale sum_j dS_ij key_j                  -> dq (tok_dtype)
+ *   dkey_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i.
+ * Token rows j >= p go to dk_tok/dv_tok (tok_dtype), summed over the q-heads
+ * of the GQA group for their own sequence. Cartridge rows j < p are summed
+ * over the whole batch and the group into dk_cart/dv_cart (float32
+ * [p, n_kv_heads, head_dim]); rows below frozen_rows are written as exact
+ * zeros. accumulate_cart != 0 adds the new cartridge gradients to the
+ * buffers' contents (frozen rows still end as zeros) instead of overwriting.
+ * No RoPE adjoint is applied: call cart_rope_tokens(inverse=1) on dq and
+ * dk_tok afterwards. All accumulation is float32.
+ */
+int cart_attn_bwd(const cart_attn_shape* s, const void* q, const void* k_tok,
+                  const void* v_tok, const void* k_cart, const void* v_cart,
+                  const void* out, const float* lse, const void* dout, void* dq,
+                  void* dk_tok, void* dv_tok, float* dk_cart, float* dv_cart,
+                  int32_t accumulate_cart, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Serving: a paged KV cache that hosts a prefix no tokens produced.
+ *   Source: Cartridges guide, "Semantics" (serving): the full prefix is
+ *   written into an empty cache, converted to the cache dtype, and the cache
+ *   is advanced to p; decode then continues at position p. "Evidence"
+ *   (serving parity). Composition section: appendToCache is the primitive.
+ *   RIG hand-off, section 5: cartridges are locked to the model geometry
+ *   and the KV dtype must match the serving cache.
+ * ------------------------------------------------------------------------ */
+typedef struct cart_cache cart_cache; /* opaque; holds only host state */
+
+typedef struct {
+  int32_t n_seqs;            /* sequences (slots) in the cache */
+  int32_t n_kv_heads;
+  int32_t head_dim;          /* 64 or 128 */
+  int32_t page_size;         /* rows per page; must be 16 */
+  int32_t max_pages_per_seq; /* columns of block_table */
+  int32_t n_pages;           /* pages in each pool */
+  cart_dtype dtype;          /* must be CART_BF16 */
+  void* k_pages;             /* [n_pages, n_kv_heads, page_size, head_dim] */
+  void* v_pages;             /* same */
+  const int32_t* block_table;/* [n_seqs, max_pages_per_seq], page ids */
+  int32_t* seq_lens;         /* [n_seqs]; must hold zeros at creation */
+} cart_cache_desc;
+/* Page ids in block_table must lie in [0, n_pages); kernels skip rows whose
+   page id does not (they neither read nor write out of bounds). Each
+   sequence holds at most max_pages_per_seq * page_size rows. The library
+   keeps a host mirror of every seq_len, so no call reads device memory back;
+   every call that changes a length also writes the device seq_lens. */
+
+int cart_cache_create(const cart_cache_desc* d /*host*/, cart_cache** out /*host*/);
+int cart_cache_destroy(cart_cache* c);
+/* seq_len := 0 for one sequence (device copy updated on `stream`). */
+int cart_cache_reset(cart_cache* c, int32_t seq, void* stream);
+/* Host mirror of one sequence's length, or -1 for a bad handle/seq. */
+int32_t cart_cache_seq_len(const cart_cache* c, int32_t seq);
+
+/* Append n_rows rows k/v [n_rows, n_kv_heads, head_dim] of dtype `src` at the
+   end of sequence `seq`, converting to the cache dtype (bf16, round to
+   nearest even), and advance the sequence by n_rows. The rows' geometry must
+   equal the cache's (else CART_ERR_GEOMETRY); the sequence must have room
+   (else CART_ERR_CACHE_FULL). n_rows = 0 is a no-op. */
+int cart_append_cache(cart_cache* c, int32_t seq, const void* k, const void* v,
+                      cart_dtype src, int32_t n_rows, int32_t n_kv_heads,
+                      int32_t head_dim, void* stream);
+
+/* Write a cartridge prefix k_cart/v_cart [p, n_kv_heads, head_dim] (one
+   layer) into an EMPTY sequence (else CART_ERR_CACHE_NOT_EMPTY), converting
+   to bf16, and advance the sequence to p. A cartridge whose head count or
+   head_dim differs from the cache's is refused with CART_ERR_GEOMETRY. */
+int cart_write_cache(cart_cache* c, int32_t seq, const void* k_cart,
+                     const void* v_cart, cart_dtype src, int32_t p,
+                     int32_t n_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * cart_decode -- one decode step (q_seq = 1) for every sequence.
+ *   Source: Cartridges guide, "Semantics" (serving) and "Evidence" (serving
+ *   parity: decode behind the written prefix matches the trainer's eval).
+ *
+ * q [n_seqs, n_q_heads, head_dim] bf16, already rotated at position seq_len.
+ * If k_new and v_new [n_seqs, n_kv_heads, head_dim] bf16 are both non-NULL
+ * they are appended at row seq_len first and every length advances by one
+ * (the token sees itself); both NULL attends over the stored rows only.
+ * Then out[s,h] = sum_j softmax_j(scale q[s,h] . K[s,j,h/g]) V[s,j,h/g] over
+ * all rows of sequence s (no mask). out: [n_seqs, n_q_heads, head_dim] bf16.
+ * scale 0 selects 1/sqrt(head_dim). Every sequence must hold >= 1 row.
+ * The GQA group n_q_heads / n_kv_heads must be 1, 2, 4 or 8
+ * (else CART_ERR_UNSUPPORTED; not a multiple of the cache's kv heads:
+ * CART_ERR_GEOMETRY). The workspace size depends only on the cache geometry
+ * and n_q_heads.
+ */
+int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                int32_t n_q_heads, float scale, void* out, void* workspace,
+                size_t workspace_bytes, void* stream);
+size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
+
+/* ------------------------------------------------------------------------
+ * Launch timing (profiling aid). When enabled, every kernel launch of this
+ * library is bracketed by two HIP events on its own stream. Kernel names:
+ * "rope", "attn_fwd", "attn_fwd_combine", "bwd_preprocess", "attn_bwd",
+ * "bwd_dq_finalize", "bwd_cart_reduce", "cache_append", "decode_append",
+ * "decode", "decode_merge". cart_timing_enable clears earlier records (after
+ * waiting for them). cart_timing_query waits for the recorded events of one
+ * kernel name and returns their summed duration (ms) and count.
+ * ------------------------------------------------------------------------ */
+int cart_timing_enable(int32_t on);
+int cart_timing_query(const char* kernel, double* total_ms, int32_t* launches);
+
+const char* cart_status_string(int status);
+const char* cart_last_error(void); /* detail of the last failure, this thread */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CARTATTN_H */

@@ -1,0 +1,534 @@
+// Backward pass of cartridge attention: gradients through the concat into
+// the token tensors and into the trainable cartridge rows.
+//
+// Source: "Cartridges: trained KV-prefix corpus compression", section
+// "Semantics (pinned to the reference implementation)": the f32-KV backward
+// routes gradients through the concat into the trainable rows, and row 0 is a
+// frozen constant. The formulas are the softmax adjoint: with
+// D_i = dO_i . O_i and P_ij = exp(scale q_i.k_j - LSE_i),
+//   dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dO_i . v_j - D_i),
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
+//
+// Design (gfx950):
+//  * preprocess: D_i and zeroing of the f32 dQ accumulator in one pass;
+//  * main kernel, one workgroup per 128-key tile (4 waves x 32 keys). A wave
+//    keeps its K and V rows as MFMA B operands in registers and its f32 dK,
+//    dV accumulators in registers for the whole loop, so the cartridge rows'
+//    gradients are summed over batch and GQA group without atomics;
+//  * the loop runs over (batch, q-head of the group, 32-query tile) units;
+//    Q and dO tiles are staged in LDS row-major and transposed, so both
+//    contractions over queries (dV += P^T dO, dK += dS^T Q) take P and dS
+//    straight from the MFMA result registers as A operands;
+//  * dS goes through LDS once per unit for dQ = dS K (K^T is staged in LDS
+//    once per workgroup); dQ is accumulated in f32 with global atomics;
+//  * cartridge tiles see every query of every sequence, token tiles only the
+//    later ones: cartridge tiles may be split over units (partial f32 sums
+//    reduced by a small kernel) to balance the grid;
+//  * block ids are remapped so one kv head's tiles share an XCD and its L2
+//    (where its dQ accumulator lines are hit by every tile).
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "timing.hpp"
+
+namespace cartattn {
+
+namespace {
+
+constexpr int kBNB = 128;      // keys per workgroup tile
+constexpr int kBQ = 32;        // queries per unit
+constexpr int kThreads = 256;
+
+struct BwdArgs {
+  const void* q;
+  const void* k_tok;
+  const void* v_tok;
+  const void* k_cart;
+  const void* v_cart;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  float* delta;       // [B][Hq][n]
+  float* dq_acc;      // [B][n][Hq][D]
+  void* dq;           // tok dtype
+  void* dk_tok;
+  void* dv_tok;
+  float* dk_cart;
+  float* dv_cart;
+  float* dk_part;     // [splits_c][p][Hkv][D]
+  float* dv_part;
+  int B, n, p, f, Hq, Hkv, g;
+  int n_ct, n_tt, nqt, splits_c;
+  int accumulate;
+  float scale, scale_log2;
+};
+
+template <typename T> struct BLds;
+template <> struct BLds<bf16> {
+  static constexpr int rpad = 8;   // row-major tiles: stride D+8 (b128 reads)
+  static constexpr int tpad = 4;   // transposed q tiles: stride 36 (b64 reads)
+};
+template <> struct BLds<float> {
+  static constexpr int rpad = 1;
+  static constexpr int tpad = 1;
+};
+
+// Same access pattern as the forward's V^T fragment: item t of MFMA m holds
+// column d_row(m*KPL + t, hl) of an LDS row.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag tr_frag(const T* row, int m, int hl);
+template <>
+__device__ __forceinline__ bf16x8 tr_frag<bf16>(const bf16* row, int m, int hl) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * m + 4 * hl);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * m + 8 + 4 * hl);
+  bf16x8 f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+template <>
+__device__ __forceinline__ float tr_frag<float>(const float* row, int m, int hl) {
+  return row[d_row(m, hl)];
+}
+
+// KPL consecutive elements of a TS row converted to an MFMA fragment of T.
+template <typename T, typename TS>
+__device__ __forceinline__ typename Mfma<T>::frag conv_frag(const TS* p);
+template <> __device__ __forceinline__ bf16x8 conv_frag<bf16, bf16>(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ __forceinline__ bf16x8 conv_frag<bf16, float>(const float* p) {
+  float v[8];
+  load8<float>(p, v);
+  bf16x8 f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f[t] = (bf16)v[t];
+  return f;
+}
+template <> __device__ __forceinline__ float conv_frag<float, float>(const float* p) {
+  return *p;
+}
+
+template <typename T> __device__ __forceinline__ typename Mfma<T>::frag zero_frag();
+template <> __device__ __forceinline__ bf16x8 zero_frag<bf16>() {
+  bf16x8 f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f[t] = (bf16)0.f;
+  return f;
+}
+template <> __device__ __forceinline__ float zero_frag<float>() { return 0.f; }
+
+template <typename T, typename TR, int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
+  using M = Mfma<T>;
+  constexpr int KPL = M::KPL;
+  constexpr int KSTEP = M::KSTEP;
+  constexpr int NKS = D / KSTEP;
+  constexpr int NDB = D / 32;
+  constexpr int NPV = 16 / KPL;          // MFMAs per 32-row contraction
+  constexpr int RSTR = D + BLds<T>::rpad;        // Qs, dOs
+  constexpr int TSTR = kBQ + BLds<T>::tpad;      // Qt, dOt
+  constexpr int KTSTR = kBNB + BLds<T>::rpad;    // Kt, dSs
+  __shared__ __align__(16) T Kt[D * KTSTR];
+  __shared__ __align__(16) T Qs[kBQ * RSTR];
+  __shared__ __align__(16) T dOs[kBQ * RSTR];
+  __shared__ __align__(16) T Qt[D * TSTR];
+  __shared__ __align__(16) T dOt[D * TSTR];
+  __shared__ __align__(16) T dSs[kBQ * KTSTR];
+  __shared__ __align__(16) float lse2s[kBQ];
+  __shared__ __align__(16) float dls[kBQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  // ---- decode the work item: per kv head, cartridge items then token items
+  const int per_kv = a.n_ct * a.splits_c + a.B * a.n_tt;
+  const int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int kv = lg / per_kv;
+  int r0 = lg % per_kv;
+  const bool cart = r0 < a.n_ct * a.splits_c;
+  int tile, split = 0, b = 0, u_begin, u_end;
+  const int units_per_head = a.nqt;
+  if (cart) {
+    tile = r0 / a.splits_c;
+    split = r0 % a.splits_c;
+    const int U = a.B * a.g * a.nqt;
+    u_begin = (int)((long long)split * U / a.splits_c);
+    u_end = (int)((long long)(split + 1) * U / a.splits_c);
+  } else {
+    r0 -= a.n_ct * a.splits_c;
+    b = r0 / a.n_tt;
+    tile = r0 % a.n_tt;
+    u_begin = 0;
+    u_end = a.g * (a.nqt - tile * (kBNB / kBQ));
+  }
+  const int j0 = tile * kBNB;                         // first row in its source
+  const int limit = cart ? a.p : a.n;                 // rows that exist
+  const int my_key = j0 + 32 * wave + l32;            // this lane's key row (B operand)
+  const size_t row_stride = (size_t)a.Hkv * D;
+
+  // ---- K, V rows of this wave as B operands; K^T of the tile into LDS
+  typename M::frag kf[NKS], vf[NKS];
+  {
+    const bool ok = my_key < limit;
+    if (cart) {
+      const TR* kp = reinterpret_cast<const TR*>(a.k_cart) + ((size_t)my_key * a.Hkv + kv) * D;
+      const TR* vp = reinterpret_cast<const TR*>(a.v_cart) + ((size_t)my_key * a.Hkv + kv) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        kf[ks] = ok ? conv_frag<T, TR>(kp + ks * KSTEP + hl * KPL) : zero_frag<T>();
+        vf[ks] = ok ? conv_frag<T, TR>(vp + ks * KSTEP + hl * KPL) : zero_frag<T>();
+      }
+    } else {
+      const size_t off = (((size_t)b * a.n + my_key) * a.Hkv + kv) * D;
+      const T* kp = reinterpret_cast<const T*>(a.k_tok) + off;
+      const T* vp = reinterpret_cast<const T*>(a.v_tok) + off;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        kf[ks] = ok ? conv_frag<T, T>(kp + ks * KSTEP + hl * KPL) : zero_frag<T>();
+        vf[ks] = ok ? conv_frag<T, T>(vp + ks * KSTEP + hl * KPL) : zero_frag<T>();
+      }
+    }
+    constexpr int CPR = D / 8;
+    constexpr int NCH = kBNB * CPR / kThreads;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int c = tid + u * kThreads;
+      const int r = c / CPR;
+      const int col = (c % CPR) * 8;
+      const int j = j0 + r;
+      float v8[8];
+      if (j < limit) {
+        if (cart)
+          load8<TR>(reinterpret_cast<const TR*>(a.k_cart) + ((size_t)j * a.Hkv + kv) * D + col, v8);
+        else
+          load8<T>(reinterpret_cast<const T*>(a.k_tok) + (((size_t)b * a.n + j) * a.Hkv + kv) * D + col, v8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Kt[(col + e) * KTSTR + r] = from_f32<T>(v8[e]);
+    }
+  }
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+
+  // dQ work split inside the workgroup: d-block and key range per wave.
+  constexpr int NKP = 4 / NDB;                 // key parts (1 for D=128, 2 for D=64)
+  const int q_db = wave % NDB;
+  const int q_kp = wave / NDB;
+  constexpr int KP_STEPS = (kBNB / NKP) / KSTEP;
+
+  for (int u = u_begin; u < u_end; ++u) {
+    int bb, hin, qt;
+    if (cart) {
+      bb = u / (a.g * units_per_head);
+      hin = (u / units_per_head) % a.g;
+      qt = u % units_per_head;
+    } else {
+      const int span = a.nqt - tile * (kBNB / kBQ);
+      bb = b;
+      hin = u / span;
+      qt = tile * (kBNB / kBQ) + u % span;
+    }
+    const int h = kv * a.g + hin;
+    const int i0 = qt * kBQ;
+
+    __syncthreads();   // previous unit is done with the staged tiles and dS
+    {
+      constexpr int CPR = D / 8;
+      constexpr int NCH = kBQ * CPR / kThreads;
+#pragma unroll
+      for (int uu = 0; uu < NCH; ++uu) {
+        const int c = tid + uu * kThreads;
+        const int r = c / CPR;
+        const int col = (c % CPR) * 8;
+        const int i = i0 + r;
+        float qv[8], ov[8];
+        if (i < a.n) {
+          const size_t off = (((size_t)bb * a.n + i) * a.Hq + h) * D + col;
+          load8<T>(reinterpret_cast<const T*>(a.q) + off, qv);
+          load8<T>(reinterpret_cast<const T*>(a.dout) + off, ov);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { qv[e] = 0.f; ov[e] = 0.f; }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const T qe = from_f32<T>(qv[e]);
+          const T oe = from_f32<T>(ov[e]);
+          Qs[r * RSTR + col + e] = qe;
+          dOs[r * RSTR + col + e] = oe;
+          Qt[(col + e) * TSTR + r] = qe;
+          dOt[(col + e) * TSTR + r] = oe;
+        }
+      }
+      if (tid < kBQ) {
+        const int i = i0 + tid;
+        const size_t li = ((size_t)bb * a.Hq + h) * a.n + i;
+        lse2s[tid] = (i < a.n) ? a.lse[li] * kLog2e : INFINITY;
+        dls[tid] = (i < a.n) ? a.delta[li] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    // S = Q K^T and dP = dO V^T: rows = queries (A from LDS), cols = this
+    // wave's keys (B in registers). Lane (key + 32 hl), reg r <-> query d_row(r, hl).
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    {
+      const T* qrow = Qs + l32 * RSTR + hl * KPL;
+      const T* orow = dOs + l32 * RSTR + hl * KPL;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = M::mma(load_frag<T>(qrow + ks * KSTEP), kf[ks], s);
+        dp = M::mma(load_frag<T>(orow + ks * KSTEP), vf[ks], dp);
+      }
+    }
+    const bool key_ok = my_key < limit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qq = d_row(r, hl);
+      const int i = i0 + qq;
+      const bool vis = key_ok && (cart || my_key <= i);   // i >= n has lse2 = +inf
+      const float pv = vis ? exp2f(s[r] * a.scale_log2 - lse2s[qq]) : 0.f;
+      s[r] = pv;                                  // P
+      dp[r] = pv * (dp[r] - dls[qq]);             // dS (unscaled)
+    }
+
+    // dV += P^T dO, dK += dS^T Q (A from registers, B = transposed tiles).
+#pragma unroll
+    for (int m = 0; m < NPV; ++m) {
+      const typename M::frag pf = pack_regs<T>(s, m);
+      const typename M::frag sf = pack_regs<T>(dp, m);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = M::mma(pf, tr_frag<T>(dOt + (32 * db + l32) * TSTR, m, hl), dv[db]);
+        dk[db] = M::mma(sf, tr_frag<T>(Qt + (32 * db + l32) * TSTR, m, hl), dk[db]);
+      }
+    }
+
+    // dS to LDS as [query][key of the tile] for dQ = dS K.
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      dSs[d_row(r, hl) * KTSTR + 32 * wave + l32] = from_f32<T>(dp[r]);
+    __syncthreads();
+
+    {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      const int kbase = q_kp * (kBNB / NKP);
+      const T* arow = dSs + l32 * KTSTR + kbase + hl * KPL;
+      const T* brow = Kt + (32 * q_db + l32) * KTSTR + kbase + hl * KPL;
+#pragma unroll
+      for (int ks = 0; ks < KP_STEPS; ++ks)
+        acc = M::mma(load_frag<T>(arow + ks * KSTEP), load_frag<T>(brow + ks * KSTEP), acc);
+      // lane (d + 32 hl), reg r <-> query d_row(r, hl), column 32*q_db + d
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + d_row(r, hl);
+        if (i < a.n)
+          atomicAdd(a.dq_acc + (((size_t)bb * a.n + i) * a.Hq + h) * D + 32 * q_db + l32,
+                    acc[r] * a.scale);
+      }
+    }
+  }
+
+  // ---- write dK, dV: lane (d + 32 hl), reg r <-> key 32*wave + d_row(r, hl)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = j0 + 32 * wave + d_row(r, hl);
+    if (j >= limit) continue;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 32 * db + l32;
+      const float gk = dk[db][r] * a.scale;
+      const float gv = dv[db][r];
+      if (cart) {
+        const size_t o = ((size_t)j * a.Hkv + kv) * D + col;
+        if (a.splits_c > 1) {
+          const size_t po = (size_t)split * a.p * row_stride + o;
+          a.dk_part[po] = gk;
+          a.dv_part[po] = gv;
+        } else if (j < a.f) {
+          a.dk_cart[o] = 0.f;
+          a.dv_cart[o] = 0.f;
+        } else if (a.accumulate) {
+          a.dk_cart[o] += gk;
+          a.dv_cart[o] += gv;
+        } else {
+          a.dk_cart[o] = gk;
+          a.dv_cart[o] = gv;
+        }
+      } else {
+        const size_t o = (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
+        reinterpret_cast<T*>(a.dk_tok)[o] = from_f32<T>(gk);
+        reinterpret_cast<T*>(a.dv_tok)[o] = from_f32<T>(gv);
+      }
+    }
+  }
+}
+
+// D_i = dO_i . O_i for every (b, h, i), and dQ accumulator := 0.
+// One wave per (b, i, h) row; 4 rows per workgroup.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int total = a.B * a.n * a.Hq;
+  if (row >= total) return;
+  const int h = row % a.Hq;
+  const int bi = row / a.Hq;
+  const int i = bi % a.n;
+  const int b = bi / a.n;
+  const T* o = reinterpret_cast<const T*>(a.out) + (size_t)row * D;
+  const T* g = reinterpret_cast<const T*>(a.dout) + (size_t)row * D;
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc += to_f32(o[lane + 64 * e]) * to_f32(g[lane + 64 * e]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) a.delta[((size_t)b * a.Hq + h) * a.n + i] = acc;
+  float* dq = a.dq_acc + (size_t)row * D;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) dq[lane + 64 * e] = 0.f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dq_finalize(const float* __restrict__ acc,
+                                                       T* __restrict__ dq, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = reinterpret_cast<const float4*>(acc)[i];
+  T* d = dq + 4 * i;
+  d[0] = from_f32<T>(v.x);
+  d[1] = from_f32<T>(v.y);
+  d[2] = from_f32<T>(v.z);
+  d[3] = from_f32<T>(v.w);
+}
+
+// Sum the split partials of the cartridge gradients; frozen rows -> 0.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_cart_reduce_t(BwdArgs a) {
+  const size_t total = (size_t)a.p * a.Hkv * D;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= total) return;
+  const int j = (int)(e / ((size_t)a.Hkv * D));
+  if (j < a.f) {
+    a.dk_cart[e] = 0.f;
+    a.dv_cart[e] = 0.f;
+    return;
+  }
+  float sk = 0.f, sv = 0.f;
+  for (int s = 0; s < a.splits_c; ++s) {
+    sk += a.dk_part[(size_t)s * total + e];
+    sv += a.dv_part[(size_t)s * total + e];
+  }
+  if (a.accumulate) {
+    a.dk_cart[e] += sk;
+    a.dv_cart[e] += sv;
+  } else {
+    a.dk_cart[e] = sk;
+    a.dv_cart[e] = sv;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+BwdPlan plan_bwd(const AttnDims& d) {
+  BwdPlan pl{};
+  const int g = d.Hq / d.Hkv;
+  pl.n_ct = (d.p + kBNB - 1) / kBNB;
+  pl.n_tt = (d.n + kBNB - 1) / kBNB;
+  pl.nqt = (d.n + kBQ - 1) / kBQ;
+  const long long U = (long long)d.B * g * pl.nqt;       // units of a cartridge tile
+  const long long tok_units = (long long)g * pl.nqt;      // units of the first token tile
+  int s = 1;
+  while (pl.n_ct > 0 && U / (2 * s) >= 8 &&
+         ((long long)d.Hkv * (pl.n_ct * s + d.B * pl.n_tt) < 512 || U / s > 2 * tok_units))
+    s *= 2;
+  pl.splits_c = s;
+  pl.grid_c = d.Hkv * pl.n_ct * s;
+  pl.grid_t = d.Hkv * d.B * pl.n_tt;
+  pl.dq_bytes = (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
+  pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);
+  pl.part_bytes = s > 1 ? (size_t)s * d.p * d.Hkv * d.D * sizeof(float) : 0;
+  return pl;
+}
+
+size_t bwd_workspace_bytes(const AttnDims& d) {
+  const BwdPlan pl = plan_bwd(d);
+  return align256(pl.dq_bytes) + align256(pl.delta_bytes) + 2 * align256(pl.part_bytes);
+}
+
+template <typename T, typename TR, int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
+  const int rows = a.B * a.n * a.Hq;
+  CART_TIMED("bwd_preprocess", st, bwd_preprocess<T, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  CART_TIMED("attn_bwd", st,
+             attn_bwd_kernel<T, TR, D><<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const size_t n4 = (size_t)rows * D / 4;
+  CART_TIMED("bwd_dq_finalize", st,
+             bwd_dq_finalize<T><<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(
+                 a.dq_acc, reinterpret_cast<T*>(a.dq), n4));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (pl.splits_c > 1) {
+    const size_t total = (size_t)a.p * a.Hkv * D;
+    CART_TIMED("bwd_cart_reduce", st,
+               bwd_cart_reduce_t<D><<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a));
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const void* v_tok,
+                      const void* k_cart, const void* v_cart, const void* out,
+                      const float* lse, const void* dout, void* dq, void* dk_tok,
+                      void* dv_tok, float* dk_cart, float* dv_cart, bool accumulate,
+                      void* ws, hipStream_t st) {
+  const BwdPlan pl = plan_bwd(d);
+  BwdArgs a{};
+  a.q = q; a.k_tok = k_tok; a.v_tok = v_tok; a.k_cart = k_cart; a.v_cart = v_cart;
+  a.out = out; a.dout = dout; a.lse = lse;
+  char* w = reinterpret_cast<char*>(ws);
+  a.dq_acc = reinterpret_cast<float*>(w);
+  w += align256(pl.dq_bytes);
+  a.delta = reinterpret_cast<float*>(w);
+  w += align256(pl.delta_bytes);
+  a.dk_part = pl.part_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  w += align256(pl.part_bytes);
+  a.dv_part = pl.part_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  a.dq = dq; a.dk_tok = dk_tok; a.dv_tok = dv_tok; a.dk_cart = dk_cart; a.dv_cart = dv_cart;
+  a.B = d.B; a.n = d.n; a.p = d.p; a.f = d.f; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
+  a.n_ct = pl.n_ct; a.n_tt = pl.n_tt; a.nqt = pl.nqt; a.splits_c = pl.splits_c;
+  a.accumulate = accumulate ? 1 : 0;
+  a.scale = d.scale;
+  a.scale_log2 = d.scale * kLog2e;
+  if (d.tok_bf16) {
+    if (d.D == 128)
+      return d.row_bf16 ? launch_bwd_t<bf16, bf16, 128>(a, pl, st)
+                        : launch_bwd_t<bf16, float, 128>(a, pl, st);
+    return d.row_bf16 ? launch_bwd_t<bf16, bf16, 64>(a, pl, st)
+                      : launch_bwd_t<bf16, float, 64>(a, pl, st);
+  }
+  if (d.D == 128) return launch_bwd_t<float, float, 128>(a, pl, st);
+  return launch_bwd_t<float, float, 64>(a, pl, st);
+}
+
+}  // namespace cartattn

@@ -1,0 +1,380 @@
+// Forward pass of end-aligned causal grouped-query attention over
+// concat(cartridge rows, real tokens).
+//
+// Source: "Cartridges: trained KV-prefix corpus compression", section
+// "Semantics (pinned to the reference implementation)": concat(sink,
+// trainable, tokens) along seq feeds grouped attention whose end-aligned
+// causal mask (source_offset = kv_seq - q_seq) lets every query see the whole
+// cartridge while staying causal over real tokens.
+//
+// Design (gfx950):
+//  * one workgroup = 4 waves = 128 query rows of ONE kv-head group: the GQA
+//    q-heads of the group are packed as extra rows, so every K/V tile staged
+//    in LDS serves all of them;
+//  * each wave owns 32 query rows of one q-head; its Q^T fragments stay in
+//    registers for the whole key loop;
+//  * S^T = K Q^T on the 32x32 MFMA (bf16 32x32x16, or f32 32x32x2 in the
+//    float32 reference mode): rows are keys, columns are queries, so the
+//    softmax statistics of a query live in one lane pair and the f32 result,
+//    cast to bf16, is directly the B operand of O^T += V^T P^T;
+//  * online softmax in f32 in the exp2 domain (scale * log2 e folded in);
+//  * the key loop streams cartridge tiles (no mask) and then token tiles
+//    (mask only on the diagonal tiles); the concat is never materialized;
+//  * when the grid would be too small to fill 256 CUs the key range is split
+//    and a combine kernel merges the partial (O, LSE) pairs by log-sum-exp;
+//  * block ids are remapped so each XCD works on one contiguous range of kv
+//    heads, keeping that head's cartridge tiles in its own L2.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "timing.hpp"
+
+namespace cartattn {
+
+namespace {
+
+constexpr int kBN = 64;        // keys per LDS tile
+constexpr int kThreads = 256;  // 4 waves
+
+struct FwdArgs {
+  const void* q;
+  const void* k_tok;
+  const void* v_tok;
+  const void* k_cart;
+  const void* v_cart;
+  void* out;
+  float* lse;
+  float* o_part;
+  float* lse_part;
+  int B, n, p, Hq, Hkv, g;
+  int hpw, wph, n_hg, n_qb, n_splits;
+  float scale_log2;
+};
+
+template <typename T> struct Lds;
+template <> struct Lds<bf16> {
+  static constexpr int kpad = 8;   // K row stride D+8 bf16: conflict-free b128 reads
+  static constexpr int vpad = 4;   // V^T row stride 68 bf16: conflict-free b64 reads
+};
+template <> struct Lds<float> {
+  static constexpr int kpad = 1;   // odd strides: conflict-free b32 reads
+  static constexpr int vpad = 1;
+};
+
+// A-operand fragment of V^T for MFMA m over a 32-key group whose LDS row
+// (one head_dim column of V) starts at `row`: item t holds key d_row(m*KPL+t).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag vt_frag(const T* row, int m, int hl);
+template <>
+__device__ __forceinline__ bf16x8 vt_frag<bf16>(const bf16* row, int m, int hl) {
+  // keys 16m + 4hl + {0..3} and 16m + 8 + 4hl + {0..3}
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + 16 * m + 4 * hl);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + 16 * m + 8 + 4 * hl);
+  bf16x8 f;
+  f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+  f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+  return f;
+}
+template <>
+__device__ __forceinline__ float vt_frag<float>(const float* row, int m, int hl) {
+  return row[d_row(m, hl)];
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_store8(T* p, const float (&v)[8]);
+template <> __device__ __forceinline__ void lds_store8<bf16>(bf16* p, const float (&v)[8]) {
+  store8<bf16>(p, v);
+}
+template <> __device__ __forceinline__ void lds_store8<float>(float* p, const float (&v)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) p[e] = v[e];
+}
+
+// Stage one tile of `rows` key/value rows into LDS: K row-major [BN][KSTR],
+// V transposed [D][VSTR]. Rows at or beyond `rows` are zero-filled.
+template <typename T, typename TS, int D>
+__device__ __forceinline__ void stage_tile(T* Ks, T* Vt, const TS* kbase, const TS* vbase,
+                                           size_t row_stride, int rows, int tid) {
+  constexpr int KSTR = D + Lds<T>::kpad;
+  constexpr int VSTR = kBN + Lds<T>::vpad;
+  constexpr int CPR = D / 8;               // 8-element chunks per row
+  constexpr int NCH = kBN * CPR / kThreads;
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int c = tid + u * kThreads;
+    const int r = c / CPR;
+    const int col = (c % CPR) * 8;
+    float kv8[8], vv8[8];
+    if (r < rows) {
+      load8<TS>(kbase + (size_t)r * row_stride + col, kv8);
+      load8<TS>(vbase + (size_t)r * row_stride + col, vv8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kv8[e] = 0.f; vv8[e] = 0.f; }
+    }
+    lds_store8<T>(Ks + r * KSTR + col, kv8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Vt[(col + e) * VSTR + r] = from_f32<T>(vv8[e]);
+  }
+}
+
+template <typename T, typename TR, int D>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
+  using M = Mfma<T>;
+  constexpr int KPL = M::KPL;
+  constexpr int KSTEP = M::KSTEP;
+  constexpr int NKS = D / KSTEP;
+  constexpr int NDB = D / 32;
+  constexpr int NKH = kBN / 32;
+  constexpr int NPV = 16 / KPL;   // PV MFMAs per 32-key group
+  constexpr int KSTR = D + Lds<T>::kpad;
+  constexpr int VSTR = kBN + Lds<T>::vpad;
+  __shared__ __align__(16) T Ks[kBN * KSTR];
+  __shared__ __align__(16) T Vt[D * VSTR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lg % a.n_splits; lg /= a.n_splits;
+  const int qb = a.n_qb - 1 - (lg % a.n_qb); lg /= a.n_qb;   // longest blocks first
+  const int hg = lg % a.n_hg; lg /= a.n_hg;
+  const int b = lg % a.B; lg /= a.B;
+  const int kv = lg;
+
+  const int hw = wave % a.hpw;
+  const int pb = wave / a.hpw;
+  const int h = kv * a.g + hg * a.hpw + hw;
+  const int i0 = (qb * a.wph + pb) * 32;
+  const bool wave_active = i0 < a.n;
+  const int my_i = i0 + l32;
+
+  const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
+  const int n_ct = (a.p + kBN - 1) / kBN;
+  const int nt = n_ct + wg_last / kBN + 1;
+  const int t_begin = (int)((long long)split * nt / a.n_splits);
+  const int t_end = (int)((long long)(split + 1) * nt / a.n_splits);
+
+  // Q^T fragments (B operand): lane (q + 32 hl) holds Q[q][ks*KSTEP + hl*KPL ..].
+  typename M::frag qf[NKS];
+  {
+    const int qi = min(my_i, a.n - 1);
+    const T* qp = reinterpret_cast<const T*>(a.q) + (((size_t)b * a.n + qi) * a.Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = load_frag<T>(qp + ks * KSTEP + hl * KPL);
+  }
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const size_t tok_stride = (size_t)a.Hkv * D;   // between consecutive rows
+  for (int t = t_begin; t < t_end; ++t) {
+    const bool cart = t < n_ct;
+    const int j0 = cart ? t * kBN : (t - n_ct) * kBN;
+    const int rows = cart ? min(kBN, a.p - j0) : min(kBN, a.n - j0);
+    __syncthreads();
+    if (cart) {
+      const TR* kb = reinterpret_cast<const TR*>(a.k_cart) + ((size_t)j0 * a.Hkv + kv) * D;
+      const TR* vb = reinterpret_cast<const TR*>(a.v_cart) + ((size_t)j0 * a.Hkv + kv) * D;
+      stage_tile<T, TR, D>(Ks, Vt, kb, vb, tok_stride, rows, tid);
+    } else {
+      const size_t off = (((size_t)b * a.n + j0) * a.Hkv + kv) * D;
+      stage_tile<T, T, D>(Ks, Vt, reinterpret_cast<const T*>(a.k_tok) + off,
+                          reinterpret_cast<const T*>(a.v_tok) + off, tok_stride, rows, tid);
+    }
+    __syncthreads();
+    if (!wave_active) continue;
+    if (!cart && j0 > i0 + 31) continue;   // whole tile above this wave's diagonal
+
+    // S^T = K Q^T for the tile's 32-key groups.
+    f32x16 s[NKH];
+#pragma unroll
+    for (int kh = 0; kh < NKH; ++kh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+      const T* krow = Ks + (32 * kh + l32) * KSTR + hl * KPL;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s[kh] = M::mma(load_frag<T>(krow + ks * KSTEP), qf[ks], s[kh]);
+    }
+
+    // Mask, scale into the exp2 domain, running max.
+    const bool diag = !cart && (j0 + kBN - 1 > i0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < NKH; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kh + d_row(r, hl);
+        bool vis = key < rows;
+        if (diag) vis = vis && (j0 + key <= my_i);
+        const float v = vis ? s[kh][r] * a.scale_log2 : -INFINITY;
+        s[kh][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = wave_max_halves(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < NKH; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2f(s[kh][r] - m_use);
+        s[kh][r] = pv;
+        ls += pv;
+      }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+
+    // O^T += V^T P^T: P^T (cast to T) is the B operand straight from s.
+#pragma unroll
+    for (int kh = 0; kh < NKH; ++kh)
+#pragma unroll
+      for (int m = 0; m < NPV; ++m) {
+        const typename M::frag pf = pack_regs<T>(s[kh], m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const T* vrow = Vt + (32 * db + l32) * VSTR + 32 * kh;
+          acc[db] = M::mma(vt_frag<T>(vrow, m, hl), pf, acc[db]);
+        }
+      }
+  }
+
+  if (!wave_active || my_i >= a.n) return;
+  l_run = wave_sum_halves(l_run);
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  if (a.n_splits == 1) {
+    T* op = reinterpret_cast<T*>(a.out) + (((size_t)b * a.n + my_i) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          op[32 * db + 8 * c + 4 * hl + e] = from_f32<T>(acc[db][4 * c + e] * inv_l);
+    if (hl == 0) a.lse[((size_t)b * a.Hq + h) * a.n + my_i] = lse;
+  } else {
+    float* op = a.o_part + ((((size_t)split * a.B + b) * a.n + my_i) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float4 v4 = make_float4(acc[db][4 * c] * inv_l, acc[db][4 * c + 1] * inv_l,
+                                acc[db][4 * c + 2] * inv_l, acc[db][4 * c + 3] * inv_l);
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * c + 4 * hl) = v4;
+      }
+    if (hl == 0)
+      a.lse_part[(((size_t)split * a.B + b) * a.Hq + h) * a.n + my_i] = lse;
+  }
+}
+
+// Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
+// One thread per (b, i, h) row, D/4 float4 lanes... kept simple: one wave per row.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void attn_fwd_combine(FwdArgs a) {
+  const int row = blockIdx.x;             // (b, i, h) with h fastest
+  const int h = row % a.Hq;
+  const int bi = row / a.Hq;
+  const int i = bi % a.n;
+  const int b = bi / a.n;
+  const int lane = threadIdx.x;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s)
+    mx = fmaxf(mx, a.lse_part[(((size_t)s * a.B + b) * a.Hq + h) * a.n + i]);
+  float tot = 0.f;
+  float o[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float ls = a.lse_part[(((size_t)s * a.B + b) * a.Hq + h) * a.n + i];
+    const float w = (ls == -INFINITY) ? 0.f : expf(ls - mx);
+    tot += w;
+    const float* op = a.o_part + ((((size_t)s * a.B + b) * a.n + i) * a.Hq + h) * D;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) o[e] += w * op[lane + 64 * e];
+  }
+  T* out = reinterpret_cast<T*>(a.out) + (((size_t)b * a.n + i) * a.Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = from_f32<T>(o[e] / tot);
+  if (lane == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = mx + logf(tot);
+}
+
+}  // namespace
+
+FwdPlan plan_fwd(const AttnDims& d) {
+  FwdPlan pl{};
+  const int g = d.Hq / d.Hkv;
+  pl.hpw = (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1);
+  pl.wph = 4 / pl.hpw;
+  pl.n_hg = g / pl.hpw;
+  pl.n_qb = (d.n + 32 * pl.wph - 1) / (32 * pl.wph);
+  const long long base = (long long)d.Hkv * d.B * pl.n_hg * pl.n_qb;
+  // Fewest key tiles any workgroup sees; never split below 4 tiles each.
+  const int min_tiles = (d.p + kBN - 1) / kBN + 1;
+  int splits = 1;
+  while (base * splits < 512 && (splits * 2) * 4 <= min_tiles) splits *= 2;
+  pl.n_splits = splits;
+  pl.grid = (int)(base * splits);
+  if (splits > 1) {
+    pl.o_part_bytes = (size_t)splits * d.B * d.n * d.Hq * d.D * sizeof(float);
+    pl.lse_part_bytes = (size_t)splits * d.B * d.Hq * d.n * sizeof(float);
+  }
+  return pl;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fwd_workspace_bytes(const AttnDims& d) {
+  const FwdPlan pl = plan_fwd(d);
+  return align256(pl.o_part_bytes) + align256(pl.lse_part_bytes);
+}
+
+template <typename T, typename TR, int D>
+static hipError_t launch_fwd_t(const FwdArgs& a, const FwdPlan& pl, hipStream_t st) {
+  CART_TIMED("attn_fwd", st, attn_fwd_kernel<T, TR, D><<<pl.grid, kThreads, 0, st>>>(a));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.n_splits == 1) return e;
+  CART_TIMED("attn_fwd_combine", st, attn_fwd_combine<T, D><<<a.B * a.n * a.Hq, 64, 0, st>>>(a));
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const AttnDims& d, const void* q, const void* k_tok, const void* v_tok,
+                      const void* k_cart, const void* v_cart, void* out, float* lse,
+                      void* ws, hipStream_t st) {
+  const FwdPlan pl = plan_fwd(d);
+  FwdArgs a{};
+  a.q = q; a.k_tok = k_tok; a.v_tok = v_tok; a.k_cart = k_cart; a.v_cart = v_cart;
+  a.out = out; a.lse = lse;
+  a.o_part = reinterpret_cast<float*>(ws);
+  a.lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(pl.o_part_bytes));
+  a.B = d.B; a.n = d.n; a.p = d.p; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
+  a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb; a.n_splits = pl.n_splits;
+  a.scale_log2 = d.scale * kLog2e;
+  if (d.tok_bf16) {
+    if (d.D == 128)
+      return d.row_bf16 ? launch_fwd_t<bf16, bf16, 128>(a, pl, st)
+                        : launch_fwd_t<bf16, float, 128>(a, pl, st);
+    return d.row_bf16 ? launch_fwd_t<bf16, bf16, 64>(a, pl, st)
+                      : launch_fwd_t<bf16, float, 64>(a, pl, st);
+  }
+  if (d.D == 128) return launch_fwd_t<float, float, 128>(a, pl, st);
+  return launch_fwd_t<float, float, 64>(a, pl, st);
+}
+
+}  // namespace cartattn

@@ -1,0 +1,377 @@
+// libcartattn C ABI: argument checking, workspace sizing, the paged-cache
+// handle and kernel launches. Every check runs on the host before any HIP
+// call, so each error path can be exercised without a GPU.
+#include "cartattn.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "launch.hpp"
+
+using namespace cartattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool sync_each_call() {
+  static const bool on = [] {
+    const char* e = getenv("CARTATTN_SYNC");
+    return e && e[0] && e[0] != '0';
+  }();
+  return on;
+}
+
+int hip_result(hipError_t e, hipStream_t st, const char* what) {
+  if (e == hipSuccess && sync_each_call()) {
+    e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess) return fail(CART_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return CART_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_dtype(int d) { return d == CART_F32 || d == CART_BF16; }
+bool valid_head_dim(int d) { return d == 64 || d == 128; }
+constexpr long long kMaxElems = (1LL << 31) - 1;   // element offsets stay in int range per tensor
+
+int check_shape(const cart_attn_shape* s) {
+  if (!s) return fail(CART_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 1 || s->q_seq < 1)
+    return fail(CART_ERR_INVALID_ARG, "batch (%d) and q_seq (%d) must be >= 1", s->batch, s->q_seq);
+  if (s->p < 0) return fail(CART_ERR_INVALID_ARG, "p (%d) must be >= 0", s->p);
+  if (s->frozen_rows < 0 || s->frozen_rows > s->p)
+    return fail(CART_ERR_INVALID_ARG, "frozen_rows (%d) must lie in [0, p=%d]", s->frozen_rows, s->p);
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(CART_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(CART_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (!valid_head_dim(s->head_dim))
+    return fail(CART_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", s->head_dim);
+  if (!(s->scale >= 0.f) || isinf(s->scale))
+    return fail(CART_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if (!valid_dtype(s->tok_dtype) || !valid_dtype(s->row_dtype))
+    return fail(CART_ERR_INVALID_ARG, "unknown dtype");
+  if (s->tok_dtype == CART_F32 && s->row_dtype != CART_F32)
+    return fail(CART_ERR_UNSUPPORTED, "f32 tokens need f32 cartridge rows");
+  const long long qe = (long long)s->batch * s->q_seq * s->n_q_heads * s->head_dim;
+  const long long ce = (long long)s->p * s->n_kv_heads * s->head_dim;
+  if (qe > kMaxElems || ce > kMaxElems)
+    return fail(CART_ERR_UNSUPPORTED, "tensor too large for 32-bit element counts");
+  const long long grid = (long long)s->batch * s->q_seq * s->n_q_heads;
+  if (grid > kMaxElems / 4) return fail(CART_ERR_UNSUPPORTED, "too many query rows");
+  return CART_OK;
+}
+
+AttnDims dims_of(const cart_attn_shape* s) {
+  AttnDims d{};
+  d.B = s->batch; d.n = s->q_seq; d.p = s->p; d.f = s->frozen_rows;
+  d.Hq = s->n_q_heads; d.Hkv = s->n_kv_heads; d.D = s->head_dim;
+  d.scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
+  d.tok_bf16 = s->tok_dtype == CART_BF16;
+  d.row_bf16 = s->row_dtype == CART_BF16;
+  return d;
+}
+
+int need_ptr(const void* p, const char* name) {
+  if (!p) return fail(CART_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(CART_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return CART_OK;
+}
+
+int opt_ptr(const void* p, const char* name) {
+  if (p && !aligned16(p)) return fail(CART_ERR_ALIGNMENT, "%s is not 16-byte aligned", name);
+  return CART_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return CART_OK;
+  if (!ws) return fail(CART_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (have < need)
+    return fail(CART_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  if (!aligned16(ws)) return fail(CART_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  return CART_OK;
+}
+
+#define CHECK(expr)               \
+  do {                            \
+    const int _st = (expr);       \
+    if (_st != CART_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+struct cart_cache {
+  cart_cache_desc d;
+  std::vector<int32_t> lens;   // host mirror of seq_lens
+};
+
+namespace {
+
+CacheDims cache_dims(const cart_cache* c) {
+  CacheDims cd{};
+  cd.n_seqs = c->d.n_seqs; cd.Hkv = c->d.n_kv_heads; cd.D = c->d.head_dim;
+  cd.page = c->d.page_size; cd.max_pages = c->d.max_pages_per_seq; cd.n_pages = c->d.n_pages;
+  cd.k_pages = c->d.k_pages; cd.v_pages = c->d.v_pages;
+  cd.block_table = c->d.block_table; cd.seq_lens = c->d.seq_lens;
+  return cd;
+}
+
+long long capacity(const cart_cache* c) {
+  return (long long)c->d.max_pages_per_seq * c->d.page_size;
+}
+
+int check_seq(const cart_cache* c, int32_t seq) {
+  if (!c) return fail(CART_ERR_INVALID_ARG, "cache handle is NULL");
+  if (seq < 0 || seq >= c->d.n_seqs)
+    return fail(CART_ERR_INVALID_ARG, "seq %d outside [0, %d)", seq, c->d.n_seqs);
+  return CART_OK;
+}
+
+int check_rows(const cart_cache* c, int32_t seq, const void* k, const void* v, cart_dtype src,
+               int32_t n_rows, int32_t n_kv_heads, int32_t head_dim) {
+  CHECK(check_seq(c, seq));
+  if (n_kv_heads != c->d.n_kv_heads || head_dim != c->d.head_dim)
+    return fail(CART_ERR_GEOMETRY, "rows have %d kv heads x %d, the cache %d x %d", n_kv_heads,
+                head_dim, c->d.n_kv_heads, c->d.head_dim);
+  if (!valid_dtype(src)) return fail(CART_ERR_INVALID_ARG, "unknown source dtype");
+  if (n_rows < 0) return fail(CART_ERR_INVALID_ARG, "row count %d < 0", n_rows);
+  if ((long long)c->lens[seq] + n_rows > capacity(c))
+    return fail(CART_ERR_CACHE_FULL, "seq %d: %d + %d rows exceed capacity %lld", seq,
+                c->lens[seq], n_rows, capacity(c));
+  if (n_rows > 0) {
+    CHECK(need_ptr(k, "k"));
+    CHECK(need_ptr(v, "v"));
+  }
+  return CART_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cart_status_string(int status) {
+  switch (status) {
+    case CART_OK: return "ok";
+    case CART_ERR_INVALID_ARG: return "invalid argument";
+    case CART_ERR_UNSUPPORTED: return "unsupported";
+    case CART_ERR_ALIGNMENT: return "misaligned pointer";
+    case CART_ERR_WORKSPACE: return "workspace missing or too small";
+    case CART_ERR_CACHE_NOT_EMPTY: return "cache sequence not empty";
+    case CART_ERR_CACHE_FULL: return "cache sequence full";
+    case CART_ERR_GEOMETRY: return "geometry mismatch";
+    case CART_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* cart_last_error(void) { return g_err; }
+
+int cart_rope_tokens(void* q, void* k, cart_dtype dt, int32_t batch, int32_t seq,
+                     int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int32_t pos_base,
+                     const int32_t* pos_offsets, double theta, int32_t inverse, void* stream) {
+  if (!valid_dtype(dt)) return fail(CART_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 0 || seq < 0) return fail(CART_ERR_INVALID_ARG, "batch and seq must be >= 0");
+  if (n_q_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (k && n_kv_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+  if (!valid_head_dim(head_dim))
+    return fail(CART_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if (!(theta > 0.0) || isinf(theta)) return fail(CART_ERR_INVALID_ARG, "theta must be > 0");
+  if (pos_base < 0) return fail(CART_ERR_INVALID_ARG, "pos_base must be >= 0");
+  const long long rows = (long long)batch * seq;
+  if (rows * (n_q_heads + (k ? n_kv_heads : 0)) * head_dim > kMaxElems || rows > 0x7fffffffLL)
+    return fail(CART_ERR_UNSUPPORTED, "tensor too large");
+  if (rows == 0) { g_err[0] = '\0'; return CART_OK; }
+  CHECK(need_ptr(q, "q"));
+  CHECK(opt_ptr(k, "k"));
+  if (pos_offsets && (reinterpret_cast<uintptr_t>(pos_offsets) & 3u))
+    return fail(CART_ERR_ALIGNMENT, "pos_offsets is not 4-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_rope(q, k, dt == CART_BF16, batch, seq, n_q_heads, k ? n_kv_heads : 0,
+                                head_dim, pos_base, pos_offsets, theta, inverse != 0, st),
+                    st, "cart_rope_tokens");
+}
+
+size_t cart_attn_workspace_size(const cart_attn_shape* s, int32_t for_backward) {
+  if (check_shape(s) != CART_OK) return 0;
+  const AttnDims d = dims_of(s);
+  return for_backward ? bwd_workspace_bytes(d) : fwd_workspace_bytes(d);
+}
+
+int cart_attn_fwd(const cart_attn_shape* s, const void* q, const void* k_tok, const void* v_tok,
+                  const void* k_cart, const void* v_cart, void* out, float* lse, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  CHECK(check_shape(s));
+  CHECK(need_ptr(q, "q"));
+  CHECK(need_ptr(k_tok, "k_tok"));
+  CHECK(need_ptr(v_tok, "v_tok"));
+  if (s->p > 0) {
+    CHECK(need_ptr(k_cart, "k_cart"));
+    CHECK(need_ptr(v_cart, "v_cart"));
+  }
+  CHECK(need_ptr(out, "out"));
+  CHECK(need_ptr(lse, "lse"));
+  const AttnDims d = dims_of(s);
+  CHECK(check_workspace(workspace, workspace_bytes, fwd_workspace_bytes(d)));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_fwd(d, q, k_tok, v_tok, k_cart, v_cart, out, lse, workspace, st), st,
+                    "cart_attn_fwd");
+}
+
+int cart_attn_bwd(const cart_attn_shape* s, const void* q, const void* k_tok, const void* v_tok,
+                  const void* k_cart, const void* v_cart, const void* out, const float* lse,
+                  const void* dout, void* dq, void* dk_tok, void* dv_tok, float* dk_cart,
+                  float* dv_cart, int32_t accumulate_cart, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  CHECK(check_shape(s));
+  CHECK(need_ptr(q, "q"));
+  CHECK(need_ptr(k_tok, "k_tok"));
+  CHECK(need_ptr(v_tok, "v_tok"));
+  CHECK(need_ptr(out, "out"));
+  CHECK(need_ptr(lse, "lse"));
+  CHECK(need_ptr(dout, "dout"));
+  CHECK(need_ptr(dq, "dq"));
+  CHECK(need_ptr(dk_tok, "dk_tok"));
+  CHECK(need_ptr(dv_tok, "dv_tok"));
+  if (s->p > 0) {
+    CHECK(need_ptr(k_cart, "k_cart"));
+    CHECK(need_ptr(v_cart, "v_cart"));
+    CHECK(need_ptr(dk_cart, "dk_cart"));
+    CHECK(need_ptr(dv_cart, "dv_cart"));
+  }
+  const AttnDims d = dims_of(s);
+  CHECK(check_workspace(workspace, workspace_bytes, bwd_workspace_bytes(d)));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_bwd(d, q, k_tok, v_tok, k_cart, v_cart, out, lse, dout, dq, dk_tok,
+                               dv_tok, dk_cart, dv_cart, accumulate_cart != 0, workspace, st),
+                    st, "cart_attn_bwd");
+}
+
+int cart_cache_create(const cart_cache_desc* d, cart_cache** out) {
+  if (!d || !out) return fail(CART_ERR_INVALID_ARG, "desc and out must be non-NULL");
+  *out = nullptr;
+  if (d->n_seqs < 1 || d->n_kv_heads < 1 || d->max_pages_per_seq < 1 || d->n_pages < 1)
+    return fail(CART_ERR_INVALID_ARG, "cache counts must be >= 1");
+  if (!valid_head_dim(d->head_dim))
+    return fail(CART_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", d->head_dim);
+  if (d->page_size != 16) return fail(CART_ERR_UNSUPPORTED, "page_size must be 16");
+  if (d->dtype != CART_BF16) return fail(CART_ERR_UNSUPPORTED, "cache dtype must be bf16");
+  if ((long long)d->n_pages * d->n_kv_heads * d->page_size * d->head_dim > (1LL << 40))
+    return fail(CART_ERR_UNSUPPORTED, "page pool too large");
+  if ((long long)d->max_pages_per_seq * d->page_size > 0x7fffffffLL)
+    return fail(CART_ERR_UNSUPPORTED, "sequence capacity too large");
+  CHECK(need_ptr(d->k_pages, "k_pages"));
+  CHECK(need_ptr(d->v_pages, "v_pages"));
+  CHECK(need_ptr(d->block_table, "block_table"));
+  CHECK(need_ptr(d->seq_lens, "seq_lens"));
+  cart_cache* c = new (std::nothrow) cart_cache;
+  if (!c) return fail(CART_ERR_INVALID_ARG, "out of host memory");
+  c->d = *d;
+  c->lens.assign(d->n_seqs, 0);
+  *out = c;
+  g_err[0] = '\0';
+  return CART_OK;
+}
+
+int cart_cache_destroy(cart_cache* c) {
+  delete c;
+  return CART_OK;
+}
+
+int cart_cache_reset(cart_cache* c, int32_t seq, void* stream) {
+  CHECK(check_seq(c, seq));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int r = hip_result(launch_cache_set_len(cache_dims(c), seq, 0, st), st, "cart_cache_reset");
+  if (r == CART_OK) c->lens[seq] = 0;
+  return r;
+}
+
+int32_t cart_cache_seq_len(const cart_cache* c, int32_t seq) {
+  if (!c || seq < 0 || seq >= c->d.n_seqs) return -1;
+  return c->lens[seq];
+}
+
+int cart_append_cache(cart_cache* c, int32_t seq, const void* k, const void* v, cart_dtype src,
+                      int32_t n_rows, int32_t n_kv_heads, int32_t head_dim, void* stream) {
+  CHECK(check_rows(c, seq, k, v, src, n_rows, n_kv_heads, head_dim));
+  if (n_rows == 0) { g_err[0] = '\0'; return CART_OK; }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int start = c->lens[seq];
+  const int r = hip_result(
+      launch_cache_append(cache_dims(c), seq, start, k, v, src == CART_BF16, n_rows, st), st,
+      "cart_append_cache");
+  if (r == CART_OK) c->lens[seq] = start + n_rows;
+  return r;
+}
+
+int cart_write_cache(cart_cache* c, int32_t seq, const void* k_cart, const void* v_cart,
+                     cart_dtype src, int32_t p, int32_t n_kv_heads, int32_t head_dim,
+                     void* stream) {
+  CHECK(check_seq(c, seq));
+  if (c->lens[seq] != 0)
+    return fail(CART_ERR_CACHE_NOT_EMPTY, "seq %d already holds %d rows", seq, c->lens[seq]);
+  return cart_append_cache(c, seq, k_cart, v_cart, src, p, n_kv_heads, head_dim, stream);
+}
+
+size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads) {
+  if (!c || n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0) return 0;
+  return plan_decode(cache_dims(c), n_q_heads).part_bytes;
+}
+
+int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                int32_t n_q_heads, float scale, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!c) return fail(CART_ERR_INVALID_ARG, "cache handle is NULL");
+  if (n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0)
+    return fail(CART_ERR_GEOMETRY, "n_q_heads %d is not a multiple of the cache's %d kv heads",
+                n_q_heads, c->d.n_kv_heads);
+  const int g = n_q_heads / c->d.n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(CART_ERR_UNSUPPORTED, "GQA group size %d not built (1, 2, 4, 8)", g);
+  if (!(scale >= 0.f) || isinf(scale)) return fail(CART_ERR_INVALID_ARG, "scale must be >= 0");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(CART_ERR_INVALID_ARG, "k_new and v_new must both be given or both be NULL");
+  CHECK(need_ptr(q, "q"));
+  CHECK(need_ptr(out, "out"));
+  CHECK(opt_ptr(k_new, "k_new"));
+  CHECK(opt_ptr(v_new, "v_new"));
+  const int add = k_new ? 1 : 0;
+  int max_len = 0;
+  for (int s = 0; s < c->d.n_seqs; ++s) {
+    const long long len = (long long)c->lens[s] + add;
+    if (len < 1) return fail(CART_ERR_INVALID_ARG, "seq %d holds no rows to attend over", s);
+    if (len > capacity(c))
+      return fail(CART_ERR_CACHE_FULL, "seq %d: appending exceeds capacity %lld", s, capacity(c));
+    if (len > max_len) max_len = (int)len;
+  }
+  const CacheDims cd = cache_dims(c);
+  CHECK(check_workspace(workspace, workspace_bytes, plan_decode(cd, n_q_heads).part_bytes));
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)c->d.head_dim);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int r = hip_result(
+      launch_decode(cd, n_q_heads, sc, q, k_new, v_new, max_len, out, workspace, st), st,
+      "cart_decode");
+  if (r == CART_OK && add)
+    for (int s = 0; s < c->d.n_seqs; ++s) c->lens[s] += 1;
+  return r;
+}
+
+}  // extern "C"

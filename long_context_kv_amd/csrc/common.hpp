@@ -1,0 +1,142 @@
+// Shared device helpers for the cartridge-attention kernels (gfx950, wave64).
+//
+// MFMA operand convention used by every attention kernel here. For the
+// 32x32 MFMAs (bf16 32x32x16 and f32 32x32x2) a wave holds:
+//   A[i][k]  in lane (i + 32*kh), item t   with k = slot(kh, t)
+//   B[k][j]  in lane (j + 32*kh), item t   with k = slot(kh, t)
+//   D[i][j]  in lane (j + 32*h),  reg r    with i = (r & 3) + 4*h + 8*(r >> 2)
+// where kh = lane / 32 and t < KPL (8 for bf16, 1 for f32). The kernels never
+// depend on how the hardware orders slot(kh, t) inside one instruction: A and
+// B are always filled from the same (kh, t) -> k map, so any order contracts
+// the right pairs. The only layout fact used is the D map above, which lets
+// the f32 result of one MFMA (rows = keys, columns = queries) be fed back as
+// the B operand of the next one after a cast, with k = the key rows in the
+// order row_of(r, h) = (r & 3) + 4*h + 8*(r >> 2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cartattn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+// float -> storage type; the bf16 conversion rounds to nearest even.
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// Row index of register r of a 32x32 MFMA result in lane half h.
+__device__ __forceinline__ constexpr int d_row(int r, int h) {
+  return (r & 3) + 4 * h + 8 * (r >> 2);
+}
+
+// Per-type MFMA policy: KPL = contraction elements per lane per
+// instruction; KSTEP = 2*KPL elements per instruction.
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 16;
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 2;
+  typedef float frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// KPL consecutive elements starting at p (16-byte aligned for bf16).
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag load_frag(const T* p);
+template <> __device__ __forceinline__ bf16x8 load_frag<bf16>(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ __forceinline__ float load_frag<float>(const float* p) { return *p; }
+
+// Item t of a fragment.
+__device__ __forceinline__ float frag_get(bf16x8 f, int t) { return (float)f[t]; }
+__device__ __forceinline__ float frag_get(float f, int) { return f; }
+
+// Build the B/A fragment for MFMA number m of the PV-type contraction from
+// the f32 result registers of a previous MFMA: items t <- regs m*KPL + t.
+template <typename T>
+__device__ __forceinline__ typename Mfma<T>::frag pack_regs(const f32x16& s, int m);
+template <> __device__ __forceinline__ bf16x8 pack_regs<bf16>(const f32x16& s, int m) {
+  bf16x8 f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) f[t] = (bf16)s[m * 8 + t];
+  return f;
+}
+template <> __device__ __forceinline__ float pack_regs<float>(const f32x16& s, int m) {
+  return s[m];
+}
+
+// Load 8 consecutive elements of type TS from global memory and convert to
+// f32 (used for staging rows into LDS with an optional dtype change).
+template <typename TS>
+__device__ __forceinline__ void load8(const TS* p, float (&v)[8]);
+template <> __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <> __device__ __forceinline__ void load8<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) v[t] = (float)a[t];
+}
+
+// Store 8 f32 values as 8 consecutive elements of type T.
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[8]);
+template <> __device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const float (&v)[8]) {
+  bf16x8 a;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) a[t] = (bf16)v[t];
+  *reinterpret_cast<bf16x8*>(p) = a;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X. Map the
+// hardware block id to a logical id so that each XCD receives one contiguous
+// range of logical ids (and therefore shares K/V and accumulators in its own
+// L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int xcd = bid % kXcd;
+  const int idx = bid / kXcd;
+  const int q = nblocks / kXcd;
+  const int r = nblocks % kXcd;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  return x + __shfl_xor(x, 32);
+}
+
+}  // namespace cartattn

@@ -1,0 +1,358 @@
+// Serving behind a cartridge: writing the prefix into a paged bf16 KV cache,
+// appending rows, and the single-token decode step.
+//
+// Source: "Cartridges: trained KV-prefix corpus compression", section
+// "Semantics (pinned to the reference implementation)", serving: the whole
+// prefix is written into an empty KV cache, converted to the cache dtype, the
+// cache is advanced to p and a normal decode continues at position p; section
+// "Composition": appending to the cache is the primitive; section "Evidence":
+// decode behind the written prefix matches the trainer's cartridge eval.
+//
+// Cache layout: k_pages/v_pages are [n_pages][Hkv][16][D] bf16, so one
+// (page, kv-head) is a contiguous 16*D*2-byte run (4 KiB at D = 128) and a
+// decode workgroup streams whole runs. block_table maps (seq, logical page)
+// to a physical page id.
+//
+// Decode is HBM-bound (4 flop per byte of K/V), so it uses no MFMA: one
+// workgroup per (sequence, kv head, split of the pages). The q-heads of the
+// GQA group share every K/V byte read. Each thread owns one 8-element chunk
+// of one row per pass and keeps a private online-softmax state per q-head;
+// the states are merged with cross-lane shuffles and through LDS at the end,
+// and a second kernel merges the splits of a sequence by log-sum-exp.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "timing.hpp"
+
+namespace cartattn {
+
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kDecThreads = 256;
+constexpr int kMaxG = 8;     // q-heads per kv head handled by one workgroup
+constexpr int kUnroll = 4;   // passes in flight per thread
+
+template <typename TS>
+__global__ __launch_bounds__(256) void cache_append_kernel(CacheDims c, int seq, int start,
+                                                           const TS* __restrict__ k,
+                                                           const TS* __restrict__ v,
+                                                           int n_rows) {
+  const int cpr = c.D / 8;
+  const size_t total = (size_t)n_rows * c.Hkv * cpr;
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e == 0) c.seq_lens[seq] = start + n_rows;
+  if (e >= total) return;
+  const int chunk = (int)(e % cpr);
+  const int h = (int)((e / cpr) % c.Hkv);
+  const int r = (int)(e / ((size_t)cpr * c.Hkv));
+  const int row = start + r;
+  const int lp = row / kPage;
+  if (lp >= c.max_pages) return;
+  const int page = c.block_table[(size_t)seq * c.max_pages + lp];
+  if (page < 0 || page >= c.n_pages) return;
+  const size_t src = ((size_t)r * c.Hkv + h) * c.D + chunk * 8;
+  const size_t dst = (((size_t)page * c.Hkv + h) * kPage + row % kPage) * c.D + chunk * 8;
+  float v8[8];
+  load8<TS>(k + src, v8);
+  store8<bf16>(reinterpret_cast<bf16*>(c.k_pages) + dst, v8);
+  load8<TS>(v + src, v8);
+  store8<bf16>(reinterpret_cast<bf16*>(c.v_pages) + dst, v8);
+}
+
+__global__ void cache_set_len_kernel(int32_t* seq_lens, int seq, int len) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) seq_lens[seq] = len;
+}
+
+// Append one new row per sequence at position seq_len[s], then seq_len += 1.
+__global__ __launch_bounds__(256) void decode_append_kernel(CacheDims c,
+                                                            const bf16* __restrict__ k_new,
+                                                            const bf16* __restrict__ v_new) {
+  const int s = blockIdx.x;
+  const int cpr = c.D / 8;
+  const int len = c.seq_lens[s];
+  __syncthreads();   // every thread has read the old length
+  const int lp = len / kPage;
+  if (lp < c.max_pages) {
+    const int page = c.block_table[(size_t)s * c.max_pages + lp];
+    if (page >= 0 && page < c.n_pages) {
+      for (int e = threadIdx.x; e < c.Hkv * cpr; e += blockDim.x) {
+        const int h = e / cpr;
+        const int chunk = e % cpr;
+        const size_t src = ((size_t)s * c.Hkv + h) * c.D + chunk * 8;
+        const size_t dst = (((size_t)page * c.Hkv + h) * kPage + len % kPage) * c.D + chunk * 8;
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(c.k_pages) + dst) =
+            *reinterpret_cast<const bf16x8*>(k_new + src);
+        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(c.v_pages) + dst) =
+            *reinterpret_cast<const bf16x8*>(v_new + src);
+      }
+    }
+  }
+  if (threadIdx.x == 0) c.seq_lens[s] = len + 1;
+}
+
+struct DecArgs {
+  CacheDims c;
+  const bf16* q;
+  bf16* out;
+  float* part;         // [n_seqs][Hq][max_splits][D + 2]: m, l, acc[D]
+  int Hq, g, pps, max_splits;
+  float scale_log2;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
+  constexpr int CPR = D / 8;                 // chunks per row
+  constexpr int RPP = kDecThreads / CPR;     // rows per pass
+  constexpr int GPW = 64 / CPR;              // row groups per wave
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int chunk = tid % CPR;
+  const int rsub = tid / CPR;
+
+  const int nb = a.max_splits;
+  const int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lg % nb;
+  const int kv = (lg / nb) % a.c.Hkv;
+  const int s = lg / (nb * a.c.Hkv);
+  const int len = a.c.seq_lens[s];
+  const int row_begin = split * a.pps * kPage;
+  // clamp to the block table's capacity so a bad device length cannot read past it
+  const int row_end = min(min(len, row_begin + a.pps * kPage), a.c.max_pages * kPage);
+
+  float qv[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    const bf16* qp = a.q + ((size_t)s * a.Hq + kv * a.g + j) * D + chunk * 8;
+    load8<bf16>(qp, qv[j]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[j][e] *= a.scale_log2;
+  }
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  }
+
+  const int32_t* bt = a.c.block_table + (size_t)s * a.c.max_pages;
+  const bf16* kp = reinterpret_cast<const bf16*>(a.c.k_pages);
+  const bf16* vp = reinterpret_cast<const bf16*>(a.c.v_pages);
+  for (int r0 = row_begin; r0 < row_end; r0 += kUnroll * RPP) {
+    float kx[kUnroll][8], vx[kUnroll][8];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int row = r0 + u * RPP + rsub;
+      int page = -1;
+      if (row < row_end) page = bt[row / kPage];
+      ok[u] = page >= 0 && page < a.c.n_pages;
+      if (ok[u]) {
+        const size_t off = (((size_t)page * a.c.Hkv + kv) * kPage + row % kPage) * D + chunk * 8;
+        load8<bf16>(kp + off, kx[u]);
+        load8<bf16>(vp + off, vx[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kx[u][e] = 0.f; vx[u][e] = 0.f; }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float sc[kUnroll];
+      float mx = m[j];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += qv[j][e] * kx[u][e];
+#pragma unroll
+        for (int off = 1; off < CPR; off <<= 1) d += __shfl_xor(d, off);
+        sc[u] = ok[u] ? d : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      const float mu = (mx == -INFINITY) ? 0.f : mx;
+      const float alpha = exp2f(m[j] - mu);
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float pv = exp2f(sc[u] - mu);
+        ls += pv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] += pv * vx[u][e];
+      }
+      l[j] = l[j] * alpha + ls;
+      m[j] = mx;
+    }
+  }
+
+  // Merge the row groups of a wave (lanes with the same chunk).
+#pragma unroll
+  for (int off = CPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float mo = __shfl_xor(m[j], off);
+      const float lo = __shfl_xor(l[j], off);
+      const float mn = fmaxf(m[j], mo);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float wa = exp2f(m[j] - mu);
+      const float wb = exp2f(mo - mu);
+      l[j] = l[j] * wa + lo * wb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] * wa + __shfl_xor(acc[j][e], off) * wb;
+      m[j] = mn;
+    }
+  }
+  (void)GPW;
+  // Merge the 4 waves through LDS.
+  __shared__ __align__(16) float sm[4][G];
+  __shared__ __align__(16) float sl[4][G];
+  __shared__ __align__(16) float sacc[4][G][D];
+  if (lane < CPR) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (lane == 0) { sm[wave][j] = m[j]; sl[wave][j] = l[j]; }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sacc[wave][j][chunk * 8 + e] = acc[j][e];
+    }
+  }
+  __syncthreads();
+  // Every thread finishes (head j, element d) pairs.
+  for (int t = tid; t < G * D; t += kDecThreads) {
+    const int j = t / D;
+    const int dd = t % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm[w][j]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    float lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = exp2f(sm[w][j] - mu);
+      lt += sl[w][j] * wt;
+      at += sacc[w][j][dd] * wt;
+    }
+    float* pp = a.part + (((size_t)s * a.Hq + kv * a.g + j) * a.max_splits + split) * (D + 2);
+    if (dd == 0) { pp[0] = mx; pp[1] = lt; }
+    pp[2 + dd] = at;
+  }
+}
+
+// out[s, h] = sum over the sequence's splits, weighted by exp2(m_split - M).
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
+  const int sh = blockIdx.x;          // s * Hq + h
+  const int s = sh / a.Hq;
+  const int lane = threadIdx.x;
+  const int len = min(a.c.seq_lens[s], a.c.max_pages * kPage);
+  const int pages = (len + kPage - 1) / kPage;
+  const int ns = min(a.max_splits, (pages + a.pps - 1) / a.pps);
+  const float* pp = a.part + (size_t)sh * a.max_splits * (D + 2);
+  float mx = -INFINITY;
+  for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * (D + 2)]);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float lt = 0.f;
+  float o[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
+  for (int t = 0; t < ns; ++t) {
+    const float w = exp2f(pp[t * (D + 2)] - mu);
+    lt += w * pp[t * (D + 2) + 1];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) o[e] += w * pp[t * (D + 2) + 2 + lane + 64 * e];
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) a.out[(size_t)sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
+}
+
+template <int D, int G>
+hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
+  const int grid = a.c.n_seqs * a.c.Hkv * a.max_splits;
+  CART_TIMED("decode", st, decode_kernel<D, G><<<grid, kDecThreads, 0, st>>>(a));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  CART_TIMED("decode_merge", st, decode_merge_kernel<D><<<a.c.n_seqs * a.Hq, 64, 0, st>>>(a));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_dec_d(const DecArgs& a, hipStream_t st) {
+  switch (a.g) {
+    case 1: return launch_dec_t<D, 1>(a, st);
+    case 2: return launch_dec_t<D, 2>(a, st);
+    case 4: return launch_dec_t<D, 4>(a, st);
+    case 8: return launch_dec_t<D, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_append(const CacheDims& c, int seq, int start, const void* k,
+                               const void* v, bool src_bf16, int n_rows, hipStream_t st) {
+  const size_t total = (size_t)n_rows * c.Hkv * (c.D / 8);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (src_bf16)
+    CART_TIMED("cache_append", st,
+               cache_append_kernel<bf16><<<blocks ? blocks : 1, 256, 0, st>>>(
+                   c, seq, start, reinterpret_cast<const bf16*>(k),
+                   reinterpret_cast<const bf16*>(v), n_rows));
+  else
+    CART_TIMED("cache_append", st,
+               cache_append_kernel<float><<<blocks ? blocks : 1, 256, 0, st>>>(
+                   c, seq, start, reinterpret_cast<const float*>(k),
+                   reinterpret_cast<const float*>(v), n_rows));
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_t st) {
+  cache_set_len_kernel<<<1, 64, 0, st>>>(c.seq_lens, seq, len);
+  return hipGetLastError();
+}
+
+DecodePlan plan_decode(const CacheDims& c, int Hq) {
+  (void)Hq;
+  DecodePlan pl{};
+  const long long work = (long long)c.n_seqs * c.Hkv * c.max_pages;
+  long long pps = (work + 2047) / 2048;
+  if (pps < 8) pps = 8;
+  if (pps > 256) pps = 256;
+  pps = (pps + 3) / 4 * 4;
+  pl.pages_per_split = (int)pps;
+  pl.max_splits = (int)((c.max_pages + pps - 1) / pps);
+  pl.part_bytes = (size_t)c.n_seqs * Hq * pl.max_splits * (c.D + 2) * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
+                         const void* k_new, const void* v_new, int max_len_after, void* out,
+                         void* ws, hipStream_t st) {
+  (void)max_len_after;
+  if (k_new) {
+    CART_TIMED("decode_append", st,
+               decode_append_kernel<<<c.n_seqs, 256, 0, st>>>(
+                   c, reinterpret_cast<const bf16*>(k_new), reinterpret_cast<const bf16*>(v_new)));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const DecodePlan pl = plan_decode(c, Hq);
+  DecArgs a{};
+  a.c = c;
+  a.q = reinterpret_cast<const bf16*>(q);
+  a.out = reinterpret_cast<bf16*>(out);
+  a.part = reinterpret_cast<float*>(ws);
+  a.Hq = Hq;
+  a.g = Hq / c.Hkv;
+  a.pps = pl.pages_per_split;
+  a.max_splits = pl.max_splits;
+  a.scale_log2 = scale * kLog2e;
+  return c.D == 128 ? launch_dec_d<128>(a, st) : launch_dec_d<64>(a, st);
+}
+
+}  // namespace cartattn

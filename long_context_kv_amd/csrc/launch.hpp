@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI host layer (cartattn.cpp) and the
+// kernel translation units. Everything here runs on the host; argument
+// checking has already been done by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cartattn {
+
+struct AttnDims {
+  int B, n, p, f;       // batch, q_seq, cartridge rows, frozen rows
+  int Hq, Hkv, D;       // heads and head_dim
+  float scale;          // resolved softmax scale (never 0)
+  bool tok_bf16;        // token tensors are bf16 (else f32)
+  bool row_bf16;        // cartridge rows are bf16 (else f32)
+};
+
+// Forward launch plan; the workspace size and the launch both derive from it.
+struct FwdPlan {
+  int hpw, wph, n_hg, n_qb, n_splits, grid;
+  size_t o_part_bytes, lse_part_bytes;
+};
+FwdPlan plan_fwd(const AttnDims& a);
+size_t fwd_workspace_bytes(const AttnDims& a);
+hipError_t launch_fwd(const AttnDims& a, const void* q, const void* k_tok, const void* v_tok,
+                      const void* k_cart, const void* v_cart, void* out, float* lse,
+                      void* ws, hipStream_t st);
+
+struct BwdPlan {
+  int n_ct, n_tt, nqt, splits_c, grid_c, grid_t;
+  size_t dq_bytes, delta_bytes, part_bytes;
+};
+BwdPlan plan_bwd(const AttnDims& a);
+size_t bwd_workspace_bytes(const AttnDims& a);
+hipError_t launch_bwd(const AttnDims& a, const void* q, const void* k_tok, const void* v_tok,
+                      const void* k_cart, const void* v_cart, const void* out,
+                      const float* lse, const void* dout, void* dq, void* dk_tok,
+                      void* dv_tok, float* dk_cart, float* dv_cart, bool accumulate,
+                      void* ws, hipStream_t st);
+
+hipError_t launch_rope(void* q, void* k, bool bf16, int B, int S, int Hq, int Hkv, int D,
+                       int pos_base, const int32_t* pos_offsets, double theta, bool inverse,
+                       hipStream_t st);
+
+struct CacheDims {
+  int n_seqs, Hkv, D, page, max_pages, n_pages;
+  void* k_pages;
+  void* v_pages;
+  const int32_t* block_table;
+  int32_t* seq_lens;
+};
+// Append rows [n_rows, Hkv, D] (f32 or bf16) at row `start` of `seq` and set
+// the device seq_len of `seq` to start + n_rows.
+hipError_t launch_cache_append(const CacheDims& c, int seq, int start, const void* k,
+                               const void* v, bool src_bf16, int n_rows, hipStream_t st);
+hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_t st);
+
+struct DecodePlan {
+  int pages_per_split, max_splits;
+  size_t part_bytes;
+};
+DecodePlan plan_decode(const CacheDims& c, int Hq);
+hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
+                         const void* k_new, const void* v_new, int max_len_after,
+                         void* out, void* ws, hipStream_t st);
+
+}  // namespace cartattn

@@ -1,0 +1,101 @@
+// Per-kernel launch timing with HIP events recorded on the launching stream.
+//
+// Off by default. When enabled (cart_timing_enable), every kernel launch of
+// the library is bracketed by two events on its own stream; cart_timing_query
+// waits for the recorded events and sums the elapsed times of one kernel
+// name. Events are pooled and reused across enable cycles.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "cartattn.h"
+#include "timing.hpp"
+
+namespace cartattn {
+
+namespace {
+
+struct Record {
+  const char* name;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Record> g_records;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void recycle_all() {
+  for (auto& r : g_records) {
+    g_pool.push_back(r.start);
+    g_pool.push_back(r.stop);
+  }
+  g_records.clear();
+}
+
+}  // namespace
+
+int timing_start(const char* name, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return -1;
+  Record r{name, take_event(), take_event()};
+  if (!r.start || !r.stop) return -1;
+  if (hipEventRecord(r.start, st) != hipSuccess) return -1;
+  g_records.push_back(r);
+  return (int)g_records.size() - 1;
+}
+
+void timing_stop(int slot, hipStream_t st) {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (slot < (int)g_records.size()) hipEventRecord(g_records[slot].stop, st);
+}
+
+}  // namespace cartattn
+
+using namespace cartattn;
+
+extern "C" {
+
+int cart_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  for (auto& r : g_records) hipEventSynchronize(r.stop);
+  recycle_all();
+  g_on = on != 0;
+  return CART_OK;
+}
+
+int cart_timing_query(const char* kernel, double* total_ms, int32_t* launches) {
+  if (!kernel || !total_ms || !launches) return CART_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_mu);
+  double tot = 0.0;
+  int n = 0;
+  for (auto& r : g_records) {
+    if (strcmp(r.name, kernel) != 0) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return CART_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return CART_ERR_HIP;
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return CART_OK;
+}
+
+}  // extern "C"

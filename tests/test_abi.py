@@ -1,0 +1,194 @@
+"""Host-side tests of the libcartattn C ABI (no GPU needed).
+
+Every argument check runs on the host before any HIP call, so each call here
+is built to FAIL validation: no test passes a made-up pointer to a call that
+would launch a kernel.
+"""
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+from long_context_kv_amd import cartattn as C
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+L = C.lib()
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+MIS = 0x10004           # misaligned
+
+
+def _declared_functions():
+    src = (ROOT / "include" / "cartattn.h").read_text()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(cart_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(C.EXPORTS) == names
+
+
+def _shape(**kw):
+    base = dict(batch=1, q_seq=16, p=8, frozen_rows=1, n_q_heads=4, n_kv_heads=2,
+                head_dim=64, scale=0.0, tok_dtype=C.CART_BF16, row_dtype=C.CART_F32)
+    base.update(kw)
+    return C.AttnShape(**base)
+
+
+def _fwd(shape, q=FAKE, kt=FAKE, vt=FAKE, kc=FAKE, vc=FAKE, out=FAKE, lse=FAKE, ws=FAKE,
+         ws_bytes=1 << 30):
+    return L.cart_attn_fwd(ctypes.byref(shape), q, kt, vt, kc, vc, out, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), C.CART_ERR_INVALID_ARG),
+    (dict(q_seq=0), C.CART_ERR_INVALID_ARG),
+    (dict(p=-1), C.CART_ERR_INVALID_ARG),
+    (dict(frozen_rows=9), C.CART_ERR_INVALID_ARG),
+    (dict(frozen_rows=-1), C.CART_ERR_INVALID_ARG),
+    (dict(n_q_heads=5), C.CART_ERR_INVALID_ARG),
+    (dict(n_kv_heads=0), C.CART_ERR_INVALID_ARG),
+    (dict(head_dim=96), C.CART_ERR_UNSUPPORTED),
+    (dict(head_dim=256), C.CART_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), C.CART_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), C.CART_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), C.CART_ERR_INVALID_ARG),
+    (dict(tok_dtype=7), C.CART_ERR_INVALID_ARG),
+    (dict(tok_dtype=C.CART_F32, row_dtype=C.CART_BF16), C.CART_ERR_UNSUPPORTED),
+    (dict(batch=4096, q_seq=1 << 20, n_q_heads=64, n_kv_heads=8), C.CART_ERR_UNSUPPORTED),
+])
+def test_shape_validation(kw, status):
+    assert _fwd(_shape(**kw)) == status
+    assert L.cart_attn_workspace_size(ctypes.byref(_shape(**kw)), 0) == 0
+    assert L.cart_last_error()
+
+
+def test_fwd_pointer_checks():
+    s = _shape()
+    assert _fwd(s, q=None) == C.CART_ERR_INVALID_ARG
+    assert _fwd(s, q=MIS) == C.CART_ERR_ALIGNMENT
+    assert _fwd(s, kc=None) == C.CART_ERR_INVALID_ARG     # p > 0 needs the cartridge
+    assert _fwd(s, lse=None) == C.CART_ERR_INVALID_ARG
+    assert _fwd(s, out=MIS) == C.CART_ERR_ALIGNMENT
+    assert b"out" in L.cart_last_error()
+
+
+def test_workspace_checks():
+    # a shape small enough that the forward needs split partials
+    s = _shape(batch=1, q_seq=64, p=4096, n_q_heads=2, n_kv_heads=1, head_dim=128)
+    need = L.cart_attn_workspace_size(ctypes.byref(s), 0)
+    assert need > 0
+    assert _fwd(s, ws=None) == C.CART_ERR_WORKSPACE
+    assert _fwd(s, ws_bytes=need - 1) == C.CART_ERR_WORKSPACE
+    assert _fwd(s, ws=MIS, ws_bytes=need) == C.CART_ERR_ALIGNMENT
+    need_b = L.cart_attn_workspace_size(ctypes.byref(s), 1)
+    assert need_b >= 64 * 2 * 128 * 4      # at least the f32 dQ accumulator
+    r = L.cart_attn_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                        FAKE, FAKE, FAKE, FAKE, 0, FAKE, need_b - 256, None)
+    assert r == C.CART_ERR_WORKSPACE
+
+
+def test_bwd_pointer_checks():
+    s = _shape()
+    args = [FAKE] * 13
+    for i in range(13):
+        a = list(args)
+        a[i] = None
+        r = L.cart_attn_bwd(ctypes.byref(s), *a, 0, FAKE, 1 << 30, None)
+        assert r == C.CART_ERR_INVALID_ARG, i
+    # p = 0: cartridge pointers may be NULL, but frozen_rows must then be 0
+    s0 = _shape(p=0, frozen_rows=1)
+    assert _fwd(s0, kc=None, vc=None) == C.CART_ERR_INVALID_ARG
+
+
+def test_rope_validation():
+    f = L.cart_rope_tokens
+    assert f(FAKE, FAKE, 5, 1, 1, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, C.CART_BF16, 1, 1, 4, 2, 80, 0, None, 1e6, 0, None) == C.CART_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, C.CART_BF16, 1, 1, 4, 2, 64, 0, None, 0.0, 0, None) == C.CART_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, C.CART_BF16, 1, 1, 4, 2, 64, -1, None, 1e6, 0, None) == C.CART_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, C.CART_BF16, -1, 1, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_ERR_INVALID_ARG
+    assert f(None, FAKE, C.CART_BF16, 1, 1, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_ERR_INVALID_ARG
+    assert f(MIS, None, C.CART_BF16, 1, 1, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_ERR_ALIGNMENT
+    assert f(FAKE, MIS, C.CART_BF16, 1, 1, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_ERR_ALIGNMENT
+    assert f(FAKE, FAKE, C.CART_BF16, 1, 1, 4, 0, 64, 0, None, 1e6, 0, None) == C.CART_ERR_INVALID_ARG
+    assert f(FAKE, None, C.CART_BF16, 1, 1, 4, 2, 64, 0, FAKE + 2, 1e6, 0, None) == C.CART_ERR_ALIGNMENT
+    # empty input is a successful no-op (nothing is launched)
+    assert f(None, None, C.CART_BF16, 0, 5, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_OK
+    assert f(None, None, C.CART_BF16, 3, 0, 4, 2, 64, 0, None, 1e6, 0, None) == C.CART_OK
+
+
+def _desc(**kw):
+    base = dict(n_seqs=2, n_kv_heads=2, head_dim=64, page_size=16, max_pages_per_seq=4,
+                n_pages=8, dtype=C.CART_BF16, k_pages=FAKE, v_pages=FAKE, block_table=FAKE,
+                seq_lens=FAKE)
+    base.update(kw)
+    return C.CacheDesc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_seqs=0), C.CART_ERR_INVALID_ARG),
+    (dict(n_pages=0), C.CART_ERR_INVALID_ARG),
+    (dict(head_dim=100), C.CART_ERR_UNSUPPORTED),
+    (dict(page_size=32), C.CART_ERR_UNSUPPORTED),
+    (dict(dtype=C.CART_F32), C.CART_ERR_UNSUPPORTED),
+    (dict(k_pages=None), C.CART_ERR_INVALID_ARG),
+    (dict(v_pages=MIS), C.CART_ERR_ALIGNMENT),
+    (dict(block_table=None), C.CART_ERR_INVALID_ARG),
+    (dict(seq_lens=None), C.CART_ERR_INVALID_ARG),
+])
+def test_cache_create_validation(kw, status):
+    h = ctypes.c_void_p()
+    assert L.cart_cache_create(ctypes.byref(_desc(**kw)), ctypes.byref(h)) == status
+    assert not h.value
+
+
+def test_cache_host_rules():
+    h = ctypes.c_void_p()
+    assert L.cart_cache_create(ctypes.byref(_desc()), ctypes.byref(h)) == C.CART_OK
+    try:
+        assert L.cart_cache_seq_len(h, 0) == 0
+        assert L.cart_cache_seq_len(h, 2) == -1
+        # geometry locked to the cache
+        r = L.cart_write_cache(h, 0, FAKE, FAKE, C.CART_F32, 8, 4, 64, None)
+        assert r == C.CART_ERR_GEOMETRY
+        r = L.cart_write_cache(h, 0, FAKE, FAKE, C.CART_F32, 8, 2, 128, None)
+        assert r == C.CART_ERR_GEOMETRY
+        # capacity is 4 pages x 16 rows
+        r = L.cart_write_cache(h, 0, FAKE, FAKE, C.CART_F32, 65, 2, 64, None)
+        assert r == C.CART_ERR_CACHE_FULL
+        assert L.cart_append_cache(h, 1, FAKE, FAKE, C.CART_BF16, 100, 2, 64, None) == \
+            C.CART_ERR_CACHE_FULL
+        assert L.cart_write_cache(h, 5, FAKE, FAKE, C.CART_F32, 8, 2, 64, None) == \
+            C.CART_ERR_INVALID_ARG
+        assert L.cart_write_cache(h, 0, None, FAKE, C.CART_F32, 8, 2, 64, None) == \
+            C.CART_ERR_INVALID_ARG
+        assert L.cart_append_cache(h, 0, FAKE, FAKE, 9, 8, 2, 64, None) == C.CART_ERR_INVALID_ARG
+        # nothing stored yet: an attend-only decode has no rows to attend over
+        ws = L.cart_decode_workspace_size(h, 4)
+        assert ws > 0
+        assert L.cart_decode(h, FAKE, None, None, 4, 0.0, FAKE, FAKE, ws, None) == \
+            C.CART_ERR_INVALID_ARG
+        assert L.cart_decode(h, FAKE, FAKE, None, 4, 0.0, FAKE, FAKE, ws, None) == \
+            C.CART_ERR_INVALID_ARG
+        assert L.cart_decode(h, FAKE, None, None, 3, 0.0, FAKE, FAKE, ws, None) == \
+            C.CART_ERR_GEOMETRY
+        assert L.cart_decode(h, FAKE, None, None, 32, 0.0, FAKE, FAKE, ws, None) == \
+            C.CART_ERR_UNSUPPORTED
+        assert L.cart_decode(h, None, FAKE, FAKE, 4, 0.0, FAKE, FAKE, ws, None) == \
+            C.CART_ERR_INVALID_ARG
+        assert L.cart_decode_workspace_size(h, 3) == 0
+        assert L.cart_decode_workspace_size(None, 4) == 0
+    finally:
+        L.cart_cache_destroy(h)
+
+
+def test_status_strings():
+    for s in range(9):
+        assert L.cart_status_string(s)
+    assert L.cart_status_string(99) == b"unknown status"
