@@ -97,7 +97,7 @@ def train_bench(C, W, shape, steps, warmup):
     C.timing_enable(True)
     total_ms = _events_ms(step, steps)
     kern = {}
-    for name in ("rope", "attn_fwd", "attn_fwd_combine", "bwd_preprocess", "attn_bwd",
+    for name in ("rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess", "attn_bwd",
                  "bwd_dq_finalize", "bwd_cart_reduce"):
         ms, cnt = C.timing_query(name)
         if cnt:

@@ -380,6 +380,293 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel: same decomposition and arithmetic as attn_bwd_kernel, with
+//  * the workgroup's K tile staged row-major in LDS once; the dQ contraction
+//    reads it with LDS transpose reads (tr_col4), so no K^T copy exists;
+//  * Q and dO tiles row-major and double-buffered; the next unit is
+//    prefetched into registers while the current one is multiplied; dO^T and
+//    Q^T operands of dV += P^T dO and dK += dS^T Q are transpose reads;
+//  * dS^T written as [key][query] with 8-byte stores straight from the MFMA
+//    result layout; dQ = dS K reads it back with transpose reads.
+// Cartridge rows arrive as bf16 (f32 master rows are cast first).
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
+  using M = Mfma<bf16>;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int KSTR = D + 16;       // K tile (transpose reads)
+  constexpr int RSTR = D + 8;        // Q, dO tiles (16-byte row reads)
+  constexpr int SSTR = kBQ + 16;     // dS^T [key][query]
+  constexpr int CPR = D / 8;
+  constexpr int NCH = kBQ * CPR / kThreads;
+  __shared__ __align__(16) bf16 Ks[kBNB * KSTR];
+  __shared__ __align__(16) bf16 Qs[2][kBQ * RSTR];
+  __shared__ __align__(16) bf16 Os[2][kBQ * RSTR];
+  __shared__ __align__(16) bf16 St[kBNB * SSTR];
+  __shared__ __align__(16) float lse2s[2][kBQ];
+  __shared__ __align__(16) float dls[2][kBQ];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int c0base = 16 * ((lane >> 4) & 1);
+
+  const int per_kv = a.n_ct * a.splits_c + a.B * a.n_tt;
+  const int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int kv = lg / per_kv;
+  int r0 = lg % per_kv;
+  const bool cart = r0 < a.n_ct * a.splits_c;
+  int tile, split = 0, b = 0, u_begin, u_end;
+  if (cart) {
+    tile = r0 / a.splits_c;
+    split = r0 % a.splits_c;
+    const int U = a.B * a.g * a.nqt;
+    u_begin = (int)((long long)split * U / a.splits_c);
+    u_end = (int)((long long)(split + 1) * U / a.splits_c);
+  } else {
+    r0 -= a.n_ct * a.splits_c;
+    b = r0 / a.n_tt;
+    tile = r0 % a.n_tt;
+    u_begin = 0;
+    u_end = a.g * (a.nqt - tile * (kBNB / kBQ));
+  }
+  const int j0 = tile * kBNB;
+  const int limit = cart ? a.p : a.n;
+  const int my_key = j0 + 32 * wave + l32;
+  const bool key_ok = my_key < limit;
+  const size_t row_stride = (size_t)a.Hkv * D;
+  const bf16* kbase = cart ? reinterpret_cast<const bf16*>(a.k_cart) + kv * D
+                           : reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+  const bf16* vbase = cart ? reinterpret_cast<const bf16*>(a.v_cart) + kv * D
+                           : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+
+  // K, V rows of this lane's key as B operands; the tile's K rows into LDS.
+  bf16x8 kf[NKS], vf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (key_ok) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)my_key * row_stride + 16 * ks + 8 * hl);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)my_key * row_stride + 16 * ks + 8 * hl);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kf[ks][e] = (bf16)0.f; vf[ks][e] = (bf16)0.f; }
+    }
+  }
+  {
+    constexpr int NK = kBNB * CPR / kThreads;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int c = tid + u * kThreads;
+      const int r = c / CPR;
+      const int col = (c % CPR) * 8;
+      bf16x8 v8;
+      if (j0 + r < limit) {
+        v8 = *reinterpret_cast<const bf16x8*>(kbase + (size_t)(j0 + r) * row_stride + col);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = (bf16)0.f;
+      }
+      *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + col]) = v8;
+    }
+  }
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+
+  auto unit_of = [&](int u, int& bb, int& h, int& i0) {
+    int hin, qt;
+    if (cart) {
+      bb = u / (a.g * a.nqt);
+      hin = (u / a.nqt) % a.g;
+      qt = u % a.nqt;
+    } else {
+      const int span = a.nqt - tile * (kBNB / kBQ);
+      bb = b;
+      hin = u / span;
+      qt = tile * (kBNB / kBQ) + u % span;
+    }
+    h = kv * a.g + hin;
+    i0 = qt * kBQ;
+  };
+
+  bf16x8 pq[NCH], po[NCH];
+  float pl2 = 0.f, pdl = 0.f;
+  auto load_unit = [&](int u) {
+    int bb, h, i0;
+    unit_of(u, bb, h, i0);
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int c = tid + ch * kThreads;
+      const int r = c / CPR;
+      const int col = (c % CPR) * 8;
+      const int i = i0 + r;
+      if (i < a.n) {
+        const size_t off = (((size_t)bb * a.n + i) * a.Hq + h) * D + col;
+        pq[ch] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.q) + off);
+        po[ch] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + off);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pq[ch][e] = (bf16)0.f; po[ch][e] = (bf16)0.f; }
+      }
+    }
+    if (tid < kBQ) {
+      const int i = i0 + tid;
+      const size_t li = ((size_t)bb * a.Hq + h) * a.n + i;
+      pl2 = (i < a.n) ? a.lse[li] * kLog2e : INFINITY;
+      pdl = (i < a.n) ? a.delta[li] : 0.f;
+    }
+  };
+  auto store_unit = [&](int buf) {
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int c = tid + ch * kThreads;
+      const int r = c / CPR;
+      const int col = (c % CPR) * 8;
+      *reinterpret_cast<bf16x8*>(&Qs[buf][r * RSTR + col]) = pq[ch];
+      *reinterpret_cast<bf16x8*>(&Os[buf][r * RSTR + col]) = po[ch];
+    }
+    if (tid < kBQ) {
+      lse2s[buf][tid] = pl2;
+      dls[buf][tid] = pdl;
+    }
+  };
+
+  constexpr int NKP = 4 / NDB;
+  const int q_db = wave % NDB;
+  const int kbeg = (wave / NDB) * (kBNB / NKP);
+  constexpr int KP_STEPS = (kBNB / NKP) / 16;
+  const float c = a.scale_log2;
+
+  if (u_begin < u_end) {
+    load_unit(u_begin);
+    store_unit(0);
+  }
+  __syncthreads();
+  for (int u = u_begin; u < u_end; ++u) {
+    const int cur = (u - u_begin) & 1;
+    const bool more = u + 1 < u_end;
+    int bb, h, i0;
+    unit_of(u, bb, h, i0);
+    if (more) load_unit(u + 1);
+
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    {
+      const bf16* qrow = &Qs[cur][l32 * RSTR + 8 * hl];
+      const bf16* orow = &Os[cur][l32 * RSTR + 8 * hl];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = M::mma(*reinterpret_cast<const bf16x8*>(qrow + 16 * ks), kf[ks], s);
+        dp = M::mma(*reinterpret_cast<const bf16x8*>(orow + 16 * ks), vf[ks], dp);
+      }
+    }
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&lse2s[cur][8 * c4 + 4 * hl]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&dls[cur][8 * c4 + 4 * hl]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * c4 + e;
+        const int i = i0 + 8 * c4 + 4 * hl + e;
+        const bool vis = key_ok && (cart || my_key <= i);
+        const float pv_ = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[e])) : 0.f;
+        s[r] = pv_;
+        dp[r] = pv_ * (dp[r] - dvv[e]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 pf = pack_regs<bf16>(s, m);
+      const bf16x8 sf = pack_regs<bf16>(dp, m);
+      const int q0 = 16 * m + 4 * hl;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int c0 = 32 * db + c0base;
+        const bf16x8 ob = cat8(tr_col4(Os[cur], RSTR, q0, c0, lane),
+                               tr_col4(Os[cur], RSTR, q0 + 8, c0, lane));
+        const bf16x8 qb = cat8(tr_col4(Qs[cur], RSTR, q0, c0, lane),
+                               tr_col4(Qs[cur], RSTR, q0 + 8, c0, lane));
+        dv[db] = M::mma(pf, ob, dv[db]);
+        dk[db] = M::mma(sf, qb, dk[db]);
+      }
+    }
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      bf16x4 v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = (bf16)dp[4 * c4 + e];
+      *reinterpret_cast<bf16x4*>(&St[(32 * wave + l32) * SSTR + 8 * c4 + 4 * hl]) = v4;
+    }
+    __syncthreads();
+
+    {
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KP_STEPS; ++ks) {
+        const int k0 = kbeg + 16 * ks + 8 * hl;
+        const bf16x8 sa = cat8(tr_col4(St, SSTR, k0, c0base, lane),
+                               tr_col4(St, SSTR, k0 + 4, c0base, lane));
+        const bf16x8 kb = cat8(tr_col4(Ks, KSTR, k0, 32 * q_db + c0base, lane),
+                               tr_col4(Ks, KSTR, k0 + 4, 32 * q_db + c0base, lane));
+        acc = M::mma(sa, kb, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + d_row(r, hl);
+        if (i < a.n)
+          atomicAdd(a.dq_acc + (((size_t)bb * a.n + i) * a.Hq + h) * D + 32 * q_db + l32,
+                    acc[r] * a.scale);
+      }
+    }
+    if (more) store_unit(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int j = j0 + 32 * wave + d_row(r, hl);
+    if (j >= limit) continue;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 32 * db + l32;
+      const float gk = dk[db][r] * a.scale;
+      const float gv = dv[db][r];
+      if (cart) {
+        const size_t o = ((size_t)j * a.Hkv + kv) * D + col;
+        if (a.splits_c > 1) {
+          const size_t po_ = (size_t)split * a.p * row_stride + o;
+          a.dk_part[po_] = gk;
+          a.dv_part[po_] = gv;
+        } else if (j < a.f) {
+          a.dk_cart[o] = 0.f;
+          a.dv_cart[o] = 0.f;
+        } else if (a.accumulate) {
+          a.dk_cart[o] += gk;
+          a.dv_cart[o] += gv;
+        } else {
+          a.dk_cart[o] = gk;
+          a.dv_cart[o] = gv;
+        }
+      } else {
+        const size_t o = (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
+        reinterpret_cast<bf16*>(a.dk_tok)[o] = (bf16)gk;
+        reinterpret_cast<bf16*>(a.dv_tok)[o] = (bf16)gv;
+      }
+    }
+  }
+}
+
 // D_i = dO_i . O_i for every (b, h, i), and dQ accumulator := 0.
 // One wave per (b, i, h) row; 4 rows per workgroup.
 template <typename T, int D>
@@ -466,22 +753,24 @@ BwdPlan plan_bwd(const AttnDims& d) {
   pl.dq_bytes = (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
   pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);
   pl.part_bytes = s > 1 ? (size_t)s * d.p * d.Hkv * d.D * sizeof(float) : 0;
+  if (d.tok_bf16 && !d.row_bf16 && d.p > 0)
+    pl.shadow_bytes = 2 * (size_t)d.p * d.Hkv * d.D * sizeof(uint16_t);
   return pl;
 }
 
 size_t bwd_workspace_bytes(const AttnDims& d) {
   const BwdPlan pl = plan_bwd(d);
-  return align256(pl.dq_bytes) + align256(pl.delta_bytes) + 2 * align256(pl.part_bytes);
+  return align256(pl.shadow_bytes) + align256(pl.dq_bytes) + align256(pl.delta_bytes) +
+         2 * align256(pl.part_bytes);
 }
 
-template <typename T, typename TR, int D>
-static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
+template <typename T, int D, typename Main>
+static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t st, Main main) {
   const int rows = a.B * a.n * a.Hq;
   CART_TIMED("bwd_preprocess", st, bwd_preprocess<T, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_TIMED("attn_bwd", st,
-             attn_bwd_kernel<T, TR, D><<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
+  CART_TIMED("attn_bwd", st, main<<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t n4 = (size_t)rows * D / 4;
   CART_TIMED("bwd_dq_finalize", st,
@@ -504,9 +793,20 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
                       void* ws, hipStream_t st) {
   const BwdPlan pl = plan_bwd(d);
   BwdArgs a{};
+  char* w = reinterpret_cast<char*>(ws);
+  if (pl.shadow_bytes) {
+    const size_t n = (size_t)d.p * d.Hkv * d.D;
+    bf16* kb = reinterpret_cast<bf16*>(w);
+    bf16* vb = kb + n;
+    hipError_t e = launch_rows_to_bf16(reinterpret_cast<const float*>(k_cart),
+                                       reinterpret_cast<const float*>(v_cart), kb, vb, n, st);
+    if (e != hipSuccess) return e;
+    k_cart = kb;
+    v_cart = vb;
+    w += align256(pl.shadow_bytes);
+  }
   a.q = q; a.k_tok = k_tok; a.v_tok = v_tok; a.k_cart = k_cart; a.v_cart = v_cart;
   a.out = out; a.dout = dout; a.lse = lse;
-  char* w = reinterpret_cast<char*>(ws);
   a.dq_acc = reinterpret_cast<float*>(w);
   w += align256(pl.dq_bytes);
   a.delta = reinterpret_cast<float*>(w);
@@ -520,15 +820,11 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.accumulate = accumulate ? 1 : 0;
   a.scale = d.scale;
   a.scale_log2 = d.scale * kLog2e;
-  if (d.tok_bf16) {
-    if (d.D == 128)
-      return d.row_bf16 ? launch_bwd_t<bf16, bf16, 128>(a, pl, st)
-                        : launch_bwd_t<bf16, float, 128>(a, pl, st);
-    return d.row_bf16 ? launch_bwd_t<bf16, bf16, 64>(a, pl, st)
-                      : launch_bwd_t<bf16, float, 64>(a, pl, st);
-  }
-  if (d.D == 128) return launch_bwd_t<float, float, 128>(a, pl, st);
-  return launch_bwd_t<float, float, 64>(a, pl, st);
+  if (d.tok_bf16)
+    return d.D == 128 ? launch_bwd_t<bf16, 128>(a, pl, st, attn_bwd_bf16_kernel<128>)
+                      : launch_bwd_t<bf16, 64>(a, pl, st, attn_bwd_bf16_kernel<64>);
+  return d.D == 128 ? launch_bwd_t<float, 128>(a, pl, st, attn_bwd_kernel<float, float, 128>)
+                    : launch_bwd_t<float, 64>(a, pl, st, attn_bwd_kernel<float, float, 64>);
 }
 
 }  // namespace cartattn

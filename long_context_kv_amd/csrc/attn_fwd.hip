@@ -284,6 +284,234 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel. Same work decomposition and softmax as attn_fwd_kernel, with:
+//  * K and V tiles copied global -> LDS by direct (VGPR-free) loads into a
+//    swizzled, double-buffered layout: the copy of tile t+1 runs while tile t
+//    is multiplied, and the loop has one barrier per tile;
+//  * the V^T operand of O^T += V^T P^T read with LDS transpose reads, so no
+//    transposed copy of V is ever written;
+//  * the running max is taken on raw scores and each probability costs one
+//    FMA and one exp2; the O accumulator is rescaled only when some query's
+//    max has grown by more than 2^8 since its last rescale (exact: the
+//    probabilities are then at most 256, well inside f32 and bf16 range).
+// Cartridge rows arrive as bf16 (f32 master rows are cast first).
+template <int D>
+struct FwdTile {
+  int j0, rows;
+  bool cart;
+};
+
+template <int D>
+__device__ __forceinline__ FwdTile<D> fwd_tile(int t, int n_ct, int p, int n) {
+  FwdTile<D> f;
+  f.cart = t < n_ct;
+  f.j0 = f.cart ? t * kBN : (t - n_ct) * kBN;
+  f.rows = f.cart ? min(kBN, p - f.j0) : min(kBN, n - f.j0);
+  return f;
+}
+
+template <int D>
+__device__ __forceinline__ void fwd_issue(bf16* Kst, bf16* Vst, int t, int n_ct, const FwdArgs& a,
+                                          int kv, const bf16* kt, const bf16* vt, int wave,
+                                          int lane) {
+  const FwdTile<D> f = fwd_tile<D>(t, n_ct, a.p, a.n);
+  const size_t row_stride = (size_t)a.Hkv * D;
+  const bf16* kb = f.cart ? reinterpret_cast<const bf16*>(a.k_cart) + ((size_t)f.j0 * a.Hkv + kv) * D
+                          : kt + (size_t)f.j0 * row_stride;
+  const bf16* vb = f.cart ? reinterpret_cast<const bf16*>(a.v_cart) + ((size_t)f.j0 * a.Hkv + kv) * D
+                          : vt + (size_t)f.j0 * row_stride;
+  dma_tile<D, kBN>(Kst, kb, row_stride, f.rows, wave, lane);
+  dma_tile<D, kBN>(Vst, vb, row_stride, f.rows, wave, lane);
+}
+
+// One key tile of the online softmax for one wave (32 queries x 64 keys).
+template <int D>
+__device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, const FwdTile<D>& f,
+                                            const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
+                                            float& m_ref, float& l_run, float c, int i0,
+                                            int my_i, int lane) {
+  using M = Mfma<bf16>;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  f32x16 s[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    bf16x8 kfr[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + sw_off<D>(32 * kh + l32, 16 * ks + 8 * hl));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s[kh] = M::mma(kfr[ks], qf[ks], s[kh]);
+  }
+  if (f.rows < kBN || (!f.cart && f.j0 + kBN - 1 > i0)) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kh + d_row(r, hl);
+        const bool vis = key < f.rows && (f.cart || f.j0 + key <= my_i);
+        s[kh][r] = vis ? s[kh][r] : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kh][r]);
+  const float mxs = wave_max_halves(mx) * c;
+  const bool grow = mxs > m_ref + 8.f;
+  if (__any(grow)) {
+    const float m_new = grow ? mxs : m_ref;
+    const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    m_ref = m_new;
+  }
+  const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float ls = 0.f;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv_ = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c, -m_use));
+      s[kh][r] = pv_;
+      ls += pv_;
+    }
+  l_run += ls;
+  const int c0base = 16 * ((lane >> 4) & 1);
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 pf = pack_regs<bf16>(s[kh], m);
+      const int r0 = 32 * kh + 16 * m + 4 * hl;
+      bf16x8 va[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        va[db] = cat8(tr_col4_sw<D>(Vs, r0, 32 * db + c0base, lane),
+                      tr_col4_sw<D>(Vs, r0 + 8, 32 * db + c0base, lane));
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = M::mma(va[db], pf, acc[db]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __align__(16) bf16 K0[kBN * D];
+  __shared__ __align__(16) bf16 V0[kBN * D];
+  __shared__ __align__(16) bf16 K1[kBN * D];
+  __shared__ __align__(16) bf16 V1[kBN * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lg % a.n_splits; lg /= a.n_splits;
+  const int qb = a.n_qb - 1 - (lg % a.n_qb); lg /= a.n_qb;
+  const int hg = lg % a.n_hg; lg /= a.n_hg;
+  const int b = lg % a.B; lg /= a.B;
+  const int kv = lg;
+
+  const int hw = wave % a.hpw;
+  const int pb = wave / a.hpw;
+  const int h = kv * a.g + hg * a.hpw + hw;
+  const int i0 = (qb * a.wph + pb) * 32;
+  const bool wave_active = i0 < a.n;
+  const int my_i = i0 + l32;
+
+  const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
+  const int n_ct = (a.p + kBN - 1) / kBN;
+  const int nt = n_ct + wg_last / kBN + 1;
+  const int t_begin = (int)((long long)split * nt / a.n_splits);
+  const int t_end = (int)((long long)(split + 1) * nt / a.n_splits);
+
+  const bf16* kt = reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+  const bf16* vt = reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+  if (t_begin < t_end) fwd_issue<D>(K0, V0, t_begin, n_ct, a, kv, kt, vt, wave, lane);
+
+  bf16x8 qf[NKS];
+  {
+    const int qi = min(my_i, a.n - 1);
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + (((size_t)b * a.n + qi) * a.Hq + h) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + hl * 8);
+  }
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_ref = -INFINITY;   // scaled (log2-domain) reference max of this query
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+
+  // Two tiles per trip, stage 0 then stage 1, so every LDS address is static.
+  for (int t = t_begin; t < t_end; t += 2) {
+    CART_WAIT_VMCNT(0);
+    lds_barrier();
+    if (t + 1 < t_end) fwd_issue<D>(K1, V1, t + 1, n_ct, a, kv, kt, vt, wave, lane);
+    {
+      const FwdTile<D> f = fwd_tile<D>(t, n_ct, a.p, a.n);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31))
+        fwd_compute<D>(K0, V0, f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
+    }
+    if (t + 1 >= t_end) break;
+    CART_WAIT_VMCNT(0);
+    lds_barrier();
+    if (t + 2 < t_end) fwd_issue<D>(K0, V0, t + 2, n_ct, a, kv, kt, vt, wave, lane);
+    {
+      const FwdTile<D> f = fwd_tile<D>(t + 1, n_ct, a.p, a.n);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31))
+        fwd_compute<D>(K1, V1, f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
+    }
+  }
+
+  if (!wave_active || my_i >= a.n) return;
+  l_run = wave_sum_halves(l_run);
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
+  if (a.n_splits == 1) {
+    bf16* op = reinterpret_cast<bf16*>(a.out) + (((size_t)b * a.n + my_i) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (bf16)(acc[db][4 * cc + e] * inv_l);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * cc + 4 * hl) = o4;
+      }
+    if (hl == 0) a.lse[((size_t)b * a.Hq + h) * a.n + my_i] = lse;
+  } else {
+    float* op = a.o_part + ((((size_t)split * a.B + b) * a.n + my_i) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        float4 v4 = make_float4(acc[db][4 * cc] * inv_l, acc[db][4 * cc + 1] * inv_l,
+                                acc[db][4 * cc + 2] * inv_l, acc[db][4 * cc + 3] * inv_l);
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * cc + 4 * hl) = v4;
+      }
+    if (hl == 0)
+      a.lse_part[(((size_t)split * a.B + b) * a.Hq + h) * a.n + my_i] = lse;
+  }
+}
+
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
 // One thread per (b, i, h) row, D/4 float4 lanes... kept simple: one wave per row.
 template <typename T, int D>
@@ -331,6 +559,8 @@ FwdPlan plan_fwd(const AttnDims& d) {
   while (base * splits < 512 && (splits * 2) * 4 <= min_tiles) splits *= 2;
   pl.n_splits = splits;
   pl.grid = (int)(base * splits);
+  if (d.tok_bf16 && !d.row_bf16 && d.p > 0)
+    pl.shadow_bytes = 2 * (size_t)d.p * d.Hkv * d.D * sizeof(uint16_t);
   if (splits > 1) {
     pl.o_part_bytes = (size_t)splits * d.B * d.n * d.Hq * d.D * sizeof(float);
     pl.lse_part_bytes = (size_t)splits * d.B * d.Hq * d.n * sizeof(float);
@@ -342,7 +572,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t fwd_workspace_bytes(const AttnDims& d) {
   const FwdPlan pl = plan_fwd(d);
-  return align256(pl.o_part_bytes) + align256(pl.lse_part_bytes);
+  return align256(pl.shadow_bytes) + align256(pl.o_part_bytes) + align256(pl.lse_part_bytes);
 }
 
 template <typename T, typename TR, int D>
@@ -354,25 +584,43 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const FwdPlan& pl, hipStream_t 
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdPlan& pl, hipStream_t st) {
+  CART_TIMED("attn_fwd", st, attn_fwd_bf16_kernel<D><<<pl.grid, kThreads, 0, st>>>(a));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.n_splits == 1) return e;
+  CART_TIMED("attn_fwd_combine", st,
+             attn_fwd_combine<bf16, D><<<a.B * a.n * a.Hq, 64, 0, st>>>(a));
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const AttnDims& d, const void* q, const void* k_tok, const void* v_tok,
                       const void* k_cart, const void* v_cart, void* out, float* lse,
                       void* ws, hipStream_t st) {
   const FwdPlan pl = plan_fwd(d);
   FwdArgs a{};
+  char* w = reinterpret_cast<char*>(ws);
+  if (pl.shadow_bytes) {
+    // bf16 shadow of the f32 cartridge rows
+    const size_t n = (size_t)d.p * d.Hkv * d.D;
+    bf16* kb = reinterpret_cast<bf16*>(w);
+    bf16* vb = kb + n;
+    hipError_t e = launch_rows_to_bf16(reinterpret_cast<const float*>(k_cart),
+                                       reinterpret_cast<const float*>(v_cart), kb, vb, n, st);
+    if (e != hipSuccess) return e;
+    k_cart = kb;
+    v_cart = vb;
+    w += align256(pl.shadow_bytes);
+  }
   a.q = q; a.k_tok = k_tok; a.v_tok = v_tok; a.k_cart = k_cart; a.v_cart = v_cart;
   a.out = out; a.lse = lse;
-  a.o_part = reinterpret_cast<float*>(ws);
-  a.lse_part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + align256(pl.o_part_bytes));
+  a.o_part = reinterpret_cast<float*>(w);
+  a.lse_part = reinterpret_cast<float*>(w + align256(pl.o_part_bytes));
   a.B = d.B; a.n = d.n; a.p = d.p; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
   a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb; a.n_splits = pl.n_splits;
   a.scale_log2 = d.scale * kLog2e;
-  if (d.tok_bf16) {
-    if (d.D == 128)
-      return d.row_bf16 ? launch_fwd_t<bf16, bf16, 128>(a, pl, st)
-                        : launch_fwd_t<bf16, float, 128>(a, pl, st);
-    return d.row_bf16 ? launch_fwd_t<bf16, bf16, 64>(a, pl, st)
-                      : launch_fwd_t<bf16, float, 64>(a, pl, st);
-  }
+  if (d.tok_bf16)
+    return d.D == 128 ? launch_fwd_bf16<128>(a, pl, st) : launch_fwd_bf16<64>(a, pl, st);
   if (d.D == 128) return launch_fwd_t<float, float, 128>(a, pl, st);
   return launch_fwd_t<float, float, 64>(a, pl, st);
 }

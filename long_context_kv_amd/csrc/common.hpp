@@ -140,3 +140,97 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
 }
 
 }  // namespace cartattn
+
+namespace cartattn {
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16). Measured lane mapping:
+// inside each group of 16 lanes, lane j receives, as item t (t = 0..3),
+// element (j % 4) of the 8-byte word addressed by lane (j / 4 + 4 t) of the
+// group. tr_col4 therefore has lane s of a group address
+// M[r0 + s/4][c0 + 4*(s%4)], so that lane j of the group ends up with the
+// column strip M[r0 + t][c0 + j], t = 0..3, of a row-major tile M.
+typedef short tr_v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 tr_col4(const bf16* tile, int stride, int r0, int c0,
+                                          int lane) {
+  const int s = lane & 15;
+  const bf16* p = tile + (r0 + (s >> 2)) * stride + c0 + 4 * (s & 3);
+  const tr_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4i16*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+}  // namespace cartattn
+
+namespace cartattn {
+
+// ---- LDS tiles for the bf16 kernels -------------------------------------
+// A tile of R rows x D bf16 is stored unpadded (row = 2*D bytes). Inside a
+// row, 16-byte chunk c lives at chunk position c ^ swz(r). The XOR spreads
+// the rows of a 16-byte row read (lanes = rows) and of a transpose read
+// (4 rows x 32 bytes per 16-lane group) over all LDS banks, and keeps every
+// wave's 1 KiB of a direct global->LDS load contiguous.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int r) {
+  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (r >> 1) & 7;
+}
+
+// Element offset of (row r, column col) in a swizzled tile.
+template <int D>
+__device__ __forceinline__ int sw_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
+}
+
+// Transpose read (see tr_col4) from a swizzled tile: lane j of each 16-lane
+// group receives rows r0..r0+3 of column c0 + j (c0 a multiple of 16).
+template <int D>
+__device__ __forceinline__ bf16x4 tr_col4_sw(const bf16* tile, int r0, int c0, int lane) {
+  const int s = lane & 15;
+  const bf16* p = tile + sw_off<D>(r0 + (s >> 2), c0 + 4 * (s & 3));
+  const tr_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) tr_v4i16*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+// Issue this wave's share of an asynchronous global->LDS copy of a tile of
+// NROWS rows x D bf16 (global rows `row_stride` elements apart) into a
+// swizzled LDS tile. The 4 waves of the workgroup each issue NROWS*D/2048
+// dwordx4 loads; lane l of one load lands at byte 16*l of that load's 1 KiB
+// LDS block. Rows at or past `rows` re-read row rows-1 (finite data that the
+// caller masks), so no address leaves the source.
+template <int D, int NROWS>
+__device__ __forceinline__ void dma_tile(bf16* lds, const bf16* src, size_t row_stride, int rows,
+                                         int wave, int lane) {
+  constexpr int PER_WAVE = NROWS * D / 512 / 4;   // 1 KiB loads per wave
+#pragma unroll
+  for (int k = 0; k < PER_WAVE; ++k) {
+    const int blk = wave * PER_WAVE + k;
+    const int off = blk * 512 + lane * 8;          // element offset of this lane's chunk
+    const int r = off / D;
+    const int c = ((off % D) >> 3) ^ swz<D>(r);
+    const int rr = r < rows ? r : rows - 1;
+    const bf16* g = src + (size_t)rr * row_stride + c * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)g, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+  }
+}
+
+// Workgroup barrier that orders LDS only: outstanding global stores and
+// atomics of the wave are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait until at most n of this wave's vector memory operations are pending
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14).
+#define CART_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt((((n) & 15) | ((((n) >> 4) & 3) << 14)) | 0x0F70)
+
+}  // namespace cartattn

@@ -20,7 +20,7 @@ struct AttnDims {
 // Forward launch plan; the workspace size and the launch both derive from it.
 struct FwdPlan {
   int hpw, wph, n_hg, n_qb, n_splits, grid;
-  size_t o_part_bytes, lse_part_bytes;
+  size_t shadow_bytes, o_part_bytes, lse_part_bytes;
 };
 FwdPlan plan_fwd(const AttnDims& a);
 size_t fwd_workspace_bytes(const AttnDims& a);
@@ -30,7 +30,7 @@ hipError_t launch_fwd(const AttnDims& a, const void* q, const void* k_tok, const
 
 struct BwdPlan {
   int n_ct, n_tt, nqt, splits_c, grid_c, grid_t;
-  size_t dq_bytes, delta_bytes, part_bytes;
+  size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes;
 };
 BwdPlan plan_bwd(const AttnDims& a);
 size_t bwd_workspace_bytes(const AttnDims& a);
@@ -39,6 +39,10 @@ hipError_t launch_bwd(const AttnDims& a, const void* q, const void* k_tok, const
                       const float* lse, const void* dout, void* dq, void* dk_tok,
                       void* dv_tok, float* dk_cart, float* dv_cart, bool accumulate,
                       void* ws, hipStream_t st);
+
+// f32 cartridge rows -> bf16 shadow (n elements per tensor, n % 4 == 0).
+hipError_t launch_rows_to_bf16(const float* k, const float* v, __bf16* kb, __bf16* vb, size_t n,
+                               hipStream_t st);
 
 hipError_t launch_rope(void* q, void* k, bool bf16, int B, int S, int Hq, int Hkv, int D,
                        int pos_base, const int32_t* pos_offsets, double theta, bool inverse,
