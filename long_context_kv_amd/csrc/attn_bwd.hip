@@ -28,6 +28,8 @@
 //    (where its dQ accumulator lines are hit by every tile).
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -49,6 +51,7 @@ struct BwdArgs {
   const void* out;
   const void* dout;
   const float* lse;
+  float* lse2;        // [B][Hq][n]: lse * log2(e), written by the preprocess
   float* delta;       // [B][Hq][n]
   float* dq_acc;      // [B][n][Hq][D]
   void* dq;           // tok dtype
@@ -381,31 +384,53 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: same decomposition and arithmetic as attn_bwd_kernel, with
-//  * the workgroup's K tile staged row-major in LDS once; the dQ contraction
-//    reads it with LDS transpose reads (tr_col4), so no K^T copy exists;
-//  * Q and dO tiles row-major and double-buffered; the next unit is
-//    prefetched into registers while the current one is multiplied; dO^T and
-//    Q^T operands of dV += P^T dO and dK += dS^T Q are transpose reads;
-//  * dS^T written as [key][query] with 8-byte stores straight from the MFMA
-//    result layout; dQ = dS K reads it back with transpose reads.
+// bf16 kernel: same decomposition and arithmetic as attn_bwd_kernel, built
+// for one wave per SIMD with little work besides the MFMAs:
+//  * the workgroup's K tile and each unit's Q, dO, LSE*log2(e) and D rows are
+//    copied global -> LDS by direct (VGPR-free) loads into padded tiles; the
+//    copy for unit u+1 is issued first thing in the step of unit u;
+//  * every transposed operand (dO^T and Q^T for dV += P^T dO, dK += dS^T Q;
+//    dS and K for dQ = dS K) is read with LDS transpose reads from row-major
+//    tiles; dS^T is written with 8-byte stores from the MFMA result layout;
+//  * software pipeline over units: the step of unit u also computes dQ of
+//    unit u-1 from the other dS^T buffer, interleaved with its own S and dP
+//    MFMAs, so there is one barrier per unit and it orders LDS only;
+//  * dQ goes to the f32 accumulator with buffer atomics whose resource ends
+//    at the unit's last query row, so rows past the end are dropped by the
+//    hardware range check; the softmax scale is folded into dS once;
+//  * per-lane copy offsets are computed once, units advance by counters, and
+//    the mask is evaluated only on diagonal or ragged units.
 // Cartridge rows arrive as bf16 (f32 master rows are cast first).
+
+// dS^T tile [key][query]: 128 x 32 bf16 with rows padded to 48 elements.
+constexpr int kSSTR = kBQ + 16;
+
+// True when no pair of this unit needs a mask for the key side: every key
+// of the workgroup tile exists and (for a token tile) every key precedes
+// every query of the unit.
+__device__ __forceinline__ bool key_ok_all(bool cart, int j0, int i0, int limit) {
+  const bool all_exist = j0 + kBNB <= limit;
+  return all_exist && (cart || j0 + kBNB - 1 <= i0);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int KSTR = D + 16;       // K tile (transpose reads)
-  constexpr int RSTR = D + 8;        // Q, dO tiles (16-byte row reads)
-  constexpr int SSTR = kBQ + 16;     // dS^T [key][query]
-  constexpr int CPR = D / 8;
-  constexpr int NCH = kBQ * CPR / kThreads;
-  __shared__ __align__(16) bf16 Ks[kBNB * KSTR];
-  __shared__ __align__(16) bf16 Qs[2][kBQ * RSTR];
-  __shared__ __align__(16) bf16 Os[2][kBQ * RSTR];
-  __shared__ __align__(16) bf16 St[kBNB * SSTR];
-  __shared__ __align__(16) float lse2s[2][kBQ];
-  __shared__ __align__(16) float dls[2][kBQ];
+  constexpr int TS = tstr<D>();
+  constexpr int CPR = TS / 8;                 // 16-byte chunks per padded row
+  constexpr int QBLK = kBQ * TS / 512;        // 1 KiB copies per Q (or dO) tile
+  constexpr int QPW = (QBLK + 3) / 4;         // ... per wave
+  __shared__ __align__(16) bf16 Ks[kBNB * TS];
+  __shared__ __align__(16) bf16 Q0[kBQ * TS];
+  __shared__ __align__(16) bf16 Q1[kBQ * TS];
+  __shared__ __align__(16) bf16 O0[kBQ * TS];
+  __shared__ __align__(16) bf16 O1[kBQ * TS];
+  __shared__ __align__(16) bf16 S0[kBNB * kSSTR];
+  __shared__ __align__(16) bf16 S1[kBNB * kSSTR];
+  __shared__ __align__(16) float L0[2 * kBQ];   // lse*log2(e) [32] | D [32]
+  __shared__ __align__(16) float L1[2 * kBQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -414,6 +439,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
   const int hl = lane >> 5;
   const int c0base = 16 * ((lane >> 4) & 1);
 
+  // ---- work item
   const int per_kv = a.n_ct * a.splits_c + a.B * a.n_tt;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int kv = lg / per_kv;
@@ -443,33 +469,83 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
   const bf16* vbase = cart ? reinterpret_cast<const bf16*>(a.v_cart) + kv * D
                            : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
 
-  // K, V rows of this lane's key as B operands; the tile's K rows into LDS.
-  bf16x8 kf[NKS], vf[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if (key_ok) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)my_key * row_stride + 16 * ks + 8 * hl);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)my_key * row_stride + 16 * ks + 8 * hl);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { kf[ks][e] = (bf16)0.f; vf[ks][e] = (bf16)0.f; }
-    }
+  // ---- unit counters: (bb, hin, qt) of the unit, advanced one unit at a time
+  const int qt0 = cart ? 0 : tile * (kBNB / kBQ);
+  int bb, hin, qt;
+  if (cart) {
+    bb = u_begin / (a.g * a.nqt);
+    hin = (u_begin / a.nqt) % a.g;
+    qt = u_begin % a.nqt;
+  } else {
+    bb = b;
+    hin = 0;
+    qt = qt0;
   }
-  {
-    constexpr int NK = kBNB * CPR / kThreads;
+  auto advance = [&](int& ubb, int& uh, int& uq) {
+    if (++uq == a.nqt) {
+      uq = qt0;
+      if (++uh == a.g) { uh = 0; ++ubb; }
+    }
+  };
+
+  // ---- per-lane offsets of this wave's share of a unit's Q / dO copy
+  const int q_row_bytes = a.Hq * D * 2;
+  int c_roff[QPW], c_coff[QPW];
 #pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      const int c = tid + u * kThreads;
-      const int r = c / CPR;
-      const int col = (c % CPR) * 8;
-      bf16x8 v8;
-      if (j0 + r < limit) {
-        v8 = *reinterpret_cast<const bf16x8*>(kbase + (size_t)(j0 + r) * row_stride + col);
-      } else {
+  for (int k = 0; k < QPW; ++k) {
+    const int chunk = (4 * k + wave) * 64 + lane;
+    const int r = chunk / CPR;
+    const int cc = chunk % CPR;
+    c_roff[k] = r * q_row_bytes;
+    c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
+  }
+  auto issue = [&](int ubb, int uh, int uq, bf16* Qst, bf16* Ost, float* Lst) {
+    const int h = kv * a.g + uh;
+    const int i0 = uq * kBQ;
+    const int rows = min(kBQ, a.n - i0);
+    const int lim = (rows - 1) * q_row_bytes;
+    const size_t base = (((size_t)ubb * a.n + i0) * a.Hq + h) * D * 2;
+    const char* qb = reinterpret_cast<const char*>(a.q) + base;
+    const char* ob = reinterpret_cast<const char*>(a.dout) + base;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v8[e] = (bf16)0.f;
+    for (int k = 0; k < QPW; ++k) {
+      const int blk = 4 * k + wave;
+      if (blk < QBLK) {
+        const int off = min(c_roff[k], lim) + c_coff[k];
+        __builtin_amdgcn_global_load_lds((const void*)(qb + off),
+            (__attribute__((address_space(3))) void*)(Qst + blk * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(ob + off),
+            (__attribute__((address_space(3))) void*)(Ost + blk * 512), 16, 0, 0);
       }
-      *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + col]) = v8;
+    }
+    if (wave == 0) {
+      const size_t li = ((size_t)ubb * a.Hq + h) * a.n + i0 + min(l32, rows - 1);
+      const float* g = (lane < 32) ? a.lse2 + li : a.delta + li;
+      __builtin_amdgcn_global_load_lds((const void*)g,
+                                       (__attribute__((address_space(3))) void*)Lst, 4, 0, 0);
+    }
+  };
+
+  // ---- dQ atomics: one buffer resource per unit, ending after row n-1
+  const int hqd = a.Hq * D;
+  const int a_voff = (4 * hl * hqd + 32 * (wave % NDB) + l32) * 4;
+  auto dq_rsrc = [&](int ubb, int uh) {
+    float* base = a.dq_acc + ((size_t)ubb * a.n * a.Hq + kv * a.g + uh) * D;
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, ((a.n - 1) * hqd + D) * 4,
+                                             0x00020000);
+  };
+
+  // ---- the wave's K, V rows as B operands; the tile's K rows into LDS
+  dma_tile<D, kBNB>(Ks, kbase + (size_t)j0 * row_stride, row_stride, min(kBNB, limit - j0), wave,
+                    lane);
+  if (u_begin < u_end) issue(bb, hin, qt, Q0, O0, L0);
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const int kr = key_ok ? my_key : limit - 1;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)kr * row_stride + 16 * ks + 8 * hl);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kr * row_stride + 16 * ks + 8 * hl);
     }
   }
 
@@ -479,108 +555,67 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
 
-  auto unit_of = [&](int u, int& bb, int& h, int& i0) {
-    int hin, qt;
-    if (cart) {
-      bb = u / (a.g * a.nqt);
-      hin = (u / a.nqt) % a.g;
-      qt = u % a.nqt;
-    } else {
-      const int span = a.nqt - tile * (kBNB / kBQ);
-      bb = b;
-      hin = u / span;
-      qt = tile * (kBNB / kBQ) + u % span;
-    }
-    h = kv * a.g + hin;
-    i0 = qt * kBQ;
-  };
-
-  bf16x8 pq[NCH], po[NCH];
-  float pl2 = 0.f, pdl = 0.f;
-  auto load_unit = [&](int u) {
-    int bb, h, i0;
-    unit_of(u, bb, h, i0);
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int c = tid + ch * kThreads;
-      const int r = c / CPR;
-      const int col = (c % CPR) * 8;
-      const int i = i0 + r;
-      if (i < a.n) {
-        const size_t off = (((size_t)bb * a.n + i) * a.Hq + h) * D + col;
-        pq[ch] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.q) + off);
-        po[ch] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const bf16*>(a.dout) + off);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { pq[ch][e] = (bf16)0.f; po[ch][e] = (bf16)0.f; }
-      }
-    }
-    if (tid < kBQ) {
-      const int i = i0 + tid;
-      const size_t li = ((size_t)bb * a.Hq + h) * a.n + i;
-      pl2 = (i < a.n) ? a.lse[li] * kLog2e : INFINITY;
-      pdl = (i < a.n) ? a.delta[li] : 0.f;
-    }
-  };
-  auto store_unit = [&](int buf) {
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int c = tid + ch * kThreads;
-      const int r = c / CPR;
-      const int col = (c % CPR) * 8;
-      *reinterpret_cast<bf16x8*>(&Qs[buf][r * RSTR + col]) = pq[ch];
-      *reinterpret_cast<bf16x8*>(&Os[buf][r * RSTR + col]) = po[ch];
-    }
-    if (tid < kBQ) {
-      lse2s[buf][tid] = pl2;
-      dls[buf][tid] = pdl;
-    }
-  };
-
   constexpr int NKP = 4 / NDB;
   const int q_db = wave % NDB;
   const int kbeg = (wave / NDB) * (kBNB / NKP);
   constexpr int KP_STEPS = (kBNB / NKP) / 16;
   const float c = a.scale_log2;
+  const float scale = a.scale;
 
-  if (u_begin < u_end) {
-    load_unit(u_begin);
-    store_unit(0);
-  }
-  __syncthreads();
-  for (int u = u_begin; u < u_end; ++u) {
-    const int cur = (u - u_begin) & 1;
-    const bool more = u + 1 < u_end;
-    int bb, h, i0;
-    unit_of(u, bb, h, i0);
-    if (more) load_unit(u + 1);
-
-    f32x16 s, dp;
+  // One step: dQ of the previous unit (if WITH_DQ) interleaved with the S and
+  // dP products of this unit, then P, dS, dV, dK and the dS^T store.
+  auto step = [&](auto with_dq, const bf16* Qs, const bf16* Os, const float* Ls, bf16* St,
+                  const bf16* Sp, int ubb, int uh, int uq, int pbb, int ph, int pq) {
+    constexpr bool WITH_DQ = decltype(with_dq)::value;
+    const int i0 = uq * kBQ;
+    f32x16 s, dp, acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-    {
-      const bf16* qrow = &Qs[cur][l32 * RSTR + 8 * hl];
-      const bf16* orow = &Os[cur][l32 * RSTR + 8 * hl];
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; acc[r] = 0.f; }
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s = M::mma(*reinterpret_cast<const bf16x8*>(qrow + 16 * ks), kf[ks], s);
-        dp = M::mma(*reinterpret_cast<const bf16x8*>(orow + 16 * ks), vf[ks], dp);
+    for (int ks = 0; ks < NKS; ++ks) {
+      if constexpr (WITH_DQ) {
+        if (ks < KP_STEPS) {
+          const int k0 = kbeg + 16 * ks + 8 * hl;
+          const bf16x8 sa = cat8(tr_col4(Sp, kSSTR, k0, c0base, lane),
+                                 tr_col4(Sp, kSSTR, k0 + 4, c0base, lane));
+          const bf16x8 kb = cat8(tr_col4(Ks, TS, k0, 32 * q_db + c0base, lane),
+                                 tr_col4(Ks, TS, k0 + 4, 32 * q_db + c0base, lane));
+          acc = M::mma(sa, kb, acc);
+        }
       }
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + t_off<D>(l32, 16 * ks + 8 * hl));
+      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Os + t_off<D>(l32, 16 * ks + 8 * hl));
+      s = M::mma(qa, kf[ks], s);
+      dp = M::mma(oa, vf[ks], dp);
     }
+    if constexpr (WITH_DQ) {
+      const auto rs = dq_rsrc(pbb, ph);
+      const int prow = pq * kBQ * hqd * 4;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+            acc[r], rs, a_voff, prow + ((r & 3) + 8 * (r >> 2)) * hqd * 4, 0);
+    }
+    // P = exp2(s*c - lse2), dS = scale * P * (dP - D)
+    const bool need_mask = (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&lse2s[cur][8 * c4 + 4 * hl]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&dls[cur][8 * c4 + 4 * hl]);
+      const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * c4 + 4 * hl);
+      const float4 d4 = *reinterpret_cast<const float4*>(Ls + kBQ + 8 * c4 + 4 * hl);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
       const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * c4 + e;
-        const int i = i0 + 8 * c4 + 4 * hl + e;
-        const bool vis = key_ok && (cart || my_key <= i);
-        const float pv_ = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[e])) : 0.f;
+        float arg = fmaf(s[r], c, -lv[e]);
+        if (need_mask) {
+          const int i = i0 + 8 * c4 + 4 * hl + e;
+          const bool vis = key_ok && i < a.n && (cart || my_key <= i);
+          arg = vis ? arg : -INFINITY;
+        }
+        const float pv_ = __builtin_amdgcn_exp2f(arg);
         s[r] = pv_;
-        dp[r] = pv_ * (dp[r] - dvv[e]);
+        dp[r] = pv_ * (dp[r] - dvv[e]) * scale;
       }
     }
 #pragma unroll
@@ -590,49 +625,84 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
       const int q0 = 16 * m + 4 * hl;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int c0 = 32 * db + c0base;
-        const bf16x8 ob = cat8(tr_col4(Os[cur], RSTR, q0, c0, lane),
-                               tr_col4(Os[cur], RSTR, q0 + 8, c0, lane));
-        const bf16x8 qb = cat8(tr_col4(Qs[cur], RSTR, q0, c0, lane),
-                               tr_col4(Qs[cur], RSTR, q0 + 8, c0, lane));
+        const int cc = 32 * db + c0base;
+        const bf16x8 ob = cat8(tr_col4(Os, TS, q0, cc, lane), tr_col4(Os, TS, q0 + 8, cc, lane));
+        const bf16x8 qb = cat8(tr_col4(Qs, TS, q0, cc, lane), tr_col4(Qs, TS, q0 + 8, cc, lane));
         dv[db] = M::mma(pf, ob, dv[db]);
         dk[db] = M::mma(sf, qb, dk[db]);
       }
     }
+    const int srow = 32 * wave + l32;
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
       bf16x4 v4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v4[e] = (bf16)dp[4 * c4 + e];
-      *reinterpret_cast<bf16x4*>(&St[(32 * wave + l32) * SSTR + 8 * c4 + 4 * hl]) = v4;
+      *reinterpret_cast<bf16x4*>(St + srow * kSSTR + 8 * c4 + 4 * hl) = v4;
     }
-    __syncthreads();
+  };
+  // the tail: dQ of the last unit alone
+  auto last_dq = [&](const bf16* Sp, int pbb, int ph, int pq) {
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KP_STEPS; ++ks) {
+      const int k0 = kbeg + 16 * ks + 8 * hl;
+      const bf16x8 sa = cat8(tr_col4(Sp, kSSTR, k0, c0base, lane),
+                             tr_col4(Sp, kSSTR, k0 + 4, c0base, lane));
+      const bf16x8 kb = cat8(tr_col4(Ks, TS, k0, 32 * q_db + c0base, lane),
+                             tr_col4(Ks, TS, k0 + 4, 32 * q_db + c0base, lane));
+      acc = M::mma(sa, kb, acc);
+    }
+    const auto rs = dq_rsrc(pbb, ph);
+    const int prow = pq * kBQ * hqd * 4;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+          acc[r], rs, a_voff, prow + ((r & 3) + 8 * (r >> 2)) * hqd * 4, 0);
+  };
 
-    {
-      f32x16 acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KP_STEPS; ++ks) {
-        const int k0 = kbeg + 16 * ks + 8 * hl;
-        const bf16x8 sa = cat8(tr_col4(St, SSTR, k0, c0base, lane),
-                               tr_col4(St, SSTR, k0 + 4, c0base, lane));
-        const bf16x8 kb = cat8(tr_col4(Ks, KSTR, k0, 32 * q_db + c0base, lane),
-                               tr_col4(Ks, KSTR, k0 + 4, 32 * q_db + c0base, lane));
-        acc = M::mma(sa, kb, acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i0 + d_row(r, hl);
-        if (i < a.n)
-          atomicAdd(a.dq_acc + (((size_t)bb * a.n + i) * a.Hq + h) * D + 32 * q_db + l32,
-                    acc[r] * a.scale);
-      }
+  if (u_begin < u_end) {
+    // first unit: buffers 0, no dQ yet
+    int nb = bb, nh = hin, nq = qt;
+    advance(nb, nh, nq);
+    CART_WAIT_VMCNT(0);
+    lds_barrier();
+    if (u_begin + 1 < u_end) issue(nb, nh, nq, Q1, O1, L1);
+    __builtin_amdgcn_sched_barrier(0);
+    step(std::false_type{}, Q0, O0, L0, S0, S1, bb, hin, qt, 0, 0, 0);
+    int pbb = bb, ph = hin, pq = qt;
+    bb = nb; hin = nh; qt = nq;
+    for (int u = u_begin + 1; u < u_end; u += 2) {
+      // unit u in buffers 1, dQ of unit u-1 from S0
+      nb = bb; nh = hin; nq = qt;
+      advance(nb, nh, nq);
+      CART_WAIT_VMCNT(0);
+      lds_barrier();
+      if (u + 1 < u_end) issue(nb, nh, nq, Q0, O0, L0);
+      __builtin_amdgcn_sched_barrier(0);
+      step(std::true_type{}, Q1, O1, L1, S1, S0, bb, hin, qt, pbb, ph, pq);
+      pbb = bb; ph = hin; pq = qt;
+      bb = nb; hin = nh; qt = nq;
+      if (u + 1 >= u_end) break;
+      // unit u+1 in buffers 0, dQ of unit u from S1
+      nb = bb; nh = hin; nq = qt;
+      advance(nb, nh, nq);
+      CART_WAIT_VMCNT(0);
+      lds_barrier();
+      if (u + 2 < u_end) issue(nb, nh, nq, Q1, O1, L1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(std::true_type{}, Q0, O0, L0, S0, S1, bb, hin, qt, pbb, ph, pq);
+      pbb = bb; ph = hin; pq = qt;
+      bb = nb; hin = nh; qt = nq;
     }
-    if (more) store_unit(cur ^ 1);
-    __syncthreads();
+    CART_WAIT_VMCNT(0);
+    lds_barrier();
+    last_dq(((u_end - u_begin) & 1) ? S0 : S1, pbb, ph, pq);
   }
 
+  // ---- dK (scale already inside dS), dV
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int j = j0 + 32 * wave + d_row(r, hl);
@@ -640,7 +710,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int col = 32 * db + l32;
-      const float gk = dk[db][r] * a.scale;
+      const float gk = dk[db][r];
       const float gv = dv[db][r];
       if (cart) {
         const size_t o = ((size_t)j * a.Hkv + kv) * D + col;
@@ -686,7 +756,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
   for (int e = 0; e < D / 64; ++e) acc += to_f32(o[lane + 64 * e]) * to_f32(g[lane + 64 * e]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) a.delta[((size_t)b * a.Hq + h) * a.n + i] = acc;
+  if (lane == 0) {
+    const size_t li = ((size_t)b * a.Hq + h) * a.n + i;
+    a.delta[li] = acc;
+    a.lse2[li] = a.lse[li] * kLog2e;
+  }
   float* dq = a.dq_acc + (size_t)row * D;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) dq[lane + 64 * e] = 0.f;
@@ -751,7 +825,7 @@ BwdPlan plan_bwd(const AttnDims& d) {
   pl.grid_c = d.Hkv * pl.n_ct * s;
   pl.grid_t = d.Hkv * d.B * pl.n_tt;
   pl.dq_bytes = (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
-  pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);
+  pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);   // and as much for lse2
   pl.part_bytes = s > 1 ? (size_t)s * d.p * d.Hkv * d.D * sizeof(float) : 0;
   if (d.tok_bf16 && !d.row_bf16 && d.p > 0)
     pl.shadow_bytes = 2 * (size_t)d.p * d.Hkv * d.D * sizeof(uint16_t);
@@ -760,7 +834,7 @@ BwdPlan plan_bwd(const AttnDims& d) {
 
 size_t bwd_workspace_bytes(const AttnDims& d) {
   const BwdPlan pl = plan_bwd(d);
-  return align256(pl.shadow_bytes) + align256(pl.dq_bytes) + align256(pl.delta_bytes) +
+  return align256(pl.shadow_bytes) + align256(pl.dq_bytes) + 2 * align256(pl.delta_bytes) +
          2 * align256(pl.part_bytes);
 }
 
@@ -810,6 +884,8 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.dq_acc = reinterpret_cast<float*>(w);
   w += align256(pl.dq_bytes);
   a.delta = reinterpret_cast<float*>(w);
+  w += align256(pl.delta_bytes);
+  a.lse2 = reinterpret_cast<float*>(w);
   w += align256(pl.delta_bytes);
   a.dk_part = pl.part_bytes ? reinterpret_cast<float*>(w) : nullptr;
   w += align256(pl.part_bytes);

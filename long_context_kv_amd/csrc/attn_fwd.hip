@@ -286,8 +286,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel. Same work decomposition and softmax as attn_fwd_kernel, with:
-//  * K and V tiles copied global -> LDS by direct (VGPR-free) loads into a
-//    swizzled, double-buffered layout: the copy of tile t+1 runs while tile t
+//  * K and V tiles copied global -> LDS by direct (VGPR-free) loads into
+//    padded, double-buffered tiles: the copy of tile t+1 runs while tile t
 //    is multiplied, and the loop has one barrier per tile;
 //  * the V^T operand of O^T += V^T P^T read with LDS transpose reads, so no
 //    transposed copy of V is ever written;
@@ -342,7 +342,7 @@ __device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, cons
     bf16x8 kfr[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + sw_off<D>(32 * kh + l32, 16 * ks + 8 * hl));
+      kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + t_off<D>(32 * kh + l32, 16 * ks + 8 * hl));
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
 #pragma unroll
@@ -396,8 +396,8 @@ __device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, cons
       bf16x8 va[NDB];
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        va[db] = cat8(tr_col4_sw<D>(Vs, r0, 32 * db + c0base, lane),
-                      tr_col4_sw<D>(Vs, r0 + 8, 32 * db + c0base, lane));
+        va[db] = cat8(tr_col4(Vs, tstr<D>(), r0, 32 * db + c0base, lane),
+                      tr_col4(Vs, tstr<D>(), r0 + 8, 32 * db + c0base, lane));
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] = M::mma(va[db], pf, acc[db]);
     }
@@ -407,10 +407,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __align__(16) bf16 K0[kBN * D];
-  __shared__ __align__(16) bf16 V0[kBN * D];
-  __shared__ __align__(16) bf16 K1[kBN * D];
-  __shared__ __align__(16) bf16 V1[kBN * D];
+  __shared__ __align__(16) bf16 K0[kBN * tstr<D>()];
+  __shared__ __align__(16) bf16 V0[kBN * tstr<D>()];
+  __shared__ __align__(16) bf16 K1[kBN * tstr<D>()];
+  __shared__ __align__(16) bf16 V1[kBN * tstr<D>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -465,6 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     if (t + 1 < t_end) fwd_issue<D>(K1, V1, t + 1, n_ct, a, kv, kt, vt, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
     {
       const FwdTile<D> f = fwd_tile<D>(t, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31))
@@ -474,6 +475,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     if (t + 2 < t_end) fwd_issue<D>(K0, V0, t + 2, n_ct, a, kv, kt, vt, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
     {
       const FwdTile<D> f = fwd_tile<D>(t + 1, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31))

@@ -169,54 +169,43 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 namespace cartattn {
 
 // ---- LDS tiles for the bf16 kernels -------------------------------------
-// A tile of R rows x D bf16 is stored unpadded (row = 2*D bytes). Inside a
-// row, 16-byte chunk c lives at chunk position c ^ swz(r). The XOR spreads
-// the rows of a 16-byte row read (lanes = rows) and of a transpose read
-// (4 rows x 32 bytes per 16-lane group) over all LDS banks, and keeps every
-// wave's 1 KiB of a direct global->LDS load contiguous.
+// A tile of R rows x D bf16 is stored with rows padded to TSTR = D + 16
+// elements. The 8-dword bank shift per row makes both access patterns of the
+// kernels conflict-free: 16-byte row reads with one row per lane, and
+// transpose reads (4 rows x 32 bytes per 16-lane group). Every fragment
+// address is then a per-lane base plus a compile-time offset.
 template <int D>
-__device__ __forceinline__ constexpr int swz(int r) {
-  if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return (r >> 1) & 7;
-}
+constexpr int tstr() { return D + 16; }
 
-// Element offset of (row r, column col) in a swizzled tile.
 template <int D>
-__device__ __forceinline__ int sw_off(int r, int col) {
-  return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
-}
-
-// Transpose read (see tr_col4) from a swizzled tile: lane j of each 16-lane
-// group receives rows r0..r0+3 of column c0 + j (c0 a multiple of 16).
-template <int D>
-__device__ __forceinline__ bf16x4 tr_col4_sw(const bf16* tile, int r0, int c0, int lane) {
-  const int s = lane & 15;
-  const bf16* p = tile + sw_off<D>(r0 + (s >> 2), c0 + 4 * (s & 3));
-  const tr_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) tr_v4i16*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
+__device__ __forceinline__ int t_off(int r, int col) { return r * tstr<D>() + col; }
 
 // Issue this wave's share of an asynchronous global->LDS copy of a tile of
-// NROWS rows x D bf16 (global rows `row_stride` elements apart) into a
-// swizzled LDS tile. The 4 waves of the workgroup each issue NROWS*D/2048
-// dwordx4 loads; lane l of one load lands at byte 16*l of that load's 1 KiB
-// LDS block. Rows at or past `rows` re-read row rows-1 (finite data that the
+// NROWS rows x D bf16 (global rows `row_stride` elements apart) into a padded
+// LDS tile. The tile is NROWS * TSTR * 2 bytes, written by 1 KiB direct loads
+// (lane l of one load lands at byte 16*l of that load's block) spread over
+// the 4 waves. Lanes whose 16 bytes fall on row padding re-read a chunk of
+// their row, and rows at or past `rows` re-read row rows-1 (finite data the
 // caller masks), so no address leaves the source.
 template <int D, int NROWS>
 __device__ __forceinline__ void dma_tile(bf16* lds, const bf16* src, size_t row_stride, int rows,
                                          int wave, int lane) {
-  constexpr int PER_WAVE = NROWS * D / 512 / 4;   // 1 KiB loads per wave
+  constexpr int CPR = tstr<D>() / 8;                  // 16-byte chunks per padded row
+  constexpr int NBLK = NROWS * tstr<D>() / 512;       // 1 KiB loads for the tile
+  static_assert(NROWS * tstr<D>() % 512 == 0, "tile must be whole 1 KiB blocks");
 #pragma unroll
-  for (int k = 0; k < PER_WAVE; ++k) {
-    const int blk = wave * PER_WAVE + k;
-    const int off = blk * 512 + lane * 8;          // element offset of this lane's chunk
-    const int r = off / D;
-    const int c = ((off % D) >> 3) ^ swz<D>(r);
-    const int rr = r < rows ? r : rows - 1;
-    const bf16* g = src + (size_t)rr * row_stride + c * 8;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)g, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+  for (int k = 0; k < (NBLK + 3) / 4; ++k) {
+    const int blk = k * 4 + wave;
+    if (blk < NBLK) {
+      const int chunk = blk * 64 + lane;
+      const int r = chunk / CPR;
+      int cc = chunk % CPR;
+      cc = cc < D / 8 ? cc : 0;
+      const int rr = r < rows ? r : rows - 1;
+      const bf16* g = src + (size_t)rr * row_stride + cc * 8;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)g, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+    }
   }
 }
 
