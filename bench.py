@@ -98,7 +98,7 @@ def train_bench(C, W, shape, steps, warmup):
     total_ms = _events_ms(step, steps)
     kern = {}
     for name in ("rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess", "attn_bwd",
-                 "bwd_dq_finalize", "bwd_cart_reduce"):
+                 "attn_bwd_dq", "bwd_dq_finalize", "bwd_cart_reduce"):
         ms, cnt = C.timing_query(name)
         if cnt:
             kern[name] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms)
@@ -219,8 +219,12 @@ def main():
     value = flop / (ms * 1e-3) / 1e12
 
     # roofline of the dominant kernel (largest share of the step's time)
+    # algorithmic flop per launch: forward QK^T + PV; the backward's dP, dV, dK
+    # are charged to the key-major kernel and dQ to the query-major one (the
+    # recomputation of S, and of dP in the dQ kernel, is not counted)
     per_launch_flop = {"attn_fwd": 4.0 * shape.head_dim * shape.visible_pairs,
-                       "attn_bwd": 8.0 * shape.head_dim * shape.visible_pairs}
+                       "attn_bwd": 6.0 * shape.head_dim * shape.visible_pairs,
+                       "attn_bwd_dq": 2.0 * shape.head_dim * shape.visible_pairs}
     dom = max(kern, key=lambda k: kern[k]["total_ms"])
     roof = None
     if dom in per_launch_flop:

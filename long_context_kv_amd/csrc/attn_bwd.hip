@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "kvtiles.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
 
@@ -63,6 +64,8 @@ struct BwdArgs {
   float* dv_part;
   int B, n, p, f, Hq, Hkv, g;
   int n_ct, n_tt, nqt, splits_c;
+  int hpw, wph, n_hg, n_qb;   // query-major grid of the dQ kernel
+  int zero_dq;                // preprocess clears the f32 dQ accumulator
   int accumulate;
   float scale, scale_log2;
 };
@@ -384,26 +387,23 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel: same decomposition and arithmetic as attn_bwd_kernel, built
-// for one wave per SIMD with little work besides the MFMAs:
-//  * the workgroup's K tile and each unit's Q, dO, LSE*log2(e) and D rows are
-//    copied global -> LDS by direct (VGPR-free) loads into padded tiles; the
-//    copy for unit u+1 is issued first thing in the step of unit u;
-//  * every transposed operand (dO^T and Q^T for dV += P^T dO, dK += dS^T Q;
-//    dS and K for dQ = dS K) is read with LDS transpose reads from row-major
-//    tiles; dS^T is written with 8-byte stores from the MFMA result layout;
-//  * software pipeline over units: the step of unit u also computes dQ of
-//    unit u-1 from the other dS^T buffer, interleaved with its own S and dP
-//    MFMAs, so there is one barrier per unit and it orders LDS only;
-//  * dQ goes to the f32 accumulator with buffer atomics whose resource ends
-//    at the unit's last query row, so rows past the end are dropped by the
-//    hardware range check; the softmax scale is folded into dS once;
-//  * per-lane copy offsets are computed once, units advance by counters, and
-//    the mask is evaluated only on diagonal or ragged units.
+// bf16 path: two kernels, neither with atomics.
+//
+// attn_bwd_kv_kernel -- dK and dV. One workgroup per 128-key tile (4 waves x
+//   32 keys; K and V rows of a wave are register operands and its f32 dK, dV
+//   stay in registers), looping over (batch, q-head, 32-query) units. Each
+//   unit's Q, dO, LSE*log2(e) and D rows are copied global -> LDS by direct
+//   loads into a 3-deep ring of padded tiles. Software pipeline: the step of
+//   unit k computes S and dP of unit k+1, then dV += P^T dO and dK += dS^T Q
+//   of unit k (operands dO^T, Q^T by LDS transpose reads) interleaved with the
+//   softmax of unit k+1, so the MFMA chains of one unit hide the latencies of
+//   the other. One LDS-only barrier per unit.
+//
+// attn_bwd_dq_kernel -- dQ, query-major like the forward: per key tile it
+//   recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T, and accumulates
+//   dQ^T += K^T dS^T in registers (K^T by transpose reads, dS^T straight from
+//   the MFMA result layout). dQ is written once, in the token dtype.
 // Cartridge rows arrive as bf16 (f32 master rows are cast first).
-
-// dS^T tile [key][query]: 128 x 32 bf16 with rows padded to 48 elements.
-constexpr int kSSTR = kBQ + 16;
 
 // True when no pair of this unit needs a mask for the key side: every key
 // of the workgroup tile exists and (for a token tile) every key precedes
@@ -414,23 +414,20 @@ __device__ __forceinline__ bool key_ok_all(bool cart, int j0, int i0, int limit)
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TS = tstr<D>();
-  constexpr int CPR = TS / 8;                 // 16-byte chunks per padded row
-  constexpr int QBLK = kBQ * TS / 512;        // 1 KiB copies per Q (or dO) tile
-  constexpr int QPW = (QBLK + 3) / 4;         // ... per wave
-  __shared__ __align__(16) bf16 Ks[kBNB * TS];
-  __shared__ __align__(16) bf16 Q0[kBQ * TS];
-  __shared__ __align__(16) bf16 Q1[kBQ * TS];
-  __shared__ __align__(16) bf16 O0[kBQ * TS];
-  __shared__ __align__(16) bf16 O1[kBQ * TS];
-  __shared__ __align__(16) bf16 S0[kBNB * kSSTR];
-  __shared__ __align__(16) bf16 S1[kBNB * kSSTR];
-  __shared__ __align__(16) float L0[2 * kBQ];   // lse*log2(e) [32] | D [32]
-  __shared__ __align__(16) float L1[2 * kBQ];
+  constexpr int CPR = TS / 8;
+  constexpr int QBLK = kBQ * TS / 512;
+  constexpr int QPW = (QBLK + 3) / 4;
+  // 3-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32]
+  constexpr int STAGE = 2 * kBQ * TS + 2 * 2 * kBQ;   // bf16 elements per stage
+  __shared__ __align__(16) bf16 ring[3 * STAGE];
+  auto Qst = [&](int st) { return ring + st * STAGE; };
+  auto Ost = [&](int st) { return ring + st * STAGE + kBQ * TS; };
+  auto Lst = [&](int st) { return reinterpret_cast<float*>(ring + st * STAGE + 2 * kBQ * TS); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -469,23 +466,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
   const bf16* vbase = cart ? reinterpret_cast<const bf16*>(a.v_cart) + kv * D
                            : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
 
-  // ---- unit counters: (bb, hin, qt) of the unit, advanced one unit at a time
+  // ---- unit counters
   const int qt0 = cart ? 0 : tile * (kBNB / kBQ);
-  int bb, hin, qt;
+  struct Unit { int bb, hin, qt; };
+  Unit cu;
   if (cart) {
-    bb = u_begin / (a.g * a.nqt);
-    hin = (u_begin / a.nqt) % a.g;
-    qt = u_begin % a.nqt;
+    cu.bb = u_begin / (a.g * a.nqt);
+    cu.hin = (u_begin / a.nqt) % a.g;
+    cu.qt = u_begin % a.nqt;
   } else {
-    bb = b;
-    hin = 0;
-    qt = qt0;
+    cu.bb = b;
+    cu.hin = 0;
+    cu.qt = qt0;
   }
-  auto advance = [&](int& ubb, int& uh, int& uq) {
-    if (++uq == a.nqt) {
-      uq = qt0;
-      if (++uh == a.g) { uh = 0; ++ubb; }
+  auto next = [&](Unit x) {
+    if (++x.qt == a.nqt) {
+      x.qt = qt0;
+      if (++x.hin == a.g) { x.hin = 0; ++x.bb; }
     }
+    return x;
   };
 
   // ---- per-lane offsets of this wave's share of a unit's Q / dO copy
@@ -499,12 +498,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
     c_roff[k] = r * q_row_bytes;
     c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
   }
-  auto issue = [&](int ubb, int uh, int uq, bf16* Qst, bf16* Ost, float* Lst) {
-    const int h = kv * a.g + uh;
-    const int i0 = uq * kBQ;
+  auto issue = [&](const Unit& x, bf16* Qst, bf16* Ost, float* Lst) {
+    const int h = kv * a.g + x.hin;
+    const int i0 = x.qt * kBQ;
     const int rows = min(kBQ, a.n - i0);
     const int lim = (rows - 1) * q_row_bytes;
-    const size_t base = (((size_t)ubb * a.n + i0) * a.Hq + h) * D * 2;
+    const size_t base = (((size_t)x.bb * a.n + i0) * a.Hq + h) * D * 2;
     const char* qb = reinterpret_cast<const char*>(a.q) + base;
     const char* ob = reinterpret_cast<const char*>(a.dout) + base;
 #pragma unroll
@@ -519,26 +518,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
       }
     }
     if (wave == 0) {
-      const size_t li = ((size_t)ubb * a.Hq + h) * a.n + i0 + min(l32, rows - 1);
+      const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0 + min(l32, rows - 1);
       const float* g = (lane < 32) ? a.lse2 + li : a.delta + li;
       __builtin_amdgcn_global_load_lds((const void*)g,
                                        (__attribute__((address_space(3))) void*)Lst, 4, 0, 0);
     }
   };
 
-  // ---- dQ atomics: one buffer resource per unit, ending after row n-1
-  const int hqd = a.Hq * D;
-  const int a_voff = (4 * hl * hqd + 32 * (wave % NDB) + l32) * 4;
-  auto dq_rsrc = [&](int ubb, int uh) {
-    float* base = a.dq_acc + ((size_t)ubb * a.n * a.Hq + kv * a.g + uh) * D;
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, ((a.n - 1) * hqd + D) * 4,
-                                             0x00020000);
-  };
-
-  // ---- the wave's K, V rows as B operands; the tile's K rows into LDS
-  dma_tile<D, kBNB>(Ks, kbase + (size_t)j0 * row_stride, row_stride, min(kBNB, limit - j0), wave,
-                    lane);
-  if (u_begin < u_end) issue(bb, hin, qt, Q0, O0, L0);
+  // ---- the wave's K, V rows as B operands
+  if (u_begin < u_end) issue(cu, Qst(0), Ost(0), Lst(0));
   bf16x8 kf[NKS], vf[NKS];
   {
     const int kr = key_ok ? my_key : limit - 1;
@@ -554,49 +542,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
-
-  constexpr int NKP = 4 / NDB;
-  const int q_db = wave % NDB;
-  const int kbeg = (wave / NDB) * (kBNB / NKP);
-  constexpr int KP_STEPS = (kBNB / NKP) / 16;
   const float c = a.scale_log2;
   const float scale = a.scale;
 
-  // One step: dQ of the previous unit (if WITH_DQ) interleaved with the S and
-  // dP products of this unit, then P, dS, dV, dK and the dS^T store.
-  auto step = [&](auto with_dq, const bf16* Qs, const bf16* Os, const float* Ls, bf16* St,
-                  const bf16* Sp, int ubb, int uh, int uq, int pbb, int ph, int pq) {
-    constexpr bool WITH_DQ = decltype(with_dq)::value;
-    const int i0 = uq * kBQ;
-    f32x16 s, dp, acc;
+  // S = Q K^T and dP = dO V^T of one unit (rows = queries of the unit,
+  // columns = this wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)).
+  auto sdp = [&](const bf16* Qs, const bf16* Os, f32x16& s, f32x16& dp) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; acc[r] = 0.f; }
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (WITH_DQ) {
-        if (ks < KP_STEPS) {
-          const int k0 = kbeg + 16 * ks + 8 * hl;
-          const bf16x8 sa = cat8(tr_col4(Sp, kSSTR, k0, c0base, lane),
-                                 tr_col4(Sp, kSSTR, k0 + 4, c0base, lane));
-          const bf16x8 kb = cat8(tr_col4(Ks, TS, k0, 32 * q_db + c0base, lane),
-                                 tr_col4(Ks, TS, k0 + 4, 32 * q_db + c0base, lane));
-          acc = M::mma(sa, kb, acc);
-        }
-      }
       const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + t_off<D>(l32, 16 * ks + 8 * hl));
       const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Os + t_off<D>(l32, 16 * ks + 8 * hl));
       s = M::mma(qa, kf[ks], s);
       dp = M::mma(oa, vf[ks], dp);
     }
-    if constexpr (WITH_DQ) {
-      const auto rs = dq_rsrc(pbb, ph);
-      const int prow = pq * kBQ * hqd * 4;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-            acc[r], rs, a_voff, prow + ((r & 3) + 8 * (r >> 2)) * hqd * 4, 0);
-    }
-    // P = exp2(s*c - lse2), dS = scale * P * (dP - D)
+  };
+  // P = exp2(s c - lse2) and dS = scale P (dP - D), packed to bf16 A operands.
+  auto softmax = [&](const Unit& x, const float* Ls, f32x16& pv, f32x16& dsv,
+                     bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
+    const int i0 = x.qt * kBQ;
     const bool need_mask = (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
@@ -607,99 +572,71 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * c4 + e;
-        float arg = fmaf(s[r], c, -lv[e]);
+        float arg = fmaf(pv[r], c, -lv[e]);       // pv holds S on entry
         if (need_mask) {
           const int i = i0 + 8 * c4 + 4 * hl + e;
           const bool vis = key_ok && i < a.n && (cart || my_key <= i);
           arg = vis ? arg : -INFINITY;
         }
-        const float pv_ = __builtin_amdgcn_exp2f(arg);
-        s[r] = pv_;
-        dp[r] = pv_ * (dp[r] - dvv[e]) * scale;
+        const float p_ = __builtin_amdgcn_exp2f(arg);
+        pv[r] = p_;
+        dsv[r] = p_ * (dsv[r] - dvv[e]) * scale;   // dsv holds dP on entry
       }
     }
+    pf[0] = pack_regs<bf16>(pv, 0);
+    pf[1] = pack_regs<bf16>(pv, 1);
+    sf[0] = pack_regs<bf16>(dsv, 0);
+    sf[1] = pack_regs<bf16>(dsv, 1);
+  };
+  // dV += P^T dO, dK += dS^T Q (B operands by transpose reads of the tiles).
+  auto dvdk = [&](const bf16* Qs, const bf16* Os, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const bf16x8 pf = pack_regs<bf16>(s, m);
-      const bf16x8 sf = pack_regs<bf16>(dp, m);
       const int q0 = 16 * m + 4 * hl;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int cc = 32 * db + c0base;
         const bf16x8 ob = cat8(tr_col4(Os, TS, q0, cc, lane), tr_col4(Os, TS, q0 + 8, cc, lane));
         const bf16x8 qb = cat8(tr_col4(Qs, TS, q0, cc, lane), tr_col4(Qs, TS, q0 + 8, cc, lane));
-        dv[db] = M::mma(pf, ob, dv[db]);
-        dk[db] = M::mma(sf, qb, dk[db]);
+        dv[db] = M::mma(pf[m], ob, dv[db]);
+        dk[db] = M::mma(sf[m], qb, dk[db]);
       }
     }
-    const int srow = 32 * wave + l32;
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      bf16x4 v4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = (bf16)dp[4 * c4 + e];
-      *reinterpret_cast<bf16x4*>(St + srow * kSSTR + 8 * c4 + 4 * hl) = v4;
-    }
-  };
-  // the tail: dQ of the last unit alone
-  auto last_dq = [&](const bf16* Sp, int pbb, int ph, int pq) {
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KP_STEPS; ++ks) {
-      const int k0 = kbeg + 16 * ks + 8 * hl;
-      const bf16x8 sa = cat8(tr_col4(Sp, kSSTR, k0, c0base, lane),
-                             tr_col4(Sp, kSSTR, k0 + 4, c0base, lane));
-      const bf16x8 kb = cat8(tr_col4(Ks, TS, k0, 32 * q_db + c0base, lane),
-                             tr_col4(Ks, TS, k0 + 4, 32 * q_db + c0base, lane));
-      acc = M::mma(sa, kb, acc);
-    }
-    const auto rs = dq_rsrc(pbb, ph);
-    const int prow = pq * kBQ * hqd * 4;
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
-          acc[r], rs, a_voff, prow + ((r & 3) + 8 * (r >> 2)) * hqd * 4, 0);
   };
 
   if (u_begin < u_end) {
-    // first unit: buffers 0, no dQ yet
-    int nb = bb, nh = hin, nq = qt;
-    advance(nb, nh, nq);
+    const int nu = u_end - u_begin;
+    Unit u1 = next(cu);
+    if (nu > 1) issue(u1, Qst(1), Ost(1), Lst(1));
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (u_begin + 1 < u_end) issue(nb, nh, nq, Q1, O1, L1);
-    __builtin_amdgcn_sched_barrier(0);
-    step(std::false_type{}, Q0, O0, L0, S0, S1, bb, hin, qt, 0, 0, 0);
-    int pbb = bb, ph = hin, pq = qt;
-    bb = nb; hin = nh; qt = nq;
-    for (int u = u_begin + 1; u < u_end; u += 2) {
-      // unit u in buffers 1, dQ of unit u-1 from S0
-      nb = bb; nh = hin; nq = qt;
-      advance(nb, nh, nq);
-      CART_WAIT_VMCNT(0);
-      lds_barrier();
-      if (u + 1 < u_end) issue(nb, nh, nq, Q0, O0, L0);
-      __builtin_amdgcn_sched_barrier(0);
-      step(std::true_type{}, Q1, O1, L1, S1, S0, bb, hin, qt, pbb, ph, pq);
-      pbb = bb; ph = hin; pq = qt;
-      bb = nb; hin = nh; qt = nq;
-      if (u + 1 >= u_end) break;
-      // unit u+1 in buffers 0, dQ of unit u from S1
-      nb = bb; nh = hin; nq = qt;
-      advance(nb, nh, nq);
-      CART_WAIT_VMCNT(0);
-      lds_barrier();
-      if (u + 2 < u_end) issue(nb, nh, nq, Q1, O1, L1);
-      __builtin_amdgcn_sched_barrier(0);
-      step(std::true_type{}, Q0, O0, L0, S0, S1, bb, hin, qt, pbb, ph, pq);
-      pbb = bb; ph = hin; pq = qt;
-      bb = nb; hin = nh; qt = nq;
+    bf16x8 pf[2], sf[2];
+    {
+      f32x16 s, dp;
+      sdp(Qst(0), Ost(0), s, dp);
+      softmax(cu, Lst(0), s, dp, pf, sf);
     }
-    CART_WAIT_VMCNT(0);
-    lds_barrier();
-    last_dq(((u_end - u_begin) & 1) ? S0 : S1, pbb, ph, pq);
+    // step k (k = 0 .. nu-2): unit k in stage k%3, unit k+1 in stage (k+1)%3,
+    // the copy of unit k+2 goes to stage (k+2)%3
+    Unit un = u1, uf = next(u1);
+    int sk = 0;
+    for (int k = 0; k < nu - 1; ++k) {
+      const int sn = sk == 2 ? 0 : sk + 1;
+      const int sf_ = sn == 2 ? 0 : sn + 1;
+      CART_WAIT_VMCNT(0);
+      lds_barrier();
+      if (k + 2 < nu) issue(uf, Qst(sf_), Ost(sf_), Lst(sf_));
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 s, dp;
+      sdp(Qst(sn), Ost(sn), s, dp);
+      __builtin_amdgcn_sched_barrier(0);
+      dvdk(Qst(sk), Ost(sk), pf, sf);
+      softmax(un, Lst(sn), s, dp, pf, sf);
+      un = uf;
+      uf = next(uf);
+      sk = sn;
+    }
+    dvdk(Qst(sk), Ost(sk), pf, sf);
   }
 
   // ---- dK (scale already inside dS), dV
@@ -737,6 +674,143 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_bf16_kernel(BwdArgs a) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
+  using M = Mfma<bf16>;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int TS = tstr<D>();
+  __shared__ __align__(16) bf16 K0[kKvTile * TS];
+  __shared__ __align__(16) bf16 V0[kKvTile * TS];
+  __shared__ __align__(16) bf16 K1[kKvTile * TS];
+  __shared__ __align__(16) bf16 V1[kKvTile * TS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+  const int c0base = 16 * ((lane >> 4) & 1);
+
+  int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = a.n_qb - 1 - (lg % a.n_qb); lg /= a.n_qb;
+  const int hg = lg % a.n_hg; lg /= a.n_hg;
+  const int b = lg % a.B; lg /= a.B;
+  const int kv = lg;
+  const int hw = wave % a.hpw;
+  const int pb = wave / a.hpw;
+  const int h = kv * a.g + hg * a.hpw + hw;
+  const int i0 = (qb * a.wph + pb) * 32;
+  const bool wave_active = i0 < a.n;
+  const int my_i = i0 + l32;
+  const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
+  const int n_ct = (a.p + kKvTile - 1) / kKvTile;
+  const int nt = n_ct + wg_last / kKvTile + 1;
+
+  const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
+  kv_issue<D>(K0, V0, 0, n_ct, src, wave, lane);
+
+  // Q^T and dO^T as B operands: lane (q + 32 hl) holds row q, 8 columns per k-step.
+  bf16x8 qf[NKS], of[NKS];
+  const int qi = min(my_i, a.n - 1);
+  {
+    const size_t off = (((size_t)b * a.n + qi) * a.Hq + h) * D + 8 * hl;
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + off;
+    const bf16* op = reinterpret_cast<const bf16*>(a.dout) + off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + 16 * ks);
+      of[ks] = *reinterpret_cast<const bf16x8*>(op + 16 * ks);
+    }
+  }
+  const size_t li = ((size_t)b * a.Hq + h) * a.n + qi;
+  const float lse2 = a.lse2[li];
+  const float dl = a.delta[li];
+  const float c = a.scale_log2;
+  const float scale = a.scale;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  auto compute = [&](const bf16* Ks, const bf16* Vs, const KvTile& f) {
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[kh][r] = 0.f; dp[kh][r] = 0.f; }
+      const bf16* krow = Ks + t_off<D>(32 * kh + l32, 8 * hl);
+      const bf16* vrow = Vs + t_off<D>(32 * kh + l32, 8 * hl);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s[kh] = M::mma(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), qf[ks], s[kh]);
+        dp[kh] = M::mma(*reinterpret_cast<const bf16x8*>(vrow + 16 * ks), of[ks], dp[kh]);
+      }
+    }
+    const bool need_mask = f.rows < kKvTile || (!f.cart && f.j0 + kKvTile - 1 > i0);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float arg = fmaf(s[kh][r], c, -lse2);
+        if (need_mask) {
+          const int key = 32 * kh + d_row(r, hl);
+          const bool vis = key < f.rows && (f.cart || f.j0 + key <= my_i);
+          arg = vis ? arg : -INFINITY;
+        }
+        const float p_ = __builtin_amdgcn_exp2f(arg);
+        dp[kh][r] = p_ * (dp[kh][r] - dl) * scale;      // dS^T
+      }
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x8 sf = pack_regs<bf16>(dp[kh], m);
+        const int r0 = 32 * kh + 16 * m + 4 * hl;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int cc = 32 * db + c0base;
+          const bf16x8 ka = cat8(tr_col4(Ks, TS, r0, cc, lane), tr_col4(Ks, TS, r0 + 8, cc, lane));
+          acc[db] = M::mma(ka, sf, acc[db]);
+        }
+      }
+  };
+
+  for (int t = 0; t < nt; t += 2) {
+    CART_WAIT_VMCNT(0);
+    lds_barrier();
+    if (t + 1 < nt) kv_issue<D>(K1, V1, t + 1, n_ct, src, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const KvTile f = kv_tile(t, n_ct, a.p, a.n);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(K0, V0, f);
+    }
+    if (t + 1 >= nt) break;
+    CART_WAIT_VMCNT(0);
+    lds_barrier();
+    if (t + 2 < nt) kv_issue<D>(K0, V0, t + 2, n_ct, src, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(K1, V1, f);
+    }
+  }
+
+  if (!wave_active || my_i >= a.n) return;
+  bf16* dqp = reinterpret_cast<bf16*>(a.dq) + (((size_t)b * a.n + my_i) * a.Hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      bf16x4 o4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[db][4 * cc + e];
+      *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * cc + 4 * hl) = o4;
+    }
+}
+
 // D_i = dO_i . O_i for every (b, h, i), and dQ accumulator := 0.
 // One wave per (b, i, h) row; 4 rows per workgroup.
 template <typename T, int D>
@@ -761,9 +835,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
     a.delta[li] = acc;
     a.lse2[li] = a.lse[li] * kLog2e;
   }
-  float* dq = a.dq_acc + (size_t)row * D;
+  if (a.zero_dq) {
+    float* dq = a.dq_acc + (size_t)row * D;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) dq[lane + 64 * e] = 0.f;
+    for (int e = 0; e < D / 64; ++e) dq[lane + 64 * e] = 0.f;
+  }
 }
 
 template <typename T>
@@ -824,7 +900,12 @@ BwdPlan plan_bwd(const AttnDims& d) {
   pl.splits_c = s;
   pl.grid_c = d.Hkv * pl.n_ct * s;
   pl.grid_t = d.Hkv * d.B * pl.n_tt;
-  pl.dq_bytes = (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
+  pl.dq_bytes = d.tok_bf16 ? 0 : (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
+  {
+    const FwdPlan fp = plan_fwd(d);   // the dQ kernel uses the forward's query blocks, unsplit
+    pl.hpw = fp.hpw; pl.wph = fp.wph; pl.n_hg = fp.n_hg; pl.n_qb = fp.n_qb;
+    pl.grid_q = d.Hkv * d.B * fp.n_hg * fp.n_qb;
+  }
   pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);   // and as much for lse2
   pl.part_bytes = s > 1 ? (size_t)s * d.p * d.Hkv * d.D * sizeof(float) : 0;
   if (d.tok_bf16 && !d.row_bf16 && d.p > 0)
@@ -838,18 +919,41 @@ size_t bwd_workspace_bytes(const AttnDims& d) {
          2 * align256(pl.part_bytes);
 }
 
-template <typename T, int D, typename Main>
-static hipError_t launch_bwd_t(const BwdArgs& a, const BwdPlan& pl, hipStream_t st, Main main) {
+// float32 reference mode: preprocess, generic kernel (dQ by atomics), dQ
+// conversion, split reduction.
+template <int D>
+static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
-  CART_TIMED("bwd_preprocess", st, bwd_preprocess<T, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
+  CART_TIMED("bwd_preprocess", st, bwd_preprocess<float, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_TIMED("attn_bwd", st, main<<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
+  CART_TIMED("attn_bwd", st,
+             attn_bwd_kernel<float, float, D><<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t n4 = (size_t)rows * D / 4;
   CART_TIMED("bwd_dq_finalize", st,
-             bwd_dq_finalize<T><<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(
-                 a.dq_acc, reinterpret_cast<T*>(a.dq), n4));
+             bwd_dq_finalize<float><<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(
+                 a.dq_acc, reinterpret_cast<float*>(a.dq), n4));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (pl.splits_c > 1) {
+    const size_t total = (size_t)a.p * a.Hkv * D;
+    CART_TIMED("bwd_cart_reduce", st,
+               bwd_cart_reduce_t<D><<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a));
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+// bf16: preprocess, dK/dV kernel, dQ kernel, split reduction.
+template <int D>
+static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
+  const int rows = a.B * a.n * a.Hq;
+  CART_TIMED("bwd_preprocess", st, bwd_preprocess<bf16, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  CART_TIMED("attn_bwd", st, attn_bwd_kv_kernel<D><<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  CART_TIMED("attn_bwd_dq", st, attn_bwd_dq_kernel<D><<<pl.grid_q, kThreads, 0, st>>>(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.splits_c > 1) {
     const size_t total = (size_t)a.p * a.Hkv * D;
@@ -896,11 +1000,10 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.accumulate = accumulate ? 1 : 0;
   a.scale = d.scale;
   a.scale_log2 = d.scale * kLog2e;
-  if (d.tok_bf16)
-    return d.D == 128 ? launch_bwd_t<bf16, 128>(a, pl, st, attn_bwd_bf16_kernel<128>)
-                      : launch_bwd_t<bf16, 64>(a, pl, st, attn_bwd_bf16_kernel<64>);
-  return d.D == 128 ? launch_bwd_t<float, 128>(a, pl, st, attn_bwd_kernel<float, float, 128>)
-                    : launch_bwd_t<float, 64>(a, pl, st, attn_bwd_kernel<float, float, 64>);
+  a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb;
+  a.zero_dq = d.tok_bf16 ? 0 : 1;
+  if (d.tok_bf16) return d.D == 128 ? launch_bwd_bf16<128>(a, pl, st) : launch_bwd_bf16<64>(a, pl, st);
+  return d.D == 128 ? launch_bwd_f32<128>(a, pl, st) : launch_bwd_f32<64>(a, pl, st);
 }
 
 }  // namespace cartattn

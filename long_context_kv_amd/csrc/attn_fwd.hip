@@ -27,6 +27,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "kvtiles.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
 
@@ -296,38 +297,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 //    max has grown by more than 2^8 since its last rescale (exact: the
 //    probabilities are then at most 256, well inside f32 and bf16 range).
 // Cartridge rows arrive as bf16 (f32 master rows are cast first).
-template <int D>
-struct FwdTile {
-  int j0, rows;
-  bool cart;
-};
-
-template <int D>
-__device__ __forceinline__ FwdTile<D> fwd_tile(int t, int n_ct, int p, int n) {
-  FwdTile<D> f;
-  f.cart = t < n_ct;
-  f.j0 = f.cart ? t * kBN : (t - n_ct) * kBN;
-  f.rows = f.cart ? min(kBN, p - f.j0) : min(kBN, n - f.j0);
-  return f;
-}
-
-template <int D>
-__device__ __forceinline__ void fwd_issue(bf16* Kst, bf16* Vst, int t, int n_ct, const FwdArgs& a,
-                                          int kv, const bf16* kt, const bf16* vt, int wave,
-                                          int lane) {
-  const FwdTile<D> f = fwd_tile<D>(t, n_ct, a.p, a.n);
-  const size_t row_stride = (size_t)a.Hkv * D;
-  const bf16* kb = f.cart ? reinterpret_cast<const bf16*>(a.k_cart) + ((size_t)f.j0 * a.Hkv + kv) * D
-                          : kt + (size_t)f.j0 * row_stride;
-  const bf16* vb = f.cart ? reinterpret_cast<const bf16*>(a.v_cart) + ((size_t)f.j0 * a.Hkv + kv) * D
-                          : vt + (size_t)f.j0 * row_stride;
-  dma_tile<D, kBN>(Kst, kb, row_stride, f.rows, wave, lane);
-  dma_tile<D, kBN>(Vst, vb, row_stride, f.rows, wave, lane);
-}
-
 // One key tile of the online softmax for one wave (32 queries x 64 keys).
 template <int D>
-__device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, const FwdTile<D>& f,
+__device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, const KvTile& f,
                                             const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
                                             float& m_ref, float& l_run, float c, int i0,
                                             int my_i, int lane) {
@@ -438,9 +410,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int t_begin = (int)((long long)split * nt / a.n_splits);
   const int t_end = (int)((long long)(split + 1) * nt / a.n_splits);
 
-  const bf16* kt = reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
-  const bf16* vt = reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
-  if (t_begin < t_end) fwd_issue<D>(K0, V0, t_begin, n_ct, a, kv, kt, vt, wave, lane);
+  const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
+  if (t_begin < t_end) kv_issue<D>(K0, V0, t_begin, n_ct, src, wave, lane);
 
   bf16x8 qf[NKS];
   {
@@ -464,20 +435,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int t = t_begin; t < t_end; t += 2) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 1 < t_end) fwd_issue<D>(K1, V1, t + 1, n_ct, a, kv, kt, vt, wave, lane);
+    if (t + 1 < t_end) kv_issue<D>(K1, V1, t + 1, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
     {
-      const FwdTile<D> f = fwd_tile<D>(t, n_ct, a.p, a.n);
+      const KvTile f = kv_tile(t, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31))
         fwd_compute<D>(K0, V0, f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
     }
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 2 < t_end) fwd_issue<D>(K0, V0, t + 2, n_ct, a, kv, kt, vt, wave, lane);
+    if (t + 2 < t_end) kv_issue<D>(K0, V0, t + 2, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
-      const FwdTile<D> f = fwd_tile<D>(t + 1, n_ct, a.p, a.n);
+      const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31))
         fwd_compute<D>(K1, V1, f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
     }

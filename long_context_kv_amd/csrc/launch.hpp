@@ -30,6 +30,7 @@ hipError_t launch_fwd(const AttnDims& a, const void* q, const void* k_tok, const
 
 struct BwdPlan {
   int n_ct, n_tt, nqt, splits_c, grid_c, grid_t;
+  int hpw, wph, n_hg, n_qb, grid_q;   // query-major dQ kernel
   size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes;
 };
 BwdPlan plan_bwd(const AttnDims& a);
