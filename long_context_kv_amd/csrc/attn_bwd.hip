@@ -420,21 +420,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   constexpr int NDB = D / 32;
   constexpr int TS = tstr<D>();
   constexpr int CPR = TS / 8;
-  constexpr int QBLK = kBQ * TS / 512;
+  constexpr int QTILE = tile_elems<D, kBQ>();
+  constexpr int QBLK = QTILE / 512;
   constexpr int QPW = (QBLK + 3) / 4;
-  // 3-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32]
-  constexpr int STAGE = 2 * kBQ * TS + 2 * 2 * kBQ;   // bf16 elements per stage
+  // 3-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
+  // A stage is read while a copy fills another one, so every LDS read of the
+  // unit loop is issued by the inline-assembly helpers, with explicit waits.
+  constexpr int STAGE = 2 * QTILE + 2 * 2 * kBQ;   // bf16 elements per stage
+  constexpr int O_OFF = 2 * QTILE;                  // byte offset of dO in a stage
+  constexpr int L_OFF = 4 * QTILE;                  // byte offset of lse / D
   __shared__ __align__(16) bf16 ring[3 * STAGE];
   auto Qst = [&](int st) { return ring + st * STAGE; };
-  auto Ost = [&](int st) { return ring + st * STAGE + kBQ * TS; };
-  auto Lst = [&](int st) { return reinterpret_cast<float*>(ring + st * STAGE + 2 * kBQ * TS); };
+  auto Ost = [&](int st) { return ring + st * STAGE + QTILE; };
+  auto Lst = [&](int st) { return reinterpret_cast<float*>(ring + st * STAGE + 2 * QTILE); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int c0base = 16 * ((lane >> 4) & 1);
 
   // ---- work item
   const int per_kv = a.n_ct * a.splits_c + a.B * a.n_tt;
@@ -465,6 +469,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
                            : reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
   const bf16* vbase = cart ? reinterpret_cast<const bf16*>(a.v_cart) + kv * D
                            : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+  // Queries i visible to this lane's key: lo <= i < n (an empty range for a
+  // key past the end of its rows).
+  const int vis_lo = !key_ok ? a.n : (cart ? 0 : my_key);
+  const uint32_t vis_span = (uint32_t)(a.n - vis_lo);
 
   // ---- unit counters
   const int qt0 = cart ? 0 : tile * (kBNB / kBQ);
@@ -498,30 +506,29 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     c_roff[k] = r * q_row_bytes;
     c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
   }
-  auto issue = [&](const Unit& x, bf16* Qst, bf16* Ost, float* Lst) {
+  auto issue = [&](const Unit& x, bf16* Qs, bf16* Os, float* Ls) {
     const int h = kv * a.g + x.hin;
     const int i0 = x.qt * kBQ;
     const int rows = min(kBQ, a.n - i0);
     const int lim = (rows - 1) * q_row_bytes;
     const size_t base = (((size_t)x.bb * a.n + i0) * a.Hq + h) * D * 2;
-    const char* qb = reinterpret_cast<const char*>(a.q) + base;
-    const char* ob = reinterpret_cast<const char*>(a.dout) + base;
+    const buf_rsrc rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, lim + D * 2);
+    const buf_rsrc ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + base, lim + D * 2);
 #pragma unroll
     for (int k = 0; k < QPW; ++k) {
       const int blk = 4 * k + wave;
       if (blk < QBLK) {
-        const int off = min(c_roff[k], lim) + c_coff[k];
-        __builtin_amdgcn_global_load_lds((const void*)(qb + off),
-            (__attribute__((address_space(3))) void*)(Qst + blk * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(ob + off),
-            (__attribute__((address_space(3))) void*)(Ost + blk * 512), 16, 0, 0);
+        const uint32_t off = min(c_roff[k], lim) + c_coff[k];
+        dma16(rq, off, Qs + blk * 512);
+        dma16(ro, off, Os + blk * 512);
       }
     }
     if (wave == 0) {
-      const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0 + min(l32, rows - 1);
-      const float* g = (lane < 32) ? a.lse2 + li : a.delta + li;
-      __builtin_amdgcn_global_load_lds((const void*)g,
-                                       (__attribute__((address_space(3))) void*)Lst, 4, 0, 0);
+      // lanes 0..31 copy lse*log2(e), lanes 32..63 copy D
+      const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0;
+      const uint32_t off = 4 * min(l32, rows - 1);
+      if (lane < 32) dma4(make_rsrc(a.lse2 + li, 4 * rows), off, Ls);
+      else dma4(make_rsrc(a.delta + li, 4 * rows), off, Ls);
     }
   };
 
@@ -543,66 +550,122 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
   const float c = a.scale_log2;
-  const float scale = a.scale;
 
-  // S = Q K^T and dP = dO V^T of one unit (rows = queries of the unit,
-  // columns = this wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)).
-  auto sdp = [&](const bf16* Qs, const bf16* Os, f32x16& s, f32x16& dp) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + t_off<D>(l32, 16 * ks + 8 * hl));
-      const bf16x8 oa = *reinterpret_cast<const bf16x8*>(Os + t_off<D>(l32, 16 * ks + 8 * hl));
-      s = M::mma(qa, kf[ks], s);
-      dp = M::mma(oa, vf[ks], dp);
-    }
+  // Per-lane LDS byte offsets inside a stage: the row fragment (row l32,
+  // 8 elements at 8 hl) and the transpose strip (tr_col4's lane pattern for
+  // rows 4 hl .., columns 16 ((lane >> 4) & 1) ..).
+  const uint32_t row_lane = 2 * t_off<D>(l32, 8 * hl);
+  const uint32_t tr_lane = 2 * ((4 * hl + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  const uint32_t ld_lane = 16 * hl;
+
+  // lse*log2(e) and D of the 16 queries of a lane's result registers
+  // (query 8 c4 + 4 hl + e of the unit for register 4 c4 + e): 8 reads.
+  struct LD { f32x4 l[4], d[4]; };
+  auto read_ld = [&](uint32_t stage, LD& x) {
+    const uint32_t base = stage + L_OFF + ld_lane;
+    static_for<4>([&](auto C4) {
+      constexpr int c4 = decltype(C4)::value;
+      x.l[c4] = lds_read16<32 * c4>(base);
+      x.d[c4] = lds_read16<4 * kBQ + 32 * c4>(base);
+    });
   };
-  // P = exp2(s c - lse2) and dS = scale P (dP - D), packed to bf16 A operands.
-  auto softmax = [&](const Unit& x, const float* Ls, f32x16& pv, f32x16& dsv,
-                     bf16x8 (&pf)[2], bf16x8 (&sf)[2]) {
+  auto tie_ld = [&](LD& x) {
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) { lds_tie(x.l[c4]); lds_tie(x.d[c4]); }
+  };
+  // P = exp2(S c - lse2) and G = P (dP - D) (the softmax scale is applied
+  // to dK once at the end), packed to bf16 A operands. s holds S and g holds
+  // dP on entry. Masked pairs (query not visible from the key) get P = 0.
+  auto softmax = [&](const Unit& x, const LD& ld, f32x16& s, f32x16& g, bf16x8 (&pf)[2],
+                     bf16x8 (&sf)[2]) {
     const int i0 = x.qt * kBQ;
     const bool need_mask = (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
+    const uint32_t rel = (uint32_t)(i0 + 4 * hl - vis_lo);
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(Ls + 8 * c4 + 4 * hl);
-      const float4 d4 = *reinterpret_cast<const float4*>(Ls + kBQ + 8 * c4 + 4 * hl);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * c4 + e;
-        float arg = fmaf(pv[r], c, -lv[e]);       // pv holds S on entry
-        if (need_mask) {
-          const int i = i0 + 8 * c4 + 4 * hl + e;
-          const bool vis = key_ok && i < a.n && (cart || my_key <= i);
-          arg = vis ? arg : -INFINITY;
-        }
-        const float p_ = __builtin_amdgcn_exp2f(arg);
-        pv[r] = p_;
-        dsv[r] = p_ * (dsv[r] - dvv[e]) * scale;   // dsv holds dP on entry
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int c4 = r >> 2, e = r & 3;
+      const float lv = ld.l[c4][e];
+      const float dl = ld.d[c4][e];
+      float arg = fmaf(s[r], c, -lv);
+      if (need_mask) arg = (rel + (uint32_t)(8 * c4 + e) < vis_span) ? arg : -INFINITY;
+      const float p_ = __builtin_amdgcn_exp2f(arg);
+      s[r] = p_;
+      g[r] = p_ * (g[r] - dl);
     }
-    pf[0] = pack_regs<bf16>(pv, 0);
-    pf[1] = pack_regs<bf16>(pv, 1);
-    sf[0] = pack_regs<bf16>(dsv, 0);
-    sf[1] = pack_regs<bf16>(dsv, 1);
+    pf[0] = pack_regs<bf16>(s, 0);
+    pf[1] = pack_regs<bf16>(s, 1);
+    sf[0] = pack_regs<bf16>(g, 0);
+    sf[1] = pack_regs<bf16>(g, 1);
   };
-  // dV += P^T dO, dK += dS^T Q (B operands by transpose reads of the tiles).
-  auto dvdk = [&](const bf16* Qs, const bf16* Os, const bf16x8 (&pf)[2], const bf16x8 (&sf)[2]) {
+  // Transpose fragment f = m * NDB + db (queries 16 m .., columns 32 db ..)
+  // of the dO and Q tiles of a stage: 4 reads.
+  struct TrOps { bf16x8 o[NKS], q[NKS]; };
+  auto tr_frag = [&](uint32_t stage, auto F, TrOps& t) {
+    constexpr int f = decltype(F)::value;
+    constexpr int off = 2 * (16 * (f / NDB) * TS + 32 * (f % NDB));
+    const uint32_t base = stage + tr_lane;
+    t.o[f] = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + 16 * TS>(base));
+    t.q[f] = cat8(lds_tr4<off>(base), lds_tr4<off + 16 * TS>(base));
+  };
+  // One MFMA stream over k-steps ks: S = Q K^T and dP = dO V^T of the next
+  // unit (rows = queries, columns = this wave's keys; lane (key + 32 hl), reg
+  // r <-> query d_row(r, hl)), dV += P^T dO and dK += G^T Q of the current
+  // unit with operand fragment ks, then the transpose reads of the next
+  // unit's fragment ks into the registers that fragment just left. The LDS
+  // reads of k-step ks are, in this order: Q / dO rows of step ks+1 (2), then
+  // fragment ks (4). Before the MFMAs of step ks only reads issued after the
+  // rows of step ks may be pending: 2 at ks = 0, 6 in between, 4 at the last
+  // step. The scheduling fences keep that order. With NEXT false only dV, dK
+  // of the current unit run, after a full wait.
+  auto stream = [&](auto next_tag, uint32_t stage, TrOps& t, const bf16x8 (&pf)[2],
+                    const bf16x8 (&sf)[2], f32x16& s, f32x16& dp) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    bf16x8 qa[2], oa[2];
+    const uint32_t rbase = stage + row_lane;
+    auto rd = [&](auto KS, int slot) {
+      constexpr int ks = decltype(KS)::value;
+      qa[slot] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(rbase));
+      oa[slot] = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(rbase));
+    };
+    if constexpr (NEXT) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int q0 = 16 * m + 4 * hl;
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      rd(std::integral_constant<int, 0>{}, 0);
+    } else {
+      lds_wait<0>();
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int cc = 32 * db + c0base;
-        const bf16x8 ob = cat8(tr_col4(Os, TS, q0, cc, lane), tr_col4(Os, TS, q0 + 8, cc, lane));
-        const bf16x8 qb = cat8(tr_col4(Qs, TS, q0, cc, lane), tr_col4(Qs, TS, q0 + 8, cc, lane));
-        dv[db] = M::mma(pf[m], ob, dv[db]);
-        dk[db] = M::mma(sf[m], qb, dk[db]);
-      }
+      for (int f = 0; f < NKS; ++f) { lds_tie(t.o[f]); lds_tie(t.q[f]); }
     }
+    static_for<NKS>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      if constexpr (NEXT) {
+        if constexpr (ks + 1 < NKS) rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks == 0) lds_wait<2>();
+        else if constexpr (ks + 1 < NKS) lds_wait<6>();
+        else lds_wait<4>();
+        lds_tie(qa[ks & 1]);
+        lds_tie(oa[ks & 1]);
+        lds_tie(t.o[ks]);
+        lds_tie(t.q[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+        s = M::mma(qa[ks & 1], kf[ks], s);
+        dp = M::mma(oa[ks & 1], vf[ks], dp);
+      }
+      constexpr int m = ks / NDB, db = ks % NDB;
+      dv[db] = M::mma(pf[m], t.o[ks], dv[db]);
+      dk[db] = M::mma(sf[m], t.q[ks], dk[db]);
+      if constexpr (NEXT) {
+        __builtin_amdgcn_sched_barrier(0);
+        tr_frag(stage, KS, t);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  const uint32_t ring_base = lds_addr(ring);
+  auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
 
   if (u_begin < u_end) {
     const int nu = u_end - u_begin;
@@ -611,13 +674,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     bf16x8 pf[2], sf[2];
+    TrOps t;
     {
+      // unit 0: S and dP, its transpose fragments, its softmax (no copy
+      // targets stage 0 meanwhile)
       f32x16 s, dp;
-      sdp(Qst(0), Ost(0), s, dp);
-      softmax(cu, Lst(0), s, dp, pf, sf);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      const uint32_t st0 = stage_addr(0);
+      static_for<NKS>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        bf16x8 qa = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(st0 + row_lane));
+        bf16x8 oa = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(st0 + row_lane));
+        tr_frag(st0, KS, t);
+        lds_wait<4>();
+        lds_tie(qa);
+        lds_tie(oa);
+        s = M::mma(qa, kf[ks], s);
+        dp = M::mma(oa, vf[ks], dp);
+      });
+      LD ld;
+      read_ld(st0, ld);
+      lds_wait<0>();
+      tie_ld(ld);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax(cu, ld, s, dp, pf, sf);
     }
-    // step k (k = 0 .. nu-2): unit k in stage k%3, unit k+1 in stage (k+1)%3,
-    // the copy of unit k+2 goes to stage (k+2)%3
+    // Step k (k = 0 .. nu-2): unit k in stage k%3 (its transpose fragments
+    // already in t), unit k+1 in stage (k+1)%3, and the copy of unit k+2 goes
+    // to stage (k+2)%3, last read in step k-1, which every wave has left at
+    // the barrier.
     Unit un = u1, uf = next(u1);
     int sk = 0;
     for (int k = 0; k < nu - 1; ++k) {
@@ -625,21 +711,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       const int sf_ = sn == 2 ? 0 : sn + 1;
       CART_WAIT_VMCNT(0);
       lds_barrier();
+      const uint32_t stn = stage_addr(sn);
+      LD ld;
+      read_ld(stn, ld);
+      __builtin_amdgcn_sched_barrier(0);
       if (k + 2 < nu) issue(uf, Qst(sf_), Ost(sf_), Lst(sf_));
       __builtin_amdgcn_sched_barrier(0);
       f32x16 s, dp;
-      sdp(Qst(sn), Ost(sn), s, dp);
+      stream(Yes{}, stn, t, pf, sf, s, dp);
+      // full wait: no value read by assembly may be copied or moved by the
+      // compiler (say, at the loop back edge) before its data has arrived
+      lds_wait<0>();
+      tie_ld(ld);
       __builtin_amdgcn_sched_barrier(0);
-      dvdk(Qst(sk), Ost(sk), pf, sf);
-      softmax(un, Lst(sn), s, dp, pf, sf);
+      softmax(un, ld, s, dp, pf, sf);
       un = uf;
       uf = next(uf);
       sk = sn;
     }
-    dvdk(Qst(sk), Ost(sk), pf, sf);
+    {
+      f32x16 s, dp;
+      stream(No{}, 0u, t, pf, sf, s, dp);
+    }
   }
 
-  // ---- dK (scale already inside dS), dV
+  // ---- dK (times the softmax scale), dV
+  const float scale = a.scale;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int j = j0 + 32 * wave + d_row(r, hl);
@@ -647,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int col = 32 * db + l32;
-      const float gk = dk[db][r];
+      const float gk = dk[db][r] * scale;
       const float gv = dv[db][r];
       if (cart) {
         const size_t o = ((size_t)j * a.Hkv + kv) * D + col;
@@ -680,10 +777,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int TS = tstr<D>();
-  __shared__ __align__(16) bf16 K0[kKvTile * TS];
-  __shared__ __align__(16) bf16 V0[kKvTile * TS];
-  __shared__ __align__(16) bf16 K1[kKvTile * TS];
-  __shared__ __align__(16) bf16 V1[kKvTile * TS];
+  __shared__ __align__(16) bf16 K0[tile_elems<D, kKvTile>()];
+  __shared__ __align__(16) bf16 V0[tile_elems<D, kKvTile>()];
+  __shared__ __align__(16) bf16 K1[tile_elems<D, kKvTile>()];
+  __shared__ __align__(16) bf16 V1[tile_elems<D, kKvTile>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

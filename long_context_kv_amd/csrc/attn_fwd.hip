@@ -379,10 +379,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __align__(16) bf16 K0[kBN * tstr<D>()];
-  __shared__ __align__(16) bf16 V0[kBN * tstr<D>()];
-  __shared__ __align__(16) bf16 K1[kBN * tstr<D>()];
-  __shared__ __align__(16) bf16 V1[kBN * tstr<D>()];
+  __shared__ __align__(16) bf16 K0[tile_elems<D, kBN>()];
+  __shared__ __align__(16) bf16 V0[tile_elems<D, kBN>()];
+  __shared__ __align__(16) bf16 K1[tile_elems<D, kBN>()];
+  __shared__ __align__(16) bf16 V1[tile_elems<D, kBN>()];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

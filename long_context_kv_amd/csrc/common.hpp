@@ -17,6 +17,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace cartattn {
 
 typedef __bf16 bf16;
@@ -169,44 +172,121 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 namespace cartattn {
 
 // ---- LDS tiles for the bf16 kernels -------------------------------------
-// A tile of R rows x D bf16 is stored with rows padded to TSTR = D + 16
-// elements. The 8-dword bank shift per row makes both access patterns of the
-// kernels conflict-free: 16-byte row reads with one row per lane, and
-// transpose reads (4 rows x 32 bytes per 16-lane group). Every fragment
-// address is then a per-lane base plus a compile-time offset.
+// A tile of R rows x D bf16 is stored with rows padded to TSTR elements. For
+// D = 128 the stride is 152 elements (76 dwords): measured on gfx950 it lets
+// both access patterns of the kernels run near the LDS peak or at the best
+// rate any plain padding reaches (16-byte row reads with one row per lane
+// about 230 B/clk per CU, transpose reads of 4 rows x 32 bytes per 16-lane
+// group about 93 B/clk; a 144-element stride gave 124 and 92). Every
+// fragment address is a per-lane base plus a compile-time offset.
 template <int D>
-constexpr int tstr() { return D + 16; }
+constexpr int tstr() { return D + 24; }
+
+// Elements allocated for a tile of NROWS rows: whole 1 KiB blocks, so that
+// the asynchronous copy of the last block stays inside the allocation.
+template <int D, int NROWS>
+constexpr int tile_elems() { return (NROWS * tstr<D>() + 511) / 512 * 512; }
 
 template <int D>
 __device__ __forceinline__ int t_off(int r, int col) { return r * tstr<D>() + col; }
 
-// Issue this wave's share of an asynchronous global->LDS copy of a tile of
-// NROWS rows x D bf16 (global rows `row_stride` elements apart) into a padded
-// LDS tile. The tile is NROWS * TSTR * 2 bytes, written by 1 KiB direct loads
-// (lane l of one load lands at byte 16*l of that load's block) spread over
-// the 4 waves. Lanes whose 16 bytes fall on row padding re-read a chunk of
-// their row, and rows at or past `rows` re-read row rows-1 (finite data the
-// caller masks), so no address leaves the source.
+// Asynchronous global->LDS copies use buffer loads with the LDS bit (MUBUF
+// encoding): lane l of one instruction writes its 16 bytes to byte 16*l past
+// the wave-uniform LDS address, and bytes at or past `bytes` of the buffer
+// read as zero. (The FLAT-encoded global_load_lds form would also count
+// against the LDS counter, which makes every later LDS wait a full drain.)
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ void dma16(buf_rsrc r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(buf_rsrc r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
+                                           (int)voff, 0, 0, 0);
+}
+
+// Issue this wave's share of an asynchronous copy of a tile of NROWS rows x D
+// bf16 (global rows `row_stride` elements apart) into a padded LDS tile of
+// tile_elems<D, NROWS>() elements, written by 1 KiB loads spread over the 4
+// waves. Lanes whose 16 bytes fall on row padding re-read a chunk of their
+// row, and rows at or past `rows` (including the rounding past NROWS) re-read
+// row rows-1 (finite data the caller masks), so no offset leaves the source
+// rows.
 template <int D, int NROWS>
 __device__ __forceinline__ void dma_tile(bf16* lds, const bf16* src, size_t row_stride, int rows,
                                          int wave, int lane) {
   constexpr int CPR = tstr<D>() / 8;                  // 16-byte chunks per padded row
-  constexpr int NBLK = NROWS * tstr<D>() / 512;       // 1 KiB loads for the tile
-  static_assert(NROWS * tstr<D>() % 512 == 0, "tile must be whole 1 KiB blocks");
+  constexpr int NBLK = tile_elems<D, NROWS>() / 512;   // 1 KiB loads for the tile
+  const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
+  const buf_rsrc r = make_rsrc(src, (uint32_t)(rows - 1) * rs_bytes + D * 2);
 #pragma unroll
   for (int k = 0; k < (NBLK + 3) / 4; ++k) {
     const int blk = k * 4 + wave;
     if (blk < NBLK) {
       const int chunk = blk * 64 + lane;
-      const int r = chunk / CPR;
+      const int rr = min(chunk / CPR, rows - 1);
       int cc = chunk % CPR;
       cc = cc < D / 8 ? cc : 0;
-      const int rr = r < rows ? r : rows - 1;
-      const bf16* g = src + (size_t)rr * row_stride + cc * 8;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)g, (__attribute__((address_space(3))) void*)(lds + blk * 512), 16, 0, 0);
+      dma16(r, (uint32_t)rr * rs_bytes + cc * 16, lds + blk * 512);
     }
   }
+}
+
+// ---- LDS reads issued as inline assembly --------------------------------
+// The compiler neither orders these after copies into LDS that are still in
+// flight nor tracks their completion: the caller guarantees that no pending
+// copy targets the bytes read, and waits with lds_wait<N>() (at most N LDS
+// operations of the wave still pending) before using a result. They are used
+// where a read of one ring stage must overlap a copy into another stage.
+// `base` is a per-lane LDS byte address, OFF a compile-time byte offset.
+// Register operands of these statements are float vectors: with integer
+// vector operands this compiler loses all but the first element.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int OFF>
+__device__ __forceinline__ f32x4 lds_read16(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  f32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF));
+  return v;
+}
+// ds_read_b64_tr_b16 (lane mapping as in tr_col4).
+template <int OFF>
+__device__ __forceinline__ bf16x4 lds_tr4(uint32_t base) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  f32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF));
+  return __builtin_bit_cast(bf16x4, v);
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+  asm volatile("s_waitcnt lgkmcnt(%0)" : : "n"(N));
+}
+// After lds_wait: pass a value read by one of the helpers above through an
+// empty volatile statement, so that every use of it (and any reuse of its
+// registers) comes after the wait. Volatile statements keep their order.
+__device__ __forceinline__ void lds_tie(f32x4& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void lds_tie(bf16x8& x) {
+  f32x4 v = __builtin_bit_cast(f32x4, x);
+  asm volatile("" : "+v"(v));
+  x = __builtin_bit_cast(bf16x8, v);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Workgroup barrier that orders LDS only: outstanding global stores and
