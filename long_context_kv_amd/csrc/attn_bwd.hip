@@ -573,53 +573,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) { lds_tie(x.l[c4]); lds_tie(x.d[c4]); }
   };
-  // P = exp2(S c - lse2) and G = P (dP - D) (the softmax scale is applied
-  // to dK once at the end), packed to bf16 A operands. s holds S and g holds
-  // dP on entry. Masked pairs (query not visible from the key) get P = 0.
-  auto softmax = [&](const Unit& x, const LD& ld, f32x16& s, f32x16& g, bf16x8 (&pf)[2],
-                     bf16x8 (&sf)[2]) {
+  auto unit_needs_mask = [&](const Unit& x) {
     const int i0 = x.qt * kBQ;
-    const bool need_mask = (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
-    const uint32_t rel = (uint32_t)(i0 + 4 * hl - vis_lo);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int c4 = r >> 2, e = r & 3;
-      const float lv = ld.l[c4][e];
-      const float dl = ld.d[c4][e];
-      float arg = fmaf(s[r], c, -lv);
-      if (need_mask) arg = (rel + (uint32_t)(8 * c4 + e) < vis_span) ? arg : -INFINITY;
-      const float p_ = __builtin_amdgcn_exp2f(arg);
-      s[r] = p_;
-      g[r] = p_ * (g[r] - dl);
-    }
-    pf[0] = pack_regs<bf16>(s, 0);
-    pf[1] = pack_regs<bf16>(s, 1);
-    sf[0] = pack_regs<bf16>(g, 0);
-    sf[1] = pack_regs<bf16>(g, 1);
+    return (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
   };
+  // Softmax of result register r: P = exp2(S c - lse2) and G = P (dP - D)
+  // in place (the softmax scale is applied to dK once at the end). Masked
+  // pairs (query not visible from the key) get P = 0.
+  auto softmax_elem = [&](auto MASK, int r, uint32_t rel, const LD& ld, f32x16& s, f32x16& g) {
+    const int c4 = r >> 2, e = r & 3;
+    float arg = fmaf(s[r], c, -ld.l[c4][e]);
+    if constexpr (decltype(MASK)::value)
+      arg = (rel + (uint32_t)(8 * c4 + e) < vis_span) ? arg : -INFINITY;
+    const float p_ = __builtin_amdgcn_exp2f(arg);
+    s[r] = p_;
+    g[r] = p_ * (g[r] - ld.d[c4][e]);
+  };
+  auto mask_rel = [&](const Unit& x) { return (uint32_t)(x.qt * kBQ + 4 * hl - vis_lo); };
   // Transpose fragment f = m * NDB + db (queries 16 m .., columns 32 db ..)
   // of the dO and Q tiles of a stage: 4 reads.
-  struct TrOps { bf16x8 o[NKS], q[NKS]; };
-  auto tr_frag = [&](uint32_t stage, auto F, TrOps& t) {
+  struct TrOp { bf16x8 o, q; };
+  auto tr_frag = [&](uint32_t stage, auto F, TrOp& t) {
     constexpr int f = decltype(F)::value;
     constexpr int off = 2 * (16 * (f / NDB) * TS + 32 * (f % NDB));
     const uint32_t base = stage + tr_lane;
-    t.o[f] = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + 16 * TS>(base));
-    t.q[f] = cat8(lds_tr4<off>(base), lds_tr4<off + 16 * TS>(base));
+    t.o = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + 16 * TS>(base));
+    t.q = cat8(lds_tr4<off>(base), lds_tr4<off + 16 * TS>(base));
   };
-  // One MFMA stream over k-steps ks: S = Q K^T and dP = dO V^T of the next
-  // unit (rows = queries, columns = this wave's keys; lane (key + 32 hl), reg
-  // r <-> query d_row(r, hl)), dV += P^T dO and dK += G^T Q of the current
-  // unit with operand fragment ks, then the transpose reads of the next
-  // unit's fragment ks into the registers that fragment just left. The LDS
-  // reads of k-step ks are, in this order: Q / dO rows of step ks+1 (2), then
-  // fragment ks (4). Before the MFMAs of step ks only reads issued after the
-  // rows of step ks may be pending: 2 at ks = 0, 6 in between, 4 at the last
-  // step. The scheduling fences keep that order. With NEXT false only dV, dK
-  // of the current unit run, after a full wait.
-  auto stream = [&](auto next_tag, uint32_t stage, TrOps& t, const bf16x8 (&pf)[2],
-                    const bf16x8 (&sf)[2], f32x16& s, f32x16& dp) {
-    constexpr bool NEXT = decltype(next_tag)::value;
+  // Phase A: S = Q K^T and dP = dO V^T of one unit (rows = queries, columns
+  // = this wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)).
+  // Two row reads per k-step, one k-step ahead of the MFMAs; it ends with a
+  // full LDS wait, which also retires every read issued before it.
+  auto phase_a = [&](uint32_t stage, f32x16& s, f32x16& dp) {
     bf16x8 qa[2], oa[2];
     const uint32_t rbase = stage + row_lane;
     auto rd = [&](auto KS, int slot) {
@@ -627,37 +612,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       qa[slot] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(rbase));
       oa[slot] = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(rbase));
     };
-    if constexpr (NEXT) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-      rd(std::integral_constant<int, 0>{}, 0);
-    } else {
-      lds_wait<0>();
-#pragma unroll
-      for (int f = 0; f < NKS; ++f) { lds_tie(t.o[f]); lds_tie(t.q[f]); }
-    }
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    rd(std::integral_constant<int, 0>{}, 0);
     static_for<NKS>([&](auto KS) {
       constexpr int ks = decltype(KS)::value;
-      if constexpr (NEXT) {
-        if constexpr (ks + 1 < NKS) rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ks == 0) lds_wait<2>();
-        else if constexpr (ks + 1 < NKS) lds_wait<6>();
-        else lds_wait<4>();
-        lds_tie(qa[ks & 1]);
-        lds_tie(oa[ks & 1]);
-        lds_tie(t.o[ks]);
-        lds_tie(t.q[ks]);
-        __builtin_amdgcn_sched_barrier(0);
-        s = M::mma(qa[ks & 1], kf[ks], s);
-        dp = M::mma(oa[ks & 1], vf[ks], dp);
+      if constexpr (ks + 1 < NKS) {
+        rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
+        lds_wait<2>();
+      } else {
+        lds_wait<0>();
       }
+      lds_tie(qa[ks & 1]);
+      lds_tie(oa[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s = M::mma(qa[ks & 1], kf[ks], s);
+      dp = M::mma(oa[ks & 1], vf[ks], dp);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // Phase B: dV += P^T dO and dK += G^T Q of the unit in `stage` (A operands
+  // pf, sf; B operands by transpose reads, issued one k-step ahead). With
+  // NEXT, each k-step also runs the softmax of 16/NKS of the next unit's
+  // result registers (s, g), so that its VALU work overlaps the MFMAs; the
+  // packed results go to pf2, sf2. Starts and ends with no LDS read pending.
+  auto phase_b = [&](auto NEXT, auto MASK, uint32_t stage, const bf16x8 (&pf)[2],
+                     const bf16x8 (&sf)[2], uint32_t rel, const LD& ld, f32x16& s, f32x16& g,
+                     bf16x8 (&pf2)[2], bf16x8 (&sf2)[2]) {
+    constexpr bool N = decltype(NEXT)::value;
+    TrOp t[2];
+    tr_frag(stage, std::integral_constant<int, 0>{}, t[0]);
+    static_for<NKS>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
       constexpr int m = ks / NDB, db = ks % NDB;
-      dv[db] = M::mma(pf[m], t.o[ks], dv[db]);
-      dk[db] = M::mma(sf[m], t.q[ks], dk[db]);
-      if constexpr (NEXT) {
-        __builtin_amdgcn_sched_barrier(0);
-        tr_frag(stage, KS, t);
+      if constexpr (ks + 1 < NKS) {
+        tr_frag(stage, std::integral_constant<int, ks + 1>{}, t[(ks + 1) & 1]);
+        lds_wait<4>();
+      } else {
+        lds_wait<0>();
+      }
+      lds_tie(t[ks & 1].o);
+      lds_tie(t[ks & 1].q);
+      __builtin_amdgcn_sched_barrier(0);
+      dv[db] = M::mma(pf[m], t[ks & 1].o, dv[db]);
+      dk[db] = M::mma(sf[m], t[ks & 1].q, dk[db]);
+      if constexpr (N) {
+        constexpr int per = 16 / NKS;   // result registers per k-step
+#pragma unroll
+        for (int j = 0; j < per; ++j) softmax_elem(MASK, per * ks + j, rel, ld, s, g);
+        if constexpr ((per * (ks + 1)) % 8 == 0) {
+          constexpr int mm = per * (ks + 1) / 8 - 1;
+          pf2[mm] = pack_regs<bf16>(s, mm);
+          sf2[mm] = pack_regs<bf16>(g, mm);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -674,36 +681,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     bf16x8 pf[2], sf[2];
-    TrOps t;
     {
-      // unit 0: S and dP, its transpose fragments, its softmax (no copy
-      // targets stage 0 meanwhile)
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+      // unit 0 (no copy targets stage 0 meanwhile): S and dP, then softmax
       const uint32_t st0 = stage_addr(0);
-      static_for<NKS>([&](auto KS) {
-        constexpr int ks = decltype(KS)::value;
-        bf16x8 qa = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(st0 + row_lane));
-        bf16x8 oa = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(st0 + row_lane));
-        tr_frag(st0, KS, t);
-        lds_wait<4>();
-        lds_tie(qa);
-        lds_tie(oa);
-        s = M::mma(qa, kf[ks], s);
-        dp = M::mma(oa, vf[ks], dp);
-      });
       LD ld;
       read_ld(st0, ld);
-      lds_wait<0>();
+      f32x16 s, g;
+      phase_a(st0, s, g);
       tie_ld(ld);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax(cu, ld, s, dp, pf, sf);
+      const uint32_t rel = mask_rel(cu);
+      if (unit_needs_mask(cu)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) softmax_elem(Yes{}, r, rel, ld, s, g);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) softmax_elem(No{}, r, rel, ld, s, g);
+      }
+      pf[0] = pack_regs<bf16>(s, 0);
+      pf[1] = pack_regs<bf16>(s, 1);
+      sf[0] = pack_regs<bf16>(g, 0);
+      sf[1] = pack_regs<bf16>(g, 1);
     }
-    // Step k (k = 0 .. nu-2): unit k in stage k%3 (its transpose fragments
-    // already in t), unit k+1 in stage (k+1)%3, and the copy of unit k+2 goes
-    // to stage (k+2)%3, last read in step k-1, which every wave has left at
-    // the barrier.
+    // Step k (k = 0 .. nu-2): unit k in stage k%3, unit k+1 in stage
+    // (k+1)%3, and the copy of unit k+2 goes to stage (k+2)%3, last read in
+    // step k-1, which every wave has left at the barrier. Phase A of unit
+    // k+1, then phase B of unit k with the softmax of unit k+1.
     Unit un = u1, uf = next(u1);
     int sk = 0;
     for (int k = 0; k < nu - 1; ++k) {
@@ -717,21 +719,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       if (k + 2 < nu) issue(uf, Qst(sf_), Ost(sf_), Lst(sf_));
       __builtin_amdgcn_sched_barrier(0);
-      f32x16 s, dp;
-      stream(Yes{}, stn, t, pf, sf, s, dp);
-      // full wait: no value read by assembly may be copied or moved by the
-      // compiler (say, at the loop back edge) before its data has arrived
-      lds_wait<0>();
+      f32x16 s, g;
+      phase_a(stn, s, g);
       tie_ld(ld);
-      __builtin_amdgcn_sched_barrier(0);
-      softmax(un, ld, s, dp, pf, sf);
+      bf16x8 pf2[2], sf2[2];
+      const uint32_t rel = mask_rel(un);
+      const uint32_t stk = stage_addr(sk);
+      // one code path: the mask select costs less than a second copy of
+      // phase B costs in register moves
+      phase_b(Yes{}, Yes{}, stk, pf, sf, rel, ld, s, g, pf2, sf2);
+      pf[0] = pf2[0]; pf[1] = pf2[1];
+      sf[0] = sf2[0]; sf[1] = sf2[1];
       un = uf;
       uf = next(uf);
       sk = sn;
     }
     {
-      f32x16 s, dp;
-      stream(No{}, 0u, t, pf, sf, s, dp);
+      LD ld;
+      f32x16 s, g;
+      bf16x8 pf2[2], sf2[2];
+      phase_b(No{}, No{}, stage_addr(sk), pf, sf, 0u, ld, s, g, pf2, sf2);
     }
   }
 
