@@ -794,7 +794,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
-  const int c0base = 16 * ((lane >> 4) & 1);
 
   int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int qb = a.n_qb - 1 - (lg % a.n_qb); lg /= a.n_qb;
@@ -839,47 +838,101 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  auto compute = [&](const bf16* Ks, const bf16* Vs, const KvTile& f) {
+  // One 64-key tile at LDS byte addresses kst, vst. All LDS reads are issued
+  // by the inline-assembly helpers with explicit waits (the copy of the next
+  // tile into the other stage is in flight meanwhile), one step ahead of the
+  // MFMAs that use them.
+  const uint32_t row_lane = 2 * t_off<D>(l32, 8 * hl);
+  const uint32_t tr_lane = 2 * ((4 * hl + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) +
+                                4 * (lane & 3));
+  auto compute = [&](uint32_t kst, uint32_t vst, const KvTile& f) {
+    // S^T = K Q^T and dP^T = V dO^T for the two 32-key halves: K and V row
+    // fragments (row 32 kh + l32, 8 elements at 16 ks + 8 hl), four reads
+    // per k-step.
     f32x16 s[2], dp[2];
+    {
+      bf16x8 kr[2][2], vr[2][2];
+      auto rd = [&](auto KS, int slot) {
+        constexpr int ks = decltype(KS)::value;
+        kr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kst + row_lane));
+        kr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<2 * 32 * TS + 32 * ks>(kst + row_lane));
+        vr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(vst + row_lane));
+        vr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<2 * 32 * TS + 32 * ks>(vst + row_lane));
+      };
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s[kh][r] = 0.f; dp[kh][r] = 0.f; }
-      const bf16* krow = Ks + t_off<D>(32 * kh + l32, 8 * hl);
-      const bf16* vrow = Vs + t_off<D>(32 * kh + l32, 8 * hl);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s[kh] = M::mma(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), qf[ks], s[kh]);
-        dp[kh] = M::mma(*reinterpret_cast<const bf16x8*>(vrow + 16 * ks), of[ks], dp[kh]);
-      }
+      for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; dp[0][r] = 0.f; dp[1][r] = 0.f; }
+      rd(std::integral_constant<int, 0>{}, 0);
+      static_for<NKS>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        if constexpr (ks + 1 < NKS) {
+          rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
+          lds_wait<4>();
+        } else {
+          lds_wait<0>();
+        }
+        lds_tie(kr[ks & 1][0]);
+        lds_tie(kr[ks & 1][1]);
+        lds_tie(vr[ks & 1][0]);
+        lds_tie(vr[ks & 1][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        s[0] = M::mma(kr[ks & 1][0], qf[ks], s[0]);
+        s[1] = M::mma(kr[ks & 1][1], qf[ks], s[1]);
+        dp[0] = M::mma(vr[ks & 1][0], of[ks], dp[0]);
+        dp[1] = M::mma(vr[ks & 1][1], of[ks], dp[1]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+    // dS^T / scale = P (dP - D) (the scale is applied to dQ at the end);
+    // key k = 32 kh + d_row(r, hl) is visible iff
+    // k < lim (its row exists and, for a token tile, it is not after the
+    // query).
     const bool need_mask = f.rows < kKvTile || (!f.cart && f.j0 + kKvTile - 1 > i0);
+    const int lim = f.cart ? f.rows : min(f.rows, my_i - f.j0 + 1);
+    const int lim_l = lim - 4 * hl;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float arg = fmaf(s[kh][r], c, -lse2);
         if (need_mask) {
-          const int key = 32 * kh + d_row(r, hl);
-          const bool vis = key < f.rows && (f.cart || f.j0 + key <= my_i);
-          arg = vis ? arg : -INFINITY;
+          const int kc = 32 * kh + (r & 3) + 8 * (r >> 2);   // key minus 4 hl
+          arg = kc < lim_l ? arg : -INFINITY;
         }
         const float p_ = __builtin_amdgcn_exp2f(arg);
-        dp[kh][r] = p_ * (dp[kh][r] - dl) * scale;      // dS^T
+        dp[kh][r] = p_ * (dp[kh][r] - dl);
       }
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const bf16x8 sf = pack_regs<bf16>(dp[kh], m);
-        const int r0 = 32 * kh + 16 * m + 4 * hl;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int cc = 32 * db + c0base;
-          const bf16x8 ka = cat8(tr_col4(Ks, TS, r0, cc, lane), tr_col4(Ks, TS, r0 + 8, cc, lane));
-          acc[db] = M::mma(ka, sf, acc[db]);
+    // dQ^T += K^T dS^T in four steps j = (kh, m): K^T fragments by transpose
+    // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
+    {
+      const uint32_t kb = kst + tr_lane;
+      bf16x8 ka[2][NDB];
+      auto rdk = [&](auto J, int slot) {
+        constexpr int j = decltype(J)::value;
+        static_for<NDB>([&](auto DB) {
+          constexpr int db = decltype(DB)::value;
+          constexpr int off = 2 * ((16 * j) * TS + 32 * db);
+          ka[slot][db] = cat8(lds_tr4<off>(kb), lds_tr4<off + 16 * TS>(kb));
+        });
+      };
+      rdk(std::integral_constant<int, 0>{}, 0);
+      static_for<4>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        constexpr int kh = j / 2, m = j % 2;
+        if constexpr (j + 1 < 4) {
+          rdk(std::integral_constant<int, j + 1>{}, (j + 1) & 1);
+          lds_wait<2 * NDB>();
+        } else {
+          lds_wait<0>();
         }
-      }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) lds_tie(ka[j & 1][db]);
+        const bf16x8 sfr = pack_regs<bf16>(dp[kh], m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = M::mma(ka[j & 1][db], sfr, acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
   };
 
   for (int t = 0; t < nt; t += 2) {
@@ -889,7 +942,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
-      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(K0, V0, f);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(lds_addr(K0), lds_addr(V0), f);
     }
     if (t + 1 >= nt) break;
     CART_WAIT_VMCNT(0);
@@ -898,7 +951,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
-      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(K1, V1, f);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(lds_addr(K1), lds_addr(V1), f);
     }
   }
 
@@ -910,7 +963,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int cc = 0; cc < 4; ++cc) {
       bf16x4 o4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o4[e] = (bf16)acc[db][4 * cc + e];
+      for (int e = 0; e < 4; ++e) o4[e] = (bf16)(acc[db][4 * cc + e] * scale);
       *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * cc + 4 * hl) = o4;
     }
 }

@@ -298,36 +298,62 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 //    probabilities are then at most 256, well inside f32 and bf16 range).
 // Cartridge rows arrive as bf16 (f32 master rows are cast first).
 // One key tile of the online softmax for one wave (32 queries x 64 keys).
+// The K and V tiles are at LDS byte addresses kst, vst. All LDS reads are
+// issued by the inline-assembly helpers with explicit waits (the copy of the
+// next tile into the other stage is in flight meanwhile), one k-step ahead
+// of the MFMAs that use them.
 template <int D>
-__device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, const KvTile& f,
+__device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const KvTile& f,
                                             const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
                                             float& m_ref, float& l_run, float c, int i0,
                                             int my_i, int lane) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
+  constexpr int TS = tstr<D>();
   const int l32 = lane & 31;
   const int hl = lane >> 5;
+  // S^T = K Q^T for the two 32-key halves: K row fragments (row 32 kh + l32,
+  // 8 elements at 16 ks + 8 hl), two reads per k-step.
   f32x16 s[2];
+  {
+    const uint32_t kb = kst + 2 * t_off<D>(l32, 8 * hl);
+    bf16x8 kfr[2][2];
+    auto rd = [&](auto KS, int slot) {
+      constexpr int ks = decltype(KS)::value;
+      kfr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
+      kfr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<2 * 32 * TS + 32 * ks>(kb));
+    };
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    bf16x8 kfr[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      kfr[ks] = *reinterpret_cast<const bf16x8*>(Ks + t_off<D>(32 * kh + l32, 16 * ks + 8 * hl));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) s[kh] = M::mma(kfr[ks], qf[ks], s[kh]);
+    for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; }
+    rd(std::integral_constant<int, 0>{}, 0);
+    static_for<NKS>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      if constexpr (ks + 1 < NKS) {
+        rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
+        lds_wait<2>();
+      } else {
+        lds_wait<0>();
+      }
+      lds_tie(kfr[ks & 1][0]);
+      lds_tie(kfr[ks & 1][1]);
+      __builtin_amdgcn_sched_barrier(0);
+      s[0] = M::mma(kfr[ks & 1][0], qf[ks], s[0]);
+      s[1] = M::mma(kfr[ks & 1][1], qf[ks], s[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
+  // Mask: key k = 32 kh + d_row(r, hl) of the tile is visible iff k < lim
+  // (its row exists and, for a token tile, it is not after the query).
   if (f.rows < kBN || (!f.cart && f.j0 + kBN - 1 > i0)) {
+    const int lim = f.cart ? f.rows : min(f.rows, my_i - f.j0 + 1);
+    const int lim_l = lim - 4 * hl;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kh + d_row(r, hl);
-        const bool vis = key < f.rows && (f.cart || f.j0 + key <= my_i);
-        s[kh][r] = vis ? s[kh][r] : -INFINITY;
+        const int kc = 32 * kh + (r & 3) + 8 * (r >> 2);   // key minus 4 hl
+        s[kh][r] = kc < lim_l ? s[kh][r] : -INFINITY;
       }
   }
   float mx = -INFINITY;
@@ -358,21 +384,39 @@ __device__ __forceinline__ void fwd_compute(const bf16* Ks, const bf16* Vs, cons
       ls += pv_;
     }
   l_run += ls;
-  const int c0base = 16 * ((lane >> 4) & 1);
+  // O^T += V^T P^T in four steps j = (kh, m): V^T fragments by transpose
+  // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
+  {
+    const uint32_t vb = vst + 2 * ((4 * hl + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) +
+                                   4 * (lane & 3));
+    bf16x8 va[2][NDB];
+    auto rdv = [&](auto J, int slot) {
+      constexpr int j = decltype(J)::value;
+      static_for<NDB>([&](auto DB) {
+        constexpr int db = decltype(DB)::value;
+        constexpr int off = 2 * ((16 * j) * TS + 32 * db);
+        va[slot][db] = cat8(lds_tr4<off>(vb), lds_tr4<off + 16 * TS>(vb));
+      });
+    };
+    rdv(std::integral_constant<int, 0>{}, 0);
+    static_for<4>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int kh = j / 2, m = j % 2;
+      if constexpr (j + 1 < 4) {
+        rdv(std::integral_constant<int, j + 1>{}, (j + 1) & 1);
+        lds_wait<2 * NDB>();
+      } else {
+        lds_wait<0>();
+      }
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
+      for (int db = 0; db < NDB; ++db) lds_tie(va[j & 1][db]);
       const bf16x8 pf = pack_regs<bf16>(s[kh], m);
-      const int r0 = 32 * kh + 16 * m + 4 * hl;
-      bf16x8 va[NDB];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        va[db] = cat8(tr_col4(Vs, tstr<D>(), r0, 32 * db + c0base, lane),
-                      tr_col4(Vs, tstr<D>(), r0 + 8, 32 * db + c0base, lane));
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = M::mma(va[db], pf, acc[db]);
-    }
+      for (int db = 0; db < NDB; ++db) acc[db] = M::mma(va[j & 1][db], pf, acc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
 }
 
 template <int D>
@@ -440,7 +484,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31))
-        fwd_compute<D>(K0, V0, f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
+        fwd_compute<D>(lds_addr(K0), lds_addr(V0), f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
     }
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
@@ -450,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31))
-        fwd_compute<D>(K1, V1, f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
+        fwd_compute<D>(lds_addr(K1), lds_addr(V1), f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
     }
   }
 

@@ -32,7 +32,8 @@ namespace {
 constexpr int kPage = 16;
 constexpr int kDecThreads = 256;
 constexpr int kMaxG = 8;     // q-heads per kv head handled by one workgroup
-constexpr int kUnroll = 4;   // passes in flight per thread
+constexpr int kUnroll = 4;   // passes per group of loads
+constexpr int kMaxPps = 256; // pages per split at most (a launch plan bound)
 
 template <typename TS>
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheDims c, int seq, int start,
@@ -139,26 +140,49 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
 
-  const int32_t* bt = a.c.block_table + (size_t)s * a.c.max_pages;
+  // Physical pages of this split, validated once, into LDS: the K/V loads
+  // then depend on no other global load.
+  __shared__ int pg[kMaxPps];
+  const int n_pg = row_end > row_begin ? (row_end - row_begin + kPage - 1) / kPage : 0;
+  {
+    const int32_t* bt = a.c.block_table + (size_t)s * a.c.max_pages + row_begin / kPage;
+    for (int i = tid; i < n_pg; i += kDecThreads) {
+      const int p = bt[i];
+      pg[i] = (p >= 0 && p < a.c.n_pages) ? p : -1;
+    }
+  }
+  __syncthreads();
+
+  // Rows are streamed kUnroll * RPP at a time; the raw 16-byte chunks of
+  // the next group are loaded before the current group is used, so two
+  // groups of loads are in flight per thread.
   const bf16* kp = reinterpret_cast<const bf16*>(a.c.k_pages);
   const bf16* vp = reinterpret_cast<const bf16*>(a.c.v_pages);
-  for (int r0 = row_begin; r0 < row_end; r0 += kUnroll * RPP) {
-    float kx[kUnroll][8], vx[kUnroll][8];
-    bool ok[kUnroll];
+  struct Grp { uint4 k[kUnroll], v[kUnroll]; bool ok[kUnroll]; };
+  auto load_grp = [&](int r0, Grp& x) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int row = r0 + u * RPP + rsub;
-      int page = -1;
-      if (row < row_end) page = bt[row / kPage];
-      ok[u] = page >= 0 && page < a.c.n_pages;
-      if (ok[u]) {
+      const int page = row < row_end ? pg[(row - row_begin) / kPage] : -1;
+      x.ok[u] = page >= 0;
+      if (x.ok[u]) {
         const size_t off = (((size_t)page * a.c.Hkv + kv) * kPage + row % kPage) * D + chunk * 8;
-        load8<bf16>(kp + off, kx[u]);
-        load8<bf16>(vp + off, vx[u]);
+        x.k[u] = *reinterpret_cast<const uint4*>(kp + off);
+        x.v[u] = *reinterpret_cast<const uint4*>(vp + off);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kx[u][e] = 0.f; vx[u][e] = 0.f; }
+        x.k[u] = make_uint4(0, 0, 0, 0);
+        x.v[u] = make_uint4(0, 0, 0, 0);
       }
+    }
+  };
+  auto use_grp = [&](const Grp& x) {
+    float kx[kUnroll][8], vx[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, x.k[u]);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, x.v[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { kx[u][e] = (float)kb[e]; vx[u][e] = (float)vb[e]; }
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
         for (int e = 0; e < 8; ++e) d += qv[j][e] * kx[u][e];
 #pragma unroll
         for (int off = 1; off < CPR; off <<= 1) d += __shfl_xor(d, off);
-        sc[u] = ok[u] ? d : -INFINITY;
+        sc[u] = x.ok[u] ? d : -INFINITY;
         mx = fmaxf(mx, sc[u]);
       }
       const float mu = (mx == -INFINITY) ? 0.f : mx;
@@ -188,6 +212,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       }
       l[j] = l[j] * alpha + ls;
       m[j] = mx;
+    }
+  };
+  constexpr int STEP = kUnroll * RPP;
+  if (row_begin < row_end) {
+    Grp cur, nxt;
+    load_grp(row_begin, cur);
+    for (int r0 = row_begin; r0 < row_end; r0 += STEP) {
+      const bool more = r0 + STEP < row_end;
+      if (more) load_grp(r0 + STEP, nxt);
+      use_grp(cur);
+      if (more) cur = nxt;
     }
   }
 
