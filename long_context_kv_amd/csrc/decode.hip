@@ -35,6 +35,25 @@ constexpr int kMaxG = 8;     // q-heads per kv head handled by one workgroup
 constexpr int kUnroll = 4;   // passes per group of loads
 constexpr int kMaxPps = 256; // pages per split at most (a launch plan bound)
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Sum over aligned groups of N lanes (N = 8 or 16) by DPP adds: swap lanes
+// 1 apart, 2 apart, then mirror halves of 8 and of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                             0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(N == 8 || N == 16, "row of 8 or 16 lanes");
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  if constexpr (N == 16) x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
 template <typename TS>
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheDims c, int seq, int start,
                                                            const TS* __restrict__ k,
@@ -123,14 +142,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   // clamp to the block table's capacity so a bad device length cannot read past it
   const int row_end = min(min(len, row_begin + a.pps * kPage), a.c.max_pages * kPage);
 
-  float qv[G][8];
+  // q chunks stay bf16: scores are bf16 x bf16 dot products accumulated in
+  // f32 (v_dot2), scaled afterwards.
+  bf16x8 qb[G];
 #pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const bf16* qp = a.q + ((size_t)s * a.Hq + kv * a.g + j) * D + chunk * 8;
-    load8<bf16>(qp, qv[j]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[j][e] *= a.scale_log2;
-  }
+  for (int j = 0; j < G; ++j)
+    qb[j] = *reinterpret_cast<const bf16x8*>(a.q + ((size_t)s * a.Hq + kv * a.g + j) * D + chunk * 8);
+  const float c = a.scale_log2;
+  // Online softmax per q-head with a lazily moved reference max m (log2
+  // domain): probabilities are exp2(score - m) <= 2^8, and acc, l are
+  // rescaled only when some score exceeds m by more than 8.
   float m[G], l[G], acc[G][8];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
@@ -159,70 +180,83 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   const bf16* kp = reinterpret_cast<const bf16*>(a.c.k_pages);
   const bf16* vp = reinterpret_cast<const bf16*>(a.c.v_pages);
   struct Grp { uint4 k[kUnroll], v[kUnroll]; bool ok[kUnroll]; };
+  // Loads are unconditional, so the wait counts stay exact: a row past the
+  // split re-reads the split's last row (a cache hit) and a row on an invalid
+  // page reads page 0; both are masked.
   auto load_grp = [&](int r0, Grp& x) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int row = r0 + u * RPP + rsub;
-      const int page = row < row_end ? pg[(row - row_begin) / kPage] : -1;
-      x.ok[u] = page >= 0;
-      if (x.ok[u]) {
-        const size_t off = (((size_t)page * a.c.Hkv + kv) * kPage + row % kPage) * D + chunk * 8;
-        x.k[u] = *reinterpret_cast<const uint4*>(kp + off);
-        x.v[u] = *reinterpret_cast<const uint4*>(vp + off);
-      } else {
-        x.k[u] = make_uint4(0, 0, 0, 0);
-        x.v[u] = make_uint4(0, 0, 0, 0);
-      }
+      const int rr = min(row, row_end - 1);
+      const int page = pg[(rr - row_begin) / kPage];
+      x.ok[u] = row < row_end && page >= 0;
+      const size_t off = (((size_t)max(page, 0) * a.c.Hkv + kv) * kPage + rr % kPage) * D + chunk * 8;
+      x.k[u] = *reinterpret_cast<const uint4*>(kp + off);
+      x.v[u] = *reinterpret_cast<const uint4*>(vp + off);
     }
   };
   auto use_grp = [&](const Grp& x) {
-    float kx[kUnroll][8], vx[kUnroll][8];
+    float p[G][kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const bf16x8 kb = __builtin_bit_cast(bf16x8, x.k[u]);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, x.v[u]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { kx[u][e] = (float)kb[e]; vx[u][e] = (float)vb[e]; }
+      for (int j = 0; j < G; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 qa = {qb[j][2 * e], qb[j][2 * e + 1]};
+          const bf16x2 ka = {kb[2 * e], kb[2 * e + 1]};
+          d = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, d, false);
+        }
+        d = row_sum<CPR>(d);
+        p[j][u] = x.ok[u] ? d * c : -INFINITY;
+      }
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      float sc[kUnroll];
-      float mx = m[j];
+      float mx = p[j][0];
+#pragma unroll
+      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, p[j][u]);
+      if (mx > m[j] + 8.f) {   // per lane; taken rarely after the first rows
+        const float alpha = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - mx);
+        l[j] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+        m[j] = mx;
+      }
+      const float mu = (m[j] == -INFINITY) ? 0.f : m[j];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) d += qv[j][e] * kx[u][e];
-#pragma unroll
-        for (int off = 1; off < CPR; off <<= 1) d += __shfl_xor(d, off);
-        sc[u] = x.ok[u] ? d : -INFINITY;
-        mx = fmaxf(mx, sc[u]);
+        p[j][u] = __builtin_amdgcn_exp2f(p[j][u] - mu);
+        l[j] += p[j][u];
       }
-      const float mu = (mx == -INFINITY) ? 0.f : mx;
-      const float alpha = exp2f(m[j] - mu);
-      float ls = 0.f;
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+    for (int u = 0; u < kUnroll; ++u) {
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, x.v[u]);
+      float vx[8];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float pv = exp2f(sc[u] - mu);
-        ls += pv;
+      for (int e = 0; e < 8; ++e) vx[e] = (float)vb[e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] += pv * vx[u][e];
-      }
-      l[j] = l[j] * alpha + ls;
-      m[j] = mx;
+      for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p[j][u], vx[e], acc[j][e]);
     }
   };
   constexpr int STEP = kUnroll * RPP;
   if (row_begin < row_end) {
-    Grp cur, nxt;
-    load_grp(row_begin, cur);
-    for (int r0 = row_begin; r0 < row_end; r0 += STEP) {
-      const bool more = r0 + STEP < row_end;
-      if (more) load_grp(r0 + STEP, nxt);
-      use_grp(cur);
-      if (more) cur = nxt;
+    // ping-pong between two register groups: the loads of the next group are
+    // in flight while the current one is used
+    Grp ga, gb;
+    load_grp(row_begin, ga);
+    for (int r0 = row_begin;;) {
+      load_grp(r0 + STEP, gb);
+      use_grp(ga);
+      if ((r0 += STEP) >= row_end) break;
+      load_grp(r0 + STEP, ga);
+      use_grp(gb);
+      if ((r0 += STEP) >= row_end) break;
     }
   }
 
