@@ -98,7 +98,8 @@ def train_bench(C, W, shape, steps, warmup):
     total_ms = _events_ms(step, steps)
     kern = {}
     for name in ("rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess", "attn_bwd",
-                 "attn_bwd_dq", "bwd_dq_finalize", "bwd_cart_reduce"):
+                 "attn_bwd_dq", "bwd_dq_combine", "bwd_tok_reduce", "bwd_dq_finalize",
+                 "bwd_cart_reduce"):
         ms, cnt = C.timing_query(name)
         if cnt:
             kern[name] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms)

@@ -28,6 +28,8 @@
 //    (where its dQ accumulator lines are hit by every tile).
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -60,8 +62,13 @@ struct BwdArgs {
   void* dv_tok;
   float* dk_cart;
   float* dv_cart;
-  float* dk_part;     // [splits_c][p][Hkv][D]
+  float* dk_part;     // [splits][p][Hkv][D]
   float* dv_part;
+  float* dk_tpart;    // [kv_stmax][B][n][Hkv][D], token-tile pieces (bf16 path)
+  float* dv_tpart;
+  float* dq_part;     // [q_splits][B][n][Hq][D], dQ key-split pieces (bf16 path)
+  int kv_target, kv_ptok, kv_stmax, q_splits;
+  int D4;             // head_dim / 4
   int B, n, p, f, Hq, Hkv, g;
   int n_ct, n_tt, nqt, splits_c;
   int hpw, wph, n_hg, n_qb;   // query-major grid of the dQ kernel
@@ -440,25 +447,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
-  // ---- work item
-  const int per_kv = a.n_ct * a.splits_c + a.B * a.n_tt;
+  // ---- work item: a piece of one key tile's unit list (pieces of cartridge
+  // tiles first, then per batch the pieces of the token tiles)
+  const int per_kv = a.n_ct * a.splits_c + a.B * a.kv_ptok;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int kv = lg / per_kv;
   int r0 = lg % per_kv;
   const bool cart = r0 < a.n_ct * a.splits_c;
-  int tile, split = 0, b = 0, u_begin, u_end;
+  int tile, split = 0, n_split = 1, b = 0, u_begin, u_end;
   if (cart) {
     tile = r0 / a.splits_c;
     split = r0 % a.splits_c;
+    n_split = a.splits_c;
     const int U = a.B * a.g * a.nqt;
     u_begin = (int)((long long)split * U / a.splits_c);
     u_end = (int)((long long)(split + 1) * U / a.splits_c);
   } else {
     r0 -= a.n_ct * a.splits_c;
-    b = r0 / a.n_tt;
-    tile = r0 % a.n_tt;
-    u_begin = 0;
-    u_end = a.g * (a.nqt - tile * (kBNB / kBQ));
+    b = r0 / a.kv_ptok;
+    r0 %= a.kv_ptok;
+    tile = 0;
+    int ut = a.g * a.nqt;
+    n_split = (ut + a.kv_target - 1) / a.kv_target;
+    while (r0 >= n_split) {
+      r0 -= n_split;
+      ++tile;
+      ut = a.g * (a.nqt - tile * (kBNB / kBQ));
+      n_split = (ut + a.kv_target - 1) / a.kv_target;
+    }
+    split = r0;
+    u_begin = (int)((long long)split * ut / n_split);
+    u_end = (int)((long long)(split + 1) * ut / n_split);
   }
   const int j0 = tile * kBNB;
   const int limit = cart ? a.p : a.n;
@@ -483,9 +502,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     cu.hin = (u_begin / a.nqt) % a.g;
     cu.qt = u_begin % a.nqt;
   } else {
+    const int nq = a.nqt - qt0;
     cu.bb = b;
-    cu.hin = 0;
-    cu.qt = qt0;
+    cu.hin = u_begin / nq;
+    cu.qt = qt0 + u_begin % nq;
   }
   auto next = [&](Unit x) {
     if (++x.qt == a.nqt) {
@@ -771,8 +791,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
         }
       } else {
         const size_t o = (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
-        reinterpret_cast<bf16*>(a.dk_tok)[o] = (bf16)gk;
-        reinterpret_cast<bf16*>(a.dv_tok)[o] = (bf16)gv;
+        if (n_split > 1) {
+          const size_t po_ = (size_t)split * a.B * a.n * row_stride + o;
+          a.dk_tpart[po_] = gk;
+          a.dv_tpart[po_] = gv;
+        } else {
+          reinterpret_cast<bf16*>(a.dk_tok)[o] = (bf16)gk;
+          reinterpret_cast<bf16*>(a.dv_tok)[o] = (bf16)gv;
+        }
       }
     }
   }
@@ -796,6 +822,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int hl = lane >> 5;
 
   int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lg % a.q_splits; lg /= a.q_splits;
   const int qb = a.n_qb - 1 - (lg % a.n_qb); lg /= a.n_qb;
   const int hg = lg % a.n_hg; lg /= a.n_hg;
   const int b = lg % a.B; lg /= a.B;
@@ -808,10 +835,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int my_i = i0 + l32;
   const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
   const int n_ct = (a.p + kKvTile - 1) / kKvTile;
-  const int nt = n_ct + wg_last / kKvTile + 1;
+  const int nt_all = n_ct + wg_last / kKvTile + 1;
+  // this workgroup's contiguous range of key tiles
+  const int t_begin = (int)((long long)split * nt_all / a.q_splits);
+  const int t_end = (int)((long long)(split + 1) * nt_all / a.q_splits);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
-  kv_issue<D>(K0, V0, 0, n_ct, src, wave, lane);
+  if (t_begin < t_end) kv_issue<D>(K0, V0, t_begin, n_ct, src, wave, lane);
 
   // Q^T and dO^T as B operands: lane (q + 32 hl) holds row q, 8 columns per k-step.
   bf16x8 qf[NKS], of[NKS];
@@ -935,19 +965,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  for (int t = 0; t < nt; t += 2) {
+  for (int t = t_begin; t < t_end; t += 2) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 1 < nt) kv_issue<D>(K1, V1, t + 1, n_ct, src, wave, lane);
+    if (t + 1 < t_end) kv_issue<D>(K1, V1, t + 1, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
       if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(lds_addr(K0), lds_addr(V0), f);
     }
-    if (t + 1 >= nt) break;
+    if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 2 < nt) kv_issue<D>(K0, V0, t + 2, n_ct, src, wave, lane);
+    if (t + 2 < t_end) kv_issue<D>(K0, V0, t + 2, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
@@ -956,7 +986,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 
   if (!wave_active || my_i >= a.n) return;
-  bf16* dqp = reinterpret_cast<bf16*>(a.dq) + (((size_t)b * a.n + my_i) * a.Hq + h) * D;
+  const size_t row = ((size_t)b * a.n + my_i) * a.Hq + h;
+  if (a.q_splits > 1) {
+    // f32 piece of this key range (a split with no tiles writes zeros)
+    float* pp = a.dq_part + ((size_t)split * a.B * a.n * a.Hq + row) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        *reinterpret_cast<float4*>(pp + 32 * db + 8 * cc + 4 * hl) =
+            make_float4(acc[db][4 * cc] * scale, acc[db][4 * cc + 1] * scale,
+                        acc[db][4 * cc + 2] * scale, acc[db][4 * cc + 3] * scale);
+    return;
+  }
+  bf16* dqp = reinterpret_cast<bf16*>(a.dq) + row * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -966,6 +1009,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) o4[e] = (bf16)(acc[db][4 * cc + e] * scale);
       *reinterpret_cast<bf16x4*>(dqp + 32 * db + 8 * cc + 4 * hl) = o4;
     }
+}
+
+// dQ = sum of the key-split pieces, in bf16 (4 elements per thread).
+__global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
+  const size_t n4 = (size_t)a.B * a.n * a.Hq * (a.D4);
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n4) return;
+  const float4* pp = reinterpret_cast<const float4*>(a.dq_part);
+  float4 t = pp[e];
+  for (int s = 1; s < a.q_splits; ++s) {
+    const float4 u = pp[(size_t)s * n4 + e];
+    t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+  }
+  bf16x4 o;
+  o[0] = (bf16)t.x; o[1] = (bf16)t.y; o[2] = (bf16)t.z; o[3] = (bf16)t.w;
+  reinterpret_cast<bf16x4*>(a.dq)[e] = o;
+}
+
+// dK, dV of token tiles cut into pieces: sum of the f32 pieces, in bf16.
+__global__ __launch_bounds__(256) void bwd_tok_reduce(BwdArgs a) {
+  const size_t n4 = (size_t)a.B * a.n * a.Hkv * (a.D4);
+  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n4) return;
+  const int j = (int)((e / ((size_t)a.Hkv * a.D4)) % a.n);
+  const int tile = j / kBNB;
+  const int ut = a.g * (a.nqt - tile * (kBNB / kBQ));
+  const int ns = (ut + a.kv_target - 1) / a.kv_target;
+  if (ns <= 1) return;   // written directly by its only piece
+  const float4* pk = reinterpret_cast<const float4*>(a.dk_tpart);
+  const float4* pv = reinterpret_cast<const float4*>(a.dv_tpart);
+  float4 k = pk[e], v = pv[e];
+  for (int s = 1; s < ns; ++s) {
+    const float4 x = pk[(size_t)s * n4 + e], y = pv[(size_t)s * n4 + e];
+    k.x += x.x; k.y += x.y; k.z += x.z; k.w += x.w;
+    v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
+  }
+  bf16x4 ok, ov;
+  ok[0] = (bf16)k.x; ok[1] = (bf16)k.y; ok[2] = (bf16)k.z; ok[3] = (bf16)k.w;
+  ov[0] = (bf16)v.x; ov[1] = (bf16)v.y; ov[2] = (bf16)v.z; ov[3] = (bf16)v.w;
+  reinterpret_cast<bf16x4*>(a.dk_tok)[e] = ok;
+  reinterpret_cast<bf16x4*>(a.dv_tok)[e] = ov;
 }
 
 // D_i = dO_i . O_i for every (b, h, i), and dQ accumulator := 0.
@@ -1049,22 +1133,58 @@ BwdPlan plan_bwd(const AttnDims& d) {
   pl.n_tt = (d.n + kBNB - 1) / kBNB;
   pl.nqt = (d.n + kBQ - 1) / kBQ;
   const long long U = (long long)d.B * g * pl.nqt;       // units of a cartridge tile
-  const long long tok_units = (long long)g * pl.nqt;      // units of the first token tile
+  auto tok_units = [&](int t) { return (long long)g * (pl.nqt - t * (kBNB / kBQ)); };
+  // float32 path: cartridge tiles only are split
   int s = 1;
   while (pl.n_ct > 0 && U / (2 * s) >= 8 &&
-         ((long long)d.Hkv * (pl.n_ct * s + d.B * pl.n_tt) < 512 || U / s > 2 * tok_units))
+         ((long long)d.Hkv * (pl.n_ct * s + d.B * pl.n_tt) < 512 || U / s > 2 * tok_units(0)))
     s *= 2;
   pl.splits_c = s;
   pl.grid_c = d.Hkv * pl.n_ct * s;
   pl.grid_t = d.Hkv * d.B * pl.n_tt;
+  // bf16 path: pieces of about kv_target units, about two pieces per CU
+  {
+    long long W = (long long)pl.n_ct * U;
+    for (int t = 0; t < pl.n_tt; ++t) W += d.B * tok_units(t);
+    // smallest piece size that needs at most two rounds of workgroups on the
+    // 256 CUs (one resident workgroup per CU)
+    long long T = (d.Hkv * W + 511) / 512;
+    if (T < 8) T = 8;
+    auto pieces = [&](long long t_) {
+      long long c = pl.n_ct > 0 ? pl.n_ct * ((U + t_ - 1) / t_) : 0;
+      for (int t = 0; t < pl.n_tt; ++t) c += d.B * ((tok_units(t) + t_ - 1) / t_);
+      return d.Hkv * c;
+    };
+    const long long t_max = std::max(U, tok_units(0));   // beyond it every tile is one piece
+    while (T < t_max && pieces(T) > 512) ++T;
+    pl.kv_target = (int)T;
+    pl.kv_splits_c = pl.n_ct > 0 ? (int)((U + T - 1) / T) : 1;
+    int ptok = 0;
+    for (int t = 0; t < pl.n_tt; ++t) ptok += (int)((tok_units(t) + T - 1) / T);
+    pl.kv_ptok = ptok;
+    pl.kv_stmax = pl.n_tt > 0 ? (int)((tok_units(0) + T - 1) / T) : 1;
+    pl.grid_kv = d.Hkv * (pl.n_ct * pl.kv_splits_c + d.B * ptok);
+    if (d.tok_bf16 && pl.kv_stmax > 1)
+      pl.tok_part_bytes = (size_t)pl.kv_stmax * d.B * d.n * d.Hkv * d.D * sizeof(float);
+  }
   pl.dq_bytes = d.tok_bf16 ? 0 : (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
   {
-    const FwdPlan fp = plan_fwd(d);   // the dQ kernel uses the forward's query blocks, unsplit
+    // the dQ kernel uses the forward's query blocks, its key tiles split
+    // like the forward's while the grid is small
+    const FwdPlan fp = plan_fwd(d);
     pl.hpw = fp.hpw; pl.wph = fp.wph; pl.n_hg = fp.n_hg; pl.n_qb = fp.n_qb;
-    pl.grid_q = d.Hkv * d.B * fp.n_hg * fp.n_qb;
+    const long long base = (long long)d.Hkv * d.B * fp.n_hg * fp.n_qb;
+    const int min_tiles = (d.p + kKvTile - 1) / kKvTile + 1;
+    int qs = 1;
+    if (d.tok_bf16)
+      while (base * qs < 512 && (qs * 2) * 4 <= min_tiles) qs *= 2;
+    pl.q_splits = qs;
+    pl.grid_q = (int)(base * qs);
+    if (qs > 1) pl.dq_part_bytes = (size_t)qs * d.B * d.n * d.Hq * d.D * sizeof(float);
   }
   pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);   // and as much for lse2
-  pl.part_bytes = s > 1 ? (size_t)s * d.p * d.Hkv * d.D * sizeof(float) : 0;
+  const int sc = d.tok_bf16 ? pl.kv_splits_c : s;
+  pl.part_bytes = sc > 1 ? (size_t)sc * d.p * d.Hkv * d.D * sizeof(float) : 0;
   if (d.tok_bf16 && !d.row_bf16 && d.p > 0)
     pl.shadow_bytes = 2 * (size_t)d.p * d.Hkv * d.D * sizeof(uint16_t);
   return pl;
@@ -1073,7 +1193,8 @@ BwdPlan plan_bwd(const AttnDims& d) {
 size_t bwd_workspace_bytes(const AttnDims& d) {
   const BwdPlan pl = plan_bwd(d);
   return align256(pl.shadow_bytes) + align256(pl.dq_bytes) + 2 * align256(pl.delta_bytes) +
-         2 * align256(pl.part_bytes);
+         2 * align256(pl.part_bytes) + 2 * align256(pl.tok_part_bytes) +
+         align256(pl.dq_part_bytes);
 }
 
 // float32 reference mode: preprocess, generic kernel (dQ by atomics), dQ
@@ -1108,11 +1229,23 @@ static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream
   CART_TIMED("bwd_preprocess", st, bwd_preprocess<bf16, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_TIMED("attn_bwd", st, attn_bwd_kv_kernel<D><<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
+  CART_TIMED("attn_bwd", st, attn_bwd_kv_kernel<D><<<pl.grid_kv, kThreads, 0, st>>>(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   CART_TIMED("attn_bwd_dq", st, attn_bwd_dq_kernel<D><<<pl.grid_q, kThreads, 0, st>>>(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (pl.splits_c > 1) {
+  if (pl.q_splits > 1) {
+    const size_t n4 = (size_t)a.B * a.n * a.Hq * (D / 4);
+    CART_TIMED("bwd_dq_combine", st,
+               bwd_dq_combine<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (pl.kv_stmax > 1) {
+    const size_t n4 = (size_t)a.B * a.n * a.Hkv * (D / 4);
+    CART_TIMED("bwd_tok_reduce", st,
+               bwd_tok_reduce<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (a.splits_c > 1) {
     const size_t total = (size_t)a.p * a.Hkv * D;
     CART_TIMED("bwd_cart_reduce", st,
                bwd_cart_reduce_t<D><<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a));
@@ -1151,9 +1284,19 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.dk_part = pl.part_bytes ? reinterpret_cast<float*>(w) : nullptr;
   w += align256(pl.part_bytes);
   a.dv_part = pl.part_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  w += align256(pl.part_bytes);
+  a.dk_tpart = pl.tok_part_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  w += align256(pl.tok_part_bytes);
+  a.dv_tpart = pl.tok_part_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  w += align256(pl.tok_part_bytes);
+  a.dq_part = pl.dq_part_bytes ? reinterpret_cast<float*>(w) : nullptr;
   a.dq = dq; a.dk_tok = dk_tok; a.dv_tok = dv_tok; a.dk_cart = dk_cart; a.dv_cart = dv_cart;
   a.B = d.B; a.n = d.n; a.p = d.p; a.f = d.f; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
-  a.n_ct = pl.n_ct; a.n_tt = pl.n_tt; a.nqt = pl.nqt; a.splits_c = pl.splits_c;
+  a.n_ct = pl.n_ct; a.n_tt = pl.n_tt; a.nqt = pl.nqt;
+  a.splits_c = d.tok_bf16 ? pl.kv_splits_c : pl.splits_c;
+  a.kv_target = pl.kv_target; a.kv_ptok = pl.kv_ptok; a.kv_stmax = pl.kv_stmax;
+  a.q_splits = pl.q_splits;
+  a.D4 = d.D / 4;
   a.accumulate = accumulate ? 1 : 0;
   a.scale = d.scale;
   a.scale_log2 = d.scale * kLog2e;

@@ -29,9 +29,14 @@ hipError_t launch_fwd(const AttnDims& a, const void* q, const void* k_tok, const
                       void* ws, hipStream_t st);
 
 struct BwdPlan {
-  int n_ct, n_tt, nqt, splits_c, grid_c, grid_t;
-  int hpw, wph, n_hg, n_qb, grid_q;   // query-major dQ kernel
-  size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes;
+  int n_ct, n_tt, nqt, splits_c, grid_c, grid_t;   // float32 path
+  // bf16 dK/dV kernel: every key tile's unit list is cut into pieces of about
+  // kv_target units (cartridge tiles into kv_splits_c pieces, token tile t
+  // into ceil(units_t / kv_target)); kv_ptok pieces per (kv head, batch) of
+  // token tiles, at most kv_stmax per token tile.
+  int kv_target, kv_splits_c, kv_ptok, kv_stmax, grid_kv;
+  int hpw, wph, n_hg, n_qb, q_splits, grid_q;     // query-major dQ kernel
+  size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes, tok_part_bytes, dq_part_bytes;
 };
 BwdPlan plan_bwd(const AttnDims& a);
 size_t bwd_workspace_bytes(const AttnDims& a);

@@ -192,3 +192,23 @@ def test_status_strings():
     for s in range(9):
         assert L.cart_status_string(s)
     assert L.cart_status_string(99) == b"unknown status"
+
+
+@pytest.mark.timeout(30)
+def test_workspace_sizes_of_the_workloads():
+    """Planning is host code: every workload shape (and a few extremes) gets a
+    finite workspace size promptly, and the backward needs at least the
+    forward's size in bf16 mode."""
+    from long_context_kv_amd import workloads as W
+    shapes = [(s.batch, s.q_seq, s.p, s.n_q_heads, s.n_kv_heads, s.head_dim)
+              for s in W.SHAPES.values() if hasattr(s, "q_seq")]
+    shapes += [(1, 1, 0, 2, 2, 64), (64, 4096, 65536, 64, 8, 128), (1, 131072, 1, 8, 8, 128),
+               (512, 32, 4, 32, 1, 128)]
+    for (b, n, p, hq, hkv, d) in shapes:
+        for tok, row in ((C.CART_BF16, C.CART_F32), (C.CART_BF16, C.CART_BF16),
+                         (C.CART_F32, C.CART_F32)):
+            s = _shape(batch=b, q_seq=n, p=p, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
+                       frozen_rows=min(1, p), tok_dtype=tok, row_dtype=row)
+            fw = L.cart_attn_workspace_size(ctypes.byref(s), 0)
+            bw = L.cart_attn_workspace_size(ctypes.byref(s), 1)
+            assert bw >= fw >= 0, (b, n, p, hq, hkv, d, tok, row)
