@@ -29,6 +29,39 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 flop/clk x 2.4 GHz, dense
 PEAK_HBM_GBPS = 8000.0
+
+# HBM bytes per launch of a kernel on a workload, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE; read counts x 2.0 from a 1 GiB copy calibration),
+# summarised in profiles/hbm_bytes_layers_and_decode.md. A figure holds only
+# for the kernel sources it was measured on: a mismatch of their hash reports
+# traffic as null.
+KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
+                  "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
+                  "decode": ("decode.hip", "common.hpp")}
+MEASURED_TRAFFIC = {
+    ("attn_bwd", "qwen3-0.6b-layer"): (94.54e6, "ecc1deed8f663929"),
+    ("attn_bwd", "qwen3-8b-layer"): (696.26e6, "ecc1deed8f663929"),
+    ("attn_fwd", "qwen3-8b-layer"): (237.42e6, "58416d21a1e1cd16"),
+    ("decode", "serving-decode"): (1225.64e6, "6e92833e52653c08"),
+}
+
+
+def _sources_sha1(kernel):
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_kv_amd", "csrc")
+    h = hashlib.sha1()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """Measured HBM bytes per launch, or None when not measured for these sources."""
+    entry = MEASURED_TRAFFIC.get((kernel, workload))
+    if entry is None or kernel not in KERNEL_SOURCES:
+        return None
+    return entry[0] if _sources_sha1(kernel) == entry[1] else None
 METRIC = "cartridge attn fwd+bwd TFLOP/s and decode GB/s, as % of MI355X roofline"
 
 
@@ -232,7 +265,8 @@ def main():
         ach = per_launch_flop[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, shape.name)}
     kernels = {}
     for k, v in kern.items():
         e = {"avg_ms": round(v["avg_ms"], 5), "launches": v["launches"]}
@@ -275,7 +309,8 @@ def main():
             ach = dec["kv_bytes"] / (dk["avg_ms"] * 1e-3) / 1e9
             droof = {"kernel": "decode", "bound": "hbm", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None}
+                     "frac": round(ach / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic("decode", W.DECODE.name)}
         result["decode"] = {
             "workload": f"{W.DECODE.name}: {W.DECODE.n_seqs} seqs, p={W.DECODE.p} + "
                         f"U{{0..{W.DECODE.max_generated}}} generated, Hq={W.DECODE.n_q_heads} "
