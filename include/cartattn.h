@@ -239,6 +239,10 @@ size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
  * kernel name and returns their summed duration (ms) and count.
  * ------------------------------------------------------------------------ */
 int cart_timing_enable(int32_t on);
+/* Restrict recording to launches of one kernel name (NULL or "" = all), so
+ * that timing one kernel adds two event records per launch of that kernel
+ * only. Kept across cart_timing_enable calls. */
+int cart_timing_only(const char* kernel);
 int cart_timing_query(const char* kernel, double* total_ms, int32_t* launches);
 
 const char* cart_status_string(int status);

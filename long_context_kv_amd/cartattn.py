@@ -45,7 +45,7 @@ EXPORTS = [
     "cart_rope_tokens", "cart_attn_workspace_size", "cart_attn_fwd", "cart_attn_bwd",
     "cart_cache_create", "cart_cache_destroy", "cart_cache_reset", "cart_cache_seq_len",
     "cart_append_cache", "cart_write_cache", "cart_decode", "cart_decode_workspace_size",
-    "cart_timing_enable", "cart_timing_query", "cart_status_string", "cart_last_error",
+    "cart_timing_enable", "cart_timing_only", "cart_timing_query", "cart_status_string", "cart_last_error",
 ]
 
 
@@ -91,6 +91,7 @@ _lib.cart_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _vp,
 _lib.cart_decode_workspace_size.argtypes = [_vp, _i32]
 _lib.cart_decode_workspace_size.restype = _sz
 _lib.cart_timing_enable.argtypes = [_i32]
+_lib.cart_timing_only.argtypes = [ctypes.c_char_p]
 _lib.cart_timing_query.argtypes = [ctypes.c_char_p, _P(ctypes.c_double), _P(_i32)]
 _lib.cart_status_string.argtypes = [ctypes.c_int]
 _lib.cart_status_string.restype = ctypes.c_char_p
@@ -288,6 +289,11 @@ class PagedCache:
 def timing_enable(on: bool) -> None:
     """Start (clearing old records) or stop per-kernel launch timing."""
     _check(_lib.cart_timing_enable(int(on)), "cart_timing_enable")
+
+
+def timing_only(kernel=None) -> None:
+    """Time only launches of `kernel` (None: every kernel)."""
+    _check(_lib.cart_timing_only(kernel.encode() if kernel else None), "cart_timing_only")
 
 
 def timing_query(kernel: str):

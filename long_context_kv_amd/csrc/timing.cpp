@@ -1,7 +1,8 @@
 // Per-kernel launch timing with HIP events recorded on the launching stream.
 //
 // Off by default. When enabled (cart_timing_enable), every kernel launch of
-// the library is bracketed by two events on its own stream; cart_timing_query
+// the library (or, after cart_timing_only, every launch of one kernel name)
+// is bracketed by two events on its own stream; cart_timing_query
 // waits for the recorded events and sums the elapsed times of one kernel
 // name. Events are pooled and reused across enable cycles.
 #include <hip/hip_runtime.h>
@@ -26,6 +27,7 @@ struct Record {
 
 std::mutex g_mu;
 bool g_on = false;
+std::string g_only;   // when not empty, only launches of this kernel name are timed
 std::vector<Record> g_records;
 std::vector<hipEvent_t> g_pool;
 
@@ -53,6 +55,7 @@ void recycle_all() {
 int timing_start(const char* name, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return -1;
+  if (!g_only.empty() && g_only != name) return -1;
   Record r{name, take_event(), take_event()};
   if (!r.start || !r.stop) return -1;
   if (hipEventRecord(r.start, st) != hipSuccess) return -1;
@@ -77,6 +80,12 @@ int cart_timing_enable(int32_t on) {
   for (auto& r : g_records) hipEventSynchronize(r.stop);
   recycle_all();
   g_on = on != 0;
+  return CART_OK;
+}
+
+int cart_timing_only(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_only = kernel ? kernel : "";
   return CART_OK;
 }
 
