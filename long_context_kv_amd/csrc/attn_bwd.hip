@@ -1146,17 +1146,22 @@ BwdPlan plan_bwd(const AttnDims& d) {
   {
     long long W = (long long)pl.n_ct * U;
     for (int t = 0; t < pl.n_tt; ++t) W += d.B * tok_units(t);
-    // smallest piece size that needs at most two rounds of workgroups on the
-    // 256 CUs (one resident workgroup per CU)
-    long long T = (d.Hkv * W + 511) / 512;
-    if (T < 8) T = 8;
+    // Pieces cost partial sums and a reduction; measured on the qwen3-0.6b
+    // layer, one round of unsplit tiles (192 workgroups on 256 CUs) beats two
+    // rounds of balanced pieces plus the reductions. So tiles are cut only
+    // when unsplit they would leave more than a quarter of the CUs idle, and
+    // then into the fewest pieces that still fit one round.
     auto pieces = [&](long long t_) {
       long long c = pl.n_ct > 0 ? pl.n_ct * ((U + t_ - 1) / t_) : 0;
       for (int t = 0; t < pl.n_tt; ++t) c += d.B * ((tok_units(t) + t_ - 1) / t_);
       return d.Hkv * c;
     };
-    const long long t_max = std::max(U, tok_units(0));   // beyond it every tile is one piece
-    while (T < t_max && pieces(T) > 512) ++T;
+    const long long t_max = std::max(U, tok_units(0));   // every tile one piece
+    long long T = t_max;
+    if (pieces(t_max) < 192) {
+      T = std::max(8LL, (d.Hkv * W + 255) / 256);
+      while (T < t_max && pieces(T) > 256) ++T;
+    }
     pl.kv_target = (int)T;
     pl.kv_splits_c = pl.n_ct > 0 ? (int)((U + T - 1) / T) : 1;
     int ptok = 0;
