@@ -1052,34 +1052,37 @@ __global__ __launch_bounds__(256) void bwd_tok_reduce(BwdArgs a) {
   reinterpret_cast<bf16x4*>(a.dv_tok)[e] = ov;
 }
 
-// D_i = dO_i . O_i for every (b, h, i), and dQ accumulator := 0.
-// One wave per (b, i, h) row; 4 rows per workgroup.
+// D_i = dO_i . O_i and lse_i * log2(e) for every (b, h, i), and (f32 tokens)
+// dQ accumulator := 0. Sixteen lanes per row (D/16 elements each), 16 rows
+// per workgroup; the row sum is taken with DPP adds.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  constexpr int EPL = D / 16;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
   const int total = a.B * a.n * a.Hq;
-  if (row >= total) return;
-  const int h = row % a.Hq;
-  const int bi = row / a.Hq;
-  const int i = bi % a.n;
-  const int b = bi / a.n;
-  const T* o = reinterpret_cast<const T*>(a.out) + (size_t)row * D;
-  const T* g = reinterpret_cast<const T*>(a.dout) + (size_t)row * D;
+  const bool ok = row < total;
+  const int rr = ok ? row : total - 1;
+  const T* o = reinterpret_cast<const T*>(a.out) + (size_t)rr * D + sub * EPL;
+  const T* g = reinterpret_cast<const T*>(a.dout) + (size_t)rr * D + sub * EPL;
   float acc = 0.f;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc += to_f32(o[lane + 64 * e]) * to_f32(g[lane + 64 * e]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) {
+  for (int e = 0; e < EPL; ++e) acc += to_f32(o[e]) * to_f32(g[e]);
+  acc = row_sum<16>(acc);
+  if (!ok) return;
+  if (sub == 0) {
+    const int h = row % a.Hq;
+    const int bi = row / a.Hq;
+    const int i = bi % a.n;
+    const int b = bi / a.n;
     const size_t li = ((size_t)b * a.Hq + h) * a.n + i;
     a.delta[li] = acc;
     a.lse2[li] = a.lse[li] * kLog2e;
   }
   if (a.zero_dq) {
-    float* dq = a.dq_acc + (size_t)row * D;
+    float* dq = a.dq_acc + (size_t)row * D + sub * EPL;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) dq[lane + 64 * e] = 0.f;
+    for (int e = 0; e < EPL; ++e) dq[e] = 0.f;
   }
 }
 
@@ -1207,7 +1210,7 @@ size_t bwd_workspace_bytes(const AttnDims& d) {
 template <int D>
 static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
-  CART_TIMED("bwd_preprocess", st, bwd_preprocess<float, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
+  CART_TIMED("bwd_preprocess", st, bwd_preprocess<float, D><<<(rows + 15) / 16, 256, 0, st>>>(a));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CART_TIMED("attn_bwd", st,
@@ -1231,7 +1234,7 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_
 template <int D>
 static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
-  CART_TIMED("bwd_preprocess", st, bwd_preprocess<bf16, D><<<(rows + 3) / 4, 256, 0, st>>>(a));
+  CART_TIMED("bwd_preprocess", st, bwd_preprocess<bf16, D><<<(rows + 15) / 16, 256, 0, st>>>(a));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CART_TIMED("attn_bwd", st, attn_bwd_kv_kernel<D><<<pl.grid_kv, kThreads, 0, st>>>(a));

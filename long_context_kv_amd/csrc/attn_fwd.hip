@@ -530,34 +530,43 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 }
 
 // Merge split partials: lse = log sum_s exp(lse_s); O = sum_s exp(lse_s - lse) O_s.
-// One thread per (b, i, h) row, D/4 float4 lanes... kept simple: one wave per row.
+// Merge the split-KV partials of each (b, i, h) row by their LSE. Sixteen
+// lanes per row (D/16 output elements each), 16 rows per workgroup.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void attn_fwd_combine(FwdArgs a) {
-  const int row = blockIdx.x;             // (b, i, h) with h fastest
+__global__ __launch_bounds__(256) void attn_fwd_combine(FwdArgs a) {
+  constexpr int EPL = D / 16;
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);   // (b, i, h), h fastest
+  const int sub = threadIdx.x & 15;
+  if (row >= a.B * a.n * a.Hq) return;
   const int h = row % a.Hq;
   const int bi = row / a.Hq;
   const int i = bi % a.n;
   const int b = bi / a.n;
-  const int lane = threadIdx.x;
+  const size_t lrow = ((size_t)b * a.Hq + h) * a.n + i;
+  const size_t lstride = (size_t)a.B * a.Hq * a.n;
+  const size_t ostride = (size_t)a.B * a.n * a.Hq * D;
   float mx = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s)
-    mx = fmaxf(mx, a.lse_part[(((size_t)s * a.B + b) * a.Hq + h) * a.n + i]);
+  for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, a.lse_part[s * lstride + lrow]);
   float tot = 0.f;
-  float o[D / 64];
+  float o[EPL];
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  const float* op = a.o_part + (size_t)row * D + sub * EPL;
   for (int s = 0; s < a.n_splits; ++s) {
-    const float ls = a.lse_part[(((size_t)s * a.B + b) * a.Hq + h) * a.n + i];
+    const float ls = a.lse_part[s * lstride + lrow];
     const float w = (ls == -INFINITY) ? 0.f : expf(ls - mx);
     tot += w;
-    const float* op = a.o_part + ((((size_t)s * a.B + b) * a.n + i) * a.Hq + h) * D;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) o[e] += w * op[lane + 64 * e];
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(op + s * ostride + e);
+      o[e] += w * v.x; o[e + 1] += w * v.y; o[e + 2] += w * v.z; o[e + 3] += w * v.w;
+    }
   }
-  T* out = reinterpret_cast<T*>(a.out) + (((size_t)b * a.n + i) * a.Hq + h) * D;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  T* out = reinterpret_cast<T*>(a.out) + (size_t)row * D + sub * EPL;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = from_f32<T>(o[e] / tot);
-  if (lane == 0) a.lse[((size_t)b * a.Hq + h) * a.n + i] = mx + logf(tot);
+  for (int e = 0; e < EPL; ++e) out[e] = from_f32<T>(o[e] * inv);
+  if (sub == 0) a.lse[lrow] = mx + logf(tot);
 }
 
 }  // namespace
@@ -597,7 +606,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, const FwdPlan& pl, hipStream_t 
   CART_TIMED("attn_fwd", st, attn_fwd_kernel<T, TR, D><<<pl.grid, kThreads, 0, st>>>(a));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_splits == 1) return e;
-  CART_TIMED("attn_fwd_combine", st, attn_fwd_combine<T, D><<<a.B * a.n * a.Hq, 64, 0, st>>>(a));
+  CART_TIMED("attn_fwd_combine", st, attn_fwd_combine<T, D><<<(a.B * a.n * a.Hq + 15) / 16, 256, 0, st>>>(a));
   return hipGetLastError();
 }
 
@@ -607,7 +616,7 @@ static hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdPlan& pl, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_splits == 1) return e;
   CART_TIMED("attn_fwd_combine", st,
-             attn_fwd_combine<bf16, D><<<a.B * a.n * a.Hq, 64, 0, st>>>(a));
+             attn_fwd_combine<bf16, D><<<(a.B * a.n * a.Hq + 15) / 16, 256, 0, st>>>(a));
   return hipGetLastError();
 }
 

@@ -135,6 +135,23 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// Sum over aligned groups of N lanes (N = 8 or 16) by DPP adds: swap lanes
+// 1 apart, 2 apart, then mirror halves of 8 and of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                             0xF, true));
+}
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(N == 8 || N == 16, "row of 8 or 16 lanes");
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  if constexpr (N == 16) x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ float wave_max_halves(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }
