@@ -430,20 +430,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   constexpr int QTILE = tile_elems<D, kBQ>();
   constexpr int QBLK = QTILE / 512;
   constexpr int QPW = (QBLK + 3) / 4;
-  // 3-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
-  // A stage is read while a copy fills another one, so every LDS read of the
-  // unit loop is issued by the inline-assembly helpers, with explicit waits.
+  // 4-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
+  // The copy of a unit is issued two steps before it is used, spread over
+  // the MFMAs of a step. Stages are read while copies fill others, so every
+  // LDS read of the unit loop is issued by the inline-assembly helpers, with
+  // explicit waits.
+  constexpr int NST = 4;
   constexpr int STAGE = 2 * QTILE + 2 * 2 * kBQ;   // bf16 elements per stage
   constexpr int O_OFF = 2 * QTILE;                  // byte offset of dO in a stage
   constexpr int L_OFF = 4 * QTILE;                  // byte offset of lse / D
-  __shared__ __align__(16) bf16 ring[3 * STAGE];
+  __shared__ __align__(16) bf16 ring[NST * STAGE];
   auto Qst = [&](int st) { return ring + st * STAGE; };
   auto Ost = [&](int st) { return ring + st * STAGE + QTILE; };
   auto Lst = [&](int st) { return reinterpret_cast<float*>(ring + st * STAGE + 2 * QTILE); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
@@ -526,34 +529,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     c_roff[k] = r * q_row_bytes;
     c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
   }
-  auto issue = [&](const Unit& x, bf16* Qs, bf16* Os, float* Ls) {
+  // The copy of one unit, in parts: part k < QPW copies this wave's k-th
+  // 1 KiB block of the Q and dO tiles, part QPW the lse (wave 0) or D
+  // (wave 1) row.
+  struct Copy { buf_rsrc rq, ro, rl; int lim, rows; bf16* Qs; bf16* Os; float* Ls; };
+  auto copy_setup = [&](const Unit& x, int st) {
+    Copy c;
     const int h = kv * a.g + x.hin;
     const int i0 = x.qt * kBQ;
-    const int rows = min(kBQ, a.n - i0);
-    const int lim = (rows - 1) * q_row_bytes;
+    c.rows = min(kBQ, a.n - i0);
+    c.lim = (c.rows - 1) * q_row_bytes;
     const size_t base = (((size_t)x.bb * a.n + i0) * a.Hq + h) * D * 2;
-    const buf_rsrc rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, lim + D * 2);
-    const buf_rsrc ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + base, lim + D * 2);
-#pragma unroll
-    for (int k = 0; k < QPW; ++k) {
+    c.rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, c.lim + D * 2);
+    c.ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + base, c.lim + D * 2);
+    const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0;
+    c.rl = make_rsrc((wave == 0 ? a.lse2 : a.delta) + li, 4 * c.rows);
+    c.Qs = Qst(st);
+    c.Os = Ost(st);
+    c.Ls = Lst(st);
+    return c;
+  };
+  auto copy_part = [&](const Copy& c, int k) {
+    if (k < QPW) {
       const int blk = 4 * k + wave;
       if (blk < QBLK) {
-        const uint32_t off = min(c_roff[k], lim) + c_coff[k];
-        dma16(rq, off, Qs + blk * 512);
-        dma16(ro, off, Os + blk * 512);
+        const uint32_t off = min(c_roff[k], c.lim) + c_coff[k];
+        dma16(c.rq, off, c.Qs + blk * 512);
+        dma16(c.ro, off, c.Os + blk * 512);
       }
+    } else if (k == QPW && wave < 2) {
+      // wave 0 copies lse*log2(e) into Ls[0, 32), wave 1 copies D into Ls[32, 64)
+      if (lane < 32) dma4(c.rl, 4 * min(l32, c.rows - 1), c.Ls + 32 * wave);
     }
-    if (wave == 0) {
-      // lanes 0..31 copy lse*log2(e), lanes 32..63 copy D
-      const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0;
-      const uint32_t off = 4 * min(l32, rows - 1);
-      if (lane < 32) dma4(make_rsrc(a.lse2 + li, 4 * rows), off, Ls);
-      else dma4(make_rsrc(a.delta + li, 4 * rows), off, Ls);
-    }
+  };
+  auto issue = [&](const Unit& x, int st) {
+    const Copy c = copy_setup(x, st);
+#pragma unroll
+    for (int k = 0; k <= QPW; ++k) copy_part(c, k);
   };
 
   // ---- the wave's K, V rows as B operands
-  if (u_begin < u_end) issue(cu, Qst(0), Ost(0), Lst(0));
+  if (u_begin < u_end) issue(cu, 0);
   bf16x8 kf[NKS], vf[NKS];
   {
     const int kr = key_ok ? my_key : limit - 1;
@@ -658,7 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // packed results go to pf2, sf2. Starts and ends with no LDS read pending.
   auto phase_b = [&](auto NEXT, auto MASK, uint32_t stage, const bf16x8 (&pf)[2],
                      const bf16x8 (&sf)[2], uint32_t rel, const LD& ld, f32x16& s, f32x16& g,
-                     bf16x8 (&pf2)[2], bf16x8 (&sf2)[2]) {
+                     bf16x8 (&pf2)[2], bf16x8 (&sf2)[2], auto&& per_step) {
     constexpr bool N = decltype(NEXT)::value;
     TrOp t[2];
     tr_frag(stage, std::integral_constant<int, 0>{}, t[0]);
@@ -676,6 +692,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       dv[db] = M::mma(pf[m], t[ks & 1].o, dv[db]);
       dk[db] = M::mma(sf[m], t[ks & 1].q, dk[db]);
+      per_step(ks);
       if constexpr (N) {
         constexpr int per = 16 / NKS;   // result registers per k-step
 #pragma unroll
@@ -694,15 +711,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const uint32_t ring_base = lds_addr(ring);
   auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
 
+  // Wait until at most the copies of `units` later units (0, 1 or 2) issued
+  // by this wave are in flight; the count is a constant per wave.
+  auto wait_copies = [&](int units) {
+    static_for<4>([&](auto W) {
+      constexpr int w = decltype(W)::value;
+      constexpr int nd = 2 * ((QBLK - w + 3) / 4) + (w < 2 ? 1 : 0);
+      if (wave == w) {
+        if (units == 2) CART_WAIT_VMCNT(2 * nd);
+        else if (units == 1) CART_WAIT_VMCNT(nd);
+        else CART_WAIT_VMCNT(0);
+      }
+    });
+  };
+  static_assert(2 * (2 * QPW + 1) < 64, "copies of two units must fit the wait count");
+  static_assert(QPW + 1 <= NKS, "a unit's copy parts must fit the k-steps of phase B");
+  auto no_extra = [](int) {};
+
   if (u_begin < u_end) {
     const int nu = u_end - u_begin;
-    Unit u1 = next(cu);
-    if (nu > 1) issue(u1, Qst(1), Ost(1), Lst(1));
-    CART_WAIT_VMCNT(0);
+    // units 0, 1, 2 are copied before the loop (unit 0's copy was issued above)
+    Unit u1 = next(cu), u2 = next(u1);
+    if (nu > 1) issue(u1, 1);
+    if (nu > 2) issue(u2, 2);
+    // unit 0 has landed once only the copies of units 1 and 2 may be pending
+    // (the K/V operand loads are older than all of them)
+    wait_copies(min(nu, 3) - 1);
     lds_barrier();
     bf16x8 pf[2], sf[2];
     {
-      // unit 0 (no copy targets stage 0 meanwhile): S and dP, then softmax
+      // unit 0: S and dP, then its softmax
       const uint32_t st0 = stage_addr(0);
       LD ld;
       read_ld(st0, ld);
@@ -710,47 +748,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       phase_a(st0, s, g);
       tie_ld(ld);
       const uint32_t rel = mask_rel(cu);
-      if (unit_needs_mask(cu)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) softmax_elem(Yes{}, r, rel, ld, s, g);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) softmax_elem(No{}, r, rel, ld, s, g);
-      }
+      for (int r = 0; r < 16; ++r) softmax_elem(Yes{}, r, rel, ld, s, g);
       pf[0] = pack_regs<bf16>(s, 0);
       pf[1] = pack_regs<bf16>(s, 1);
       sf[0] = pack_regs<bf16>(g, 0);
       sf[1] = pack_regs<bf16>(g, 1);
     }
-    // Step k (k = 0 .. nu-2): unit k in stage k%3, unit k+1 in stage
-    // (k+1)%3, and the copy of unit k+2 goes to stage (k+2)%3, last read in
-    // step k-1, which every wave has left at the barrier. Phase A of unit
-    // k+1, then phase B of unit k with the softmax of unit k+1.
-    Unit un = u1, uf = next(u1);
+    // Step k (k = 0 .. nu-2): unit k in stage k%4, unit k+1 in stage
+    // (k+1)%4, unit k+2's copy possibly in flight; the copy of unit k+3 goes
+    // to stage (k+3)%4 (last read in step k-1, which every wave has left at
+    // the barrier), its parts issued between the MFMAs of phase B. Phase A of
+    // unit k+1, then phase B of unit k with the softmax of unit k+1.
+    Unit un = u1, uf = next(u2);
     int sk = 0;
     for (int k = 0; k < nu - 1; ++k) {
-      const int sn = sk == 2 ? 0 : sk + 1;
-      const int sf_ = sn == 2 ? 0 : sn + 1;
-      CART_WAIT_VMCNT(0);
+      const int sn = (sk + 1) & (NST - 1);
+      const int sf_ = (sk + 3) & (NST - 1);
+      wait_copies(k + 2 < nu ? 1 : 0);   // unit k+1 has landed
       lds_barrier();
       const uint32_t stn = stage_addr(sn);
       LD ld;
       read_ld(stn, ld);
-      __builtin_amdgcn_sched_barrier(0);
-      if (k + 2 < nu) issue(uf, Qst(sf_), Ost(sf_), Lst(sf_));
-      __builtin_amdgcn_sched_barrier(0);
       f32x16 s, g;
       phase_a(stn, s, g);
       tie_ld(ld);
       bf16x8 pf2[2], sf2[2];
       const uint32_t rel = mask_rel(un);
-      const uint32_t stk = stage_addr(sk);
+      const bool more = k + 3 < nu;
+      const Copy cp = copy_setup(uf, sf_);
+      auto copy_step = [&](int ks) {
+        if (more) copy_part(cp, ks);
+      };
       // one code path: the mask select costs less than a second copy of
       // phase B costs in register moves
-      phase_b(Yes{}, Yes{}, stk, pf, sf, rel, ld, s, g, pf2, sf2);
+      phase_b(Yes{}, Yes{}, stage_addr(sk), pf, sf, rel, ld, s, g, pf2, sf2, copy_step);
       pf[0] = pf2[0]; pf[1] = pf2[1];
       sf[0] = sf2[0]; sf[1] = sf2[1];
-      un = uf;
+      un = next(un);
       uf = next(uf);
       sk = sn;
     }
@@ -758,7 +793,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       LD ld;
       f32x16 s, g;
       bf16x8 pf2[2], sf2[2];
-      phase_b(No{}, No{}, stage_addr(sk), pf, sf, 0u, ld, s, g, pf2, sf2);
+      phase_b(No{}, No{}, stage_addr(sk), pf, sf, 0u, ld, s, g, pf2, sf2, no_extra);
     }
   }
 
