@@ -530,8 +530,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
   }
   // The copy of one unit, in parts: part k < QPW copies this wave's k-th
-  // 1 KiB block of the Q and dO tiles, part QPW the lse (wave 0) or D
-  // (wave 1) row.
+  // 1 KiB block of the Q and dO tiles, part QPW the lse (wave 2) or D
+  // (wave 3) row in two halves. Every wave issues the same number of copies
+  // per unit, so the wait counts of the ring are constants.
+  constexpr int NDMA = 2 * QPW;
+  static_assert(2 * ((QBLK + 3) / 4) == NDMA && 2 * ((QBLK + 2) / 4) == NDMA &&
+                    2 * ((QBLK + 1) / 4) + 2 == NDMA && 2 * (QBLK / 4) + 2 == NDMA,
+                "copies per unit differ between waves");
   struct Copy { buf_rsrc rq, ro, rl; int lim, rows; bf16* Qs; bf16* Os; float* Ls; };
   auto copy_setup = [&](const Unit& x, int st) {
     Copy c;
@@ -543,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     c.rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, c.lim + D * 2);
     c.ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + base, c.lim + D * 2);
     const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0;
-    c.rl = make_rsrc((wave == 0 ? a.lse2 : a.delta) + li, 4 * c.rows);
+    c.rl = make_rsrc((wave == 2 ? a.lse2 : a.delta) + li, 4 * c.rows);
     c.Qs = Qst(st);
     c.Os = Ost(st);
     c.Ls = Lst(st);
@@ -557,9 +562,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
         dma16(c.rq, off, c.Qs + blk * 512);
         dma16(c.ro, off, c.Os + blk * 512);
       }
-    } else if (k == QPW && wave < 2) {
-      // wave 0 copies lse*log2(e) into Ls[0, 32), wave 1 copies D into Ls[32, 64)
-      if (lane < 32) dma4(c.rl, 4 * min(l32, c.rows - 1), c.Ls + 32 * wave);
+    } else if (k == QPW && wave >= 2) {
+      // wave 2 copies lse*log2(e) into Ls[0, 32), wave 3 copies D into Ls[32, 64)
+      float* dst = c.Ls + 32 * (wave - 2);
+      if (lane < 16) {
+        dma4(c.rl, 4 * min(lane, c.rows - 1), dst);
+        dma4(c.rl, 4 * min(lane + 16, c.rows - 1), dst + 16);
+      }
     }
   };
   auto issue = [&](const Unit& x, int st) {
@@ -711,20 +720,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const uint32_t ring_base = lds_addr(ring);
   auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
 
-  // Wait until at most the copies of `units` later units (0, 1 or 2) issued
-  // by this wave are in flight; the count is a constant per wave.
+  // Wait until at most the copies of `units` later units (0, 1 or 2) are in
+  // flight.
   auto wait_copies = [&](int units) {
-    static_for<4>([&](auto W) {
-      constexpr int w = decltype(W)::value;
-      constexpr int nd = 2 * ((QBLK - w + 3) / 4) + (w < 2 ? 1 : 0);
-      if (wave == w) {
-        if (units == 2) CART_WAIT_VMCNT(2 * nd);
-        else if (units == 1) CART_WAIT_VMCNT(nd);
-        else CART_WAIT_VMCNT(0);
-      }
-    });
+    if (units == 2) CART_WAIT_VMCNT(2 * NDMA);
+    else if (units == 1) CART_WAIT_VMCNT(NDMA);
+    else CART_WAIT_VMCNT(0);
   };
-  static_assert(2 * (2 * QPW + 1) < 64, "copies of two units must fit the wait count");
+  static_assert(2 * NDMA < 64, "copies of two units must fit the wait count");
   static_assert(QPW + 1 <= NKS, "a unit's copy parts must fit the k-steps of phase B");
   auto no_extra = [](int) {};
 
