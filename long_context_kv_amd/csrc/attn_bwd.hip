@@ -425,10 +425,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int TS = tstr<D>();
-  constexpr int CPR = TS / 8;
-  constexpr int QTILE = tile_elems<D, kBQ>();
-  constexpr int QBLK = QTILE / 512;
+  using TL = Tile<D>;
+  // Q / dO tiles in whole 1 KiB blocks, 2 more than a multiple of 4 (waves 0
+  // and 1 copy one block more than waves 2 and 3, which copy lse and D)
+  constexpr int QBLK0 = (tile_elems<D, kBQ>() + 511) / 512;
+  constexpr int QBLK = QBLK0 + ((2 - QBLK0 % 4) + 4) % 4;
+  constexpr int QTILE = QBLK * 512;
   constexpr int QPW = (QBLK + 3) / 4;
   // 4-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
   // The copy of a unit is issued two steps before it is used, spread over
@@ -523,9 +525,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   int c_roff[QPW], c_coff[QPW];
 #pragma unroll
   for (int k = 0; k < QPW; ++k) {
-    const int chunk = (4 * k + wave) * 64 + lane;
-    const int r = chunk / CPR;
-    const int cc = chunk % CPR;
+    int r, cc;
+    TL::locate((4 * k + wave) * 64 + lane, r, cc);
     c_roff[k] = r * q_row_bytes;
     c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
   }
@@ -599,8 +600,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // Per-lane LDS byte offsets inside a stage: the row fragment (row l32,
   // 8 elements at 8 hl) and the transpose strip (tr_col4's lane pattern for
   // rows 4 hl .., columns 16 ((lane >> 4) & 1) ..).
-  const uint32_t row_lane = 2 * t_off<D>(l32, 8 * hl);
-  const uint32_t tr_lane = 2 * ((4 * hl + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  const uint32_t row_lane = TL::off(l32, 8 * hl);
+  const uint32_t tr_lane = TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   const uint32_t ld_lane = 16 * hl;
 
   // lse*log2(e) and D of the 16 queries of a lane's result registers
@@ -640,10 +641,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   struct TrOp { bf16x8 o, q; };
   auto tr_frag = [&](uint32_t stage, auto F, TrOp& t) {
     constexpr int f = decltype(F)::value;
-    constexpr int off = 2 * (16 * (f / NDB) * TS + 32 * (f % NDB));
+    constexpr int off = TL::rows(16 * (f / NDB)) + 2 * 32 * (f % NDB);
     const uint32_t base = stage + tr_lane;
-    t.o = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + 16 * TS>(base));
-    t.q = cat8(lds_tr4<off>(base), lds_tr4<off + 16 * TS>(base));
+    t.o = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + TL::rows(8)>(base));
+    t.q = cat8(lds_tr4<off>(base), lds_tr4<off + TL::rows(8)>(base));
   };
   // Phase A: S = Q K^T and dP = dO V^T of one unit (rows = queries, columns
   // = this wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)).
@@ -847,7 +848,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int TS = tstr<D>();
+  using TL = Tile<D>;
   __shared__ __align__(16) bf16 K0[tile_elems<D, kKvTile>()];
   __shared__ __align__(16) bf16 V0[tile_elems<D, kKvTile>()];
   __shared__ __align__(16) bf16 K1[tile_elems<D, kKvTile>()];
@@ -879,7 +880,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int t_end = (int)((long long)(split + 1) * nt_all / a.q_splits);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
-  if (t_begin < t_end) kv_issue<D>(K0, V0, t_begin, n_ct, src, wave, lane);
+  const KvMap<D> kmap(wave, lane);
+  if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
 
   // Q^T and dO^T as B operands: lane (q + 32 hl) holds row q, 8 columns per k-step.
   bf16x8 qf[NKS], of[NKS];
@@ -910,9 +912,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   // by the inline-assembly helpers with explicit waits (the copy of the next
   // tile into the other stage is in flight meanwhile), one step ahead of the
   // MFMAs that use them.
-  const uint32_t row_lane = 2 * t_off<D>(l32, 8 * hl);
-  const uint32_t tr_lane = 2 * ((4 * hl + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) +
-                                4 * (lane & 3));
+  const uint32_t row_lane = TL::off(l32, 8 * hl);
+  const uint32_t tr_lane = TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   auto compute = [&](uint32_t kst, uint32_t vst, const KvTile& f) {
     // S^T = K Q^T and dP^T = V dO^T for the two 32-key halves: K and V row
     // fragments (row 32 kh + l32, 8 elements at 16 ks + 8 hl), four reads
@@ -923,9 +924,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       auto rd = [&](auto KS, int slot) {
         constexpr int ks = decltype(KS)::value;
         kr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kst + row_lane));
-        kr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<2 * 32 * TS + 32 * ks>(kst + row_lane));
+        kr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(kst + row_lane));
         vr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(vst + row_lane));
-        vr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<2 * 32 * TS + 32 * ks>(vst + row_lane));
+        vr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(vst + row_lane));
       };
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; dp[0][r] = 0.f; dp[1][r] = 0.f; }
@@ -978,8 +979,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         constexpr int j = decltype(J)::value;
         static_for<NDB>([&](auto DB) {
           constexpr int db = decltype(DB)::value;
-          constexpr int off = 2 * ((16 * j) * TS + 32 * db);
-          ka[slot][db] = cat8(lds_tr4<off>(kb), lds_tr4<off + 16 * TS>(kb));
+          constexpr int off = TL::rows(16 * j) + 2 * 32 * db;
+          ka[slot][db] = cat8(lds_tr4<off>(kb), lds_tr4<off + TL::rows(8)>(kb));
         });
       };
       rdk(std::integral_constant<int, 0>{}, 0);
@@ -1006,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   for (int t = t_begin; t < t_end; t += 2) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 1 < t_end) kv_issue<D>(K1, V1, t + 1, n_ct, src, wave, lane);
+    if (t + 1 < t_end) kv_issue<D>(kmap, K1, V1, t + 1, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
@@ -1015,7 +1016,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 2 < t_end) kv_issue<D>(K0, V0, t + 2, n_ct, src, wave, lane);
+    if (t + 2 < t_end) kv_issue<D>(kmap, K0, V0, t + 2, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);

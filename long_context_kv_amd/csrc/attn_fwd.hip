@@ -310,19 +310,19 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int TS = tstr<D>();
+  using TL = Tile<D>;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
   // S^T = K Q^T for the two 32-key halves: K row fragments (row 32 kh + l32,
   // 8 elements at 16 ks + 8 hl), two reads per k-step.
   f32x16 s[2];
   {
-    const uint32_t kb = kst + 2 * t_off<D>(l32, 8 * hl);
+    const uint32_t kb = kst + TL::off(l32, 8 * hl);
     bf16x8 kfr[2][2];
     auto rd = [&](auto KS, int slot) {
       constexpr int ks = decltype(KS)::value;
       kfr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
-      kfr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<2 * 32 * TS + 32 * ks>(kb));
+      kfr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(kb));
     };
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; }
@@ -387,15 +387,14 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
   // O^T += V^T P^T in four steps j = (kh, m): V^T fragments by transpose
   // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
   {
-    const uint32_t vb = vst + 2 * ((4 * hl + ((lane & 15) >> 2)) * TS + 16 * ((lane >> 4) & 1) +
-                                   4 * (lane & 3));
+    const uint32_t vb = vst + TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
     bf16x8 va[2][NDB];
     auto rdv = [&](auto J, int slot) {
       constexpr int j = decltype(J)::value;
       static_for<NDB>([&](auto DB) {
         constexpr int db = decltype(DB)::value;
-        constexpr int off = 2 * ((16 * j) * TS + 32 * db);
-        va[slot][db] = cat8(lds_tr4<off>(vb), lds_tr4<off + 16 * TS>(vb));
+        constexpr int off = TL::rows(16 * j) + 2 * 32 * db;
+        va[slot][db] = cat8(lds_tr4<off>(vb), lds_tr4<off + TL::rows(8)>(vb));
       });
     };
     rdv(std::integral_constant<int, 0>{}, 0);
@@ -455,7 +454,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int t_end = (int)((long long)(split + 1) * nt / a.n_splits);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
-  if (t_begin < t_end) kv_issue<D>(K0, V0, t_begin, n_ct, src, wave, lane);
+  const KvMap<D> kmap(wave, lane);
+  if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
 
   bf16x8 qf[NKS];
   {
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int t = t_begin; t < t_end; t += 2) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 1 < t_end) kv_issue<D>(K1, V1, t + 1, n_ct, src, wave, lane);
+    if (t + 1 < t_end) kv_issue<D>(kmap, K1, V1, t + 1, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 2 < t_end) kv_issue<D>(K0, V0, t + 2, n_ct, src, wave, lane);
+    if (t + 2 < t_end) kv_issue<D>(kmap, K0, V0, t + 2, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);

@@ -189,23 +189,81 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 namespace cartattn {
 
 // ---- LDS tiles for the bf16 kernels -------------------------------------
-// A tile of R rows x D bf16 is stored with rows padded to TSTR elements. For
-// D = 128 the stride is 152 elements (76 dwords): measured on gfx950 it lets
-// both access patterns of the kernels run near the LDS peak or at the best
-// rate any plain padding reaches (16-byte row reads with one row per lane
-// about 230 B/clk per CU, transpose reads of 4 rows x 32 bytes per 16-lane
-// group about 93 B/clk; a 144-element stride gave 124 and 92). Every
-// fragment address is a per-lane base plus a compile-time offset.
+// A tile of R rows x D bf16 (R a multiple of 8) is stored row by row in
+// groups of 8 rows. Row j of a group starts phi(j) 16-byte chunks past its
+// unpadded place, and groups are GRP bytes apart. The shifts are chosen for
+// the two read patterns of the kernels, on an LDS of 64 four-byte banks:
+//  * a 16-byte row fragment per lane, rows 16 i .. 16 i + 15 of one column
+//    chunk per 16 lanes: the 16 rows start in 16 different chunk residues
+//    (mod 16) of the bank space;
+//  * a transpose read, 4 rows x 64 bytes per 32 lanes: the 4 rows of an
+//    aligned group of 4 start in residues 4 apart, so their 16-dword windows
+//    are disjoint.
+// Rows 0-3 of a group take residues = 0 (mod 4), rows 4-7 residues = 1, and
+// GRP = 2 (mod 4) chunks moves the next group to residues 2 and 3. Measured
+// on gfx950 for D = 128 this gives about 222 B/clk per CU for row fragments
+// and 178 B/clk for transpose reads, against 213 and 111 for a plain row
+// padding of 24 elements (the best plain padding for both patterns at
+// once). Every fragment address is a per-lane base plus a compile-time
+// offset, since row offsets used as immediates are multiples of 8 rows.
 template <int D>
-constexpr int tstr() { return D + 24; }
+struct Tile {
+  static constexpr int RC = D / 8;   // 16-byte chunks of a row
+  static constexpr int phi(int j) {
+    int f = 0, used = 0;
+    for (int r = 0;; ++r) {
+      if ((r & 3) == 0) used = 0;
+      while ((((RC * r + f) & 3) != (r >> 2)) || ((used >> ((RC * r + f) & 15)) & 1)) ++f;
+      used |= 1 << ((RC * r + f) & 15);
+      if (r == j) return f;
+    }
+  }
+  // first chunk of row j (0..7) inside its group
+  static constexpr int start(int j) { return RC * j + phi(j); }
+  static constexpr int span() { return start(7) + RC; }
+  static constexpr int GC = span() + ((2 - span() % 4) + 4) % 4;   // chunks per group
+  static constexpr int GRP = 16 * GC;                              // bytes per group
+  // start(j) for a run-time j in closed form (checked against start below)
+  __host__ __device__ static constexpr int start_rt(int j) {
+    return RC * j + 4 * (RC == 16 ? j : j >> 1) - 3 * (j >> 2);
+  }
+  static constexpr bool closed_form_ok() {
+    for (int j = 0; j < 8; ++j)
+      if (start_rt(j) != start(j)) return false;
+    return true;
+  }
+  // byte offset of (row r, column col) in the tile
+  __host__ __device__ static constexpr int off(int r, int col) {
+    return (r >> 3) * GRP + 16 * start_rt(r & 7) + 2 * col;
+  }
+  // byte offset between rows r and r + rows8 (rows8 a multiple of 8)
+  static constexpr int rows(int rows8) { return rows8 / 8 * GRP; }
+  // Row and column chunk stored at chunk position pos of the tile; cc >= RC
+  // marks padding.
+  __host__ __device__ static inline void locate(int pos, int& row, int& cc) {
+    // evaluated by the compiler (start() is a loop, kept off the GPU)
+    constexpr int st[8] = {start(0), start(1), start(2), start(3),
+                           start(4), start(5), start(6), start(7)};
+    const int g = pos / GC;
+    const int o = pos - g * GC;
+    int j = 0, s = 0;
+#pragma unroll
+    for (int t = 1; t < 8; ++t)
+      if (o >= st[t]) { j = t; s = st[t]; }
+    row = 8 * g + j;
+    cc = o - s;
+  }
+};
+static_assert(Tile<128>::GC % 4 == 2 && Tile<64>::GC % 4 == 2, "group size");
+static_assert(Tile<128>::closed_form_ok() && Tile<64>::closed_form_ok(), "row starts");
+static_assert(Tile<128>::GRP == 2464 && Tile<64>::GRP == 1184, "tile layout");
 
-// Elements allocated for a tile of NROWS rows: whole 1 KiB blocks, so that
-// the asynchronous copy of the last block stays inside the allocation.
+// Elements of a tile of NROWS rows (a multiple of 8 elements).
 template <int D, int NROWS>
-constexpr int tile_elems() { return (NROWS * tstr<D>() + 511) / 512 * 512; }
-
-template <int D>
-__device__ __forceinline__ int t_off(int r, int col) { return r * tstr<D>() + col; }
+constexpr int tile_elems() {
+  static_assert(NROWS % 8 == 0, "tiles hold whole groups of 8 rows");
+  return (NROWS / 8) * Tile<D>::GRP / 2;
+}
 
 // Asynchronous global->LDS copies use buffer loads with the LDS bit (MUBUF
 // encoding): lane l of one instruction writes its 16 bytes to byte 16*l past
@@ -226,29 +284,47 @@ __device__ __forceinline__ void dma4(buf_rsrc r, uint32_t voff, void* lds) {
                                            (int)voff, 0, 0, 0);
 }
 
-// Issue this wave's share of an asynchronous copy of a tile of NROWS rows x D
-// bf16 (global rows `row_stride` elements apart) into a padded LDS tile of
-// tile_elems<D, NROWS>() elements, written by 1 KiB loads spread over the 4
-// waves. Lanes whose 16 bytes fall on row padding re-read a chunk of their
-// row, and rows at or past `rows` (including the rounding past NROWS) re-read
-// row rows-1 (finite data the caller masks), so no offset leaves the source
-// rows.
+// Per-lane source positions of this wave's share of the asynchronous copy of
+// a tile of NROWS rows x D bf16 into an LDS tile of tile_elems<D, NROWS>()
+// elements laid out as Tile<D> describes: 1 KiB loads spread over the 4
+// waves, lane l of block blk writing chunk position 64 blk + l (lanes past
+// the end of the tile in the last block are switched off). Computed once per
+// kernel: pk[k] = row << 16 | byte offset of the column chunk, for the
+// wave's k-th block. Lanes whose 16 bytes fall on padding re-read chunk 0 of
+// a row.
 template <int D, int NROWS>
-__device__ __forceinline__ void dma_tile(bf16* lds, const bf16* src, size_t row_stride, int rows,
-                                         int wave, int lane) {
-  constexpr int CPR = tstr<D>() / 8;                  // 16-byte chunks per padded row
-  constexpr int NBLK = tile_elems<D, NROWS>() / 512;   // 1 KiB loads for the tile
+struct TileMap {
+  static constexpr int CHUNKS = tile_elems<D, NROWS>() / 8;
+  static constexpr int NBLK = (CHUNKS + 63) / 64;
+  static constexpr int LAST = CHUNKS - 64 * (NBLK - 1);   // lanes of the last block
+  static constexpr int NK = (NBLK + 3) / 4;
+  uint32_t pk[NK];
+  __device__ TileMap(int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      int rr, cc;
+      Tile<D>::locate((4 * k + wave) * 64 + lane, rr, cc);
+      pk[k] = (uint32_t)rr << 16 | (uint32_t)(cc < D / 8 ? cc : 0) * 16;
+    }
+  }
+};
+
+// Issue this wave's share of the copy of a tile of NROWS rows (global rows
+// `row_stride` elements apart) into `lds`. Rows at or past `rows`
+// (including the rounding past NROWS) re-read row rows-1 (finite data the
+// caller masks), so no offset leaves the source rows.
+template <int D, int NROWS>
+__device__ __forceinline__ void dma_tile(const TileMap<D, NROWS>& m, bf16* lds, const bf16* src,
+                                         size_t row_stride, int rows, int wave, int lane) {
   const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
   const buf_rsrc r = make_rsrc(src, (uint32_t)(rows - 1) * rs_bytes + D * 2);
 #pragma unroll
-  for (int k = 0; k < (NBLK + 3) / 4; ++k) {
+  for (int k = 0; k < TileMap<D, NROWS>::NK; ++k) {
     const int blk = k * 4 + wave;
-    if (blk < NBLK) {
-      const int chunk = blk * 64 + lane;
-      const int rr = min(chunk / CPR, rows - 1);
-      int cc = chunk % CPR;
-      cc = cc < D / 8 ? cc : 0;
-      dma16(r, (uint32_t)rr * rs_bytes + cc * 16, lds + blk * 512);
+    if (blk < TileMap<D, NROWS>::NBLK) {
+      const uint32_t rr = min(m.pk[k] >> 16, (uint32_t)(rows - 1));
+      if (blk < TileMap<D, NROWS>::NBLK - 1 || lane < TileMap<D, NROWS>::LAST)
+        dma16(r, rr * rs_bytes + (m.pk[k] & 0xffffu), lds + blk * 512);
     }
   }
 }

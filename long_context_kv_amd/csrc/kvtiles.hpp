@@ -48,15 +48,18 @@ __device__ __forceinline__ KvSrc<D> kv_src(const void* k_cart, const void* v_car
   return s;
 }
 
+template <int D>
+using KvMap = TileMap<D, kKvTile>;
+
 // Issue this wave's share of the copy of tile t's K and V rows.
 template <int D>
-__device__ __forceinline__ void kv_issue(bf16* Kst, bf16* Vst, int t, int n_ct,
-                                         const KvSrc<D>& s, int wave, int lane) {
+__device__ __forceinline__ void kv_issue(const KvMap<D>& m, bf16* Kst, bf16* Vst, int t,
+                                         int n_ct, const KvSrc<D>& s, int wave, int lane) {
   const KvTile f = kv_tile(t, n_ct, s.p, s.n);
   const bf16* kb = (f.cart ? s.kc : s.kt) + (size_t)f.j0 * s.row_stride;
   const bf16* vb = (f.cart ? s.vc : s.vt) + (size_t)f.j0 * s.row_stride;
-  dma_tile<D, kKvTile>(Kst, kb, s.row_stride, f.rows, wave, lane);
-  dma_tile<D, kKvTile>(Vst, vb, s.row_stride, f.rows, wave, lane);
+  dma_tile<D, kKvTile>(m, Kst, kb, s.row_stride, f.rows, wave, lane);
+  dma_tile<D, kKvTile>(m, Vst, vb, s.row_stride, f.rows, wave, lane);
 }
 
 }  // namespace cartattn
