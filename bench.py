@@ -84,8 +84,8 @@ def _events_ms(fn, n):
 
 
 TRAIN_KERNELS = ("rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess",
-                 "attn_bwd", "attn_bwd_dq", "bwd_dq_combine", "bwd_tok_reduce",
-                 "bwd_dq_finalize", "bwd_cart_reduce")
+                 "attn_bwd", "attn_bwd_dq", "bwd_dq_combine", "bwd_dq_finalize",
+                 "bwd_cart_reduce")
 
 
 def train_bench(C, W, shape, steps, warmup):

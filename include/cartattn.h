@@ -231,8 +231,9 @@ size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
  * Launch timing (profiling aid). When enabled, every kernel launch of this
  * library is bracketed by two HIP events on its own stream. Kernel names:
  * "rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess",
- * "attn_bwd" (dK/dV), "attn_bwd_dq" (dQ of bf16 tokens), "bwd_dq_combine",
- * "bwd_tok_reduce", "bwd_dq_finalize" (dQ of f32 tokens), "bwd_cart_reduce",
+ * "attn_bwd" (dK/dV, including the reduction of key tiles cut into pieces,
+ * for bf16 tokens), "attn_bwd_dq" (dQ of bf16 tokens), "bwd_dq_combine",
+ * "bwd_dq_finalize" (dQ of f32 tokens), "bwd_cart_reduce" (f32 tokens),
  * "cache_append", "decode_append",
  * "decode", "decode_merge". cart_timing_enable clears earlier records (after
  * waiting for them). cart_timing_query waits for the recorded events of one

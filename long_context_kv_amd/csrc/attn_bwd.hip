@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <vector>
 
 #include <type_traits>
 
@@ -67,6 +68,8 @@ struct BwdArgs {
   float* dk_tpart;    // [kv_stmax][B][n][Hkv][D], token-tile pieces (bf16 path)
   float* dv_tpart;
   float* dq_part;     // [q_splits][B][n][Hq][D], dQ key-split pieces (bf16 path)
+  int* kv_cnt;        // [Hkv][n_ct + B n_tt] finished pieces per key tile (bf16 path)
+  int n_cnt;
   int kv_target, kv_ptok, kv_stmax, q_splits;
   int D4;             // head_dim / 4
   int B, n, p, f, Hq, Hkv, g;
@@ -801,44 +804,120 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     }
   }
 
-  // ---- dK (times the softmax scale), dV
+  // ---- dK (times the softmax scale), dV. A tile cut into pieces: every
+  // piece stores its f32 partial sums, and the piece that finishes last adds
+  // them up in piece order (the same sum whichever piece that is) and writes
+  // the tile's result.
   const float scale = a.scale;
+  auto out_off = [&](int j, int col) {
+    return cart ? ((size_t)j * a.Hkv + kv) * D + col
+                : (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
+  };
+  auto write = [&](int j, int col, float gk, float gv) {
+    const size_t o = out_off(j, col);
+    if (cart) {
+      if (j < a.f) {
+        a.dk_cart[o] = 0.f;
+        a.dv_cart[o] = 0.f;
+      } else if (a.accumulate) {
+        a.dk_cart[o] += gk;
+        a.dv_cart[o] += gv;
+      } else {
+        a.dk_cart[o] = gk;
+        a.dv_cart[o] = gv;
+      }
+    } else {
+      reinterpret_cast<bf16*>(a.dk_tok)[o] = (bf16)gk;
+      reinterpret_cast<bf16*>(a.dv_tok)[o] = (bf16)gv;
+    }
+  };
+  if (n_split == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 32 * wave + d_row(r, hl);
+      if (j >= limit) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        write(j, 32 * db + l32, dk[db][r] * scale, dv[db][r]);
+    }
+    return;
+  }
+  // Partial sums are exchanged at device scope without cache maintenance:
+  // stored write-through past the XCD's L2 (device-scope atomic stores),
+  // and read back around it (device-scope loads through buffer descriptors
+  // over this tile's rows of each piece's region; rows past the end fall
+  // outside and read as zero). A plain device-scope fence here would write
+  // back and invalidate the whole L2 of the XCD for every piece. (The
+  // stores are not buffer stores: a buffer store of a bit-cast accumulator
+  // element was compiled to store element 0 of its vector for every row.)
+  const size_t pstride = cart ? (size_t)a.p * row_stride : (size_t)a.B * a.n * row_stride;
+  const size_t pbase = cart ? 0 : (size_t)b * a.n * row_stride;
+  const uint32_t pbytes = (uint32_t)((size_t)limit * row_stride * 4);
+  float* pk = cart ? a.dk_part : a.dk_tpart;
+  float* pv = cart ? a.dv_part : a.dv_tpart;
+  const uint32_t lane_off = (uint32_t)((((size_t)(j0 + 32 * wave + 4 * hl)) * a.Hkv + kv) * D + l32) * 4;
+  const uint32_t row4 = (uint32_t)row_stride * 4;
+  auto roff = [&](int r) { return lane_off + (uint32_t)((r & 3) + 8 * (r >> 2)) * row4; };
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int j = j0 + 32 * wave + d_row(r, hl);
     if (j >= limit) continue;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int col = 32 * db + l32;
-      const float gk = dk[db][r] * scale;
-      const float gv = dv[db][r];
-      if (cart) {
-        const size_t o = ((size_t)j * a.Hkv + kv) * D + col;
-        if (a.splits_c > 1) {
-          const size_t po_ = (size_t)split * a.p * row_stride + o;
-          a.dk_part[po_] = gk;
-          a.dv_part[po_] = gv;
-        } else if (j < a.f) {
-          a.dk_cart[o] = 0.f;
-          a.dv_cart[o] = 0.f;
-        } else if (a.accumulate) {
-          a.dk_cart[o] += gk;
-          a.dv_cart[o] += gv;
-        } else {
-          a.dk_cart[o] = gk;
-          a.dv_cart[o] = gv;
+      const size_t o = (size_t)split * pstride + out_off(j, 32 * db + l32);
+      __hip_atomic_store(pk + o, dk[db][r] * scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pv + o, dv[db][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // every store of the workgroup complete, then count this piece in
+  __shared__ int last_piece;
+  CART_WAIT_VMCNT(0);
+  __syncthreads();
+  if (tid == 0) {
+    const int cid = cart ? kv * a.n_ct + tile : a.Hkv * a.n_ct + (kv * a.B + b) * a.n_tt + tile;
+    last_piece = __hip_atomic_fetch_add(a.kv_cnt + cid, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == n_split - 1;
+  }
+  __syncthreads();
+  if (!last_piece) return;
+  // piece-major, so that each pass issues a piece's loads of RPASS result
+  // registers at once (64 loads for D = 128, 16 for D = 64, which keeps its
+  // two workgroups per CU)
+  constexpr int RPASS = D == 128 ? 8 : 4;
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += RPASS) {
+    float sk[RPASS][NDB], sv[RPASS][NDB];
+#pragma unroll
+    for (int r = 0; r < RPASS; ++r)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) { sk[r][db] = 0.f; sv[r][db] = 0.f; }
+    for (int i = 0; i < n_split; ++i) {
+      const buf_rsrc rk = make_rsrc(pk + (size_t)i * pstride + pbase, pbytes);
+      const buf_rsrc rv = make_rsrc(pv + (size_t)i * pstride + pbase, pbytes);
+      uint32_t tk[RPASS][NDB], tv[RPASS][NDB];
+#pragma unroll
+      for (int r = 0; r < RPASS; ++r)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          tk[r][db] = __builtin_amdgcn_raw_buffer_load_b32(rk, roff(r0 + r) + 128 * db, 0, kCpolDevice);
+          tv[r][db] = __builtin_amdgcn_raw_buffer_load_b32(rv, roff(r0 + r) + 128 * db, 0, kCpolDevice);
         }
-      } else {
-        const size_t o = (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
-        if (n_split > 1) {
-          const size_t po_ = (size_t)split * a.B * a.n * row_stride + o;
-          a.dk_tpart[po_] = gk;
-          a.dv_tpart[po_] = gv;
-        } else {
-          reinterpret_cast<bf16*>(a.dk_tok)[o] = (bf16)gk;
-          reinterpret_cast<bf16*>(a.dv_tok)[o] = (bf16)gv;
+      // all of the pass's loads in flight before the first add
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < RPASS; ++r)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          sk[r][db] += __builtin_bit_cast(float, tk[r][db]);
+          sv[r][db] += __builtin_bit_cast(float, tv[r][db]);
         }
-      }
+    }
+#pragma unroll
+    for (int r = 0; r < RPASS; ++r) {
+      const int j = j0 + 32 * wave + d_row(r0 + r, hl);
+      if (j >= limit) continue;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) write(j, 32 * db + l32, sk[r][db], sv[r][db]);
     }
   }
 }
@@ -1066,34 +1145,10 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
   reinterpret_cast<bf16x4*>(a.dq)[e] = o;
 }
 
-// dK, dV of token tiles cut into pieces: sum of the f32 pieces, in bf16.
-__global__ __launch_bounds__(256) void bwd_tok_reduce(BwdArgs a) {
-  const size_t n4 = (size_t)a.B * a.n * a.Hkv * (a.D4);
-  const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= n4) return;
-  const int j = (int)((e / ((size_t)a.Hkv * a.D4)) % a.n);
-  const int tile = j / kBNB;
-  const int ut = a.g * (a.nqt - tile * (kBNB / kBQ));
-  const int ns = (ut + a.kv_target - 1) / a.kv_target;
-  if (ns <= 1) return;   // written directly by its only piece
-  const float4* pk = reinterpret_cast<const float4*>(a.dk_tpart);
-  const float4* pv = reinterpret_cast<const float4*>(a.dv_tpart);
-  float4 k = pk[e], v = pv[e];
-  for (int s = 1; s < ns; ++s) {
-    const float4 x = pk[(size_t)s * n4 + e], y = pv[(size_t)s * n4 + e];
-    k.x += x.x; k.y += x.y; k.z += x.z; k.w += x.w;
-    v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
-  }
-  bf16x4 ok, ov;
-  ok[0] = (bf16)k.x; ok[1] = (bf16)k.y; ok[2] = (bf16)k.z; ok[3] = (bf16)k.w;
-  ov[0] = (bf16)v.x; ov[1] = (bf16)v.y; ov[2] = (bf16)v.z; ov[3] = (bf16)v.w;
-  reinterpret_cast<bf16x4*>(a.dk_tok)[e] = ok;
-  reinterpret_cast<bf16x4*>(a.dv_tok)[e] = ov;
-}
-
-// D_i = dO_i . O_i and lse_i * log2(e) for every (b, h, i), and (f32 tokens)
-// dQ accumulator := 0. Sixteen lanes per row (D/16 elements each), 16 rows
-// per workgroup; the row sum is taken with DPP adds.
+// D_i = dO_i . O_i and lse_i * log2(e) for every (b, h, i), (f32 tokens) dQ
+// accumulator := 0, and (bf16) the key tiles' piece counters := 0. Sixteen
+// lanes per row (D/16 elements each), 16 rows per workgroup; the row sum is
+// taken with DPP adds.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
   constexpr int EPL = D / 16;
@@ -1108,6 +1163,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc += to_f32(o[e]) * to_f32(g[e]);
   acc = row_sum<16>(acc);
+  for (int c = blockIdx.x * 256 + threadIdx.x; c < a.n_cnt; c += gridDim.x * 256) a.kv_cnt[c] = 0;
   if (!ok) return;
   if (sub == 0) {
     const int h = row % a.Hq;
@@ -1168,7 +1224,27 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+static BwdPlan make_plan_bwd(const AttnDims& d);
+
+// Plans are cached per thread by shape: the work split is chosen by a small
+// simulation that costs up to a few milliseconds on large shapes.
 BwdPlan plan_bwd(const AttnDims& d) {
+  struct Entry { AttnDims d; BwdPlan pl; bool used; };
+  thread_local Entry cache[8] = {};
+  thread_local int next_slot = 0;
+  auto same = [](const AttnDims& x, const AttnDims& y) {
+    return x.B == y.B && x.n == y.n && x.p == y.p && x.f == y.f && x.Hq == y.Hq &&
+           x.Hkv == y.Hkv && x.D == y.D && x.tok_bf16 == y.tok_bf16 && x.row_bf16 == y.row_bf16;
+  };
+  for (const Entry& e : cache)
+    if (e.used && same(e.d, d)) return e.pl;
+  const BwdPlan pl = make_plan_bwd(d);
+  cache[next_slot] = Entry{d, pl, true};
+  next_slot = (next_slot + 1) % 8;
+  return pl;
+}
+
+static BwdPlan make_plan_bwd(const AttnDims& d) {
   BwdPlan pl{};
   const int g = d.Hq / d.Hkv;
   pl.n_ct = (d.p + kBNB - 1) / kBNB;
@@ -1184,25 +1260,53 @@ BwdPlan plan_bwd(const AttnDims& d) {
   pl.splits_c = s;
   pl.grid_c = d.Hkv * pl.n_ct * s;
   pl.grid_t = d.Hkv * d.B * pl.n_tt;
-  // bf16 path: pieces of about kv_target units, about two pieces per CU
+  // bf16 path: every key tile's units cut into pieces of at most kv_target
+  // units (a tile of u units into ceil(u / T) nearly equal pieces), T chosen
+  // by a model of the dispatch: the grid's pieces, in order, are dealt to the
+  // 8 XCDs in contiguous ranges (the kernel's block id remap), and each XCD
+  // starts its pieces in order on its first free workgroup slot (32 CUs x
+  // workgroups per CU). A piece costs its units plus a fixed overhead (key
+  // tile load, pipeline fill, result store; a partial store and the
+  // reduction when cut). The candidate with the smallest modelled finish
+  // time wins, the largest T among equals.
   {
-    long long W = (long long)pl.n_ct * U;
-    for (int t = 0; t < pl.n_tt; ++t) W += d.B * tok_units(t);
-    // Pieces cost partial sums and a reduction; measured on the qwen3-0.6b
-    // layer, one round of unsplit tiles (192 workgroups on 256 CUs) beats two
-    // rounds of balanced pieces plus the reductions. So tiles are cut only
-    // when unsplit they would leave more than a quarter of the CUs idle, and
-    // then into the fewest pieces that still fit one round.
-    auto pieces = [&](long long t_) {
-      long long c = pl.n_ct > 0 ? pl.n_ct * ((U + t_ - 1) / t_) : 0;
-      for (int t = 0; t < pl.n_tt; ++t) c += d.B * ((tok_units(t) + t_ - 1) / t_);
-      return d.Hkv * c;
-    };
     const long long t_max = std::max(U, tok_units(0));   // every tile one piece
+    const int slots = 32 * (d.D == 128 ? 1 : 2);
+    auto finish = [&](long long T) {
+      std::vector<std::pair<long long, long long>> pieces;   // (units, pieces of its tile)
+      auto tile = [&](long long u) {
+        const long long ns = (u + T - 1) / T;
+        for (long long i = 0; i < ns; ++i) pieces.emplace_back((i + 1) * u / ns - i * u / ns, ns);
+      };
+      for (int kv = 0; kv < d.Hkv; ++kv) {
+        for (int c = 0; c < pl.n_ct; ++c) tile(U);
+        for (int b = 0; b < d.B; ++b)
+          for (int t = 0; t < pl.n_tt; ++t) tile(tok_units(t));
+      }
+      const size_t G = pieces.size(), q = G / 8, r = G % 8;
+      double worst = 0.0;
+      size_t first = 0;
+      std::vector<double> slot(slots);   // min-heap of slot free times
+      for (size_t x = 0; x < 8; ++x) {
+        const size_t cnt = x < r ? q + 1 : q;
+        std::fill(slot.begin(), slot.end(), 0.0);
+        for (size_t i = first; i < first + cnt; ++i) {
+          std::pop_heap(slot.begin(), slot.end(), std::greater<double>());
+          slot.back() += (double)pieces[i].first + (pieces[i].second > 1 ? 2.5 : 1.5);
+          std::push_heap(slot.begin(), slot.end(), std::greater<double>());
+        }
+        worst = std::max(worst, *std::max_element(slot.begin(), slot.end()));
+        first += cnt;
+      }
+      return worst;
+    };
     long long T = t_max;
-    if (pieces(t_max) < 192) {
-      T = std::max(8LL, (d.Hkv * W + 255) / 256);
-      while (T < t_max && pieces(T) > 256) ++T;
+    double best = finish(T);
+    for (int k = 2; k <= 8; ++k) {
+      const long long c = std::max(4LL, (t_max + k - 1) / k);
+      if (c >= T) continue;
+      const double f = finish(c);
+      if (f < best - 1e-9) { best = f; T = c; }
     }
     pl.kv_target = (int)T;
     pl.kv_splits_c = pl.n_ct > 0 ? (int)((U + T - 1) / T) : 1;
@@ -1213,6 +1317,7 @@ BwdPlan plan_bwd(const AttnDims& d) {
     pl.grid_kv = d.Hkv * (pl.n_ct * pl.kv_splits_c + d.B * ptok);
     if (d.tok_bf16 && pl.kv_stmax > 1)
       pl.tok_part_bytes = (size_t)pl.kv_stmax * d.B * d.n * d.Hkv * d.D * sizeof(float);
+    if (d.tok_bf16) pl.cnt_bytes = (size_t)d.Hkv * (pl.n_ct + d.B * pl.n_tt) * sizeof(int);
   }
   pl.dq_bytes = d.tok_bf16 ? 0 : (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
   {
@@ -1241,7 +1346,7 @@ size_t bwd_workspace_bytes(const AttnDims& d) {
   const BwdPlan pl = plan_bwd(d);
   return align256(pl.shadow_bytes) + align256(pl.dq_bytes) + 2 * align256(pl.delta_bytes) +
          2 * align256(pl.part_bytes) + 2 * align256(pl.tok_part_bytes) +
-         align256(pl.dq_part_bytes);
+         align256(pl.dq_part_bytes) + align256(pl.cnt_bytes);
 }
 
 // float32 reference mode: preprocess, generic kernel (dQ by atomics), dQ
@@ -1269,7 +1374,8 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_
   return e;
 }
 
-// bf16: preprocess, dK/dV kernel, dQ kernel, split reduction.
+// bf16: preprocess, dK/dV kernel (its pieces reduced in the kernel), dQ
+// kernel, dQ split reduction.
 template <int D>
 static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
@@ -1285,18 +1391,6 @@ static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream
     CART_TIMED("bwd_dq_combine", st,
                bwd_dq_combine<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (pl.kv_stmax > 1) {
-    const size_t n4 = (size_t)a.B * a.n * a.Hkv * (D / 4);
-    CART_TIMED("bwd_tok_reduce", st,
-               bwd_tok_reduce<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a));
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (a.splits_c > 1) {
-    const size_t total = (size_t)a.p * a.Hkv * D;
-    CART_TIMED("bwd_cart_reduce", st,
-               bwd_cart_reduce_t<D><<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a));
-    e = hipGetLastError();
   }
   return e;
 }
@@ -1337,6 +1431,9 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.dv_tpart = pl.tok_part_bytes ? reinterpret_cast<float*>(w) : nullptr;
   w += align256(pl.tok_part_bytes);
   a.dq_part = pl.dq_part_bytes ? reinterpret_cast<float*>(w) : nullptr;
+  w += align256(pl.dq_part_bytes);
+  a.kv_cnt = pl.cnt_bytes ? reinterpret_cast<int*>(w) : nullptr;
+  a.n_cnt = (int)(pl.cnt_bytes / sizeof(int));
   a.dq = dq; a.dk_tok = dk_tok; a.dv_tok = dv_tok; a.dk_cart = dk_cart; a.dv_cart = dv_cart;
   a.B = d.B; a.n = d.n; a.p = d.p; a.f = d.f; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
   a.n_ct = pl.n_ct; a.n_tt = pl.n_tt; a.nqt = pl.nqt;

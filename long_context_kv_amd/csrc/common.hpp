@@ -275,6 +275,9 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+// Cache-policy operand of a buffer load coherent at device scope on gfx950
+// (the SC1 bit: the load is served from beyond the XCD's L2).
+constexpr int kCpolDevice = 16;
 __device__ __forceinline__ void dma16(buf_rsrc r, uint32_t voff, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            (int)voff, 0, 0, 0);

@@ -36,7 +36,7 @@ struct BwdPlan {
   // token tiles, at most kv_stmax per token tile.
   int kv_target, kv_splits_c, kv_ptok, kv_stmax, grid_kv;
   int hpw, wph, n_hg, n_qb, q_splits, grid_q;     // query-major dQ kernel
-  size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes, tok_part_bytes, dq_part_bytes;
+  size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes, tok_part_bytes, dq_part_bytes, cnt_bytes;
 };
 BwdPlan plan_bwd(const AttnDims& a);
 size_t bwd_workspace_bytes(const AttnDims& a);
