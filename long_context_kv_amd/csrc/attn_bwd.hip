@@ -435,12 +435,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   constexpr int QBLK = QBLK0 + ((2 - QBLK0 % 4) + 4) % 4;
   constexpr int QTILE = QBLK * 512;
   constexpr int QPW = (QBLK + 3) / 4;
-  // 4-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
-  // The copy of a unit is issued two steps before it is used, spread over
-  // the MFMAs of a step. Stages are read while copies fill others, so every
-  // LDS read of the unit loop is issued by the inline-assembly helpers, with
-  // explicit waits.
-  constexpr int NST = 4;
+  // 5-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
+  // A step of the unit loop reads three stages (row fragments of one unit,
+  // lse and D of the next older one, transpose fragments of the one before
+  // that); the copy of a unit is issued two steps before its first use,
+  // spread over the MFMAs of a step. Stages are read while copies fill
+  // others, so every LDS read of the unit loop is issued by the
+  // inline-assembly helpers, with explicit waits.
+  constexpr int NST = 5;
   constexpr int STAGE = 2 * QTILE + 2 * 2 * kBQ;   // bf16 elements per stage
   constexpr int O_OFF = 2 * QTILE;                  // byte offset of dO in a stage
   constexpr int L_OFF = 4 * QTILE;                  // byte offset of lse / D
@@ -581,7 +583,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     for (int k = 0; k <= QPW; ++k) copy_part(c, k);
   };
 
-  // ---- the wave's K, V rows as B operands
+  // ---- the wave's K, V rows as B operands (units 0 and 1 are copied around
+  // these loads)
   if (u_begin < u_end) issue(cu, 0);
   bf16x8 kf[NKS], vf[NKS];
   {
@@ -592,6 +595,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kr * row_stride + 16 * ks + 8 * hl);
     }
   }
+  const int nu = u_end - u_begin;
+  if (nu > 1) issue(next(cu), 1);
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -601,42 +606,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const float c = a.scale_log2;
 
   // Per-lane LDS byte offsets inside a stage: the row fragment (row l32,
-  // 8 elements at 8 hl) and the transpose strip (tr_col4's lane pattern for
-  // rows 4 hl .., columns 16 ((lane >> 4) & 1) ..).
+  // 8 elements at 8 hl), the transpose strip (tr_col4's lane pattern for
+  // rows 4 hl .., columns 16 ((lane >> 4) & 1) ..) and lse / D (queries
+  // 8 c4 + 4 hl .. of a lane's result registers 4 c4 ..).
   const uint32_t row_lane = TL::off(l32, 8 * hl);
   const uint32_t tr_lane = TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-  const uint32_t ld_lane = 16 * hl;
+  const uint32_t ld_lane = L_OFF + 16 * hl;
 
-  // lse*log2(e) and D of the 16 queries of a lane's result registers
-  // (query 8 c4 + 4 hl + e of the unit for register 4 c4 + e): 8 reads.
-  struct LD { f32x4 l[4], d[4]; };
-  auto read_ld = [&](uint32_t stage, LD& x) {
-    const uint32_t base = stage + L_OFF + ld_lane;
-    static_for<4>([&](auto C4) {
-      constexpr int c4 = decltype(C4)::value;
-      x.l[c4] = lds_read16<32 * c4>(base);
-      x.d[c4] = lds_read16<4 * kBQ + 32 * c4>(base);
-    });
-  };
-  auto tie_ld = [&](LD& x) {
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) { lds_tie(x.l[c4]); lds_tie(x.d[c4]); }
-  };
-  auto unit_needs_mask = [&](const Unit& x) {
-    const int i0 = x.qt * kBQ;
-    return (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
-  };
   // Softmax of result register r: P = exp2(S c - lse2) and G = P (dP - D)
   // in place (the softmax scale is applied to dK once at the end). Masked
   // pairs (query not visible from the key) get P = 0.
-  auto softmax_elem = [&](auto MASK, int r, uint32_t rel, const LD& ld, f32x16& s, f32x16& g) {
-    const int c4 = r >> 2, e = r & 3;
-    float arg = fmaf(s[r], c, -ld.l[c4][e]);
-    if constexpr (decltype(MASK)::value)
-      arg = (rel + (uint32_t)(8 * c4 + e) < vis_span) ? arg : -INFINITY;
+  auto softmax_elem = [&](int r, uint32_t rel, float l2, float dd, f32x16& s, f32x16& g) {
+    float arg = fmaf(s[r], c, -l2);
+    arg = (rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < vis_span) ? arg : -INFINITY;
     const float p_ = __builtin_amdgcn_exp2f(arg);
     s[r] = p_;
-    g[r] = p_ * (g[r] - ld.d[c4][e]);
+    g[r] = p_ * (g[r] - dd);
   };
   auto mask_rel = [&](const Unit& x) { return (uint32_t)(x.qt * kBQ + 4 * hl - vis_lo); };
   // Transpose fragment f = m * NDB + db (queries 16 m .., columns 32 db ..)
@@ -649,159 +634,164 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     t.o = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + TL::rows(8)>(base));
     t.q = cat8(lds_tr4<off>(base), lds_tr4<off + TL::rows(8)>(base));
   };
-  // Phase A: S = Q K^T and dP = dO V^T of one unit (rows = queries, columns
-  // = this wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)).
-  // Two row reads per k-step, one k-step ahead of the MFMAs; it ends with a
-  // full LDS wait, which also retires every read issued before it.
-  auto phase_a = [&](uint32_t stage, f32x16& s, f32x16& dp) {
-    bf16x8 qa[2], oa[2];
-    const uint32_t rbase = stage + row_lane;
-    auto rd = [&](auto KS, int slot) {
-      constexpr int ks = decltype(KS)::value;
-      qa[slot] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(rbase));
-      oa[slot] = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(rbase));
-    };
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-    rd(std::integral_constant<int, 0>{}, 0);
-    static_for<NKS>([&](auto KS) {
-      constexpr int ks = decltype(KS)::value;
-      if constexpr (ks + 1 < NKS) {
-        rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
-        lds_wait<2>();
-      } else {
-        lds_wait<0>();
-      }
-      lds_tie(qa[ks & 1]);
-      lds_tie(oa[ks & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      s = M::mma(qa[ks & 1], kf[ks], s);
-      dp = M::mma(oa[ks & 1], vf[ks], dp);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
-  // Phase B: dV += P^T dO and dK += G^T Q of the unit in `stage` (A operands
-  // pf, sf; B operands by transpose reads, issued one k-step ahead). With
-  // NEXT, each k-step also runs the softmax of 16/NKS of the next unit's
-  // result registers (s, g), so that its VALU work overlaps the MFMAs; the
-  // packed results go to pf2, sf2. Starts and ends with no LDS read pending.
-  auto phase_b = [&](auto NEXT, auto MASK, uint32_t stage, const bf16x8 (&pf)[2],
-                     const bf16x8 (&sf)[2], uint32_t rel, const LD& ld, f32x16& s, f32x16& g,
-                     bf16x8 (&pf2)[2], bf16x8 (&sf2)[2], auto&& per_step) {
-    constexpr bool N = decltype(NEXT)::value;
-    TrOp t[2];
-    tr_frag(stage, std::integral_constant<int, 0>{}, t[0]);
-    static_for<NKS>([&](auto KS) {
-      constexpr int ks = decltype(KS)::value;
-      constexpr int m = ks / NDB, db = ks % NDB;
-      if constexpr (ks + 1 < NKS) {
-        tr_frag(stage, std::integral_constant<int, ks + 1>{}, t[(ks + 1) & 1]);
-        lds_wait<4>();
-      } else {
-        lds_wait<0>();
-      }
-      lds_tie(t[ks & 1].o);
-      lds_tie(t[ks & 1].q);
-      __builtin_amdgcn_sched_barrier(0);
-      dv[db] = M::mma(pf[m], t[ks & 1].o, dv[db]);
-      dk[db] = M::mma(sf[m], t[ks & 1].q, dk[db]);
-      per_step(ks);
-      if constexpr (N) {
-        constexpr int per = 16 / NKS;   // result registers per k-step
-#pragma unroll
-        for (int j = 0; j < per; ++j) softmax_elem(MASK, per * ks + j, rel, ld, s, g);
-        if constexpr ((per * (ks + 1)) % 8 == 0) {
-          constexpr int mm = per * (ks + 1) / 8 - 1;
-          pf2[mm] = pack_regs<bf16>(s, mm);
-          sf2[mm] = pack_regs<bf16>(g, mm);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  };
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   const uint32_t ring_base = lds_addr(ring);
   auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
 
-  // Wait until at most the copies of `units` later units (0, 1 or 2) are in
+  // Wait until at most the copies of `units` later units (0 or 1) are in
   // flight.
   auto wait_copies = [&](int units) {
-    if (units == 2) CART_WAIT_VMCNT(2 * NDMA);
-    else if (units == 1) CART_WAIT_VMCNT(NDMA);
+    if (units == 1) CART_WAIT_VMCNT(NDMA);
     else CART_WAIT_VMCNT(0);
   };
-  static_assert(2 * NDMA < 64, "copies of two units must fit the wait count");
-  static_assert(QPW + 1 <= NKS, "a unit's copy parts must fit the k-steps of phase B");
-  auto no_extra = [](int) {};
+  static_assert(NDMA < 64, "copies of a unit must fit the wait count");
+  static_assert(QPW + 1 <= NKS, "a unit's copy parts must fit the k-steps of a step");
 
-  if (u_begin < u_end) {
-    const int nu = u_end - u_begin;
-    // units 0, 1, 2 are copied before the loop (unit 0's copy was issued above)
-    Unit u1 = next(cu), u2 = next(u1);
-    if (nu > 1) issue(u1, 1);
-    if (nu > 2) issue(u2, 2);
-    // unit 0 has landed once only the copies of units 1 and 2 may be pending
-    // (the K/V operand loads are older than all of them)
-    wait_copies(min(nu, 3) - 1);
-    lds_barrier();
-    bf16x8 pf[2], sf[2];
-    {
-      // unit 0: S and dP, then its softmax
-      const uint32_t st0 = stage_addr(0);
-      LD ld;
-      read_ld(st0, ld);
-      f32x16 s, g;
-      phase_a(st0, s, g);
-      tie_ld(ld);
-      const uint32_t rel = mask_rel(cu);
+  // Step j of the unit loop, software-pipelined over three units:
+  //  A: S = Q K^T and dP = dO V^T of unit j (rows = queries, columns = this
+  //     wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)), from
+  //     row fragments of its stage, into (sa, ga);
+  //  S: the softmax of unit j-1 (ss, gs, computed by the previous step),
+  //     packed to bf16 operands (pn, gn);
+  //  B: dV += P^T dO and dK += G^T Q of unit j-2 (operands pb, gb) with the
+  //     transpose fragments of its stage.
+  // The three are independent, so the MFMAs of A and B and the VALU work of
+  // S interleave in every k-step; each k-step's LDS reads (and the copy part
+  // of unit j+2, when `more`) are issued one k-step ahead. Starts and ends
+  // with no LDS read pending.
+  constexpr int PER = 16 / NKS;   // softmax result registers per k-step
+  auto step = [&](auto HA, auto HS, auto HB, uint32_t stA, uint32_t stL, uint32_t stB,
+                  uint32_t rel, f32x16& sa, f32x16& ga, f32x16& ss, f32x16& gs,
+                  const bf16x8 (&pb)[2], const bf16x8 (&gb)[2], bf16x8 (&pn)[2],
+                  bf16x8 (&gn)[2], const Copy& cp, bool more) {
+    constexpr bool A = decltype(HA)::value, S = decltype(HS)::value, BB = decltype(HB)::value;
+    bf16x8 qa[2], oa[2];
+    TrOp t[2];
+    f32x4 lq[2], dq4[2];
+    // reads of k-step ks: 2 row fragments (A), 4 transpose reads (B), and
+    // lse / D of the lane's registers 4 c4 .. at the first k-step using them (S)
+    auto n_reads = [](int ks) {
+      return (A ? 2 : 0) + (BB ? 4 : 0) + ((S && (PER * ks) % 4 == 0) ? 2 : 0);
+    };
+    auto batch = [&](auto KS, int slot) {
+      constexpr int ks = decltype(KS)::value;
+      if constexpr (A) {
+        qa[slot] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(stA + row_lane));
+        oa[slot] = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(stA + row_lane));
+      }
+      if constexpr (S && (PER * ks) % 4 == 0) {
+        constexpr int c4 = PER * ks / 4;
+        lq[c4 & 1] = lds_read16<32 * c4>(stL + ld_lane);
+        dq4[c4 & 1] = lds_read16<4 * kBQ + 32 * c4>(stL + ld_lane);
+      }
+      if constexpr (BB) tr_frag(stB, KS, t[slot]);
+    };
+    if constexpr (A) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) softmax_elem(Yes{}, r, rel, ld, s, g);
-      pf[0] = pack_regs<bf16>(s, 0);
-      pf[1] = pack_regs<bf16>(s, 1);
-      sf[0] = pack_regs<bf16>(g, 0);
-      sf[1] = pack_regs<bf16>(g, 1);
+      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; ga[r] = 0.f; }
     }
-    // Step k (k = 0 .. nu-2): unit k in stage k%4, unit k+1 in stage
-    // (k+1)%4, unit k+2's copy possibly in flight; the copy of unit k+3 goes
-    // to stage (k+3)%4 (last read in step k-1, which every wave has left at
-    // the barrier), its parts issued between the MFMAs of phase B. Phase A of
-    // unit k+1, then phase B of unit k with the softmax of unit k+1.
-    Unit un = u1, uf = next(u2);
-    int sk = 0;
-    for (int k = 0; k < nu - 1; ++k) {
-      const int sn = (sk + 1) & (NST - 1);
-      const int sf_ = (sk + 3) & (NST - 1);
-      wait_copies(k + 2 < nu ? 1 : 0);   // unit k+1 has landed
+    batch(std::integral_constant<int, 0>{}, 0);
+    static_for<NKS>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      if constexpr (ks + 1 < NKS) {
+        batch(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
+        constexpr int nr = n_reads(ks + 1);
+        lds_wait<nr>();
+      } else {
+        lds_wait<0>();
+      }
+      if constexpr (A) { lds_tie(qa[ks & 1]); lds_tie(oa[ks & 1]); }
+      if constexpr (BB) { lds_tie(t[ks & 1].o); lds_tie(t[ks & 1].q); }
+      if constexpr (S && (PER * ks) % 4 == 0) {
+        lds_tie(lq[(PER * ks / 4) & 1]);
+        lds_tie(dq4[(PER * ks / 4) & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (A) {
+        sa = M::mma(qa[ks & 1], kf[ks], sa);
+        ga = M::mma(oa[ks & 1], vf[ks], ga);
+      }
+      if constexpr (BB) {
+        constexpr int m = ks / NDB, db = ks % NDB;
+        dv[db] = M::mma(pb[m], t[ks & 1].o, dv[db]);
+        dk[db] = M::mma(gb[m], t[ks & 1].q, dk[db]);
+      }
+      if (more) copy_part(cp, ks);
+      if constexpr (S) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int r = PER * ks + j;
+          const int c4 = r >> 2;
+          softmax_elem(r, rel, lq[c4 & 1][r & 3], dq4[c4 & 1][r & 3], ss, gs);
+        }
+        if constexpr ((PER * (ks + 1)) % 8 == 0) {
+          constexpr int mm = PER * (ks + 1) / 8 - 1;
+          pn[mm] = pack_regs<bf16>(ss, mm);
+          gn[mm] = pack_regs<bf16>(gs, mm);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  if (nu > 0) {
+    // Fixed roles: phase A accumulates into (sa, ga), the softmax works on
+    // (ss, gs) and writes (pn, gn), phase B reads (pb, gb); between steps
+    // the results move one stage on.
+    f32x16 sa, ga, ss, gs;
+    bf16x8 pb[2], gb[2], pn[2], gn[2];
+    const Copy none{};
+    // units j-1 (softmax) and j+2 (copy) of step j
+    Unit us = cu, uc = next(next(cu));
+    int sj = 0;   // stage of unit j (unit u lives in stage u % NST)
+    auto st_of = [&](int back) { return stage_addr(sj >= back ? sj - back : sj - back + NST); };
+    auto rotate = [&]() {
+      ss = sa;
+      gs = ga;
+      pb[0] = pn[0]; pb[1] = pn[1];
+      gb[0] = gn[0]; gb[1] = gn[1];
+      sj = sj + 1 == NST ? 0 : sj + 1;
+    };
+    // j = 0: phase A of unit 0
+    wait_copies(nu > 1 ? 1 : 0);
+    lds_barrier();
+    step(Yes{}, No{}, No{}, st_of(0), 0u, 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
+         copy_setup(uc, (sj + 2) % NST), nu > 2);
+    uc = next(uc);
+    rotate();
+    // j = 1: phase A of unit 1 (if any) and the softmax of unit 0
+    if (nu > 1) {
+      wait_copies(nu > 2 ? 1 : 0);
       lds_barrier();
-      const uint32_t stn = stage_addr(sn);
-      LD ld;
-      read_ld(stn, ld);
-      f32x16 s, g;
-      phase_a(stn, s, g);
-      tie_ld(ld);
-      bf16x8 pf2[2], sf2[2];
-      const uint32_t rel = mask_rel(un);
-      const bool more = k + 3 < nu;
-      const Copy cp = copy_setup(uf, sf_);
-      auto copy_step = [&](int ks) {
-        if (more) copy_part(cp, ks);
-      };
-      // one code path: the mask select costs less than a second copy of
-      // phase B costs in register moves
-      phase_b(Yes{}, Yes{}, stage_addr(sk), pf, sf, rel, ld, s, g, pf2, sf2, copy_step);
-      pf[0] = pf2[0]; pf[1] = pf2[1];
-      sf[0] = sf2[0]; sf[1] = sf2[1];
-      un = next(un);
-      uf = next(uf);
-      sk = sn;
+      step(Yes{}, Yes{}, No{}, st_of(0), st_of(1), 0u, mask_rel(us), sa, ga, ss, gs, pb, gb, pn,
+           gn, copy_setup(uc, (sj + 2) % NST), nu > 3);
+    } else {
+      step(No{}, Yes{}, No{}, 0u, st_of(1), 0u, mask_rel(us), sa, ga, ss, gs, pb, gb, pn, gn, none,
+           false);
     }
-    {
-      LD ld;
-      f32x16 s, g;
-      bf16x8 pf2[2], sf2[2];
-      phase_b(No{}, No{}, stage_addr(sk), pf, sf, 0u, ld, s, g, pf2, sf2, no_extra);
+    us = next(us);
+    uc = next(uc);
+    rotate();
+    // j = 2 .. nu-1: all three
+    for (int j = 2; j < nu; ++j) {
+      wait_copies(j + 1 < nu ? 1 : 0);
+      lds_barrier();
+      step(Yes{}, Yes{}, Yes{}, st_of(0), st_of(1), st_of(2), mask_rel(us), sa, ga, ss, gs, pb, gb,
+           pn, gn, copy_setup(uc, (sj + 2) % NST), j + 2 < nu);
+      us = next(us);
+      uc = next(uc);
+      rotate();
     }
+    // j = nu: softmax of unit nu-1 and phase B of unit nu-2 (nu >= 2); then
+    // j = nu+1: phase B of unit nu-1. No copies remain, so no waits. (With
+    // nu = 1 the softmax of unit 0 ran at j = 1 and j = 2 is past the loop.)
+    if (nu > 1) {
+      step(No{}, Yes{}, Yes{}, 0u, st_of(1), st_of(2), mask_rel(us), sa, ga, ss, gs, pb, gb, pn,
+           gn, none, false);
+      rotate();
+    }
+    step(No{}, No{}, Yes{}, 0u, 0u, st_of(2), 0u, sa, ga, ss, gs, pb, gb, pn, gn, none, false);
   }
 
   // ---- dK (times the softmax scale), dV. A tile cut into pieces: every
