@@ -435,14 +435,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   constexpr int QBLK = QBLK0 + ((2 - QBLK0 % 4) + 4) % 4;
   constexpr int QTILE = QBLK * 512;
   constexpr int QPW = (QBLK + 3) / 4;
-  // 5-deep ring of unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
+  // Ring of AHEAD + 3 unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
   // A step of the unit loop reads three stages (row fragments of one unit,
   // lse and D of the next older one, transpose fragments of the one before
-  // that); the copy of a unit is issued two steps before its first use,
+  // that); the copy of a unit is issued AHEAD steps before its first use,
   // spread over the MFMAs of a step. Stages are read while copies fill
   // others, so every LDS read of the unit loop is issued by the
   // inline-assembly helpers, with explicit waits.
-  constexpr int NST = 5;
+  constexpr int AHEAD = 3;          // step j copies unit j + AHEAD
+  constexpr int NST = AHEAD + 3;
   constexpr int STAGE = 2 * QTILE + 2 * 2 * kBQ;   // bf16 elements per stage
   constexpr int O_OFF = 2 * QTILE;                  // byte offset of dO in a stage
   constexpr int L_OFF = 4 * QTILE;                  // byte offset of lse / D
@@ -596,7 +597,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     }
   }
   const int nu = u_end - u_begin;
-  if (nu > 1) issue(next(cu), 1);
+  {
+    Unit x = cu;
+    for (int u = 1; u < min(nu, AHEAD); ++u) {
+      x = next(x);
+      issue(x, u);
+    }
+  }
 
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -639,13 +646,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const uint32_t ring_base = lds_addr(ring);
   auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
 
-  // Wait until at most the copies of `units` later units (0 or 1) are in
-  // flight.
-  auto wait_copies = [&](int units) {
-    if (units == 1) CART_WAIT_VMCNT(NDMA);
+  // At the top of step j, unit j has landed once at most the copies of the
+  // units after it (j+1 .. j+AHEAD-1, those that exist) are in flight.
+  auto wait_unit = [&](int j) {
+    const int later = min(AHEAD - 1, nu - 1 - j);
+    static_assert(AHEAD <= 3, "wait counts below cover up to two later units");
+    if (later >= 2) CART_WAIT_VMCNT(2 * NDMA);
+    else if (later == 1) CART_WAIT_VMCNT(NDMA);
     else CART_WAIT_VMCNT(0);
   };
-  static_assert(NDMA < 64, "copies of a unit must fit the wait count");
+  static_assert(2 * NDMA < 64, "copies of two units must fit the wait count");
   static_assert(QPW + 1 <= NKS, "a unit's copy parts must fit the k-steps of a step");
 
   // Step j of the unit loop, software-pipelined over three units:
@@ -658,7 +668,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   //     transpose fragments of its stage.
   // The three are independent, so the MFMAs of A and B and the VALU work of
   // S interleave in every k-step; each k-step's LDS reads (and the copy part
-  // of unit j+2, when `more`) are issued one k-step ahead. Starts and ends
+  // of unit j+AHEAD, when `more`) are issued one k-step ahead. Starts and ends
   // with no LDS read pending.
   constexpr int PER = 16 / NKS;   // softmax result registers per k-step
   auto step = [&](auto HA, auto HS, auto HB, uint32_t stA, uint32_t stL, uint32_t stB,
@@ -742,8 +752,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     f32x16 sa, ga, ss, gs;
     bf16x8 pb[2], gb[2], pn[2], gn[2];
     const Copy none{};
-    // units j-1 (softmax) and j+2 (copy) of step j
-    Unit us = cu, uc = next(next(cu));
+    // units j-1 (softmax) and j+AHEAD (copy) of step j
+    Unit us = cu, uc = cu;
+    for (int u = 0; u < AHEAD; ++u) uc = next(uc);
     int sj = 0;   // stage of unit j (unit u lives in stage u % NST)
     auto st_of = [&](int back) { return stage_addr(sj >= back ? sj - back : sj - back + NST); };
     auto rotate = [&]() {
@@ -754,18 +765,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       sj = sj + 1 == NST ? 0 : sj + 1;
     };
     // j = 0: phase A of unit 0
-    wait_copies(nu > 1 ? 1 : 0);
+    wait_unit(0);
     lds_barrier();
     step(Yes{}, No{}, No{}, st_of(0), 0u, 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
-         copy_setup(uc, (sj + 2) % NST), nu > 2);
+         copy_setup(uc, (sj + AHEAD) % NST), nu > AHEAD);
     uc = next(uc);
     rotate();
     // j = 1: phase A of unit 1 (if any) and the softmax of unit 0
     if (nu > 1) {
-      wait_copies(nu > 2 ? 1 : 0);
+      wait_unit(1);
       lds_barrier();
       step(Yes{}, Yes{}, No{}, st_of(0), st_of(1), 0u, mask_rel(us), sa, ga, ss, gs, pb, gb, pn,
-           gn, copy_setup(uc, (sj + 2) % NST), nu > 3);
+           gn, copy_setup(uc, (sj + AHEAD) % NST), nu > 1 + AHEAD);
     } else {
       step(No{}, Yes{}, No{}, 0u, st_of(1), 0u, mask_rel(us), sa, ga, ss, gs, pb, gb, pn, gn, none,
            false);
@@ -775,10 +786,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     rotate();
     // j = 2 .. nu-1: all three
     for (int j = 2; j < nu; ++j) {
-      wait_copies(j + 1 < nu ? 1 : 0);
+      wait_unit(j);
       lds_barrier();
       step(Yes{}, Yes{}, Yes{}, st_of(0), st_of(1), st_of(2), mask_rel(us), sa, ga, ss, gs, pb, gb,
-           pn, gn, copy_setup(uc, (sj + 2) % NST), j + 2 < nu);
+           pn, gn, copy_setup(uc, (sj + AHEAD) % NST), j + AHEAD < nu);
       us = next(us);
       uc = next(uc);
       rotate();

@@ -6,12 +6,15 @@
 // positions p, p+1, .... "RIG minimal cognition engine implementation
 // hand-off", section 5: a shifted base position silently corrupts attention.
 //
-// Pairs (k, k + d/2) rotate by pos * theta^(-2k/d). The angle and its cosine
-// and sine are computed in double precision (positions reach 2e4, where a
-// float angle would be off by ~1e-3 rad); the rotation itself is f32 and the
-// result is rounded to the tensor's dtype. The kernel is HBM-bound: one
-// workgroup per token, lanes over k so each row half is read coalesced, and
-// each lane computes its cos/sin once and reuses it for every head.
+// Pairs (k, k + d/2) rotate by pos * theta^(-2k/d). The frequencies are
+// computed on the host in double precision; on the device the angle is formed
+// and reduced modulo 2 pi in double precision (positions reach 2e4, where a
+// float angle would be off by ~1e-3 rad), and the cosine and sine of the
+// reduced angle (|r| <= pi) are f32. The rotation itself is f32 and the result
+// is rounded to the tensor's dtype. The kernel is HBM-bound: one workgroup per
+// token; its first d/2 lanes put the token's cos/sin table in LDS, then every
+// lane rotates 4 consecutive pairs of one head row per pass (8- or 16-byte
+// loads of each row half).
 #include <math.h>
 
 #include "common.hpp"
@@ -22,51 +25,73 @@ namespace cartattn {
 
 namespace {
 
+struct RopeFreq {
+  double inv_freq[64];   // theta^(-2k/d), k < d/2
+};
+
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
                                                    int S, int Hq, int Hkv, int pos_base,
                                                    const int32_t* __restrict__ pos_offsets,
-                                                   double log_theta, float sign) {
+                                                   RopeFreq fr, float sign) {
   constexpr int HALF = D / 2;
-  constexpr int HPP = 256 / HALF;   // heads handled per pass
-  const int tok = blockIdx.x;       // b * S + i
+  constexpr int TPR = HALF / 4;      // threads per head row (4 pairs each)
+  constexpr int RPP = 256 / TPR;     // head rows per pass
+  typedef typename Vec4<T>::type V4;
+  __shared__ float cs[HALF], sn[HALF];
+  const int tok = blockIdx.x;        // b * S + i
   const int b = tok / S;
   const int i = tok % S;
-  const int kk = threadIdx.x % HALF;
-  const int hsub = threadIdx.x / HALF;
-  const long long pos = (long long)pos_base + (pos_offsets ? pos_offsets[b] : 0) + i;
-  const double inv_freq = exp(-2.0 * (double)kk / (double)D * log_theta);
-  double sd, cd;
-  sincos((double)pos * inv_freq, &sd, &cd);
-  const float c = (float)cd;
-  const float s = (float)sd * sign;
-  T* qr = q + (size_t)tok * Hq * D;
-  for (int h = hsub; h < Hq; h += HPP) {
-    T* x = qr + (size_t)h * D;
-    const float lo = to_f32(x[kk]);
-    const float hi = to_f32(x[kk + HALF]);
-    x[kk] = from_f32<T>(lo * c - hi * s);
-    x[kk + HALF] = from_f32<T>(hi * c + lo * s);
+  if (threadIdx.x < HALF) {
+    const long long pos = (long long)pos_base + (pos_offsets ? pos_offsets[b] : 0) + i;
+    const double ang = (double)pos * fr.inv_freq[threadIdx.x];
+    constexpr double kTwoPi = 6.283185307179586476925286766559;
+    const double r = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
+    float sf, cf;
+    sincosf((float)r, &sf, &cf);
+    cs[threadIdx.x] = cf;
+    sn[threadIdx.x] = sf * sign;
   }
+  __syncthreads();
+  const int k4 = 4 * (threadIdx.x % TPR);
+  const int hsub = threadIdx.x / TPR;
+  float c[4], s_[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { c[e] = cs[k4 + e]; s_[e] = sn[k4 + e]; }
+  auto rot = [&](T* x) {
+    V4 lo = *reinterpret_cast<const V4*>(x + k4);
+    V4 hi = *reinterpret_cast<const V4*>(x + HALF + k4);
+    V4 ol, oh;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float l = to_f32(lo[e]), h = to_f32(hi[e]);
+      ol[e] = from_f32<T>(l * c[e] - h * s_[e]);
+      oh[e] = from_f32<T>(h * c[e] + l * s_[e]);
+    }
+    *reinterpret_cast<V4*>(x + k4) = ol;
+    *reinterpret_cast<V4*>(x + HALF + k4) = oh;
+  };
+  T* qr = q + (size_t)tok * Hq * D;
+  for (int h = hsub; h < Hq; h += RPP) rot(qr + (size_t)h * D);
   if (k) {
     T* kr = k + (size_t)tok * Hkv * D;
-    for (int h = hsub; h < Hkv; h += HPP) {
-      T* x = kr + (size_t)h * D;
-      const float lo = to_f32(x[kk]);
-      const float hi = to_f32(x[kk + HALF]);
-      x[kk] = from_f32<T>(lo * c - hi * s);
-      x[kk + HALF] = from_f32<T>(hi * c + lo * s);
-    }
+    for (int h = hsub; h < Hkv; h += RPP) rot(kr + (size_t)h * D);
   }
 }
 
 template <typename T, int D>
 hipError_t launch_t(void* q, void* k, int B, int S, int Hq, int Hkv, int pos_base,
                     const int32_t* pos_offsets, double theta, bool inverse, hipStream_t st) {
+  RopeFreq fr{};
+  for (int kk = 0; kk < D / 2; ++kk) fr.inv_freq[kk] = exp(-2.0 * (double)kk / (double)D * log(theta));
   CART_TIMED("rope", st,
              rope_kernel<T, D><<<B * S, 256, 0, st>>>(
                  reinterpret_cast<T*>(q), reinterpret_cast<T*>(k), S, Hq, Hkv, pos_base,
-                 pos_offsets, log(theta), inverse ? -1.f : 1.f));
+                 pos_offsets, fr, inverse ? -1.f : 1.f));
   return hipGetLastError();
 }
 
