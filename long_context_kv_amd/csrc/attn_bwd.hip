@@ -1355,21 +1355,20 @@ size_t bwd_workspace_bytes(const AttnDims& d) {
 template <int D>
 static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
-  CART_TIMED("bwd_preprocess", st, bwd_preprocess<float, D><<<(rows + 15) / 16, 256, 0, st>>>(a));
+  CART_LAUNCH("bwd_preprocess", (bwd_preprocess<float, D>), (rows + 15) / 16, 256, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_TIMED("attn_bwd", st,
-             attn_bwd_kernel<float, float, D><<<pl.grid_c + pl.grid_t, kThreads, 0, st>>>(a));
+  CART_LAUNCH("attn_bwd", (attn_bwd_kernel<float, float, D>), pl.grid_c + pl.grid_t, kThreads, 0,
+              st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t n4 = (size_t)rows * D / 4;
-  CART_TIMED("bwd_dq_finalize", st,
-             bwd_dq_finalize<float><<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(
-                 a.dq_acc, reinterpret_cast<float*>(a.dq), n4));
+  CART_LAUNCH("bwd_dq_finalize", (bwd_dq_finalize<float>), (unsigned)((n4 + 255) / 256), 256, 0, st,
+              a.dq_acc, reinterpret_cast<float*>(a.dq), n4);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.splits_c > 1) {
     const size_t total = (size_t)a.p * a.Hkv * D;
-    CART_TIMED("bwd_cart_reduce", st,
-               bwd_cart_reduce_t<D><<<(unsigned)((total + 255) / 256), 256, 0, st>>>(a));
+    CART_LAUNCH("bwd_cart_reduce", (bwd_cart_reduce_t<D>), (unsigned)((total + 255) / 256), 256, 0,
+                st, a);
     e = hipGetLastError();
   }
   return e;
@@ -1380,17 +1379,16 @@ static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_
 template <int D>
 static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
-  CART_TIMED("bwd_preprocess", st, bwd_preprocess<bf16, D><<<(rows + 15) / 16, 256, 0, st>>>(a));
+  CART_LAUNCH("bwd_preprocess", (bwd_preprocess<bf16, D>), (rows + 15) / 16, 256, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_TIMED("attn_bwd", st, attn_bwd_kv_kernel<D><<<pl.grid_kv, kThreads, 0, st>>>(a));
+  CART_LAUNCH("attn_bwd", (attn_bwd_kv_kernel<D>), pl.grid_kv, kThreads, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  CART_TIMED("attn_bwd_dq", st, attn_bwd_dq_kernel<D><<<pl.grid_q, kThreads, 0, st>>>(a));
+  CART_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<D>), pl.grid_q, kThreads, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.q_splits > 1) {
     const size_t n4 = (size_t)a.B * a.n * a.Hq * (D / 4);
-    CART_TIMED("bwd_dq_combine", st,
-               bwd_dq_combine<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>(a));
+    CART_LAUNCH("bwd_dq_combine", (bwd_dq_combine), (unsigned)((n4 + 255) / 256), 256, 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return e;

@@ -603,20 +603,21 @@ size_t fwd_workspace_bytes(const AttnDims& d) {
 
 template <typename T, typename TR, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, const FwdPlan& pl, hipStream_t st) {
-  CART_TIMED("attn_fwd", st, attn_fwd_kernel<T, TR, D><<<pl.grid, kThreads, 0, st>>>(a));
+  CART_LAUNCH("attn_fwd", (attn_fwd_kernel<T, TR, D>), pl.grid, kThreads, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_splits == 1) return e;
-  CART_TIMED("attn_fwd_combine", st, attn_fwd_combine<T, D><<<(a.B * a.n * a.Hq + 15) / 16, 256, 0, st>>>(a));
+  CART_LAUNCH("attn_fwd_combine", (attn_fwd_combine<T, D>), (a.B * a.n * a.Hq + 15) / 16, 256, 0,
+              st, a);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_fwd_bf16(const FwdArgs& a, const FwdPlan& pl, hipStream_t st) {
-  CART_TIMED("attn_fwd", st, attn_fwd_bf16_kernel<D><<<pl.grid, kThreads, 0, st>>>(a));
+  CART_LAUNCH("attn_fwd", (attn_fwd_bf16_kernel<D>), pl.grid, kThreads, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_splits == 1) return e;
-  CART_TIMED("attn_fwd_combine", st,
-             attn_fwd_combine<bf16, D><<<(a.B * a.n * a.Hq + 15) / 16, 256, 0, st>>>(a));
+  CART_LAUNCH("attn_fwd_combine", (attn_fwd_combine<bf16, D>), (a.B * a.n * a.Hq + 15) / 16, 256, 0,
+              st, a);
   return hipGetLastError();
 }
 

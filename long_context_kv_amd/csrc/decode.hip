@@ -326,10 +326,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 template <int D, int G>
 hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
   const int grid = a.c.n_seqs * a.c.Hkv * a.max_splits;
-  CART_TIMED("decode", st, decode_kernel<D, G><<<grid, kDecThreads, 0, st>>>(a));
+  CART_LAUNCH("decode", (decode_kernel<D, G>), grid, kDecThreads, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_TIMED("decode_merge", st, decode_merge_kernel<D><<<a.c.n_seqs * a.Hq, 64, 0, st>>>(a));
+  CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.Hq, 64, 0, st, a);
   return hipGetLastError();
 }
 
@@ -351,15 +351,13 @@ hipError_t launch_cache_append(const CacheDims& c, int seq, int start, const voi
   const size_t total = (size_t)n_rows * c.Hkv * (c.D / 8);
   const unsigned blocks = (unsigned)((total + 255) / 256);
   if (src_bf16)
-    CART_TIMED("cache_append", st,
-               cache_append_kernel<bf16><<<blocks ? blocks : 1, 256, 0, st>>>(
-                   c, seq, start, reinterpret_cast<const bf16*>(k),
-                   reinterpret_cast<const bf16*>(v), n_rows));
+    CART_LAUNCH("cache_append", (cache_append_kernel<bf16>), blocks ? blocks : 1, 256, 0, st, c,
+                seq, start, reinterpret_cast<const bf16*>(k), reinterpret_cast<const bf16*>(v),
+                n_rows);
   else
-    CART_TIMED("cache_append", st,
-               cache_append_kernel<float><<<blocks ? blocks : 1, 256, 0, st>>>(
-                   c, seq, start, reinterpret_cast<const float*>(k),
-                   reinterpret_cast<const float*>(v), n_rows));
+    CART_LAUNCH("cache_append", (cache_append_kernel<float>), blocks ? blocks : 1, 256, 0, st, c,
+                seq, start, reinterpret_cast<const float*>(k), reinterpret_cast<const float*>(v),
+                n_rows);
   return hipGetLastError();
 }
 
@@ -387,9 +385,8 @@ hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
                          void* ws, hipStream_t st) {
   (void)max_len_after;
   if (k_new) {
-    CART_TIMED("decode_append", st,
-               decode_append_kernel<<<c.n_seqs, 256, 0, st>>>(
-                   c, reinterpret_cast<const bf16*>(k_new), reinterpret_cast<const bf16*>(v_new)));
+    CART_LAUNCH("decode_append", (decode_append_kernel), c.n_seqs, 256, 0, st, c,
+                reinterpret_cast<const bf16*>(k_new), reinterpret_cast<const bf16*>(v_new));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -88,10 +88,8 @@ hipError_t launch_t(void* q, void* k, int B, int S, int Hq, int Hkv, int pos_bas
                     const int32_t* pos_offsets, double theta, bool inverse, hipStream_t st) {
   RopeFreq fr{};
   for (int kk = 0; kk < D / 2; ++kk) fr.inv_freq[kk] = exp(-2.0 * (double)kk / (double)D * log(theta));
-  CART_TIMED("rope", st,
-             rope_kernel<T, D><<<B * S, 256, 0, st>>>(
-                 reinterpret_cast<T*>(q), reinterpret_cast<T*>(k), S, Hq, Hkv, pos_base,
-                 pos_offsets, fr, inverse ? -1.f : 1.f));
+  CART_LAUNCH("rope", (rope_kernel<T, D>), B * S, 256, 0, st, reinterpret_cast<T*>(q),
+              reinterpret_cast<T*>(k), S, Hq, Hkv, pos_base, pos_offsets, fr, inverse ? -1.f : 1.f);
   return hipGetLastError();
 }
 

@@ -39,10 +39,9 @@ hipError_t launch_rows_to_bf16(const float* k, const float* v, bf16* kb, bf16* v
   if (n4 == 0) return hipSuccess;
   size_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  CART_TIMED("rows_to_bf16", st,
-             rows_to_bf16_kernel<<<(unsigned)blocks, 256, 0, st>>>(
-                 reinterpret_cast<const float4*>(k), reinterpret_cast<const float4*>(v),
-                 reinterpret_cast<bf16x4*>(kb), reinterpret_cast<bf16x4*>(vb), n4));
+  CART_LAUNCH("rows_to_bf16", (rows_to_bf16_kernel), (unsigned)blocks, 256, 0, st,
+              reinterpret_cast<const float4*>(k), reinterpret_cast<const float4*>(v),
+              reinterpret_cast<bf16x4*>(kb), reinterpret_cast<bf16x4*>(vb), n4);
   return hipGetLastError();
 }
 

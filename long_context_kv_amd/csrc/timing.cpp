@@ -2,7 +2,7 @@
 //
 // Off by default. When enabled (cart_timing_enable), every kernel launch of
 // the library (or, after cart_timing_only, every launch of one kernel name)
-// is bracketed by two events on its own stream; cart_timing_query
+// carries a start and a stop event in its dispatch; cart_timing_query
 // waits for the recorded events and sums the elapsed times of one kernel
 // name. Events are pooled and reused across enable cycles.
 #include <hip/hip_runtime.h>
@@ -37,8 +37,11 @@ hipEvent_t take_event() {
     g_pool.pop_back();
     return e;
   }
+  // Timing-only events: no system-scope fence (cache writeback and
+  // invalidation) when they are recorded, which would otherwise stall the
+  // stream for several microseconds around every timed launch.
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -52,21 +55,17 @@ void recycle_all() {
 
 }  // namespace
 
-int timing_start(const char* name, hipStream_t st) {
+void timing_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  *start = nullptr;
+  *stop = nullptr;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return -1;
-  if (!g_only.empty() && g_only != name) return -1;
+  if (!g_on) return;
+  if (!g_only.empty() && g_only != name) return;
   Record r{name, take_event(), take_event()};
-  if (!r.start || !r.stop) return -1;
-  if (hipEventRecord(r.start, st) != hipSuccess) return -1;
+  if (!r.start || !r.stop) return;
   g_records.push_back(r);
-  return (int)g_records.size() - 1;
-}
-
-void timing_stop(int slot, hipStream_t st) {
-  if (slot < 0) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  if (slot < (int)g_records.size()) hipEventRecord(g_records[slot].stop, st);
+  *start = r.start;
+  *stop = r.stop;
 }
 
 }  // namespace cartattn
