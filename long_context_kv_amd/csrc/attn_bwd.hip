@@ -1011,6 +1011,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; dp[0][r] = 0.f; dp[1][r] = 0.f; }
       rd(std::integral_constant<int, 0>{}, 0);
+      // MFMA phases run at a raised wave priority, so that the other wave of
+      // the SIMD fills the VALU slots with its softmax meanwhile
+      __builtin_amdgcn_s_setprio(1);
       static_for<NKS>([&](auto KS) {
         constexpr int ks = decltype(KS)::value;
         if constexpr (ks + 1 < NKS) {
@@ -1031,6 +1034,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       });
     }
+    __builtin_amdgcn_s_setprio(0);
     // dS^T / scale = P (dP - D) (the scale is applied to dQ at the end);
     // key k = 32 kh + d_row(r, hl) is visible iff
     // k < lim (its row exists and, for a token tile, it is not after the
@@ -1064,6 +1068,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         });
       };
       rdk(std::integral_constant<int, 0>{}, 0);
+      __builtin_amdgcn_s_setprio(1);
       static_for<4>([&](auto J) {
         constexpr int j = decltype(J)::value;
         constexpr int kh = j / 2, m = j % 2;
@@ -1081,6 +1086,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         for (int db = 0; db < NDB; ++db) acc[db] = M::mma(ka[j & 1][db], sfr, acc[db]);
         __builtin_amdgcn_sched_barrier(0);
       });
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 

@@ -327,6 +327,9 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; }
     rd(std::integral_constant<int, 0>{}, 0);
+    // MFMA phases run at a raised wave priority, so that the other wave of
+    // the SIMD fills the VALU slots with its softmax meanwhile
+    __builtin_amdgcn_s_setprio(1);
     static_for<NKS>([&](auto KS) {
       constexpr int ks = decltype(KS)::value;
       if constexpr (ks + 1 < NKS) {
@@ -343,6 +346,7 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
       __builtin_amdgcn_sched_barrier(0);
     });
   }
+  __builtin_amdgcn_s_setprio(0);
   // Mask: key k = 32 kh + d_row(r, hl) of the tile is visible iff k < lim
   // (its row exists and, for a token tile, it is not after the query).
   if (f.rows < kBN || (!f.cart && f.j0 + kBN - 1 > i0)) {
@@ -398,6 +402,7 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
       });
     };
     rdv(std::integral_constant<int, 0>{}, 0);
+    __builtin_amdgcn_s_setprio(1);
     static_for<4>([&](auto J) {
       constexpr int j = decltype(J)::value;
       constexpr int kh = j / 2, m = j % 2;
@@ -415,6 +420,7 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
       for (int db = 0; db < NDB; ++db) acc[db] = M::mma(va[j & 1][db], pf, acc[db]);
       __builtin_amdgcn_sched_barrier(0);
     });
+    __builtin_amdgcn_s_setprio(0);
   }
 }
 
