@@ -467,8 +467,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const bool cart = r0 < a.n_ct * a.splits_c;
   int tile, split = 0, n_split = 1, b = 0, u_begin, u_end;
   if (cart) {
-    tile = r0 / a.splits_c;
-    split = r0 % a.splits_c;
+    // split-major: the workgroups that run together (consecutive ids on one
+    // XCD) read the same window of units, so their Q / dO copies share the L2
+    split = r0 / a.n_ct;
+    tile = r0 % a.n_ct;
     n_split = a.splits_c;
     const int U = a.B * a.g * a.nqt;
     u_begin = (int)((long long)split * U / a.splits_c);
@@ -1286,7 +1288,10 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
         for (long long i = 0; i < ns; ++i) pieces.emplace_back((i + 1) * u / ns - i * u / ns, ns);
       };
       for (int kv = 0; kv < d.Hkv; ++kv) {
-        for (int c = 0; c < pl.n_ct; ++c) tile(U);
+        // cartridge tiles split-major (every tile has the same pieces)
+        const long long ns = (U + T - 1) / T;
+        for (long long i = 0; i < ns; ++i)
+          for (int c = 0; c < pl.n_ct; ++c) pieces.emplace_back((i + 1) * U / ns - i * U / ns, ns);
         for (int b = 0; b < d.B; ++b)
           for (int t = 0; t < pl.n_tt; ++t) tile(tok_units(t));
       }
