@@ -56,7 +56,7 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   float* lse2;        // [B][Hq][n]: lse * log2(e), written by the preprocess
-  float* delta;       // [B][Hq][n]
+  float* delta;       // [B][Hq][n], -D (D = dO . O per row)
   float* dq_acc;      // [B][n][Hq][D]
   void* dq;           // tok dtype
   void* dk_tok;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
       const bool vis = key_ok && (cart || my_key <= i);   // i >= n has lse2 = +inf
       const float pv = vis ? exp2f(s[r] * a.scale_log2 - lse2s[qq]) : 0.f;
       s[r] = pv;                                  // P
-      dp[r] = pv * (dp[r] - dls[qq]);             // dS (unscaled)
+      dp[r] = pv * (dp[r] + dls[qq]);             // dS (unscaled)
     }
 
     // dV += P^T dO, dK += dS^T Q (A from registers, B = transposed tiles).
@@ -623,16 +623,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const uint32_t ld_lane = L_OFF + 16 * hl;
 
   // Softmax of result register r: P = exp2(S c - lse2) and G = P (dP - D)
-  // in place (the softmax scale is applied to dK once at the end). Masked
-  // pairs (query not visible from the key) get P = 0.
-  auto softmax_elem = [&](int r, uint32_t rel, float l2, float dd, f32x16& s, f32x16& g) {
-    float arg = fmaf(s[r], c, -l2);
-    arg = (rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < vis_span) ? arg : -INFINITY;
-    const float p_ = __builtin_amdgcn_exp2f(arg);
+  // in place (the softmax scale is applied to dK once at the end). Pairs
+  // whose query the key cannot see get P = G = 0 afterwards, in the packed
+  // operands, for the units that have such pairs (mask_packed).
+  auto softmax_elem = [&](int r, float l2, float nd, f32x16& s, f32x16& g) {
+    const float p_ = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
     s[r] = p_;
-    g[r] = p_ * (g[r] - dd);
+    g[r] = fmaf(p_, g[r], p_ * nd);   // P dP + P (-D)
+  };
+  // Zero the packed P and G of the pairs of a unit that the key cannot see
+  // (rel = mask_rel of the unit): the bf16 halves of each 32-bit word are
+  // kept or cleared by an AND mask, whatever the unmasked values were.
+  auto mask_packed = [&](uint32_t rel, bf16x8 (&pp)[2], bf16x8 (&gg)[2]) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      uint4 pw = __builtin_bit_cast(uint4, pp[mm]), gw = __builtin_bit_cast(uint4, gg[mm]);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r0 = 8 * mm + 2 * e;   // registers r0, r0 + 1 of the word
+        const bool v0 = rel + (uint32_t)(8 * (r0 >> 2) + (r0 & 3)) < vis_span;
+        const bool v1 = rel + (uint32_t)(8 * ((r0 + 1) >> 2) + ((r0 + 1) & 3)) < vis_span;
+        w[e] = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
+      }
+      pw.x &= w[0]; pw.y &= w[1]; pw.z &= w[2]; pw.w &= w[3];
+      gw.x &= w[0]; gw.y &= w[1]; gw.z &= w[2]; gw.w &= w[3];
+      pp[mm] = __builtin_bit_cast(bf16x8, pw);
+      gg[mm] = __builtin_bit_cast(bf16x8, gw);
+    }
   };
   auto mask_rel = [&](const Unit& x) { return (uint32_t)(x.qt * kBQ + 4 * hl - vis_lo); };
+  auto unit_needs_mask = [&](const Unit& x) {
+    const int i0 = x.qt * kBQ;
+    return (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
+  };
   // Transpose fragment f = m * NDB + db (queries 16 m .., columns 32 db ..)
   // of the dO and Q tiles of a stage: 4 reads.
   struct TrOp { bf16x8 o, q; };
@@ -674,15 +698,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // with no LDS read pending.
   constexpr int PER = 16 / NKS;   // softmax result registers per k-step
   auto step = [&](auto HA, auto HS, auto HB, uint32_t stA, uint32_t stL, uint32_t stB,
-                  uint32_t rel, f32x16& sa, f32x16& ga, f32x16& ss, f32x16& gs,
+                  f32x16& sa, f32x16& ga, f32x16& ss, f32x16& gs,
                   const bf16x8 (&pb)[2], const bf16x8 (&gb)[2], bf16x8 (&pn)[2],
                   bf16x8 (&gn)[2], const Copy& cp, bool more) {
     constexpr bool A = decltype(HA)::value, S = decltype(HS)::value, BB = decltype(HB)::value;
     bf16x8 qa[2], oa[2];
     TrOp t[2];
-    f32x4 lq[2], dq4[2];
+    f32x4 lq[2], dn[2];
     // reads of k-step ks: 2 row fragments (A), 4 transpose reads (B), and
-    // lse / D of the lane's registers 4 c4 .. at the first k-step using them (S)
+    // lse and -D of the lane's registers 4 c4 .. of unit j-1 at the first
+    // k-step using them (S)
     auto n_reads = [](int ks) {
       return (A ? 2 : 0) + (BB ? 4 : 0) + ((S && (PER * ks) % 4 == 0) ? 2 : 0);
     };
@@ -695,7 +720,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       if constexpr (S && (PER * ks) % 4 == 0) {
         constexpr int c4 = PER * ks / 4;
         lq[c4 & 1] = lds_read16<32 * c4>(stL + ld_lane);
-        dq4[c4 & 1] = lds_read16<4 * kBQ + 32 * c4>(stL + ld_lane);
+        dn[c4 & 1] = lds_read16<4 * kBQ + 32 * c4>(stL + ld_lane);
       }
       if constexpr (BB) tr_frag(stB, KS, t[slot]);
     };
@@ -713,11 +738,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       } else {
         lds_wait<0>();
       }
-      if constexpr (A) { lds_tie(qa[ks & 1]); lds_tie(oa[ks & 1]); }
+      if constexpr (A) {
+        lds_tie(qa[ks & 1]);
+        lds_tie(oa[ks & 1]);
+
+      }
       if constexpr (BB) { lds_tie(t[ks & 1].o); lds_tie(t[ks & 1].q); }
       if constexpr (S && (PER * ks) % 4 == 0) {
         lds_tie(lq[(PER * ks / 4) & 1]);
-        lds_tie(dq4[(PER * ks / 4) & 1]);
+        lds_tie(dn[(PER * ks / 4) & 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (A) {
@@ -735,7 +764,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
         for (int j = 0; j < PER; ++j) {
           const int r = PER * ks + j;
           const int c4 = r >> 2;
-          softmax_elem(r, rel, lq[c4 & 1][r & 3], dq4[c4 & 1][r & 3], ss, gs);
+          softmax_elem(r, lq[c4 & 1][r & 3], dn[c4 & 1][r & 3], ss, gs);
         }
         if constexpr ((PER * (ks + 1)) % 8 == 0) {
           constexpr int mm = PER * (ks + 1) / 8 - 1;
@@ -766,10 +795,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       gb[0] = gn[0]; gb[1] = gn[1];
       sj = sj + 1 == NST ? 0 : sj + 1;
     };
+    // after a step with the softmax of unit `us`: its pairs the key cannot
+    // see are cleared in the packed operands
+    auto mask_us = [&]() {
+      if (unit_needs_mask(us)) mask_packed(mask_rel(us), pn, gn);
+    };
     // j = 0: phase A of unit 0
     wait_unit(0);
     lds_barrier();
-    step(Yes{}, No{}, No{}, st_of(0), 0u, 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
+    step(Yes{}, No{}, No{}, st_of(0), 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
          copy_setup(uc, (sj + AHEAD) % NST), nu > AHEAD);
     uc = next(uc);
     rotate();
@@ -777,12 +811,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     if (nu > 1) {
       wait_unit(1);
       lds_barrier();
-      step(Yes{}, Yes{}, No{}, st_of(0), st_of(1), 0u, mask_rel(us), sa, ga, ss, gs, pb, gb, pn,
-           gn, copy_setup(uc, (sj + AHEAD) % NST), nu > 1 + AHEAD);
+      step(Yes{}, Yes{}, No{}, st_of(0), st_of(1), 0u, sa, ga, ss, gs, pb, gb, pn, gn,
+           copy_setup(uc, (sj + AHEAD) % NST), nu > 1 + AHEAD);
     } else {
-      step(No{}, Yes{}, No{}, 0u, st_of(1), 0u, mask_rel(us), sa, ga, ss, gs, pb, gb, pn, gn, none,
-           false);
+      step(No{}, Yes{}, No{}, 0u, st_of(1), 0u, sa, ga, ss, gs, pb, gb, pn, gn, none, false);
     }
+    mask_us();
     us = next(us);
     uc = next(uc);
     rotate();
@@ -790,8 +824,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     for (int j = 2; j < nu; ++j) {
       wait_unit(j);
       lds_barrier();
-      step(Yes{}, Yes{}, Yes{}, st_of(0), st_of(1), st_of(2), mask_rel(us), sa, ga, ss, gs, pb, gb,
-           pn, gn, copy_setup(uc, (sj + AHEAD) % NST), j + AHEAD < nu);
+      step(Yes{}, Yes{}, Yes{}, st_of(0), st_of(1), st_of(2), sa, ga, ss, gs, pb, gb, pn, gn,
+           copy_setup(uc, (sj + AHEAD) % NST), j + AHEAD < nu);
+      mask_us();
       us = next(us);
       uc = next(uc);
       rotate();
@@ -800,11 +835,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     // j = nu+1: phase B of unit nu-1. No copies remain, so no waits. (With
     // nu = 1 the softmax of unit 0 ran at j = 1 and j = 2 is past the loop.)
     if (nu > 1) {
-      step(No{}, Yes{}, Yes{}, 0u, st_of(1), st_of(2), mask_rel(us), sa, ga, ss, gs, pb, gb, pn,
-           gn, none, false);
+      step(No{}, Yes{}, Yes{}, 0u, st_of(1), st_of(2), sa, ga, ss, gs, pb, gb, pn, gn, none, false);
+      mask_us();
       rotate();
     }
-    step(No{}, No{}, Yes{}, 0u, 0u, st_of(2), 0u, sa, ga, ss, gs, pb, gb, pn, gn, none, false);
+    step(No{}, No{}, Yes{}, 0u, 0u, st_of(2), sa, ga, ss, gs, pb, gb, pn, gn, none, false);
   }
 
   // ---- dK (times the softmax scale), dV. A tile cut into pieces: every
@@ -1054,7 +1089,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
           arg = kc < lim_l ? arg : -INFINITY;
         }
         const float p_ = __builtin_amdgcn_exp2f(arg);
-        dp[kh][r] = p_ * (dp[kh][r] - dl);
+        dp[kh][r] = p_ * (dp[kh][r] + dl);
       }
     // dQ^T += K^T dS^T in four steps j = (kh, m): K^T fragments by transpose
     // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
@@ -1154,7 +1189,8 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
   reinterpret_cast<bf16x4*>(a.dq)[e] = o;
 }
 
-// D_i = dO_i . O_i and lse_i * log2(e) for every (b, h, i), (f32 tokens) dQ
+// -D_i = -(dO_i . O_i) (stored negated: G = P dP + P (-D) is one multiply
+// and one FMA) and lse_i * log2(e) for every (b, h, i), (f32 tokens) dQ
 // accumulator := 0, and (bf16) the key tiles' piece counters := 0. Sixteen
 // lanes per row (D/16 elements each), 16 rows per workgroup; the row sum is
 // taken with DPP adds.
@@ -1180,7 +1216,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
     const int i = bi % a.n;
     const int b = bi / a.n;
     const size_t li = ((size_t)b * a.Hq + h) * a.n + i;
-    a.delta[li] = acc;
+    a.delta[li] = -acc;
     a.lse2[li] = a.lse[li] * kLog2e;
   }
   if (a.zero_dq) {
