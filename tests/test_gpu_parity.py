@@ -180,6 +180,39 @@ def test_attention_parity_small(C, case, mode):
     assert np.max(np.abs(f64(lse) - lse_ref)) <= (1e-5 if mode == "f32" else 2e-2)
 
 
+# Shapes that give the dK/dV kernel's software pipeline pieces of 1, 2, 3 and
+# many units, ragged query tiles, GQA groups of 1 to 4, key tiles cut into
+# pieces (reduced in the kernel) and token-heavy grids.
+PIPELINE = [
+    # name, B, n, p, Hq, Hkv, d
+    ("units-1", 1, 20, 100, 1, 1, 128),
+    ("units-2", 1, 40, 130, 2, 1, 128),
+    ("units-3-ragged", 1, 70, 260, 3, 1, 128),
+    ("pieces-g4", 2, 200, 600, 8, 2, 128),
+    ("pieces-d64", 2, 150, 500, 8, 2, 64),
+    ("token-heavy", 1, 500, 16, 4, 2, 128),
+]
+
+
+@pytest.mark.parametrize("case", PIPELINE, ids=[c[0] for c in PIPELINE])
+def test_attention_parity_pipeline_edges(C, case):
+    name, B, n, p, Hq, Hkv, d = case
+    say("pipeline", name)
+    x = W.train_inputs(_shape(name, B, n, p, Hq, Hkv, d, torch.bfloat16, torch.float32, 91))
+    g = _dev(x)
+    o, lse = C.attn_fwd(g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"], frozen_rows=1)
+    grads = C.attn_bwd(g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"], o, lse, g["dout"],
+                       frozen_rows=1)
+    torch.cuda.synchronize()
+    args = [f64(x[k]) for k in ("q", "k_tok", "v_tok", "k_cart", "v_cart")]
+    o_ref, _ = O.attn_fwd(*args)
+    gr = O.attn_bwd(*args, f64(x["dout"]), frozen_rows=1)
+    got = dict(o=o, dq=grads[0], dk_tok=grads[1], dv_tok=grads[2], dk_cart=grads[3],
+               dv_cart=grads[4])
+    ref = dict(o=o_ref, dq=gr[0], dk_tok=gr[1], dv_tok=gr[2], dk_cart=gr[3], dv_cart=gr[4])
+    _compare(got, ref, TOL_BF16, 1)
+
+
 def test_peaked_softmax_and_accumulate(C):
     """Sharper scores (q x 4) stress the online-softmax rescaling; a second
     backward with accumulate_cart adds into the cartridge gradients."""
