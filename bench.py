@@ -39,10 +39,10 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "qwen3-0.6b-layer"): (94.54e6, "ecc1deed8f663929"),
-    ("attn_bwd", "qwen3-8b-layer"): (696.26e6, "ecc1deed8f663929"),
-    ("attn_fwd", "qwen3-8b-layer"): (237.42e6, "58416d21a1e1cd16"),
-    ("decode", "serving-decode"): (1225.64e6, "6e92833e52653c08"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (175.53e6, "f214b727f9f78f81"),
+    ("attn_bwd", "qwen3-8b-layer"): (1163.66e6, "f214b727f9f78f81"),
+    ("attn_fwd", "qwen3-8b-layer"): (235.63e6, "da5103b717b3d371"),
+    ("decode", "serving-decode"): (1225.64e6, "2d62769d62840f58"),
 }
 
 
