@@ -506,9 +506,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const int vis_lo = !key_ok ? a.n : (cart ? 0 : my_key);
   const uint32_t vis_span = (uint32_t)(a.n - vis_lo);
 
-  // ---- unit counters
+  // ---- unit cursor: (batch, q-head of the group, query tile) and the
+  // offsets of its Q / dO rows (bytes) and of its lse / D (elements); within
+  // a head the next unit is one query tile further, so only a change of head
+  // recomputes them
   const int qt0 = cart ? 0 : tile * (kBNB / kBQ);
-  struct Unit { int bb, hin, qt; };
+  const uint32_t q_row_bytes = (uint32_t)(a.Hq * D * 2);
+  struct Unit { int bb, hin, qt; size_t qoff, loff; };
+  auto locate_unit = [&](Unit& x) {
+    const int h = kv * a.g + x.hin;
+    x.qoff = (((size_t)x.bb * a.n + (size_t)x.qt * kBQ) * a.Hq + h) * (size_t)(D * 2);
+    x.loff = ((size_t)x.bb * a.Hq + h) * a.n + (size_t)x.qt * kBQ;
+  };
   Unit cu;
   if (cart) {
     cu.bb = u_begin / (a.g * a.nqt);
@@ -520,75 +529,80 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     cu.hin = u_begin / nq;
     cu.qt = qt0 + u_begin % nq;
   }
+  locate_unit(cu);
   auto next = [&](Unit x) {
     if (++x.qt == a.nqt) {
       x.qt = qt0;
       if (++x.hin == a.g) { x.hin = 0; ++x.bb; }
+      locate_unit(x);
+    } else {
+      x.qoff += (size_t)kBQ * q_row_bytes;
+      x.loff += kBQ;
     }
     return x;
   };
+  // Units whose pairs are not all visible (some key of the tile missing, the
+  // query tile ragged, or a token tile's diagonal) take the mask.
+  const bool mask_all = j0 + kBNB > limit;
+  const int q_full = a.n / kBQ;                          // first ragged query tile
+  const int q_diag = cart ? 0 : qt0 + kBNB / kBQ;        // first tile past the diagonal
+  auto needs_mask = [&](int qt) { return mask_all || qt >= q_full || qt < q_diag; };
 
-  // ---- per-lane offsets of this wave's share of a unit's Q / dO copy
-  const int q_row_bytes = a.Hq * D * 2;
-  int c_roff[QPW], c_coff[QPW];
+  // ---- per-lane offsets of this wave's share of a unit's Q / dO copy. Rows
+  // past the unit's last (ragged tile, or the rounding of the tile to whole
+  // blocks) fall outside the copy's buffer range and read as zeros, which the
+  // mask discards.
+  static_assert(QBLK == 4 * (QPW - 1) + 2, "waves 0, 1 copy the last two blocks");
+  uint32_t c_off[QPW];
 #pragma unroll
   for (int k = 0; k < QPW; ++k) {
     int r, cc;
     TL::locate((4 * k + wave) * 64 + lane, r, cc);
-    c_roff[k] = r * q_row_bytes;
-    c_coff[k] = (cc < D / 8 ? cc : 0) * 16;
+    c_off[k] = (uint32_t)r * q_row_bytes + (uint32_t)(cc < D / 8 ? cc : 0) * 16;
   }
-  // The copy of one unit, in parts: part k < QPW copies this wave's k-th
-  // 1 KiB block of the Q and dO tiles, part QPW the lse (wave 2) or D
-  // (wave 3) row in two halves. Every wave issues the same number of copies
-  // per unit, so the wait counts of the ring are constants.
+  // The copy of one unit, in parts: part k < QPW-1 copies this wave's k-th
+  // 1 KiB block of the Q and dO tiles; in part QPW-1 waves 0 and 1 copy the
+  // last two blocks while wave 2 copies lse*log2(e) and wave 3 -D, in halves
+  // of 16 rows. Every wave issues the same number of copies per unit, and a
+  // copy past the piece's last unit (its buffer range empty) still issues its
+  // loads, which read nothing: the wait counts of the ring are constants.
   constexpr int NDMA = 2 * QPW;
-  static_assert(2 * ((QBLK + 3) / 4) == NDMA && 2 * ((QBLK + 2) / 4) == NDMA &&
-                    2 * ((QBLK + 1) / 4) + 2 == NDMA && 2 * (QBLK / 4) + 2 == NDMA,
-                "copies per unit differ between waves");
-  struct Copy { buf_rsrc rq, ro, rl; int lim, rows; bf16* Qs; bf16* Os; float* Ls; };
-  auto copy_setup = [&](const Unit& x, int st) {
+  const float* lbase = wave == 2 ? a.lse2 : a.delta;
+  struct Copy { buf_rsrc rq, ro, rl; uint32_t dst; };
+  auto copy_setup = [&](const Unit& x, uint32_t dst, bool real) {
     Copy c;
-    const int h = kv * a.g + x.hin;
-    const int i0 = x.qt * kBQ;
-    c.rows = min(kBQ, a.n - i0);
-    c.lim = (c.rows - 1) * q_row_bytes;
-    const size_t base = (((size_t)x.bb * a.n + i0) * a.Hq + h) * D * 2;
-    c.rq = make_rsrc(reinterpret_cast<const char*>(a.q) + base, c.lim + D * 2);
-    c.ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + base, c.lim + D * 2);
-    const size_t li = ((size_t)x.bb * a.Hq + h) * a.n + i0;
-    c.rl = make_rsrc((wave == 2 ? a.lse2 : a.delta) + li, 4 * c.rows);
-    c.Qs = Qst(st);
-    c.Os = Ost(st);
-    c.Ls = Lst(st);
+    const int rows = min(kBQ, a.n - x.qt * kBQ);
+    const uint32_t nq = real ? (uint32_t)(rows - 1) * q_row_bytes + D * 2 : 0u;
+    c.rq = make_rsrc(reinterpret_cast<const char*>(a.q) + x.qoff, nq);
+    c.ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + x.qoff, nq);
+    c.rl = make_rsrc(lbase + x.loff, real ? 4u * (uint32_t)rows : 0u);
+    c.dst = dst;
     return c;
   };
+  const uint32_t ring_base = lds_addr(ring);
   auto copy_part = [&](const Copy& c, int k) {
-    if (k < QPW) {
-      const int blk = 4 * k + wave;
-      if (blk < QBLK) {
-        const uint32_t off = min(c_roff[k], c.lim) + c_coff[k];
-        dma16(c.rq, off, c.Qs + blk * 512);
-        dma16(c.ro, off, c.Os + blk * 512);
-      }
-    } else if (k == QPW && wave >= 2) {
-      // wave 2 copies lse*log2(e) into Ls[0, 32), wave 3 copies D into Ls[32, 64)
-      float* dst = c.Ls + 32 * (wave - 2);
-      if (lane < 16) {
-        dma4(c.rl, 4 * min(lane, c.rows - 1), dst);
-        dma4(c.rl, 4 * min(lane + 16, c.rows - 1), dst + 16);
-      }
+    const uint32_t st = c.dst - ring_base;   // byte offset of the stage in the ring
+    if (k < QPW - 1 || wave < 2) {
+      const uint32_t blk = 4 * k + wave;
+      dma16_at(c.rq, c_off[k], ring, st + blk * 1024);
+      dma16_at(c.ro, c_off[k], ring, st + O_OFF + blk * 1024);
+    } else if (lane < 16) {
+      const uint32_t dst = st + L_OFF + 128 * (wave - 2);
+      dma4_at(c.rl, 4 * lane, ring, dst);
+      dma4_at(c.rl, 4 * lane + 64, ring, dst + 64);
     }
   };
-  auto issue = [&](const Unit& x, int st) {
-    const Copy c = copy_setup(x, st);
+  auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
+  auto issue = [&](const Unit& x, int st, bool real) {
+    const Copy c = copy_setup(x, stage_addr(st), real);
 #pragma unroll
-    for (int k = 0; k <= QPW; ++k) copy_part(c, k);
+    for (int k = 0; k < QPW; ++k) copy_part(c, k);
   };
 
-  // ---- the wave's K, V rows as B operands (units 0 and 1 are copied around
-  // these loads)
-  if (u_begin < u_end) issue(cu, 0);
+  // ---- the wave's K, V rows as B operands (the copies of units 0 .. AHEAD-1
+  // are issued around these loads)
+  const int nu = u_end - u_begin;
+  if (nu > 0) issue(cu, 0, true);
   bf16x8 kf[NKS], vf[NKS];
   {
     const int kr = key_ok ? my_key : limit - 1;
@@ -598,12 +612,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kr * row_stride + 16 * ks + 8 * hl);
     }
   }
-  const int nu = u_end - u_begin;
-  {
+  if (nu > 0) {
     Unit x = cu;
-    for (int u = 1; u < min(nu, AHEAD); ++u) {
+    for (int u = 1; u < AHEAD; ++u) {
       x = next(x);
-      issue(x, u);
+      issue(x, u, u < nu);
     }
   }
 
@@ -652,11 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       gg[mm] = __builtin_bit_cast(bf16x8, gw);
     }
   };
-  auto mask_rel = [&](const Unit& x) { return (uint32_t)(x.qt * kBQ + 4 * hl - vis_lo); };
-  auto unit_needs_mask = [&](const Unit& x) {
-    const int i0 = x.qt * kBQ;
-    return (i0 + kBQ > a.n) || !key_ok_all(cart, j0, i0, limit);
-  };
+  auto mask_rel = [&](int qt) { return (uint32_t)(qt * kBQ + 4 * hl - vis_lo); };
   // Transpose fragment f = m * NDB + db (queries 16 m .., columns 32 db ..)
   // of the dO and Q tiles of a stage: 4 reads.
   struct TrOp { bf16x8 o, q; };
@@ -669,20 +678,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   };
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
-  const uint32_t ring_base = lds_addr(ring);
-  auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
 
   // At the top of step j, unit j has landed once at most the copies of the
-  // units after it (j+1 .. j+AHEAD-1, those that exist) are in flight.
-  auto wait_unit = [&](int j) {
-    const int later = min(AHEAD - 1, nu - 1 - j);
-    static_assert(AHEAD <= 3, "wait counts below cover up to two later units");
-    if (later >= 2) CART_WAIT_VMCNT(2 * NDMA);
-    else if (later == 1) CART_WAIT_VMCNT(NDMA);
-    else CART_WAIT_VMCNT(0);
-  };
+  // AHEAD-1 units after it are in flight (every step issues one unit's copy).
   static_assert(2 * NDMA < 64, "copies of two units must fit the wait count");
-  static_assert(QPW + 1 <= NKS, "a unit's copy parts must fit the k-steps of a step");
+  static_assert(QPW <= NKS, "a unit's copy parts must fit the k-steps of a step");
+  auto wait_unit = [&]() { CART_WAIT_VMCNT((AHEAD - 1) * NDMA); };
 
   // Step j of the unit loop, software-pipelined over three units:
   //  A: S = Q K^T and dP = dO V^T of unit j (rows = queries, columns = this
@@ -700,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   auto step = [&](auto HA, auto HS, auto HB, uint32_t stA, uint32_t stL, uint32_t stB,
                   f32x16& sa, f32x16& ga, f32x16& ss, f32x16& gs,
                   const bf16x8 (&pb)[2], const bf16x8 (&gb)[2], bf16x8 (&pn)[2],
-                  bf16x8 (&gn)[2], const Copy& cp, bool more) {
+                  bf16x8 (&gn)[2], const Copy& cp) {
     constexpr bool A = decltype(HA)::value, S = decltype(HS)::value, BB = decltype(HB)::value;
     bf16x8 qa[2], oa[2];
     TrOp t[2];
@@ -758,7 +759,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
         dv[db] = M::mma(pb[m], t[ks & 1].o, dv[db]);
         dk[db] = M::mma(gb[m], t[ks & 1].q, dk[db]);
       }
-      if (more) copy_part(cp, ks);
+      if constexpr (A && ks < QPW) copy_part(cp, ks);
       if constexpr (S) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
@@ -783,63 +784,75 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     f32x16 sa, ga, ss, gs;
     bf16x8 pb[2], gb[2], pn[2], gn[2];
     const Copy none{};
-    // units j-1 (softmax) and j+AHEAD (copy) of step j
-    Unit us = cu, uc = cu;
+    // the unit copied at step j (j + AHEAD) and the query tile of the unit
+    // whose softmax runs (j - 1)
+    Unit uc = cu;
     for (int u = 0; u < AHEAD; ++u) uc = next(uc);
-    int sj = 0;   // stage of unit j (unit u lives in stage u % NST)
-    auto st_of = [&](int back) { return stage_addr(sj >= back ? sj - back : sj - back + NST); };
+    int qs = cu.qt;
+    // LDS addresses of the stages of units j, j-1, j-2 and j+AHEAD (unit u
+    // lives in stage u % NST; AHEAD + 3 == NST, so unit j+1+AHEAD takes the
+    // stage of unit j-2)
+    static_assert(AHEAD + 3 == NST, "stage rotation");
+    const uint32_t st_last = stage_addr(NST - 1);
+    uint32_t s0 = stage_addr(0), s1 = st_last, s2 = stage_addr(NST - 2), sc = stage_addr(AHEAD);
     auto rotate = [&]() {
       ss = sa;
       gs = ga;
       pb[0] = pn[0]; pb[1] = pn[1];
       gb[0] = gn[0]; gb[1] = gn[1];
-      sj = sj + 1 == NST ? 0 : sj + 1;
+      sc = s2;
+      s2 = s1;
+      s1 = s0;
+      s0 = s0 == st_last ? ring_base : s0 + (uint32_t)(2 * STAGE);
     };
-    // after a step with the softmax of unit `us`: its pairs the key cannot
-    // see are cleared in the packed operands
+    // after a step with the softmax of the unit of query tile qs: its pairs
+    // the key cannot see are cleared in the packed operands
     auto mask_us = [&]() {
-      if (unit_needs_mask(us)) mask_packed(mask_rel(us), pn, gn);
+      if (needs_mask(qs)) mask_packed(mask_rel(qs), pn, gn);
+      qs = qs + 1 == a.nqt ? qt0 : qs + 1;
     };
     // j = 0: phase A of unit 0
-    wait_unit(0);
-    lds_barrier();
-    step(Yes{}, No{}, No{}, st_of(0), 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
-         copy_setup(uc, (sj + AHEAD) % NST), nu > AHEAD);
+    wait_unit();
+    lds_barrier_waited();
+    step(Yes{}, No{}, No{}, s0, 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
+         copy_setup(uc, sc, AHEAD < nu));
     uc = next(uc);
     rotate();
     // j = 1: phase A of unit 1 (if any) and the softmax of unit 0
     if (nu > 1) {
-      wait_unit(1);
-      lds_barrier();
-      step(Yes{}, Yes{}, No{}, st_of(0), st_of(1), 0u, sa, ga, ss, gs, pb, gb, pn, gn,
-           copy_setup(uc, (sj + AHEAD) % NST), nu > 1 + AHEAD);
+      wait_unit();
+      lds_barrier_waited();
+      step(Yes{}, Yes{}, No{}, s0, s1, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
+           copy_setup(uc, sc, 1 + AHEAD < nu));
     } else {
-      step(No{}, Yes{}, No{}, 0u, st_of(1), 0u, sa, ga, ss, gs, pb, gb, pn, gn, none, false);
+      step(No{}, Yes{}, No{}, 0u, s1, 0u, sa, ga, ss, gs, pb, gb, pn, gn, none);
     }
     mask_us();
-    us = next(us);
     uc = next(uc);
     rotate();
     // j = 2 .. nu-1: all three
     for (int j = 2; j < nu; ++j) {
-      wait_unit(j);
-      lds_barrier();
-      step(Yes{}, Yes{}, Yes{}, st_of(0), st_of(1), st_of(2), sa, ga, ss, gs, pb, gb, pn, gn,
-           copy_setup(uc, (sj + AHEAD) % NST), j + AHEAD < nu);
+      wait_unit();
+      lds_barrier_waited();
+      step(Yes{}, Yes{}, Yes{}, s0, s1, s2, sa, ga, ss, gs, pb, gb, pn, gn,
+           copy_setup(uc, sc, j + AHEAD < nu));
       mask_us();
-      us = next(us);
       uc = next(uc);
       rotate();
     }
     // j = nu: softmax of unit nu-1 and phase B of unit nu-2 (nu >= 2); then
-    // j = nu+1: phase B of unit nu-1. No copies remain, so no waits. (With
-    // nu = 1 the softmax of unit 0 ran at j = 1 and j = 2 is past the loop.)
+    // j = nu+1: phase B of unit nu-1. Their stages landed before step nu-1.
+    // (With nu = 1 the softmax of unit 0 ran at j = 1 and j = 2 is past the
+    // loop.)
     if (nu > 1) {
-      step(No{}, Yes{}, Yes{}, 0u, st_of(1), st_of(2), sa, ga, ss, gs, pb, gb, pn, gn, none, false);
+      step(No{}, Yes{}, Yes{}, 0u, s1, s2, sa, ga, ss, gs, pb, gb, pn, gn, none);
       mask_us();
       rotate();
     }
-    step(No{}, No{}, Yes{}, 0u, 0u, st_of(2), sa, ga, ss, gs, pb, gb, pn, gn, none, false);
+    step(No{}, No{}, Yes{}, 0u, 0u, s2, sa, ga, ss, gs, pb, gb, pn, gn, none);
+    // the copies past the piece's last unit read nothing but still write
+    // their LDS stages: let them finish before the workgroup can end
+    CART_WAIT_VMCNT(0);
   }
 
   // ---- dK (times the softmax scale), dV. A tile cut into pieces: every

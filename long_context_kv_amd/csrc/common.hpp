@@ -286,6 +286,16 @@ __device__ __forceinline__ void dma4(buf_rsrc r, uint32_t voff, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
                                            (int)voff, 0, 0, 0);
 }
+// The same with the LDS destination `off` bytes past `lds` (an offset into
+// the object `lds` points to, so the compiler still knows what is written).
+__device__ __forceinline__ void dma16_at(buf_rsrc r, uint32_t voff, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) char*)lds + off, 16, (int)voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4_at(buf_rsrc r, uint32_t voff, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) char*)lds + off, 4, (int)voff, 0, 0, 0);
+}
 
 // Per-lane source positions of this wave's share of the asynchronous copy of
 // a tile of NROWS rows x D bf16 into an LDS tile of tile_elems<D, NROWS>()
@@ -391,6 +401,18 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier for code whose LDS traffic is all explicitly waited for:
+// LDS reads issued by the inline-assembly helpers (lds_wait) and copies into
+// LDS (CART_WAIT_VMCNT). lds_barrier's release fence would also wait for
+// every copy still in flight, including those of tiles needed only later;
+// this one keeps them in flight. The scheduling barriers keep the compiler
+// from moving any instruction across it.
+__device__ __forceinline__ void lds_barrier_waited() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wait until at most n of this wave's vector memory operations are pending
