@@ -45,6 +45,7 @@ namespace {
 constexpr int kBNB = 128;      // keys per workgroup tile
 constexpr int kBQ = 32;        // queries per unit
 constexpr int kThreads = 256;
+constexpr int kKvThreads = 512;   // dK/dV kernel: 4 pairs of waves
 
 struct BwdArgs {
   const void* q;
@@ -399,15 +400,16 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 path: two kernels, neither with atomics.
 //
-// attn_bwd_kv_kernel -- dK and dV. One workgroup per 128-key tile (4 waves x
-//   32 keys; K and V rows of a wave are register operands and its f32 dK, dV
-//   stay in registers), looping over (batch, q-head, 32-query) units. Each
-//   unit's Q, dO, LSE*log2(e) and D rows are copied global -> LDS by direct
-//   loads into a 3-deep ring of padded tiles. Software pipeline: the step of
-//   unit k computes S and dP of unit k+1, then dV += P^T dO and dK += dS^T Q
-//   of unit k (operands dO^T, Q^T by LDS transpose reads) interleaved with the
-//   softmax of unit k+1, so the MFMA chains of one unit hide the latencies of
-//   the other. One LDS-only barrier per unit.
+// attn_bwd_kv_kernel -- dK and dV. One workgroup (8 waves) per piece of a
+//   128-key tile's list of (batch, q-head, 32-query) units. Waves k and k+4
+//   (one SIMD) share keys 32k .. 32k+31 and split the work by role: wave k
+//   computes S = Q K^T, the softmax P and dV += P^T dO; wave k+4 computes
+//   dP = dO V^T, dS = P (dP - D) with P handed over through LDS, and
+//   dK += dS^T Q. Each keeps one operand (K or V rows) and one f32
+//   accumulator in registers, so two waves fit each SIMD and one's softmax
+//   runs beside the other's MFMAs. Each unit's Q, dO, LSE*log2(e) and -D rows
+//   are copied global -> LDS by direct loads into a ring of padded tiles
+//   three units ahead; one LDS-only barrier per unit.
 //
 // attn_bwd_dq_kernel -- dQ, query-major like the forward: per key tile it
 //   recomputes S^T = K Q^T and dP^T = V dO^T, forms dS^T, and accumulates
@@ -424,37 +426,39 @@ __device__ __forceinline__ bool key_ok_all(bool cart, int j0, int i0, int limit)
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   using TL = Tile<D>;
-  // Q / dO tiles in whole 1 KiB blocks, 2 more than a multiple of 4 (waves 0
-  // and 1 copy one block more than waves 2 and 3, which copy lse and D)
+  // Q / dO tiles in whole 1 KiB blocks, 2 more than a multiple of 4, so that
+  // the copy of a unit (2 QBLK blocks and the four 16-row halves of lse and
+  // -D) splits evenly over the 8 waves
   constexpr int QBLK0 = (tile_elems<D, kBQ>() + 511) / 512;
   constexpr int QBLK = QBLK0 + ((2 - QBLK0 % 4) + 4) % 4;
   constexpr int QTILE = QBLK * 512;
-  constexpr int QPW = (QBLK + 3) / 4;
-  // Ring of AHEAD + 3 unit stages: Q tile | dO tile | lse*log2(e) [32], D [32].
-  // A step of the unit loop reads three stages (row fragments of one unit,
-  // lse and D of the next older one, transpose fragments of the one before
-  // that); the copy of a unit is issued AHEAD steps before its first use,
-  // spread over the MFMAs of a step. Stages are read while copies fill
-  // others, so every LDS read of the unit loop is issued by the
-  // inline-assembly helpers, with explicit waits.
-  constexpr int AHEAD = 3;          // step j copies unit j + AHEAD
-  constexpr int NST = AHEAD + 3;
+  constexpr int NOPS = (2 * QBLK + 4) / 8;   // copies per wave per unit
+  static_assert((2 * QBLK + 4) % 8 == 0, "copies per unit must split over 8 waves");
+  // Ring of AHEAD + 2 unit stages: Q tile | dO tile | lse*log2(e) [32], -D [32].
+  // Step j reads the stages of units j (row fragments, lse) and j-1
+  // (transpose fragments, -D) and issues the copy of unit j + AHEAD, spread
+  // over its MFMAs; stages are read while copies fill others, so every LDS
+  // access of the unit loop is issued by the inline-assembly helpers with
+  // explicit waits.
+  constexpr int AHEAD = 3;
+  constexpr int NST = AHEAD + 2;
   constexpr int STAGE = 2 * QTILE + 2 * 2 * kBQ;   // bf16 elements per stage
   constexpr int O_OFF = 2 * QTILE;                  // byte offset of dO in a stage
-  constexpr int L_OFF = 4 * QTILE;                  // byte offset of lse / D
+  constexpr int L_OFF = 4 * QTILE;                  // byte offset of lse / -D
+  constexpr int XSLOT = 4 * 4096;                   // bytes of one P hand-over slot
   __shared__ __align__(16) bf16 ring[NST * STAGE];
-  auto Qst = [&](int st) { return ring + st * STAGE; };
-  auto Ost = [&](int st) { return ring + st * STAGE + QTILE; };
-  auto Lst = [&](int st) { return reinterpret_cast<float*>(ring + st * STAGE + 2 * QTILE); };
+  __shared__ __align__(16) float xchg[2 * XSLOT / 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+  const int pair = wave & 3;       // keys 32 pair .. of the tile
+  const bool grole = wave >= 4;    // G role (dP, dK) or P role (S, dV)
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   }
   const int j0 = tile * kBNB;
   const int limit = cart ? a.p : a.n;
-  const int my_key = j0 + 32 * wave + l32;
+  const int my_key = j0 + 32 * pair + l32;
   const bool key_ok = my_key < limit;
   const size_t row_stride = (size_t)a.Hkv * D;
   const bf16* kbase = cart ? reinterpret_cast<const bf16*>(a.k_cart) + kv * D
@@ -548,69 +552,78 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const int q_diag = cart ? 0 : qt0 + kBNB / kBQ;        // first tile past the diagonal
   auto needs_mask = [&](int qt) { return mask_all || qt >= q_full || qt < q_diag; };
 
-  // ---- per-lane offsets of this wave's share of a unit's Q / dO copy. Rows
-  // past the unit's last (ragged tile, or the rounding of the tile to whole
-  // blocks) fall outside the copy's buffer range and read as zeros, which the
-  // mask discards.
-  static_assert(QBLK == 4 * (QPW - 1) + 2, "waves 0, 1 copy the last two blocks");
-  uint32_t c_off[QPW];
+  // ---- this wave's copies of a unit: copy o = wave + 8 i of the list
+  // (Q blocks, dO blocks, lse halves, -D halves). Rows past the unit's last
+  // (ragged tile, or the rounding of the tile to whole blocks) fall outside
+  // the copy's buffer range and read as zeros, which the mask discards.
+  uint32_t c_off[NOPS], c_dst[NOPS];
+  bool c_dout[NOPS];
 #pragma unroll
-  for (int k = 0; k < QPW; ++k) {
-    int r, cc;
-    TL::locate((4 * k + wave) * 64 + lane, r, cc);
-    c_off[k] = (uint32_t)r * q_row_bytes + (uint32_t)(cc < D / 8 ? cc : 0) * 16;
+  for (int i = 0; i < NOPS; ++i) {
+    const int o = wave + 8 * i;
+    if (o < 2 * QBLK) {
+      const bool od = o >= QBLK;
+      const int blk = od ? o - QBLK : o;
+      int r, cc;
+      TL::locate(blk * 64 + lane, r, cc);
+      c_off[i] = (uint32_t)r * q_row_bytes + (uint32_t)(cc < D / 8 ? cc : 0) * 16;
+      c_dst[i] = (od ? O_OFF : 0) + blk * 1024;
+      c_dout[i] = od;
+    } else {
+      const int hh = o - 2 * QBLK;   // 0, 1: lse halves; 2, 3: -D halves
+      c_off[i] = 4 * (lane + 16 * (hh & 1));
+      c_dst[i] = L_OFF + 128 * (hh >> 1) + 64 * (hh & 1);
+      c_dout[i] = false;
+    }
   }
-  // The copy of one unit, in parts: part k < QPW-1 copies this wave's k-th
-  // 1 KiB block of the Q and dO tiles; in part QPW-1 waves 0 and 1 copy the
-  // last two blocks while wave 2 copies lse*log2(e) and wave 3 -D, in halves
-  // of 16 rows. Every wave issues the same number of copies per unit, and a
-  // copy past the piece's last unit (its buffer range empty) still issues its
-  // loads, which read nothing: the wait counts of the ring are constants.
-  constexpr int NDMA = 2 * QPW;
-  const float* lbase = wave == 2 ? a.lse2 : a.delta;
-  struct Copy { buf_rsrc rq, ro, rl; uint32_t dst; };
-  auto copy_setup = [&](const Unit& x, uint32_t dst, bool real) {
+  // only the last copy of waves 4..7 is an lse / -D half
+  const bool lcopy = wave >= 4;
+  const float* lbase = wave >= 6 ? a.delta : a.lse2;
+  const char* obase[NOPS];
+#pragma unroll
+  for (int i = 0; i < NOPS; ++i)
+    obase[i] = reinterpret_cast<const char*>(c_dout[i] ? a.dout : a.q);
+  // Every wave issues NOPS copies per unit, and a copy past the piece's last
+  // unit (its buffer range empty) still issues its loads, which read
+  // nothing: the wait counts of the ring are constants.
+  struct Copy { buf_rsrc r[NOPS]; uint32_t st; };
+  const uint32_t ring_base = lds_addr(ring);
+  auto copy_setup = [&](const Unit& x, uint32_t st_addr, bool real) {
     Copy c;
     const int rows = min(kBQ, a.n - x.qt * kBQ);
     const uint32_t nq = real ? (uint32_t)(rows - 1) * q_row_bytes + D * 2 : 0u;
-    c.rq = make_rsrc(reinterpret_cast<const char*>(a.q) + x.qoff, nq);
-    c.ro = make_rsrc(reinterpret_cast<const char*>(a.dout) + x.qoff, nq);
-    c.rl = make_rsrc(lbase + x.loff, real ? 4u * (uint32_t)rows : 0u);
-    c.dst = dst;
+#pragma unroll
+    for (int i = 0; i < NOPS - 1; ++i) c.r[i] = make_rsrc(obase[i] + x.qoff, nq);
+    c.r[NOPS - 1] = lcopy ? make_rsrc(lbase + x.loff, real ? 4u * (uint32_t)rows : 0u)
+                          : make_rsrc(obase[NOPS - 1] + x.qoff, nq);
+    c.st = st_addr - ring_base;   // byte offset of the stage in the ring
     return c;
   };
-  const uint32_t ring_base = lds_addr(ring);
-  auto copy_part = [&](const Copy& c, int k) {
-    const uint32_t st = c.dst - ring_base;   // byte offset of the stage in the ring
-    if (k < QPW - 1 || wave < 2) {
-      const uint32_t blk = 4 * k + wave;
-      dma16_at(c.rq, c_off[k], ring, st + blk * 1024);
-      dma16_at(c.ro, c_off[k], ring, st + O_OFF + blk * 1024);
+  auto copy_part = [&](const Copy& c, int i) {
+    if (i < NOPS - 1 || !lcopy) {
+      dma16_at(c.r[i], c_off[i], ring, c.st + c_dst[i]);
     } else if (lane < 16) {
-      const uint32_t dst = st + L_OFF + 128 * (wave - 2);
-      dma4_at(c.rl, 4 * lane, ring, dst);
-      dma4_at(c.rl, 4 * lane + 64, ring, dst + 64);
+      dma4_at(c.r[i], c_off[i], ring, c.st + c_dst[i]);
     }
   };
   auto stage_addr = [&](int st) { return ring_base + (uint32_t)(2 * STAGE) * st; };
   auto issue = [&](const Unit& x, int st, bool real) {
     const Copy c = copy_setup(x, stage_addr(st), real);
 #pragma unroll
-    for (int k = 0; k < QPW; ++k) copy_part(c, k);
+    for (int i = 0; i < NOPS; ++i) copy_part(c, i);
   };
 
-  // ---- the wave's K, V rows as B operands (the copies of units 0 .. AHEAD-1
-  // are issued around these loads)
+  // ---- the wave's operand rows (K for the P role, V for the G role) as B
+  // operands; the copies of units 0 .. AHEAD-1 are issued around these loads
   const int nu = u_end - u_begin;
   if (nu > 0) issue(cu, 0, true);
-  bf16x8 kf[NKS], vf[NKS];
+  bf16x8 kvf[NKS];
   {
+    const bf16* ob = grole ? vbase : kbase;
     const int kr = key_ok ? my_key : limit - 1;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)kr * row_stride + 16 * ks + 8 * hl);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kr * row_stride + 16 * ks + 8 * hl);
-    }
+    for (int ks = 0; ks < NKS; ++ks)
+      kvf[ks] = *reinterpret_cast<const bf16x8*>(ob + (size_t)kr * row_stride + 16 * ks + 8 * hl);
   }
   if (nu > 0) {
     Unit x = cu;
@@ -620,276 +633,232 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     }
   }
 
-  f32x16 dk[NDB], dv[NDB];
+  // dV (P role) or dK (G role) of the wave's 32 keys
+  f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   const float c = a.scale_log2;
 
   // Per-lane LDS byte offsets inside a stage: the row fragment (row l32,
   // 8 elements at 8 hl), the transpose strip (tr_col4's lane pattern for
-  // rows 4 hl .., columns 16 ((lane >> 4) & 1) ..) and lse / D (queries
-  // 8 c4 + 4 hl .. of a lane's result registers 4 c4 ..).
+  // rows 4 hl .., columns 16 ((lane >> 4) & 1) ..) and lse / -D (queries
+  // 8 c4 + 4 hl .. of a lane's result registers 4 c4 ..); the lane's 16-byte
+  // words of the P hand-over (4 words of 4 result registers, 1 KiB apart).
   const uint32_t row_lane = TL::off(l32, 8 * hl);
   const uint32_t tr_lane = TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
   const uint32_t ld_lane = L_OFF + 16 * hl;
-
-  // Softmax of result register r: P = exp2(S c - lse2) and G = P (dP - D)
-  // in place (the softmax scale is applied to dK once at the end). Pairs
-  // whose query the key cannot see get P = G = 0 afterwards, in the packed
-  // operands, for the units that have such pairs (mask_packed).
-  auto softmax_elem = [&](int r, float l2, float nd, f32x16& s, f32x16& g) {
-    const float p_ = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
-    s[r] = p_;
-    g[r] = fmaf(p_, g[r], p_ * nd);   // P dP + P (-D)
-  };
-  // Zero the packed P and G of the pairs of a unit that the key cannot see
-  // (rel = mask_rel of the unit): the bf16 halves of each 32-bit word are
-  // kept or cleared by an AND mask, whatever the unmasked values were.
-  auto mask_packed = [&](uint32_t rel, bf16x8 (&pp)[2], bf16x8 (&gg)[2]) {
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      uint4 pw = __builtin_bit_cast(uint4, pp[mm]), gw = __builtin_bit_cast(uint4, gg[mm]);
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r0 = 8 * mm + 2 * e;   // registers r0, r0 + 1 of the word
-        const bool v0 = rel + (uint32_t)(8 * (r0 >> 2) + (r0 & 3)) < vis_span;
-        const bool v1 = rel + (uint32_t)(8 * ((r0 + 1) >> 2) + ((r0 + 1) & 3)) < vis_span;
-        w[e] = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
-      }
-      pw.x &= w[0]; pw.y &= w[1]; pw.z &= w[2]; pw.w &= w[3];
-      gw.x &= w[0]; gw.y &= w[1]; gw.z &= w[2]; gw.w &= w[3];
-      pp[mm] = __builtin_bit_cast(bf16x8, pw);
-      gg[mm] = __builtin_bit_cast(bf16x8, gw);
-    }
-  };
+  const uint32_t x_lane = lds_addr(xchg) + 4096 * pair + 16 * lane;
   auto mask_rel = [&](int qt) { return (uint32_t)(qt * kBQ + 4 * hl - vis_lo); };
   // Transpose fragment f = m * NDB + db (queries 16 m .., columns 32 db ..)
-  // of the dO and Q tiles of a stage: 4 reads.
-  struct TrOp { bf16x8 o, q; };
-  auto tr_frag = [&](uint32_t stage, auto F, TrOp& t) {
+  // of the dO (P role) or Q (G role) tile of a stage: 2 reads.
+  auto tr_frag = [&](auto G, uint32_t stage, auto F) {
     constexpr int f = decltype(F)::value;
-    constexpr int off = TL::rows(16 * (f / NDB)) + 2 * 32 * (f % NDB);
+    constexpr int off = (decltype(G)::value ? 0 : O_OFF) + TL::rows(16 * (f / NDB)) + 2 * 32 * (f % NDB);
     const uint32_t base = stage + tr_lane;
-    t.o = cat8(lds_tr4<O_OFF + off>(base), lds_tr4<O_OFF + off + TL::rows(8)>(base));
-    t.q = cat8(lds_tr4<off>(base), lds_tr4<off + TL::rows(8)>(base));
+    return cat8(lds_tr4<off>(base), lds_tr4<off + TL::rows(8)>(base));
   };
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
 
-  // At the top of step j, unit j has landed once at most the copies of the
-  // AHEAD-1 units after it are in flight (every step issues one unit's copy).
-  static_assert(2 * NDMA < 64, "copies of two units must fit the wait count");
-  static_assert(QPW <= NKS, "a unit's copy parts must fit the k-steps of a step");
-  auto wait_unit = [&]() { CART_WAIT_VMCNT((AHEAD - 1) * NDMA); };
-
-  // Step j of the unit loop, software-pipelined over three units:
-  //  A: S = Q K^T and dP = dO V^T of unit j (rows = queries, columns = this
-  //     wave's keys; lane (key + 32 hl), reg r <-> query d_row(r, hl)), from
-  //     row fragments of its stage, into (sa, ga);
-  //  S: the softmax of unit j-1 (ss, gs, computed by the previous step),
-  //     packed to bf16 operands (pn, gn);
-  //  B: dV += P^T dO and dK += G^T Q of unit j-2 (operands pb, gb) with the
-  //     transpose fragments of its stage.
-  // The three are independent, so the MFMAs of A and B and the VALU work of
-  // S interleave in every k-step; each k-step's LDS reads (and the copy part
-  // of unit j+AHEAD, when `more`) are issued one k-step ahead. Starts and ends
-  // with no LDS read pending.
-  constexpr int PER = 16 / NKS;   // softmax result registers per k-step
-  auto step = [&](auto HA, auto HS, auto HB, uint32_t stA, uint32_t stL, uint32_t stB,
-                  f32x16& sa, f32x16& ga, f32x16& ss, f32x16& gs,
-                  const bf16x8 (&pb)[2], const bf16x8 (&gb)[2], bf16x8 (&pn)[2],
-                  bf16x8 (&gn)[2], const Copy& cp) {
-    constexpr bool A = decltype(HA)::value, S = decltype(HS)::value, BB = decltype(HB)::value;
-    bf16x8 qa[2], oa[2];
-    TrOp t[2];
-    f32x4 lq[2], dn[2];
-    // reads of k-step ks: 2 row fragments (A), 4 transpose reads (B), and
-    // lse and -D of the lane's registers 4 c4 .. of unit j-1 at the first
-    // k-step using them (S)
-    auto n_reads = [](int ks) {
-      return (A ? 2 : 0) + (BB ? 4 : 0) + ((S && (PER * ks) % 4 == 0) ? 2 : 0);
-    };
+  // Step j of one wave. Phase A (unit j < nu): the 32 x 32 block X = R W^T
+  // with R the unit's Q (P role) or dO (G role) row fragments and W the
+  // wave's K or V rows, into xa (rows = queries, columns = keys; lane
+  // (key + 32 hl), reg r <-> query d_row(r, hl)). Phase B (unit j-1): acc +=
+  // Y^T T with Y the packed operand of unit j-1 (P or G) and T the transpose
+  // fragments of its dO or Q tile. The two interleave per k-step, each
+  // k-step's LDS reads (and a copy of unit j + AHEAD, in phase A) issued one
+  // k-step ahead.
+  auto mfma_steps = [&](auto G, auto HA, auto HB, uint32_t stA, uint32_t stB, f32x16& xa,
+                        const bf16x8 (&yb)[2], const Copy& cp) {
+    constexpr bool A = decltype(HA)::value, B = decltype(HB)::value;
+    constexpr int ROFF = decltype(G)::value ? O_OFF : 0;   // row fragments of dO or Q
+    bf16x8 ra[2], tb[2];
+    constexpr int NR = (A ? 1 : 0) + (B ? 2 : 0);
     auto batch = [&](auto KS, int slot) {
       constexpr int ks = decltype(KS)::value;
-      if constexpr (A) {
-        qa[slot] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(stA + row_lane));
-        oa[slot] = __builtin_bit_cast(bf16x8, lds_read16<O_OFF + 32 * ks>(stA + row_lane));
-      }
-      if constexpr (S && (PER * ks) % 4 == 0) {
-        constexpr int c4 = PER * ks / 4;
-        lq[c4 & 1] = lds_read16<32 * c4>(stL + ld_lane);
-        dn[c4 & 1] = lds_read16<4 * kBQ + 32 * c4>(stL + ld_lane);
-      }
-      if constexpr (BB) tr_frag(stB, KS, t[slot]);
+      if constexpr (A) ra[slot] = __builtin_bit_cast(bf16x8, lds_read16<ROFF + 32 * ks>(stA + row_lane));
+      if constexpr (B) tb[slot] = tr_frag(G, stB, KS);
     };
     if constexpr (A) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sa[r] = 0.f; ga[r] = 0.f; }
+      for (int r = 0; r < 16; ++r) xa[r] = 0.f;
     }
     batch(std::integral_constant<int, 0>{}, 0);
     static_for<NKS>([&](auto KS) {
       constexpr int ks = decltype(KS)::value;
       if constexpr (ks + 1 < NKS) {
         batch(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
-        constexpr int nr = n_reads(ks + 1);
-        lds_wait<nr>();
+        lds_wait<NR>();
       } else {
         lds_wait<0>();
       }
-      if constexpr (A) {
-        lds_tie(qa[ks & 1]);
-        lds_tie(oa[ks & 1]);
-
-      }
-      if constexpr (BB) { lds_tie(t[ks & 1].o); lds_tie(t[ks & 1].q); }
-      if constexpr (S && (PER * ks) % 4 == 0) {
-        lds_tie(lq[(PER * ks / 4) & 1]);
-        lds_tie(dn[(PER * ks / 4) & 1]);
-      }
+      if constexpr (A) lds_tie(ra[ks & 1]);
+      if constexpr (B) lds_tie(tb[ks & 1]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (A) {
-        sa = M::mma(qa[ks & 1], kf[ks], sa);
-        ga = M::mma(oa[ks & 1], vf[ks], ga);
-      }
-      if constexpr (BB) {
+      if constexpr (A) xa = M::mma(ra[ks & 1], kvf[ks], xa);
+      if constexpr (B) {
         constexpr int m = ks / NDB, db = ks % NDB;
-        dv[db] = M::mma(pb[m], t[ks & 1].o, dv[db]);
-        dk[db] = M::mma(gb[m], t[ks & 1].q, dk[db]);
+        acc[db] = M::mma(yb[m], tb[ks & 1], acc[db]);
       }
-      if constexpr (A && ks < QPW) copy_part(cp, ks);
-      if constexpr (S) {
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int r = PER * ks + j;
-          const int c4 = r >> 2;
-          softmax_elem(r, lq[c4 & 1][r & 3], dn[c4 & 1][r & 3], ss, gs);
-        }
-        if constexpr ((PER * (ks + 1)) % 8 == 0) {
-          constexpr int mm = PER * (ks + 1) / 8 - 1;
-          pn[mm] = pack_regs<bf16>(ss, mm);
-          gn[mm] = pack_regs<bf16>(gs, mm);
-        }
-      }
+      if constexpr (A && ks < NOPS) copy_part(cp, ks);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
 
-  if (nu > 0) {
-    // Fixed roles: phase A accumulates into (sa, ga), the softmax works on
-    // (ss, gs) and writes (pn, gn), phase B reads (pb, gb); between steps
-    // the results move one stage on.
-    f32x16 sa, ga, ss, gs;
-    bf16x8 pb[2], gb[2], pn[2], gn[2];
+  // P role, step j: phase A = S of unit j, phase B = dV += P^T dO of unit
+  // j-1; then the softmax of unit j: P = exp2(S c - lse2), cleared where the
+  // key cannot see the query, handed to the G wave of the pair (slot j % 2)
+  // and packed for the next step.
+  auto p_step = [&](auto HA, auto HB, uint32_t stA, uint32_t stB, f32x16& s, bf16x8 (&pp)[2],
+                    const Copy& cp, int qt, uint32_t xw) {
+    constexpr bool A = decltype(HA)::value;
+    mfma_steps(No{}, HA, HB, stA, stB, s, pp, cp);
+    if constexpr (A) {
+      f32x4 lq[4];
+      lq[0] = lds_read16<0>(stA + ld_lane);
+      lq[1] = lds_read16<32>(stA + ld_lane);
+      lq[2] = lds_read16<64>(stA + ld_lane);
+      lq[3] = lds_read16<96>(stA + ld_lane);
+      lds_wait<0>();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lds_tie(lq[q]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq[r >> 2][r & 3]));
+      if (needs_mask(qt)) {
+        const uint32_t rel = mask_rel(qt);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          s[r] = rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < vis_span ? s[r] : 0.f;
+      }
+      lds_write16<0>(xw, f32x4{s[0], s[1], s[2], s[3]});
+      lds_write16<1024>(xw, f32x4{s[4], s[5], s[6], s[7]});
+      lds_write16<2048>(xw, f32x4{s[8], s[9], s[10], s[11]});
+      lds_write16<3072>(xw, f32x4{s[12], s[13], s[14], s[15]});
+      pp[0] = pack_regs<bf16>(s, 0);
+      pp[1] = pack_regs<bf16>(s, 1);
+      lds_wait<0>();
+    }
+  };
+  // G role, step j: first G = P (dP - D) of unit j-1 from its P (slot
+  // (j-1) % 2) and dP (computed by the previous step), packed; then phase A
+  // = dP of unit j, phase B = dK += G^T Q of unit j-1.
+  auto g_step = [&](auto HA, auto HB, uint32_t stA, uint32_t stB, f32x16& dp, bf16x8 (&gg)[2],
+                    const Copy& cp, uint32_t xr) {
+    constexpr bool B = decltype(HB)::value;
+    if constexpr (B) {
+      f32x4 pv[4], dn[4];
+      pv[0] = lds_read16<0>(xr);
+      pv[1] = lds_read16<1024>(xr);
+      pv[2] = lds_read16<2048>(xr);
+      pv[3] = lds_read16<3072>(xr);
+      dn[0] = lds_read16<4 * kBQ>(stB + ld_lane);
+      dn[1] = lds_read16<4 * kBQ + 32>(stB + ld_lane);
+      dn[2] = lds_read16<4 * kBQ + 64>(stB + ld_lane);
+      dn[3] = lds_read16<4 * kBQ + 96>(stB + ld_lane);
+      lds_wait<0>();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { lds_tie(pv[q]); lds_tie(dn[q]); }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p_ = pv[r >> 2][r & 3];
+        dp[r] = fmaf(p_, dp[r], p_ * dn[r >> 2][r & 3]);   // P dP + P (-D)
+      }
+      gg[0] = pack_regs<bf16>(dp, 0);
+      gg[1] = pack_regs<bf16>(dp, 1);
+    }
+    mfma_steps(Yes{}, HA, HB, stA, stB, dp, gg, cp);
+  };
+
+  // The unit loop of one role (compile-time, so that each role's loop has
+  // its own register assignment).
+  auto drive = [&](auto G) {
+    constexpr bool GR = decltype(G)::value;
+    f32x16 xa;          // S (P role) or dP (G role) of the newest unit
+    bf16x8 yb[2];       // packed P (P role) or G (G role) of the unit before
     const Copy none{};
-    // the unit copied at step j (j + AHEAD) and the query tile of the unit
-    // whose softmax runs (j - 1)
+    // the unit copied at step j (j + AHEAD) and the query tile of unit j
     Unit uc = cu;
     for (int u = 0; u < AHEAD; ++u) uc = next(uc);
     int qs = cu.qt;
-    // LDS addresses of the stages of units j, j-1, j-2 and j+AHEAD (unit u
-    // lives in stage u % NST; AHEAD + 3 == NST, so unit j+1+AHEAD takes the
-    // stage of unit j-2)
-    static_assert(AHEAD + 3 == NST, "stage rotation");
+    // LDS addresses of the stages of units j, j-1 and j+AHEAD (unit u lives
+    // in stage u % NST; AHEAD + 2 == NST, so unit j+1+AHEAD takes the stage
+    // of unit j-1)
+    static_assert(AHEAD + 2 == NST, "stage rotation");
     const uint32_t st_last = stage_addr(NST - 1);
-    uint32_t s0 = stage_addr(0), s1 = st_last, s2 = stage_addr(NST - 2), sc = stage_addr(AHEAD);
+    uint32_t s0 = stage_addr(0), s1 = st_last, sc = stage_addr(AHEAD);
+    uint32_t xs = 0;   // byte offset of slot j % 2
     auto rotate = [&]() {
-      ss = sa;
-      gs = ga;
-      pb[0] = pn[0]; pb[1] = pn[1];
-      gb[0] = gn[0]; gb[1] = gn[1];
-      sc = s2;
-      s2 = s1;
+      sc = s1;
       s1 = s0;
       s0 = s0 == st_last ? ring_base : s0 + (uint32_t)(2 * STAGE);
+      xs ^= (uint32_t)XSLOT;
     };
-    // after a step with the softmax of the unit of query tile qs: its pairs
-    // the key cannot see are cleared in the packed operands
-    auto mask_us = [&]() {
-      if (needs_mask(qs)) mask_packed(mask_rel(qs), pn, gn);
-      qs = qs + 1 == a.nqt ? qt0 : qs + 1;
+    auto run = [&](auto HA, auto HB, const Copy& cp) {
+      if constexpr (GR)
+        g_step(HA, HB, s0, s1, xa, yb, cp, x_lane + (xs ^ (uint32_t)XSLOT));
+      else
+        p_step(HA, HB, s0, s1, xa, yb, cp, qs, x_lane + xs);
     };
     // j = 0: phase A of unit 0
-    wait_unit();
+    CART_WAIT_VMCNT((AHEAD - 1) * NOPS);
     lds_barrier_waited();
-    step(Yes{}, No{}, No{}, s0, 0u, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
-         copy_setup(uc, sc, AHEAD < nu));
+    run(Yes{}, No{}, copy_setup(uc, sc, AHEAD < nu));
     uc = next(uc);
+    qs = qs + 1 == a.nqt ? qt0 : qs + 1;
     rotate();
-    // j = 1: phase A of unit 1 (if any) and the softmax of unit 0
-    if (nu > 1) {
-      wait_unit();
+    // j = 1 .. nu-1: unit j (phase A) and unit j-1 (phase B)
+    for (int j = 1; j < nu; ++j) {
+      CART_WAIT_VMCNT((AHEAD - 1) * NOPS);
       lds_barrier_waited();
-      step(Yes{}, Yes{}, No{}, s0, s1, 0u, sa, ga, ss, gs, pb, gb, pn, gn,
-           copy_setup(uc, sc, 1 + AHEAD < nu));
-    } else {
-      step(No{}, Yes{}, No{}, 0u, s1, 0u, sa, ga, ss, gs, pb, gb, pn, gn, none);
-    }
-    mask_us();
-    uc = next(uc);
-    rotate();
-    // j = 2 .. nu-1: all three
-    for (int j = 2; j < nu; ++j) {
-      wait_unit();
-      lds_barrier_waited();
-      step(Yes{}, Yes{}, Yes{}, s0, s1, s2, sa, ga, ss, gs, pb, gb, pn, gn,
-           copy_setup(uc, sc, j + AHEAD < nu));
-      mask_us();
+      run(Yes{}, Yes{}, copy_setup(uc, sc, j + AHEAD < nu));
       uc = next(uc);
+      qs = qs + 1 == a.nqt ? qt0 : qs + 1;
       rotate();
     }
-    // j = nu: softmax of unit nu-1 and phase B of unit nu-2 (nu >= 2); then
-    // j = nu+1: phase B of unit nu-1. Their stages landed before step nu-1.
-    // (With nu = 1 the softmax of unit 0 ran at j = 1 and j = 2 is past the
-    // loop.)
-    if (nu > 1) {
-      step(No{}, Yes{}, Yes{}, 0u, s1, s2, sa, ga, ss, gs, pb, gb, pn, gn, none);
-      mask_us();
-      rotate();
-    }
-    step(No{}, No{}, Yes{}, 0u, 0u, s2, sa, ga, ss, gs, pb, gb, pn, gn, none);
+    // j = nu: phase B of unit nu-1 (its stage landed before step nu-1)
+    lds_barrier_waited();
+    run(No{}, Yes{}, none);
+  };
+  if (nu > 0) {
+    if (grole) drive(Yes{});
+    else drive(No{});
     // the copies past the piece's last unit read nothing but still write
     // their LDS stages: let them finish before the workgroup can end
     CART_WAIT_VMCNT(0);
   }
+  static_assert(2 * NOPS < 64, "copies of two units must fit the wait count");
+  static_assert(NOPS <= NKS, "a unit's copies must fit the k-steps of a step");
 
-  // ---- dK (times the softmax scale), dV. A tile cut into pieces: every
-  // piece stores its f32 partial sums, and the piece that finishes last adds
-  // them up in piece order (the same sum whichever piece that is) and writes
-  // the tile's result.
-  const float scale = a.scale;
+  // ---- dV (P role) or dK times the softmax scale (G role). A tile cut into
+  // pieces: every piece stores its f32 partial sums, and the piece that
+  // finishes last adds them up in piece order (the same sum whichever piece
+  // that is) and writes the tile's result.
+  const float oscale = grole ? a.scale : 1.f;
   auto out_off = [&](int j, int col) {
     return cart ? ((size_t)j * a.Hkv + kv) * D + col
                 : (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
   };
-  auto write = [&](int j, int col, float gk, float gv) {
+  float* const out_cart = grole ? a.dk_cart : a.dv_cart;
+  bf16* const out_tok = reinterpret_cast<bf16*>(grole ? a.dk_tok : a.dv_tok);
+  auto write = [&](int j, int col, float g) {
     const size_t o = out_off(j, col);
     if (cart) {
-      if (j < a.f) {
-        a.dk_cart[o] = 0.f;
-        a.dv_cart[o] = 0.f;
-      } else if (a.accumulate) {
-        a.dk_cart[o] += gk;
-        a.dv_cart[o] += gv;
-      } else {
-        a.dk_cart[o] = gk;
-        a.dv_cart[o] = gv;
-      }
+      if (j < a.f) out_cart[o] = 0.f;
+      else if (a.accumulate) out_cart[o] += g;
+      else out_cart[o] = g;
     } else {
-      reinterpret_cast<bf16*>(a.dk_tok)[o] = (bf16)gk;
-      reinterpret_cast<bf16*>(a.dv_tok)[o] = (bf16)gv;
+      out_tok[o] = (bf16)g;
     }
   };
   if (n_split == 1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int j = j0 + 32 * wave + d_row(r, hl);
+      const int j = j0 + 32 * pair + d_row(r, hl);
       if (j >= limit) continue;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        write(j, 32 * db + l32, dk[db][r] * scale, dv[db][r]);
+      for (int db = 0; db < NDB; ++db) write(j, 32 * db + l32, acc[db][r] * oscale);
     }
     return;
   }
@@ -904,20 +873,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const size_t pstride = cart ? (size_t)a.p * row_stride : (size_t)a.B * a.n * row_stride;
   const size_t pbase = cart ? 0 : (size_t)b * a.n * row_stride;
   const uint32_t pbytes = (uint32_t)((size_t)limit * row_stride * 4);
-  float* pk = cart ? a.dk_part : a.dk_tpart;
-  float* pv = cart ? a.dv_part : a.dv_tpart;
-  const uint32_t lane_off = (uint32_t)((((size_t)(j0 + 32 * wave + 4 * hl)) * a.Hkv + kv) * D + l32) * 4;
+  float* const part = grole ? (cart ? a.dk_part : a.dk_tpart) : (cart ? a.dv_part : a.dv_tpart);
+  const uint32_t lane_off = (uint32_t)((((size_t)(j0 + 32 * pair + 4 * hl)) * a.Hkv + kv) * D + l32) * 4;
   const uint32_t row4 = (uint32_t)row_stride * 4;
   auto roff = [&](int r) { return lane_off + (uint32_t)((r & 3) + 8 * (r >> 2)) * row4; };
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int j = j0 + 32 * wave + d_row(r, hl);
+    const int j = j0 + 32 * pair + d_row(r, hl);
     if (j >= limit) continue;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const size_t o = (size_t)split * pstride + out_off(j, 32 * db + l32);
-      __hip_atomic_store(pk + o, dk[db][r] * scale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pv + o, dv[db][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(part + o, acc[db][r] * oscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   // every store of the workgroup complete, then count this piece in
@@ -932,43 +899,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   __syncthreads();
   if (!last_piece) return;
   // piece-major, so that each pass issues a piece's loads of RPASS result
-  // registers at once (64 loads for D = 128, 16 for D = 64, which keeps its
-  // two workgroups per CU)
-  constexpr int RPASS = D == 128 ? 8 : 4;
+  // registers at once (32 loads)
+  constexpr int RPASS = D == 128 ? 8 : 16;
 #pragma unroll
   for (int r0 = 0; r0 < 16; r0 += RPASS) {
-    float sk[RPASS][NDB], sv[RPASS][NDB];
+    float sg[RPASS][NDB];
 #pragma unroll
     for (int r = 0; r < RPASS; ++r)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) { sk[r][db] = 0.f; sv[r][db] = 0.f; }
+      for (int db = 0; db < NDB; ++db) sg[r][db] = 0.f;
     for (int i = 0; i < n_split; ++i) {
-      const buf_rsrc rk = make_rsrc(pk + (size_t)i * pstride + pbase, pbytes);
-      const buf_rsrc rv = make_rsrc(pv + (size_t)i * pstride + pbase, pbytes);
-      uint32_t tk[RPASS][NDB], tv[RPASS][NDB];
+      const buf_rsrc rp = make_rsrc(part + (size_t)i * pstride + pbase, pbytes);
+      uint32_t tg[RPASS][NDB];
 #pragma unroll
       for (int r = 0; r < RPASS; ++r)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          tk[r][db] = __builtin_amdgcn_raw_buffer_load_b32(rk, roff(r0 + r) + 128 * db, 0, kCpolDevice);
-          tv[r][db] = __builtin_amdgcn_raw_buffer_load_b32(rv, roff(r0 + r) + 128 * db, 0, kCpolDevice);
-        }
+        for (int db = 0; db < NDB; ++db)
+          tg[r][db] = __builtin_amdgcn_raw_buffer_load_b32(rp, roff(r0 + r) + 128 * db, 0, kCpolDevice);
       // all of the pass's loads in flight before the first add
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < RPASS; ++r)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          sk[r][db] += __builtin_bit_cast(float, tk[r][db]);
-          sv[r][db] += __builtin_bit_cast(float, tv[r][db]);
-        }
+        for (int db = 0; db < NDB; ++db) sg[r][db] += __builtin_bit_cast(float, tg[r][db]);
     }
 #pragma unroll
     for (int r = 0; r < RPASS; ++r) {
-      const int j = j0 + 32 * wave + d_row(r0 + r, hl);
+      const int j = j0 + 32 * pair + d_row(r0 + r, hl);
       if (j >= limit) continue;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) write(j, 32 * db + l32, sk[r][db], sv[r][db]);
+      for (int db = 0; db < NDB; ++db) write(j, 32 * db + l32, sg[r][db]);
     }
   }
 }
@@ -1329,7 +1289,7 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   // time wins, the largest T among equals.
   {
     const long long t_max = std::max(U, tok_units(0));   // every tile one piece
-    const int slots = 32 * (d.D == 128 ? 1 : 2);
+    const int slots = 32;   // one dK/dV workgroup per CU
     auto finish = [&](long long T) {
       std::vector<std::pair<long long, long long>> pieces;   // (units, pieces of its tile)
       auto tile = [&](long long u) {
@@ -1442,7 +1402,7 @@ static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream
   CART_LAUNCH("bwd_preprocess", (bwd_preprocess<bf16, D>), (rows + 15) / 16, 256, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_LAUNCH("attn_bwd", (attn_bwd_kv_kernel<D>), pl.grid_kv, kThreads, 0, st, a);
+  CART_LAUNCH("attn_bwd", (attn_bwd_kv_kernel<D>), pl.grid_kv, kKvThreads, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   CART_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<D>), pl.grid_q, kThreads, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

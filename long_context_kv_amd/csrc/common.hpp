@@ -370,6 +370,12 @@ __device__ __forceinline__ bf16x4 lds_tr4(uint32_t base) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(base), "n"(OFF));
   return __builtin_bit_cast(bf16x4, v);
 }
+// ds_write_b128 of a float vector (completion counted like the reads).
+template <int OFF>
+__device__ __forceinline__ void lds_write16(uint32_t base, f32x4 v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset is 16 bits");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(base), "v"(v), "n"(OFF));
+}
 template <int N>
 __device__ __forceinline__ void lds_wait() {
   static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
