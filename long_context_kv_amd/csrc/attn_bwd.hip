@@ -768,7 +768,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       gg[0] = pack_regs<bf16>(dp, 0);
       gg[1] = pack_regs<bf16>(dp, 1);
     }
+    // MFMAs at raised priority: the P wave's softmax VALU work runs beside
+    // them without holding them back
+    __builtin_amdgcn_s_setprio(2);
     mfma_steps(Yes{}, HA, HB, stA, stB, dp, gg, cp);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // The unit loop of one role (compile-time, so that each role's loop has
