@@ -39,10 +39,10 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "qwen3-0.6b-layer"): (175.53e6, "f214b727f9f78f81"),
-    ("attn_bwd", "qwen3-8b-layer"): (1163.66e6, "f214b727f9f78f81"),
-    ("attn_fwd", "qwen3-8b-layer"): (235.63e6, "da5103b717b3d371"),
-    ("decode", "serving-decode"): (1225.64e6, "2d62769d62840f58"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (175.17e6, "501e4d718d6f5841"),
+    ("attn_bwd", "qwen3-8b-layer"): (1144.19e6, "501e4d718d6f5841"),
+    ("attn_fwd", "qwen3-8b-layer"): (235.14e6, "858ff8b9b6457138"),
+    ("decode", "serving-decode"): (1225.64e6, "2e03429fb7f92a55"),
 }
 
 
