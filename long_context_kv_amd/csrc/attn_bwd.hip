@@ -1286,11 +1286,13 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   // units (a tile of u units into ceil(u / T) nearly equal pieces), T chosen
   // by a model of the dispatch: the grid's pieces, in order, are dealt to the
   // 8 XCDs in contiguous ranges (the kernel's block id remap), and each XCD
-  // starts its pieces in order on its first free workgroup slot (32 CUs x
-  // workgroups per CU). A piece costs its units plus a fixed overhead (key
-  // tile load, pipeline fill, result store; a partial store and the
-  // reduction when cut). The candidate with the smallest modelled finish
-  // time wins, the largest T among equals.
+  // starts its pieces in order on its first free workgroup slot (32 CUs, one
+  // dK/dV workgroup each). A piece costs its units plus a fixed overhead, in
+  // units, from measured per-workgroup timelines: ~7 uncut (operand rows,
+  // pipeline fill and drain, result store), ~12 cut (with its partial store)
+  // plus its share of the tile's reduction by the last piece (~10). The
+  // candidate with the smallest modelled finish time wins, the largest T
+  // among equals.
   {
     const long long t_max = std::max(U, tok_units(0));   // every tile one piece
     const int slots = 32;   // one dK/dV workgroup per CU
@@ -1317,7 +1319,8 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
         std::fill(slot.begin(), slot.end(), 0.0);
         for (size_t i = first; i < first + cnt; ++i) {
           std::pop_heap(slot.begin(), slot.end(), std::greater<double>());
-          slot.back() += (double)pieces[i].first + (pieces[i].second > 1 ? 2.5 : 1.5);
+          slot.back() += (double)pieces[i].first +
+                         (pieces[i].second > 1 ? 12.0 + 10.0 / (double)pieces[i].second : 7.0);
           std::push_heap(slot.begin(), slot.end(), std::greater<double>());
         }
         worst = std::max(worst, *std::max_element(slot.begin(), slot.end()));
