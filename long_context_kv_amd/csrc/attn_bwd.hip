@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const int hl = lane >> 5;
 
   // ---- work item: a piece of one key tile's unit list (pieces of cartridge
-  // tiles first, then per batch the pieces of the token tiles)
+  // tiles first, then the pieces of the token tiles, tile-major)
   const int per_kv = a.n_ct * a.splits_c + a.B * a.kv_ptok;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int kv = lg / per_kv;
@@ -480,19 +480,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     u_begin = (int)((long long)split * U / a.splits_c);
     u_end = (int)((long long)(split + 1) * U / a.splits_c);
   } else {
+    // token pieces tile-major (the larger tiles, nearer the start, first),
+    // then by batch, then by piece
     r0 -= a.n_ct * a.splits_c;
-    b = r0 / a.kv_ptok;
-    r0 %= a.kv_ptok;
     tile = 0;
     int ut = a.g * a.nqt;
     n_split = (ut + a.kv_target - 1) / a.kv_target;
-    while (r0 >= n_split) {
-      r0 -= n_split;
+    while (r0 >= a.B * n_split) {
+      r0 -= a.B * n_split;
       ++tile;
       ut = a.g * (a.nqt - tile * (kBNB / kBQ));
       n_split = (ut + a.kv_target - 1) / a.kv_target;
     }
-    split = r0;
+    b = r0 / n_split;
+    split = r0 % n_split;
     u_begin = (int)((long long)split * ut / n_split);
     u_end = (int)((long long)(split + 1) * ut / n_split);
   }
@@ -1307,8 +1308,8 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
         const long long ns = (U + T - 1) / T;
         for (long long i = 0; i < ns; ++i)
           for (int c = 0; c < pl.n_ct; ++c) pieces.emplace_back((i + 1) * U / ns - i * U / ns, ns);
-        for (int b = 0; b < d.B; ++b)
-          for (int t = 0; t < pl.n_tt; ++t) tile(tok_units(t));
+        for (int t = 0; t < pl.n_tt; ++t)
+          for (int b = 0; b < d.B; ++b) tile(tok_units(t));
       }
       const size_t G = pieces.size(), q = G / 8, r = G % 8;
       double worst = 0.0;
