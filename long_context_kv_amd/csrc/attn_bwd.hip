@@ -951,7 +951,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
@@ -1054,19 +1054,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     // key k = 32 kh + d_row(r, hl) is visible iff
     // k < lim (its row exists and, for a token tile, it is not after the
     // query).
-    const bool need_mask = f.rows < kKvTile || (!f.cart && f.j0 + kKvTile - 1 > i0);
-    const int lim = f.cart ? f.rows : min(f.rows, my_i - f.j0 + 1);
-    const int lim_l = lim - 4 * hl;
+    // (one branch for the whole tile: tiles that need no mask skip it)
+    if (f.rows < kKvTile || (!f.cart && f.j0 + kKvTile - 1 > i0)) {
+      const int lim = f.cart ? f.rows : min(f.rows, my_i - f.j0 + 1);
+      const int lim_l = lim - 4 * hl;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kc = 32 * kh + (r & 3) + 8 * (r >> 2);   // key minus 4 hl
+          s[kh][r] = kc < lim_l ? s[kh][r] : -INFINITY;
+        }
+    }
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float arg = fmaf(s[kh][r], c, -lse2);
-        if (need_mask) {
-          const int kc = 32 * kh + (r & 3) + 8 * (r >> 2);   // key minus 4 hl
-          arg = kc < lim_l ? arg : -INFINITY;
-        }
-        const float p_ = __builtin_amdgcn_exp2f(arg);
+        const float p_ = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c, -lse2));
         dp[kh][r] = p_ * (dp[kh][r] + dl);
       }
     // dQ^T += K^T dS^T in four steps j = (kh, m): K^T fragments by transpose
