@@ -10,22 +10,20 @@
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
 //
 // Design (gfx950):
-//  * preprocess: D_i and zeroing of the f32 dQ accumulator in one pass;
-//  * main kernel, one workgroup per 128-key tile (4 waves x 32 keys). A wave
-//    keeps its K and V rows as MFMA B operands in registers and its f32 dK,
-//    dV accumulators in registers for the whole loop, so the cartridge rows'
-//    gradients are summed over batch and GQA group without atomics;
-//  * the loop runs over (batch, q-head of the group, 32-query tile) units;
-//    Q and dO tiles are staged in LDS row-major and transposed, so both
-//    contractions over queries (dV += P^T dO, dK += dS^T Q) take P and dS
-//    straight from the MFMA result registers as A operands;
-//  * dS goes through LDS once per unit for dQ = dS K (K^T is staged in LDS
-//    once per workgroup); dQ is accumulated in f32 with global atomics;
-//  * cartridge tiles see every query of every sequence, token tiles only the
-//    later ones: cartridge tiles may be split over units (partial f32 sums
-//    reduced by a small kernel) to balance the grid;
-//  * block ids are remapped so one kv head's tiles share an XCD and its L2
-//    (where its dQ accumulator lines are hit by every tile).
+//  * preprocess: -D_i, lse_i log2(e) and (float32 mode) zeroing of the f32 dQ
+//    accumulator in one pass;
+//  * float32 reference mode, one generic kernel: a workgroup per 128-key
+//    tile (4 waves x 32 keys) keeps its K, V rows as MFMA operands and its
+//    f32 dK, dV in registers over a loop of (batch, q-head of the group,
+//    32-query tile) units, Q and dO staged in LDS; dS goes through LDS once
+//    per unit for dQ = dS K, accumulated in f32 with global atomics;
+//    cartridge tiles may be split over units (partial sums reduced by a
+//    small kernel) to balance the grid;
+//  * bf16 path: a dK/dV kernel (two wave roles per key group, pieces of a
+//    tile summed by the tile's last piece) and a query-major dQ kernel that
+//    recomputes S and dP, described below; the only atomics are one counter
+//    per piece;
+//  * block ids are remapped so one kv head's tiles share an XCD and its L2.
 #include <math.h>
 
 #include <algorithm>
@@ -398,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path: two kernels, neither with atomics.
+// bf16 path: two kernels.
 //
 // attn_bwd_kv_kernel -- dK and dV. One workgroup (8 waves) per piece of a
 //   128-key tile's list of (batch, q-head, 32-query) units. Waves k and k+4
@@ -416,14 +414,6 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 //   dQ^T += K^T dS^T in registers (K^T by transpose reads, dS^T straight from
 //   the MFMA result layout). dQ is written once, in the token dtype.
 // Cartridge rows arrive as bf16 (f32 master rows are cast first).
-
-// True when no pair of this unit needs a mask for the key side: every key
-// of the workgroup tile exists and (for a token tile) every key precedes
-// every query of the unit.
-__device__ __forceinline__ bool key_ok_all(bool cart, int j0, int i0, int limit) {
-  const bool all_exist = j0 + kBNB <= limit;
-  return all_exist && (cart || j0 + kBNB - 1 <= i0);
-}
 
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
