@@ -39,9 +39,9 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "qwen3-0.6b-layer"): (175.17e6, "501e4d718d6f5841"),
-    ("attn_bwd", "qwen3-8b-layer"): (1144.19e6, "501e4d718d6f5841"),
-    ("attn_fwd", "qwen3-8b-layer"): (235.14e6, "858ff8b9b6457138"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (42.53e6, "f3bb293819a794d0"),
+    ("attn_bwd", "qwen3-8b-layer"): (998.61e6, "f3bb293819a794d0"),
+    ("attn_fwd", "qwen3-8b-layer"): (234.3e6, "ab31a56ae011eddb"),
     ("decode", "serving-decode"): (1225.64e6, "2e03429fb7f92a55"),
 }
 
