@@ -40,6 +40,8 @@ namespace cartattn {
 
 namespace {
 
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
+
 constexpr int kBNB = 128;      // keys per workgroup tile
 constexpr int kBQ = 32;        // queries per unit
 constexpr int kThreads = 256;
@@ -858,29 +860,33 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     return;
   }
   // Partial sums are exchanged at device scope without cache maintenance:
-  // stored write-through past the XCD's L2 (device-scope atomic stores),
-  // and read back around it (device-scope loads through buffer descriptors
-  // over this tile's rows of each piece's region; rows past the end fall
-  // outside and read as zero). A plain device-scope fence here would write
-  // back and invalidate the whole L2 of the XCD for every piece. (The
-  // stores are not buffer stores: a buffer store of a bit-cast accumulator
-  // element was compiled to store element 0 of its vector for every row.)
-  const size_t pstride = cart ? (size_t)a.p * row_stride : (size_t)a.B * a.n * row_stride;
-  const size_t pbase = cart ? 0 : (size_t)b * a.n * row_stride;
-  const uint32_t pbytes = (uint32_t)((size_t)limit * row_stride * 4);
+  // each wave stores its accumulator registers lane-major (16-byte words,
+  // 1 KiB per instruction) write-through past the XCD's L2 (device-scope
+  // buffer stores), and the last piece reads them back around its L2
+  // (device-scope buffer loads). A plain device-scope fence here would write
+  // back and invalidate the whole L2 of the XCD for every piece.
+  constexpr int NQ = 4 * NDB;                        // 16-byte words per lane
+  const size_t region = (size_t)NQ * 1024;          // bytes per wave and piece
+  const int tile_id = cart ? kv * a.n_ct + tile : (kv * a.B + b) * a.n_tt + tile;
+  const int n_tiles = cart ? a.Hkv * a.n_ct : a.Hkv * a.B * a.n_tt;
   float* const part = grole ? (cart ? a.dk_part : a.dk_tpart) : (cart ? a.dv_part : a.dv_tpart);
-  const uint32_t lane_off = (uint32_t)((((size_t)(j0 + 32 * pair + 4 * hl)) * a.Hkv + kv) * D + l32) * 4;
-  const uint32_t row4 = (uint32_t)row_stride * 4;
-  auto roff = [&](int r) { return lane_off + (uint32_t)((r & 3) + 8 * (r >> 2)) * row4; };
+  auto piece_rsrc = [&](int i) {
+    const char* base = reinterpret_cast<const char*>(part) +
+                       (((size_t)i * n_tiles + tile_id) * 4 + pair) * region;
+    return make_rsrc(base, (uint32_t)region);
+  };
+  {
+    const buf_rsrc rp = piece_rsrc(split);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int j = j0 + 32 * pair + d_row(r, hl);
-    if (j >= limit) continue;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const size_t o = (size_t)split * pstride + out_off(j, 32 * db + l32);
-      __hip_atomic_store(part + o, acc[db][r] * oscale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+      for (int cc = 0; cc < 4; ++cc) {
+        const f32x4 v = {acc[db][4 * cc] * oscale, acc[db][4 * cc + 1] * oscale,
+                         acc[db][4 * cc + 2] * oscale, acc[db][4 * cc + 3] * oscale};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, v), rp,
+                                               (uint32_t)((db * 4 + cc) * 1024 + lane * 16), 0,
+                                               kCpolDevice);
+      }
   }
   // every store of the workgroup complete, then count this piece in
   __shared__ int last_piece;
@@ -893,37 +899,46 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (!last_piece) return;
-  // piece-major, so that each pass issues a piece's loads of RPASS result
-  // registers at once (32 loads)
-  constexpr int RPASS = D == 128 ? 8 : 16;
+  // The last piece adds the pieces in piece order (the same sum whichever
+  // piece is last), its own from registers, the others' words HQ at a time
+  // (two passes: the sums, the loads and the accumulator fit the registers).
+  constexpr int HQ = NQ / 2;
 #pragma unroll
-  for (int r0 = 0; r0 < 16; r0 += RPASS) {
-    float sg[RPASS][NDB];
+  for (int h = 0; h < 2; ++h) {
+    f32x4 sg[HQ];
 #pragma unroll
-    for (int r = 0; r < RPASS; ++r)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) sg[r][db] = 0.f;
+    for (int q = 0; q < HQ; ++q) sg[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < n_split; ++i) {
-      const buf_rsrc rp = make_rsrc(part + (size_t)i * pstride + pbase, pbytes);
-      uint32_t tg[RPASS][NDB];
+      if (i == split) {
 #pragma unroll
-      for (int r = 0; r < RPASS; ++r)
+        for (int q = 0; q < HQ; ++q) {
+          const int w = h * HQ + q, db = w / 4, cc = w % 4;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          tg[r][db] = __builtin_amdgcn_raw_buffer_load_b32(rp, roff(r0 + r) + 128 * db, 0, kCpolDevice);
+          for (int e = 0; e < 4; ++e) sg[q][e] += acc[db][4 * cc + e] * oscale;
+        }
+        continue;
+      }
+      const buf_rsrc rp = piece_rsrc(i);
+      v4u32 t[HQ];
+#pragma unroll
+      for (int q = 0; q < HQ; ++q)
+        t[q] = __builtin_amdgcn_raw_buffer_load_b128(rp, (uint32_t)((h * HQ + q) * 1024 + lane * 16), 0,
+                                                     kCpolDevice);
       // all of the pass's loads in flight before the first add
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < RPASS; ++r)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) sg[r][db] += __builtin_bit_cast(float, tg[r][db]);
+      for (int q = 0; q < HQ; ++q) sg[q] += __builtin_bit_cast(f32x4, t[q]);
     }
+    // words h HQ .. : db = w / 4, registers 4 (w % 4) .. of the accumulator
 #pragma unroll
-    for (int r = 0; r < RPASS; ++r) {
-      const int j = j0 + 32 * pair + d_row(r0 + r, hl);
-      if (j >= limit) continue;
+    for (int q = 0; q < HQ; ++q) {
+      const int w = h * HQ + q, db = w / 4, cc = w % 4;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) write(j, 32 * db + l32, sg[r][db]);
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * cc + e;
+        const int j = j0 + 32 * pair + d_row(r, hl);
+        if (j < limit) write(j, 32 * db + l32, sg[q][e]);
+      }
     }
   }
 }
@@ -1339,7 +1354,8 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
     pl.kv_stmax = pl.n_tt > 0 ? (int)((tok_units(0) + T - 1) / T) : 1;
     pl.grid_kv = d.Hkv * (pl.n_ct * pl.kv_splits_c + d.B * ptok);
     if (d.tok_bf16 && pl.kv_stmax > 1)
-      pl.tok_part_bytes = (size_t)pl.kv_stmax * d.B * d.n * d.Hkv * d.D * sizeof(float);
+      pl.tok_part_bytes =
+          (size_t)pl.kv_stmax * d.B * pl.n_tt * kBNB * d.Hkv * d.D * sizeof(float);
     if (d.tok_bf16) pl.cnt_bytes = (size_t)d.Hkv * (pl.n_ct + d.B * pl.n_tt) * sizeof(int);
   }
   pl.dq_bytes = d.tok_bf16 ? 0 : (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
@@ -1359,7 +1375,9 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   }
   pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);   // and as much for lse2
   const int sc = d.tok_bf16 ? pl.kv_splits_c : s;
-  pl.part_bytes = sc > 1 ? (size_t)sc * d.p * d.Hkv * d.D * sizeof(float) : 0;
+  // (bf16: whole 128-key tiles of lane-major words; float32: rows)
+  pl.part_bytes =
+      sc > 1 ? (size_t)sc * (d.tok_bf16 ? pl.n_ct * kBNB : d.p) * d.Hkv * d.D * sizeof(float) : 0;
   if (d.tok_bf16 && !d.row_bf16 && d.p > 0)
     pl.shadow_bytes = 2 * (size_t)d.p * d.Hkv * d.D * sizeof(uint16_t);
   return pl;
