@@ -71,6 +71,12 @@ struct BwdArgs {
   float* dq_part;     // [q_splits][B][n][Hq][D], dQ key-split pieces (bf16 path)
   int* kv_cnt;        // [Hkv][n_ct + B n_tt] finished pieces per key tile (bf16 path)
   int n_cnt;
+  // f32 cartridge rows rounded to the bf16 shadow by the preprocess (bf16 path)
+  const f32x4* cast_k;
+  const f32x4* cast_v;
+  bf16x4* cast_kb;
+  bf16x4* cast_vb;
+  size_t cast_n4;
   int kv_target, kv_ptok, kv_stmax, q_splits;
   int D4;             // head_dim / 4
   int B, n, p, f, Hq, Hkv, g;
@@ -1167,6 +1173,7 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
   if (e >= n4) return;
   const float4* pp = reinterpret_cast<const float4*>(a.dq_part);
   float4 t = pp[e];
+#pragma unroll 4
   for (int s = 1; s < a.q_splits; ++s) {
     const float4 u = pp[(size_t)s * n4 + e];
     t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
@@ -1196,6 +1203,14 @@ __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
   for (int e = 0; e < EPL; ++e) acc += to_f32(o[e]) * to_f32(g[e]);
   acc = row_sum<16>(acc);
   for (int c = blockIdx.x * 256 + threadIdx.x; c < a.n_cnt; c += gridDim.x * 256) a.kv_cnt[c] = 0;
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < a.cast_n4; c += (size_t)gridDim.x * 256) {
+    const f32x4 x = a.cast_k[c], y = a.cast_v[c];
+    bf16x4 xb, yb;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { xb[e] = (bf16)x[e]; yb[e] = (bf16)y[e]; }
+    a.cast_kb[c] = xb;
+    a.cast_vb[c] = yb;
+  }
   if (!ok) return;
   if (sub == 0) {
     const int h = row % a.Hq;
@@ -1443,12 +1458,16 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   BwdArgs a{};
   char* w = reinterpret_cast<char*>(ws);
   if (pl.shadow_bytes) {
+    // the preprocess kernel (bf16 path, which is the only one with a shadow)
+    // rounds the rows before the kernels that read them
     const size_t n = (size_t)d.p * d.Hkv * d.D;
     bf16* kb = reinterpret_cast<bf16*>(w);
     bf16* vb = kb + n;
-    hipError_t e = launch_rows_to_bf16(reinterpret_cast<const float*>(k_cart),
-                                       reinterpret_cast<const float*>(v_cart), kb, vb, n, st);
-    if (e != hipSuccess) return e;
+    a.cast_k = reinterpret_cast<const f32x4*>(k_cart);
+    a.cast_v = reinterpret_cast<const f32x4*>(v_cart);
+    a.cast_kb = reinterpret_cast<bf16x4*>(kb);
+    a.cast_vb = reinterpret_cast<bf16x4*>(vb);
+    a.cast_n4 = n / 4;
     k_cart = kb;
     v_cart = vb;
     w += align256(pl.shadow_bytes);

@@ -552,12 +552,14 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(FwdArgs a) {
   const size_t lstride = (size_t)a.B * a.Hq * a.n;
   const size_t ostride = (size_t)a.B * a.n * a.Hq * D;
   float mx = -INFINITY;
+#pragma unroll 4
   for (int s = 0; s < a.n_splits; ++s) mx = fmaxf(mx, a.lse_part[s * lstride + lrow]);
   float tot = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
   const float* op = a.o_part + (size_t)row * D + sub * EPL;
+#pragma unroll 4
   for (int s = 0; s < a.n_splits; ++s) {
     const float ls = a.lse_part[s * lstride + lrow];
     const float w = (ls == -INFINITY) ? 0.f : expf(ls - mx);

@@ -12,9 +12,9 @@
 // float angle would be off by ~1e-3 rad), and the cosine and sine of the
 // reduced angle (|r| <= pi) are f32. The rotation itself is f32 and the result
 // is rounded to the tensor's dtype. The kernel is HBM-bound: one workgroup per
-// token; its first d/2 lanes put the token's cos/sin table in LDS, then every
-// lane rotates 4 consecutive pairs of one head row per pass (8- or 16-byte
-// loads of each row half).
+// token; every lane loads 4 consecutive pairs of one head row per pass (8- or
+// 16-byte loads of each row half), the first pass before the token's first d/2
+// lanes put its cos/sin table in LDS.
 #include <math.h>
 
 #include "common.hpp"
@@ -46,6 +46,23 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
   const int tok = blockIdx.x;        // b * S + i
   const int b = tok / S;
   const int i = tok % S;
+  const int k4 = 4 * (threadIdx.x % TPR);
+  const int hsub = threadIdx.x / TPR;
+  T* qr = q + (size_t)tok * Hq * D;
+  T* kr = k ? k + (size_t)tok * Hkv * D : nullptr;
+  // the first pass's rows are loaded before the table is built, so their
+  // latency overlaps the angle reduction
+  const bool q0 = hsub < Hq;
+  const bool k0 = kr && hsub < Hkv;
+  V4 qlo{}, qhi{}, klo{}, khi{};
+  if (q0) {
+    qlo = *reinterpret_cast<const V4*>(qr + (size_t)hsub * D + k4);
+    qhi = *reinterpret_cast<const V4*>(qr + (size_t)hsub * D + HALF + k4);
+  }
+  if (k0) {
+    klo = *reinterpret_cast<const V4*>(kr + (size_t)hsub * D + k4);
+    khi = *reinterpret_cast<const V4*>(kr + (size_t)hsub * D + HALF + k4);
+  }
   if (threadIdx.x < HALF) {
     const long long pos = (long long)pos_base + (pos_offsets ? pos_offsets[b] : 0) + i;
     const double ang = (double)pos * fr.inv_freq[threadIdx.x];
@@ -57,14 +74,10 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
     sn[threadIdx.x] = sf * sign;
   }
   __syncthreads();
-  const int k4 = 4 * (threadIdx.x % TPR);
-  const int hsub = threadIdx.x / TPR;
   float c[4], s_[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) { c[e] = cs[k4 + e]; s_[e] = sn[k4 + e]; }
-  auto rot = [&](T* x) {
-    V4 lo = *reinterpret_cast<const V4*>(x + k4);
-    V4 hi = *reinterpret_cast<const V4*>(x + HALF + k4);
+  auto rot_store = [&](T* x, const V4& lo, const V4& hi) {
     V4 ol, oh;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -75,12 +88,14 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
     *reinterpret_cast<V4*>(x + k4) = ol;
     *reinterpret_cast<V4*>(x + HALF + k4) = oh;
   };
-  T* qr = q + (size_t)tok * Hq * D;
-  for (int h = hsub; h < Hq; h += RPP) rot(qr + (size_t)h * D);
-  if (k) {
-    T* kr = k + (size_t)tok * Hkv * D;
-    for (int h = hsub; h < Hkv; h += RPP) rot(kr + (size_t)h * D);
-  }
+  auto rot = [&](T* x) {
+    rot_store(x, *reinterpret_cast<const V4*>(x + k4), *reinterpret_cast<const V4*>(x + HALF + k4));
+  };
+  if (q0) rot_store(qr + (size_t)hsub * D, qlo, qhi);
+  if (k0) rot_store(kr + (size_t)hsub * D, klo, khi);
+  for (int h = hsub + RPP; h < Hq; h += RPP) rot(qr + (size_t)h * D);
+  if (kr)
+    for (int h = hsub + RPP; h < Hkv; h += RPP) rot(kr + (size_t)h * D);
 }
 
 template <typename T, int D>
