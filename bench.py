@@ -39,10 +39,10 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "qwen3-0.6b-layer"): (42.53e6, "f3bb293819a794d0"),
-    ("attn_bwd", "qwen3-8b-layer"): (998.61e6, "f3bb293819a794d0"),
-    ("attn_fwd", "qwen3-8b-layer"): (234.3e6, "ab31a56ae011eddb"),
-    ("decode", "serving-decode"): (1225.64e6, "2e03429fb7f92a55"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (42.5e6, "5711f9f84dd4c322"),
+    ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "5711f9f84dd4c322"),
+    ("attn_fwd", "qwen3-8b-layer"): (234.4e6, "85adaaf3fdb779c3"),
+    ("decode", "serving-decode"): (1225.6e6, "2e03429fb7f92a55"),
 }
 
 
