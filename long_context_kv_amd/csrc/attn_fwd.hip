@@ -318,35 +318,52 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
   f32x16 s[2];
   {
     const uint32_t kb = kst + TL::off(l32, 8 * hl);
-    bf16x8 kfr[2][2];
-    auto rd = [&](auto KS, int slot) {
+    bf16x8 kfr[3][2];
+    auto rd = [&](auto KS) {
       constexpr int ks = decltype(KS)::value;
-      kfr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
-      kfr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(kb));
+      kfr[ks % 3][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
+      kfr[ks % 3][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(kb));
     };
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; }
-    rd(std::integral_constant<int, 0>{}, 0);
+    rd(std::integral_constant<int, 0>{});
+    rd(std::integral_constant<int, 1>{});
     // MFMA phases run at a raised wave priority, so that the other wave of
     // the SIMD fills the VALU slots with its softmax meanwhile
     __builtin_amdgcn_s_setprio(1);
     static_for<NKS>([&](auto KS) {
       constexpr int ks = decltype(KS)::value;
-      if constexpr (ks + 1 < NKS) {
-        rd(std::integral_constant<int, ks + 1>{}, (ks + 1) & 1);
+      if constexpr (ks + 2 < NKS) {
+        rd(std::integral_constant<int, ks + 2>{});
+        lds_wait<4>();
+      } else if constexpr (ks + 1 < NKS) {
         lds_wait<2>();
       } else {
         lds_wait<0>();
       }
-      lds_tie(kfr[ks & 1][0]);
-      lds_tie(kfr[ks & 1][1]);
+      lds_tie(kfr[ks % 3][0]);
+      lds_tie(kfr[ks % 3][1]);
       __builtin_amdgcn_sched_barrier(0);
-      s[0] = M::mma(kfr[ks & 1][0], qf[ks], s[0]);
-      s[1] = M::mma(kfr[ks & 1][1], qf[ks], s[1]);
+      s[0] = M::mma(kfr[ks % 3][0], qf[ks], s[0]);
+      s[1] = M::mma(kfr[ks % 3][1], qf[ks], s[1]);
       __builtin_amdgcn_sched_barrier(0);
     });
   }
   __builtin_amdgcn_s_setprio(0);
+  // V^T fragments for O^T += V^T P^T, by transpose reads of rows 32 kh + 16 m
+  // .. for step j = (kh, m); the first step's reads are issued here, so that
+  // they land while the softmax runs.
+  const uint32_t vb = vst + TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  bf16x8 va[2][NDB];
+  auto rdv = [&](auto J, int slot) {
+    constexpr int j = decltype(J)::value;
+    static_for<NDB>([&](auto DB) {
+      constexpr int db = decltype(DB)::value;
+      constexpr int off = TL::rows(16 * j) + 2 * 32 * db;
+      va[slot][db] = cat8(lds_tr4<off>(vb), lds_tr4<off + TL::rows(8)>(vb));
+    });
+  };
+  rdv(std::integral_constant<int, 0>{}, 0);
   // Mask: key k = 32 kh + d_row(r, hl) of the tile is visible iff k < lim
   // (its row exists and, for a token tile, it is not after the query).
   if (f.rows < kBN || (!f.cart && f.j0 + kBN - 1 > i0)) {
@@ -388,20 +405,9 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
       ls += pv_;
     }
   l_run += ls;
-  // O^T += V^T P^T in four steps j = (kh, m): V^T fragments by transpose
-  // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
+  // O^T += V^T P^T in four steps j = (kh, m), each step's V^T reads (8 per
+  // step) issued one step ahead.
   {
-    const uint32_t vb = vst + TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-    bf16x8 va[2][NDB];
-    auto rdv = [&](auto J, int slot) {
-      constexpr int j = decltype(J)::value;
-      static_for<NDB>([&](auto DB) {
-        constexpr int db = decltype(DB)::value;
-        constexpr int off = TL::rows(16 * j) + 2 * 32 * db;
-        va[slot][db] = cat8(lds_tr4<off>(vb), lds_tr4<off + TL::rows(8)>(vb));
-      });
-    };
-    rdv(std::integral_constant<int, 0>{}, 0);
     __builtin_amdgcn_s_setprio(1);
     static_for<4>([&](auto J) {
       constexpr int j = decltype(J)::value;

@@ -152,11 +152,24 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// Combine lane l with lane l ^ 32 by gfx950's v_permlane32_swap (a VALU
+// lane swap; a shuffle would go through LDS and wait for it). Both lanes get
+// the lower-half value first and the upper-half value second, so their
+// results are bit-identical. Written as inline assembly with both registers
+// as outputs (the compiler builtin's second result was dropped in codegen),
+// with wait states around it for the VALU hazards.
+__device__ __forceinline__ float2 halves_pair(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return make_float2(a, b);
+}
 __device__ __forceinline__ float wave_max_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const float2 p = halves_pair(x);
+  return fmaxf(p.x, p.y);
 }
 __device__ __forceinline__ float wave_sum_halves(float x) {
-  return x + __shfl_xor(x, 32);
+  const float2 p = halves_pair(x);
+  return p.x + p.y;
 }
 
 }  // namespace cartattn
