@@ -1375,11 +1375,15 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   }
   pl.dq_bytes = d.tok_bf16 ? 0 : (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
   {
-    // the dQ kernel uses the forward's query blocks, its key tiles split
-    // like the forward's while the grid is small
-    const FwdPlan fp = plan_fwd(d);
-    pl.hpw = fp.hpw; pl.wph = fp.wph; pl.n_hg = fp.n_hg; pl.n_qb = fp.n_qb;
-    const long long base = (long long)d.Hkv * d.B * fp.n_hg * fp.n_qb;
+    // dQ workgroups of 4 waves x 32 query rows, the q-heads of a GQA group
+    // packed as extra rows (up to 4 per workgroup); key tiles split while
+    // the grid is small
+    const int g = d.Hq / d.Hkv;
+    pl.hpw = (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1);
+    pl.wph = 4 / pl.hpw;
+    pl.n_hg = g / pl.hpw;
+    pl.n_qb = (d.n + 32 * pl.wph - 1) / (32 * pl.wph);
+    const long long base = (long long)d.Hkv * d.B * pl.n_hg * pl.n_qb;
     const int min_tiles = (d.p + kKvTile - 1) / kKvTile + 1;
     int qs = 1;
     if (d.tok_bf16)
