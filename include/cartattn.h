@@ -230,7 +230,8 @@ size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
 /* ------------------------------------------------------------------------
  * Launch timing (profiling aid). When enabled, every kernel launch of this
  * library is bracketed by two HIP events on its own stream. Kernel names:
- * "rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess",
+ * "rope", "rows_to_bf16" (the forward's bf16 shadow of f32 cartridge rows;
+ * the backward's is made by "bwd_preprocess"), "attn_fwd", "attn_fwd_combine", "bwd_preprocess",
  * "attn_bwd" (dK/dV, including the reduction of key tiles cut into pieces,
  * for bf16 tokens), "attn_bwd_dq" (dQ of bf16 tokens), "bwd_dq_combine",
  * "bwd_dq_finalize" (dQ of f32 tokens), "bwd_cart_reduce" (f32 tokens),

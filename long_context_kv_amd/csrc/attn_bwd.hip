@@ -11,7 +11,8 @@
 //
 // Design (gfx950):
 //  * preprocess: -D_i, lse_i log2(e) and (float32 mode) zeroing of the f32 dQ
-//    accumulator in one pass;
+//    accumulator in one pass; with bf16 tokens it also rounds the f32
+//    cartridge rows to their bf16 shadow;
 //  * float32 reference mode, one generic kernel: a workgroup per 128-key
 //    tile (4 waves x 32 keys) keeps its K, V rows as MFMA operands and its
 //    f32 dK, dV in registers over a loop of (batch, q-head of the group,
@@ -1185,7 +1186,8 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
 
 // -D_i = -(dO_i . O_i) (stored negated: G = P dP + P (-D) is one multiply
 // and one FMA) and lse_i * log2(e) for every (b, h, i), (f32 tokens) dQ
-// accumulator := 0, and (bf16) the key tiles' piece counters := 0. Sixteen
+// accumulator := 0, and (bf16) the key tiles' piece counters := 0 and the
+// bf16 shadow of f32 cartridge rows (grid-stride, 4 elements a thread). Sixteen
 // lanes per row (D/16 elements each), 16 rows per workgroup; the row sum is
 // taken with DPP adds.
 template <typename T, int D>
