@@ -14,7 +14,9 @@
 // to a physical page id.
 //
 // Decode is HBM-bound (4 flop per byte of K/V), so it uses no MFMA: one
-// workgroup per (sequence, kv head, split of the pages). The q-heads of the
+// workgroup per (sequence, kv head, split of the pages); a sequence's pages
+// are cut into ns = ceil(pages / pages-per-split) nearly equal splits, so
+// the workgroups of a step run about equally long. The q-heads of the
 // GQA group share every K/V byte read. Each thread owns one 8-element chunk
 // of one row per pass and keeps a private online-softmax state per q-head;
 // the states are merged with cross-lane shuffles and through LDS at the end,
@@ -121,9 +123,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   const int kv = (lg / nb) % a.c.Hkv;
   const int s = lg / (nb * a.c.Hkv);
   const int len = a.c.seq_lens[s];
-  const int row_begin = split * a.pps * kPage;
-  // clamp to the block table's capacity so a bad device length cannot read past it
-  const int row_end = min(min(len, row_begin + a.pps * kPage), a.c.max_pages * kPage);
+  // the sequence's pages in ns nearly equal splits (ns as the merge counts them)
+  const int len_c = min(len, a.c.max_pages * kPage);
+  const int pages = (len_c + kPage - 1) / kPage;
+  const int ns = min(nb, (pages + a.pps - 1) / a.pps);
+  const int pb = split < ns ? (int)((long long)split * pages / ns) : pages;
+  const int pe = split < ns ? (int)((long long)(split + 1) * pages / ns) : pages;
+  const int row_begin = pb * kPage;
+  const int row_end = min(len_c, pe * kPage);
 
   // q chunks stay bf16: scores are bf16 x bf16 dot products accumulated in
   // f32 (v_dot2), scaled afterwards.
