@@ -40,9 +40,9 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
     ("attn_bwd", "qwen3-0.6b-layer"): (42.5e6, "455b4aa28c09e419"),
-    ("attn_bwd", "qwen3-8b-layer"): (1012.6e6, "455b4aa28c09e419"),
-    ("attn_fwd", "qwen3-8b-layer"): (235.7e6, "af9090a87cee9e9a"),
-    ("decode", "serving-decode"): (1225.6e6, "214085abf220dbc9"),
+    ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "455b4aa28c09e419"),
+    ("attn_fwd", "qwen3-8b-layer"): (234.5e6, "af9090a87cee9e9a"),
+    ("decode", "serving-decode"): (1225.6e6, "181d9c2273e0b279"),
 }
 
 
