@@ -1,13 +1,23 @@
 """Benchmark of the cartridge-attention hot path on one MI355X.
 
-A step is one pass of the training hot path over one layer batch: RoPE on
-the real-token Q/K at positions p + i, the forward, the backward (into the
-token tensors and the f32 cartridge-row gradients, frozen row 0) and the
-RoPE adjoint on dQ and dK. The headline `value` is its algorithmic fwd+bwd
-TFLOP/s (visible pairs only: 4*d*V_pairs forward, 8*d*V_pairs backward;
-RoPE time is inside the step time). The serving half of the path -- writing
-the cartridge into a paged bf16 cache and decoding behind it -- is measured
-on the serving-decode workload and reported in `decode` (GB/s of K/V read).
+A step is one pass of the training hot path over every layer of the
+workload: per layer RoPE on the real-token Q/K at positions p + i and the
+forward, then per layer in reverse the backward (into the token tensors and
+the f32 cartridge-row gradients, frozen row 0) and the RoPE adjoint on dQ and
+dK. Each step starts from the seeded Q/K (a device copy of the seeded
+tensors into the buffers RoPE rotates in place). The headline `value` is the
+algorithmic fwd+bwd TFLOP/s of the long-cartridge workload (28 layers, the
+largest that fits one GPU; visible pairs only: 4*d*V_pairs forward,
+8*d*V_pairs backward; RoPE and the copies are inside the step time). The
+serving half of the path -- writing the cartridge into a paged bf16 cache and
+decoding behind it -- is measured on the serving-decode workload and reported
+in `decode` (GB/s of K/V read). The two single-layer training workloads are
+reported in `extra_workloads`.
+
+The timed loop records no event between kernels: per-kernel durations come
+from separate passes over the same steps (one with events around every
+launch for the breakdown, one with events around the dominant kernel's
+launches only for its roofline line).
 
 Inputs are seeded N(0, 1) tensors resident in HBM before timing starts.
 The CPU float64 oracle is timed beside it on a bounded sample (cpu_baseline).
@@ -88,6 +98,41 @@ TRAIN_KERNELS = ("rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_pr
                  "bwd_cart_reduce")
 
 
+def measure(C, step, steps, warmup, names, tag):
+    """Warm up; a breakdown pass with events on every launch; the timed loop
+    (no per-launch events); a pass with events on the dominant kernel only.
+    Returns (ms per step of the timed loop, per-kernel records, dominant)."""
+    import torch
+    _progress(f"{tag}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    C.timing_only(None)
+    C.timing_enable(True)
+    nb = min(steps, 5)
+    _events_ms(step, nb)
+    kern = {}
+    for name in names:
+        ms, cnt = C.timing_query(name)
+        if cnt:
+            kern[name] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms, per_step_ms=ms / nb,
+                              pass_="breakdown")
+    C.timing_enable(False)
+    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    _progress(f"{tag}: timing {steps} steps")
+    total_ms = _events_ms(step, steps)
+    _progress(f"{tag}: {total_ms / steps:.3f} ms/step; kernel pass ({dom})")
+    C.timing_only(dom)
+    C.timing_enable(True)
+    kp_ms = _events_ms(step, steps)
+    ms, cnt = C.timing_query(dom)
+    kern[dom] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms, per_step_ms=ms / steps,
+                     pass_="kernel", pass_step_ms=kp_ms / steps)
+    C.timing_enable(False)
+    C.timing_only(None)
+    return total_ms / steps, kern, dom
+
+
 def train_bench(C, W, shape, steps, warmup):
     import torch
     dev = torch.device("cuda")
@@ -97,13 +142,13 @@ def train_bench(C, W, shape, steps, warmup):
     for l in range(layers):
         x = W.train_inputs(shape, seed=shape.seed + l)
         g = {k: v.to(dev) for k, v in x.items()}
-        q, kt = g["q"], g["k_tok"]
-        B, n, Hq, d = q.shape
-        shp = C.attn_shape(q, kt, shape.p, shape.frozen_rows, 0.0, g["k_cart"].dtype)
-        st = dict(g=g, shp=shp,
-                  o=torch.empty_like(q),
+        q0, k0 = g["q"], g["k_tok"]
+        B, n, Hq, d = q0.shape
+        shp = C.attn_shape(q0, k0, shape.p, shape.frozen_rows, 0.0, g["k_cart"].dtype)
+        st = dict(g=g, q0=q0, k0=k0, q=torch.empty_like(q0), k=torch.empty_like(k0), shp=shp,
+                  o=torch.empty_like(q0),
                   lse=torch.empty(B, Hq, n, dtype=torch.float32, device=dev),
-                  dq=torch.empty_like(q), dkt=torch.empty_like(kt),
+                  dq=torch.empty_like(q0), dkt=torch.empty_like(k0),
                   dvt=torch.empty_like(g["v_tok"]),
                   dkc=torch.empty(g["k_cart"].shape, dtype=torch.float32, device=dev),
                   dvc=torch.empty(g["v_cart"].shape, dtype=torch.float32, device=dev),
@@ -114,49 +159,26 @@ def train_bench(C, W, shape, steps, warmup):
     p = shape.p
 
     def step():
-        # forward over every layer, then backward in reverse (training order)
+        # forward over every layer, then backward in reverse (training order);
+        # RoPE rotates in place, so each step first restores the seeded Q/K
         for s in L:
             g = s["g"]
-            C.cart_rope_tokens(g["q"], g["k_tok"], pos_base=p, theta=W.THETA)
-            C.cart_attn_fwd(s["shp"], g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"],
+            s["q"].copy_(s["q0"])
+            s["k"].copy_(s["k0"])
+            C.cart_rope_tokens(s["q"], s["k"], pos_base=p, theta=W.THETA)
+            C.cart_attn_fwd(s["shp"], s["q"], s["k"], g["v_tok"], g["k_cart"], g["v_cart"],
                             s["o"], s["lse"], s["wsf"])
         for s in reversed(L):
             g = s["g"]
-            C.cart_attn_bwd(s["shp"], g["q"], g["k_tok"], g["v_tok"], g["k_cart"],
+            C.cart_attn_bwd(s["shp"], s["q"], s["k"], g["v_tok"], g["k_cart"],
                             g["v_cart"], s["o"], s["lse"], g["dout"], s["dq"], s["dkt"],
                             s["dvt"], s["dkc"], s["dvc"], False, s["wsb"])
             C.cart_rope_tokens(s["dq"], s["dkt"], pos_base=p, theta=W.THETA, inverse=True)
 
-    _progress(f"{shape.name}: warmup {warmup}")
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    # breakdown pass (outside the timed region): every launch timed, which adds
-    # two event records per launch of host work
-    C.timing_only(None)
-    C.timing_enable(True)
-    nb = min(steps, 5)
-    _events_ms(step, nb)
-    kern = {}
-    for name in TRAIN_KERNELS:
-        ms, cnt = C.timing_query(name)
-        if cnt:
-            kern[name] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms, per_step_ms=ms / nb,
-                              pass_="breakdown")
-    C.timing_enable(False)
-    dom = max(kern, key=lambda k: kern[k]["total_ms"])
-    # timed region: events on the dominant kernel's launches only
-    _progress(f"{shape.name}: timing {steps} steps")
-    C.timing_only(dom)
-    C.timing_enable(True)
-    total_ms = _events_ms(step, steps)
-    ms, cnt = C.timing_query(dom)
-    kern[dom] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms, per_step_ms=ms / steps,
-                     pass_="timed")
-    C.timing_enable(False)
-    C.timing_only(None)
-    _progress(f"{shape.name}: {total_ms / steps:.3f} ms/step")
-    return total_ms / steps, kern, dom
+    out = measure(C, step, steps, warmup, TRAIN_KERNELS, shape.name)
+    del L
+    torch.cuda.empty_cache()
+    return out
 
 
 def decode_bench(C, W, shape, steps, warmup):
@@ -187,28 +209,11 @@ def decode_bench(C, W, shape, steps, warmup):
     def step():
         cache.decode(q, out, ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    # breakdown pass, then the timed region with events on the decode kernel only
-    C.timing_only(None)
-    C.timing_enable(True)
-    _events_ms(step, min(steps, 5))
-    kern = {}
-    ms, cnt = C.timing_query("decode_merge")
-    if cnt:
-        kern["decode_merge"] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms, pass_="breakdown")
-    C.timing_only("decode")
-    C.timing_enable(True)
-    total_ms = _events_ms(step, steps)
-    ms, cnt = C.timing_query("decode")
-    kern["decode"] = dict(avg_ms=ms / cnt, launches=cnt, total_ms=ms, pass_="timed")
-    C.timing_enable(False)
-    C.timing_only(None)
+    ms, kern, dom = measure(C, step, steps, warmup, ("decode", "decode_merge"), shape.name)
     kv_bytes = sum(lens) * Hkv * d * 2 * 2
     wr_bytes = S * shape.p * Hkv * d * 2 * (4 + 2)      # f32 read + bf16 write, K and V
     cache.close()
-    return dict(ms=total_ms / steps, kv_bytes=kv_bytes, lens=lens, kern=kern,
+    return dict(ms=ms, kv_bytes=kv_bytes, lens=lens, kern=kern, dom=dom,
                 write_ms=wr_ms, write_kernel_ms=ms_app, write_bytes=wr_bytes)
 
 
@@ -250,14 +255,61 @@ def cpu_baseline(W, shape):
                       f"{reps} rep(s) in {dt:.1f} s"}
 
 
+PER_LAUNCH_NOTE = ("per-launch HIP-event averages: the dominant kernel's from a pass over the "
+                   "same steps with events on its launches only (pass_step_ms: that pass's step "
+                   "time), the others from a breakdown pass with events around every launch; "
+                   "ms_per_step comes from a loop with no per-launch events")
+
+
+def train_record(W, shape, ms, kern, dom):
+    """Headline numbers of one training workload from its measurement."""
+    flop = shape.fwd_flop() + shape.bwd_flop()
+    value = flop / (ms * 1e-3) / 1e12
+    # algorithmic flop per launch (one layer): forward QK^T + PV; the
+    # backward's dP, dV, dK are charged to the key-major kernel and dQ to the
+    # query-major one (the recomputation of S, and of dP in the dQ kernel, is
+    # not counted)
+    d, vp = shape.head_dim, shape.visible_pairs
+    per_launch_flop = {"attn_fwd": 4.0 * d * vp, "attn_bwd": 6.0 * d * vp,
+                       "attn_bwd_dq": 2.0 * d * vp}
+    roof = None
+    if dom in per_launch_flop:
+        ach = per_launch_flop[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, shape.name),
+                "work_per_launch": f"{per_launch_flop[dom]:.4e} flop ({dom}: "
+                                   f"{int(per_launch_flop[dom] / (d * vp))}*d*V_pairs, "
+                                   f"V_pairs={vp})"}
+    kernels = {}
+    for k, v in kern.items():
+        e = {"avg_ms": round(v["avg_ms"], 5), "launches": v["launches"], "pass": v["pass_"]}
+        if "pass_step_ms" in v:
+            e["pass_step_ms"] = round(v["pass_step_ms"], 4)
+        if k in per_launch_flop:
+            t = per_launch_flop[k] / (v["avg_ms"] * 1e-3) / 1e12
+            e.update(tflops=round(t, 2), frac=round(t / PEAK_BF16_TFLOPS, 4))
+        kernels[k] = e
+    return value, roof, kernels
+
+
+def workload_name(shape):
+    return (f"{shape.name}: B={shape.batch} Hq={shape.n_q_heads} Hkv={shape.n_kv_heads} "
+            f"d={shape.head_dim} p={shape.p} n={shape.q_seq} layers={shape.layers}, "
+            f"rope+fwd+bwd+rope^T")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the single-layer training workloads reported beside the headline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -274,31 +326,9 @@ def main():
 
     shape = W.SHAPES[args.config]
     ms, kern, dom = train_bench(C, W, shape, args.steps, args.warmup)
-    flop = shape.fwd_flop() + shape.bwd_flop()
-    value = flop / (ms * 1e-3) / 1e12
-
-    # roofline of the dominant kernel (largest share of the step's time)
-    # algorithmic flop per launch: forward QK^T + PV; the backward's dP, dV, dK
-    # are charged to the key-major kernel and dQ to the query-major one (the
-    # recomputation of S, and of dP in the dQ kernel, is not counted)
-    per_launch_flop = {"attn_fwd": 4.0 * shape.head_dim * shape.visible_pairs,
-                       "attn_bwd": 6.0 * shape.head_dim * shape.visible_pairs,
-                       "attn_bwd_dq": 2.0 * shape.head_dim * shape.visible_pairs}
-    roof = None
-    if dom in per_launch_flop:
-        ach = per_launch_flop[dom] / (kern[dom]["avg_ms"] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom, shape.name)}
-    kernels = {}
-    for k, v in kern.items():
-        e = {"avg_ms": round(v["avg_ms"], 5), "launches": v["launches"], "pass": v["pass_"]}
-        if k in per_launch_flop:
-            t = per_launch_flop[k] / (v["avg_ms"] * 1e-3) / 1e12
-            e.update(tflops=round(t, 2), frac=round(t / PEAK_BF16_TFLOPS, 4))
-        kernels[k] = e
+    value, roof, kernels = train_record(W, shape, ms, kern, dom)
     attn_ms = sum(kern[k]["per_step_ms"] for k in kern if k != "rope")
+    flop = shape.fwd_flop() + shape.bwd_flop()
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -312,23 +342,33 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{shape.name}: B={shape.batch} Hq={shape.n_q_heads} "
-                               f"Hkv={shape.n_kv_heads} d={shape.head_dim} p={shape.p} "
-                               f"n={shape.q_seq} layers={shape.layers}, rope+fwd+bwd+rope^T",
+        "config": {"workload": workload_name(shape),
                    "batch": shape.batch, "q_seq": shape.q_seq, "p": shape.p,
                    "n_q_heads": shape.n_q_heads, "n_kv_heads": shape.n_kv_heads,
                    "head_dim": shape.head_dim, "layers": shape.layers,
                    "frozen_rows": shape.frozen_rows, "parallelism": "none (1 GPU)"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "attn_only_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 2),
+        "fa_convention_tflops": round((14.0 / 12.0) * value, 2),
         "roofline": roof,
         "kernels": kernels,
-        "kernels_note": "per-launch HIP-event averages; the dominant kernel's from the timed region "
-                        "(events on its launches only), the others from an untimed breakdown pass "
-                        "that records events around every launch",
+        "kernels_note": PER_LAUNCH_NOTE,
     }
+    if not args.no_extra:
+        extra = {}
+        for cfg in (2, 3):
+            if cfg == args.config:
+                continue
+            sh = W.SHAPES[cfg]
+            e_ms, e_kern, e_dom = train_bench(C, W, sh, args.steps, args.warmup)
+            e_val, e_roof, e_kernels = train_record(W, sh, e_ms, e_kern, e_dom)
+            extra[sh.name] = {"workload": workload_name(sh), "value": round(e_val, 2),
+                              "unit": "TFLOP/s", "ms_per_step": round(e_ms, 4),
+                              "frac_of_peak": round(e_val / PEAK_BF16_TFLOPS, 4),
+                              "roofline": e_roof, "kernels": e_kernels}
+        result["extra_workloads"] = extra
     if not args.no_decode:
-        dec = decode_bench(C, W, W.DECODE, args.steps, args.warmup)
+        dec = decode_bench(C, W, W.DECODE, max(args.steps, 20), args.warmup)
         gbps = dec["kv_bytes"] / (dec["ms"] * 1e-3) / 1e9
         dk = dec["kern"].get("decode")
         droof = None
@@ -337,7 +377,9 @@ def main():
             droof = {"kernel": "decode", "bound": "hbm", "achieved": round(ach, 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(ach / PEAK_HBM_GBPS, 4),
-                     "traffic": measured_traffic("decode", W.DECODE.name)}
+                     "traffic": measured_traffic("decode", W.DECODE.name),
+                     "work_per_launch": f"{dec['kv_bytes']} B of K/V (sum over sequences of "
+                                        f"len * Hkv * d * 2 tensors * 2 B)"}
         result["decode"] = {
             "workload": f"{W.DECODE.name}: {W.DECODE.n_seqs} seqs, p={W.DECODE.p} + "
                         f"U{{0..{W.DECODE.max_generated}}} generated, Hq={W.DECODE.n_q_heads} "

@@ -151,6 +151,29 @@ int cart_attn_bwd(const cart_attn_shape* s, const void* q, const void* k_tok,
                   int32_t accumulate_cart, void* workspace, size_t workspace_bytes,
                   void* stream);
 
+/*
+ * cart_attn_schedule_query -- how cart_attn_fwd / cart_attn_bwd will split
+ * the work of shape `s` (host pointer) over the GPU. Host-only (no HIP call,
+ * no device memory); the same plan the launches use, so a caller or a test
+ * can see which code paths a shape takes (for example whether key tiles are
+ * cut into pieces that the dK/dV kernel reduces itself). Not one of the
+ * method's operations: a diagnostic of this library's schedule.
+ * Returns CART_ERR_INVALID_ARG (or _UNSUPPORTED) for a bad shape or NULL out.
+ */
+typedef struct {
+  int32_t fwd_grid;               /* forward workgroups */
+  int32_t fwd_key_splits;         /* > 1: key range split, partials merged by LSE */
+  int32_t bwd_cart_tiles;         /* 128-row cartridge key tiles per kv head */
+  int32_t bwd_tok_tiles;          /* 128-row token key tiles per (batch, kv head) */
+  int32_t bwd_units_per_piece;    /* target (batch, q-head, 32-query) units per piece */
+  int32_t bwd_cart_pieces;        /* pieces per cartridge tile (> 1: cut, reduced in-kernel) */
+  int32_t bwd_tok_pieces_max;     /* most pieces of one token tile (> 1: cut) */
+  int32_t bwd_kv_grid;            /* dK/dV workgroups */
+  int32_t bwd_dq_grid;            /* dQ workgroups */
+  int32_t bwd_dq_key_splits;      /* > 1: dQ key range split, pieces summed after */
+} cart_attn_schedule;
+int cart_attn_schedule_query(const cart_attn_shape* s, cart_attn_schedule* out);
+
 /* ------------------------------------------------------------------------
  * Serving: a paged KV cache that hosts a prefix no tokens produced.
  *   Source: Cartridges guide, "Semantics" (serving): the full prefix is
@@ -226,6 +249,7 @@ int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_n
                 int32_t n_q_heads, float scale, void* out, void* workspace,
                 size_t workspace_bytes, void* stream);
 size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
+
 
 /* ------------------------------------------------------------------------
  * Launch timing (profiling aid). When enabled, every kernel launch of this

@@ -45,6 +45,7 @@ EXPORTS = [
     "cart_rope_tokens", "cart_attn_workspace_size", "cart_attn_fwd", "cart_attn_bwd",
     "cart_cache_create", "cart_cache_destroy", "cart_cache_reset", "cart_cache_seq_len",
     "cart_append_cache", "cart_write_cache", "cart_decode", "cart_decode_workspace_size",
+    "cart_attn_schedule_query",
     "cart_timing_enable", "cart_timing_only", "cart_timing_query", "cart_status_string", "cart_last_error",
 ]
 
@@ -56,6 +57,13 @@ class AttnShape(ctypes.Structure):
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("scale", ctypes.c_float), ("tok_dtype", ctypes.c_int), ("row_dtype", ctypes.c_int),
     ]
+
+
+class AttnSchedule(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "fwd_grid", "fwd_key_splits", "bwd_cart_tiles", "bwd_tok_tiles", "bwd_units_per_piece",
+        "bwd_cart_pieces", "bwd_tok_pieces_max", "bwd_kv_grid", "bwd_dq_grid",
+        "bwd_dq_key_splits")]
 
 
 class CacheDesc(ctypes.Structure):
@@ -90,6 +98,7 @@ _lib.cart_write_cache.argtypes = [_vp, _i32, _vp, _vp, ctypes.c_int, _i32, _i32,
 _lib.cart_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
 _lib.cart_decode_workspace_size.argtypes = [_vp, _i32]
 _lib.cart_decode_workspace_size.restype = _sz
+_lib.cart_attn_schedule_query.argtypes = [_P(AttnShape), _P(AttnSchedule)]
 _lib.cart_timing_enable.argtypes = [_i32]
 _lib.cart_timing_only.argtypes = [ctypes.c_char_p]
 _lib.cart_timing_query.argtypes = [ctypes.c_char_p, _P(ctypes.c_double), _P(_i32)]
@@ -176,6 +185,14 @@ def cart_attn_bwd(shape: AttnShape, q, k_tok, v_tok, k_cart, v_cart, out, lse, d
                               _ptr(dq), _ptr(dk_tok), _ptr(dv_tok), _ptr(dk_cart),
                               _ptr(dv_cart), int(accumulate_cart), _ptr(workspace), ws_bytes,
                               _stream(stream)), "cart_attn_bwd")
+
+
+def cart_attn_schedule_query(shape: AttnShape) -> AttnSchedule:
+    """The work split cart_attn_fwd / cart_attn_bwd will use (host-only)."""
+    out = AttnSchedule()
+    _check(_lib.cart_attn_schedule_query(ctypes.byref(shape), ctypes.byref(out)),
+           "cart_attn_schedule_query")
+    return out
 
 
 # ------------------------------------------------------------ conveniences

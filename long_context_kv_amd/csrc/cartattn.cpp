@@ -265,6 +265,40 @@ int cart_attn_bwd(const cart_attn_shape* s, const void* q, const void* k_tok, co
                     st, "cart_attn_bwd");
 }
 
+int cart_attn_schedule_query(const cart_attn_shape* s, cart_attn_schedule* out) {
+  CHECK(check_shape(s));
+  if (!out) return fail(CART_ERR_INVALID_ARG, "out is NULL");
+  const AttnDims d = dims_of(s);
+  const FwdPlan fp = plan_fwd(d);
+  const BwdPlan bp = plan_bwd(d);
+  cart_attn_schedule r{};
+  r.fwd_grid = fp.grid;
+  r.fwd_key_splits = fp.n_splits;
+  r.bwd_cart_tiles = bp.n_ct;
+  r.bwd_tok_tiles = bp.n_tt;
+  if (d.tok_bf16) {
+    r.bwd_units_per_piece = bp.kv_target;
+    r.bwd_cart_pieces = bp.kv_splits_c;
+    r.bwd_tok_pieces_max = bp.kv_stmax;
+    r.bwd_kv_grid = bp.grid_kv;
+    r.bwd_dq_grid = bp.grid_q;
+    r.bwd_dq_key_splits = bp.q_splits;
+  } else {
+    // float32 reference mode: one kernel, cartridge tiles split over units,
+    // dQ accumulated in the same kernel
+    const long long units = (long long)d.B * (d.Hq / d.Hkv) * bp.nqt;
+    r.bwd_units_per_piece = (int)((units + bp.splits_c - 1) / bp.splits_c);
+    r.bwd_cart_pieces = bp.splits_c;
+    r.bwd_tok_pieces_max = 1;
+    r.bwd_kv_grid = bp.grid_c + bp.grid_t;
+    r.bwd_dq_grid = 0;
+    r.bwd_dq_key_splits = 1;
+  }
+  *out = r;
+  g_err[0] = '\0';
+  return CART_OK;
+}
+
 int cart_cache_create(const cart_cache_desc* d, cart_cache** out) {
   if (!d || !out) return fail(CART_ERR_INVALID_ARG, "desc and out must be non-NULL");
   *out = nullptr;
@@ -336,9 +370,12 @@ size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads) {
   return plan_decode(cache_dims(c), n_q_heads).part_bytes;
 }
 
-int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
-                int32_t n_q_heads, float scale, void* out, void* workspace,
-                size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks shared by both decode entry points; on success *part is the bytes
+// of split partials the launch needs.
+int check_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                 int32_t n_q_heads, float scale, void* out, size_t* part) {
   if (!c) return fail(CART_ERR_INVALID_ARG, "cache handle is NULL");
   if (n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0)
     return fail(CART_ERR_GEOMETRY, "n_q_heads %d is not a multiple of the cache's %d kv heads",
@@ -354,24 +391,38 @@ int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_n
   CHECK(opt_ptr(k_new, "k_new"));
   CHECK(opt_ptr(v_new, "v_new"));
   const int add = k_new ? 1 : 0;
-  int max_len = 0;
   for (int s = 0; s < c->d.n_seqs; ++s) {
     const long long len = (long long)c->lens[s] + add;
     if (len < 1) return fail(CART_ERR_INVALID_ARG, "seq %d holds no rows to attend over", s);
     if (len > capacity(c))
       return fail(CART_ERR_CACHE_FULL, "seq %d: appending exceeds capacity %lld", s, capacity(c));
-    if (len > max_len) max_len = (int)len;
   }
-  const CacheDims cd = cache_dims(c);
-  CHECK(check_workspace(workspace, workspace_bytes, plan_decode(cd, n_q_heads).part_bytes));
+  *part = plan_decode(cache_dims(c), n_q_heads).part_bytes;
+  return CART_OK;
+}
+
+int run_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+               int32_t n_q_heads, float scale, void* out, void* ws, void* stream,
+               const char* what) {
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)c->d.head_dim);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int r = hip_result(
-      launch_decode(cd, n_q_heads, sc, q, k_new, v_new, max_len, out, workspace, st), st,
-      "cart_decode");
-  if (r == CART_OK && add)
+  const int r = hip_result(launch_decode(cache_dims(c), n_q_heads, sc, q, k_new, v_new, 0, out,
+                                         ws, st),
+                           st, what);
+  if (r == CART_OK && k_new)
     for (int s = 0; s < c->d.n_seqs; ++s) c->lens[s] += 1;
   return r;
+}
+
+}  // namespace
+
+int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                int32_t n_q_heads, float scale, void* out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  size_t part = 0;
+  CHECK(check_decode(c, q, k_new, v_new, n_q_heads, scale, out, &part));
+  CHECK(check_workspace(workspace, workspace_bytes, part));
+  return run_decode(c, q, k_new, v_new, n_q_heads, scale, out, workspace, stream, "cart_decode");
 }
 
 }  // extern "C"

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -26,7 +27,9 @@ struct Record {
 };
 
 std::mutex g_mu;
-bool g_on = false;
+// Read without the lock on every launch: when timing is off (the normal case)
+// a launch costs one relaxed load here and takes no lock.
+std::atomic<bool> g_on{false};
 std::string g_only;   // when not empty, only launches of this kernel name are timed
 std::vector<Record> g_records;
 std::vector<hipEvent_t> g_pool;
@@ -58,8 +61,9 @@ void recycle_all() {
 void timing_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
   *start = nullptr;
   *stop = nullptr;
+  if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on) return;
+  if (!g_on.load(std::memory_order_relaxed)) return;
   if (!g_only.empty() && g_only != name) return;
   Record r{name, take_event(), take_event()};
   if (!r.start || !r.stop) return;
@@ -78,7 +82,7 @@ int cart_timing_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_mu);
   for (auto& r : g_records) hipEventSynchronize(r.stop);
   recycle_all();
-  g_on = on != 0;
+  g_on.store(on != 0, std::memory_order_relaxed);
   return CART_OK;
 }
 

@@ -156,4 +156,39 @@ def decode_inputs(shape: DecodeShape, n_seqs: Optional[int] = None,
                         max_pages, n_pages)
 
 
+@dataclasses.dataclass
+class RaggedDecodeInputs:
+    k_cart: List[torch.Tensor]    # per seq [prefix[s], Hkv, d] float32
+    v_cart: List[torch.Tensor]
+    k_gen: List[torch.Tensor]     # per seq [generated[s], Hkv, d] bfloat16
+    v_gen: List[torch.Tensor]
+    q: torch.Tensor               # [S, Hq, d] bfloat16
+    k_new: torch.Tensor           # [S, Hkv, d] bfloat16, one appended row each
+    v_new: torch.Tensor
+    page_perm: torch.Tensor       # physical page order, int32, S * max_pages
+    n_pages: int
+
+
+def decode_inputs_ragged(prefix: List[int], generated: List[int], n_q_heads: int,
+                         n_kv_heads: int, head_dim: int, max_pages: int,
+                         seed: int) -> RaggedDecodeInputs:
+    """Serving inputs with a given prefix and generated length per sequence,
+    drawn in this order: per sequence its prefix K/V (float32) and generated
+    K/V (bfloat16); q; the appended row's K/V; a random physical page order."""
+    g = torch.Generator().manual_seed(seed)
+    S, Hq, Hkv, d = len(prefix), n_q_heads, n_kv_heads, head_dim
+    kc, vc, kg, vg = [], [], [], []
+    for s in range(S):
+        kc.append(_randn(g, (prefix[s], Hkv, d), torch.float32))
+        vc.append(_randn(g, (prefix[s], Hkv, d), torch.float32))
+        kg.append(_randn(g, (generated[s], Hkv, d), torch.bfloat16))
+        vg.append(_randn(g, (generated[s], Hkv, d), torch.bfloat16))
+    q = _randn(g, (S, Hq, d), torch.bfloat16)
+    k_new = _randn(g, (S, Hkv, d), torch.bfloat16)
+    v_new = _randn(g, (S, Hkv, d), torch.bfloat16)
+    n_pages = S * max_pages
+    perm = torch.randperm(n_pages, generator=g).to(torch.int32)
+    return RaggedDecodeInputs(kc, vc, kg, vg, q, k_new, v_new, perm, n_pages)
+
+
 SHAPES = {1: TINY, 2: QWEN3_0_6B, 3: QWEN3_8B, 4: DECODE, 5: LONG}

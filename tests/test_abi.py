@@ -211,3 +211,63 @@ def test_workspace_sizes_of_the_workloads():
             fw = L.cart_attn_workspace_size(ctypes.byref(s), 0)
             bw = L.cart_attn_workspace_size(ctypes.byref(s), 1)
             assert 0 <= fw < (1 << 40) and 0 <= bw < (1 << 40), (b, n, p, hq, hkv, d, tok, row)
+
+
+# Shapes of the GPU parity cases (name, B, n, p, Hq, Hkv, d) whose dK/dV
+# schedule must cut key tiles into pieces, so the in-kernel reduction of a
+# cut tile stays covered by the GPU tests; and shapes that must not.
+CUT_SHAPES = [
+    ("pieces-g4", 2, 200, 600, 8, 2, 128),
+    ("pieces-d64", 2, 150, 500, 8, 2, 64),
+    ("token-heavy", 1, 500, 16, 4, 2, 128),
+    ("ragged-g4", 2, 77, 200, 8, 2, 128),
+    ("g8", 1, 70, 130, 16, 2, 128),
+]
+UNCUT_SHAPES = [
+    ("units-1", 1, 20, 100, 1, 1, 128),
+    ("units-2", 1, 40, 130, 2, 1, 128),
+    ("units-3-ragged", 1, 70, 260, 3, 1, 128),
+]
+
+
+def _sched(B, n, p, Hq, Hkv, d, tok=C.CART_BF16, row=C.CART_F32):
+    return C.cart_attn_schedule_query(_shape(batch=B, q_seq=n, p=p, n_q_heads=Hq,
+                                             n_kv_heads=Hkv, head_dim=d, frozen_rows=min(1, p),
+                                             tok_dtype=tok, row_dtype=row))
+
+
+@pytest.mark.parametrize("case", CUT_SHAPES, ids=[c[0] for c in CUT_SHAPES])
+def test_schedule_cuts_key_tiles(case):
+    s = _sched(*case[1:])
+    assert s.bwd_cart_pieces > 1 and s.bwd_tok_pieces_max > 1, case[0]
+    # the grid holds every piece: cartridge tiles x pieces + the token pieces
+    assert s.bwd_kv_grid >= case[5] * (s.bwd_cart_tiles * s.bwd_cart_pieces +
+                                       case[1] * s.bwd_tok_tiles)
+
+
+@pytest.mark.parametrize("case", UNCUT_SHAPES, ids=[c[0] for c in UNCUT_SHAPES])
+def test_schedule_uncut_small_pipelines(case):
+    s = _sched(*case[1:])
+    assert s.bwd_cart_pieces == 1 and s.bwd_tok_pieces_max == 1, case[0]
+
+
+def test_schedule_of_the_workloads():
+    from long_context_kv_amd import workloads as W
+    c2 = _sched(1, 1024, 2048, 16, 8, 128)
+    # the small layer splits the key range of the forward and of the dQ kernel
+    assert c2.fwd_key_splits > 1 and c2.bwd_dq_key_splits > 1
+    assert c2.fwd_grid >= 512
+    for sh in (W.QWEN3_8B, W.LONG):
+        s = _sched(sh.batch, sh.q_seq, sh.p, sh.n_q_heads, sh.n_kv_heads, sh.head_dim)
+        assert s.fwd_key_splits == 1 and s.bwd_dq_key_splits == 1, sh.name
+        assert s.bwd_cart_tiles == (sh.p + 127) // 128
+        assert s.bwd_tok_tiles == (sh.q_seq + 127) // 128
+    f32 = _sched(1, 16, 8, 4, 2, 64, C.CART_F32, C.CART_F32)
+    assert f32.bwd_dq_grid == 0 and f32.bwd_kv_grid >= 2
+
+
+def test_schedule_validation():
+    bad = ctypes.byref(_shape(batch=0))
+    out = C.AttnSchedule()
+    assert L.cart_attn_schedule_query(bad, ctypes.byref(out)) == C.CART_ERR_INVALID_ARG
+    assert L.cart_attn_schedule_query(ctypes.byref(_shape()), None) == C.CART_ERR_INVALID_ARG

@@ -273,13 +273,26 @@ def _heads_subset(x, kv_heads, g):
     return out, qh
 
 
+_FULL = {}
+
+
+def _full_gpu(C, sh, seed):
+    """GPU outputs of one full-size layer, computed once per (shape, seed)."""
+    key = (sh.name, seed)
+    if key not in _FULL:
+        _FULL.clear()                       # keep one layer's outputs at a time
+        x = W.train_inputs(sh, seed=seed)
+        say(sh.name, "seed", seed, "GPU step")
+        got = _gpu_step(C, x, sh.p, sh.frozen_rows)
+        _FULL[key] = (x, {k: v.cpu() for k, v in got.items()})
+    return _FULL[key]
+
+
 def _full_config(C, sh, seed, kv_heads):
-    x = W.train_inputs(sh, seed=seed)
-    say(sh.name, "seed", seed, "GPU step")
-    got = _gpu_step(C, x, sh.p, sh.frozen_rows)
+    x, got = _full_gpu(C, sh, seed)
     g = sh.n_q_heads // sh.n_kv_heads
     xs, qh = _heads_subset(x, kv_heads, g)
-    say(sh.name, "oracle on kv heads", kv_heads)
+    say(sh.name, "seed", seed, "oracle on kv heads", kv_heads)
     ref = _oracle_step(xs, sh.p, sh.frozen_rows)
     sub = dict(o=got["o"][:, :, qh], dq=got["dq"][:, :, qh], dk_tok=got["dk_tok"][:, :, kv_heads],
                dv_tok=got["dv_tok"][:, :, kv_heads], dk_cart=got["dk_cart"][:, kv_heads],
@@ -287,20 +300,89 @@ def _full_config(C, sh, seed, kv_heads):
     return _compare(sub, ref, TOL_BF16, sh.frozen_rows)
 
 
+# Every kv head of every full-size layer meets the oracle; the heads are
+# compared in two halves so that each test stays well under a minute of
+# oracle time on the host.
+HALVES = [list(range(0, 4)), list(range(4, 8))]
+
+
 def test_config_qwen3_0_6b_layer(C):
     errs = _full_config(C, W.QWEN3_0_6B, W.QWEN3_0_6B.seed, list(range(8)))
     say("errors", errs)
 
 
-def test_config_qwen3_8b_layer(C):
-    errs = _full_config(C, W.QWEN3_8B, W.QWEN3_8B.seed, [0, 5])
+@pytest.mark.parametrize("half", [0, 1])
+def test_config_qwen3_8b_layer(C, half):
+    errs = _full_config(C, W.QWEN3_8B, W.QWEN3_8B.seed, HALVES[half])
     say("errors", errs)
 
 
+@pytest.mark.parametrize("half", [0, 1])
 @pytest.mark.parametrize("layer", [0, 27])
-def test_config_long_cartridge_layer(C, layer):
-    errs = _full_config(C, W.LONG, W.LONG.seed + layer, [layer % 8])
+def test_config_long_cartridge_layer(C, layer, half):
+    errs = _full_config(C, W.LONG, W.LONG.seed + layer, HALVES[half])
     say("errors", errs)
+
+
+# ------------------------------------------------------ invariants / edges
+
+def test_frozen_rows_three(C):
+    """frozen_rows = 3: rows 0..2 of both cartridge gradients are exactly zero
+    (the unfrozen gradient there is not), the rest match the oracle."""
+    sh = W.TrainShape("frozen3", 2, 90, 150, 8, 2, 128, torch.bfloat16, torch.float32, 13,
+                      frozen_rows=3)
+    x = W.train_inputs(sh)
+    say("frozen rows 3")
+    got = _gpu_step(C, x, sh.p, 3)
+    ref = _oracle_step(x, sh.p, 3)
+    _compare(got, ref, TOL_BF16, 3)
+    free = _oracle_step(x, sh.p, 0)
+    assert np.max(np.abs(free["dk_cart"][:3])) > 0 and np.max(np.abs(free["dv_cart"][:3])) > 0
+
+
+@pytest.mark.parametrize("case", [("pieces-g4", 2, 200, 600, 8, 2, 128),
+                                  ("qwen3-0.6b-layer", 1, 1024, 2048, 16, 8, 128)],
+                         ids=["pieces-g4", "qwen3-0.6b-layer"])
+def test_bf16_repeat_run_is_bitwise(C, case):
+    """The bf16 path takes no float atomics (cut tiles and key splits are
+    summed in a fixed order), so two runs on the same inputs agree bit for bit."""
+    name, B, n, p, Hq, Hkv, d = case
+    sh = _shape(name, B, n, p, Hq, Hkv, d, torch.bfloat16, torch.float32, 17)
+    x = W.train_inputs(sh)
+    say("repeat run", name)
+    a = _gpu_step(C, x, p, 1)
+    b = _gpu_step(C, x, p, 1)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_key_shift_invariance(C):
+    """Adding one vector c to every key row (cartridge and token) shifts each
+    query's scores by q.c, which the softmax removes: O and every gradient are
+    unchanged. The GPU run on shifted keys matches the oracle on the
+    unshifted ones."""
+    sh = _shape("shift", 2, 80, 140, 8, 2, 128, torch.bfloat16, torch.float32, 23)
+    x = W.train_inputs(sh)
+    c = torch.randn(2, 128, generator=torch.Generator().manual_seed(24)) * 0.5
+    xs = dict(x)
+    xs["k_tok"] = (x["k_tok"].float() + c).to(torch.bfloat16)
+    xs["k_cart"] = x["k_cart"] + c
+    g = _dev(xs)
+    say("key shift")
+    o, lse = C.attn_fwd(g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"])
+    grads = C.attn_bwd(g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"], o, lse,
+                       g["dout"])
+    torch.cuda.synchronize()
+    args = [f64(x[k]) for k in ("q", "k_tok", "v_tok", "k_cart", "v_cart")]
+    o_ref, _ = O.attn_fwd(*args)
+    gr = O.attn_bwd(*args, f64(x["dout"]), frozen_rows=1)
+    assert rel(f64(o), o_ref) <= TOL_BF16
+    for t in (0, 2, 4):                     # dQ, dV_tok, dV_cart: unchanged by the shift
+        assert rel(f64(grads[t])[1:] if t == 4 else f64(grads[t]),
+                   gr[t][1:] if t == 4 else gr[t]) <= TOL_BF16, t
+    # dK (token and cartridge) too, up to bf16 rounding of the shifted keys
+    assert rel(f64(grads[1]), gr[1]) <= TOL_BF16
+    assert rel(f64(grads[3])[1:], gr[3][1:]) <= TOL_BF16
 
 
 # ------------------------------------------------------------------ serving
@@ -409,3 +491,51 @@ def test_serving_parity_decode_equals_fwd(C):
 def test_config_serving_decode(C):
     sh = W.DECODE
     _serving_check(C, sh, sh.n_seqs, sh.p, sh.max_generated)
+
+
+# GQA groups 1, 2, 4, 8 at head_dim 64 and 128, with sequences of very
+# different lengths in one cache: 1 row, a few pages, a mid length and the
+# full capacity, so that some sequences have fewer splits than the launch's
+# maximum (idle split workgroups) and the merge counts them per sequence.
+DECODE_VARIANTS = [(g, d) for d in (64, 128) for g in (1, 2, 4, 8)]
+
+
+@pytest.mark.parametrize("g,d", DECODE_VARIANTS, ids=[f"g{g}-d{d}" for g, d in DECODE_VARIANTS])
+def test_decode_variants_ragged(C, g, d):
+    Hkv = 2
+    Hq = g * Hkv
+    max_pages = 40                                   # 640 rows per sequence
+    prefix = [1, 20, 257, 600, 100]
+    gen = [0, 13, 50, 40, 0]
+    di = W.decode_inputs_ragged(prefix, gen, Hq, Hkv, d, max_pages, seed=300 + 10 * g + d)
+    n_seqs = len(prefix)
+    cache = C.PagedCache(n_seqs, Hkv, d, max_pages, di.n_pages,
+                         di.page_perm.view(n_seqs, max_pages), "cuda")
+    oc = O.DenseCache(n_seqs, Hkv, d)
+    say("decode variant", g, d)
+    for s in range(n_seqs):
+        cache.write(s, di.k_cart[s].cuda(), di.v_cart[s].cuda())
+        oc.write(s, f64(di.k_cart[s]), f64(di.v_cart[s]))
+        if gen[s]:
+            cache.append(s, di.k_gen[s].cuda(), di.v_gen[s].cuda())
+            oc.append(s, f64(di.k_gen[s]), f64(di.v_gen[s]))
+    lens = [cache.seq_len(s) for s in range(n_seqs)]
+    assert lens == [a + b for a, b in zip(prefix, gen)] and max(lens) == 640
+    nbytes = cache.decode_workspace_size(Hq)
+    ws = C.workspace(nbytes, "cuda")
+    out = torch.empty(n_seqs, Hq, d, dtype=torch.bfloat16, device="cuda")
+    cache.decode(di.q.cuda(), out, ws)
+    torch.cuda.synchronize()
+    assert rel(f64(out), O.decode_step(oc, f64(di.q))) <= TOL_BF16
+    # at least 3 splits for the longest sequence: the merge really merges
+    assert nbytes >= n_seqs * Hq * 3 * (d + 2) * 4
+    # then a step that appends one row to every sequence: the full one is
+    # first reset and given its prefix alone again (in the oracle too)
+    cache.reset(3)
+    cache.write(3, di.k_cart[3].cuda(), di.v_cart[3].cuda())
+    oc.k[3], oc.v[3] = oc.k[3][:prefix[3]], oc.v[3][:prefix[3]]
+    cache.decode(di.q.cuda(), out, ws, k_new=di.k_new.cuda(), v_new=di.v_new.cuda())
+    torch.cuda.synchronize()
+    ref = O.decode_step(oc, f64(di.q), f64(di.k_new), f64(di.v_new))
+    assert rel(f64(out), ref) <= TOL_BF16
+    cache.close()
