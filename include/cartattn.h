@@ -250,6 +250,23 @@ int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_n
                 size_t workspace_bytes, void* stream);
 size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
 
+/*
+ * cart_decode_noalloc -- cart_decode without a workspace argument and without
+ * any device allocation, for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks, kernels and results as cart_decode; the split
+ * partials go to a scratch array that the library holds in device memory
+ * (one per GPU, kept until the process ends), of at most
+ * cart_decode_noalloc_max_bytes() bytes: a cache/head geometry whose
+ * cart_decode_workspace_size() exceeds it is refused with CART_ERR_WORKSPACE.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (concurrent streams or threads) race and must be serialized by the
+ * caller. The first call on a device looks up the scratch's address there
+ * (a HIP runtime query; CART_ERR_HIP if it fails).
+ */
+int cart_decode_noalloc(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                        int32_t n_q_heads, float scale, void* out, void* stream);
+size_t cart_decode_noalloc_max_bytes(void);
 
 /* ------------------------------------------------------------------------
  * Launch timing (profiling aid). When enabled, every kernel launch of this

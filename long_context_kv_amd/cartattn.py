@@ -45,7 +45,7 @@ EXPORTS = [
     "cart_rope_tokens", "cart_attn_workspace_size", "cart_attn_fwd", "cart_attn_bwd",
     "cart_cache_create", "cart_cache_destroy", "cart_cache_reset", "cart_cache_seq_len",
     "cart_append_cache", "cart_write_cache", "cart_decode", "cart_decode_workspace_size",
-    "cart_attn_schedule_query",
+    "cart_decode_noalloc", "cart_decode_noalloc_max_bytes", "cart_attn_schedule_query",
     "cart_timing_enable", "cart_timing_only", "cart_timing_query", "cart_status_string", "cart_last_error",
 ]
 
@@ -98,6 +98,9 @@ _lib.cart_write_cache.argtypes = [_vp, _i32, _vp, _vp, ctypes.c_int, _i32, _i32,
 _lib.cart_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
 _lib.cart_decode_workspace_size.argtypes = [_vp, _i32]
 _lib.cart_decode_workspace_size.restype = _sz
+_lib.cart_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _vp]
+_lib.cart_decode_noalloc_max_bytes.argtypes = []
+_lib.cart_decode_noalloc_max_bytes.restype = _sz
 _lib.cart_attn_schedule_query.argtypes = [_P(AttnShape), _P(AttnSchedule)]
 _lib.cart_timing_enable.argtypes = [_i32]
 _lib.cart_timing_only.argtypes = [ctypes.c_char_p]
@@ -301,6 +304,19 @@ class PagedCache:
         _check(_lib.cart_decode(self.handle, _ptr(q), _ptr(k_new), _ptr(v_new), q.shape[1],
                                 scale, _ptr(out), _ptr(workspace_t), ws_bytes, _stream(stream)),
                "cart_decode")
+
+
+    def decode_noalloc(self, q: torch.Tensor, out: torch.Tensor,
+                       k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,
+                       scale: float = 0.0, stream=None) -> None:
+        """cart_decode_noalloc: the same step with the library's own scratch."""
+        _check(_lib.cart_decode_noalloc(self.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                        q.shape[1], scale, _ptr(out), _stream(stream)),
+               "cart_decode_noalloc")
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(_lib.cart_decode_noalloc_max_bytes())
 
 
 def timing_enable(on: bool) -> None:

@@ -425,4 +425,24 @@ int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_n
   return run_decode(c, q, k_new, v_new, n_q_heads, scale, out, workspace, stream, "cart_decode");
 }
 
+int cart_decode_noalloc(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                        int32_t n_q_heads, float scale, void* out, void* stream) {
+  size_t part = 0;
+  CHECK(check_decode(c, q, k_new, v_new, n_q_heads, scale, out, &part));
+  if (part > kDecodeScratchBytes)
+    return fail(CART_ERR_WORKSPACE,
+                "cart_decode_noalloc: %zu bytes of split partials exceed the library's "
+                "%zu-byte scratch (use cart_decode with a workspace)",
+                part, kDecodeScratchBytes);
+  void* ws = nullptr;
+  if (part > 0) {
+    const hipError_t e = decode_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(CART_ERR_HIP, "cart_decode_noalloc: scratch address: %s", hipGetErrorString(e));
+  }
+  return run_decode(c, q, k_new, v_new, n_q_heads, scale, out, ws, stream, "cart_decode_noalloc");
+}
+
+size_t cart_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
+
 }  // extern "C"

@@ -23,6 +23,8 @@
 // and a second kernel merges the splits of a sequence by log-sum-exp.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "timing.hpp"
@@ -352,6 +354,35 @@ hipError_t launch_dec_d(const DecArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Device memory of the allocation-free decode entry point: the split
+// partials live in this file-scope array instead of a caller's workspace.
+// Every GPU the library runs on holds one copy until the process ends; all
+// calls on one GPU share it (the last call's partials stay in it).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  // Host code must not pass `scratch` itself to a kernel (on the host it is
+  // only a stand-in for the symbol); its device address is looked up once
+  // per device, with that device current, and kept.
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_cache_append(const CacheDims& c, int seq, int start, const void* k,
                                const void* v, bool src_bf16, int n_rows, hipStream_t st) {

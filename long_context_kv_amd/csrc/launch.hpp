@@ -76,4 +76,9 @@ hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
                          const void* k_new, const void* v_new, int max_len_after,
                          void* out, void* ws, hipStream_t st);
 
+// Library-held decode scratch (allocation-free entry point): its size, and
+// its device address on the current device (looked up on first use there).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace cartattn
