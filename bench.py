@@ -42,7 +42,8 @@ PEAK_HBM_GBPS = 8000.0
 
 # HBM bytes per launch of a kernel on a workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE; read counts x 2.0 from a 1 GiB copy calibration),
-# summarised in profiles/hbm_bytes_layers_and_decode.md. A figure holds only
+# summarised in profiles/hbm_bytes_long-cartridge-28l_and_decode.md and
+# profiles/hbm_bytes_layers_and_decode.md. A figure holds only
 # for the kernel sources it was measured on: a mismatch of their hash reports
 # traffic as null.
 KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
@@ -51,6 +52,7 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
 MEASURED_TRAFFIC = {
     ("attn_bwd", "qwen3-0.6b-layer"): (42.5e6, "455b4aa28c09e419"),
     ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "455b4aa28c09e419"),
+    ("attn_bwd", "long-cartridge-28l"): (405.8e6, "455b4aa28c09e419"),
     ("attn_fwd", "qwen3-8b-layer"): (234.5e6, "af9090a87cee9e9a"),
     ("decode", "serving-decode"): (1225.6e6, "181d9c2273e0b279"),
 }
@@ -217,6 +219,68 @@ def decode_bench(C, W, shape, steps, warmup):
                 write_ms=wr_ms, write_kernel_ms=ms_app, write_bytes=wr_bytes)
 
 
+def steps_bench(C, W, shape, steps, warmup):
+    """The steps either side of the attention on one layer of `shape`: the
+    fused q/k RMSNorm + RoPE (forward and input gradient) on its token Q/K,
+    Adam (with the bf16 copy) on its two f32 cartridge tensors, and the
+    concatenation of the same rows given as four composed parts."""
+    import torch
+    dev = torch.device("cuda")
+    x = W.train_inputs(shape, seed=shape.seed)
+    q, k, gq = x["q"].to(dev), x["k_tok"].to(dev), x["dout"].to(dev)
+    gk = x["v_tok"].to(dev)
+    d = shape.head_dim
+    g = torch.Generator().manual_seed(shape.seed + 1)
+    w_q = (torch.rand(d, generator=g) + 0.5).to(dev)
+    w_k = (torch.rand(d, generator=g) + 0.5).to(dev)
+    qo, ko, dqi, dki = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(q),
+                        torch.empty_like(k))
+    rows = {n: x[n].to(dev) for n in ("k_cart", "v_cart")}
+    grads = {n: torch.randn(x[n].shape, generator=g).to(dev) for n in rows}
+    mom = {n: (torch.zeros_like(rows[n]), torch.zeros_like(rows[n])) for n in rows}
+    shadow = {n: torch.empty(rows[n].shape, dtype=torch.bfloat16, device=dev) for n in rows}
+    # composition: the same rows as four parts of p/4 rows each, composed
+    # into the bf16 rows the attention reads
+    cut = [shape.p // 4] * 3 + [shape.p - 3 * (shape.p // 4)]
+    kparts = list(torch.split(rows["k_cart"], cut))
+    vparts = list(torch.split(rows["v_cart"], cut))
+    parts = C.parts_desc(kparts, vparts, [1] * 4)
+    Hkv = shape.n_kv_heads
+    kcomp = torch.empty(shape.p, Hkv, d, dtype=torch.bfloat16, device=dev)
+    vcomp = torch.empty_like(kcomp)
+    del x
+    t = [0]
+
+    def step():
+        C.cart_compose_rows(parts, torch.float32, Hkv, d, kcomp, vcomp)
+        C.cart_qk_norm_rope(q, k, qo, ko, w_q, w_k, shape.p, 1e-6, None, W.THETA)
+        C.cart_qk_norm_rope_bwd(q, k, gq, gk, dqi, dki, w_q, w_k, shape.p, 1e-6, None, W.THETA)
+        t[0] += 1
+        for n in rows:
+            C.cart_adam_rows(rows[n], grads[n], mom[n][0], mom[n][1], t[0], 2e-3,
+                             frozen_rows=shape.frozen_rows, rows_bf16=shadow[n])
+
+    names = ("compose_rows", "qk_norm_rope", "qk_norm_rope_bwd", "adam_rows")
+    _, kern, _ = measure(C, step, steps, warmup, names, shape.name + " steps around attention")
+    tok_elems = q.numel() + k.numel()
+    cart_elems = rows["k_cart"].numel()
+    ebytes = 2 if q.dtype == torch.bfloat16 else 4
+    algo = {"qk_norm_rope": 2 * ebytes * tok_elems,            # read x, write y
+            "qk_norm_rope_bwd": 3 * ebytes * tok_elems,        # read x, g; write dx
+            "adam_rows": 30 * cart_elems,                      # x, g, m, v in; x, m, v, bf16 out
+            "compose_rows": 2 * 6 * cart_elems}                # K and V: f32 in, bf16 out
+    out = {}
+    for name, k in kern.items():
+        avg = k["avg_ms"]
+        gbps = algo[name] / (avg * 1e-3) / 1e9
+        out[name] = {"avg_ms": round(avg, 5), "launches": k["launches"], "pass": k["pass_"],
+                     "bytes_per_launch": algo[name],
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+    return out
+
+
 def cpu_baseline(W, shape):
     """The oracle (numpy float64) timed on a bounded sample of the layer: the
     first kv heads of sequence 0 (their GQA q-heads, all queries, all keys),
@@ -308,6 +372,8 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-steps", action="store_true",
+                    help="skip the q/k norm + RoPE and Adam kernels of one layer")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the single-layer training workloads reported beside the headline")
     args = ap.parse_args()
@@ -367,6 +433,8 @@ def main():
                               "frac_of_peak": round(e_val / PEAK_BF16_TFLOPS, 4),
                               "roofline": e_roof, "kernels": e_kernels}
         result["extra_workloads"] = extra
+    if not args.no_steps:
+        result["steps_around_attention"] = steps_bench(C, W, shape, args.steps, args.warmup)
     if not args.no_decode:
         dec = decode_bench(C, W, W.DECODE, max(args.steps, 20), args.warmup)
         gbps = dec["kv_bytes"] / (dec["ms"] * 1e-3) / 1e9

@@ -99,6 +99,76 @@ int cart_rope_tokens(void* q, void* k, cart_dtype dt, int32_t batch, int32_t seq
                      int32_t inverse, void* stream);
 
 /*
+ * cart_qk_norm_rope -- the per-head RMS normalization of the real-token
+ * queries and keys followed by RoPE, in one pass (the step before attention).
+ *   Source: Cartridges guide, "Semantics": cartridge keys are rows of the KV
+ *   cache, i.e. taken after the q/k normalization and after RoPE, so the
+ *   real tokens' queries and keys enter the attention normalized and rotated
+ *   at positions p, p+1, .... The normalization is the Qwen3 q/k RMSNorm.
+ *
+ * q_in [batch, seq, n_q_heads, head_dim], k_in [batch, seq, n_kv_heads,
+ * head_dim] (k_in may be NULL, then k_out and w_k are ignored) of dtype `dt`;
+ * w_q, w_k: float32 [head_dim] weights. For each head row x:
+ *   y = x * w / sqrt(mean(x^2) + eps),
+ * then y is rotated exactly as cart_rope_tokens rotates (position
+ * pos_base + pos_offsets[b] + i, theta, angle in double precision). The
+ * arithmetic is f32 and the result is rounded once to `dt` into q_out/k_out,
+ * which may be q_in/k_in (in place) when the backward is not needed.
+ * batch * seq = 0 is a no-op. eps > 0.
+ */
+int cart_qk_norm_rope(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                      const float* w_q, const float* w_k, cart_dtype dt, int32_t batch,
+                      int32_t seq, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      float eps, int32_t pos_base, const int32_t* pos_offsets, double theta,
+                      void* stream);
+
+/*
+ * cart_qk_norm_rope_bwd -- the gradient of cart_qk_norm_rope with respect to
+ * its inputs (the weights are frozen: no weight gradient).
+ *   Source: as cart_qk_norm_rope; the gradients of the real tokens' queries
+ *   and keys flow back through it towards earlier layers (and their
+ *   cartridges, through the residual stream).
+ *
+ * q_in/k_in: the forward's inputs; dq_out/dk_out: gradients of its outputs
+ * (the attention backward's dq, dk_tok). With r = 1/sqrt(mean(x^2) + eps)
+ * and dy = the output gradient rotated by -angle:
+ *   dx = r w dy - (r^3 / head_dim) x sum_j(w_j dy_j x_j)
+ * into dq_in/dk_in (dtype `dt`), which may alias dq_out/dk_out but not the
+ * inputs (CART_ERR_INVALID_ARG). Other arguments as for the forward.
+ */
+int cart_qk_norm_rope_bwd(const void* q_in, const void* k_in, const void* dq_out,
+                          const void* dk_out, void* dq_in, void* dk_in, const float* w_q,
+                          const float* w_k, cart_dtype dt, int32_t batch, int32_t seq,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float eps,
+                          int32_t pos_base, const int32_t* pos_offsets, double theta,
+                          void* stream);
+
+/*
+ * cart_adam_rows -- one Adam step on a cartridge tensor (the step after the
+ * backward), optionally writing its bf16 copy for the next step's attention.
+ *   Source: Cartridges guide, "Semantics" (objective paragraph): Adam, no
+ *   weight decay, no schedule, lr 2e-2; row 0 is frozen (frozen_prefix);
+ *   "Learning rate vs batch size (measured)": lr 2e-3 at small batches.
+ *
+ * rows, grad, m, v: float32 [n_rows, row_elems] (for a cartridge tensor
+ * [p, n_kv_heads, head_dim]: n_rows = p, row_elems = n_kv_heads * head_dim);
+ * m and v are the caller-owned moments (zero before step 1). For every
+ * element of rows >= frozen_rows, at step `step` >= 1:
+ *   m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2;
+ *   x -= (lr / (1 - b1^step)) m / (sqrt(v) / sqrt(1 - b2^step) + eps).
+ * Frozen rows keep x, m and v. rows_bf16 (nullable, bf16 [n_rows,
+ * row_elems]) receives every row of the updated x rounded to nearest even:
+ * passing it as bf16 cartridge rows to cart_attn_fwd / cart_attn_bwd is
+ * the same as passing the f32 rows. row_elems % 4 == 0; 16-byte aligned.
+ * The hyperparameters are given in double precision; the bias corrections
+ * and the factors (1 - beta) are formed in double and rounded once to f32,
+ * the update itself is f32.
+ */
+int cart_adam_rows(float* rows, const float* grad, float* m, float* v, void* rows_bf16,
+                   int64_t n_rows, int32_t row_elems, int32_t frozen_rows, int32_t step,
+                   double lr, double beta1, double beta2, double eps, void* stream);
+
+/*
  * Workspace bytes that cart_attn_fwd (for_backward = 0) or cart_attn_bwd
  * (for_backward = 1) needs for shape `s` (host pointer). Returns 0 for an
  * invalid shape. The workspace is caller-owned device memory, 256-byte
@@ -175,6 +245,56 @@ typedef struct {
 int cart_attn_schedule_query(const cart_attn_shape* s, cart_attn_schedule* out);
 
 /* ------------------------------------------------------------------------
+ * Composed cartridges.
+ *   Source: Cartridges guide, section "Composition": independently trained
+ *   cartridges compose by concatenation (part 0's rows, then part 1's, ...);
+ *   real tokens sit at RoPE positions starting at the composed length; every
+ *   part keeps the rotations it was trained at; the composed prefix is one
+ *   concatenation per layer, so the attention backward routes gradients into
+ *   every part's trainable rows while each part's sink stays frozen; serving
+ *   writes the parts in order into an empty cache with the append primitive.
+ *
+ * A composed layer runs the single-cartridge calls on the composed rows:
+ *   cart_compose_rows  -> k_cart, v_cart [P, Hkv, d] (P = cart_parts_rows)
+ *   cart_rope_tokens(pos_base = P), cart_attn_fwd(p = P)
+ *   cart_attn_bwd_composed -> dk_cart, dv_cart [P, Hkv, d] float32, part i's
+ *     gradient being rows off_i .. off_i + rows[i] - 1 (off_i = the rows of
+ *     the parts before it), each part's first frozen[i] rows exact zeros.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t n_parts;          /* 1 .. 64 */
+  const int32_t* rows;      /* (host) [n_parts]: rows of each part, >= 0 */
+  const int32_t* frozen;    /* (host) [n_parts]: frozen rows of each part, 0..rows[i] */
+  const void* const* k;     /* (host) [n_parts] device pointers: part i's K [rows[i], Hkv, d] */
+  const void* const* v;     /* (host) [n_parts] device pointers: part i's V */
+} cart_parts;
+
+/* Composed length P = sum of rows[], or -1 for an invalid description. */
+int32_t cart_parts_rows(const cart_parts* parts);
+
+/* Concatenate the parts' K and V rows (dtype src) into k_out/v_out
+   [P, n_kv_heads, head_dim] of dtype dst, rounding f32 to bf16 to nearest
+   even (bf16 -> f32 is CART_ERR_UNSUPPORTED). With dst = bf16 the result is
+   what cart_attn_fwd/bwd would round f32 rows to, so passing it as bf16 rows
+   gives the same results as passing f32 rows. Parts with 0 rows may have
+   NULL pointers. */
+int cart_compose_rows(const cart_parts* parts, cart_dtype src, int32_t n_kv_heads,
+                      int32_t head_dim, void* k_out, void* v_out, cart_dtype dst,
+                      void* stream);
+
+/* cart_attn_bwd over a composed prefix: s->p must equal the composed length
+   and s->frozen_rows is ignored (each part freezes its own first frozen[i]
+   rows; only rows[] and frozen[] of `parts` are read). k_cart/v_cart are the
+   composed rows; dk_cart/dv_cart receive the composed gradient. Everything
+   else is as for cart_attn_bwd (same workspace size). */
+int cart_attn_bwd_composed(const cart_attn_shape* s, const cart_parts* parts, const void* q,
+                           const void* k_tok, const void* v_tok, const void* k_cart,
+                           const void* v_cart, const void* out, const float* lse,
+                           const void* dout, void* dq, void* dk_tok, void* dv_tok,
+                           float* dk_cart, float* dv_cart, int32_t accumulate_cart,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Serving: a paged KV cache that hosts a prefix no tokens produced.
  *   Source: Cartridges guide, "Semantics" (serving): the full prefix is
  *   written into an empty cache, converted to the cache dtype, and the cache
@@ -228,6 +348,14 @@ int cart_write_cache(cart_cache* c, int32_t seq, const void* k_cart,
                      const void* v_cart, cart_dtype src, int32_t p,
                      int32_t n_kv_heads, int32_t head_dim, void* stream);
 
+/* Write a composed prefix into an EMPTY sequence (else CART_ERR_CACHE_NOT_EMPTY):
+   the parts in order, each appended with cart_append_cache (dtype src,
+   converted to bf16), so the sequence ends at the composed length. Geometry
+   and the capacity for all parts are checked before anything is appended. */
+int cart_write_composed_cache(cart_cache* c, int32_t seq, const cart_parts* parts,
+                              cart_dtype src, int32_t n_kv_heads, int32_t head_dim,
+                              void* stream);
+
 /*
  * cart_decode -- one decode step (q_seq = 1) for every sequence.
  *   Source: Cartridges guide, "Semantics" (serving) and "Evidence" (serving
@@ -249,6 +377,33 @@ int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_n
                 int32_t n_q_heads, float scale, void* out, void* workspace,
                 size_t workspace_bytes, void* stream);
 size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads);
+
+/*
+ * cart_decode_verify -- one verify step of n_tokens draft tokens per
+ * sequence (speculative decoding) behind the cache.
+ *   Source: Cartridges guide, "Batched self-study (measured)": every stream
+ *   verifies a span of draft tokens in one pass, attention per stream
+ *   against its own cache, greedy acceptance per row, rejected rows removed
+ *   by truncating rewinds (cart_cache_truncate).
+ *
+ * q [n_seqs, n_tokens, n_q_heads, head_dim] bf16, token t rotated at
+ * position seq_len + t; k_new, v_new [n_seqs, n_tokens, n_kv_heads,
+ * head_dim] bf16 (required) are appended first, so every sequence grows by
+ * n_tokens; token t then attends over rows 0 .. old_len + t (itself and the
+ * drafts before it, not those after). out [n_seqs, n_tokens, n_q_heads,
+ * head_dim] bf16. n_tokens in [1, 64]; n_tokens = 1 is cart_decode with an
+ * appended row. Other rules as for cart_decode; its workspace is
+ * cart_decode_verify_workspace_size(c, n_tokens, n_q_heads) bytes.
+ */
+int cart_decode_verify(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                       int32_t n_tokens, int32_t n_q_heads, float scale, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+size_t cart_decode_verify_workspace_size(const cart_cache* c, int32_t n_tokens,
+                                         int32_t n_q_heads);
+
+/* Shorten one sequence to new_len rows (0 <= new_len <= its length), e.g. to
+   drop the rejected drafts of a verify step; cart_cache_reset is new_len 0. */
+int cart_cache_truncate(cart_cache* c, int32_t seq, int32_t new_len, void* stream);
 
 /*
  * cart_decode_noalloc -- cart_decode without a workspace argument and without

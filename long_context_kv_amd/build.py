@@ -23,7 +23,8 @@ BUILD = HERE / "_build"
 LIB = HERE / "libcartattn.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["cartattn.cpp", "timing.cpp", "rope.hip", "rows.hip", "attn_fwd.hip", "attn_bwd.hip", "decode.hip"]
+SOURCES = ["cartattn.cpp", "timing.cpp", "rope.hip", "rows.hip", "attn_fwd.hip", "attn_bwd.hip",
+           "decode.hip", "qknorm.hip", "adam.hip", "compose.hip"]
 
 COMMON = [
     "--offload-arch=gfx950",

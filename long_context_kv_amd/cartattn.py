@@ -42,9 +42,12 @@ CART_BF16 = 1
 _DTYPES = {torch.float32: CART_F32, torch.bfloat16: CART_BF16}
 
 EXPORTS = [
-    "cart_rope_tokens", "cart_attn_workspace_size", "cart_attn_fwd", "cart_attn_bwd",
+    "cart_rope_tokens", "cart_qk_norm_rope", "cart_qk_norm_rope_bwd", "cart_adam_rows",
+    "cart_attn_workspace_size", "cart_parts_rows", "cart_compose_rows",
+    "cart_attn_bwd_composed", "cart_write_composed_cache", "cart_attn_fwd", "cart_attn_bwd",
     "cart_cache_create", "cart_cache_destroy", "cart_cache_reset", "cart_cache_seq_len",
     "cart_append_cache", "cart_write_cache", "cart_decode", "cart_decode_workspace_size",
+    "cart_decode_verify", "cart_decode_verify_workspace_size", "cart_cache_truncate",
     "cart_decode_noalloc", "cart_decode_noalloc_max_bytes", "cart_attn_schedule_query",
     "cart_timing_enable", "cart_timing_only", "cart_timing_query", "cart_status_string", "cart_last_error",
 ]
@@ -76,6 +79,12 @@ class CacheDesc(ctypes.Structure):
     ]
 
 
+class Parts(ctypes.Structure):
+    _fields_ = [("n_parts", ctypes.c_int32), ("rows", ctypes.POINTER(ctypes.c_int32)),
+                ("frozen", ctypes.POINTER(ctypes.c_int32)),
+                ("k", ctypes.POINTER(ctypes.c_void_p)), ("v", ctypes.POINTER(ctypes.c_void_p))]
+
+
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _sz = ctypes.c_size_t
@@ -83,7 +92,21 @@ _P = ctypes.POINTER
 
 _lib.cart_rope_tokens.argtypes = [_vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _vp, ctypes.c_double, _i32, _vp]
+_lib.cart_qk_norm_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
+                                   _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_double, _vp]
+_lib.cart_qk_norm_rope_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
+                                       _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                       ctypes.c_double, _vp]
+_lib.cart_adam_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _i32, _i32, _i32,
+                                ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                ctypes.c_double, _vp]
 _lib.cart_attn_workspace_size.argtypes = [_P(AttnShape), _i32]
+_lib.cart_parts_rows.argtypes = [_P(Parts)]
+_lib.cart_parts_rows.restype = _i32
+_lib.cart_compose_rows.argtypes = [_P(Parts), ctypes.c_int, _i32, _i32, _vp, _vp, ctypes.c_int, _vp]
+_lib.cart_attn_bwd_composed.argtypes = [_P(AttnShape), _P(Parts), _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.cart_write_composed_cache.argtypes = [_vp, _i32, _P(Parts), ctypes.c_int, _i32, _i32, _vp]
 _lib.cart_attn_workspace_size.restype = _sz
 _lib.cart_attn_fwd.argtypes = [_P(AttnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.cart_attn_bwd.argtypes = [_P(AttnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -98,6 +121,11 @@ _lib.cart_write_cache.argtypes = [_vp, _i32, _vp, _vp, ctypes.c_int, _i32, _i32,
 _lib.cart_decode.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
 _lib.cart_decode_workspace_size.argtypes = [_vp, _i32]
 _lib.cart_decode_workspace_size.restype = _sz
+_lib.cart_decode_verify.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _sz,
+                                    _vp]
+_lib.cart_decode_verify_workspace_size.argtypes = [_vp, _i32, _i32]
+_lib.cart_decode_verify_workspace_size.restype = _sz
+_lib.cart_cache_truncate.argtypes = [_vp, _i32, _i32, _vp]
 _lib.cart_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _vp, _vp]
 _lib.cart_decode_noalloc_max_bytes.argtypes = []
 _lib.cart_decode_noalloc_max_bytes.restype = _sz
@@ -167,6 +195,45 @@ def cart_rope_tokens(q: torch.Tensor, k: Optional[torch.Tensor], pos_base: int,
            "cart_rope_tokens")
 
 
+def cart_qk_norm_rope(q_in: torch.Tensor, k_in: Optional[torch.Tensor], q_out: torch.Tensor,
+                      k_out: Optional[torch.Tensor], w_q: torch.Tensor,
+                      w_k: Optional[torch.Tensor], pos_base: int, eps: float = 1e-6,
+                      pos_offsets: Optional[torch.Tensor] = None, theta: float = 1.0e6,
+                      stream=None) -> None:
+    """q_out/k_out = RoPE(RMSNorm(q_in/k_in)) (may be in place)."""
+    B, S, Hq, d = q_in.shape
+    Hkv = k_in.shape[2] if k_in is not None else 0
+    _check(_lib.cart_qk_norm_rope(_ptr(q_in), _ptr(k_in), _ptr(q_out), _ptr(k_out), _ptr(w_q),
+                                  _ptr(w_k), _dt(q_in), B, S, Hq, Hkv, d, eps, pos_base,
+                                  _ptr(pos_offsets), theta, _stream(stream)),
+           "cart_qk_norm_rope")
+
+
+def cart_qk_norm_rope_bwd(q_in, k_in, dq_out, dk_out, dq_in, dk_in, w_q, w_k, pos_base: int,
+                          eps: float = 1e-6, pos_offsets=None, theta: float = 1.0e6,
+                          stream=None) -> None:
+    """dq_in/dk_in = input gradients of cart_qk_norm_rope."""
+    B, S, Hq, d = q_in.shape
+    Hkv = k_in.shape[2] if k_in is not None else 0
+    _check(_lib.cart_qk_norm_rope_bwd(_ptr(q_in), _ptr(k_in), _ptr(dq_out), _ptr(dk_out),
+                                      _ptr(dq_in), _ptr(dk_in), _ptr(w_q), _ptr(w_k), _dt(q_in),
+                                      B, S, Hq, Hkv, d, eps, pos_base, _ptr(pos_offsets), theta,
+                                      _stream(stream)),
+           "cart_qk_norm_rope_bwd")
+
+
+def cart_adam_rows(rows: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
+                   step: int, lr: float, frozen_rows: int = 1, beta1: float = 0.9,
+                   beta2: float = 0.999, eps: float = 1e-8,
+                   rows_bf16: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One Adam step on f32 rows [n_rows, ...] (rows below frozen_rows kept)."""
+    n_rows = rows.shape[0]
+    row_elems = rows.numel() // max(n_rows, 1)
+    _check(_lib.cart_adam_rows(_ptr(rows), _ptr(grad), _ptr(m), _ptr(v), _ptr(rows_bf16),
+                               n_rows, row_elems, frozen_rows, step, lr, beta1, beta2, eps,
+                               _stream(stream)), "cart_adam_rows")
+
+
 def cart_attn_workspace_size(shape: AttnShape, for_backward: bool) -> int:
     return int(_lib.cart_attn_workspace_size(ctypes.byref(shape), int(for_backward)))
 
@@ -196,6 +263,42 @@ def cart_attn_schedule_query(shape: AttnShape) -> AttnSchedule:
     _check(_lib.cart_attn_schedule_query(ctypes.byref(shape), ctypes.byref(out)),
            "cart_attn_schedule_query")
     return out
+
+
+def parts_desc(k_parts, v_parts, frozen) -> Parts:
+    """A cart_parts description of device tensors (kept alive by the caller).
+    The arrays it points to are attached to the returned object."""
+    n = len(k_parts)
+    rows = (ctypes.c_int32 * n)(*[int(k.shape[0]) for k in k_parts])
+    fr = (ctypes.c_int32 * n)(*[int(f) for f in frozen])
+    kp = (ctypes.c_void_p * n)(*[k.data_ptr() if k.numel() else None for k in k_parts])
+    vp = (ctypes.c_void_p * n)(*[v.data_ptr() if v.numel() else None for v in v_parts])
+    d = Parts(n, rows, fr, kp, vp)
+    d._keep = (rows, fr, kp, vp)
+    return d
+
+
+def cart_parts_rows(parts: Parts) -> int:
+    return int(_lib.cart_parts_rows(ctypes.byref(parts)))
+
+
+def cart_compose_rows(parts: Parts, src_dtype, n_kv_heads: int, head_dim: int, k_out, v_out,
+                      stream=None) -> None:
+    _check(_lib.cart_compose_rows(ctypes.byref(parts), _DTYPES[src_dtype], n_kv_heads, head_dim,
+                                  _ptr(k_out), _ptr(v_out), _dt(k_out), _stream(stream)),
+           "cart_compose_rows")
+
+
+def cart_attn_bwd_composed(shape: AttnShape, parts: Parts, q, k_tok, v_tok, k_cart, v_cart, out,
+                           lse, dout, dq, dk_tok, dv_tok, dk_cart, dv_cart,
+                           accumulate_cart: bool, workspace, stream=None) -> None:
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.cart_attn_bwd_composed(ctypes.byref(shape), ctypes.byref(parts), _ptr(q),
+                                       _ptr(k_tok), _ptr(v_tok), _ptr(k_cart), _ptr(v_cart),
+                                       _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk_tok),
+                                       _ptr(dv_tok), _ptr(dk_cart), _ptr(dv_cart),
+                                       int(accumulate_cart), _ptr(workspace), ws_bytes,
+                                       _stream(stream)), "cart_attn_bwd_composed")
 
 
 # ------------------------------------------------------------ conveniences
@@ -293,6 +396,27 @@ class PagedCache:
         _check(_lib.cart_write_cache(self.handle, seq, _ptr(k_cart), _ptr(v_cart),
                                      _dt(k_cart), p, Hkv, d, _stream(stream)),
                "cart_write_cache")
+
+    def write_composed(self, seq: int, parts: "Parts", src_dtype, stream=None) -> None:
+        _check(_lib.cart_write_composed_cache(self.handle, seq, ctypes.byref(parts),
+                                              _DTYPES[src_dtype], self.n_kv_heads, self.head_dim,
+                                              _stream(stream)), "cart_write_composed_cache")
+
+    def truncate(self, seq: int, new_len: int, stream=None) -> None:
+        _check(_lib.cart_cache_truncate(self.handle, seq, new_len, _stream(stream)),
+               "cart_cache_truncate")
+
+    def verify_workspace_size(self, n_tokens: int, n_q_heads: int) -> int:
+        return int(_lib.cart_decode_verify_workspace_size(self.handle, n_tokens, n_q_heads))
+
+    def verify(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+               out: torch.Tensor, workspace_t: Optional[torch.Tensor], scale: float = 0.0,
+               stream=None) -> None:
+        """cart_decode_verify: q [S, k, Hq, d], k_new/v_new [S, k, Hkv, d]."""
+        ws_bytes = 0 if workspace_t is None else workspace_t.numel() * workspace_t.element_size()
+        _check(_lib.cart_decode_verify(self.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       q.shape[1], q.shape[2], scale, _ptr(out), _ptr(workspace_t),
+                                       ws_bytes, _stream(stream)), "cart_decode_verify")
 
     def decode_workspace_size(self, n_q_heads: int) -> int:
         return int(_lib.cart_decode_workspace_size(self.handle, n_q_heads))

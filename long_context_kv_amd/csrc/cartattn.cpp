@@ -166,6 +166,50 @@ int check_rows(const cart_cache* c, int32_t seq, const void* k, const void* v, c
 
 }  // namespace
 
+namespace {
+
+// Validate a parts description and fill the kernels' table. need_ptrs: the
+// parts' row pointers must be given (16-byte aligned) for parts with rows.
+int parts_table(const cart_parts* parts, bool need_ptrs, PartTable* t) {
+  if (!parts) return fail(CART_ERR_INVALID_ARG, "parts is NULL");
+  if (parts->n_parts < 1 || parts->n_parts > kMaxParts)
+    return fail(CART_ERR_INVALID_ARG, "n_parts (%d) must lie in [1, %d]", parts->n_parts,
+                kMaxParts);
+  if (!parts->rows || !parts->frozen)
+    return fail(CART_ERR_INVALID_ARG, "parts->rows and parts->frozen must be given");
+  if (need_ptrs && (!parts->k || !parts->v))
+    return fail(CART_ERR_INVALID_ARG, "parts->k and parts->v must be given");
+  *t = PartTable{};
+  t->n = parts->n_parts;
+  long long off = 0;
+  for (int i = 0; i < t->n; ++i) {
+    const int r = parts->rows[i], f = parts->frozen[i];
+    if (r < 0) return fail(CART_ERR_INVALID_ARG, "part %d has %d rows", i, r);
+    if (f < 0 || f > r)
+      return fail(CART_ERR_INVALID_ARG, "part %d: frozen rows %d outside [0, %d]", i, f, r);
+    t->rows[i] = r;
+    t->frozen[i] = f;
+    t->off[i] = (int)off;
+    off += r;
+    if (off > 0x7fffffffLL) return fail(CART_ERR_UNSUPPORTED, "composed prefix too long");
+    if (need_ptrs) {
+      if (r > 0) {
+        char name[32];
+        snprintf(name, sizeof(name), "parts->k[%d]", i);
+        CHECK(need_ptr(parts->k[i], name));
+        snprintf(name, sizeof(name), "parts->v[%d]", i);
+        CHECK(need_ptr(parts->v[i], name));
+      }
+      t->k[i] = parts->k[i];
+      t->v[i] = parts->v[i];
+    }
+  }
+  t->off[t->n] = (int)off;
+  return CART_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* cart_status_string(int status) {
@@ -208,6 +252,113 @@ int cart_rope_tokens(void* q, void* k, cart_dtype dt, int32_t batch, int32_t seq
   return hip_result(launch_rope(q, k, dt == CART_BF16, batch, seq, n_q_heads, k ? n_kv_heads : 0,
                                 head_dim, pos_base, pos_offsets, theta, inverse != 0, st),
                     st, "cart_rope_tokens");
+}
+
+namespace {
+
+int check_norm_rope(cart_dtype dt, int32_t batch, int32_t seq, int32_t n_q_heads,
+                    int32_t n_kv_heads, int32_t head_dim, float eps, int32_t pos_base,
+                    const int32_t* pos_offsets, double theta, const void* k, const float* w_k) {
+  if (!valid_dtype(dt)) return fail(CART_ERR_INVALID_ARG, "unknown dtype");
+  if (batch < 0 || seq < 0) return fail(CART_ERR_INVALID_ARG, "batch and seq must be >= 0");
+  if (n_q_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (k && n_kv_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+  if (!valid_head_dim(head_dim))
+    return fail(CART_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if (!(eps > 0.f) || isinf(eps)) return fail(CART_ERR_INVALID_ARG, "eps must be > 0");
+  if (!(theta > 0.0) || isinf(theta)) return fail(CART_ERR_INVALID_ARG, "theta must be > 0");
+  if (pos_base < 0) return fail(CART_ERR_INVALID_ARG, "pos_base must be >= 0");
+  const long long rows = (long long)batch * seq;
+  if (rows * (n_q_heads + (k ? n_kv_heads : 0)) * head_dim > kMaxElems || rows > 0x7fffffffLL)
+    return fail(CART_ERR_UNSUPPORTED, "tensor too large");
+  if (k && !w_k) return fail(CART_ERR_INVALID_ARG, "w_k is NULL but k is given");
+  if (pos_offsets && (reinterpret_cast<uintptr_t>(pos_offsets) & 3u))
+    return fail(CART_ERR_ALIGNMENT, "pos_offsets is not 4-byte aligned");
+  return CART_OK;
+}
+
+}  // namespace
+
+int cart_qk_norm_rope(const void* q_in, const void* k_in, void* q_out, void* k_out,
+                      const float* w_q, const float* w_k, cart_dtype dt, int32_t batch,
+                      int32_t seq, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      float eps, int32_t pos_base, const int32_t* pos_offsets, double theta,
+                      void* stream) {
+  CHECK(check_norm_rope(dt, batch, seq, n_q_heads, n_kv_heads, head_dim, eps, pos_base,
+                        pos_offsets, theta, k_in, w_k));
+  if ((long long)batch * seq == 0) { g_err[0] = '\0'; return CART_OK; }
+  CHECK(need_ptr(q_in, "q_in"));
+  CHECK(need_ptr(q_out, "q_out"));
+  CHECK(need_ptr(w_q, "w_q"));
+  if (k_in) {
+    CHECK(need_ptr(k_in, "k_in"));
+    CHECK(need_ptr(k_out, "k_out"));
+    CHECK(need_ptr(w_k, "w_k"));
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_qk_norm_rope(q_in, k_in, nullptr, nullptr, q_out, k_in ? k_out : nullptr,
+                                        w_q, w_k, dt == CART_BF16, batch, seq, n_q_heads,
+                                        k_in ? n_kv_heads : 0, head_dim, eps, pos_base,
+                                        pos_offsets, theta, false, st),
+                    st, "cart_qk_norm_rope");
+}
+
+int cart_qk_norm_rope_bwd(const void* q_in, const void* k_in, const void* dq_out,
+                          const void* dk_out, void* dq_in, void* dk_in, const float* w_q,
+                          const float* w_k, cart_dtype dt, int32_t batch, int32_t seq,
+                          int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, float eps,
+                          int32_t pos_base, const int32_t* pos_offsets, double theta,
+                          void* stream) {
+  CHECK(check_norm_rope(dt, batch, seq, n_q_heads, n_kv_heads, head_dim, eps, pos_base,
+                        pos_offsets, theta, k_in, w_k));
+  if ((long long)batch * seq == 0) { g_err[0] = '\0'; return CART_OK; }
+  CHECK(need_ptr(q_in, "q_in"));
+  CHECK(need_ptr(dq_out, "dq_out"));
+  CHECK(need_ptr(dq_in, "dq_in"));
+  CHECK(need_ptr(w_q, "w_q"));
+  if (k_in) {
+    CHECK(need_ptr(k_in, "k_in"));
+    CHECK(need_ptr(dk_out, "dk_out"));
+    CHECK(need_ptr(dk_in, "dk_in"));
+    CHECK(need_ptr(w_k, "w_k"));
+  }
+  if (dq_in == q_in || (k_in && dk_in == k_in))
+    return fail(CART_ERR_INVALID_ARG, "the input gradient may not overwrite the inputs");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_qk_norm_rope(q_in, k_in, dq_out, k_in ? dk_out : nullptr, dq_in,
+                                        k_in ? dk_in : nullptr, w_q, w_k, dt == CART_BF16, batch,
+                                        seq, n_q_heads, k_in ? n_kv_heads : 0, head_dim, eps,
+                                        pos_base, pos_offsets, theta, true, st),
+                    st, "cart_qk_norm_rope_bwd");
+}
+
+int cart_adam_rows(float* rows, const float* grad, float* m, float* v, void* rows_bf16,
+                   int64_t n_rows, int32_t row_elems, int32_t frozen_rows, int32_t step,
+                   double lr, double beta1, double beta2, double eps, void* stream) {
+  if (n_rows < 0 || row_elems < 1)
+    return fail(CART_ERR_INVALID_ARG, "n_rows must be >= 0 and row_elems >= 1");
+  if (row_elems % 4 != 0)
+    return fail(CART_ERR_UNSUPPORTED, "row_elems (%d) must be a multiple of 4", row_elems);
+  if (frozen_rows < 0 || frozen_rows > n_rows)
+    return fail(CART_ERR_INVALID_ARG, "frozen_rows (%d) must lie in [0, n_rows]", frozen_rows);
+  if (step < 1) return fail(CART_ERR_INVALID_ARG, "step (%d) must be >= 1", step);
+  if (!(lr >= 0.0) || isinf(lr)) return fail(CART_ERR_INVALID_ARG, "lr must be finite and >= 0");
+  if (!(beta1 >= 0.0 && beta1 < 1.0) || !(beta2 >= 0.0 && beta2 < 1.0))
+    return fail(CART_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+  if (!(eps > 0.0) || isinf(eps)) return fail(CART_ERR_INVALID_ARG, "eps must be > 0");
+  const long long n = (long long)n_rows * row_elems;
+  if (n > (1LL << 40)) return fail(CART_ERR_UNSUPPORTED, "tensor too large");
+  if (n == 0) { g_err[0] = '\0'; return CART_OK; }
+  CHECK(need_ptr(rows, "rows"));
+  CHECK(need_ptr(grad, "grad"));
+  CHECK(need_ptr(m, "m"));
+  CHECK(need_ptr(v, "v"));
+  CHECK(opt_ptr(rows_bf16, "rows_bf16"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_adam_rows(rows, grad, m, v, rows_bf16, (size_t)n,
+                                     (size_t)frozen_rows * row_elems, step, lr, beta1, beta2,
+                                     eps, st),
+                    st, "cart_adam_rows");
 }
 
 size_t cart_attn_workspace_size(const cart_attn_shape* s, int32_t for_backward) {
@@ -299,6 +450,57 @@ int cart_attn_schedule_query(const cart_attn_shape* s, cart_attn_schedule* out) 
   return CART_OK;
 }
 
+int32_t cart_parts_rows(const cart_parts* parts) {
+  PartTable t;
+  if (parts_table(parts, false, &t) != CART_OK) return -1;
+  return t.off[t.n];
+}
+
+int cart_compose_rows(const cart_parts* parts, cart_dtype src, int32_t n_kv_heads,
+                      int32_t head_dim, void* k_out, void* v_out, cart_dtype dst,
+                      void* stream) {
+  PartTable t;
+  CHECK(parts_table(parts, true, &t));
+  if (!valid_dtype(src) || !valid_dtype(dst)) return fail(CART_ERR_INVALID_ARG, "unknown dtype");
+  if (src == CART_BF16 && dst == CART_F32)
+    return fail(CART_ERR_UNSUPPORTED, "bf16 parts compose into bf16 rows only");
+  if (n_kv_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+  if (!valid_head_dim(head_dim))
+    return fail(CART_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  const long long total = (long long)t.off[t.n] * n_kv_heads * head_dim;
+  if (total > kMaxElems) return fail(CART_ERR_UNSUPPORTED, "composed prefix too large");
+  if (total == 0) { g_err[0] = '\0'; return CART_OK; }
+  CHECK(need_ptr(k_out, "k_out"));
+  CHECK(need_ptr(v_out, "v_out"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_compose_rows(t, src == CART_BF16, dst == CART_BF16,
+                                        n_kv_heads * head_dim, k_out, v_out, st),
+                    st, "cart_compose_rows");
+}
+
+int cart_attn_bwd_composed(const cart_attn_shape* s, const cart_parts* parts, const void* q,
+                           const void* k_tok, const void* v_tok, const void* k_cart,
+                           const void* v_cart, const void* out, const float* lse,
+                           const void* dout, void* dq, void* dk_tok, void* dv_tok,
+                           float* dk_cart, float* dv_cart, int32_t accumulate_cart,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  PartTable t;
+  CHECK(parts_table(parts, false, &t));
+  if (!s) return fail(CART_ERR_INVALID_ARG, "shape is NULL");
+  if (s->p != t.off[t.n])
+    return fail(CART_ERR_INVALID_ARG, "shape p (%d) differs from the parts' %d rows", s->p,
+                t.off[t.n]);
+  // the first part's frozen rows are a prefix the backward zeroes itself; the
+  // others' are zeroed after it (both end as exact zeros)
+  cart_attn_shape s0 = *s;
+  s0.frozen_rows = t.frozen[0];
+  CHECK(cart_attn_bwd(&s0, q, k_tok, v_tok, k_cart, v_cart, out, lse, dout, dq, dk_tok, dv_tok,
+                      dk_cart, dv_cart, accumulate_cart, workspace, workspace_bytes, stream));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_zero_frozen(t, s->n_kv_heads * s->head_dim, dk_cart, dv_cart, st),
+                    st, "cart_attn_bwd_composed");
+}
+
 int cart_cache_create(const cart_cache_desc* d, cart_cache** out) {
   if (!d || !out) return fail(CART_ERR_INVALID_ARG, "desc and out must be non-NULL");
   *out = nullptr;
@@ -365,18 +567,40 @@ int cart_write_cache(cart_cache* c, int32_t seq, const void* k_cart, const void*
   return cart_append_cache(c, seq, k_cart, v_cart, src, p, n_kv_heads, head_dim, stream);
 }
 
+int cart_write_composed_cache(cart_cache* c, int32_t seq, const cart_parts* parts,
+                              cart_dtype src, int32_t n_kv_heads, int32_t head_dim,
+                              void* stream) {
+  PartTable t;
+  CHECK(parts_table(parts, true, &t));
+  CHECK(check_seq(c, seq));
+  if (c->lens[seq] != 0)
+    return fail(CART_ERR_CACHE_NOT_EMPTY, "seq %d already holds %d rows", seq, c->lens[seq]);
+  // every check up front, so a refused composition appends nothing:
+  // geometry and dtype (as for zero rows), then the capacity for all parts
+  CHECK(check_rows(c, seq, nullptr, nullptr, src, 0, n_kv_heads, head_dim));
+  if ((long long)t.off[t.n] > capacity(c))
+    return fail(CART_ERR_CACHE_FULL, "seq %d: %d composed rows exceed capacity %lld", seq,
+                t.off[t.n], capacity(c));
+  for (int i = 0; i < t.n; ++i)
+    CHECK(cart_append_cache(c, seq, t.k[i], t.v[i], src, t.rows[i], n_kv_heads, head_dim,
+                            stream));
+  return CART_OK;
+}
+
 size_t cart_decode_workspace_size(const cart_cache* c, int32_t n_q_heads) {
   if (!c || n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0) return 0;
-  return plan_decode(cache_dims(c), n_q_heads).part_bytes;
+  return plan_decode(cache_dims(c), n_q_heads, 1).part_bytes;
 }
 
 namespace {
 
-// Checks shared by both decode entry points; on success *part is the bytes
-// of split partials the launch needs.
+// Checks shared by the decode entry points (kq query tokens per sequence,
+// whose rows k_new/v_new are appended first when given); on success *part
+// is the bytes of split partials the launch needs.
 int check_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
-                 int32_t n_q_heads, float scale, void* out, size_t* part) {
+                 int32_t kq, int32_t n_q_heads, float scale, void* out, size_t* part) {
   if (!c) return fail(CART_ERR_INVALID_ARG, "cache handle is NULL");
+  if (kq < 1 || kq > 64) return fail(CART_ERR_INVALID_ARG, "tokens per sequence (%d) outside [1, 64]", kq);
   if (n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0)
     return fail(CART_ERR_GEOMETRY, "n_q_heads %d is not a multiple of the cache's %d kv heads",
                 n_q_heads, c->d.n_kv_heads);
@@ -390,27 +614,27 @@ int check_decode(cart_cache* c, const void* q, const void* k_new, const void* v_
   CHECK(need_ptr(out, "out"));
   CHECK(opt_ptr(k_new, "k_new"));
   CHECK(opt_ptr(v_new, "v_new"));
-  const int add = k_new ? 1 : 0;
+  const int add = k_new ? kq : 0;
   for (int s = 0; s < c->d.n_seqs; ++s) {
     const long long len = (long long)c->lens[s] + add;
     if (len < 1) return fail(CART_ERR_INVALID_ARG, "seq %d holds no rows to attend over", s);
     if (len > capacity(c))
       return fail(CART_ERR_CACHE_FULL, "seq %d: appending exceeds capacity %lld", s, capacity(c));
   }
-  *part = plan_decode(cache_dims(c), n_q_heads).part_bytes;
+  *part = plan_decode(cache_dims(c), n_q_heads, kq).part_bytes;
   return CART_OK;
 }
 
-int run_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+int run_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new, int32_t kq,
                int32_t n_q_heads, float scale, void* out, void* ws, void* stream,
                const char* what) {
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)c->d.head_dim);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int r = hip_result(launch_decode(cache_dims(c), n_q_heads, sc, q, k_new, v_new, 0, out,
+  const int r = hip_result(launch_decode(cache_dims(c), n_q_heads, kq, sc, q, k_new, v_new, out,
                                          ws, st),
                            st, what);
   if (r == CART_OK && k_new)
-    for (int s = 0; s < c->d.n_seqs; ++s) c->lens[s] += 1;
+    for (int s = 0; s < c->d.n_seqs; ++s) c->lens[s] += kq;
   return r;
 }
 
@@ -420,15 +644,47 @@ int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_n
                 int32_t n_q_heads, float scale, void* out, void* workspace,
                 size_t workspace_bytes, void* stream) {
   size_t part = 0;
-  CHECK(check_decode(c, q, k_new, v_new, n_q_heads, scale, out, &part));
+  CHECK(check_decode(c, q, k_new, v_new, 1, n_q_heads, scale, out, &part));
   CHECK(check_workspace(workspace, workspace_bytes, part));
-  return run_decode(c, q, k_new, v_new, n_q_heads, scale, out, workspace, stream, "cart_decode");
+  return run_decode(c, q, k_new, v_new, 1, n_q_heads, scale, out, workspace, stream,
+                    "cart_decode");
+}
+
+int cart_decode_verify(cart_cache* c, const void* q, const void* k_new, const void* v_new,
+                       int32_t n_tokens, int32_t n_q_heads, float scale, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new)
+    return fail(CART_ERR_INVALID_ARG, "a verify step appends its rows: k_new and v_new needed");
+  size_t part = 0;
+  CHECK(check_decode(c, q, k_new, v_new, n_tokens, n_q_heads, scale, out, &part));
+  CHECK(check_workspace(workspace, workspace_bytes, part));
+  return run_decode(c, q, k_new, v_new, n_tokens, n_q_heads, scale, out, workspace, stream,
+                    "cart_decode_verify");
+}
+
+size_t cart_decode_verify_workspace_size(const cart_cache* c, int32_t n_tokens,
+                                         int32_t n_q_heads) {
+  if (!c || n_tokens < 1 || n_tokens > 64 || n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0)
+    return 0;
+  return plan_decode(cache_dims(c), n_q_heads, n_tokens).part_bytes;
+}
+
+int cart_cache_truncate(cart_cache* c, int32_t seq, int32_t new_len, void* stream) {
+  CHECK(check_seq(c, seq));
+  if (new_len < 0 || new_len > c->lens[seq])
+    return fail(CART_ERR_INVALID_ARG, "seq %d: new length %d outside [0, %d]", seq, new_len,
+                c->lens[seq]);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int r = hip_result(launch_cache_set_len(cache_dims(c), seq, new_len, st), st,
+                           "cart_cache_truncate");
+  if (r == CART_OK) c->lens[seq] = new_len;
+  return r;
 }
 
 int cart_decode_noalloc(cart_cache* c, const void* q, const void* k_new, const void* v_new,
                         int32_t n_q_heads, float scale, void* out, void* stream) {
   size_t part = 0;
-  CHECK(check_decode(c, q, k_new, v_new, n_q_heads, scale, out, &part));
+  CHECK(check_decode(c, q, k_new, v_new, 1, n_q_heads, scale, out, &part));
   if (part > kDecodeScratchBytes)
     return fail(CART_ERR_WORKSPACE,
                 "cart_decode_noalloc: %zu bytes of split partials exceed the library's "
@@ -440,7 +696,8 @@ int cart_decode_noalloc(cart_cache* c, const void* q, const void* k_new, const v
     if (e != hipSuccess)
       return fail(CART_ERR_HIP, "cart_decode_noalloc: scratch address: %s", hipGetErrorString(e));
   }
-  return run_decode(c, q, k_new, v_new, n_q_heads, scale, out, ws, stream, "cart_decode_noalloc");
+  return run_decode(c, q, k_new, v_new, 1, n_q_heads, scale, out, ws, stream,
+                    "cart_decode_noalloc");
 }
 
 size_t cart_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }

@@ -35,7 +35,6 @@ namespace {
 
 constexpr int kPage = 16;
 constexpr int kDecThreads = 256;
-constexpr int kMaxG = 8;     // q-heads per kv head handled by one workgroup
 constexpr int kUnroll = 4;   // passes per group of loads
 constexpr int kMaxPps = 256; // pages per split at most (a launch plan bound)
 
@@ -72,43 +71,52 @@ __global__ void cache_set_len_kernel(int32_t* seq_lens, int seq, int len) {
   if (threadIdx.x == 0 && blockIdx.x == 0) seq_lens[seq] = len;
 }
 
-// Append one new row per sequence at position seq_len[s], then seq_len += 1.
+// Append kq new rows per sequence at positions seq_len[s] .. seq_len[s] +
+// kq - 1 (rows [s, t, Hkv, D] of k_new/v_new), then seq_len += kq.
 __global__ __launch_bounds__(256) void decode_append_kernel(CacheDims c,
                                                             const bf16* __restrict__ k_new,
-                                                            const bf16* __restrict__ v_new) {
+                                                            const bf16* __restrict__ v_new,
+                                                            int kq) {
   const int s = blockIdx.x;
   const int cpr = c.D / 8;
   const int len = c.seq_lens[s];
   __syncthreads();   // every thread has read the old length
-  const int lp = len / kPage;
-  if (lp < c.max_pages) {
+  for (int e = threadIdx.x; e < kq * c.Hkv * cpr; e += blockDim.x) {
+    const int t = e / (c.Hkv * cpr);
+    const int h = (e / cpr) % c.Hkv;
+    const int chunk = e % cpr;
+    const int row = len + t;
+    const int lp = row / kPage;
+    if (lp >= c.max_pages) continue;
     const int page = c.block_table[(size_t)s * c.max_pages + lp];
-    if (page >= 0 && page < c.n_pages) {
-      for (int e = threadIdx.x; e < c.Hkv * cpr; e += blockDim.x) {
-        const int h = e / cpr;
-        const int chunk = e % cpr;
-        const size_t src = ((size_t)s * c.Hkv + h) * c.D + chunk * 8;
-        const size_t dst = (((size_t)page * c.Hkv + h) * kPage + len % kPage) * c.D + chunk * 8;
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(c.k_pages) + dst) =
-            *reinterpret_cast<const bf16x8*>(k_new + src);
-        *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(c.v_pages) + dst) =
-            *reinterpret_cast<const bf16x8*>(v_new + src);
-      }
-    }
+    if (page < 0 || page >= c.n_pages) continue;
+    const size_t src = (((size_t)s * kq + t) * c.Hkv + h) * c.D + chunk * 8;
+    const size_t dst = (((size_t)page * c.Hkv + h) * kPage + row % kPage) * c.D + chunk * 8;
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(c.k_pages) + dst) =
+        *reinterpret_cast<const bf16x8*>(k_new + src);
+    *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(c.v_pages) + dst) =
+        *reinterpret_cast<const bf16x8*>(v_new + src);
   }
-  if (threadIdx.x == 0) c.seq_lens[s] = len + 1;
+  __syncthreads();   // the old length is read by every thread before it moves
+  if (threadIdx.x == 0) c.seq_lens[s] = len + kq;
 }
 
 struct DecArgs {
   CacheDims c;
-  const bf16* q;
-  bf16* out;
-  float* part;         // [n_seqs][Hq][max_splits][D + 2]: m, l, acc[D]
+  const bf16* q;       // [n_seqs][kq][Hq][D]
+  bf16* out;           // [n_seqs][kq][Hq][D]
+  float* part;         // [n_seqs][kq * Hq][max_splits][D + 2]: m, l, acc[D]
   int Hq, g, pps, max_splits;
+  int kq;              // query tokens per sequence (1: decode; > 1: verify)
+  int n_chunks;        // workgroups per (sequence, kv head, split): query rows / R
   float scale_log2;
 };
 
-template <int D, int G>
+// R query rows per workgroup: rows c R .. c R + R - 1 (chunk c) of the
+// (token, q-head) rows r = t g + j that read kv head kv; token t of a verify
+// step sees the stored rows below len - kq + t + 1 (MASKED; a plain decode
+// step sees every stored row).
+template <int D, int G, bool MASKED>
 __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   constexpr int CPR = D / 8;                 // chunks per row
   constexpr int RPP = kDecThreads / CPR;     // rows per pass
@@ -122,9 +130,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   const int nb = a.max_splits;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int split = lg % nb;
-  const int kv = (lg / nb) % a.c.Hkv;
-  const int s = lg / (nb * a.c.Hkv);
+  const int chunk_id = (lg / nb) % a.n_chunks;
+  const int kv = (lg / (nb * a.n_chunks)) % a.c.Hkv;
+  const int s = lg / (nb * a.n_chunks * a.c.Hkv);
   const int len = a.c.seq_lens[s];
+  const int n_rows = a.kq * a.g;   // query rows of this (sequence, kv head)
   // the sequence's pages in ns nearly equal splits (ns as the merge counts them)
   const int len_c = min(len, a.c.max_pages * kPage);
   const int pages = (len_c + kPage - 1) / kPage;
@@ -137,9 +147,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   // q chunks stay bf16: scores are bf16 x bf16 dot products accumulated in
   // f32 (v_dot2), scaled afterwards.
   bf16x8 qb[G];
+  int lim[G];   // rows below lim[j] are visible to query row j
 #pragma unroll
-  for (int j = 0; j < G; ++j)
-    qb[j] = *reinterpret_cast<const bf16x8*>(a.q + ((size_t)s * a.Hq + kv * a.g + j) * D + chunk * 8);
+  for (int j = 0; j < G; ++j) {
+    const int r = min(chunk_id * G + j, n_rows - 1);
+    const int tok = r / a.g;
+    qb[j] = *reinterpret_cast<const bf16x8*>(
+        a.q + (((size_t)s * a.kq + tok) * a.Hq + kv * a.g + r % a.g) * D + chunk * 8);
+    lim[j] = chunk_id * G + j < n_rows ? len - a.kq + tok + 1 : 0;
+  }
   const float c = a.scale_log2;
   // Online softmax per q-head with a lazily moved reference max m (log2
   // domain): probabilities are exp2(score - m) <= 2^8, and acc, l are
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
   // groups of loads are in flight per thread.
   const bf16* kp = reinterpret_cast<const bf16*>(a.c.k_pages);
   const bf16* vp = reinterpret_cast<const bf16*>(a.c.v_pages);
-  struct Grp { uint4 k[kUnroll], v[kUnroll]; bool ok[kUnroll]; };
+  struct Grp { uint4 k[kUnroll], v[kUnroll]; bool ok[kUnroll]; int row[kUnroll]; };
   // Loads are unconditional, so the wait counts stay exact: a row past the
   // split re-reads the split's last row (a cache hit) and a row on an invalid
   // page reads page 0; both are masked.
@@ -182,6 +198,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       const int rr = min(row, row_end - 1);
       const int page = pg[(rr - row_begin) / kPage];
       x.ok[u] = row < row_end && page >= 0;
+      if constexpr (MASKED) x.row[u] = row;
       const size_t off = (((size_t)max(page, 0) * a.c.Hkv + kv) * kPage + rr % kPage) * D + chunk * 8;
       x.k[u] = *reinterpret_cast<const uint4*>(kp + off);
       x.v[u] = *reinterpret_cast<const uint4*>(vp + off);
@@ -202,7 +219,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
           d = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, d, false);
         }
         d = row_sum<CPR>(d);
-        p[j][u] = x.ok[u] ? d * c : -INFINITY;
+        bool ok = x.ok[u];
+        if constexpr (MASKED) ok = ok && x.row[u] < lim[j];
+        p[j][u] = ok ? d * c : -INFINITY;
       }
     }
 #pragma unroll
@@ -298,7 +317,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
       lt += sl[w][j] * wt;
       at += sacc[w][j][dd] * wt;
     }
-    float* pp = a.part + (((size_t)s * a.Hq + kv * a.g + j) * a.max_splits + split) * (D + 2);
+    const int r = chunk_id * G + j;
+    if (r >= n_rows) continue;
+    const int tok = r / a.g;
+    float* pp = a.part + ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + r % a.g) * a.max_splits +
+                          split) * (D + 2);
     if (dd == 0) { pp[0] = mx; pp[1] = lt; }
     pp[2 + dd] = at;
   }
@@ -307,8 +330,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
 // out[s, h] = sum over the sequence's splits, weighted by exp2(m_split - M).
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
-  const int sh = blockIdx.x;          // s * Hq + h
-  const int s = sh / a.Hq;
+  const int sh = blockIdx.x;          // (s * kq + t) * Hq + h
+  const int s = sh / (a.Hq * a.kq);
   const int lane = threadIdx.x;
   const int len = min(a.c.seq_lens[s], a.c.max_pages * kPage);
   const int pages = (len + kPage - 1) / kPage;
@@ -332,24 +355,39 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   for (int e = 0; e < D / 64; ++e) a.out[(size_t)sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
 }
 
-template <int D, int G>
+template <int D, int G, bool MASKED>
 hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
-  const int grid = a.c.n_seqs * a.c.Hkv * a.max_splits;
-  CART_LAUNCH("decode", (decode_kernel<D, G>), grid, kDecThreads, 0, st, a);
+  const int grid = a.c.n_seqs * a.c.Hkv * a.n_chunks * a.max_splits;
+  CART_LAUNCH("decode", (decode_kernel<D, G, MASKED>), grid, kDecThreads, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.Hq, 64, 0, st, a);
+  CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
   return hipGetLastError();
 }
 
+// Rows per workgroup: the kv head's query rows (g per token, kq tokens), at
+// most 8 (the per-row online-softmax state lives in registers).
+inline int dec_rows(int g, int kq) {
+  const int n = g * kq;
+  return n >= 8 ? 8 : (n >= 4 ? 4 : (n >= 2 ? 2 : 1));
+}
+
 template <int D>
-hipError_t launch_dec_d(const DecArgs& a, hipStream_t st) {
-  switch (a.g) {
-    case 1: return launch_dec_t<D, 1>(a, st);
-    case 2: return launch_dec_t<D, 2>(a, st);
-    case 4: return launch_dec_t<D, 4>(a, st);
-    case 8: return launch_dec_t<D, 8>(a, st);
-    default: return hipErrorInvalidValue;
+hipError_t launch_dec_d(DecArgs a, hipStream_t st) {
+  const int R = dec_rows(a.g, a.kq);
+  a.n_chunks = (a.g * a.kq + R - 1) / R;
+  if (a.kq == 1) {
+    switch (R) {
+      case 1: return launch_dec_t<D, 1, false>(a, st);
+      case 2: return launch_dec_t<D, 2, false>(a, st);
+      case 4: return launch_dec_t<D, 4, false>(a, st);
+      default: return launch_dec_t<D, 8, false>(a, st);
+    }
+  }
+  switch (R) {
+    case 2: return launch_dec_t<D, 2, true>(a, st);
+    case 4: return launch_dec_t<D, 4, true>(a, st);
+    default: return launch_dec_t<D, 8, true>(a, st);
   }
 }
 
@@ -404,8 +442,7 @@ hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_
   return hipGetLastError();
 }
 
-DecodePlan plan_decode(const CacheDims& c, int Hq) {
-  (void)Hq;
+DecodePlan plan_decode(const CacheDims& c, int Hq, int kq) {
   DecodePlan pl{};
   const long long work = (long long)c.n_seqs * c.Hkv * c.max_pages;
   long long pps = (work + 2047) / 2048;
@@ -414,21 +451,20 @@ DecodePlan plan_decode(const CacheDims& c, int Hq) {
   pps = (pps + 3) / 4 * 4;
   pl.pages_per_split = (int)pps;
   pl.max_splits = (int)((c.max_pages + pps - 1) / pps);
-  pl.part_bytes = (size_t)c.n_seqs * Hq * pl.max_splits * (c.D + 2) * sizeof(float);
+  pl.part_bytes = (size_t)c.n_seqs * kq * Hq * pl.max_splits * (c.D + 2) * sizeof(float);
   return pl;
 }
 
-hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
-                         const void* k_new, const void* v_new, int max_len_after, void* out,
-                         void* ws, hipStream_t st) {
-  (void)max_len_after;
+hipError_t launch_decode(const CacheDims& c, int Hq, int kq, float scale, const void* q,
+                         const void* k_new, const void* v_new, void* out, void* ws,
+                         hipStream_t st) {
   if (k_new) {
     CART_LAUNCH("decode_append", (decode_append_kernel), c.n_seqs, 256, 0, st, c,
-                reinterpret_cast<const bf16*>(k_new), reinterpret_cast<const bf16*>(v_new));
+                reinterpret_cast<const bf16*>(k_new), reinterpret_cast<const bf16*>(v_new), kq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const DecodePlan pl = plan_decode(c, Hq);
+  const DecodePlan pl = plan_decode(c, Hq, kq);
   DecArgs a{};
   a.c = c;
   a.q = reinterpret_cast<const bf16*>(q);
@@ -438,6 +474,7 @@ hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
   a.g = Hq / c.Hkv;
   a.pps = pl.pages_per_split;
   a.max_splits = pl.max_splits;
+  a.kq = kq;
   a.scale_log2 = scale * kLog2e;
   return c.D == 128 ? launch_dec_d<128>(a, st) : launch_dec_d<64>(a, st);
 }

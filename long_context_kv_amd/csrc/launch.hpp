@@ -54,6 +54,39 @@ hipError_t launch_rope(void* q, void* k, bool bf16, int B, int S, int Hq, int Hk
                        int pos_base, const int32_t* pos_offsets, double theta, bool inverse,
                        hipStream_t st);
 
+// q/k RMSNorm + RoPE (bwd = false: q_out/k_out = rotate(norm(q_in/k_in));
+// bwd = true: q_out/k_out = input gradients from the output gradients gq/gk).
+hipError_t launch_qk_norm_rope(const void* q_in, const void* k_in, const void* gq,
+                               const void* gk, void* q_out, void* k_out, const float* w_q,
+                               const float* w_k, bool bf16_, int B, int S, int Hq, int Hkv,
+                               int D, float eps, int pos_base, const int32_t* pos_offsets,
+                               double theta, bool bwd, hipStream_t st);
+
+// Adam on n f32 elements (n % 4 == 0), the first `frozen` left unchanged;
+// xb (nullable) receives the bf16 rounding of every updated element.
+hipError_t launch_adam_rows(float* x, const float* g, float* m, float* v, void* xb, size_t n,
+                            size_t frozen, int step, double lr, double b1, double b2,
+                            double eps, hipStream_t st);
+
+// A composed prefix: the parts' row counts, frozen rows, row offsets in the
+// composition and device pointers (passed by value to the kernels).
+constexpr int kMaxParts = 64;
+struct PartTable {
+  int n;
+  int rows[kMaxParts];
+  int frozen[kMaxParts];
+  int off[kMaxParts + 1];
+  const void* k[kMaxParts];
+  const void* v[kMaxParts];
+};
+// Concatenate the parts' K and V rows (row_elems = Hkv * D elements each,
+// f32 or bf16) into k_out/v_out (bf16, or f32 from f32).
+hipError_t launch_compose_rows(const PartTable& t, bool src_bf16, bool dst_bf16, int row_elems,
+                               void* k_out, void* v_out, hipStream_t st);
+// Zero every part's frozen rows of the composed f32 gradients.
+hipError_t launch_zero_frozen(const PartTable& t, int row_elems, float* dk, float* dv,
+                              hipStream_t st);
+
 struct CacheDims {
   int n_seqs, Hkv, D, page, max_pages, n_pages;
   void* k_pages;
@@ -71,10 +104,12 @@ struct DecodePlan {
   int pages_per_split, max_splits;
   size_t part_bytes;
 };
-DecodePlan plan_decode(const CacheDims& c, int Hq);
-hipError_t launch_decode(const CacheDims& c, int Hq, float scale, const void* q,
-                         const void* k_new, const void* v_new, int max_len_after,
-                         void* out, void* ws, hipStream_t st);
+// kq query tokens per sequence: 1 for a decode step, more for a verify step
+// (whose k_new/v_new rows, kq per sequence, are appended first).
+DecodePlan plan_decode(const CacheDims& c, int Hq, int kq);
+hipError_t launch_decode(const CacheDims& c, int Hq, int kq, float scale, const void* q,
+                         const void* k_new, const void* v_new, void* out, void* ws,
+                         hipStream_t st);
 
 // Library-held decode scratch (allocation-free entry point): its size, and
 // its device address on the current device (looked up on first use there).

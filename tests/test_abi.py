@@ -271,3 +271,129 @@ def test_schedule_validation():
     out = C.AttnSchedule()
     assert L.cart_attn_schedule_query(bad, ctypes.byref(out)) == C.CART_ERR_INVALID_ARG
     assert L.cart_attn_schedule_query(ctypes.byref(_shape()), None) == C.CART_ERR_INVALID_ARG
+
+
+def test_qk_norm_rope_validation():
+    f, b = L.cart_qk_norm_rope, L.cart_qk_norm_rope_bwd
+    ok = dict(dt=C.CART_BF16, B=1, S=4, Hq=4, Hkv=2, d=64, eps=1e-6, base=0, offs=None, th=1e6)
+
+    def fw(q=FAKE, k=FAKE, qo=FAKE, ko=FAKE, wq=FAKE, wk=FAKE, **kw):
+        a = dict(ok, **kw)
+        return f(q, k, qo, ko, wq, wk, a["dt"], a["B"], a["S"], a["Hq"], a["Hkv"], a["d"],
+                 a["eps"], a["base"], a["offs"], a["th"], None)
+
+    assert fw(dt=3) == C.CART_ERR_INVALID_ARG
+    assert fw(d=96) == C.CART_ERR_UNSUPPORTED
+    assert fw(eps=0.0) == C.CART_ERR_INVALID_ARG
+    assert fw(th=-1.0) == C.CART_ERR_INVALID_ARG
+    assert fw(base=-3) == C.CART_ERR_INVALID_ARG
+    assert fw(wk=None) == C.CART_ERR_INVALID_ARG          # keys given without their weights
+    assert fw(q=None) == C.CART_ERR_INVALID_ARG
+    assert fw(wq=MIS) == C.CART_ERR_ALIGNMENT
+    assert fw(ko=None) == C.CART_ERR_INVALID_ARG
+    assert fw(offs=FAKE + 2) == C.CART_ERR_ALIGNMENT
+    assert fw(q=None, S=0) == C.CART_OK                   # empty: nothing launched
+    # backward: the input gradient may not overwrite the inputs
+    r = b(FAKE, None, FAKE + 16, None, FAKE, None, FAKE, None, C.CART_BF16, 1, 4, 4, 2, 64,
+          1e-6, 0, None, 1e6, None)
+    assert r == C.CART_ERR_INVALID_ARG and b"overwrite" in L.cart_last_error()
+    r = b(FAKE, None, None, None, FAKE + 16, None, FAKE, None, C.CART_BF16, 1, 4, 4, 2, 64,
+          1e-6, 0, None, 1e6, None)
+    assert r == C.CART_ERR_INVALID_ARG
+
+
+def test_adam_rows_validation():
+    f = L.cart_adam_rows
+
+    def call(rows=FAKE, grad=FAKE, m=FAKE, v=FAKE, xb=None, n=8, e=64, fr=1, t=1, lr=2e-2,
+             b1=0.9, b2=0.999, eps=1e-8):
+        return f(rows, grad, m, v, xb, n, e, fr, t, lr, b1, b2, eps, None)
+
+    assert call(e=6) == C.CART_ERR_UNSUPPORTED
+    assert call(n=-1) == C.CART_ERR_INVALID_ARG
+    assert call(fr=9) == C.CART_ERR_INVALID_ARG
+    assert call(t=0) == C.CART_ERR_INVALID_ARG
+    assert call(lr=-1.0) == C.CART_ERR_INVALID_ARG
+    assert call(b1=1.0) == C.CART_ERR_INVALID_ARG
+    assert call(b2=-0.1) == C.CART_ERR_INVALID_ARG
+    assert call(eps=0.0) == C.CART_ERR_INVALID_ARG
+    assert call(m=None) == C.CART_ERR_INVALID_ARG
+    assert call(xb=MIS) == C.CART_ERR_ALIGNMENT
+    assert call(rows=None, n=0, fr=0) == C.CART_OK         # empty: nothing launched
+
+
+def _parts(rows, frozen, ptr=FAKE):
+    n = len(rows)
+    kp = (ctypes.c_void_p * n)(*[ptr if r else None for r in rows])
+    vp = (ctypes.c_void_p * n)(*[ptr if r else None for r in rows])
+    p = C.Parts(n, (ctypes.c_int32 * n)(*rows), (ctypes.c_int32 * n)(*frozen), kp, vp)
+    p._keep = (kp, vp)
+    return p
+
+
+def test_parts_validation():
+    assert L.cart_parts_rows(ctypes.byref(_parts([3, 0, 5], [1, 0, 2]))) == 8
+    assert L.cart_parts_rows(ctypes.byref(_parts([3, -1], [1, 0]))) == -1
+    assert L.cart_parts_rows(ctypes.byref(_parts([3, 2], [1, 3]))) == -1
+    assert L.cart_parts_rows(ctypes.byref(_parts([1] * 65, [0] * 65))) == -1
+    assert L.cart_parts_rows(None) == -1
+    comp = L.cart_compose_rows
+    assert comp(ctypes.byref(_parts([3, 5], [1, 1])), C.CART_BF16, 2, 64, FAKE, FAKE,
+                C.CART_F32, None) == C.CART_ERR_UNSUPPORTED
+    assert comp(ctypes.byref(_parts([3, 5], [1, 1], ptr=MIS)), C.CART_F32, 2, 64, FAKE, FAKE,
+                C.CART_BF16, None) == C.CART_ERR_ALIGNMENT
+    assert comp(ctypes.byref(_parts([3, 5], [1, 1])), C.CART_F32, 2, 80, FAKE, FAKE,
+                C.CART_BF16, None) == C.CART_ERR_UNSUPPORTED
+    assert comp(ctypes.byref(_parts([3, 5], [1, 1])), C.CART_F32, 2, 64, None, FAKE,
+                C.CART_BF16, None) == C.CART_ERR_INVALID_ARG
+    assert comp(ctypes.byref(_parts([0, 0], [0, 0], ptr=None)), C.CART_F32, 2, 64, None, None,
+                C.CART_BF16, None) == C.CART_OK          # nothing to compose
+    # the composed backward wants the shape's p to be the composed length
+    s = _shape(p=9)
+    r = L.cart_attn_bwd_composed(ctypes.byref(s), ctypes.byref(_parts([3, 5], [1, 1])),
+                                 *([FAKE] * 13), 0, FAKE, 1 << 30, None)
+    assert r == C.CART_ERR_INVALID_ARG and b"parts" in L.cart_last_error()
+
+
+def test_write_composed_cache_refusals():
+    h = ctypes.c_void_p()
+    assert L.cart_cache_create(ctypes.byref(_desc()), ctypes.byref(h)) == C.CART_OK
+    try:
+        w = L.cart_write_composed_cache
+        # 4 pages x 16 rows = 64 rows: 40 + 30 do not fit; nothing is appended
+        assert w(h, 0, ctypes.byref(_parts([40, 30], [1, 1])), C.CART_F32, 2, 64, None) == \
+            C.CART_ERR_CACHE_FULL
+        assert L.cart_cache_seq_len(h, 0) == 0
+        assert w(h, 0, ctypes.byref(_parts([4, 3], [1, 1])), C.CART_F32, 4, 64, None) == \
+            C.CART_ERR_GEOMETRY
+        assert w(h, 0, ctypes.byref(_parts([4, 3], [1, 1], ptr=None)), C.CART_F32, 2, 64,
+                 None) == C.CART_ERR_INVALID_ARG
+        assert w(h, 9, ctypes.byref(_parts([4, 3], [1, 1])), C.CART_F32, 2, 64, None) == \
+            C.CART_ERR_INVALID_ARG
+    finally:
+        L.cart_cache_destroy(h)
+
+
+def test_verify_and_truncate_host_rules():
+    h = ctypes.c_void_p()
+    assert L.cart_cache_create(ctypes.byref(_desc()), ctypes.byref(h)) == C.CART_OK
+    try:
+        ws = L.cart_decode_verify_workspace_size(h, 4, 4)
+        assert ws == 4 * L.cart_decode_workspace_size(h, 4)   # 4 tokens: 4x the partials
+        assert L.cart_decode_verify_workspace_size(h, 0, 4) == 0
+        assert L.cart_decode_verify_workspace_size(h, 65, 4) == 0
+        v = L.cart_decode_verify
+        # drafts are appended: k_new / v_new are required
+        assert v(h, FAKE, None, None, 4, 4, 0.0, FAKE, FAKE, ws, None) == C.CART_ERR_INVALID_ARG
+        assert v(h, FAKE, FAKE, FAKE, 0, 4, 0.0, FAKE, FAKE, ws, None) == C.CART_ERR_INVALID_ARG
+        assert v(h, FAKE, FAKE, FAKE, 4, 3, 0.0, FAKE, FAKE, ws, None) == C.CART_ERR_GEOMETRY
+        assert v(h, FAKE, FAKE, FAKE, 4, 4, 0.0, FAKE, FAKE, ws - 1, None) == C.CART_ERR_WORKSPACE
+        # capacity is 64 rows: 65 drafts at once do not fit (refused as too many)
+        assert v(h, FAKE, FAKE, FAKE, 65, 4, 0.0, FAKE, FAKE, 1 << 30, None) == \
+            C.CART_ERR_INVALID_ARG
+        # truncation only shortens
+        assert L.cart_cache_truncate(h, 0, 1, None) == C.CART_ERR_INVALID_ARG
+        assert L.cart_cache_truncate(h, 0, -1, None) == C.CART_ERR_INVALID_ARG
+        assert L.cart_cache_truncate(h, 7, 0, None) == C.CART_ERR_INVALID_ARG
+    finally:
+        L.cart_cache_destroy(h)

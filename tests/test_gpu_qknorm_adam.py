@@ -1,0 +1,132 @@
+"""GPU parity of the steps either side of the attention -- the fused q/k
+RMSNorm + RoPE (forward and input gradient) and Adam on the cartridge rows --
+through the C ABI against the CPU float64 oracle on the same seeded inputs.
+
+Tolerances: 1e-5 (normwise) for float32 tensors, 2e-2 for bfloat16 ones;
+frozen rows bit for bit unchanged; the bf16 copy written by Adam equal bit
+for bit to the nearest-even rounding of the f32 rows it wrote.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cartattn_oracle as O
+from oracle import qknorm_adam as N
+from long_context_kv_amd import workloads as W
+from tests._common import f64, rel, say
+
+pytestmark = pytest.mark.gpu
+
+TH = W.THETA
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def C():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from long_context_kv_amd import cartattn
+    return cartattn
+
+
+def _norm_inputs(B, S, Hq, Hkv, d, dtype, seed):
+    x = W.train_inputs(W.TrainShape("nr", B, S, 0, Hq, Hkv, d, dtype, dtype, seed))
+    g = torch.Generator().manual_seed(seed + 1)
+    w_q = torch.rand(d, generator=g) + 0.5
+    w_k = torch.rand(d, generator=g) + 0.5
+    # raw projections of a few units of scale; the output gradient
+    return x["q"] * 3, x["k_tok"] * 3, x["dout"], x["v_tok"][:, :, :Hkv], w_q, w_k
+
+
+CASES = [
+    # name, B, S, Hq, Hkv, d, dtype, pos_base, offsets
+    ("bf16-d128", 2, 33, 16, 8, 128, torch.bfloat16, 4096, [0, 1000]),
+    ("f32-d64", 3, 17, 6, 2, 64, torch.float32, 8, [0, 5, 20000]),
+    ("bf16-d64-mha", 1, 40, 4, 4, 64, torch.bfloat16, 0, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_qk_norm_rope_fwd_bwd(C, case):
+    name, B, S, Hq, Hkv, d, dt, base, offs = case
+    tol = 1e-5 if dt == torch.float32 else 2e-2
+    q, k, gq, gk, w_q, w_k = _norm_inputs(B, S, Hq, Hkv, d, dt, 51)
+    q, k = q.to(dt), k.to(dt)
+    gk = gk[:, :, :Hkv].contiguous().to(dt)
+    gq = gq.to(dt)
+    po = torch.tensor(offs, dtype=torch.int32) if offs else None
+    pos = O.token_positions(B, S, base, offs)
+    qd, kd, wqd, wkd = q.cuda(), k.cuda(), w_q.cuda(), w_k.cuda()
+    qo, ko = torch.empty_like(qd), torch.empty_like(kd)
+    say("qk norm rope", name)
+    C.cart_qk_norm_rope(qd, kd, qo, ko, wqd, wkd, base, EPS,
+                        po.cuda() if po is not None else None, TH)
+    dqi, dki = torch.empty_like(qd), torch.empty_like(kd)
+    C.cart_qk_norm_rope_bwd(qd, kd, gq.cuda(), gk.cuda(), dqi, dki, wqd, wkd, base, EPS,
+                            po.cuda() if po is not None else None, TH)
+    torch.cuda.synchronize()
+    assert rel(f64(qo), N.qk_norm_rope(f64(q), f64(w_q), pos, TH, EPS)) <= tol
+    assert rel(f64(ko), N.qk_norm_rope(f64(k), f64(w_k), pos, TH, EPS)) <= tol
+    assert rel(f64(dqi), N.qk_norm_rope_bwd(f64(q), f64(w_q), pos, TH, EPS, f64(gq))) <= tol
+    assert rel(f64(dki), N.qk_norm_rope_bwd(f64(k), f64(w_k), pos, TH, EPS, f64(gk))) <= tol
+    # in place (forward), and the input gradient written over its output gradient
+    C.cart_qk_norm_rope(qd, kd, qd, kd, wqd, wkd, base, EPS,
+                        po.cuda() if po is not None else None, TH)
+    g2 = gq.cuda()
+    C.cart_qk_norm_rope_bwd(q.cuda(), None, g2, None, g2, None, wqd, None, base, EPS,
+                            po.cuda() if po is not None else None, TH)
+    torch.cuda.synchronize()
+    assert torch.equal(qd, qo) and torch.equal(kd, ko)
+    assert torch.equal(g2, dqi)
+
+
+def test_qk_norm_rope_long_cartridge_layer(C):
+    """The long-cartridge layer's token Q/K (4096 tokens behind p = 16384)."""
+    sh = W.LONG
+    q, k, gq, gk, w_q, w_k = _norm_inputs(1, sh.q_seq, sh.n_q_heads, sh.n_kv_heads,
+                                          sh.head_dim, torch.bfloat16, 500)
+    q, k, gq = q.to(torch.bfloat16), k.to(torch.bfloat16), gq.to(torch.bfloat16)
+    gk = gk.contiguous().to(torch.bfloat16)
+    pos = O.token_positions(1, sh.q_seq, sh.p)
+    qd, kd = q.cuda(), k.cuda()
+    qo, ko = torch.empty_like(qd), torch.empty_like(kd)
+    dqi, dki = torch.empty_like(qd), torch.empty_like(kd)
+    say("qk norm rope, long-cartridge layer")
+    C.cart_qk_norm_rope(qd, kd, qo, ko, w_q.cuda(), w_k.cuda(), sh.p, EPS, None, TH)
+    C.cart_qk_norm_rope_bwd(qd, kd, gq.cuda(), gk.cuda(), dqi, dki, w_q.cuda(), w_k.cuda(),
+                            sh.p, EPS, None, TH)
+    torch.cuda.synchronize()
+    assert rel(f64(qo), N.qk_norm_rope(f64(q), f64(w_q), pos, TH, EPS)) <= 2e-2
+    assert rel(f64(ko), N.qk_norm_rope(f64(k), f64(w_k), pos, TH, EPS)) <= 2e-2
+    assert rel(f64(dqi), N.qk_norm_rope_bwd(f64(q), f64(w_q), pos, TH, EPS, f64(gq))) <= 2e-2
+    assert rel(f64(dki), N.qk_norm_rope_bwd(f64(k), f64(w_k), pos, TH, EPS, f64(gk))) <= 2e-2
+
+
+@pytest.mark.parametrize("rows,hkv,d,frozen,lr", [(16384, 8, 128, 1, 2e-2),
+                                                  (37, 2, 64, 3, 2e-3),
+                                                  (5, 1, 64, 0, 2e-2)],
+                         ids=["long-cartridge", "ragged-f3", "no-frozen"])
+def test_adam_rows(C, rows, hkv, d, frozen, lr):
+    g = torch.Generator().manual_seed(rows + d)
+    x0 = torch.randn(rows, hkv, d, generator=g)
+    xd = x0.cuda()
+    m = torch.zeros_like(xd)
+    v = torch.zeros_like(xd)
+    xb = torch.empty(rows, hkv, d, dtype=torch.bfloat16, device="cuda")
+    xr, mr, vr = f64(x0), np.zeros(x0.shape), np.zeros(x0.shape)
+    for t in range(1, 4):
+        gr = torch.randn(rows, hkv, d, generator=g)
+        x_prev = xd.clone()
+        say("adam", rows, "step", t)
+        C.cart_adam_rows(xd, gr.cuda(), m, v, t, lr, frozen_rows=frozen, rows_bf16=xb)
+        torch.cuda.synchronize()
+        xr, mr, vr = N.adam_step(xr, f64(gr), mr, vr, t, lr, frozen_rows=frozen)
+        assert rel(f64(xd), xr) <= 1e-5 and rel(f64(m), mr) <= 1e-5 and rel(f64(v), vr) <= 1e-5
+        dx = f64(xd) - f64(x_prev)
+        dref = xr - f64(x_prev)
+        assert rel(dx[frozen:], dref[frozen:]) <= 1e-4
+        assert torch.equal(xd[:frozen].cpu(), x0[:frozen])
+        assert not bool(m[:frozen].any()) and not bool(v[:frozen].any())
+        assert np.array_equal(f64(xb), O.round_bf16(xd.cpu().numpy()))
+        xr = f64(xd)            # follow the GPU's f32 rows from here on
