@@ -68,7 +68,14 @@ typedef struct {
   float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim) */
   cart_dtype tok_dtype; /* Q, token K/V, O, dO, dQ, token dK/dV */
   cart_dtype row_dtype; /* cartridge K/V storage (f32 master rows or bf16) */
+  int32_t window;       /* 0: none; W > 0: sliding window, see below */
 } cart_attn_shape;
+/* Sliding window (local attention layers, e.g. gemma4's; Cartridges guide,
+   section "gemma4 (measured)": such layers see the cartridge exactly as a
+   real prefix, within the window, and the window may cut through it):
+   the query of token i, at position p + i, sees only the rows at positions
+   above p + i - W (cartridge row j is at position j, token row t at p + t),
+   itself included. W >= p + q_seq is the same as no window. */
 /* Supported dtype pairs: (tok F32, rows F32) is the float32 reference mode
    (all arithmetic in f32); (tok BF16, rows F32 or BF16) is the bf16 mode:
    MFMA operands are bf16 (f32 rows are rounded to nearest-even on load),
@@ -183,7 +190,7 @@ size_t cart_attn_workspace_size(const cart_attn_shape* s, int32_t for_backward);
  *
  * For query i of (b, h) and concatenated row j in [0, p + q_seq):
  *   key_j = k_cart[j, h/g] if j < p else k_tok[b, j - p, h/g] (same for V);
- *   row j is visible iff j <= i + p;
+ *   row j is visible iff j <= i + p (and, with a window W, j > i + p - W);
  *   out[b,i,h] = sum_j softmax_j(scale * q[b,i,h] . key_j) v_j;
  *   lse[b,h,i] = log sum_j exp(scale * q[b,i,h] . key_j)   (visible j).
  * The concat is virtual: the two row sources are read in place.

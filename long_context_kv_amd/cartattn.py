@@ -59,6 +59,7 @@ class AttnShape(ctypes.Structure):
         ("frozen_rows", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("scale", ctypes.c_float), ("tok_dtype", ctypes.c_int), ("row_dtype", ctypes.c_int),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -174,12 +175,13 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def attn_shape(q: torch.Tensor, k_tok: torch.Tensor, p: int, frozen_rows: int = 1,
-               scale: float = 0.0, row_dtype: Optional[torch.dtype] = None) -> AttnShape:
+               scale: float = 0.0, row_dtype: Optional[torch.dtype] = None,
+               window: int = 0) -> AttnShape:
     """Shape struct from Q [B, n, Hq, d] and token K [B, n, Hkv, d]."""
     B, n, Hq, d = q.shape
     Hkv = k_tok.shape[2]
     rd = _DTYPES[row_dtype] if row_dtype is not None else _dt(q)
-    return AttnShape(B, n, p, frozen_rows, Hq, Hkv, d, scale, _dt(q), rd)
+    return AttnShape(B, n, p, frozen_rows, Hq, Hkv, d, scale, _dt(q), rd, window)
 
 
 # ---------------------------------------------------------------- raw calls
@@ -311,11 +313,11 @@ def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def attn_fwd(q, k_tok, v_tok, k_cart, v_cart, frozen_rows: int = 1, scale: float = 0.0,
-             stream=None):
+             stream=None, window: int = 0):
     """Allocate O, LSE and the workspace, run cart_attn_fwd, return (O, LSE)."""
     p = 0 if k_cart is None else k_cart.shape[0]
     rd = k_cart.dtype if k_cart is not None else q.dtype
-    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd)
+    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd, window)
     out = torch.empty_like(q)
     B, n, Hq, _ = q.shape
     lse = torch.empty(B, Hq, n, dtype=torch.float32, device=q.device)
@@ -326,14 +328,14 @@ def attn_fwd(q, k_tok, v_tok, k_cart, v_cart, frozen_rows: int = 1, scale: float
 
 def attn_bwd(q, k_tok, v_tok, k_cart, v_cart, out, lse, dout, frozen_rows: int = 1,
              scale: float = 0.0, dk_cart=None, dv_cart=None, accumulate_cart: bool = False,
-             stream=None):
+             stream=None, window: int = 0):
     """Allocate gradients and workspace, run cart_attn_bwd.
 
     Returns (dq, dk_tok, dv_tok, dk_cart, dv_cart); cartridge gradients are
     float32 [p, Hkv, d] (the given buffers when passed)."""
     p = 0 if k_cart is None else k_cart.shape[0]
     rd = k_cart.dtype if k_cart is not None else q.dtype
-    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd)
+    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd, window)
     dq = torch.empty_like(q)
     dk_tok = torch.empty_like(k_tok)
     dv_tok = torch.empty_like(v_tok)

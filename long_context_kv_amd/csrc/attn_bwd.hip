@@ -79,12 +79,14 @@ struct BwdArgs {
   bf16x4* cast_vb;
   size_t cast_n4;
   int kv_target, kv_ptok, kv_stmax, q_splits;
+  int kv_cart_pieces;         // dK/dV pieces of the cartridge tiles of one kv head
   int D4;             // head_dim / 4
   int B, n, p, f, Hq, Hkv, g;
   int n_ct, n_tt, nqt, splits_c;
   int hpw, wph, n_hg, n_qb;   // query-major grid of the dQ kernel
   int zero_dq;                // preprocess clears the f32 dQ accumulator
   int accumulate;
+  int window;                 // > 0: sliding window (positions above p + i - window)
   float scale, scale_log2;
 };
 
@@ -324,7 +326,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int qq = d_row(r, hl);
       const int i = i0 + qq;
-      const bool vis = key_ok && (cart || my_key <= i);   // i >= n has lse2 = +inf
+      bool vis = key_ok && (cart || my_key <= i);   // i >= n has lse2 = +inf
+      if (a.window > 0) vis = vis && ((cart ? my_key : a.p + my_key) > i + a.p - a.window);
       const float pv = vis ? exp2f(s[r] * a.scale_log2 - lse2s[qq]) : 0.f;
       s[r] = pv;                                  // P
       dp[r] = pv * (dp[r] + dls[qq]);             // dS (unscaled)
@@ -463,32 +466,62 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
 
   // ---- work item: a piece of one key tile's unit list (pieces of cartridge
   // tiles first, then the pieces of the token tiles, tile-major)
-  const int per_kv = a.n_ct * a.splits_c + a.B * a.kv_ptok;
+  // Query tiles [qt0, qt_hi) of a key tile that hold a query seeing one of
+  // its rows: all of them, or with a sliding window those below the last
+  // row's window end (position + window - p).
+  auto tile_qt_hi = [&](bool c_, int t_) -> int {
+    if (a.window <= 0) return a.nqt;
+    const int last = min(t_ * kBNB + kBNB - 1, (c_ ? a.p : a.n) - 1);
+    const int hi = (c_ ? last - a.p : last) + a.window;   // queries below hi see it
+    return max(0, min(a.nqt, (hi + kBQ - 1) / kBQ));
+  };
+  const int per_kv = a.kv_cart_pieces + a.B * a.kv_ptok;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int kv = lg / per_kv;
   int r0 = lg % per_kv;
-  const bool cart = r0 < a.n_ct * a.splits_c;
-  int tile, split = 0, n_split = 1, b = 0, u_begin, u_end;
-  if (cart) {
+  const bool cart = r0 < a.kv_cart_pieces;
+  int tile, split = 0, n_split = 1, b = 0, u_begin, u_end, qt_hi;
+  if (cart && a.window <= 0) {
     // split-major: the workgroups that run together (consecutive ids on one
     // XCD) read the same window of units, so their Q / dO copies share the L2
     split = r0 / a.n_ct;
     tile = r0 % a.n_ct;
     n_split = a.splits_c;
+    qt_hi = a.nqt;
     const int U = a.B * a.g * a.nqt;
     u_begin = (int)((long long)split * U / a.splits_c);
     u_end = (int)((long long)(split + 1) * U / a.splits_c);
+  } else if (cart) {
+    // sliding window: the cartridge tiles see different query ranges, so
+    // their pieces are dealt tile-major (a tile no query sees: one piece
+    // with no units, which writes its zero gradient)
+    tile = 0;
+    qt_hi = tile_qt_hi(true, 0);
+    int U = a.B * a.g * qt_hi;
+    n_split = max(1, (U + a.kv_target - 1) / a.kv_target);
+    while (r0 >= n_split) {
+      r0 -= n_split;
+      ++tile;
+      qt_hi = tile_qt_hi(true, tile);
+      U = a.B * a.g * qt_hi;
+      n_split = max(1, (U + a.kv_target - 1) / a.kv_target);
+    }
+    split = r0;
+    u_begin = (int)((long long)split * U / n_split);
+    u_end = (int)((long long)(split + 1) * U / n_split);
   } else {
     // token pieces tile-major (the larger tiles, nearer the start, first),
     // then by batch, then by piece
-    r0 -= a.n_ct * a.splits_c;
+    r0 -= a.kv_cart_pieces;
     tile = 0;
-    int ut = a.g * a.nqt;
+    qt_hi = tile_qt_hi(false, 0);
+    int ut = a.g * qt_hi;
     n_split = (ut + a.kv_target - 1) / a.kv_target;
     while (r0 >= a.B * n_split) {
       r0 -= a.B * n_split;
       ++tile;
-      ut = a.g * (a.nqt - tile * (kBNB / kBQ));
+      qt_hi = tile_qt_hi(false, tile);
+      ut = a.g * (qt_hi - tile * (kBNB / kBQ));
       n_split = (ut + a.kv_target - 1) / a.kv_target;
     }
     b = r0 / n_split;
@@ -505,10 +538,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
                            : reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
   const bf16* vbase = cart ? reinterpret_cast<const bf16*>(a.v_cart) + kv * D
                            : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
-  // Queries i visible to this lane's key: lo <= i < n (an empty range for a
-  // key past the end of its rows).
+  // Queries i visible to this lane's key: lo <= i < hi (an empty range for a
+  // key past the end of its rows); hi is n, or with a sliding window the
+  // key's window end.
   const int vis_lo = !key_ok ? a.n : (cart ? 0 : my_key);
-  const uint32_t vis_span = (uint32_t)(a.n - vis_lo);
+  const int vis_hi = a.window > 0 ? min(a.n, (cart ? my_key - a.p : my_key) + a.window) : a.n;
+  const uint32_t vis_span = (uint32_t)max(0, vis_hi - vis_lo);
 
   // ---- unit cursor: (batch, q-head of the group, query tile) and the
   // offsets of its Q / dO rows (bytes) and of its lse / D (elements); within
@@ -523,19 +558,22 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     x.loff = ((size_t)x.bb * a.Hq + h) * a.n + (size_t)x.qt * kBQ;
   };
   Unit cu;
+  // query tiles per (batch, head) of this key tile (at least 1 for the
+  // division; a tile without units never follows its cursor)
+  const int nq = max(1, qt_hi - qt0);
   if (cart) {
-    cu.bb = u_begin / (a.g * a.nqt);
-    cu.hin = (u_begin / a.nqt) % a.g;
-    cu.qt = u_begin % a.nqt;
+    cu.bb = u_begin / (a.g * nq);
+    cu.hin = (u_begin / nq) % a.g;
+    cu.qt = u_begin % nq;
   } else {
-    const int nq = a.nqt - qt0;
     cu.bb = b;
     cu.hin = u_begin / nq;
     cu.qt = qt0 + u_begin % nq;
   }
   locate_unit(cu);
+  const int qt_end = qt0 + nq;
   auto next = [&](Unit x) {
-    if (++x.qt == a.nqt) {
+    if (++x.qt == qt_end) {
       x.qt = qt0;
       if (++x.hin == a.g) { x.hin = 0; ++x.bb; }
       locate_unit(x);
@@ -550,7 +588,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const bool mask_all = j0 + kBNB > limit;
   const int q_full = a.n / kBQ;                          // first ragged query tile
   const int q_diag = cart ? 0 : qt0 + kBNB / kBQ;        // first tile past the diagonal
-  auto needs_mask = [&](int qt) { return mask_all || qt >= q_full || qt < q_diag; };
+  // with a sliding window, the first query past the window of the tile's
+  // first row (later queries lose rows of the tile)
+  const int q_win = a.window > 0 ? (cart ? j0 - a.p : j0) + a.window : (1 << 30);
+  auto needs_mask = [&](int qt) {
+    return mask_all || qt >= q_full || qt < q_diag || qt * kBQ + kBQ > q_win;
+  };
 
   // ---- this wave's copies of a unit: copy o = wave + 8 i of the list
   // (Q blocks, dO blocks, lse halves, -D halves). Rows past the unit's last
@@ -810,7 +853,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     lds_barrier_waited();
     run(Yes{}, No{}, copy_setup(uc, sc, AHEAD < nu));
     uc = next(uc);
-    qs = qs + 1 == a.nqt ? qt0 : qs + 1;
+    qs = qs + 1 == qt_end ? qt0 : qs + 1;
     rotate();
     // j = 1 .. nu-1: unit j (phase A) and unit j-1 (phase B)
     for (int j = 1; j < nu; ++j) {
@@ -818,7 +861,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       lds_barrier_waited();
       run(Yes{}, Yes{}, copy_setup(uc, sc, j + AHEAD < nu));
       uc = next(uc);
-      qs = qs + 1 == a.nqt ? qt0 : qs + 1;
+      qs = qs + 1 == qt_end ? qt0 : qs + 1;
       rotate();
     }
     // j = nu: phase B of unit nu-1 (its stage landed before step nu-1)
@@ -982,9 +1025,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
   const int n_ct = (a.p + kKvTile - 1) / kKvTile;
   const int nt_all = n_ct + wg_last / kKvTile + 1;
-  // this workgroup's contiguous range of key tiles
-  const int t_begin = (int)((long long)split * nt_all / a.q_splits);
-  const int t_end = (int)((long long)(split + 1) * nt_all / a.q_splits);
+  // this workgroup's contiguous range of key tiles (with a sliding window,
+  // from the first tile its earliest query can see)
+  const int t_lo = first_window_tile(a.window, qb * a.wph * 32, a.p, n_ct);
+  const int t_begin = t_lo + (int)((long long)split * (nt_all - t_lo) / a.q_splits);
+  const int t_end = t_lo + (int)((long long)(split + 1) * (nt_all - t_lo) / a.q_splits);
+  // first position the wave's first query sees (no window: far below 0)
+  const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
   const KvMap<D> kmap(wave, lane);
@@ -1063,19 +1110,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     // dS^T / scale = P (dP - D) (the scale is applied to dQ at the end);
-    // key k = 32 kh + d_row(r, hl) is visible iff
-    // k < lim (its row exists and, for a token tile, it is not after the
-    // query).
+    // key k = 32 kh + d_row(r, hl) is visible iff lo <= k < lim (its row
+    // exists and, for a token tile, it is not after the query; with a
+    // sliding window, it is not before the query's window).
     // (one branch for the whole tile: tiles that need no mask skip it)
-    if (f.rows < kKvTile || (!f.cart && f.j0 + kKvTile - 1 > i0)) {
+    if (f.rows < kKvTile || (!f.cart && f.j0 + kKvTile - 1 > i0) || f.abs0 < win_lo + 31) {
       const int lim = f.cart ? f.rows : min(f.rows, my_i - f.j0 + 1);
       const int lim_l = lim - 4 * hl;
+      const int lo_l = win_lo + (my_i - i0) - f.abs0 - 4 * hl;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kc = 32 * kh + (r & 3) + 8 * (r >> 2);   // key minus 4 hl
-          s[kh][r] = kc < lim_l ? s[kh][r] : -INFINITY;
+          s[kh][r] = (kc < lim_l && kc >= lo_l) ? s[kh][r] : -INFINITY;
         }
     }
 #pragma unroll
@@ -1128,7 +1176,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
-      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(lds_addr(K0), lds_addr(V0), f);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
+        compute(lds_addr(K0), lds_addr(V0), f);
     }
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
@@ -1137,7 +1186,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
-      if (wave_active && (f.cart || f.j0 <= i0 + 31)) compute(lds_addr(K1), lds_addr(V1), f);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
+        compute(lds_addr(K1), lds_addr(V1), f);
     }
   }
 
@@ -1283,7 +1333,8 @@ BwdPlan plan_bwd(const AttnDims& d) {
   thread_local int next_slot = 0;
   auto same = [](const AttnDims& x, const AttnDims& y) {
     return x.B == y.B && x.n == y.n && x.p == y.p && x.f == y.f && x.Hq == y.Hq &&
-           x.Hkv == y.Hkv && x.D == y.D && x.tok_bf16 == y.tok_bf16 && x.row_bf16 == y.row_bf16;
+           x.Hkv == y.Hkv && x.D == y.D && x.tok_bf16 == y.tok_bf16 && x.row_bf16 == y.row_bf16 &&
+           x.window == y.window;
   };
   for (const Entry& e : cache)
     if (e.used && same(e.d, d)) return e.pl;
@@ -1321,21 +1372,40 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   // candidate with the smallest modelled finish time wins, the largest T
   // among equals.
   {
-    const long long t_max = std::max(U, tok_units(0));   // every tile one piece
+    // query tiles below qt_hi(t) see a row of key tile t (all, or with a
+    // sliding window those below the window end of the tile's last row)
+    auto qt_hi = [&](bool c, int t) -> long long {
+      if (d.window <= 0) return pl.nqt;
+      const long long last = std::min<long long>((long long)t * kBNB + kBNB - 1, (c ? d.p : d.n) - 1);
+      const long long hi = (c ? last - d.p : last) + d.window;
+      return std::max(0LL, std::min<long long>(pl.nqt, (hi + kBQ - 1) / kBQ));
+    };
+    auto cart_units = [&](int t) { return (long long)d.B * g * qt_hi(true, t); };
+    auto tok_units_w = [&](int t) { return (long long)g * (qt_hi(false, t) - t * (kBNB / kBQ)); };
+    const bool windowed = d.window > 0;
+    long long t_max = 0;   // every tile one piece
+    for (int t = 0; t < pl.n_ct; ++t) t_max = std::max(t_max, cart_units(t));
+    for (int t = 0; t < pl.n_tt; ++t) t_max = std::max(t_max, tok_units_w(t));
+    t_max = std::max(t_max, 1LL);
     const int slots = 32;   // one dK/dV workgroup per CU
     auto finish = [&](long long T) {
       std::vector<std::pair<long long, long long>> pieces;   // (units, pieces of its tile)
-      auto tile = [&](long long u) {
-        const long long ns = (u + T - 1) / T;
+      auto tile = [&](long long u, bool at_least_one) {
+        long long ns = (u + T - 1) / T;
+        if (at_least_one && ns < 1) ns = 1;
         for (long long i = 0; i < ns; ++i) pieces.emplace_back((i + 1) * u / ns - i * u / ns, ns);
       };
       for (int kv = 0; kv < d.Hkv; ++kv) {
-        // cartridge tiles split-major (every tile has the same pieces)
-        const long long ns = (U + T - 1) / T;
-        for (long long i = 0; i < ns; ++i)
-          for (int c = 0; c < pl.n_ct; ++c) pieces.emplace_back((i + 1) * U / ns - i * U / ns, ns);
+        if (!windowed) {
+          // cartridge tiles split-major (every tile has the same pieces)
+          const long long ns = (U + T - 1) / T;
+          for (long long i = 0; i < ns; ++i)
+            for (int c = 0; c < pl.n_ct; ++c) pieces.emplace_back((i + 1) * U / ns - i * U / ns, ns);
+        } else {
+          for (int c = 0; c < pl.n_ct; ++c) tile(cart_units(c), true);
+        }
         for (int t = 0; t < pl.n_tt; ++t)
-          for (int b = 0; b < d.B; ++b) tile(tok_units(t));
+          for (int b = 0; b < d.B; ++b) tile(tok_units_w(t), false);
       }
       const size_t G = pieces.size(), q = G / 8, r = G % 8;
       double worst = 0.0;
@@ -1364,12 +1434,27 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
       if (f < best - 1e-9) { best = f; T = c; }
     }
     pl.kv_target = (int)T;
-    pl.kv_splits_c = pl.n_ct > 0 ? (int)((U + T - 1) / T) : 1;
-    int ptok = 0;
-    for (int t = 0; t < pl.n_tt; ++t) ptok += (int)((tok_units(t) + T - 1) / T);
+    if (!windowed) {
+      pl.kv_splits_c = pl.n_ct > 0 ? (int)((U + T - 1) / T) : 1;
+      pl.kv_cart_pieces = pl.n_ct * pl.kv_splits_c;
+    } else {
+      pl.kv_splits_c = 1;
+      pl.kv_cart_pieces = 0;
+      for (int t = 0; t < pl.n_ct; ++t) {
+        const int ns = std::max(1, (int)((cart_units(t) + T - 1) / T));
+        pl.kv_splits_c = std::max(pl.kv_splits_c, ns);
+        pl.kv_cart_pieces += ns;
+      }
+    }
+    int ptok = 0, stmax = 1;
+    for (int t = 0; t < pl.n_tt; ++t) {
+      const int ns = (int)((tok_units_w(t) + T - 1) / T);
+      ptok += ns;
+      stmax = std::max(stmax, ns);
+    }
     pl.kv_ptok = ptok;
-    pl.kv_stmax = pl.n_tt > 0 ? (int)((tok_units(0) + T - 1) / T) : 1;
-    pl.grid_kv = d.Hkv * (pl.n_ct * pl.kv_splits_c + d.B * ptok);
+    pl.kv_stmax = pl.n_tt > 0 ? stmax : 1;
+    pl.grid_kv = d.Hkv * (pl.kv_cart_pieces + d.B * ptok);
     if (d.tok_bf16 && pl.kv_stmax > 1)
       pl.tok_part_bytes =
           (size_t)pl.kv_stmax * d.B * pl.n_tt * kBNB * d.Hkv * d.D * sizeof(float);
@@ -1504,6 +1589,8 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.splits_c = d.tok_bf16 ? pl.kv_splits_c : pl.splits_c;
   a.kv_target = pl.kv_target; a.kv_ptok = pl.kv_ptok; a.kv_stmax = pl.kv_stmax;
   a.q_splits = pl.q_splits;
+  a.kv_cart_pieces = pl.kv_cart_pieces;
+  a.window = d.window;
   a.D4 = d.D / 4;
   a.accumulate = accumulate ? 1 : 0;
   a.scale = d.scale;

@@ -50,6 +50,7 @@ struct FwdArgs {
   float* lse_part;
   int B, n, p, Hq, Hkv, g;
   int hpw, wph, n_hg, n_qb, n_splits;
+  int window;          // > 0: sliding window (positions above p + i - window)
   float scale_log2;
 };
 
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
         const int key = 32 * kh + d_row(r, hl);
         bool vis = key < rows;
         if (diag) vis = vis && (j0 + key <= my_i);
+        if (a.window > 0) vis = vis && ((cart ? j0 : a.p + j0) + key > my_i + a.p - a.window);
         const float v = vis ? s[kh][r] * a.scale_log2 : -INFINITY;
         s[kh][r] = v;
         mx = fmaxf(mx, v);
@@ -306,7 +308,7 @@ template <int D>
 __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const KvTile& f,
                                             const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
                                             float& m_ref, float& l_run, float c, int i0,
-                                            int my_i, int lane) {
+                                            int my_i, int lane, int win_lo) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -364,17 +366,20 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
     });
   };
   rdv(std::integral_constant<int, 0>{}, 0);
-  // Mask: key k = 32 kh + d_row(r, hl) of the tile is visible iff k < lim
-  // (its row exists and, for a token tile, it is not after the query).
-  if (f.rows < kBN || (!f.cart && f.j0 + kBN - 1 > i0)) {
+  // Mask: key k = 32 kh + d_row(r, hl) of the tile is visible iff lo <= k <
+  // lim (its row exists and, for a token tile, it is not after the query;
+  // with a sliding window, it is not before the window of the query, whose
+  // first visible position is win_lo + my_i - i0 for this lane).
+  if (f.rows < kBN || (!f.cart && f.j0 + kBN - 1 > i0) || f.abs0 < win_lo + 31) {
     const int lim = f.cart ? f.rows : min(f.rows, my_i - f.j0 + 1);
     const int lim_l = lim - 4 * hl;
+    const int lo_l = win_lo + (my_i - i0) - f.abs0 - 4 * hl;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kc = 32 * kh + (r & 3) + 8 * (r >> 2);   // key minus 4 hl
-        s[kh][r] = kc < lim_l ? s[kh][r] : -INFINITY;
+        s[kh][r] = (kc < lim_l && kc >= lo_l) ? s[kh][r] : -INFINITY;
       }
   }
   float mx = -INFINITY;
@@ -462,8 +467,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
   const int n_ct = (a.p + kBN - 1) / kBN;
   const int nt = n_ct + wg_last / kBN + 1;
-  const int t_begin = (int)((long long)split * nt / a.n_splits);
-  const int t_end = (int)((long long)(split + 1) * nt / a.n_splits);
+  // with a sliding window the tiles before the workgroup's first window are
+  // skipped; the rest are split between the key-split workgroups
+  const int t_lo = first_window_tile(a.window, qb * a.wph * 32, a.p, n_ct);
+  const int t_begin = t_lo + (int)((long long)split * (nt - t_lo) / a.n_splits);
+  const int t_end = t_lo + (int)((long long)(split + 1) * (nt - t_lo) / a.n_splits);
+  // first position the wave's first query sees (no window: far below 0)
+  const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
   const KvMap<D> kmap(wave, lane);
@@ -495,8 +505,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
     {
       const KvTile f = kv_tile(t, n_ct, a.p, a.n);
-      if (wave_active && (f.cart || f.j0 <= i0 + 31))
-        fwd_compute<D>(lds_addr(K0), lds_addr(V0), f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
+        fwd_compute<D>(lds_addr(K0), lds_addr(V0), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
+                       win_lo);
     }
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
@@ -505,8 +516,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
-      if (wave_active && (f.cart || f.j0 <= i0 + 31))
-        fwd_compute<D>(lds_addr(K1), lds_addr(V1), f, qf, acc, m_ref, l_run, c, i0, my_i, lane);
+      if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
+        fwd_compute<D>(lds_addr(K1), lds_addr(V1), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
+                       win_lo);
     }
   }
 
@@ -659,6 +671,7 @@ hipError_t launch_fwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.lse_part = reinterpret_cast<float*>(w + align256(pl.o_part_bytes));
   a.B = d.B; a.n = d.n; a.p = d.p; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
   a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb; a.n_splits = pl.n_splits;
+  a.window = d.window;
   a.scale_log2 = d.scale * kLog2e;
   if (d.tok_bf16)
     return d.D == 128 ? launch_fwd_bf16<128>(a, pl, st) : launch_fwd_bf16<64>(a, pl, st);

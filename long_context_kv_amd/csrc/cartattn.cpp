@@ -72,6 +72,7 @@ int check_shape(const cart_attn_shape* s) {
     return fail(CART_ERR_INVALID_ARG, "unknown dtype");
   if (s->tok_dtype == CART_F32 && s->row_dtype != CART_F32)
     return fail(CART_ERR_UNSUPPORTED, "f32 tokens need f32 cartridge rows");
+  if (s->window < 0) return fail(CART_ERR_INVALID_ARG, "window (%d) must be >= 0", s->window);
   const long long qe = (long long)s->batch * s->q_seq * s->n_q_heads * s->head_dim;
   const long long ce = (long long)s->p * s->n_kv_heads * s->head_dim;
   if (qe > kMaxElems || ce > kMaxElems)
@@ -88,6 +89,8 @@ AttnDims dims_of(const cart_attn_shape* s) {
   d.scale = s->scale > 0.f ? s->scale : 1.0f / sqrtf((float)s->head_dim);
   d.tok_bf16 = s->tok_dtype == CART_BF16;
   d.row_bf16 = s->row_dtype == CART_BF16;
+  // a window reaching every row is no window (one plan, one code path)
+  d.window = (s->window > 0 && (long long)s->window < (long long)s->p + s->q_seq) ? s->window : 0;
   return d;
 }
 

@@ -10,9 +10,11 @@ namespace cartattn {
 constexpr int kKvTile = 64;   // rows per key tile of the query-major kernels
 
 // Tile t of one (batch, kv head): tiles [0, n_ct) hold cartridge rows, the
-// rest hold real tokens; j0 is the tile's first row in its own source.
+// rest hold real tokens; j0 is the tile's first row in its own source and
+// abs0 its position in the concatenation (cartridge row j at j, token i at
+// p + i).
 struct KvTile {
-  int j0, rows;
+  int j0, rows, abs0;
   bool cart;
 };
 
@@ -21,7 +23,18 @@ __device__ __forceinline__ KvTile kv_tile(int t, int n_ct, int p, int n) {
   f.cart = t < n_ct;
   f.j0 = f.cart ? t * kKvTile : (t - n_ct) * kKvTile;
   f.rows = f.cart ? min(kKvTile, p - f.j0) : min(kKvTile, n - f.j0);
+  f.abs0 = f.cart ? f.j0 : p + f.j0;
   return f;
+}
+
+// Sliding window (window > 0): the query at position p + i sees the rows at
+// positions above p + i - window. First tile holding a row that the query at
+// position p + i0 (the earliest of a workgroup) can see.
+__device__ __forceinline__ int first_window_tile(int window, int i0, int p, int n_ct) {
+  if (window <= 0) return 0;
+  const int a = p + i0 - window + 1;   // first visible position
+  if (a <= 0) return 0;
+  return a < p ? a / kKvTile : n_ct + (a - p) / kKvTile;
 }
 
 // Bases of one (batch, kv head)'s rows; consecutive rows are Hkv*D apart.

@@ -15,6 +15,7 @@ struct AttnDims {
   float scale;          // resolved softmax scale (never 0)
   bool tok_bf16;        // token tensors are bf16 (else f32)
   bool row_bf16;        // cartridge rows are bf16 (else f32)
+  int window;           // > 0: sliding window of positions (0: none)
 };
 
 // Forward launch plan; the workspace size and the launch both derive from it.
@@ -35,6 +36,7 @@ struct BwdPlan {
   // into ceil(units_t / kv_target)); kv_ptok pieces per (kv head, batch) of
   // token tiles, at most kv_stmax per token tile.
   int kv_target, kv_splits_c, kv_ptok, kv_stmax, grid_kv;
+  int kv_cart_pieces;   // dK/dV pieces of one kv head's cartridge tiles
   int hpw, wph, n_hg, n_qb, q_splits, grid_q;     // query-major dQ kernel
   size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes, tok_part_bytes, dq_part_bytes, cnt_bytes;
 };

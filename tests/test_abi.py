@@ -397,3 +397,17 @@ def test_verify_and_truncate_host_rules():
         assert L.cart_cache_truncate(h, 7, 0, None) == C.CART_ERR_INVALID_ARG
     finally:
         L.cart_cache_destroy(h)
+
+
+def test_window_schedule_and_validation():
+    assert _fwd(_shape(window=-1)) == C.CART_ERR_INVALID_ARG
+    full = _sched(1, 4096, 16384, 16, 8, 128)
+    s = C.cart_attn_schedule_query(_shape(batch=1, q_seq=4096, p=16384, n_q_heads=16,
+                                          n_kv_heads=8, head_dim=128, window=1024))
+    # a 1024-row window leaves most of the cartridge unseen: every key tile
+    # keeps its piece, but with far fewer (batch, head, query-tile) units
+    assert s.bwd_kv_grid == full.bwd_kv_grid and s.bwd_cart_tiles == full.bwd_cart_tiles
+    assert 3 * s.bwd_units_per_piece < full.bwd_units_per_piece
+    wide = C.cart_attn_schedule_query(_shape(batch=1, q_seq=4096, p=16384, n_q_heads=16,
+                                             n_kv_heads=8, head_dim=128, window=20480))
+    assert wide.bwd_kv_grid == full.bwd_kv_grid     # a window reaching every row is none
