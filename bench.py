@@ -281,6 +281,173 @@ def steps_bench(C, W, shape, steps, warmup):
     return out
 
 
+def variants_bench(C, W, shape, steps, warmup):
+    """One layer of `shape` (its first layer's inputs) in the variant modes:
+    behind a sliding window of 4096 positions that cuts the cartridge, with
+    the tokens as four packed segments, and with the cartridge as four
+    composed parts. Each line is the mode's fwd+bwd step (RoPE included;
+    algorithmic flop over the pairs the mode leaves visible)."""
+    import torch
+    dev = torch.device("cuda")
+    x = W.train_inputs(shape, seed=shape.seed)
+    g = {k: v.to(dev) for k, v in x.items()}
+    del x
+    p, n, d, Hq = shape.p, shape.q_seq, shape.head_dim, shape.n_q_heads
+    out = {}
+
+    def run(name, pairs, make_step):
+        step = make_step()
+        ms, kern, dom = measure(C, step, steps, warmup, TRAIN_KERNELS + ("compose_rows",
+                                                                        "zero_frozen"), name)
+        flop = 12.0 * d * pairs
+        ach = None
+        if dom in ("attn_fwd", "attn_bwd", "attn_bwd_dq"):
+            share = {"attn_fwd": 4.0, "attn_bwd": 6.0, "attn_bwd_dq": 2.0}[dom]
+            ach = share * d * pairs / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+        out[name] = {"value": round(flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                     "ms_per_step": round(ms, 4), "visible_pairs": pairs,
+                     "frac_of_peak": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(ach / PEAK_BF16_TFLOPS, 4)} if ach else None,
+                     "kernels": {k: round(v["avg_ms"], 5) for k, v in kern.items()}}
+
+    def buffers(q, k):
+        return dict(qw=torch.empty_like(q), kw=torch.empty_like(k), o=torch.empty_like(q),
+                    dq=torch.empty_like(q), dkt=torch.empty_like(k), dvt=torch.empty_like(k),
+                    dkc=torch.empty(g["k_cart"].shape, dtype=torch.float32, device=dev),
+                    dvc=torch.empty(g["v_cart"].shape, dtype=torch.float32, device=dev))
+
+    # sliding window of 4096 positions: every query sees exactly 4096 rows
+    W_ = 4096
+    def window_step():
+        b = buffers(g["q"], g["k_tok"])
+        shp = C.attn_shape(g["q"], g["k_tok"], p, 1, 0.0, torch.float32, window=W_)
+        lse = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
+        wsf = C.workspace(C.cart_attn_workspace_size(shp, False), dev)
+        wsb = C.workspace(C.cart_attn_workspace_size(shp, True), dev)
+
+        def step():
+            b["qw"].copy_(g["q"]); b["kw"].copy_(g["k_tok"])
+            C.cart_rope_tokens(b["qw"], b["kw"], pos_base=p, theta=W.THETA)
+            C.cart_attn_fwd(shp, b["qw"], b["kw"], g["v_tok"], g["k_cart"], g["v_cart"], b["o"],
+                            lse, wsf)
+            C.cart_attn_bwd(shp, b["qw"], b["kw"], g["v_tok"], g["k_cart"], g["v_cart"], b["o"],
+                            lse, g["dout"], b["dq"], b["dkt"], b["dvt"], b["dkc"], b["dvc"],
+                            False, wsb)
+            C.cart_rope_tokens(b["dq"], b["dkt"], pos_base=p, theta=W.THETA, inverse=True)
+        return step
+    vis_w = shape.batch * Hq * sum(min(W_, p + i + 1) for i in range(n))
+    run(f"window-{W_}", vis_w, window_step)
+
+    # packed: the n tokens as four segments
+    seg = [n // 4, n // 8, n // 2, n - n // 4 - n // 8 - n // 2]
+    def packed_step():
+        q, k, v, do = (g[t][0] for t in ("q", "k_tok", "v_tok", "dout"))
+        b = buffers(q, k)
+        shp = C.attn_shape(q, k, p, 1, 0.0, torch.float32, seg_lens=seg)
+        lse = torch.empty(len(seg), Hq, max(seg), dtype=torch.float32, device=dev)
+        wsf = C.workspace(C.cart_attn_workspace_size(shp, False), dev)
+        wsb = C.workspace(C.cart_attn_workspace_size(shp, True), dev)
+
+        def step():
+            b["qw"].copy_(q); b["kw"].copy_(k)
+            C.cart_rope_tokens_packed(b["qw"], b["kw"], seg, pos_base=p, theta=W.THETA)
+            C.cart_attn_fwd(shp, b["qw"], b["kw"], v, g["k_cart"], g["v_cart"], b["o"], lse, wsf)
+            C.cart_attn_bwd(shp, b["qw"], b["kw"], v, g["k_cart"], g["v_cart"], b["o"], lse, do,
+                            b["dq"], b["dkt"], b["dvt"], b["dkc"], b["dvc"], False, wsb)
+            C.cart_rope_tokens_packed(b["dq"], b["dkt"], seg, pos_base=p, theta=W.THETA,
+                                      inverse=True)
+        return step
+    vis_p = Hq * sum(m * p + m * (m + 1) // 2 for m in seg)
+    run("packed-" + "+".join(str(m) for m in seg), vis_p, packed_step)
+
+    # composed: the cartridge as four parts of p/4 rows, each with its sink
+    cut = [p // 4] * 3 + [p - 3 * (p // 4)]
+    def composed_step():
+        b = buffers(g["q"], g["k_tok"])
+        kp = list(torch.split(g["k_cart"], cut))
+        vp = list(torch.split(g["v_cart"], cut))
+        parts = C.parts_desc(kp, vp, [1] * 4)
+        kc = torch.empty(g["k_cart"].shape, dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        shp = C.attn_shape(g["q"], g["k_tok"], p, 1, 0.0, torch.bfloat16)
+        lse = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
+        wsf = C.workspace(C.cart_attn_workspace_size(shp, False), dev)
+        wsb = C.workspace(C.cart_attn_workspace_size(shp, True), dev)
+        Hkv = shape.n_kv_heads
+
+        def step():
+            b["qw"].copy_(g["q"]); b["kw"].copy_(g["k_tok"])
+            C.cart_compose_rows(parts, torch.float32, Hkv, d, kc, vc)
+            C.cart_rope_tokens(b["qw"], b["kw"], pos_base=p, theta=W.THETA)
+            C.cart_attn_fwd(shp, b["qw"], b["kw"], g["v_tok"], kc, vc, b["o"], lse, wsf)
+            C.cart_attn_bwd_composed(shp, parts, b["qw"], b["kw"], g["v_tok"], kc, vc, b["o"],
+                                     lse, g["dout"], b["dq"], b["dkt"], b["dvt"], b["dkc"],
+                                     b["dvc"], False, wsb)
+            C.cart_rope_tokens(b["dq"], b["dkt"], pos_base=p, theta=W.THETA, inverse=True)
+        return step
+    run("composed-4-parts", shape.visible_pairs, composed_step)
+    del g
+    torch.cuda.empty_cache()
+    return out
+
+
+def verify_bench(C, W, shape, steps, warmup, n_tokens=4):
+    """The serving-decode workload verifying n_tokens drafts per sequence:
+    each step appends the drafts and attends; the cache is truncated back
+    between the timed blocks (outside the timing). GB/s of K/V read."""
+    import torch
+    dev = torch.device("cuda")
+    di = W.decode_inputs(shape)
+    S, Hq, Hkv, d = shape.n_seqs, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    mp = di.max_pages_per_seq + (n_tokens * (steps + warmup) + 15) // 16 + 1
+    perm = torch.randperm(S * mp, generator=torch.Generator().manual_seed(shape.seed + 1))
+    cache = C.PagedCache(S, Hkv, d, mp, S * mp, perm.to(torch.int32).view(S, mp), dev)
+    kc, vc = di.k_cart.to(dev), di.v_cart.to(dev)
+    for s in range(S):
+        cache.write(s, kc, vc)
+        if di.generated[s]:
+            cache.append(s, di.k_gen[s].to(dev), di.v_gen[s].to(dev))
+    g0 = torch.Generator().manual_seed(shape.seed + 2)
+    q = torch.randn(S, n_tokens, Hq, d, generator=g0).to(torch.bfloat16).to(dev)
+    kn = torch.randn(S, n_tokens, Hkv, d, generator=g0).to(torch.bfloat16).to(dev)
+    vn = torch.randn(S, n_tokens, Hkv, d, generator=g0).to(torch.bfloat16).to(dev)
+    out = torch.empty(S, n_tokens, Hq, d, dtype=torch.bfloat16, device=dev)
+    ws = C.workspace(cache.verify_workspace_size(n_tokens, Hq), dev)
+    lens0 = [cache.seq_len(s) for s in range(S)]
+
+    def step():
+        cache.verify(q, kn, vn, out, ws)
+
+    for _ in range(warmup):
+        step()
+    for s in range(S):
+        cache.truncate(s, lens0[s])
+    torch.cuda.synchronize()
+    ms = _events_ms(step, steps) / steps
+    # rows read: every step reads each sequence's rows after its append
+    kv_bytes = sum(sum(l + n_tokens * (j + 1) for l in lens0) for j in range(steps)) \
+        * Hkv * d * 2 * 2 / steps
+    C.timing_only("decode")
+    C.timing_enable(True)
+    for s in range(S):
+        cache.truncate(s, lens0[s])
+    _events_ms(step, steps)
+    kms, cnt = C.timing_query("decode")
+    C.timing_enable(False)
+    C.timing_only(None)
+    cache.close()
+    kavg = kms / cnt
+    return {"workload": f"{shape.name}, {n_tokens} draft tokens per sequence",
+            "value": round(kv_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(ms, 4), "kv_bytes_per_step": int(kv_bytes),
+            "roofline": {"kernel": "decode", "bound": "hbm",
+                         "achieved": round(kv_bytes / (kavg * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(kv_bytes / (kavg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}}
+
+
 def cpu_baseline(W, shape):
     """The oracle (numpy float64) timed on a bounded sample of the layer: the
     first kv heads of sequence 0 (their GQA q-heads, all queries, all keys),
@@ -372,6 +539,8 @@ def main():
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the window / packed / composed runs of one layer")
     ap.add_argument("--no-steps", action="store_true",
                     help="skip the q/k norm + RoPE and Adam kernels of one layer")
     ap.add_argument("--no-extra", action="store_true",
@@ -435,6 +604,8 @@ def main():
         result["extra_workloads"] = extra
     if not args.no_steps:
         result["steps_around_attention"] = steps_bench(C, W, shape, args.steps, args.warmup)
+    if not args.no_variants:
+        result["variants"] = variants_bench(C, W, shape, args.steps, args.warmup)
     if not args.no_decode:
         dec = decode_bench(C, W, W.DECODE, max(args.steps, 20), args.warmup)
         gbps = dec["kv_bytes"] / (dec["ms"] * 1e-3) / 1e9
@@ -457,6 +628,7 @@ def main():
             "roofline": droof,
             "kernels": {k: {"avg_ms": round(v["avg_ms"], 5), "launches": v["launches"],
                             "pass": v["pass_"]} for k, v in dec["kern"].items()},
+            "verify": verify_bench(C, W, W.DECODE, max(args.steps, 20), args.warmup),
             "write_cache": {"ms": round(dec["write_ms"], 3),
                             "kernel_ms": round(dec["write_kernel_ms"], 3),
                             "GB/s": round(dec["write_bytes"] / (dec["write_kernel_ms"] * 1e-3)

@@ -6,10 +6,11 @@
  * already rotated (RoPE at positions 0..p-1) and are never rotated again;
  * real tokens sit at RoPE positions p, p+1, ...; row 0 is a frozen "sink".
  * Attention runs over concat(sink, trainable rows, real tokens) with the
- * end-aligned causal mask, source_offset = kv_seq - q_seq = p, so every
- * query sees the whole cartridge and is causal over real tokens. Gradients
- * flow through the concat into the trainable rows; serving writes the prefix
- * into an empty KV cache and decodes behind it.
+ * causal mask aligned to the end (source_offset = kv_seq - q_seq = p): all p
+ * prefix rows are visible to every token's query, and among the real tokens
+ * a query reaches only itself and the tokens before it. Gradients flow
+ * through the concat into the trainable rows; serving writes the prefix into
+ * an empty KV cache and decodes behind it.
  *   Source: "Cartridges: trained KV-prefix corpus compression" (Fucina
  *   guide), section "Semantics (pinned to the reference implementation)".
  *
@@ -69,6 +70,7 @@ typedef struct {
   cart_dtype tok_dtype; /* Q, token K/V, O, dO, dQ, token dK/dV */
   cart_dtype row_dtype; /* cartridge K/V storage (f32 master rows or bf16) */
   int32_t window;       /* 0: none; W > 0: sliding window, see below */
+  const int32_t* seg_lens; /* (host) NULL, or [batch] packed segment lengths, see below */
 } cart_attn_shape;
 /* Sliding window (local attention layers, e.g. gemma4's; Cartridges guide,
    section "gemma4 (measured)": such layers see the cartridge exactly as a
@@ -76,6 +78,19 @@ typedef struct {
    the query of token i, at position p + i, sees only the rows at positions
    above p + i - W (cartridge row j is at position j, token row t at p + t),
    itself included. W >= p + q_seq is the same as no window. */
+/* Packed segments (Cartridges guide, "Deliberate divergences from the
+   reference": a group of conversations runs as contiguous segments of one
+   forward, RoPE restarting and attention running per segment behind the one
+   shared prefix, whose gradient sums over the segments): with seg_lens set,
+   the token tensors hold batch = 1..64 segments back to back -- Q, O, dO, dQ
+   [T, n_q_heads, head_dim], token K/V and their gradients [T, n_kv_heads,
+   head_dim], T = the sum of seg_lens -- segment b at rows off_b ..
+   off_b + seg_lens[b] - 1 (off_b = the lengths before it). Each segment
+   attends like one sequence of the batch (its token i at position p + i;
+   rotate with cart_rope_tokens_packed). 1 <= seg_lens[b] <= q_seq, and LSE
+   keeps the padded layout [batch, n_q_heads, q_seq] (entries past a
+   segment's end are not written or read). The array is read during the call
+   only. */
 /* Supported dtype pairs: (tok F32, rows F32) is the float32 reference mode
    (all arithmetic in f32); (tok BF16, rows F32 or BF16) is the bf16 mode:
    MFMA operands are bf16 (f32 rows are rounded to nearest-even on load),
@@ -104,6 +119,15 @@ int cart_rope_tokens(void* q, void* k, cart_dtype dt, int32_t batch, int32_t seq
                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                      int32_t pos_base, const int32_t* pos_offsets, double theta,
                      int32_t inverse, void* stream);
+
+/* cart_rope_tokens over packed segments: q [T, n_q_heads, head_dim] and k
+   [T, n_kv_heads, head_dim] (nullable) hold n_segs (1..64) segments back to
+   back, of lengths seg_lens (host, each >= 1, T = their sum); token t of a
+   segment sits at position pos_base + t (positions restart per segment). */
+int cart_rope_tokens_packed(void* q, void* k, cart_dtype dt, int32_t n_segs,
+                            const int32_t* seg_lens, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t pos_base, double theta, int32_t inverse,
+                            void* stream);
 
 /*
  * cart_qk_norm_rope -- the per-head RMS normalization of the real-token
@@ -303,9 +327,9 @@ int cart_attn_bwd_composed(const cart_attn_shape* s, const cart_parts* parts, co
 
 /* ------------------------------------------------------------------------
  * Serving: a paged KV cache that hosts a prefix no tokens produced.
- *   Source: Cartridges guide, "Semantics" (serving): the full prefix is
- *   written into an empty cache, converted to the cache dtype, and the cache
- *   is advanced to p; decode then continues at position p. "Evidence"
+ *   Source: Cartridges guide, "Semantics" (serving): an empty cache receives
+ *   all p prefix rows in its own dtype, its length becomes p, and ordinary
+ *   decoding resumes at position p. "Evidence"
  *   (serving parity). Composition section: appendToCache is the primitive.
  *   RIG hand-off, section 5: cartridges are locked to the model geometry
  *   and the KV dtype must match the serving cache.

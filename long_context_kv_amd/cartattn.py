@@ -42,7 +42,7 @@ CART_BF16 = 1
 _DTYPES = {torch.float32: CART_F32, torch.bfloat16: CART_BF16}
 
 EXPORTS = [
-    "cart_rope_tokens", "cart_qk_norm_rope", "cart_qk_norm_rope_bwd", "cart_adam_rows",
+    "cart_rope_tokens", "cart_rope_tokens_packed", "cart_qk_norm_rope", "cart_qk_norm_rope_bwd", "cart_adam_rows",
     "cart_attn_workspace_size", "cart_parts_rows", "cart_compose_rows",
     "cart_attn_bwd_composed", "cart_write_composed_cache", "cart_attn_fwd", "cart_attn_bwd",
     "cart_cache_create", "cart_cache_destroy", "cart_cache_reset", "cart_cache_seq_len",
@@ -59,7 +59,7 @@ class AttnShape(ctypes.Structure):
         ("frozen_rows", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("scale", ctypes.c_float), ("tok_dtype", ctypes.c_int), ("row_dtype", ctypes.c_int),
-        ("window", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("seg_lens", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -93,6 +93,8 @@ _P = ctypes.POINTER
 
 _lib.cart_rope_tokens.argtypes = [_vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _vp, ctypes.c_double, _i32, _vp]
+_lib.cart_rope_tokens_packed.argtypes = [_vp, _vp, ctypes.c_int, _i32, _P(_i32), _i32, _i32, _i32,
+                                         _i32, ctypes.c_double, _i32, _vp]
 _lib.cart_qk_norm_rope.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
                                    _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_double, _vp]
 _lib.cart_qk_norm_rope_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32,
@@ -176,12 +178,22 @@ def _dt(t: torch.Tensor) -> int:
 
 def attn_shape(q: torch.Tensor, k_tok: torch.Tensor, p: int, frozen_rows: int = 1,
                scale: float = 0.0, row_dtype: Optional[torch.dtype] = None,
-               window: int = 0) -> AttnShape:
-    """Shape struct from Q [B, n, Hq, d] and token K [B, n, Hkv, d]."""
-    B, n, Hq, d = q.shape
-    Hkv = k_tok.shape[2]
+               window: int = 0, seg_lens=None) -> AttnShape:
+    """Shape struct from Q [B, n, Hq, d] and token K [B, n, Hkv, d], or, for
+    packed segments (seg_lens: their lengths), Q [T, Hq, d] and K [T, Hkv, d].
+    A packed shape keeps its length array alive as an attribute."""
     rd = _DTYPES[row_dtype] if row_dtype is not None else _dt(q)
-    return AttnShape(B, n, p, frozen_rows, Hq, Hkv, d, scale, _dt(q), rd, window)
+    if seg_lens is None:
+        B, n, Hq, d = q.shape
+        Hkv = k_tok.shape[2]
+        return AttnShape(B, n, p, frozen_rows, Hq, Hkv, d, scale, _dt(q), rd, window, None)
+    T, Hq, d = q.shape
+    Hkv = k_tok.shape[1]
+    lens = (ctypes.c_int32 * len(seg_lens))(*[int(x) for x in seg_lens])
+    s = AttnShape(len(seg_lens), max(seg_lens), p, frozen_rows, Hq, Hkv, d, scale, _dt(q), rd,
+                  window, lens)
+    s._lens = lens
+    return s
 
 
 # ---------------------------------------------------------------- raw calls
@@ -195,6 +207,18 @@ def cart_rope_tokens(q: torch.Tensor, k: Optional[torch.Tensor], pos_base: int,
     _check(_lib.cart_rope_tokens(_ptr(q), _ptr(k), _dt(q), B, S, Hq, Hkv, d, pos_base,
                                  _ptr(pos_offsets), theta, int(inverse), _stream(stream)),
            "cart_rope_tokens")
+
+
+def cart_rope_tokens_packed(q: torch.Tensor, k: Optional[torch.Tensor], seg_lens, pos_base: int,
+                            theta: float = 1.0e6, inverse: bool = False, stream=None) -> None:
+    """Rotate packed q [T, Hq, d] (and k [T, Hkv, d]) in place; positions
+    restart at pos_base in every segment."""
+    T, Hq, d = q.shape
+    Hkv = k.shape[1] if k is not None else 0
+    lens = (ctypes.c_int32 * len(seg_lens))(*[int(x) for x in seg_lens])
+    _check(_lib.cart_rope_tokens_packed(_ptr(q), _ptr(k), _dt(q), len(seg_lens), lens, Hq, Hkv, d,
+                                        pos_base, theta, int(inverse), _stream(stream)),
+           "cart_rope_tokens_packed")
 
 
 def cart_qk_norm_rope(q_in: torch.Tensor, k_in: Optional[torch.Tensor], q_out: torch.Tensor,
@@ -313,13 +337,13 @@ def workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def attn_fwd(q, k_tok, v_tok, k_cart, v_cart, frozen_rows: int = 1, scale: float = 0.0,
-             stream=None, window: int = 0):
+             stream=None, window: int = 0, seg_lens=None):
     """Allocate O, LSE and the workspace, run cart_attn_fwd, return (O, LSE)."""
     p = 0 if k_cart is None else k_cart.shape[0]
     rd = k_cart.dtype if k_cart is not None else q.dtype
-    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd, window)
+    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd, window, seg_lens)
     out = torch.empty_like(q)
-    B, n, Hq, _ = q.shape
+    B, n, Hq = shape.batch, shape.q_seq, shape.n_q_heads
     lse = torch.empty(B, Hq, n, dtype=torch.float32, device=q.device)
     ws = workspace(cart_attn_workspace_size(shape, False), q.device)
     cart_attn_fwd(shape, q, k_tok, v_tok, k_cart, v_cart, out, lse, ws, stream)
@@ -328,14 +352,14 @@ def attn_fwd(q, k_tok, v_tok, k_cart, v_cart, frozen_rows: int = 1, scale: float
 
 def attn_bwd(q, k_tok, v_tok, k_cart, v_cart, out, lse, dout, frozen_rows: int = 1,
              scale: float = 0.0, dk_cart=None, dv_cart=None, accumulate_cart: bool = False,
-             stream=None, window: int = 0):
+             stream=None, window: int = 0, seg_lens=None):
     """Allocate gradients and workspace, run cart_attn_bwd.
 
     Returns (dq, dk_tok, dv_tok, dk_cart, dv_cart); cartridge gradients are
     float32 [p, Hkv, d] (the given buffers when passed)."""
     p = 0 if k_cart is None else k_cart.shape[0]
     rd = k_cart.dtype if k_cart is not None else q.dtype
-    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd, window)
+    shape = attn_shape(q, k_tok, p, frozen_rows, scale, rd, window, seg_lens)
     dq = torch.empty_like(q)
     dk_tok = torch.empty_like(k_tok)
     dv_tok = torch.empty_like(v_tok)

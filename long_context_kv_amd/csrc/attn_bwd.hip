@@ -87,6 +87,8 @@ struct BwdArgs {
   int zero_dq;                // preprocess clears the f32 dQ accumulator
   int accumulate;
   int window;                 // > 0: sliding window (positions above p + i - window)
+  int kv_tok_pieces;          // dK/dV pieces of one kv head's token tiles (all sequences)
+  Segs seg;                   // token rows of each sequence; n is the longest
   float scale, scale_log2;
 };
 
@@ -189,11 +191,13 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
     r0 -= a.n_ct * a.splits_c;
     b = r0 / a.n_tt;
     tile = r0 % a.n_tt;
+    if (tile * kBNB >= a.seg.len(b, a.n)) return;     // past a packed segment's end
     u_begin = 0;
-    u_end = a.g * (a.nqt - tile * (kBNB / kBQ));
+    u_end = a.g * ((a.seg.len(b, a.n) + kBQ - 1) / kBQ - tile * (kBNB / kBQ));
   }
+  const int base = a.seg.base(b, a.n);                // token tiles: the sequence's rows
   const int j0 = tile * kBNB;                         // first row in its source
-  const int limit = cart ? a.p : a.n;                 // rows that exist
+  const int limit = cart ? a.p : a.seg.len(b, a.n);   // rows that exist
   const int my_key = j0 + 32 * wave + l32;            // this lane's key row (B operand)
   const size_t row_stride = (size_t)a.Hkv * D;
 
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
         vf[ks] = ok ? conv_frag<T, TR>(vp + ks * KSTEP + hl * KPL) : zero_frag<T>();
       }
     } else {
-      const size_t off = (((size_t)b * a.n + my_key) * a.Hkv + kv) * D;
+      const size_t off = (((size_t)base + my_key) * a.Hkv + kv) * D;
       const T* kp = reinterpret_cast<const T*>(a.k_tok) + off;
       const T* vp = reinterpret_cast<const T*>(a.v_tok) + off;
 #pragma unroll
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
         if (cart)
           load8<TR>(reinterpret_cast<const TR*>(a.k_cart) + ((size_t)j * a.Hkv + kv) * D + col, v8);
         else
-          load8<T>(reinterpret_cast<const T*>(a.k_tok) + (((size_t)b * a.n + j) * a.Hkv + kv) * D + col, v8);
+          load8<T>(reinterpret_cast<const T*>(a.k_tok) + (((size_t)base + j) * a.Hkv + kv) * D + col, v8);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v8[e] = 0.f;
@@ -261,13 +265,15 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
       hin = (u / units_per_head) % a.g;
       qt = u % units_per_head;
     } else {
-      const int span = a.nqt - tile * (kBNB / kBQ);
+      const int span = (a.seg.len(b, a.n) + kBQ - 1) / kBQ - tile * (kBNB / kBQ);
       bb = b;
       hin = u / span;
       qt = tile * (kBNB / kBQ) + u % span;
     }
     const int h = kv * a.g + hin;
     const int i0 = qt * kBQ;
+    const int nbb = a.seg.len(bb, a.n);     // the unit's sequence: length and first row
+    const int bbase = a.seg.base(bb, a.n);
 
     __syncthreads();   // previous unit is done with the staged tiles and dS
     {
@@ -280,8 +286,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
         const int col = (c % CPR) * 8;
         const int i = i0 + r;
         float qv[8], ov[8];
-        if (i < a.n) {
-          const size_t off = (((size_t)bb * a.n + i) * a.Hq + h) * D + col;
+        if (i < nbb) {
+          const size_t off = (((size_t)bbase + i) * a.Hq + h) * D + col;
           load8<T>(reinterpret_cast<const T*>(a.q) + off, qv);
           load8<T>(reinterpret_cast<const T*>(a.dout) + off, ov);
         } else {
@@ -301,8 +307,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
       if (tid < kBQ) {
         const int i = i0 + tid;
         const size_t li = ((size_t)bb * a.Hq + h) * a.n + i;
-        lse2s[tid] = (i < a.n) ? a.lse[li] * kLog2e : INFINITY;
-        dls[tid] = (i < a.n) ? a.delta[li] : 0.f;
+        lse2s[tid] = (i < nbb) ? a.lse[li] * kLog2e : INFINITY;
+        dls[tid] = (i < nbb) ? a.delta[li] : 0.f;
       }
     }
     __syncthreads();
@@ -365,8 +371,8 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int i = i0 + d_row(r, hl);
-        if (i < a.n)
-          atomicAdd(a.dq_acc + (((size_t)bb * a.n + i) * a.Hq + h) * D + 32 * q_db + l32,
+        if (i < nbb)
+          atomicAdd(a.dq_acc + (((size_t)bbase + i) * a.Hq + h) * D + 32 * q_db + l32,
                     acc[r] * a.scale);
       }
     }
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
           a.dv_cart[o] = gv;
         }
       } else {
-        const size_t o = (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
+        const size_t o = (((size_t)base + j) * a.Hkv + kv) * D + col;
         reinterpret_cast<T*>(a.dk_tok)[o] = from_f32<T>(gk);
         reinterpret_cast<T*>(a.dv_tok)[o] = from_f32<T>(gv);
       }
@@ -427,6 +433,18 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_kernel(BwdArgs a) {
 //   the MFMA result layout). dQ is written once, in the token dtype.
 // Cartridge rows arrive as bf16 (f32 master rows are cast first).
 
+
+// Entry i of the segment offsets of the dK/dV kernel's argument. A run-time
+// index into an array member of a by-value kernel argument makes the
+// compiler copy the whole argument to per-lane scratch memory; reading it in
+// place in the kernarg segment (where BwdArgs, the kernel's only argument,
+// starts at offset 0) keeps every read a scalar load.
+__device__ inline int bwd_seg_off(int i) {
+  const auto* kb = (const __attribute__((address_space(4))) char*)(
+      __builtin_amdgcn_kernarg_segment_ptr());
+  return *(const __attribute__((address_space(4))) int*)(
+      kb + offsetof(BwdArgs, seg) + offsetof(Segs, off) + sizeof(int) * i);
+}
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
@@ -466,29 +484,43 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
 
   // ---- work item: a piece of one key tile's unit list (pieces of cartridge
   // tiles first, then the pieces of the token tiles, tile-major)
-  // Query tiles [qt0, qt_hi) of a key tile that hold a query seeing one of
-  // its rows: all of them, or with a sliding window those below the last
-  // row's window end (position + window - p).
-  auto tile_qt_hi = [&](bool c_, int t_) -> int {
-    if (a.window <= 0) return a.nqt;
-    const int last = min(t_ * kBNB + kBNB - 1, (c_ ? a.p : a.n) - 1);
-    const int hi = (c_ ? last - a.p : last) + a.window;   // queries below hi see it
-    return max(0, min(a.nqt, (hi + kBQ - 1) / kBQ));
+  // Sequence b_: its length, first token row, and the query tiles below
+  // qt_hi that hold a query seeing a row of key tile t_ (all of its query
+  // tiles, or with a sliding window those below the window end of the
+  // tile's last row).
+  const bool packed = a.seg.packed != 0;
+  auto len_of = [&](int b_) {
+    b_ = min(b_, a.B - 1);
+    return packed ? bwd_seg_off(b_ + 1) - bwd_seg_off(b_) : a.n;
   };
-  const int per_kv = a.kv_cart_pieces + a.B * a.kv_ptok;
+  auto base_of = [&](int b_) { return packed ? bwd_seg_off(min(b_, a.B - 1)) : b_ * a.n; };
+  auto qt_hi_of = [&](bool c_, int t_, int b_) -> int {
+    const int nq_ = (len_of(b_) + kBQ - 1) / kBQ;
+    if (a.window <= 0) return nq_;
+    const int last = min(t_ * kBNB + kBNB - 1, (c_ ? a.p : len_of(b_)) - 1);
+    const int hi = (c_ ? last - a.p : last) + a.window;   // queries below hi see it
+    return max(0, min(nq_, (hi + kBQ - 1) / kBQ));
+  };
+  // units (sequence, head, query tile) of cartridge tile t_
+  auto cart_units = [&](int t_) {
+    if (!packed) return a.B * a.g * qt_hi_of(true, t_, 0);
+    int u_ = 0;
+    for (int b_ = 0; b_ < a.B; ++b_) u_ += a.g * qt_hi_of(true, t_, b_);
+    return u_;
+  };
+  const int per_kv = a.kv_cart_pieces + a.kv_tok_pieces;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int kv = lg / per_kv;
   int r0 = lg % per_kv;
   const bool cart = r0 < a.kv_cart_pieces;
-  int tile, split = 0, n_split = 1, b = 0, u_begin, u_end, qt_hi;
+  int tile, split = 0, n_split = 1, b = 0, u_begin, u_end;
   if (cart && a.window <= 0) {
     // split-major: the workgroups that run together (consecutive ids on one
     // XCD) read the same window of units, so their Q / dO copies share the L2
     split = r0 / a.n_ct;
     tile = r0 % a.n_ct;
     n_split = a.splits_c;
-    qt_hi = a.nqt;
-    const int U = a.B * a.g * a.nqt;
+    const int U = cart_units(0);    // every cartridge tile sees every query
     u_begin = (int)((long long)split * U / a.splits_c);
     u_end = (int)((long long)(split + 1) * U / a.splits_c);
   } else if (cart) {
@@ -496,86 +528,113 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     // their pieces are dealt tile-major (a tile no query sees: one piece
     // with no units, which writes its zero gradient)
     tile = 0;
-    qt_hi = tile_qt_hi(true, 0);
-    int U = a.B * a.g * qt_hi;
+    int U = cart_units(0);
     n_split = max(1, (U + a.kv_target - 1) / a.kv_target);
-    while (r0 >= n_split) {
+    while (r0 >= n_split && tile + 1 < a.n_ct) {
       r0 -= n_split;
       ++tile;
-      qt_hi = tile_qt_hi(true, tile);
-      U = a.B * a.g * qt_hi;
+      U = cart_units(tile);
       n_split = max(1, (U + a.kv_target - 1) / a.kv_target);
     }
+    if (r0 >= n_split) return;   // beyond the planned pieces (never, by construction)
     split = r0;
     u_begin = (int)((long long)split * U / n_split);
     u_end = (int)((long long)(split + 1) * U / n_split);
   } else {
     // token pieces tile-major (the larger tiles, nearer the start, first),
-    // then by batch, then by piece
+    // then by sequence (those long enough to have the tile), then by piece
     r0 -= a.kv_cart_pieces;
-    tile = 0;
-    qt_hi = tile_qt_hi(false, 0);
-    int ut = a.g * qt_hi;
-    n_split = (ut + a.kv_target - 1) / a.kv_target;
-    while (r0 >= a.B * n_split) {
-      r0 -= a.B * n_split;
-      ++tile;
-      qt_hi = tile_qt_hi(false, tile);
-      ut = a.g * (qt_hi - tile * (kBNB / kBQ));
-      n_split = (ut + a.kv_target - 1) / a.kv_target;
+    int ut = 0;
+    for (tile = 0; tile < a.n_tt; ++tile) {
+      if (!packed) {
+        ut = a.g * (qt_hi_of(false, tile, 0) - tile * (kBNB / kBQ));
+        n_split = (ut + a.kv_target - 1) / a.kv_target;
+        if (r0 < a.B * n_split) { b = r0 / n_split; r0 %= n_split; break; }
+        r0 -= a.B * n_split;
+        continue;
+      }
+      bool found = false;
+      for (b = 0; b < a.B; ++b) {
+        if (tile * kBNB >= len_of(b)) continue;
+        ut = a.g * (qt_hi_of(false, tile, b) - tile * (kBNB / kBQ));
+        n_split = (ut + a.kv_target - 1) / a.kv_target;
+        if (r0 < n_split) { found = true; break; }
+        r0 -= n_split;
+      }
+      if (found) break;
     }
-    b = r0 / n_split;
-    split = r0 % n_split;
+    if (tile >= a.n_tt) return;  // beyond the planned pieces (never, by construction)
+    split = r0;
     u_begin = (int)((long long)split * ut / n_split);
     u_end = (int)((long long)(split + 1) * ut / n_split);
   }
   const int j0 = tile * kBNB;
-  const int limit = cart ? a.p : a.n;
+  const int nb = cart ? 0 : len_of(b);      // a token tile's sequence length
+  const int limit = cart ? a.p : nb;
   const int my_key = j0 + 32 * pair + l32;
   const bool key_ok = my_key < limit;
   const size_t row_stride = (size_t)a.Hkv * D;
   const bf16* kbase = cart ? reinterpret_cast<const bf16*>(a.k_cart) + kv * D
-                           : reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+                           : reinterpret_cast<const bf16*>(a.k_tok) + ((size_t)base_of(b) * a.Hkv + kv) * D;
   const bf16* vbase = cart ? reinterpret_cast<const bf16*>(a.v_cart) + kv * D
-                           : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)b * a.n * a.Hkv + kv) * D;
+                           : reinterpret_cast<const bf16*>(a.v_tok) + ((size_t)base_of(b) * a.Hkv + kv) * D;
   // Queries i visible to this lane's key: lo <= i < hi (an empty range for a
-  // key past the end of its rows); hi is n, or with a sliding window the
-  // key's window end.
-  const int vis_lo = !key_ok ? a.n : (cart ? 0 : my_key);
-  const int vis_hi = a.window > 0 ? min(a.n, (cart ? my_key - a.p : my_key) + a.window) : a.n;
-  const uint32_t vis_span = (uint32_t)max(0, vis_hi - vis_lo);
+  // key past the end of its rows); hi is the query's sequence length (a
+  // cartridge key: per unit), or with a sliding window the key's window end
+  // if that comes first.
+  const int vis_lo = !key_ok ? (1 << 30) : (cart ? 0 : my_key);
+  const int win_hi = a.window > 0 ? (cart ? my_key - a.p : my_key) + a.window : (1 << 30);
+  auto vis_span_for = [&](int len_) { return (uint32_t)max(0, min(len_, win_hi) - vis_lo); };
 
-  // ---- unit cursor: (batch, q-head of the group, query tile) and the
-  // offsets of its Q / dO rows (bytes) and of its lse / D (elements); within
-  // a head the next unit is one query tile further, so only a change of head
-  // recomputes them
+  // ---- unit cursor: (sequence, q-head of the group, query tile), the end
+  // of its query tiles, and the offsets of its Q / dO rows (bytes) and of
+  // its lse / D (elements); within a head the next unit is one query tile
+  // further, so only a change of head recomputes them
   const int qt0 = cart ? 0 : tile * (kBNB / kBQ);
   const uint32_t q_row_bytes = (uint32_t)(a.Hq * D * 2);
-  struct Unit { int bb, hin, qt; size_t qoff, loff; };
+  struct Unit { int bb, hin, qt, qt_end, len; size_t qoff, loff; };
   auto locate_unit = [&](Unit& x) {
     const int h = kv * a.g + x.hin;
-    x.qoff = (((size_t)x.bb * a.n + (size_t)x.qt * kBQ) * a.Hq + h) * (size_t)(D * 2);
+    x.len = len_of(x.bb);
+    x.qoff = (((size_t)base_of(x.bb) + (size_t)x.qt * kBQ) * a.Hq + h) * (size_t)(D * 2);
     x.loff = ((size_t)x.bb * a.Hq + h) * a.n + (size_t)x.qt * kBQ;
   };
+  // query tiles of the unit's sequence that this key tile serves
+  auto qt_end_of = [&](int bb_) { return bb_ < a.B ? qt_hi_of(cart, tile, bb_) : qt0 + 1; };
   Unit cu;
-  // query tiles per (batch, head) of this key tile (at least 1 for the
-  // division; a tile without units never follows its cursor)
-  const int nq = max(1, qt_hi - qt0);
   if (cart) {
-    cu.bb = u_begin / (a.g * nq);
-    cu.hin = (u_begin / nq) % a.g;
-    cu.qt = u_begin % nq;
+    int u = u_begin, bb = 0, nq_ = qt_end_of(0);
+    if (!packed) {
+      const int nqu = max(1, nq_);   // the same for every sequence
+      bb = u / (a.g * nqu);
+      u -= bb * a.g * nqu;
+      nq_ = nqu;
+    } else {
+      while (bb < a.B - 1 && u >= a.g * nq_) { u -= a.g * nq_; nq_ = qt_end_of(++bb); }
+      nq_ = max(1, nq_);
+    }
+    cu.bb = bb;
+    cu.hin = u / nq_;
+    cu.qt = u % nq_;
+    cu.qt_end = nq_;
   } else {
+    const int nq_ = max(1, qt_end_of(b) - qt0);
     cu.bb = b;
-    cu.hin = u_begin / nq;
-    cu.qt = qt0 + u_begin % nq;
+    cu.hin = u_begin / nq_;
+    cu.qt = qt0 + u_begin % nq_;
+    cu.qt_end = qt0 + nq_;
   }
   locate_unit(cu);
-  const int qt_end = qt0 + nq;
   auto next = [&](Unit x) {
-    if (++x.qt == qt_end) {
+    if (++x.qt == x.qt_end) {
       x.qt = qt0;
-      if (++x.hin == a.g) { x.hin = 0; ++x.bb; }
+      if (++x.hin == a.g) {
+        x.hin = 0;
+        ++x.bb;
+        // a cartridge tile skips the sequences none of whose queries see it
+        if (cart) while (x.bb < a.B && qt_end_of(x.bb) == 0) ++x.bb;
+        x.qt_end = max(qt0 + 1, qt_end_of(x.bb));
+      }
       locate_unit(x);
     } else {
       x.qoff += (size_t)kBQ * q_row_bytes;
@@ -586,13 +645,13 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // Units whose pairs are not all visible (some key of the tile missing, the
   // query tile ragged, or a token tile's diagonal) take the mask.
   const bool mask_all = j0 + kBNB > limit;
-  const int q_full = a.n / kBQ;                          // first ragged query tile
   const int q_diag = cart ? 0 : qt0 + kBNB / kBQ;        // first tile past the diagonal
   // with a sliding window, the first query past the window of the tile's
   // first row (later queries lose rows of the tile)
   const int q_win = a.window > 0 ? (cart ? j0 - a.p : j0) + a.window : (1 << 30);
-  auto needs_mask = [&](int qt) {
-    return mask_all || qt >= q_full || qt < q_diag || qt * kBQ + kBQ > q_win;
+  // (len: the unit's sequence length; its first ragged query tile is len / 32)
+  auto needs_mask = [&](int qt, int len) {
+    return mask_all || qt >= len / kBQ || qt < q_diag || qt * kBQ + kBQ > q_win;
   };
 
   // ---- this wave's copies of a unit: copy o = wave + 8 i of the list
@@ -633,7 +692,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   const uint32_t ring_base = lds_addr(ring);
   auto copy_setup = [&](const Unit& x, uint32_t st_addr, bool real) {
     Copy c;
-    const int rows = min(kBQ, a.n - x.qt * kBQ);
+    const int rows = min(kBQ, x.len - x.qt * kBQ);
     const uint32_t nq = real ? (uint32_t)(rows - 1) * q_row_bytes + D * 2 : 0u;
 #pragma unroll
     for (int i = 0; i < NOPS - 1; ++i) c.r[i] = make_rsrc(obase[i] + x.qoff, nq);
@@ -755,7 +814,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // key cannot see the query, handed to the G wave of the pair (slot j % 2)
   // and packed for the next step.
   auto p_step = [&](auto HA, auto HB, uint32_t stA, uint32_t stB, f32x16& s, bf16x8 (&pp)[2],
-                    const Copy& cp, int qt, uint32_t xw) {
+                    const Copy& cp, int qt, int len, uint32_t xw) {
     constexpr bool A = decltype(HA)::value;
     mfma_steps(No{}, HA, HB, stA, stB, s, pp, cp);
     if constexpr (A) {
@@ -769,8 +828,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       for (int q = 0; q < 4; ++q) lds_tie(lq[q]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq[r >> 2][r & 3]));
-      if (needs_mask(qt)) {
+      if (needs_mask(qt, len)) {
         const uint32_t rel = mask_rel(qt);
+        const uint32_t vis_span = vis_span_for(len);
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           s[r] = rel + (uint32_t)(8 * (r >> 2) + (r & 3)) < vis_span ? s[r] : 0.f;
@@ -825,10 +885,28 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     f32x16 xa;          // S (P role) or dP (G role) of the newest unit
     bf16x8 yb[2];       // packed P (P role) or G (G role) of the unit before
     const Copy none{};
-    // the unit copied at step j (j + AHEAD) and the query tile of unit j
+    // the unit copied at step j (j + AHEAD), and the query tiles and
+    // sequence lengths of units j .. j + AHEAD - 1 (they set the mask of
+    // unit j), shifted along as the copies advance
+    static_assert(AHEAD == 3, "the mask shift register holds AHEAD units");
     Unit uc = cu;
-    for (int u = 0; u < AHEAD; ++u) uc = next(uc);
-    int qs = cu.qt;
+    int mq[AHEAD], ml[AHEAD];
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) {
+      mq[u] = uc.qt;
+      ml[u] = uc.len;
+      uc = next(uc);
+    }
+    auto shift = [&]() {
+#pragma unroll
+      for (int u = 0; u + 1 < AHEAD; ++u) {
+        mq[u] = mq[u + 1];
+        ml[u] = ml[u + 1];
+      }
+      mq[AHEAD - 1] = uc.qt;
+      ml[AHEAD - 1] = uc.len;
+      uc = next(uc);
+    };
     // LDS addresses of the stages of units j, j-1 and j+AHEAD (unit u lives
     // in stage u % NST; AHEAD + 2 == NST, so unit j+1+AHEAD takes the stage
     // of unit j-1)
@@ -846,22 +924,20 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       if constexpr (GR)
         g_step(HA, HB, s0, s1, xa, yb, cp, x_lane + (xs ^ (uint32_t)XSLOT));
       else
-        p_step(HA, HB, s0, s1, xa, yb, cp, qs, x_lane + xs);
+        p_step(HA, HB, s0, s1, xa, yb, cp, mq[0], ml[0], x_lane + xs);
     };
     // j = 0: phase A of unit 0
     CART_WAIT_VMCNT((AHEAD - 1) * NOPS);
     lds_barrier_waited();
     run(Yes{}, No{}, copy_setup(uc, sc, AHEAD < nu));
-    uc = next(uc);
-    qs = qs + 1 == qt_end ? qt0 : qs + 1;
+    shift();
     rotate();
     // j = 1 .. nu-1: unit j (phase A) and unit j-1 (phase B)
     for (int j = 1; j < nu; ++j) {
       CART_WAIT_VMCNT((AHEAD - 1) * NOPS);
       lds_barrier_waited();
       run(Yes{}, Yes{}, copy_setup(uc, sc, j + AHEAD < nu));
-      uc = next(uc);
-      qs = qs + 1 == qt_end ? qt0 : qs + 1;
+      shift();
       rotate();
     }
     // j = nu: phase B of unit nu-1 (its stage landed before step nu-1)
@@ -883,9 +959,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // finishes last adds them up in piece order (the same sum whichever piece
   // that is) and writes the tile's result.
   const float oscale = grole ? a.scale : 1.f;
+  const size_t tok_base = cart ? 0 : (size_t)base_of(b);
   auto out_off = [&](int j, int col) {
     return cart ? ((size_t)j * a.Hkv + kv) * D + col
-                : (((size_t)b * a.n + j) * a.Hkv + kv) * D + col;
+                : ((tok_base + j) * a.Hkv + kv) * D + col;
   };
   float* const out_cart = grole ? a.dk_cart : a.dv_cart;
   bf16* const out_tok = reinterpret_cast<bf16*>(grole ? a.dk_tok : a.dv_tok);
@@ -1020,9 +1097,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int pb = wave / a.hpw;
   const int h = kv * a.g + hg * a.hpw + hw;
   const int i0 = (qb * a.wph + pb) * 32;
-  const bool wave_active = i0 < a.n;
+  const int base = a.seg.base(b, a.n);   // the sequence's first token row
+  const int nb = a.seg.len(b, a.n);      // and its length
+  if (qb * a.wph * 32 >= nb) return;     // no query of this workgroup exists
+  const bool wave_active = i0 < nb;
   const int my_i = i0 + l32;
-  const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
+  const int wg_last = min(nb, (qb + 1) * a.wph * 32) - 1;
   const int n_ct = (a.p + kKvTile - 1) / kKvTile;
   const int nt_all = n_ct + wg_last / kKvTile + 1;
   // this workgroup's contiguous range of key tiles (with a sliding window,
@@ -1033,15 +1113,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   // first position the wave's first query sees (no window: far below 0)
   const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
-  const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
+  const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, base, nb, a.p, a.Hkv, kv);
   const KvMap<D> kmap(wave, lane);
   if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
 
   // Q^T and dO^T as B operands: lane (q + 32 hl) holds row q, 8 columns per k-step.
   bf16x8 qf[NKS], of[NKS];
-  const int qi = min(my_i, a.n - 1);
+  const int qi = min(my_i, nb - 1);
   {
-    const size_t off = (((size_t)b * a.n + qi) * a.Hq + h) * D + 8 * hl;
+    const size_t off = (((size_t)base + qi) * a.Hq + h) * D + 8 * hl;
     const bf16* qp = reinterpret_cast<const bf16*>(a.q) + off;
     const bf16* op = reinterpret_cast<const bf16*>(a.dout) + off;
 #pragma unroll
@@ -1175,7 +1255,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     if (t + 1 < t_end) kv_issue<D>(kmap, K1, V1, t + 1, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
-      const KvTile f = kv_tile(t, n_ct, a.p, a.n);
+      const KvTile f = kv_tile(t, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
         compute(lds_addr(K0), lds_addr(V0), f);
     }
@@ -1185,17 +1265,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     if (t + 2 < t_end) kv_issue<D>(kmap, K0, V0, t + 2, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
-      const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
+      const KvTile f = kv_tile(t + 1, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
         compute(lds_addr(K1), lds_addr(V1), f);
     }
   }
 
-  if (!wave_active || my_i >= a.n) return;
-  const size_t row = ((size_t)b * a.n + my_i) * a.Hq + h;
+  if (!wave_active || my_i >= nb) return;
   if (a.q_splits > 1) {
-    // f32 piece of this key range (a split with no tiles writes zeros)
-    float* pp = a.dq_part + ((size_t)split * a.B * a.n * a.Hq + row) * D;
+    // f32 piece of this key range (a split with no tiles writes zeros), in
+    // the padded [split][b][i][h] layout
+    const size_t prow = ((size_t)b * a.n + my_i) * a.Hq + h;
+    float* pp = a.dq_part + ((size_t)split * a.B * a.n * a.Hq + prow) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -1205,6 +1286,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
                         acc[db][4 * cc + 2] * scale, acc[db][4 * cc + 3] * scale);
     return;
   }
+  const size_t row = ((size_t)base + my_i) * a.Hq + h;
   bf16* dqp = reinterpret_cast<bf16*>(a.dq) + row * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -1222,6 +1304,14 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
   const size_t n4 = (size_t)a.B * a.n * a.Hq * (a.D4);
   const size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= n4) return;
+  // e walks the padded [b][i][h][D/4] pieces; dQ is written at the row of
+  // (b, i), and nothing past a packed segment's end
+  const size_t r = e / a.D4;
+  const int bi = (int)(r / a.Hq);
+  const int i = bi % a.n;
+  const int b = bi / a.n;
+  if (i >= a.seg.len(b, a.n)) return;
+  const size_t out = (((size_t)a.seg.base(b, a.n) + i) * a.Hq + r % a.Hq) * a.D4 + e % a.D4;
   const float4* pp = reinterpret_cast<const float4*>(a.dq_part);
   float4 t = pp[e];
 #pragma unroll 4
@@ -1231,7 +1321,7 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
   }
   bf16x4 o;
   o[0] = (bf16)t.x; o[1] = (bf16)t.y; o[2] = (bf16)t.z; o[3] = (bf16)t.w;
-  reinterpret_cast<bf16x4*>(a.dq)[e] = o;
+  reinterpret_cast<bf16x4*>(a.dq)[out] = o;
 }
 
 // -D_i = -(dO_i . O_i) (stored negated: G = P dP + P (-D) is one multiply
@@ -1243,9 +1333,9 @@ __global__ __launch_bounds__(256) void bwd_dq_combine(BwdArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
   constexpr int EPL = D / 16;
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);   // token row * Hq + h
   const int sub = threadIdx.x & 15;
-  const int total = a.B * a.n * a.Hq;
+  const int total = a.seg.rows(a.B, a.n) * a.Hq;
   const bool ok = row < total;
   const int rr = ok ? row : total - 1;
   const T* o = reinterpret_cast<const T*>(a.out) + (size_t)rr * D + sub * EPL;
@@ -1266,9 +1356,18 @@ __global__ __launch_bounds__(256) void bwd_preprocess(BwdArgs a) {
   if (!ok) return;
   if (sub == 0) {
     const int h = row % a.Hq;
-    const int bi = row / a.Hq;
-    const int i = bi % a.n;
-    const int b = bi / a.n;
+    const int t = row / a.Hq;
+    int b = t / a.n, i = t % a.n;
+    if (a.seg.packed) {
+      // the packed segment holding row t
+      int lo = 0, hi = a.seg.packed;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.seg.off[mid] <= t) lo = mid; else hi = mid;
+      }
+      b = lo;
+      i = t - a.seg.off[lo];
+    }
     const size_t li = ((size_t)b * a.Hq + h) * a.n + i;
     a.delta[li] = -acc;
     a.lse2[li] = a.lse[li] * kLog2e;
@@ -1334,7 +1433,9 @@ BwdPlan plan_bwd(const AttnDims& d) {
   auto same = [](const AttnDims& x, const AttnDims& y) {
     return x.B == y.B && x.n == y.n && x.p == y.p && x.f == y.f && x.Hq == y.Hq &&
            x.Hkv == y.Hkv && x.D == y.D && x.tok_bf16 == y.tok_bf16 && x.row_bf16 == y.row_bf16 &&
-           x.window == y.window;
+           x.window == y.window && x.seg.packed == y.seg.packed &&
+           (!x.seg.packed ||
+            std::equal(x.seg.off, x.seg.off + x.seg.packed + 1, y.seg.off));
   };
   for (const Entry& e : cache)
     if (e.used && same(e.d, d)) return e.pl;
@@ -1372,20 +1473,35 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   // candidate with the smallest modelled finish time wins, the largest T
   // among equals.
   {
-    // query tiles below qt_hi(t) see a row of key tile t (all, or with a
-    // sliding window those below the window end of the tile's last row)
-    auto qt_hi = [&](bool c, int t) -> long long {
-      if (d.window <= 0) return pl.nqt;
-      const long long last = std::min<long long>((long long)t * kBNB + kBNB - 1, (c ? d.p : d.n) - 1);
+    // query tiles below qt_hi(t, b) of sequence b see a row of key tile t
+    // (all of them, or with a sliding window those below the window end of
+    // the tile's last row); token tile t exists for sequences longer than
+    // t * 128
+    auto len_of = [&](int b) { return d.seg.len(b, d.n); };
+    auto qt_hi = [&](bool c, int t, int b) -> long long {
+      const long long nq = (len_of(b) + kBQ - 1) / kBQ;
+      if (d.window <= 0) return nq;
+      const long long last =
+          std::min<long long>((long long)t * kBNB + kBNB - 1, (c ? d.p : len_of(b)) - 1);
       const long long hi = (c ? last - d.p : last) + d.window;
-      return std::max(0LL, std::min<long long>(pl.nqt, (hi + kBQ - 1) / kBQ));
+      return std::max(0LL, std::min<long long>(nq, (hi + kBQ - 1) / kBQ));
     };
-    auto cart_units = [&](int t) { return (long long)d.B * g * qt_hi(true, t); };
-    auto tok_units_w = [&](int t) { return (long long)g * (qt_hi(false, t) - t * (kBNB / kBQ)); };
+    auto cart_units = [&](int t) {
+      long long u = 0;
+      for (int b = 0; b < d.B; ++b) u += (long long)g * qt_hi(true, t, b);
+      return u;
+    };
+    auto tok_units_w = [&](int t, int b) {
+      return (long long)g * (qt_hi(false, t, b) - t * (kBNB / kBQ));
+    };
+    auto has_tile = [&](int t, int b) { return (long long)t * kBNB < len_of(b); };
     const bool windowed = d.window > 0;
+    const long long Uc = pl.n_ct > 0 ? cart_units(0) : 0;   // every tile's, without a window
     long long t_max = 0;   // every tile one piece
-    for (int t = 0; t < pl.n_ct; ++t) t_max = std::max(t_max, cart_units(t));
-    for (int t = 0; t < pl.n_tt; ++t) t_max = std::max(t_max, tok_units_w(t));
+    for (int t = 0; t < pl.n_ct; ++t) t_max = std::max(t_max, windowed ? cart_units(t) : Uc);
+    for (int t = 0; t < pl.n_tt; ++t)
+      for (int b = 0; b < d.B; ++b)
+        if (has_tile(t, b)) t_max = std::max(t_max, tok_units_w(t, b));
     t_max = std::max(t_max, 1LL);
     const int slots = 32;   // one dK/dV workgroup per CU
     auto finish = [&](long long T) {
@@ -1398,14 +1514,16 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
       for (int kv = 0; kv < d.Hkv; ++kv) {
         if (!windowed) {
           // cartridge tiles split-major (every tile has the same pieces)
-          const long long ns = (U + T - 1) / T;
+          const long long ns = (Uc + T - 1) / T;
           for (long long i = 0; i < ns; ++i)
-            for (int c = 0; c < pl.n_ct; ++c) pieces.emplace_back((i + 1) * U / ns - i * U / ns, ns);
+            for (int c = 0; c < pl.n_ct; ++c)
+              pieces.emplace_back((i + 1) * Uc / ns - i * Uc / ns, ns);
         } else {
           for (int c = 0; c < pl.n_ct; ++c) tile(cart_units(c), true);
         }
         for (int t = 0; t < pl.n_tt; ++t)
-          for (int b = 0; b < d.B; ++b) tile(tok_units_w(t), false);
+          for (int b = 0; b < d.B; ++b)
+            if (has_tile(t, b)) tile(tok_units_w(t, b), false);
       }
       const size_t G = pieces.size(), q = G / 8, r = G % 8;
       double worst = 0.0;
@@ -1435,7 +1553,7 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
     }
     pl.kv_target = (int)T;
     if (!windowed) {
-      pl.kv_splits_c = pl.n_ct > 0 ? (int)((U + T - 1) / T) : 1;
+      pl.kv_splits_c = pl.n_ct > 0 ? (int)((Uc + T - 1) / T) : 1;
       pl.kv_cart_pieces = pl.n_ct * pl.kv_splits_c;
     } else {
       pl.kv_splits_c = 1;
@@ -1447,14 +1565,17 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
       }
     }
     int ptok = 0, stmax = 1;
-    for (int t = 0; t < pl.n_tt; ++t) {
-      const int ns = (int)((tok_units_w(t) + T - 1) / T);
-      ptok += ns;
-      stmax = std::max(stmax, ns);
-    }
-    pl.kv_ptok = ptok;
+    for (int t = 0; t < pl.n_tt; ++t)
+      for (int b = 0; b < d.B; ++b) {
+        if (!has_tile(t, b)) continue;
+        const int ns = (int)((tok_units_w(t, b) + T - 1) / T);
+        ptok += ns;
+        stmax = std::max(stmax, ns);
+      }
+    pl.kv_tok_pieces = ptok;
+    pl.kv_ptok = d.B > 0 ? ptok / d.B : 0;   // per sequence, uniform batches only
     pl.kv_stmax = pl.n_tt > 0 ? stmax : 1;
-    pl.grid_kv = d.Hkv * (pl.kv_cart_pieces + d.B * ptok);
+    pl.grid_kv = d.Hkv * (pl.kv_cart_pieces + ptok);
     if (d.tok_bf16 && pl.kv_stmax > 1)
       pl.tok_part_bytes =
           (size_t)pl.kv_stmax * d.B * pl.n_tt * kBNB * d.Hkv * d.D * sizeof(float);
@@ -1501,13 +1622,14 @@ size_t bwd_workspace_bytes(const AttnDims& d) {
 template <int D>
 static hipError_t launch_bwd_f32(const BwdArgs& a, const BwdPlan& pl, hipStream_t st) {
   const int rows = a.B * a.n * a.Hq;
+  const int tok_rows = a.seg.rows(a.B, a.n) * a.Hq;   // packed: the rows that exist
   CART_LAUNCH("bwd_preprocess", (bwd_preprocess<float, D>), (rows + 15) / 16, 256, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CART_LAUNCH("attn_bwd", (attn_bwd_kernel<float, float, D>), pl.grid_c + pl.grid_t, kThreads, 0,
               st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const size_t n4 = (size_t)rows * D / 4;
+  const size_t n4 = (size_t)tok_rows * D / 4;
   CART_LAUNCH("bwd_dq_finalize", (bwd_dq_finalize<float>), (unsigned)((n4 + 255) / 256), 256, 0, st,
               a.dq_acc, reinterpret_cast<float*>(a.dq), n4);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1590,7 +1712,9 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.kv_target = pl.kv_target; a.kv_ptok = pl.kv_ptok; a.kv_stmax = pl.kv_stmax;
   a.q_splits = pl.q_splits;
   a.kv_cart_pieces = pl.kv_cart_pieces;
+  a.kv_tok_pieces = pl.kv_tok_pieces;
   a.window = d.window;
+  a.seg = d.seg;
   a.D4 = d.D / 4;
   a.accumulate = accumulate ? 1 : 0;
   a.scale = d.scale;

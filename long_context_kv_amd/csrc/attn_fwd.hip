@@ -2,10 +2,10 @@
 // concat(cartridge rows, real tokens).
 //
 // Source: "Cartridges: trained KV-prefix corpus compression", section
-// "Semantics (pinned to the reference implementation)": concat(sink,
-// trainable, tokens) along seq feeds grouped attention whose end-aligned
-// causal mask (source_offset = kv_seq - q_seq) lets every query see the whole
-// cartridge while staying causal over real tokens.
+// "Semantics (pinned to the reference implementation)": the sequence axis
+// holds concat(sink, trainable, tokens); the grouped attention's causal mask
+// is aligned to the end (source_offset = kv_seq - q_seq), so each query has
+// all prefix rows in view and, among the tokens, itself and those before it.
 //
 // Design (gfx950):
 //  * one workgroup = 4 waves = 128 query rows of ONE kv-head group: the GQA
@@ -52,6 +52,7 @@ struct FwdArgs {
   int hpw, wph, n_hg, n_qb, n_splits;
   int window;          // > 0: sliding window (positions above p + i - window)
   float scale_log2;
+  Segs seg;            // token rows of each sequence; n is the longest
 };
 
 template <typename T> struct Lds;
@@ -152,10 +153,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   const int pb = wave / a.hpw;
   const int h = kv * a.g + hg * a.hpw + hw;
   const int i0 = (qb * a.wph + pb) * 32;
-  const bool wave_active = i0 < a.n;
+  const int base = a.seg.base(b, a.n);   // the sequence's first token row
+  const int nb = a.seg.len(b, a.n);      // and its length
+  if (qb * a.wph * 32 >= nb) return;     // no query of this workgroup exists
+  const bool wave_active = i0 < nb;
   const int my_i = i0 + l32;
 
-  const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
+  const int wg_last = min(nb, (qb + 1) * a.wph * 32) - 1;
   const int n_ct = (a.p + kBN - 1) / kBN;
   const int nt = n_ct + wg_last / kBN + 1;
   const int t_begin = (int)((long long)split * nt / a.n_splits);
@@ -164,8 +168,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   // Q^T fragments (B operand): lane (q + 32 hl) holds Q[q][ks*KSTEP + hl*KPL ..].
   typename M::frag qf[NKS];
   {
-    const int qi = min(my_i, a.n - 1);
-    const T* qp = reinterpret_cast<const T*>(a.q) + (((size_t)b * a.n + qi) * a.Hq + h) * D;
+    const int qi = min(my_i, nb - 1);
+    const T* qp = reinterpret_cast<const T*>(a.q) + (((size_t)base + qi) * a.Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[ks] = load_frag<T>(qp + ks * KSTEP + hl * KPL);
   }
@@ -182,14 +186,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
   for (int t = t_begin; t < t_end; ++t) {
     const bool cart = t < n_ct;
     const int j0 = cart ? t * kBN : (t - n_ct) * kBN;
-    const int rows = cart ? min(kBN, a.p - j0) : min(kBN, a.n - j0);
+    const int rows = cart ? min(kBN, a.p - j0) : min(kBN, nb - j0);
     __syncthreads();
     if (cart) {
       const TR* kb = reinterpret_cast<const TR*>(a.k_cart) + ((size_t)j0 * a.Hkv + kv) * D;
       const TR* vb = reinterpret_cast<const TR*>(a.v_cart) + ((size_t)j0 * a.Hkv + kv) * D;
       stage_tile<T, TR, D>(Ks, Vt, kb, vb, tok_stride, rows, tid);
     } else {
-      const size_t off = (((size_t)b * a.n + j0) * a.Hkv + kv) * D;
+      const size_t off = (((size_t)base + j0) * a.Hkv + kv) * D;
       stage_tile<T, T, D>(Ks, Vt, reinterpret_cast<const T*>(a.k_tok) + off,
                           reinterpret_cast<const T*>(a.v_tok) + off, tok_stride, rows, tid);
     }
@@ -258,12 +262,12 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
       }
   }
 
-  if (!wave_active || my_i >= a.n) return;
+  if (!wave_active || my_i >= nb) return;
   l_run = wave_sum_halves(l_run);
   const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   if (a.n_splits == 1) {
-    T* op = reinterpret_cast<T*>(a.out) + (((size_t)b * a.n + my_i) * a.Hq + h) * D;
+    T* op = reinterpret_cast<T*>(a.out) + (((size_t)base + my_i) * a.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -461,10 +465,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int pb = wave / a.hpw;
   const int h = kv * a.g + hg * a.hpw + hw;
   const int i0 = (qb * a.wph + pb) * 32;
-  const bool wave_active = i0 < a.n;
+  const int base = a.seg.base(b, a.n);   // the sequence's first token row
+  const int nb = a.seg.len(b, a.n);      // and its length
+  if (qb * a.wph * 32 >= nb) return;     // no query of this workgroup exists
+  const bool wave_active = i0 < nb;
   const int my_i = i0 + l32;
 
-  const int wg_last = min(a.n, (qb + 1) * a.wph * 32) - 1;
+  const int wg_last = min(nb, (qb + 1) * a.wph * 32) - 1;
   const int n_ct = (a.p + kBN - 1) / kBN;
   const int nt = n_ct + wg_last / kBN + 1;
   // with a sliding window the tiles before the workgroup's first window are
@@ -475,14 +482,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   // first position the wave's first query sees (no window: far below 0)
   const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
-  const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, a.B, a.n, a.p, a.Hkv, b, kv);
+  const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, base, nb, a.p, a.Hkv, kv);
   const KvMap<D> kmap(wave, lane);
   if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
 
   bf16x8 qf[NKS];
   {
-    const int qi = min(my_i, a.n - 1);
-    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + (((size_t)b * a.n + qi) * a.Hq + h) * D;
+    const int qi = min(my_i, nb - 1);
+    const bf16* qp = reinterpret_cast<const bf16*>(a.q) + (((size_t)base + qi) * a.Hq + h) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + hl * 8);
@@ -504,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (t + 1 < t_end) kv_issue<D>(kmap, K1, V1, t + 1, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
     {
-      const KvTile f = kv_tile(t, n_ct, a.p, a.n);
+      const KvTile f = kv_tile(t, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
         fwd_compute<D>(lds_addr(K0), lds_addr(V0), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
                        win_lo);
@@ -515,19 +522,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (t + 2 < t_end) kv_issue<D>(kmap, K0, V0, t + 2, n_ct, src, wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     {
-      const KvTile f = kv_tile(t + 1, n_ct, a.p, a.n);
+      const KvTile f = kv_tile(t + 1, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
         fwd_compute<D>(lds_addr(K1), lds_addr(V1), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
                        win_lo);
     }
   }
 
-  if (!wave_active || my_i >= a.n) return;
+  if (!wave_active || my_i >= nb) return;
   l_run = wave_sum_halves(l_run);
   const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
   if (a.n_splits == 1) {
-    bf16* op = reinterpret_cast<bf16*>(a.out) + (((size_t)b * a.n + my_i) * a.Hq + h) * D;
+    bf16* op = reinterpret_cast<bf16*>(a.out) + (((size_t)base + my_i) * a.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -566,6 +573,7 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(FwdArgs a) {
   const int bi = row / a.Hq;
   const int i = bi % a.n;
   const int b = bi / a.n;
+  if (i >= a.seg.len(b, a.n)) return;     // past a packed segment's end
   const size_t lrow = ((size_t)b * a.Hq + h) * a.n + i;
   const size_t lstride = (size_t)a.B * a.Hq * a.n;
   const size_t ostride = (size_t)a.B * a.n * a.Hq * D;
@@ -589,7 +597,8 @@ __global__ __launch_bounds__(256) void attn_fwd_combine(FwdArgs a) {
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  T* out = reinterpret_cast<T*>(a.out) + (size_t)row * D + sub * EPL;
+  T* out = reinterpret_cast<T*>(a.out) + (((size_t)a.seg.base(b, a.n) + i) * a.Hq + h) * D +
+           sub * EPL;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) out[e] = from_f32<T>(o[e] * inv);
   if (sub == 0) a.lse[lrow] = mx + logf(tot);
@@ -672,6 +681,7 @@ hipError_t launch_fwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.B = d.B; a.n = d.n; a.p = d.p; a.Hq = d.Hq; a.Hkv = d.Hkv; a.g = d.Hq / d.Hkv;
   a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb; a.n_splits = pl.n_splits;
   a.window = d.window;
+  a.seg = d.seg;
   a.scale_log2 = d.scale * kLog2e;
   if (d.tok_bf16)
     return d.D == 128 ? launch_fwd_bf16<128>(a, pl, st) : launch_fwd_bf16<64>(a, pl, st);

@@ -73,6 +73,19 @@ int check_shape(const cart_attn_shape* s) {
   if (s->tok_dtype == CART_F32 && s->row_dtype != CART_F32)
     return fail(CART_ERR_UNSUPPORTED, "f32 tokens need f32 cartridge rows");
   if (s->window < 0) return fail(CART_ERR_INVALID_ARG, "window (%d) must be >= 0", s->window);
+  if (s->seg_lens) {
+    if (s->batch > kMaxSegs)
+      return fail(CART_ERR_UNSUPPORTED, "%d packed segments (at most %d)", s->batch, kMaxSegs);
+    long long total = 0;
+    for (int b = 0; b < s->batch; ++b) {
+      if (s->seg_lens[b] < 1 || s->seg_lens[b] > s->q_seq)
+        return fail(CART_ERR_INVALID_ARG, "segment %d has length %d (1..q_seq=%d)", b,
+                    s->seg_lens[b], s->q_seq);
+      total += s->seg_lens[b];
+    }
+    if (total * s->n_q_heads * s->head_dim > kMaxElems)
+      return fail(CART_ERR_UNSUPPORTED, "packed tensor too large");
+  }
   const long long qe = (long long)s->batch * s->q_seq * s->n_q_heads * s->head_dim;
   const long long ce = (long long)s->p * s->n_kv_heads * s->head_dim;
   if (qe > kMaxElems || ce > kMaxElems)
@@ -91,6 +104,11 @@ AttnDims dims_of(const cart_attn_shape* s) {
   d.row_bf16 = s->row_dtype == CART_BF16;
   // a window reaching every row is no window (one plan, one code path)
   d.window = (s->window > 0 && (long long)s->window < (long long)s->p + s->q_seq) ? s->window : 0;
+  d.seg = Segs{};
+  if (s->seg_lens) {
+    d.seg.packed = s->batch;
+    for (int b = 0; b < s->batch; ++b) d.seg.off[b + 1] = d.seg.off[b] + s->seg_lens[b];
+  }
   return d;
 }
 
@@ -253,8 +271,42 @@ int cart_rope_tokens(void* q, void* k, cart_dtype dt, int32_t batch, int32_t seq
     return fail(CART_ERR_ALIGNMENT, "pos_offsets is not 4-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   return hip_result(launch_rope(q, k, dt == CART_BF16, batch, seq, n_q_heads, k ? n_kv_heads : 0,
-                                head_dim, pos_base, pos_offsets, theta, inverse != 0, st),
+                                head_dim, pos_base, pos_offsets, theta, inverse != 0, nullptr, st),
                     st, "cart_rope_tokens");
+}
+
+int cart_rope_tokens_packed(void* q, void* k, cart_dtype dt, int32_t n_segs,
+                            const int32_t* seg_lens, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int32_t pos_base, double theta, int32_t inverse,
+                            void* stream) {
+  if (n_segs < 1 || n_segs > kMaxSegs)
+    return fail(CART_ERR_INVALID_ARG, "n_segs (%d) must lie in [1, %d]", n_segs, kMaxSegs);
+  if (!seg_lens) return fail(CART_ERR_INVALID_ARG, "seg_lens is NULL");
+  Segs sg{};
+  sg.packed = n_segs;
+  for (int b = 0; b < n_segs; ++b) {
+    if (seg_lens[b] < 1) return fail(CART_ERR_INVALID_ARG, "segment %d has length %d", b, seg_lens[b]);
+    if ((long long)sg.off[b] + seg_lens[b] > 0x7fffffffLL)
+      return fail(CART_ERR_UNSUPPORTED, "too many packed rows");
+    sg.off[b + 1] = sg.off[b] + seg_lens[b];
+  }
+  const int T = sg.off[n_segs];
+  // the remaining checks are cart_rope_tokens' for one sequence of T rows
+  if (!valid_dtype(dt)) return fail(CART_ERR_INVALID_ARG, "unknown dtype");
+  if (n_q_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_q_heads must be >= 1");
+  if (k && n_kv_heads < 1) return fail(CART_ERR_INVALID_ARG, "n_kv_heads must be >= 1");
+  if (!valid_head_dim(head_dim))
+    return fail(CART_ERR_UNSUPPORTED, "head_dim %d not built (64 or 128)", head_dim);
+  if (!(theta > 0.0) || isinf(theta)) return fail(CART_ERR_INVALID_ARG, "theta must be > 0");
+  if (pos_base < 0) return fail(CART_ERR_INVALID_ARG, "pos_base must be >= 0");
+  if ((long long)T * (n_q_heads + (k ? n_kv_heads : 0)) * head_dim > kMaxElems)
+    return fail(CART_ERR_UNSUPPORTED, "tensor too large");
+  CHECK(need_ptr(q, "q"));
+  CHECK(opt_ptr(k, "k"));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_rope(q, k, dt == CART_BF16, 1, T, n_q_heads, k ? n_kv_heads : 0,
+                                head_dim, pos_base, nullptr, theta, inverse != 0, &sg, st),
+                    st, "cart_rope_tokens_packed");
 }
 
 namespace {

@@ -2,9 +2,9 @@
 // appending rows, and the single-token decode step.
 //
 // Source: "Cartridges: trained KV-prefix corpus compression", section
-// "Semantics (pinned to the reference implementation)", serving: the whole
-// prefix is written into an empty KV cache, converted to the cache dtype, the
-// cache is advanced to p and a normal decode continues at position p; section
+// "Semantics (pinned to the reference implementation)", serving: an empty KV
+// cache receives all p prefix rows in its own dtype, its length becomes p,
+// and ordinary decoding resumes at position p; section
 // "Composition": appending to the cache is the primitive; section "Evidence":
 // decode behind the written prefix matches the trainer's cartridge eval.
 //

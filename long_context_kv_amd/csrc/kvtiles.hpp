@@ -45,19 +45,19 @@ struct KvSrc {
   int p, n;
 };
 
+// base: the sequence's first token row; n: its length.
 template <int D>
 __device__ __forceinline__ KvSrc<D> kv_src(const void* k_cart, const void* v_cart,
-                                           const void* k_tok, const void* v_tok, int B, int n,
-                                           int p, int Hkv, int b, int kv) {
+                                           const void* k_tok, const void* v_tok, int base, int n,
+                                           int p, int Hkv, int kv) {
   KvSrc<D> s;
   s.kc = reinterpret_cast<const bf16*>(k_cart) + (size_t)kv * D;
   s.vc = reinterpret_cast<const bf16*>(v_cart) + (size_t)kv * D;
-  s.kt = reinterpret_cast<const bf16*>(k_tok) + ((size_t)b * n * Hkv + kv) * D;
-  s.vt = reinterpret_cast<const bf16*>(v_tok) + ((size_t)b * n * Hkv + kv) * D;
+  s.kt = reinterpret_cast<const bf16*>(k_tok) + ((size_t)base * Hkv + kv) * D;
+  s.vt = reinterpret_cast<const bf16*>(v_tok) + ((size_t)base * Hkv + kv) * D;
   s.row_stride = (size_t)Hkv * D;
   s.p = p;
   s.n = n;
-  (void)B;
   return s;
 }
 

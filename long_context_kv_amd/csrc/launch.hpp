@@ -9,6 +9,19 @@
 
 namespace cartattn {
 
+// Where each sequence's token rows are. A uniform batch: sequence b at rows
+// b n .. b n + n - 1. Packed segments (at most kMaxSegs): segment b at rows
+// off[b] .. off[b+1] - 1 of one packed tensor, of length off[b+1] - off[b]
+// (<= n, the longest). Passed by value to the kernels.
+constexpr int kMaxSegs = 64;
+struct Segs {
+  int packed;             // 0: a uniform batch; else the number of segments
+  int off[kMaxSegs + 1];
+  __host__ __device__ int base(int b, int n) const { return packed ? off[b] : b * n; }
+  __host__ __device__ int len(int b, int n) const { return packed ? off[b + 1] - off[b] : n; }
+  __host__ __device__ int rows(int B, int n) const { return packed ? off[B] : B * n; }
+};
+
 struct AttnDims {
   int B, n, p, f;       // batch, q_seq, cartridge rows, frozen rows
   int Hq, Hkv, D;       // heads and head_dim
@@ -16,6 +29,7 @@ struct AttnDims {
   bool tok_bf16;        // token tensors are bf16 (else f32)
   bool row_bf16;        // cartridge rows are bf16 (else f32)
   int window;           // > 0: sliding window of positions (0: none)
+  Segs seg;             // token rows of each sequence (uniform or packed)
 };
 
 // Forward launch plan; the workspace size and the launch both derive from it.
@@ -37,6 +51,7 @@ struct BwdPlan {
   // token tiles, at most kv_stmax per token tile.
   int kv_target, kv_splits_c, kv_ptok, kv_stmax, grid_kv;
   int kv_cart_pieces;   // dK/dV pieces of one kv head's cartridge tiles
+  int kv_tok_pieces;    // dK/dV pieces of one kv head's token tiles (all sequences)
   int hpw, wph, n_hg, n_qb, q_splits, grid_q;     // query-major dQ kernel
   size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes, tok_part_bytes, dq_part_bytes, cnt_bytes;
 };
@@ -52,9 +67,11 @@ hipError_t launch_bwd(const AttnDims& a, const void* q, const void* k_tok, const
 hipError_t launch_rows_to_bf16(const float* k, const float* v, __bf16* kb, __bf16* vb, size_t n,
                                hipStream_t st);
 
+// seg (nullable): packed segments, token t of segment b at position
+// pos_base + (t - off[b]); B, S are then 1 and the packed row count.
 hipError_t launch_rope(void* q, void* k, bool bf16, int B, int S, int Hq, int Hkv, int D,
                        int pos_base, const int32_t* pos_offsets, double theta, bool inverse,
-                       hipStream_t st);
+                       const Segs* seg, hipStream_t st);
 
 // q/k RMSNorm + RoPE (bwd = false: q_out/k_out = rotate(norm(q_in/k_in));
 // bwd = true: q_out/k_out = input gradients from the output gradients gq/gk).

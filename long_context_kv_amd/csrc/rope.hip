@@ -37,15 +37,26 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
                                                    int S, int Hq, int Hkv, int pos_base,
                                                    const int32_t* __restrict__ pos_offsets,
-                                                   RopeFreq fr, float sign) {
+                                                   RopeFreq fr, float sign, Segs seg) {
   constexpr int HALF = D / 2;
   constexpr int TPR = HALF / 4;      // threads per head row (4 pairs each)
   constexpr int RPP = 256 / TPR;     // head rows per pass
   typedef typename Vec4<T>::type V4;
   __shared__ float cs[HALF], sn[HALF];
-  const int tok = blockIdx.x;        // b * S + i
-  const int b = tok / S;
-  const int i = tok % S;
+  const int tok = blockIdx.x;        // b * S + i, or the packed row
+  int b = tok / S;
+  int i = tok % S;
+  if (seg.packed) {
+    // the segment holding the row (off[] ascending): positions restart at
+    // pos_base in every segment
+    int lo = 0, hi = seg.packed;     // packed = the number of segments
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (seg.off[mid] <= tok) lo = mid; else hi = mid;
+    }
+    b = lo;
+    i = tok - seg.off[lo];
+  }
   const int k4 = 4 * (threadIdx.x % TPR);
   const int hsub = threadIdx.x / TPR;
   T* qr = q + (size_t)tok * Hq * D;
@@ -64,7 +75,8 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
     khi = *reinterpret_cast<const V4*>(kr + (size_t)hsub * D + HALF + k4);
   }
   if (threadIdx.x < HALF) {
-    const long long pos = (long long)pos_base + (pos_offsets ? pos_offsets[b] : 0) + i;
+    const long long pos =
+        (long long)pos_base + (pos_offsets && !seg.packed ? pos_offsets[b] : 0) + i;
     const double ang = (double)pos * fr.inv_freq[threadIdx.x];
     constexpr double kTwoPi = 6.283185307179586476925286766559;
     const double r = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
@@ -100,11 +112,13 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
 
 template <typename T, int D>
 hipError_t launch_t(void* q, void* k, int B, int S, int Hq, int Hkv, int pos_base,
-                    const int32_t* pos_offsets, double theta, bool inverse, hipStream_t st) {
+                    const int32_t* pos_offsets, double theta, bool inverse, const Segs& seg,
+                    hipStream_t st) {
   RopeFreq fr{};
   for (int kk = 0; kk < D / 2; ++kk) fr.inv_freq[kk] = exp(-2.0 * (double)kk / (double)D * log(theta));
   CART_LAUNCH("rope", (rope_kernel<T, D>), B * S, 256, 0, st, reinterpret_cast<T*>(q),
-              reinterpret_cast<T*>(k), S, Hq, Hkv, pos_base, pos_offsets, fr, inverse ? -1.f : 1.f);
+              reinterpret_cast<T*>(k), S, Hq, Hkv, pos_base, pos_offsets, fr, inverse ? -1.f : 1.f,
+              seg);
   return hipGetLastError();
 }
 
@@ -112,12 +126,14 @@ hipError_t launch_t(void* q, void* k, int B, int S, int Hq, int Hkv, int pos_bas
 
 hipError_t launch_rope(void* q, void* k, bool bf16_, int B, int S, int Hq, int Hkv, int D,
                        int pos_base, const int32_t* pos_offsets, double theta, bool inverse,
-                       hipStream_t st) {
+                       const Segs* seg, hipStream_t st) {
+  Segs sg{};
+  if (seg) sg = *seg;
   if (bf16_)
-    return D == 128 ? launch_t<bf16, 128>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, st)
-                    : launch_t<bf16, 64>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, st);
-  return D == 128 ? launch_t<float, 128>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, st)
-                  : launch_t<float, 64>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, st);
+    return D == 128 ? launch_t<bf16, 128>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, sg, st)
+                    : launch_t<bf16, 64>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, sg, st);
+  return D == 128 ? launch_t<float, 128>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, sg, st)
+                  : launch_t<float, 64>(q, k, B, S, Hq, Hkv, pos_base, pos_offsets, theta, inverse, sg, st);
 }
 
 }  // namespace cartattn

@@ -18,12 +18,12 @@ Sources (titles of the pages the method is described on):
   K/V of shape [p, kv_head, d] in KV-cache space, keys already rotated at
   positions 0..p-1 and never rotated again; real tokens at RoPE positions
   p, p+1, ...; row 0 a frozen constant; attention over
-  concat(sink, trainable, tokens) with the end-aligned causal mask
-  (source_offset = kv_seq - q_seq), so every query sees the whole cartridge
-  and is causal over real tokens; an f32-KV backward routes gradients through
-  the concat into the trainable rows; serving writes the prefix into an empty
-  cache (converted to the cache dtype), advances it to p and decodes from
-  position p.
+  concat(sink, trainable, tokens) with the causal mask aligned to the end
+  (source_offset = kv_seq - q_seq): all prefix rows are visible to each
+  query, and among the tokens a query reaches itself and the earlier ones;
+  the backward in f32 carries gradients through the concat into the
+  trainable rows; for serving, an empty cache takes the p prefix rows in its
+  own dtype, its length becomes p, and decoding resumes at position p.
 * Same page, section "Evidence": gradcheck with kv_seq > q_seq and GQA;
   zero-training prefill equivalence; serving parity of decode behind the
   written prefix.
@@ -277,9 +277,9 @@ def causal_prefill_bwd(q, k, v, dout, scale: float = 0.0):
 
 
 # --------------------------------------------------------------------------
-# Serving ("Semantics", serving: the prefix is written into an empty cache,
-# converted to the cache dtype, the cache is advanced to p and decode goes on
-# at position p; "Evidence", serving parity).
+# Serving ("Semantics", serving: an empty cache takes the prefix rows in its
+# own dtype, its length becomes p, decoding resumes at position p;
+# "Evidence", serving parity).
 # --------------------------------------------------------------------------
 
 def round_bf16(x):

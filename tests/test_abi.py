@@ -411,3 +411,34 @@ def test_window_schedule_and_validation():
     wide = C.cart_attn_schedule_query(_shape(batch=1, q_seq=4096, p=16384, n_q_heads=16,
                                              n_kv_heads=8, head_dim=128, window=20480))
     assert wide.bwd_kv_grid == full.bwd_kv_grid     # a window reaching every row is none
+
+
+def test_packed_validation_and_schedule():
+    lens = (ctypes.c_int32 * 3)(10, 0, 5)
+    s = _shape(batch=3, q_seq=10)
+    s.seg_lens = lens
+    assert _fwd(s) == C.CART_ERR_INVALID_ARG            # a segment of length 0
+    lens[1] = 11
+    assert _fwd(s) == C.CART_ERR_INVALID_ARG            # longer than q_seq
+    lens[1] = 7
+    assert L.cart_attn_workspace_size(ctypes.byref(s), 1) > 0
+    many = (ctypes.c_int32 * 65)(*([1] * 65))
+    s65 = _shape(batch=65, q_seq=1)
+    s65.seg_lens = many
+    assert _fwd(s65) == C.CART_ERR_UNSUPPORTED
+    r = L.cart_rope_tokens_packed(FAKE, None, C.CART_BF16, 0, lens, 4, 2, 64, 0, 1e6, 0, None)
+    assert r == C.CART_ERR_INVALID_ARG
+    r = L.cart_rope_tokens_packed(FAKE, None, C.CART_BF16, 3, None, 4, 2, 64, 0, 1e6, 0, None)
+    assert r == C.CART_ERR_INVALID_ARG
+    # packed segments of equal length schedule exactly like the batch
+    eq = (ctypes.c_int32 * 4)(*([512] * 4))
+    sp = _shape(batch=4, q_seq=512, p=2048, n_q_heads=16, n_kv_heads=8, head_dim=128)
+    sp.seg_lens = eq
+    sb = _shape(batch=4, q_seq=512, p=2048, n_q_heads=16, n_kv_heads=8, head_dim=128)
+    a, b = C.cart_attn_schedule_query(sp), C.cart_attn_schedule_query(sb)
+    assert [getattr(a, f) for f, _ in a._fields_] == [getattr(b, f) for f, _ in b._fields_]
+    # ragged segments: fewer token tiles than the padded batch would have
+    rag = (ctypes.c_int32 * 4)(512, 100, 30, 250)
+    sr = _shape(batch=4, q_seq=512, p=2048, n_q_heads=16, n_kv_heads=8, head_dim=128)
+    sr.seg_lens = rag
+    assert C.cart_attn_schedule_query(sr).bwd_kv_grid < b.bwd_kv_grid
