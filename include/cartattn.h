@@ -462,8 +462,9 @@ size_t cart_decode_noalloc_max_bytes(void);
  * "attn_bwd" (dK/dV, including the reduction of key tiles cut into pieces,
  * for bf16 tokens), "attn_bwd_dq" (dQ of bf16 tokens), "bwd_dq_combine",
  * "bwd_dq_finalize" (dQ of f32 tokens), "bwd_cart_reduce" (f32 tokens),
- * "cache_append", "decode_append",
- * "decode", "decode_merge". cart_timing_enable clears earlier records (after
+ * "cache_append", "decode_append", "decode", "decode_merge", "qk_norm_rope",
+ * "qk_norm_rope_bwd", "adam_rows", "compose_rows", "zero_frozen" (the
+ * per-part frozen rows of cart_attn_bwd_composed). cart_timing_enable clears earlier records (after
  * waiting for them). cart_timing_query waits for the recorded events of one
  * kernel name and returns their summed duration (ms) and count.
  * ------------------------------------------------------------------------ */
