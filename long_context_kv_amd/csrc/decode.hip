@@ -37,6 +37,7 @@ constexpr int kPage = 16;
 constexpr int kDecThreads = 256;
 constexpr int kUnroll = 4;   // passes per group of loads
 constexpr int kMaxPps = 256; // pages per split at most (a launch plan bound)
+constexpr int kPartHead = 4; // floats before a split partial's accumulator (m, l, 2 unused)
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -105,7 +106,7 @@ struct DecArgs {
   CacheDims c;
   const bf16* q;       // [n_seqs][kq][Hq][D]
   bf16* out;           // [n_seqs][kq][Hq][D]
-  float* part;         // [n_seqs][kq * Hq][max_splits][D + 2]: m, l, acc[D]
+  float* part;         // [n_seqs][kq * Hq][max_splits][kPartHead + D]: m, l, -, -, acc[D]
   int Hq, g, pps, max_splits;
   int kq;              // query tokens per sequence (1: decode; > 1: verify)
   int n_chunks;        // workgroups per (sequence, kv head, split): query rows / R
@@ -321,9 +322,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
     if (r >= n_rows) continue;
     const int tok = r / a.g;
     float* pp = a.part + ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + r % a.g) * a.max_splits +
-                          split) * (D + 2);
+                          split) * (kPartHead + D);
     if (dd == 0) { pp[0] = mx; pp[1] = lt; }
-    pp[2 + dd] = at;
+    pp[kPartHead + dd] = at;
   }
 }
 
@@ -336,23 +337,307 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   const int len = min(a.c.seq_lens[s], a.c.max_pages * kPage);
   const int pages = (len + kPage - 1) / kPage;
   const int ns = min(a.max_splits, (pages + a.pps - 1) / a.pps);
-  const float* pp = a.part + (size_t)sh * a.max_splits * (D + 2);
+  constexpr int PS = kPartHead + D;   // floats per partial
+  const float* pp = a.part + (size_t)sh * a.max_splits * PS;
   float mx = -INFINITY;
-  for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * (D + 2)]);
+  for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * PS]);
   const float mu = (mx == -INFINITY) ? 0.f : mx;
   float lt = 0.f;
   float o[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
   for (int t = 0; t < ns; ++t) {
-    const float w = exp2f(pp[t * (D + 2)] - mu);
-    lt += w * pp[t * (D + 2) + 1];
+    const float w = exp2f(pp[t * PS] - mu);
+    lt += w * pp[t * PS + 1];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) o[e] += w * pp[t * (D + 2) + 2 + lane + 64 * e];
+    for (int e = 0; e < D / 64; ++e) o[e] += w * pp[t * PS + kPartHead + lane + 64 * e];
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) a.out[(size_t)sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
+}
+
+// ---- MFMA decode / verify -------------------------------------------------
+// A verify step has kq * g query rows per (sequence, kv head); the VALU
+// kernel above takes at most 8 of them per workgroup and so reads every K/V
+// byte once per 8 rows. This kernel takes up to 32 rows as the columns of
+// 32x32x16 bf16 MFMAs, so a K/V byte is read once for all of them: over
+// tiles of two pages (32 keys), S^T = K Q^T, an online softmax per row (the
+// forward's, lazily rescaled), then O^T += V^T P^T with V^T taken by LDS
+// transpose reads. Each wave streams its own tiles (the waves of a
+// workgroup take alternate tiles of the split) through a private
+// double-buffered LDS ring filled by direct global->LDS loads, one 16-row
+// tile per page, so no barrier orders the page stream; the waves' states are
+// merged through LDS at the end and written as one split partial.
+constexpr int kMmaWaves = 1;
+
+template <int D, bool MASKED>
+__global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
+  using M = Mfma<bf16>;
+  using TL = Tile<D>;
+  constexpr int NKS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int PT = tile_elems<D, kPage>();   // bf16 elements of one page's LDS tile
+  constexpr int CH = PT / 8;                    // its 16-byte chunk positions
+  constexpr int NB = (CH + 63) / 64;            // 1 KiB copies per page tile
+  constexpr int LASTL = CH - 64 * (NB - 1);     // lanes of the last, partial copy
+  constexpr int NDMA = 2 * 2 * NB;              // copies per tile (2 pages, K and V)
+  static_assert(2 * PT == tile_elems<D, 2 * kPage>(), "two page tiles form one 32-row tile");
+  // [wave][stage][K, V][two page tiles]
+  __shared__ __align__(16) bf16 ring[kMmaWaves][2][2][2 * PT];
+  __shared__ int pg[kMaxPps];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hl = lane >> 5;
+
+  const int nb = a.max_splits;
+  const int lg = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lg % nb;
+  const int chunk_id = (lg / nb) % a.n_chunks;
+  const int kv = (lg / (nb * a.n_chunks)) % a.c.Hkv;
+  const int s = lg / (nb * a.n_chunks * a.c.Hkv);
+  const int len = a.c.seq_lens[s];
+  const int n_rows = a.kq * a.g;
+  const int len_c = min(len, a.c.max_pages * kPage);
+  const int pages = (len_c + kPage - 1) / kPage;
+  const int ns = min(nb, (pages + a.pps - 1) / a.pps);
+  const int pb = split < ns ? (int)((long long)split * pages / ns) : pages;
+  const int pe = split < ns ? (int)((long long)(split + 1) * pages / ns) : pages;
+  const int row_begin = pb * kPage;
+  const int row_end = min(len_c, pe * kPage);
+  const int n_pg = pe - pb;
+
+  // This lane's query row (column l32 of every MFMA): Q^T fragments, and the
+  // rows it may see (a verify token t sees rows below len - kq + t + 1).
+  const int my_row = chunk_id * 32 + l32;
+  const bool row_ok = my_row < n_rows;
+  bf16x8 qf[NKS];
+  int hi_row = row_end;
+  {
+    const int r = min(my_row, n_rows - 1);
+    const int tok = r / a.g;
+    const bf16* qp = a.q + (((size_t)s * a.kq + tok) * a.Hq + kv * a.g + r % a.g) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16 + hl * 8);
+      if (!row_ok) qf[ks] = bf16x8{};
+    }
+    if constexpr (MASKED) hi_row = min(hi_row, len - a.kq + tok + 1);
+    if (!row_ok) hi_row = 0;
+  }
+
+  // the split's physical pages (-1: outside the pool, read as zeros, masked)
+  for (int i = tid; i < n_pg; i += 64 * kMmaWaves) {
+    const int pgid = a.c.block_table[(size_t)s * a.c.max_pages + pb + i];
+    pg[i] = (pgid >= 0 && pgid < a.c.n_pages) ? pgid : -1;
+  }
+  __syncthreads();
+
+  // Copy map of a page tile: lane l of copy k writes chunk position 64 k + l,
+  // which holds (row, column chunk) of the page's 16 x D run; padding
+  // positions re-read chunk 0 of their row.
+  uint32_t src_off[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    int rr, cc;
+    TL::locate(64 * k + lane, rr, cc);
+    src_off[k] = (uint32_t)(rr * D + (cc < D / 8 ? cc : 0) * 8) * 2;
+  }
+  const bf16* kpool = reinterpret_cast<const bf16*>(a.c.k_pages);
+  const bf16* vpool = reinterpret_cast<const bf16*>(a.c.v_pages);
+  // Tile t of the split: pages 2t and 2t + 1. Rows at or past row_end read as
+  // zeros (the buffer range ends there), so no stale or non-finite bytes
+  // enter the products.
+  const int n_tiles = (n_pg + 1) / 2;
+  auto issue = [&](int t, int st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * t + h;
+      const int page = i < n_pg ? pg[i] : -1;
+      const int rows = page >= 0 ? min(kPage, max(0, row_end - (row_begin + i * kPage))) : 0;
+      const size_t base = ((size_t)max(page, 0) * a.c.Hkv + kv) * kPage * D;
+      const buf_rsrc rk = make_rsrc(kpool + base, (uint32_t)(rows * D * 2));
+      const buf_rsrc rv = make_rsrc(vpool + base, (uint32_t)(rows * D * 2));
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        if (k < NB - 1 || lane < LASTL) {
+          dma16_at(rk, src_off[k], ring[wave][st][0], (uint32_t)(h * PT * 2 + k * 1024));
+          dma16_at(rv, src_off[k], ring[wave][st][1], (uint32_t)(h * PT * 2 + k * 1024));
+        }
+      }
+    }
+  };
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  float m_ref = -INFINITY;   // log2-domain reference max of this lane's row
+  float l_run = 0.f;
+  const float c = a.scale_log2;
+
+  auto compute = [&](int t, int st) {
+    const uint32_t kst = lds_addr(ring[wave][st][0]);
+    const uint32_t vst = lds_addr(ring[wave][st][1]);
+    // S^T = K Q^T: K row fragments (row l32, 8 elements at 16 ks + 8 hl)
+    f32x16 sc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    const uint32_t kb = kst + TL::off(l32, 8 * hl);
+    bf16x8 kf[NKS];
+    static_for<NKS>([&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      kf[ks] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
+    });
+    lds_wait<0>();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) lds_tie(kf[ks]);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sc = M::mma(kf[ks], qf[ks], sc);
+    // V^T fragments of the two 16-key steps, by transpose reads
+    const uint32_t vb =
+        vst + TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    bf16x8 va[2][NDB];
+    static_for<2>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      static_for<NDB>([&](auto DB) {
+        constexpr int db = decltype(DB)::value;
+        constexpr int off = TL::rows(16 * j) + 2 * 32 * db;
+        va[j][db] = cat8(lds_tr4<off>(vb), lds_tr4<off + TL::rows(8)>(vb));
+      });
+    });
+    // keys lo <= k < hi of the tile are visible to this lane's row
+    const int row0 = row_begin + 32 * t;
+    const bool ok0 = pg[2 * t] >= 0;
+    const bool ok1 = 2 * t + 1 < n_pg && pg[2 * t + 1] >= 0;
+    const int lo = ok0 ? 0 : kPage;
+    const int hi = ok1 ? min(32, hi_row - row0) : min(kPage, hi_row - row0);
+    if (lo > 0 || hi < 32) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k = d_row(r, hl);
+        sc[r] = (k >= lo && k < hi) ? sc[r] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    const float mxs = wave_max_halves(mx) * c;
+    const bool grow = mxs > m_ref + 8.f;
+    if (__any(grow)) {
+      const float m_new = grow ? mxs : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -m_use));
+      sc[r] = pv;
+      l_run += pv;
+    }
+    lds_wait<0>();
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) lds_tie(va[j][db]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 pf = pack_regs<bf16>(sc, j);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = M::mma(va[j][db], pf, acc[db]);
+    }
+  };
+
+  // this wave's tiles: wave, wave + kMmaWaves, ... (two stages, static
+  // addresses: the loop is unrolled by two)
+  const int t0 = wave;
+  if (t0 < n_tiles) issue(t0, 0);
+  for (int t = t0; t < n_tiles; t += 2 * kMmaWaves) {
+    if (t + kMmaWaves < n_tiles) {
+      issue(t + kMmaWaves, 1);
+      CART_WAIT_VMCNT(NDMA);
+    } else {
+      CART_WAIT_VMCNT(0);
+    }
+    compute(t, 0);
+    const int t1 = t + kMmaWaves;
+    if (t1 >= n_tiles) break;
+    if (t1 + kMmaWaves < n_tiles) {
+      issue(t1 + kMmaWaves, 0);
+      CART_WAIT_VMCNT(NDMA);
+    } else {
+      CART_WAIT_VMCNT(0);
+    }
+    compute(t1, 1);
+  }
+  CART_WAIT_VMCNT(0);
+  l_run = wave_sum_halves(l_run);
+
+  // Merge the waves through LDS (the rings are free once every wave is here):
+  // red[w][row][d] holds wave w's unnormalised O, sm/sl its row max and sum.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(&ring[0][0][0][0]);
+  static_assert(sizeof(ring) >= (size_t)kMmaWaves * 32 * D * 4 + 2 * kMmaWaves * 32 * 4,
+                "the merge fits the rings");
+  float* sm = red + kMmaWaves * 32 * D;
+  float* sl = sm + kMmaWaves * 32;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const f32x4 v = {acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2],
+                       acc[db][4 * cc + 3]};
+      *reinterpret_cast<f32x4*>(red + ((size_t)wave * 32 + l32) * D + 32 * db + 8 * cc + 4 * hl) = v;
+    }
+  if (hl == 0) {
+    sm[wave * 32 + l32] = m_ref;
+    sl[wave * 32 + l32] = l_run;
+  }
+  __syncthreads();
+  constexpr int PS = kPartHead + D;
+  for (int e = tid; e < 32 * D; e += 64 * kMmaWaves) {
+    const int r = e / D;
+    const int dd = e % D;
+    const int row = chunk_id * 32 + r;
+    if (row >= n_rows) break;   // rows grow with e
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kMmaWaves; ++w) mx = fmaxf(mx, sm[w * 32 + r]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    float lt = 0.f, at = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMmaWaves; ++w) {
+      const float wt = exp2f(sm[w * 32 + r] - mu);
+      lt += sl[w * 32 + r] * wt;
+      at += red[((size_t)w * 32 + r) * D + dd] * wt;
+    }
+    const int tok = row / a.g;
+    float* pp = a.part +
+                ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + row % a.g) * a.max_splits + split) * PS;
+    if (dd == 0) { pp[0] = mx; pp[1] = lt; }
+    pp[kPartHead + dd] = at;
+  }
+}
+
+template <int D, bool MASKED>
+hipError_t launch_dec_mma(DecArgs a, hipStream_t st) {
+  a.n_chunks = (a.g * a.kq + 31) / 32;
+  const int grid = a.c.n_seqs * a.c.Hkv * a.n_chunks * a.max_splits;
+  CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED>), grid, 64 * kMmaWaves, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
+  return hipGetLastError();
 }
 
 template <int D, int G, bool MASKED>
@@ -374,6 +659,12 @@ inline int dec_rows(int g, int kq) {
 
 template <int D>
 hipError_t launch_dec_d(DecArgs a, hipStream_t st) {
+  // more than 4 query rows per kv head: the MFMA kernel, which reads K/V
+  // once for up to 32 of them (measured: as fast as the VALU kernel at 4
+  // rows, and half again as fast at 8, where the VALU kernel's per-row work
+  // holds it back)
+  if (a.g * a.kq > 4)
+    return a.kq == 1 ? launch_dec_mma<D, false>(a, st) : launch_dec_mma<D, true>(a, st);
   const int R = dec_rows(a.g, a.kq);
   a.n_chunks = (a.g * a.kq + R - 1) / R;
   if (a.kq == 1) {
@@ -451,7 +742,7 @@ DecodePlan plan_decode(const CacheDims& c, int Hq, int kq) {
   pps = (pps + 3) / 4 * 4;
   pl.pages_per_split = (int)pps;
   pl.max_splits = (int)((c.max_pages + pps - 1) / pps);
-  pl.part_bytes = (size_t)c.n_seqs * kq * Hq * pl.max_splits * (c.D + 2) * sizeof(float);
+  pl.part_bytes = (size_t)c.n_seqs * kq * Hq * pl.max_splits * (kPartHead + c.D) * sizeof(float);
   return pl;
 }
 

@@ -67,8 +67,12 @@ def test_one_token_verify_is_the_decode_step(C):
     b.close()
 
 
-CASES = [(g, k, d) for g, k in ((1, 8), (2, 3), (4, 2), (4, 4), (8, 4), (4, 16)) for d in (128,)]
-CASES += [(4, 4, 64)]
+# rows per kv head = g * k: up to 4 take the per-row VALU kernel, more the
+# MFMA kernel (32 rows per workgroup: 72 rows are three chunks, the last
+# ragged; 64 drafts is the largest verify step)
+CASES = [(g, k, d) for g, k in ((1, 3), (2, 2), (1, 8), (2, 3), (4, 2), (4, 4), (8, 4), (4, 16),
+                                (8, 9), (1, 64)) for d in (128,)]
+CASES += [(4, 4, 64), (2, 2, 64)]
 
 
 @pytest.mark.parametrize("g,k,d", CASES, ids=[f"g{g}-k{k}-d{d}" for g, k, d in CASES])
