@@ -43,18 +43,18 @@ PEAK_HBM_GBPS = 8000.0
 # HBM bytes per launch of a kernel on a workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE; read counts x 2.0 from a 1 GiB copy calibration),
 # summarised in profiles/hbm_bytes_long-cartridge-28l_and_decode.md and
-# profiles/hbm_bytes_layers_and_decode.md. A figure holds only
+# profiles/hbm_bytes_qwen3-layers.md. A figure holds only
 # for the kernel sources it was measured on: a mismatch of their hash reports
 # traffic as null.
 KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "qwen3-0.6b-layer"): (42.5e6, "455b4aa28c09e419"),
-    ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "455b4aa28c09e419"),
-    ("attn_bwd", "long-cartridge-28l"): (405.8e6, "455b4aa28c09e419"),
-    ("attn_fwd", "qwen3-8b-layer"): (234.5e6, "af9090a87cee9e9a"),
-    ("decode", "serving-decode"): (1225.6e6, "181d9c2273e0b279"),
+    ("attn_bwd", "long-cartridge-28l"): (405.9e6, "6b317bbf5982d54e"),
+    ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "6b317bbf5982d54e"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "6b317bbf5982d54e"),
+    ("attn_fwd", "long-cartridge-28l"): (128.3e6, "4d0973d6ac4dfd42"),
+    ("decode", "serving-decode"): (1225.7e6, "546e6c7bb7a3fc0d"),
 }
 
 
