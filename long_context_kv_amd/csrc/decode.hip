@@ -13,14 +13,18 @@
 // decode workgroup streams whole runs. block_table maps (seq, logical page)
 // to a physical page id.
 //
-// Decode is HBM-bound (4 flop per byte of K/V), so it uses no MFMA: one
-// workgroup per (sequence, kv head, split of the pages); a sequence's pages
-// are cut into ns = ceil(pages / pages-per-split) nearly equal splits, so
-// the workgroups of a step run about equally long. The q-heads of the
-// GQA group share every K/V byte read. Each thread owns one 8-element chunk
-// of one row per pass and keeps a private online-softmax state per q-head;
-// the states are merged with cross-lane shuffles and through LDS at the end,
-// and a second kernel merges the splits of a sequence by log-sum-exp.
+// Decode is HBM-bound (4 flop per byte of K/V at a GQA group of 4): one
+// one-wave workgroup per (sequence, kv head, split of the pages, chunk of up
+// to 32 query rows); a sequence's pages are cut into ns = ceil(pages /
+// pages-per-split) nearly equal splits, so the workgroups of a step run
+// about equally long, and the splits are sized so that a step's workgroups
+// are about as many as the GPU holds at once. The query rows of one kv head
+// (its GQA q-heads, times the draft tokens of a verify step) are the columns
+// of bf16 MFMAs, so each K/V byte is read once for all of them; the MFMA
+// work is idle most of the time, but it costs the wave almost no issue slots,
+// where per-row dot products on the VALU did (an earlier VALU kernel reached
+// 5.3 TB/s at 4 rows per kv head and a third less at 8). A second kernel
+// merges the splits of a sequence by log-sum-exp.
 #include <math.h>
 
 #include <mutex>
@@ -34,12 +38,8 @@ namespace cartattn {
 namespace {
 
 constexpr int kPage = 16;
-constexpr int kDecThreads = 256;
-constexpr int kUnroll = 4;   // passes per group of loads
-constexpr int kMaxPps = 256; // pages per split at most (a launch plan bound)
+constexpr int kMaxPps = 256; // pages per split at most
 constexpr int kPartHead = 4; // floats before a split partial's accumulator (m, l, 2 unused)
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 template <typename TS>
 __global__ __launch_bounds__(256) void cache_append_kernel(CacheDims c, int seq, int start,
@@ -113,221 +113,6 @@ struct DecArgs {
   float scale_log2;
 };
 
-// R query rows per workgroup: rows c R .. c R + R - 1 (chunk c) of the
-// (token, q-head) rows r = t g + j that read kv head kv; token t of a verify
-// step sees the stored rows below len - kq + t + 1 (MASKED; a plain decode
-// step sees every stored row).
-template <int D, int G, bool MASKED>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(DecArgs a) {
-  constexpr int CPR = D / 8;                 // chunks per row
-  constexpr int RPP = kDecThreads / CPR;     // rows per pass
-  constexpr int GPW = 64 / CPR;              // row groups per wave
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int chunk = tid % CPR;
-  const int rsub = tid / CPR;
-
-  const int nb = a.max_splits;
-  const int lg = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = lg % nb;
-  const int chunk_id = (lg / nb) % a.n_chunks;
-  const int kv = (lg / (nb * a.n_chunks)) % a.c.Hkv;
-  const int s = lg / (nb * a.n_chunks * a.c.Hkv);
-  const int len = a.c.seq_lens[s];
-  const int n_rows = a.kq * a.g;   // query rows of this (sequence, kv head)
-  // the sequence's pages in ns nearly equal splits (ns as the merge counts them)
-  const int len_c = min(len, a.c.max_pages * kPage);
-  const int pages = (len_c + kPage - 1) / kPage;
-  const int ns = min(nb, (pages + a.pps - 1) / a.pps);
-  const int pb = split < ns ? (int)((long long)split * pages / ns) : pages;
-  const int pe = split < ns ? (int)((long long)(split + 1) * pages / ns) : pages;
-  const int row_begin = pb * kPage;
-  const int row_end = min(len_c, pe * kPage);
-
-  // q chunks stay bf16: scores are bf16 x bf16 dot products accumulated in
-  // f32 (v_dot2), scaled afterwards.
-  bf16x8 qb[G];
-  int lim[G];   // rows below lim[j] are visible to query row j
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const int r = min(chunk_id * G + j, n_rows - 1);
-    const int tok = r / a.g;
-    qb[j] = *reinterpret_cast<const bf16x8*>(
-        a.q + (((size_t)s * a.kq + tok) * a.Hq + kv * a.g + r % a.g) * D + chunk * 8);
-    lim[j] = chunk_id * G + j < n_rows ? len - a.kq + tok + 1 : 0;
-  }
-  const float c = a.scale_log2;
-  // Online softmax per q-head with a lazily moved reference max m (log2
-  // domain): probabilities are exp2(score - m) <= 2^8, and acc, l are
-  // rescaled only when some score exceeds m by more than 8.
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-  }
-
-  // Physical pages of this split, validated once, into LDS: the K/V loads
-  // then depend on no other global load.
-  __shared__ int pg[kMaxPps];
-  const int n_pg = row_end > row_begin ? (row_end - row_begin + kPage - 1) / kPage : 0;
-  {
-    const int32_t* bt = a.c.block_table + (size_t)s * a.c.max_pages + row_begin / kPage;
-    for (int i = tid; i < n_pg; i += kDecThreads) {
-      const int p = bt[i];
-      pg[i] = (p >= 0 && p < a.c.n_pages) ? p : -1;
-    }
-  }
-  __syncthreads();
-
-  // Rows are streamed kUnroll * RPP at a time; the raw 16-byte chunks of
-  // the next group are loaded before the current group is used, so two
-  // groups of loads are in flight per thread.
-  const bf16* kp = reinterpret_cast<const bf16*>(a.c.k_pages);
-  const bf16* vp = reinterpret_cast<const bf16*>(a.c.v_pages);
-  struct Grp { uint4 k[kUnroll], v[kUnroll]; bool ok[kUnroll]; int row[kUnroll]; };
-  // Loads are unconditional, so the wait counts stay exact: a row past the
-  // split re-reads the split's last row (a cache hit) and a row on an invalid
-  // page reads page 0; both are masked.
-  auto load_grp = [&](int r0, Grp& x) {
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int row = r0 + u * RPP + rsub;
-      const int rr = min(row, row_end - 1);
-      const int page = pg[(rr - row_begin) / kPage];
-      x.ok[u] = row < row_end && page >= 0;
-      if constexpr (MASKED) x.row[u] = row;
-      const size_t off = (((size_t)max(page, 0) * a.c.Hkv + kv) * kPage + rr % kPage) * D + chunk * 8;
-      x.k[u] = *reinterpret_cast<const uint4*>(kp + off);
-      x.v[u] = *reinterpret_cast<const uint4*>(vp + off);
-    }
-  };
-  auto use_grp = [&](const Grp& x) {
-    float p[G][kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, x.k[u]);
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        float d = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 qa = {qb[j][2 * e], qb[j][2 * e + 1]};
-          const bf16x2 ka = {kb[2 * e], kb[2 * e + 1]};
-          d = __builtin_amdgcn_fdot2_f32_bf16(qa, ka, d, false);
-        }
-        d = row_sum<CPR>(d);
-        bool ok = x.ok[u];
-        if constexpr (MASKED) ok = ok && x.row[u] < lim[j];
-        p[j][u] = ok ? d * c : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float mx = p[j][0];
-#pragma unroll
-      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, p[j][u]);
-      if (mx > m[j] + 8.f) {   // per lane; taken rarely after the first rows
-        const float alpha = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - mx);
-        l[j] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
-        m[j] = mx;
-      }
-      const float mu = (m[j] == -INFINITY) ? 0.f : m[j];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        p[j][u] = __builtin_amdgcn_exp2f(p[j][u] - mu);
-        l[j] += p[j][u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, x.v[u]);
-      float vx[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vx[e] = (float)vb[e];
-#pragma unroll
-      for (int j = 0; j < G; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(p[j][u], vx[e], acc[j][e]);
-    }
-  };
-  constexpr int STEP = kUnroll * RPP;
-  if (row_begin < row_end) {
-    // ping-pong between two register groups: the loads of the next group are
-    // in flight while the current one is used
-    Grp ga, gb;
-    load_grp(row_begin, ga);
-    for (int r0 = row_begin;;) {
-      load_grp(r0 + STEP, gb);
-      use_grp(ga);
-      if ((r0 += STEP) >= row_end) break;
-      load_grp(r0 + STEP, ga);
-      use_grp(gb);
-      if ((r0 += STEP) >= row_end) break;
-    }
-  }
-
-  // Merge the row groups of a wave (lanes with the same chunk).
-#pragma unroll
-  for (int off = CPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float mo = __shfl_xor(m[j], off);
-      const float lo = __shfl_xor(l[j], off);
-      const float mn = fmaxf(m[j], mo);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float wa = exp2f(m[j] - mu);
-      const float wb = exp2f(mo - mu);
-      l[j] = l[j] * wa + lo * wb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] = acc[j][e] * wa + __shfl_xor(acc[j][e], off) * wb;
-      m[j] = mn;
-    }
-  }
-  (void)GPW;
-  // Merge the 4 waves through LDS.
-  __shared__ __align__(16) float sm[4][G];
-  __shared__ __align__(16) float sl[4][G];
-  __shared__ __align__(16) float sacc[4][G][D];
-  if (lane < CPR) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (lane == 0) { sm[wave][j] = m[j]; sl[wave][j] = l[j]; }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sacc[wave][j][chunk * 8 + e] = acc[j][e];
-    }
-  }
-  __syncthreads();
-  // Every thread finishes (head j, element d) pairs.
-  for (int t = tid; t < G * D; t += kDecThreads) {
-    const int j = t / D;
-    const int dd = t % D;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, sm[w][j]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float lt = 0.f, at = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float wt = exp2f(sm[w][j] - mu);
-      lt += sl[w][j] * wt;
-      at += sacc[w][j][dd] * wt;
-    }
-    const int r = chunk_id * G + j;
-    if (r >= n_rows) continue;
-    const int tok = r / a.g;
-    float* pp = a.part + ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + r % a.g) * a.max_splits +
-                          split) * (kPartHead + D);
-    if (dd == 0) { pp[0] = mx; pp[1] = lt; }
-    pp[kPartHead + dd] = at;
-  }
-}
-
 // out[s, h] = sum over the sequence's splits, weighted by exp2(m_split - M).
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
@@ -357,22 +142,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   for (int e = 0; e < D / 64; ++e) a.out[(size_t)sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
 }
 
-// ---- MFMA decode / verify -------------------------------------------------
-// A verify step has kq * g query rows per (sequence, kv head); the VALU
-// kernel above takes at most 8 of them per workgroup and so reads every K/V
-// byte once per 8 rows. This kernel takes up to 32 rows as the columns of
-// 32x32x16 bf16 MFMAs, so a K/V byte is read once for all of them: over
-// tiles of two pages (32 keys), S^T = K Q^T, an online softmax per row (the
-// forward's, lazily rescaled), then O^T += V^T P^T with V^T taken by LDS
-// transpose reads. Each wave streams its own tiles (the waves of a
-// workgroup take alternate tiles of the split) through a private
-// double-buffered LDS ring filled by direct global->LDS loads, one 16-row
-// tile per page, so no barrier orders the page stream; the waves' states are
-// merged through LDS at the end and written as one split partial.
-constexpr int kMmaWaves = 1;
+// ---- the decode / verify kernel --------------------------------------------
+// Up to 32 query rows (tokens x q-heads of one kv head) are the columns of
+// 32x32x16 bf16 MFMAs: over tiles of two pages (32 keys), S^T = K Q^T, an
+// online softmax per row (the forward's, lazily rescaled), then
+// O^T += V^T P^T with V^T taken by LDS transpose reads. One wave per
+// workgroup streams the split's tiles through a private LDS ring of NST
+// tiles filled by direct global->LDS loads (one 16-row tile per page), so no
+// barrier orders the page stream. The ring is the workgroup's only LDS: its
+// size (with the register count) sets how many workgroups a CU holds, and
+// HBM keeps streaming at full rate only while most of the step's workgroups
+// are resident at once.
+constexpr int kMmaWavesPerSimd = 2;   // register budget: waves per SIMD to fit
 
-template <int D, bool MASKED>
-__global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
+template <int D, bool MASKED, int NST>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kMmaWavesPerSimd)))
+void decode_mma_kernel(DecArgs a) {
   using M = Mfma<bf16>;
   using TL = Tile<D>;
   constexpr int NKS = D / 16;
@@ -383,13 +168,10 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
   constexpr int LASTL = CH - 64 * (NB - 1);     // lanes of the last, partial copy
   constexpr int NDMA = 2 * 2 * NB;              // copies per tile (2 pages, K and V)
   static_assert(2 * PT == tile_elems<D, 2 * kPage>(), "two page tiles form one 32-row tile");
-  // [wave][stage][K, V][two page tiles]
-  __shared__ __align__(16) bf16 ring[kMmaWaves][2][2][2 * PT];
-  __shared__ int pg[kMaxPps];
+  // [stage][K, V][two page tiles]
+  __shared__ __align__(16) bf16 ring[NST][2][2 * PT];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
 
@@ -409,6 +191,7 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
   const int row_begin = pb * kPage;
   const int row_end = min(len_c, pe * kPage);
   const int n_pg = pe - pb;
+  const int32_t* bt = a.c.block_table + (size_t)s * a.c.max_pages + pb;
 
   // This lane's query row (column l32 of every MFMA): Q^T fragments, and the
   // rows it may see (a verify token t sees rows below len - kq + t + 1).
@@ -429,13 +212,6 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
     if (!row_ok) hi_row = 0;
   }
 
-  // the split's physical pages (-1: outside the pool, read as zeros, masked)
-  for (int i = tid; i < n_pg; i += 64 * kMmaWaves) {
-    const int pgid = a.c.block_table[(size_t)s * a.c.max_pages + pb + i];
-    pg[i] = (pgid >= 0 && pgid < a.c.n_pages) ? pgid : -1;
-  }
-  __syncthreads();
-
   // Copy map of a page tile: lane l of copy k writes chunk position 64 k + l,
   // which holds (row, column chunk) of the page's 16 x D run; padding
   // positions re-read chunk 0 of their row.
@@ -448,15 +224,19 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
   }
   const bf16* kpool = reinterpret_cast<const bf16*>(a.c.k_pages);
   const bf16* vpool = reinterpret_cast<const bf16*>(a.c.v_pages);
-  // Tile t of the split: pages 2t and 2t + 1. Rows at or past row_end read as
-  // zeros (the buffer range ends there), so no stale or non-finite bytes
-  // enter the products.
+  // Tile t of the split: pages 2t and 2t + 1 (ids outside the pool read as
+  // zeros and are masked). Rows at or past row_end read as zeros too (the
+  // buffer range ends there), so no stale or non-finite bytes enter the
+  // products. Returns the tile's page-validity bits.
   const int n_tiles = (n_pg + 1) / 2;
   auto issue = [&](int t, int st) {
+    int okb = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * t + h;
-      const int page = i < n_pg ? pg[i] : -1;
+      int page = i < n_pg ? bt[i] : -1;
+      if (page >= a.c.n_pages) page = -1;
+      okb |= (page >= 0) << h;
       const int rows = page >= 0 ? min(kPage, max(0, row_end - (row_begin + i * kPage))) : 0;
       const size_t base = ((size_t)max(page, 0) * a.c.Hkv + kv) * kPage * D;
       const buf_rsrc rk = make_rsrc(kpool + base, (uint32_t)(rows * D * 2));
@@ -464,11 +244,12 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         if (k < NB - 1 || lane < LASTL) {
-          dma16_at(rk, src_off[k], ring[wave][st][0], (uint32_t)(h * PT * 2 + k * 1024));
-          dma16_at(rv, src_off[k], ring[wave][st][1], (uint32_t)(h * PT * 2 + k * 1024));
+          dma16_at(rk, src_off[k], ring[st][0], (uint32_t)(h * PT * 2 + k * 1024));
+          dma16_at(rv, src_off[k], ring[st][1], (uint32_t)(h * PT * 2 + k * 1024));
         }
       }
     }
+    return okb;
   };
 
   f32x16 acc[NDB];
@@ -480,9 +261,9 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
   float l_run = 0.f;
   const float c = a.scale_log2;
 
-  auto compute = [&](int t, int st) {
-    const uint32_t kst = lds_addr(ring[wave][st][0]);
-    const uint32_t vst = lds_addr(ring[wave][st][1]);
+  auto compute = [&](int t, int st, int okb) {
+    const uint32_t kst = lds_addr(ring[st][0]);
+    const uint32_t vst = lds_addr(ring[st][1]);
     // S^T = K Q^T: K row fragments (row l32, 8 elements at 16 ks + 8 hl)
     f32x16 sc;
 #pragma unroll
@@ -512,10 +293,8 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
     });
     // keys lo <= k < hi of the tile are visible to this lane's row
     const int row0 = row_begin + 32 * t;
-    const bool ok0 = pg[2 * t] >= 0;
-    const bool ok1 = 2 * t + 1 < n_pg && pg[2 * t + 1] >= 0;
-    const int lo = ok0 ? 0 : kPage;
-    const int hi = ok1 ? min(32, hi_row - row0) : min(kPage, hi_row - row0);
+    const int lo = (okb & 1) ? 0 : kPage;
+    const int hi = (okb & 2) ? min(32, hi_row - row0) : min(kPage, hi_row - row0);
     if (lo > 0 || hi < 32) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -558,128 +337,76 @@ __global__ __launch_bounds__(64 * kMmaWaves) void decode_mma_kernel(DecArgs a) {
     }
   };
 
-  // this wave's tiles: wave, wave + kMmaWaves, ... (two stages, static
-  // addresses: the loop is unrolled by two)
-  const int t0 = wave;
-  if (t0 < n_tiles) issue(t0, 0);
-  for (int t = t0; t < n_tiles; t += 2 * kMmaWaves) {
-    if (t + kMmaWaves < n_tiles) {
-      issue(t + kMmaWaves, 1);
-      CART_WAIT_VMCNT(NDMA);
-    } else {
+  if constexpr (NST == 1) {
+    for (int t = 0; t < n_tiles; ++t) {
+      const int okb = issue(t, 0);
       CART_WAIT_VMCNT(0);
+      compute(t, 0, okb);
     }
-    compute(t, 0);
-    const int t1 = t + kMmaWaves;
-    if (t1 >= n_tiles) break;
-    if (t1 + kMmaWaves < n_tiles) {
-      issue(t1 + kMmaWaves, 0);
-      CART_WAIT_VMCNT(NDMA);
-    } else {
-      CART_WAIT_VMCNT(0);
+  } else {
+    static_assert(NST == 2, "one or two stages");
+    // two stages with static addresses: the loop is unrolled by two
+    int ok0 = n_tiles > 0 ? issue(0, 0) : 0;
+    for (int t = 0; t < n_tiles; t += 2) {
+      int ok1 = 0;
+      if (t + 1 < n_tiles) {
+        ok1 = issue(t + 1, 1);
+        CART_WAIT_VMCNT(NDMA);
+      } else {
+        CART_WAIT_VMCNT(0);
+      }
+      compute(t, 0, ok0);
+      if (t + 1 >= n_tiles) break;
+      if (t + 2 < n_tiles) {
+        ok0 = issue(t + 2, 0);
+        CART_WAIT_VMCNT(NDMA);
+      } else {
+        CART_WAIT_VMCNT(0);
+      }
+      compute(t + 1, 1, ok1);
     }
-    compute(t1, 1);
   }
   CART_WAIT_VMCNT(0);
   l_run = wave_sum_halves(l_run);
 
-  // Merge the waves through LDS (the rings are free once every wave is here):
-  // red[w][row][d] holds wave w's unnormalised O, sm/sl its row max and sum.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(&ring[0][0][0][0]);
-  static_assert(sizeof(ring) >= (size_t)kMmaWaves * 32 * D * 4 + 2 * kMmaWaves * 32 * 4,
-                "the merge fits the rings");
-  float* sm = red + kMmaWaves * 32 * D;
-  float* sl = sm + kMmaWaves * 32;
+  // The split partial of this lane's row: m, l (lane half 0) and the
+  // unnormalised O, whose d = 32 db + d_row(r, hl) elements the lane holds
+  // in 4-element runs.
+  if (!row_ok) return;
+  const int tok = my_row / a.g;
+  float* pp = a.part + ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + my_row % a.g) * a.max_splits +
+                        split) * (kPartHead + D);
+  if (hl == 0) { pp[0] = m_ref; pp[1] = l_run; }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const f32x4 v = {acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2],
-                       acc[db][4 * cc + 3]};
-      *reinterpret_cast<f32x4*>(red + ((size_t)wave * 32 + l32) * D + 32 * db + 8 * cc + 4 * hl) = v;
-    }
-  if (hl == 0) {
-    sm[wave * 32 + l32] = m_ref;
-    sl[wave * 32 + l32] = l_run;
-  }
-  __syncthreads();
-  constexpr int PS = kPartHead + D;
-  for (int e = tid; e < 32 * D; e += 64 * kMmaWaves) {
-    const int r = e / D;
-    const int dd = e % D;
-    const int row = chunk_id * 32 + r;
-    if (row >= n_rows) break;   // rows grow with e
-    float mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kMmaWaves; ++w) mx = fmaxf(mx, sm[w * 32 + r]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float lt = 0.f, at = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMmaWaves; ++w) {
-      const float wt = exp2f(sm[w * 32 + r] - mu);
-      lt += sl[w * 32 + r] * wt;
-      at += red[((size_t)w * 32 + r) * D + dd] * wt;
-    }
-    const int tok = row / a.g;
-    float* pp = a.part +
-                ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + row % a.g) * a.max_splits + split) * PS;
-    if (dd == 0) { pp[0] = mx; pp[1] = lt; }
-    pp[kPartHead + dd] = at;
-  }
+    for (int cc = 0; cc < 4; ++cc)
+      *reinterpret_cast<f32x4*>(pp + kPartHead + 32 * db + 8 * cc + 4 * hl) =
+          f32x4{acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2], acc[db][4 * cc + 3]};
 }
+
+// Ring stages of the MFMA decode kernel. One stage (19 KiB of LDS at
+// D = 128, 188 registers) lets a CU hold eight of these one-wave workgroups,
+// so nearly all of a step's splits stream at once; two stages (the next
+// tile's copies in flight during a tile's arithmetic) need twice the LDS and
+// more registers, and the four workgroups a CU then holds streamed 15% slower
+// (4.8 against 5.6 TB/s on the 64-sequence serving cache).
+constexpr int kMmaStages = 1;
 
 template <int D, bool MASKED>
 hipError_t launch_dec_mma(DecArgs a, hipStream_t st) {
   a.n_chunks = (a.g * a.kq + 31) / 32;
   const int grid = a.c.n_seqs * a.c.Hkv * a.n_chunks * a.max_splits;
-  CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED>), grid, 64 * kMmaWaves, 0, st, a);
+  CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED, kMmaStages>), grid, 64, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
   return hipGetLastError();
-}
-
-template <int D, int G, bool MASKED>
-hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
-  const int grid = a.c.n_seqs * a.c.Hkv * a.n_chunks * a.max_splits;
-  CART_LAUNCH("decode", (decode_kernel<D, G, MASKED>), grid, kDecThreads, 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
-  return hipGetLastError();
-}
-
-// Rows per workgroup: the kv head's query rows (g per token, kq tokens), at
-// most 8 (the per-row online-softmax state lives in registers).
-inline int dec_rows(int g, int kq) {
-  const int n = g * kq;
-  return n >= 8 ? 8 : (n >= 4 ? 4 : (n >= 2 ? 2 : 1));
 }
 
 template <int D>
 hipError_t launch_dec_d(DecArgs a, hipStream_t st) {
-  // more than 4 query rows per kv head: the MFMA kernel, which reads K/V
-  // once for up to 32 of them (measured: as fast as the VALU kernel at 4
-  // rows, and half again as fast at 8, where the VALU kernel's per-row work
-  // holds it back)
-  if (a.g * a.kq > 4)
-    return a.kq == 1 ? launch_dec_mma<D, false>(a, st) : launch_dec_mma<D, true>(a, st);
-  const int R = dec_rows(a.g, a.kq);
-  a.n_chunks = (a.g * a.kq + R - 1) / R;
-  if (a.kq == 1) {
-    switch (R) {
-      case 1: return launch_dec_t<D, 1, false>(a, st);
-      case 2: return launch_dec_t<D, 2, false>(a, st);
-      case 4: return launch_dec_t<D, 4, false>(a, st);
-      default: return launch_dec_t<D, 8, false>(a, st);
-    }
-  }
-  switch (R) {
-    case 2: return launch_dec_t<D, 2, true>(a, st);
-    case 4: return launch_dec_t<D, 4, true>(a, st);
-    default: return launch_dec_t<D, 8, true>(a, st);
-  }
+  return a.kq == 1 ? launch_dec_mma<D, false>(a, st) : launch_dec_mma<D, true>(a, st);
 }
 
 }  // namespace
@@ -733,12 +460,19 @@ hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_
   return hipGetLastError();
 }
 
+// Pages per split: about as many (sequence, kv head, split) workgroups as
+// the GPU holds at once when every sequence is full (256 CUs x 8 one-wave
+// workgroups; fewer splits leave CUs short of streams, more run in a second
+// round: 6 or 8 splits per sequence instead of 4 measured 11% and 3% slower
+// on the 64-sequence serving cache), between 8 and kMaxPps pages.
+constexpr long long kResidentWgs = 256 * 8;
+
 DecodePlan plan_decode(const CacheDims& c, int Hq, int kq) {
   DecodePlan pl{};
   const long long work = (long long)c.n_seqs * c.Hkv * c.max_pages;
-  long long pps = (work + 2047) / 2048;
+  long long pps = (work + kResidentWgs - 1) / kResidentWgs;
   if (pps < 8) pps = 8;
-  if (pps > 256) pps = 256;
+  if (pps > kMaxPps) pps = kMaxPps;
   pps = (pps + 3) / 4 * 4;
   pl.pages_per_split = (int)pps;
   pl.max_splits = (int)((c.max_pages + pps - 1) / pps);
