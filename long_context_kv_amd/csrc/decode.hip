@@ -147,16 +147,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 // 32x32x16 bf16 MFMAs: over tiles of two pages (32 keys), S^T = K Q^T, an
 // online softmax per row (the forward's, lazily rescaled), then
 // O^T += V^T P^T with V^T taken by LDS transpose reads. One wave per
-// workgroup streams the split's tiles through a private LDS ring of NST
-// tiles filled by direct global->LDS loads (one 16-row tile per page), so no
-// barrier orders the page stream. The ring is the workgroup's only LDS: its
-// size (with the register count) sets how many workgroups a CU holds, and
-// HBM keeps streaming at full rate only while most of the step's workgroups
-// are resident at once.
-constexpr int kMmaWavesPerSimd = 2;   // register budget: waves per SIMD to fit
-
-template <int D, bool MASKED, int NST>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kMmaWavesPerSimd)))
+// workgroup streams the split's tiles through one LDS tile (19 KiB at
+// D = 128) filled by direct global->LDS loads, a 16-row tile per page, so no
+// barrier orders the page stream. With 188 registers or fewer (two waves
+// per SIMD) a CU holds eight of these workgroups, and the splits of a step
+// (kResidentWgs) stream at once: measured on the 64-sequence serving cache,
+// HBM streams at full rate only while most of the step's workgroups are
+// resident. A second tile in flight per wave, which needs twice the LDS and
+// so halves the resident workgroups, was 13% slower; one-page tiles with two
+// stages, or three waves per SIMD, were no faster.
+template <int D, bool MASKED>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mma_kernel(DecArgs a) {
   using M = Mfma<bf16>;
   using TL = Tile<D>;
@@ -166,10 +167,9 @@ void decode_mma_kernel(DecArgs a) {
   constexpr int CH = PT / 8;                    // its 16-byte chunk positions
   constexpr int NB = (CH + 63) / 64;            // 1 KiB copies per page tile
   constexpr int LASTL = CH - 64 * (NB - 1);     // lanes of the last, partial copy
-  constexpr int NDMA = 2 * 2 * NB;              // copies per tile (2 pages, K and V)
   static_assert(2 * PT == tile_elems<D, 2 * kPage>(), "two page tiles form one 32-row tile");
-  // [stage][K, V][two page tiles]
-  __shared__ __align__(16) bf16 ring[NST][2][2 * PT];
+  // [K, V][two page tiles]
+  __shared__ __align__(16) bf16 tile[2][2 * PT];
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31;
@@ -229,7 +229,7 @@ void decode_mma_kernel(DecArgs a) {
   // buffer range ends there), so no stale or non-finite bytes enter the
   // products. Returns the tile's page-validity bits.
   const int n_tiles = (n_pg + 1) / 2;
-  auto issue = [&](int t, int st) {
+  auto issue = [&](int t) {
     int okb = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -244,8 +244,8 @@ void decode_mma_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         if (k < NB - 1 || lane < LASTL) {
-          dma16_at(rk, src_off[k], ring[st][0], (uint32_t)(h * PT * 2 + k * 1024));
-          dma16_at(rv, src_off[k], ring[st][1], (uint32_t)(h * PT * 2 + k * 1024));
+          dma16_at(rk, src_off[k], tile[0], (uint32_t)(h * PT * 2 + k * 1024));
+          dma16_at(rv, src_off[k], tile[1], (uint32_t)(h * PT * 2 + k * 1024));
         }
       }
     }
@@ -261,24 +261,28 @@ void decode_mma_kernel(DecArgs a) {
   float l_run = 0.f;
   const float c = a.scale_log2;
 
-  auto compute = [&](int t, int st, int okb) {
-    const uint32_t kst = lds_addr(ring[st][0]);
-    const uint32_t vst = lds_addr(ring[st][1]);
+  auto compute = [&](int t, int okb) {
+    const uint32_t kst = lds_addr(tile[0]);
+    const uint32_t vst = lds_addr(tile[1]);
     // S^T = K Q^T: K row fragments (row l32, 8 elements at 16 ks + 8 hl)
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
     const uint32_t kb = kst + TL::off(l32, 8 * hl);
-    bf16x8 kf[NKS];
-    static_for<NKS>([&](auto KS) {
-      constexpr int ks = decltype(KS)::value;
-      kf[ks] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
+    // (in two halves of the k-steps, so that half the fragments are live)
+    static_for<2>([&](auto H) {
+      constexpr int h0 = decltype(H)::value * (NKS / 2);
+      bf16x8 kf[NKS / 2];
+      static_for<NKS / 2>([&](auto KS) {
+        constexpr int ks = decltype(KS)::value;
+        kf[ks] = __builtin_bit_cast(bf16x8, lds_read16<32 * (h0 + ks)>(kb));
+      });
+      lds_wait<0>();
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks) lds_tie(kf[ks]);
+#pragma unroll
+      for (int ks = 0; ks < NKS / 2; ++ks) sc = M::mma(kf[ks], qf[h0 + ks], sc);
     });
-    lds_wait<0>();
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) lds_tie(kf[ks]);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) sc = M::mma(kf[ks], qf[ks], sc);
     // V^T fragments of the two 16-key steps, by transpose reads
     const uint32_t vb =
         vst + TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
@@ -292,7 +296,7 @@ void decode_mma_kernel(DecArgs a) {
       });
     });
     // keys lo <= k < hi of the tile are visible to this lane's row
-    const int row0 = row_begin + 32 * t;
+    const int row0 = row_begin + 2 * kPage * t;
     const int lo = (okb & 1) ? 0 : kPage;
     const int hi = (okb & 2) ? min(32, hi_row - row0) : min(kPage, hi_row - row0);
     if (lo > 0 || hi < 32) {
@@ -337,34 +341,12 @@ void decode_mma_kernel(DecArgs a) {
     }
   };
 
-  if constexpr (NST == 1) {
-    for (int t = 0; t < n_tiles; ++t) {
-      const int okb = issue(t, 0);
-      CART_WAIT_VMCNT(0);
-      compute(t, 0, okb);
-    }
-  } else {
-    static_assert(NST == 2, "one or two stages");
-    // two stages with static addresses: the loop is unrolled by two
-    int ok0 = n_tiles > 0 ? issue(0, 0) : 0;
-    for (int t = 0; t < n_tiles; t += 2) {
-      int ok1 = 0;
-      if (t + 1 < n_tiles) {
-        ok1 = issue(t + 1, 1);
-        CART_WAIT_VMCNT(NDMA);
-      } else {
-        CART_WAIT_VMCNT(0);
-      }
-      compute(t, 0, ok0);
-      if (t + 1 >= n_tiles) break;
-      if (t + 2 < n_tiles) {
-        ok0 = issue(t + 2, 0);
-        CART_WAIT_VMCNT(NDMA);
-      } else {
-        CART_WAIT_VMCNT(0);
-      }
-      compute(t + 1, 1, ok1);
-    }
+  // one tile at a time: the other resident workgroups' copies keep HBM busy
+  // while this one computes
+  for (int t = 0; t < n_tiles; ++t) {
+    const int okb = issue(t);
+    CART_WAIT_VMCNT(0);
+    compute(t, okb);
   }
   CART_WAIT_VMCNT(0);
   l_run = wave_sum_halves(l_run);
@@ -385,19 +367,11 @@ void decode_mma_kernel(DecArgs a) {
           f32x4{acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2], acc[db][4 * cc + 3]};
 }
 
-// Ring stages of the MFMA decode kernel. One stage (19 KiB of LDS at
-// D = 128, 188 registers) lets a CU hold eight of these one-wave workgroups,
-// so nearly all of a step's splits stream at once; two stages (the next
-// tile's copies in flight during a tile's arithmetic) need twice the LDS and
-// more registers, and the four workgroups a CU then holds streamed 15% slower
-// (4.8 against 5.6 TB/s on the 64-sequence serving cache).
-constexpr int kMmaStages = 1;
-
 template <int D, bool MASKED>
 hipError_t launch_dec_mma(DecArgs a, hipStream_t st) {
   a.n_chunks = (a.g * a.kq + 31) / 32;
   const int grid = a.c.n_seqs * a.c.Hkv * a.n_chunks * a.max_splits;
-  CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED, kMmaStages>), grid, 64, 0, st, a);
+  CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED>), grid, 64, 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
