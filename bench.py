@@ -42,8 +42,8 @@ PEAK_HBM_GBPS = 8000.0
 
 # HBM bytes per launch of a kernel on a workload, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE; read counts x 2.0 from a 1 GiB copy calibration),
-# summarised in profiles/hbm_bytes_long-cartridge-28l_and_decode.md and
-# profiles/hbm_bytes_qwen3-layers.md. A figure holds only
+# summarised in profiles/hbm_bytes_long-cartridge-28l.md, hbm_bytes_qwen3-layers.md and
+# hbm_bytes_serving-decode.md. A figure holds only
 # for the kernel sources it was measured on: a mismatch of their hash reports
 # traffic as null.
 KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
     ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "6b317bbf5982d54e"),
     ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "6b317bbf5982d54e"),
     ("attn_fwd", "long-cartridge-28l"): (128.3e6, "4d0973d6ac4dfd42"),
-    ("decode", "serving-decode"): (1225.7e6, "546e6c7bb7a3fc0d"),
+    ("decode", "serving-decode"): (1225.6e6, "a61976bdbabaebcd"),
 }
 
 
