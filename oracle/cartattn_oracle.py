@@ -31,7 +31,7 @@ Sources (titles of the pages the method is described on):
   cartridge file layout and its RoPE warning): a shifted base position
   silently corrupts attention.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * scale defaults to 1/sqrt(d);
 * q-head h reads kv-head h // (Hq / Hkv) (contiguous GQA groups);

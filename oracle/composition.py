@@ -15,7 +15,7 @@ one concatenation per layer, so the attention backward routes gradients into
 every part's trainable rows while every part's sink stays frozen; serving
 writes the parts in order into an empty cache with the append primitive.
 
-Readings (listed in the design doc): each part freezes its own first
+Readings: each part freezes its own first
 ``frozen[i]`` rows (the base method's frozen_prefix, per part); the tokens'
 first position is the composed length P = sum of the parts' rows.
 """

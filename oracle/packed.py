@@ -16,7 +16,7 @@ training step is one forward/backward for the group; section "Deliberate
 divergences from the paper": the packed forward shares one prefix across
 its segments.
 
-Readings (listed in the design doc): segment s occupies packed rows
+Readings: segment s occupies packed rows
 cu[s] .. cu[s+1]-1 (cu = running sum of the lengths); its token t sits at
 RoPE position p + t; the cartridge gradient is the sum over segments.
 """

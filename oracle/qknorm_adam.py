@@ -17,7 +17,7 @@ Sources (titles of the pages the method is described on):
   (lr 2e-2). Section "Learning rate vs batch size (measured)": lr 2e-3 at
   small batches.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * the normalization is the Qwen3 q/k RMSNorm over one head row with a
   learned weight: y = x * w / sqrt(mean(x^2) + eps) (eps 1e-6 for Qwen3);

@@ -19,7 +19,7 @@ Sources (titles of the pages the method is described on):
   stream against its own cache, greedy acceptance per row with truncating
   rewinds of the rejected rows.
 
-Readings (listed in DESIGN.md):
+Readings:
 
 * window W >= 1: the query at position P sees the rows at positions
   P - W + 1 .. P (the W most recent positions, itself included); cartridge
