@@ -284,8 +284,8 @@ def steps_bench(C, W, shape, steps, warmup):
 def variants_bench(C, W, shape, steps, warmup):
     """One layer of `shape` (its first layer's inputs) in the variant modes:
     behind a sliding window of 4096 positions that cuts the cartridge, with
-    the tokens as four packed segments, and with the cartridge as four
-    composed parts. Each line is the mode's fwd+bwd step (RoPE included;
+    the tokens as four packed segments, with the cartridge as four composed
+    parts, and with the cartridge rows given in bf16. Each line is the mode's fwd+bwd step (RoPE included;
     algorithmic flop over the pairs the mode leaves visible)."""
     import torch
     dev = torch.device("cuda")
@@ -388,6 +388,27 @@ def variants_bench(C, W, shape, steps, warmup):
             C.cart_rope_tokens(b["dq"], b["dkt"], pos_base=p, theta=W.THETA, inverse=True)
         return step
     run("composed-4-parts", shape.visible_pairs, composed_step)
+
+    # bf16 cartridge rows (the copy cart_adam_rows writes beside the f32
+    # master rows): the attention reads them directly, with no cast
+    def bf16_rows_step():
+        b = buffers(g["q"], g["k_tok"])
+        kc = g["k_cart"].to(torch.bfloat16)
+        vc = g["v_cart"].to(torch.bfloat16)
+        shp = C.attn_shape(g["q"], g["k_tok"], p, 1, 0.0, torch.bfloat16)
+        lse = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
+        wsf = C.workspace(C.cart_attn_workspace_size(shp, False), dev)
+        wsb = C.workspace(C.cart_attn_workspace_size(shp, True), dev)
+
+        def step():
+            b["qw"].copy_(g["q"]); b["kw"].copy_(g["k_tok"])
+            C.cart_rope_tokens(b["qw"], b["kw"], pos_base=p, theta=W.THETA)
+            C.cart_attn_fwd(shp, b["qw"], b["kw"], g["v_tok"], kc, vc, b["o"], lse, wsf)
+            C.cart_attn_bwd(shp, b["qw"], b["kw"], g["v_tok"], kc, vc, b["o"], lse, g["dout"],
+                            b["dq"], b["dkt"], b["dvt"], b["dkc"], b["dvc"], False, wsb)
+            C.cart_rope_tokens(b["dq"], b["dkt"], pos_base=p, theta=W.THETA, inverse=True)
+        return step
+    run("bf16-rows", shape.visible_pairs, bf16_rows_step)
     del g
     torch.cuda.empty_cache()
     return out
