@@ -95,9 +95,79 @@ def _events_ms(fn, n):
     return e0.elapsed_time(e1)
 
 
+class ClockSampler:
+    """The GPU's current graphics clock, read through amdsmi every `period`
+    seconds by a background thread while a timed loop runs. The peaks the
+    roofline lines use are quoted at 2.4 GHz, and boxes of one model do not
+    all hold that clock under load, so the bench reports what it saw. Stays
+    off (summary None) if amdsmi or the device cannot be found."""
+
+    def __init__(self, period=0.002):
+        self.period = period
+        self.samples = []
+        self.handle = None
+
+    def _pick(self, amdsmi):
+        import torch
+        hs = amdsmi.amdsmi_get_processor_handles()
+        if len(hs) == 1:
+            return hs[0]
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        for h in hs:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)       # "dddd:bb:dd.f"
+            if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                return h
+        return None
+
+    def __enter__(self):
+        import threading
+        self.stop = threading.Event()
+        try:
+            import amdsmi
+            self.amdsmi = amdsmi
+            amdsmi.amdsmi_init()
+            self.handle = self._pick(amdsmi)
+        except Exception:
+            self.handle = None
+        if self.handle is not None:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+        return self
+
+    def _run(self):
+        import time
+        kind = self.amdsmi.AmdSmiClkType.GFX
+        while not self.stop.is_set():
+            try:
+                self.samples.append(float(self.amdsmi.amdsmi_get_clock_info(self.handle, kind)["clk"]))
+            except Exception:
+                return
+            time.sleep(self.period)
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        if self.handle is not None:
+            self.thread.join()
+            try:
+                self.amdsmi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return {"mean_mhz": round(sum(xs) / len(xs), 1), "min_mhz": xs[0], "max_mhz": xs[-1],
+                "samples": len(xs)}
+
+
 TRAIN_KERNELS = ("rope", "rows_to_bf16", "attn_fwd", "attn_fwd_combine", "bwd_preprocess",
                  "attn_bwd", "attn_bwd_dq", "bwd_dq_combine", "bwd_dq_finalize",
                  "bwd_cart_reduce")
+
+
+CLOCKS = {}   # graphics clock seen during each timed loop, by its tag
 
 
 def measure(C, step, steps, warmup, names, tag):
@@ -122,7 +192,9 @@ def measure(C, step, steps, warmup, names, tag):
     C.timing_enable(False)
     dom = max(kern, key=lambda k: kern[k]["total_ms"])
     _progress(f"{tag}: timing {steps} steps")
-    total_ms = _events_ms(step, steps)
+    with ClockSampler() as clk:
+        total_ms = _events_ms(step, steps)
+    CLOCKS[tag] = clk.summary()
     _progress(f"{tag}: {total_ms / steps:.3f} ms/step; kernel pass ({dom})")
     C.timing_only(dom)
     C.timing_enable(True)
@@ -655,6 +727,15 @@ def main():
                             "GB/s": round(dec["write_bytes"] / (dec["write_kernel_ms"] * 1e-3)
                                           / 1e9, 1) if dec["write_kernel_ms"] else None},
         }
+    clk = CLOCKS.get(shape.name)
+    result["clock"] = {
+        "note": "graphics clock read through amdsmi every 2 ms during the timed loops; the peaks "
+                "above assume 2400 MHz",
+        "headline": clk,
+        "decode": None if args.no_decode else CLOCKS.get(W.DECODE.name)}
+    if clk:
+        result["frac_of_peak_at_measured_clock"] = round(
+            value / (PEAK_BF16_TFLOPS * clk["mean_mhz"] / 2400.0), 4)
     if not args.no_cpu_baseline:
         _progress("cpu baseline (oracle sample)")
         result["cpu_baseline"] = cpu_baseline(W, shape)
