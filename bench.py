@@ -50,11 +50,11 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "long-cartridge-28l"): (405.9e6, "6b317bbf5982d54e"),
-    ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "6b317bbf5982d54e"),
-    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "6b317bbf5982d54e"),
-    ("attn_fwd", "long-cartridge-28l"): (128.3e6, "4d0973d6ac4dfd42"),
-    ("decode", "serving-decode"): (1225.6e6, "a61976bdbabaebcd"),
+    ("attn_bwd", "long-cartridge-28l"): (405.9e6, "ee5d48460afdb625"),
+    ("attn_bwd", "qwen3-8b-layer"): (1016.4e6, "ee5d48460afdb625"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "ee5d48460afdb625"),
+    ("attn_fwd", "long-cartridge-28l"): (128.3e6, "a2689f3fb7beeee7"),
+    ("decode", "serving-decode"): (1225.6e6, "dea4467aa5f33278"),
 }
 
 

@@ -295,10 +295,6 @@ __device__ __forceinline__ void dma16(buf_rsrc r, uint32_t voff, void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            (int)voff, 0, 0, 0);
 }
-__device__ __forceinline__ void dma4(buf_rsrc r, uint32_t voff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4,
-                                           (int)voff, 0, 0, 0);
-}
 // The same with the LDS destination `off` bytes past `lds` (an offset into
 // the object `lds` points to, so the compiler still knows what is written).
 __device__ __forceinline__ void dma16_at(buf_rsrc r, uint32_t voff, void* lds, uint32_t off) {
