@@ -135,3 +135,33 @@ def test_verify_serving_decode_workload(C):
     torch.cuda.synchronize()
     assert rel(f64(out), V.verify_step(oc, f64(q), f64(kn), f64(vn))) <= TOL
     cache.close()
+
+
+@pytest.mark.parametrize("g", [4, 8])
+def test_decode_skips_pages_outside_the_pool(C, g):
+    """Block-table entries outside [0, n_pages) are skipped: the decode
+    attends over the rows of the valid pages only (they read as zeros and
+    are masked, never dereferenced)."""
+    Hkv, d = 2, 128
+    Hq = g * Hkv
+    prefix, gen = [300, 129], [20, 0]
+    cache, _ = _filled(C, prefix, gen, Hq, Hkv, d, 40, 500 + g)
+    di = W.decode_inputs_ragged(prefix, gen, Hq, Hkv, d, 40, seed=500 + g)
+    # sequence 0 loses logical page 3 (an id past the pool) and page 7 (a
+    # negative id); its other 18 pages stay
+    cache.block_table[0, 3] = di.n_pages + 5
+    cache.block_table[0, 7] = -1
+    keep = np.ones(prefix[0] + gen[0], dtype=bool)
+    keep[48:64] = False
+    keep[112:128] = False
+    oc = O.DenseCache(2, Hkv, d)
+    k0 = np.concatenate([f64(di.k_cart[0]), f64(di.k_gen[0])])
+    v0 = np.concatenate([f64(di.v_cart[0]), f64(di.v_gen[0])])
+    oc.write(0, k0[keep], v0[keep])
+    oc.write(1, f64(di.k_cart[1]), f64(di.v_cart[1]))
+    out = torch.empty(2, Hq, d, dtype=torch.bfloat16, device="cuda")
+    say("decode with pages outside the pool", g)
+    cache.decode(di.q.cuda(), out, C.workspace(cache.decode_workspace_size(Hq), "cuda"))
+    torch.cuda.synchronize()
+    ref = O.decode_step(oc, f64(di.q))
+    assert rel(f64(out), ref) <= TOL
