@@ -539,3 +539,45 @@ def test_decode_variants_ragged(C, g, d):
     ref = O.decode_step(oc, f64(di.q), f64(di.k_new), f64(di.v_new))
     assert rel(f64(out), ref) <= TOL_BF16
     cache.close()
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16-f32rows"])
+def test_custom_softmax_scale(C, mode):
+    """A positive scale other than 1/sqrt(d) reaches every kernel: forward,
+    both backward kernels and the decode (compared with the oracle at the
+    same scale)."""
+    tok = torch.float32 if mode == "f32" else torch.bfloat16
+    name, B, n, p, Hq, Hkv, d = ("scale", 2, 90, 150, 8, 2, 128)
+    sc = 0.05
+    x = W.train_inputs(_shape(name, B, n, p, Hq, Hkv, d, tok, torch.float32, 78))
+    g = _dev(x)
+    say("custom scale", mode)
+    o, lse = C.attn_fwd(g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"], scale=sc)
+    grads = C.attn_bwd(g["q"], g["k_tok"], g["v_tok"], g["k_cart"], g["v_cart"], o, lse,
+                       g["dout"], scale=sc)
+    torch.cuda.synchronize()
+    args = [f64(x[k]) for k in ("q", "k_tok", "v_tok", "k_cart", "v_cart")]
+    o_ref, _ = O.attn_fwd(*args, scale=sc)
+    gr = O.attn_bwd(*args, f64(x["dout"]), scale=sc, frozen_rows=1)
+    got = dict(o=o, dq=grads[0], dk_tok=grads[1], dv_tok=grads[2], dk_cart=grads[3],
+               dv_cart=grads[4])
+    ref = dict(o=o_ref, dq=gr[0], dk_tok=gr[1], dv_tok=gr[2], dk_cart=gr[3], dv_cart=gr[4])
+    _compare(got, ref, TOL_F32 if mode == "f32" else TOL_BF16, 1, names=list(ref))
+
+
+def test_custom_scale_decode(C):
+    shape = W.DecodeShape("dec-scale", 3, 40, 30, 8, 2, 128, 16, 14)
+    di = W.decode_inputs(shape, n_seqs=3, p=40, max_generated=30)
+    cache, bt = _make_cache(C, di, 3, 2, 128)
+    oc = O.DenseCache(3, 2, 128)
+    for s in range(3):
+        cache.write(s, di.k_cart.cuda(), di.v_cart.cuda())
+        oc.write(s, f64(di.k_cart), f64(di.v_cart))
+        if di.generated[s]:
+            cache.append(s, di.k_gen[s].cuda(), di.v_gen[s].cuda())
+            oc.append(s, f64(di.k_gen[s]), f64(di.v_gen[s]))
+    out = torch.empty(3, 8, 128, dtype=torch.bfloat16, device="cuda")
+    say("custom scale decode")
+    cache.decode(di.q.cuda(), out, C.workspace(cache.decode_workspace_size(8), "cuda"), scale=0.3)
+    torch.cuda.synchronize()
+    assert rel(f64(out), O.decode_step(oc, f64(di.q), scale=0.3)) <= TOL_BF16
