@@ -461,10 +461,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   static_assert((2 * QBLK + 4) % 8 == 0, "copies per unit must split over 8 waves");
   // Ring of AHEAD + 2 unit stages: Q tile | dO tile | lse*log2(e) [32], -D [32].
   // Step j reads the stages of units j (row fragments, lse) and j-1
-  // (transpose fragments, -D) and issues the copy of unit j + AHEAD, spread
-  // over its MFMAs; stages are read while copies fill others, so every LDS
-  // access of the unit loop is issued by the inline-assembly helpers with
-  // explicit waits.
+  // (transpose fragments, -D) and issues the copy of unit j + AHEAD before
+  // its MFMAs (a copy issued between MFMAs holds the wave's next MFMAs up
+  // until the memory pipeline takes it); stages are read while copies fill
+  // others, so every LDS access of the unit loop is issued by the
+  // inline-assembly helpers with explicit waits.
   constexpr int AHEAD = 3;
   constexpr int NST = AHEAD + 2;
   constexpr int STAGE = 2 * QTILE + 2 * 2 * kBQ;   // bf16 elements per stage
@@ -770,8 +771,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   // (key + 32 hl), reg r <-> query d_row(r, hl)). Phase B (unit j-1): acc +=
   // Y^T T with Y the packed operand of unit j-1 (P or G) and T the transpose
   // fragments of its dO or Q tile. The two interleave per k-step, each
-  // k-step's LDS reads (and a copy of unit j + AHEAD, in phase A) issued one
-  // k-step ahead.
+  // k-step's LDS reads issued one k-step ahead; with phase A, the copies of
+  // unit j + AHEAD go out first.
   auto mfma_steps = [&](auto G, auto HA, auto HB, uint32_t stA, uint32_t stB, f32x16& xa,
                         const bf16x8 (&yb)[2], const Copy& cp) {
     constexpr bool A = decltype(HA)::value, B = decltype(HB)::value;
@@ -786,6 +787,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     if constexpr (A) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) xa[r] = 0.f;
+    }
+    if constexpr (A) {
+#pragma unroll
+      for (int i = 0; i < NOPS; ++i) copy_part(cp, i);
     }
     batch(std::integral_constant<int, 0>{}, 0);
     static_for<NKS>([&](auto KS) {
@@ -804,7 +809,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
         constexpr int m = ks / NDB, db = ks % NDB;
         acc[db] = M::mma(yb[m], tb[ks & 1], acc[db]);
       }
-      if constexpr (A && ks < NOPS) copy_part(cp, ks);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
@@ -952,7 +956,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     CART_WAIT_VMCNT(0);
   }
   static_assert(2 * NOPS < 64, "copies of two units must fit the wait count");
-  static_assert(NOPS <= NKS, "a unit's copies must fit the k-steps of a step");
 
   // ---- dV (P role) or dK times the softmax scale (G role). A tile cut into
   // pieces: every piece stores its f32 partial sums, and the piece that
@@ -1070,6 +1073,11 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   }
 }
 
+// Where a tile's compute in the dQ kernel issues the copy of the next tile
+// (all before the S, dP MFMAs measured fastest of the placements tried).
+template <int D> constexpr int kDqCopyA = KvCopy<D>::N;
+template <int D> constexpr int kDqCopyB = KvCopy<D>::N;
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
@@ -1114,7 +1122,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, base, nb, a.p, a.Hkv, kv);
-  const KvMap<D> kmap(wave, lane);
+  const KvMap<D> kmap = kv_map<D>(a.Hkv, wave, lane);
   if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
 
   // Q^T and dO^T as B operands: lane (q + 32 hl) holds row q, 8 columns per k-step.
@@ -1148,7 +1156,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   // MFMAs that use them.
   const uint32_t row_lane = TL::off(l32, 8 * hl);
   const uint32_t tr_lane = TL::off(4 * hl + ((lane & 15) >> 2), 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-  auto compute = [&](uint32_t kst, uint32_t vst, const KvTile& f) {
+  // The copy of the next tile (cp): copies [0, kDqCopyA) are issued before
+  // the S, dP MFMAs, [kDqCopyA, kDqCopyB) after them, the rest before the dQ
+  // MFMAs.
+  auto compute = [&](uint32_t kst, uint32_t vst, const KvTile& f, const KvCopy<D>& cp) {
     // S^T = K Q^T and dP^T = V dO^T for the two 32-key halves: K and V row
     // fragments (row 32 kh + l32, 8 elements at 16 ks + 8 hl), four reads
     // per k-step.
@@ -1162,6 +1173,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         vr[slot][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(vst + row_lane));
         vr[slot][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(vst + row_lane));
       };
+      cp.template range<0, kDqCopyA<D>>(kmap, wave, lane);
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; dp[0][r] = 0.f; dp[1][r] = 0.f; }
       rd(std::integral_constant<int, 0>{}, 0);
@@ -1189,6 +1201,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
       });
     }
     __builtin_amdgcn_s_setprio(0);
+    cp.template range<kDqCopyA<D>, kDqCopyB<D>>(kmap, wave, lane);
     // dS^T / scale = P (dP - D) (the scale is applied to dQ at the end);
     // key k = 32 kh + d_row(r, hl) is visible iff lo <= k < lim (its row
     // exists and, for a token tile, it is not after the query; with a
@@ -1213,6 +1226,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         const float p_ = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c, -lse2));
         dp[kh][r] = p_ * (dp[kh][r] + dl);
       }
+    cp.template range<kDqCopyB<D>, KvCopy<D>::N>(kmap, wave, lane);
     // dQ^T += K^T dS^T in four steps j = (kh, m): K^T fragments by transpose
     // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
     {
@@ -1249,25 +1263,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
+  // After each barrier no wave reads the other stage any more; the copy of
+  // the next tile into it is issued by this tile's compute (all at once by a
+  // wave that skips the tile).
   for (int t = t_begin; t < t_end; t += 2) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 1 < t_end) kv_issue<D>(kmap, K1, V1, t + 1, n_ct, src, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
     {
+      const KvCopy<D> cp = kv_copy<D>(src, K1, V1, t + 1, n_ct, t + 1 < t_end);
       const KvTile f = kv_tile(t, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
-        compute(lds_addr(K0), lds_addr(V0), f);
+        compute(lds_addr(K0), lds_addr(V0), f, cp);
+      else
+        cp.all(kmap, wave, lane);
     }
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 2 < t_end) kv_issue<D>(kmap, K0, V0, t + 2, n_ct, src, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
     {
+      const KvCopy<D> cp = kv_copy<D>(src, K0, V0, t + 2, n_ct, t + 2 < t_end);
       const KvTile f = kv_tile(t + 1, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
-        compute(lds_addr(K1), lds_addr(V1), f);
+        compute(lds_addr(K1), lds_addr(V1), f, cp);
+      else
+        cp.all(kmap, wave, lane);
     }
   }
 

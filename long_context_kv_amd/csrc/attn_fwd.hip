@@ -308,11 +308,20 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(FwdArgs a) {
 // issued by the inline-assembly helpers with explicit waits (the copy of the
 // next tile into the other stage is in flight meanwhile), one k-step ahead
 // of the MFMAs that use them.
+// Where a tile's compute issues the copy of the next tile: copies
+// [0, kFwdCopyA) before the S MFMAs, [kFwdCopyA, kFwdCopyB) after them,
+// the rest before the PV MFMAs. All before the S MFMAs measured fastest; a
+// copy issued between MFMAs stalls the MFMAs behind it until the memory
+// pipeline takes it.
+template <int D> constexpr int kFwdCopyA = KvCopy<D>::N;
+template <int D> constexpr int kFwdCopyB = KvCopy<D>::N;
+
 template <int D>
 __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const KvTile& f,
                                             const bf16x8 (&qf)[D / 16], f32x16 (&acc)[D / 32],
                                             float& m_ref, float& l_run, float c, int i0,
-                                            int my_i, int lane, int win_lo) {
+                                            int my_i, int lane, int win_lo, const KvCopy<D>& cp,
+                                            const KvMap<D>& kmap, int wave) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -330,6 +339,7 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
       kfr[ks % 3][0] = __builtin_bit_cast(bf16x8, lds_read16<32 * ks>(kb));
       kfr[ks % 3][1] = __builtin_bit_cast(bf16x8, lds_read16<TL::rows(32) + 32 * ks>(kb));
     };
+    cp.template range<0, kFwdCopyA<D>>(kmap, wave, lane);
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[0][r] = 0.f; s[1][r] = 0.f; }
     rd(std::integral_constant<int, 0>{});
@@ -356,6 +366,7 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
     });
   }
   __builtin_amdgcn_s_setprio(0);
+  cp.template range<kFwdCopyA<D>, kFwdCopyB<D>>(kmap, wave, lane);
   // V^T fragments for O^T += V^T P^T, by transpose reads of rows 32 kh + 16 m
   // .. for step j = (kh, m); the first step's reads are issued here, so that
   // they land while the softmax runs.
@@ -414,6 +425,7 @@ __device__ __forceinline__ void fwd_compute(uint32_t kst, uint32_t vst, const Kv
       ls += pv_;
     }
   l_run += ls;
+  cp.template range<kFwdCopyB<D>, KvCopy<D>::N>(kmap, wave, lane);
   // O^T += V^T P^T in four steps j = (kh, m), each step's V^T reads (8 per
   // step) issued one step ahead.
   {
@@ -483,7 +495,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, base, nb, a.p, a.Hkv, kv);
-  const KvMap<D> kmap(wave, lane);
+  const KvMap<D> kmap = kv_map<D>(a.Hkv, wave, lane);
   if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
 
   bf16x8 qf[NKS];
@@ -505,27 +517,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale_log2;
 
   // Two tiles per trip, stage 0 then stage 1, so every LDS address is static.
+  // After the barrier no wave reads the other stage any more; the copy of
+  // the next tile into it is issued by this tile's compute (all at once by a
+  // wave that skips the tile).
   for (int t = t_begin; t < t_end; t += 2) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 1 < t_end) kv_issue<D>(kmap, K1, V1, t + 1, n_ct, src, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the math
     {
+      const KvCopy<D> cp = kv_copy<D>(src, K1, V1, t + 1, n_ct, t + 1 < t_end);
       const KvTile f = kv_tile(t, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
         fwd_compute<D>(lds_addr(K0), lds_addr(V0), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
-                       win_lo);
+                       win_lo, cp, kmap, wave);
+      else
+        cp.all(kmap, wave, lane);
     }
     if (t + 1 >= t_end) break;
     CART_WAIT_VMCNT(0);
     lds_barrier();
-    if (t + 2 < t_end) kv_issue<D>(kmap, K0, V0, t + 2, n_ct, src, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
     {
+      const KvCopy<D> cp = kv_copy<D>(src, K0, V0, t + 2, n_ct, t + 2 < t_end);
       const KvTile f = kv_tile(t + 1, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
         fwd_compute<D>(lds_addr(K1), lds_addr(V1), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
-                       win_lo);
+                       win_lo, cp, kmap, wave);
+      else
+        cp.all(kmap, wave, lane);
     }
   }
 

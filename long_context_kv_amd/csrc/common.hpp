@@ -306,48 +306,50 @@ __device__ __forceinline__ void dma4_at(buf_rsrc r, uint32_t voff, void* lds, ui
       r, (__attribute__((address_space(3))) char*)lds + off, 4, (int)voff, 0, 0, 0);
 }
 
-// Per-lane source positions of this wave's share of the asynchronous copy of
-// a tile of NROWS rows x D bf16 into an LDS tile of tile_elems<D, NROWS>()
-// elements laid out as Tile<D> describes: 1 KiB loads spread over the 4
-// waves, lane l of block blk writing chunk position 64 blk + l (lanes past
-// the end of the tile in the last block are switched off). Computed once per
-// kernel: pk[k] = row << 16 | byte offset of the column chunk, for the
-// wave's k-th block. Lanes whose 16 bytes fall on padding re-read chunk 0 of
-// a row.
+// Per-lane source offsets of this wave's share of the asynchronous copy of
+// a tile of NROWS rows x D bf16 (global rows rs_bytes bytes apart) into an
+// LDS tile of tile_elems<D, NROWS>() elements laid out as Tile<D> describes:
+// 1 KiB loads spread over the 4 waves, lane l of block blk writing chunk
+// position 64 blk + l (lanes past the end of the tile in the last block are
+// switched off). Computed once per kernel: off[k] = byte offset of this
+// lane's chunk in the wave's k-th block, the same for every tile. Lanes
+// whose 16 bytes fall on padding re-read chunk 0 of their row.
 template <int D, int NROWS>
 struct TileMap {
   static constexpr int CHUNKS = tile_elems<D, NROWS>() / 8;
   static constexpr int NBLK = (CHUNKS + 63) / 64;
   static constexpr int LAST = CHUNKS - 64 * (NBLK - 1);   // lanes of the last block
   static constexpr int NK = (NBLK + 3) / 4;
-  uint32_t pk[NK];
-  __device__ TileMap(int wave, int lane) {
+  uint32_t off[NK];
+  __device__ TileMap(int wave, int lane, uint32_t rs_bytes) {
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       int rr, cc;
       Tile<D>::locate((4 * k + wave) * 64 + lane, rr, cc);
-      pk[k] = (uint32_t)rr << 16 | (uint32_t)(cc < D / 8 ? cc : 0) * 16;
+      off[k] = (uint32_t)rr * rs_bytes + (uint32_t)(cc < D / 8 ? cc : 0) * 16;
     }
   }
 };
 
-// Issue this wave's share of the copy of a tile of NROWS rows (global rows
-// `row_stride` elements apart) into `lds`. Rows at or past `rows`
-// (including the rounding past NROWS) re-read row rows-1 (finite data the
-// caller masks), so no offset leaves the source rows.
+// Block k (0 <= k < NK) of this wave's share of the copy of a tile into
+// `lds`, read through `r`, whose range ends with the tile's last row: chunks
+// of rows past it (a partial tile) read as zeros, finite data the caller
+// masks. Blocks that are whole for every wave are issued with all lanes on
+// and no branch; only the tile's last block switches lanes off (a single
+// condition mixing the wave-uniform block test with the lane test made the
+// compiler mask and branch around every copy). k must be a compile-time
+// constant after inlining.
 template <int D, int NROWS>
-__device__ __forceinline__ void dma_tile(const TileMap<D, NROWS>& m, bf16* lds, const bf16* src,
-                                         size_t row_stride, int rows, int wave, int lane) {
-  const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
-  const buf_rsrc r = make_rsrc(src, (uint32_t)(rows - 1) * rs_bytes + D * 2);
-#pragma unroll
-  for (int k = 0; k < TileMap<D, NROWS>::NK; ++k) {
-    const int blk = k * 4 + wave;
-    if (blk < TileMap<D, NROWS>::NBLK) {
-      const uint32_t rr = min(m.pk[k] >> 16, (uint32_t)(rows - 1));
-      if (blk < TileMap<D, NROWS>::NBLK - 1 || lane < TileMap<D, NROWS>::LAST)
-        dma16(r, rr * rs_bytes + (m.pk[k] & 0xffffu), lds + blk * 512);
-    }
+__device__ __forceinline__ void dma_block(const TileMap<D, NROWS>& m, int k, bf16* lds,
+                                          buf_rsrc r, int wave, int lane) {
+  using TM = TileMap<D, NROWS>;
+  const int blk = k * 4 + wave;   // wave-uniform
+  if (4 * k + 3 < TM::NBLK - 1) {
+    dma16(r, m.off[k], lds + blk * 512);
+  } else if (blk < TM::NBLK - 1) {
+    dma16(r, m.off[k], lds + blk * 512);
+  } else if (blk == TM::NBLK - 1) {
+    if (lane < TM::LAST) dma16(r, m.off[k], lds + blk * 512);
   }
 }
 

@@ -64,15 +64,78 @@ __device__ __forceinline__ KvSrc<D> kv_src(const void* k_cart, const void* v_car
 template <int D>
 using KvMap = TileMap<D, kKvTile>;
 
-// Issue this wave's share of the copy of tile t's K and V rows.
+// The copy map of one (batch, kv head)'s rows (Hkv*D elements apart).
+template <int D>
+__device__ __forceinline__ KvMap<D> kv_map(int Hkv, int wave, int lane) {
+  return KvMap<D>(wave, lane, (uint32_t)(Hkv * D * 2));
+}
+
+// The copy of one tile's K and V rows as this wave's single copy
+// instructions, so that a caller can place them inside its compute:
+// issue<J>() (J < N) issues copy J, the first NK of them K's blocks, the
+// rest V's.
+// With `on` false (no tile left to copy) every issue is a no-op.
+// The buffer descriptors are built at the copy from wave-uniform values read
+// from lane 0 (a descriptor carried across the branch around a tile's
+// compute was otherwise taken for divergent, and every copy became a loop
+// over distinct descriptors).
+template <int D>
+struct KvCopy {
+  static constexpr int NK = KvMap<D>::NK;
+  static constexpr int N = 2 * NK;
+  const bf16 *ks, *vs;   // the tile's first K and V rows
+  uint32_t bytes;        // buffer range: through the tile's last row
+  bf16 *kd, *vd;
+  bool on;
+
+  __device__ __forceinline__ static buf_rsrc rsrc(const bf16* p, uint32_t n) {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return make_rsrc((const void*)(uintptr_t)((uint64_t)hi << 32 | lo),
+                     __builtin_amdgcn_readfirstlane(n));
+  }
+  template <int J>
+  __device__ __forceinline__ void issue(const KvMap<D>& m, int wave, int lane) const {
+    static_assert(J >= 0 && J < N, "copy index");
+    if (!on) return;
+    if constexpr (J < NK)
+      dma_block<D, kKvTile>(m, J, kd, rsrc(ks, bytes), wave, lane);
+    else
+      dma_block<D, kKvTile>(m, J - NK, vd, rsrc(vs, bytes), wave, lane);
+  }
+  // Copies LO .. HI-1.
+  template <int LO, int HI>
+  __device__ __forceinline__ void range(const KvMap<D>& m, int wave, int lane) const {
+    static_assert(0 <= LO && LO <= HI && HI <= N, "copy range");
+    static_for<HI - LO>([&](auto I) { this->template issue<LO + decltype(I)::value>(m, wave, lane); });
+  }
+  __device__ __forceinline__ void all(const KvMap<D>& m, int wave, int lane) const {
+    static_for<N>([&](auto J) { this->template issue<decltype(J)::value>(m, wave, lane); });
+  }
+};
+
+// Prepare the copy of tile t into the stage (Kst, Vst); `on` false when
+// there is no tile t to copy (nothing is read then).
+template <int D>
+__device__ __forceinline__ KvCopy<D> kv_copy(const KvSrc<D>& s, bf16* Kst, bf16* Vst, int t,
+                                             int n_ct, bool on) {
+  KvCopy<D> c;
+  const KvTile f = kv_tile(t, n_ct, s.p, s.n);
+  c.bytes = (uint32_t)(max(f.rows, 1) - 1) * (uint32_t)(s.row_stride * 2) + D * 2;
+  c.ks = (f.cart ? s.kc : s.kt) + (size_t)f.j0 * s.row_stride;
+  c.vs = (f.cart ? s.vc : s.vt) + (size_t)f.j0 * s.row_stride;
+  c.kd = Kst;
+  c.vd = Vst;
+  c.on = on;
+  return c;
+}
+
+// Issue this wave's share of the copy of tile t's K and V rows at once.
 template <int D>
 __device__ __forceinline__ void kv_issue(const KvMap<D>& m, bf16* Kst, bf16* Vst, int t,
                                          int n_ct, const KvSrc<D>& s, int wave, int lane) {
-  const KvTile f = kv_tile(t, n_ct, s.p, s.n);
-  const bf16* kb = (f.cart ? s.kc : s.kt) + (size_t)f.j0 * s.row_stride;
-  const bf16* vb = (f.cart ? s.vc : s.vt) + (size_t)f.j0 * s.row_stride;
-  dma_tile<D, kKvTile>(m, Kst, kb, s.row_stride, f.rows, wave, lane);
-  dma_tile<D, kKvTile>(m, Vst, vb, s.row_stride, f.rows, wave, lane);
+  kv_copy<D>(s, Kst, Vst, t, n_ct, true).all(m, wave, lane);
 }
 
 }  // namespace cartattn
