@@ -1073,13 +1073,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
   }
 }
 
+// Waves of a dQ workgroup; they share each K/V tile they copy.
+constexpr int kDqWaves = 4;
+
 // Where a tile's compute in the dQ kernel issues the copy of the next tile
 // (all before the S, dP MFMAs measured fastest of the placements tried).
-template <int D> constexpr int kDqCopyA = KvCopy<D>::N;
-template <int D> constexpr int kDqCopyB = KvCopy<D>::N;
+template <int D> constexpr int kDqCopyA = KvCopy<D, kDqWaves>::N;
+template <int D> constexpr int kDqCopyB = KvCopy<D, kDqWaves>::N;
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void attn_bwd_dq_kernel(BwdArgs a) {
   using M = Mfma<bf16>;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -1122,8 +1125,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int win_lo = a.window > 0 ? a.p + i0 - a.window + 1 : -(1 << 30);
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, base, nb, a.p, a.Hkv, kv);
-  const KvMap<D> kmap = kv_map<D>(a.Hkv, wave, lane);
-  if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
+  const KvMap<D, kDqWaves> kmap = kv_map<D, kDqWaves>(a.Hkv, wave, lane);
+  KvWalk<D> walk(src, n_ct, t_begin);
+  if (t_begin < t_end) kv_copy<D, kDqWaves>(walk, K0, V0, true).all(kmap, wave, lane);
 
   // Q^T and dO^T as B operands: lane (q + 32 hl) holds row q, 8 columns per k-step.
   bf16x8 qf[NKS], of[NKS];
@@ -1159,7 +1163,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   // The copy of the next tile (cp): copies [0, kDqCopyA) are issued before
   // the S, dP MFMAs, [kDqCopyA, kDqCopyB) after them, the rest before the dQ
   // MFMAs.
-  auto compute = [&](uint32_t kst, uint32_t vst, const KvTile& f, const KvCopy<D>& cp) {
+  auto compute = [&](uint32_t kst, uint32_t vst, const KvTile& f, const KvCopy<D, kDqWaves>& cp) {
     // S^T = K Q^T and dP^T = V dO^T for the two 32-key halves: K and V row
     // fragments (row 32 kh + l32, 8 elements at 16 ks + 8 hl), four reads
     // per k-step.
@@ -1226,7 +1230,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
         const float p_ = __builtin_amdgcn_exp2f(fmaf(s[kh][r], c, -lse2));
         dp[kh][r] = p_ * (dp[kh][r] + dl);
       }
-    cp.template range<kDqCopyB<D>, KvCopy<D>::N>(kmap, wave, lane);
+    cp.template range<kDqCopyB<D>, KvCopy<D, kDqWaves>::N>(kmap, wave, lane);
     // dQ^T += K^T dS^T in four steps j = (kh, m): K^T fragments by transpose
     // reads of rows 32 kh + 16 m .. (8 reads per step, one step ahead).
     {
@@ -1270,7 +1274,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     {
-      const KvCopy<D> cp = kv_copy<D>(src, K1, V1, t + 1, n_ct, t + 1 < t_end);
+      if (t + 1 < t_end) walk.next();
+      const KvCopy<D, kDqWaves> cp = kv_copy<D, kDqWaves>(walk, K1, V1, t + 1 < t_end);
       const KvTile f = kv_tile(t, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
         compute(lds_addr(K0), lds_addr(V0), f, cp);
@@ -1281,7 +1286,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     {
-      const KvCopy<D> cp = kv_copy<D>(src, K0, V0, t + 2, n_ct, t + 2 < t_end);
+      if (t + 2 < t_end) walk.next();
+      const KvCopy<D, kDqWaves> cp = kv_copy<D, kDqWaves>(walk, K0, V0, t + 2 < t_end);
       const KvTile f = kv_tile(t + 1, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kKvTile > win_lo)
         compute(lds_addr(K1), lds_addr(V1), f, cp);
@@ -1602,19 +1608,19 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
   }
   pl.dq_bytes = d.tok_bf16 ? 0 : (size_t)d.B * d.n * d.Hq * d.D * sizeof(float);
   {
-    // dQ workgroups of 4 waves x 32 query rows, the q-heads of a GQA group
-    // packed as extra rows (up to 4 per workgroup); key tiles split while
-    // the grid is small
+    // dQ workgroups of kDqWaves waves x 32 query rows, the q-heads of a GQA
+    // group packed as extra rows (up to 4 per workgroup); key tiles split
+    // while the grid is small (under two rounds of 4-wave workgroups)
     const int g = d.Hq / d.Hkv;
     pl.hpw = (g % 4 == 0) ? 4 : ((g % 2 == 0) ? 2 : 1);
-    pl.wph = 4 / pl.hpw;
+    pl.wph = kDqWaves / pl.hpw;
     pl.n_hg = g / pl.hpw;
     pl.n_qb = (d.n + 32 * pl.wph - 1) / (32 * pl.wph);
     const long long base = (long long)d.Hkv * d.B * pl.n_hg * pl.n_qb;
     const int min_tiles = (d.p + kKvTile - 1) / kKvTile + 1;
     int qs = 1;
     if (d.tok_bf16)
-      while (base * qs < 512 && (qs * 2) * 4 <= min_tiles) qs *= 2;
+      while (base * qs < 512 * 4 / kDqWaves && (qs * 2) * 4 <= min_tiles) qs *= 2;
     pl.q_splits = qs;
     pl.grid_q = (int)(base * qs);
     if (qs > 1) pl.dq_part_bytes = (size_t)qs * d.B * d.n * d.Hq * d.D * sizeof(float);
@@ -1671,7 +1677,7 @@ static hipError_t launch_bwd_bf16(const BwdArgs& a, const BwdPlan& pl, hipStream
   if (e != hipSuccess) return e;
   CART_LAUNCH("attn_bwd", (attn_bwd_kv_kernel<D>), pl.grid_kv, kKvThreads, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  CART_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<D>), pl.grid_q, kThreads, 0, st, a);
+  CART_LAUNCH("attn_bwd_dq", (attn_bwd_dq_kernel<D>), pl.grid_q, 64 * kDqWaves, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (pl.q_splits > 1) {
     const size_t n4 = (size_t)a.B * a.n * a.Hq * (D / 4);

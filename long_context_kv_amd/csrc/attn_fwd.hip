@@ -496,7 +496,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   const KvSrc<D> src = kv_src<D>(a.k_cart, a.v_cart, a.k_tok, a.v_tok, base, nb, a.p, a.Hkv, kv);
   const KvMap<D> kmap = kv_map<D>(a.Hkv, wave, lane);
-  if (t_begin < t_end) kv_issue<D>(kmap, K0, V0, t_begin, n_ct, src, wave, lane);
+  KvWalk<D> walk(src, n_ct, t_begin);
+  if (t_begin < t_end) kv_copy<D>(walk, K0, V0, true).all(kmap, wave, lane);
 
   bf16x8 qf[NKS];
   {
@@ -524,7 +525,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     {
-      const KvCopy<D> cp = kv_copy<D>(src, K1, V1, t + 1, n_ct, t + 1 < t_end);
+      if (t + 1 < t_end) walk.next();
+      const KvCopy<D> cp = kv_copy<D>(walk, K1, V1, t + 1 < t_end);
       const KvTile f = kv_tile(t, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
         fwd_compute<D>(lds_addr(K0), lds_addr(V0), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,
@@ -536,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     CART_WAIT_VMCNT(0);
     lds_barrier();
     {
-      const KvCopy<D> cp = kv_copy<D>(src, K0, V0, t + 2, n_ct, t + 2 < t_end);
+      if (t + 2 < t_end) walk.next();
+      const KvCopy<D> cp = kv_copy<D>(walk, K0, V0, t + 2 < t_end);
       const KvTile f = kv_tile(t + 1, n_ct, a.p, nb);
       if (wave_active && (f.cart || f.j0 <= i0 + 31) && f.abs0 + kBN > win_lo)
         fwd_compute<D>(lds_addr(K1), lds_addr(V1), f, qf, acc, m_ref, l_run, c, i0, my_i, lane,

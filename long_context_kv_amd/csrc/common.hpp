@@ -309,23 +309,24 @@ __device__ __forceinline__ void dma4_at(buf_rsrc r, uint32_t voff, void* lds, ui
 // Per-lane source offsets of this wave's share of the asynchronous copy of
 // a tile of NROWS rows x D bf16 (global rows rs_bytes bytes apart) into an
 // LDS tile of tile_elems<D, NROWS>() elements laid out as Tile<D> describes:
-// 1 KiB loads spread over the 4 waves, lane l of block blk writing chunk
-// position 64 blk + l (lanes past the end of the tile in the last block are
-// switched off). Computed once per kernel: off[k] = byte offset of this
-// lane's chunk in the wave's k-th block, the same for every tile. Lanes
-// whose 16 bytes fall on padding re-read chunk 0 of their row.
-template <int D, int NROWS>
+// 1 KiB loads spread over the NWAVE waves of the workgroup, lane l of block
+// blk = NWAVE k + wave writing chunk position 64 blk + l (lanes past the end
+// of the tile in the last block are switched off). Computed once per
+// kernel: off[k] = byte offset of this lane's chunk in the wave's k-th
+// block, the same for every tile. Lanes whose 16 bytes fall on padding
+// re-read chunk 0 of their row.
+template <int D, int NROWS, int NWAVE = 4>
 struct TileMap {
   static constexpr int CHUNKS = tile_elems<D, NROWS>() / 8;
   static constexpr int NBLK = (CHUNKS + 63) / 64;
   static constexpr int LAST = CHUNKS - 64 * (NBLK - 1);   // lanes of the last block
-  static constexpr int NK = (NBLK + 3) / 4;
+  static constexpr int NK = (NBLK + NWAVE - 1) / NWAVE;
   uint32_t off[NK];
   __device__ TileMap(int wave, int lane, uint32_t rs_bytes) {
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
       int rr, cc;
-      Tile<D>::locate((4 * k + wave) * 64 + lane, rr, cc);
+      Tile<D>::locate((NWAVE * k + wave) * 64 + lane, rr, cc);
       off[k] = (uint32_t)rr * rs_bytes + (uint32_t)(cc < D / 8 ? cc : 0) * 16;
     }
   }
@@ -339,12 +340,12 @@ struct TileMap {
 // condition mixing the wave-uniform block test with the lane test made the
 // compiler mask and branch around every copy). k must be a compile-time
 // constant after inlining.
-template <int D, int NROWS>
-__device__ __forceinline__ void dma_block(const TileMap<D, NROWS>& m, int k, bf16* lds,
+template <int D, int NROWS, int NWAVE>
+__device__ __forceinline__ void dma_block(const TileMap<D, NROWS, NWAVE>& m, int k, bf16* lds,
                                           buf_rsrc r, int wave, int lane) {
-  using TM = TileMap<D, NROWS>;
-  const int blk = k * 4 + wave;   // wave-uniform
-  if (4 * k + 3 < TM::NBLK - 1) {
+  using TM = TileMap<D, NROWS, NWAVE>;
+  const int blk = k * NWAVE + wave;   // wave-uniform
+  if (NWAVE * k + NWAVE - 1 < TM::NBLK - 1) {
     dma16(r, m.off[k], lds + blk * 512);
   } else if (blk < TM::NBLK - 1) {
     dma16(r, m.off[k], lds + blk * 512);

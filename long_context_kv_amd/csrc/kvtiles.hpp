@@ -61,13 +61,14 @@ __device__ __forceinline__ KvSrc<D> kv_src(const void* k_cart, const void* v_car
   return s;
 }
 
-template <int D>
-using KvMap = TileMap<D, kKvTile>;
+// The copy map of a workgroup of NWAVE waves.
+template <int D, int NWAVE = 4>
+using KvMap = TileMap<D, kKvTile, NWAVE>;
 
 // The copy map of one (batch, kv head)'s rows (Hkv*D elements apart).
-template <int D>
-__device__ __forceinline__ KvMap<D> kv_map(int Hkv, int wave, int lane) {
-  return KvMap<D>(wave, lane, (uint32_t)(Hkv * D * 2));
+template <int D, int NWAVE = 4>
+__device__ __forceinline__ KvMap<D, NWAVE> kv_map(int Hkv, int wave, int lane) {
+  return KvMap<D, NWAVE>(wave, lane, (uint32_t)(Hkv * D * 2));
 }
 
 // The copy of one tile's K and V rows as this wave's single copy
@@ -79,9 +80,10 @@ __device__ __forceinline__ KvMap<D> kv_map(int Hkv, int wave, int lane) {
 // from lane 0 (a descriptor carried across the branch around a tile's
 // compute was otherwise taken for divergent, and every copy became a loop
 // over distinct descriptors).
-template <int D>
+template <int D, int NWAVE = 4>
 struct KvCopy {
-  static constexpr int NK = KvMap<D>::NK;
+  using Map = KvMap<D, NWAVE>;
+  static constexpr int NK = Map::NK;
   static constexpr int N = 2 * NK;
   const bf16 *ks, *vs;   // the tile's first K and V rows
   uint32_t bytes;        // buffer range: through the tile's last row
@@ -96,46 +98,71 @@ struct KvCopy {
                      __builtin_amdgcn_readfirstlane(n));
   }
   template <int J>
-  __device__ __forceinline__ void issue(const KvMap<D>& m, int wave, int lane) const {
+  __device__ __forceinline__ void issue(const Map& m, int wave, int lane) const {
     static_assert(J >= 0 && J < N, "copy index");
     if (!on) return;
     if constexpr (J < NK)
-      dma_block<D, kKvTile>(m, J, kd, rsrc(ks, bytes), wave, lane);
+      dma_block<D, kKvTile, NWAVE>(m, J, kd, rsrc(ks, bytes), wave, lane);
     else
-      dma_block<D, kKvTile>(m, J - NK, vd, rsrc(vs, bytes), wave, lane);
+      dma_block<D, kKvTile, NWAVE>(m, J - NK, vd, rsrc(vs, bytes), wave, lane);
   }
   // Copies LO .. HI-1.
   template <int LO, int HI>
-  __device__ __forceinline__ void range(const KvMap<D>& m, int wave, int lane) const {
+  __device__ __forceinline__ void range(const Map& m, int wave, int lane) const {
     static_assert(0 <= LO && LO <= HI && HI <= N, "copy range");
     static_for<HI - LO>([&](auto I) { this->template issue<LO + decltype(I)::value>(m, wave, lane); });
   }
-  __device__ __forceinline__ void all(const KvMap<D>& m, int wave, int lane) const {
+  __device__ __forceinline__ void all(const Map& m, int wave, int lane) const {
     static_for<N>([&](auto J) { this->template issue<decltype(J)::value>(m, wave, lane); });
   }
 };
 
-// Prepare the copy of tile t into the stage (Kst, Vst); `on` false when
-// there is no tile t to copy (nothing is read then).
+// Consecutive key tiles of one (batch, kv head), walked one at a time: the
+// current tile's first K and V rows move by one tile per step (and to the
+// first token row when the walk leaves the cartridge), so a step costs a
+// few scalar adds instead of a 64-bit product per tile.
 template <int D>
-__device__ __forceinline__ KvCopy<D> kv_copy(const KvSrc<D>& s, bf16* Kst, bf16* Vst, int t,
-                                             int n_ct, bool on) {
-  KvCopy<D> c;
-  const KvTile f = kv_tile(t, n_ct, s.p, s.n);
-  c.bytes = (uint32_t)(max(f.rows, 1) - 1) * (uint32_t)(s.row_stride * 2) + D * 2;
-  c.ks = (f.cart ? s.kc : s.kt) + (size_t)f.j0 * s.row_stride;
-  c.vs = (f.cart ? s.vc : s.vt) + (size_t)f.j0 * s.row_stride;
+struct KvWalk {
+  KvSrc<D> s;
+  int n_ct;
+  int t;               // the current tile
+  const bf16 *k, *v;   // its first K and V rows
+
+  __device__ __forceinline__ KvWalk(const KvSrc<D>& src, int n_ct_, int t0)
+      : s(src), n_ct(n_ct_), t(t0) {
+    const KvTile f = kv_tile(t0, n_ct, s.p, s.n);
+    k = (f.cart ? s.kc : s.kt) + (size_t)f.j0 * s.row_stride;
+    v = (f.cart ? s.vc : s.vt) + (size_t)f.j0 * s.row_stride;
+  }
+  __device__ __forceinline__ void next() {
+    ++t;
+    if (t == n_ct) {
+      k = s.kt;
+      v = s.vt;
+    } else {
+      k += (size_t)kKvTile * s.row_stride;
+      v += (size_t)kKvTile * s.row_stride;
+    }
+  }
+  // rows of the current tile (1 .. kKvTile)
+  __device__ __forceinline__ int rows() const {
+    return t < n_ct ? min(kKvTile, s.p - t * kKvTile) : min(kKvTile, s.n - (t - n_ct) * kKvTile);
+  }
+};
+
+// Prepare the copy of the walk's current tile into the stage (Kst, Vst);
+// `on` false when there is no tile to copy (nothing is read then).
+template <int D, int NWAVE = 4>
+__device__ __forceinline__ KvCopy<D, NWAVE> kv_copy(const KvWalk<D>& w, bf16* Kst, bf16* Vst,
+                                                    bool on) {
+  KvCopy<D, NWAVE> c;
+  c.bytes = (uint32_t)(w.rows() - 1) * (uint32_t)(w.s.row_stride * 2) + D * 2;
+  c.ks = w.k;
+  c.vs = w.v;
   c.kd = Kst;
   c.vd = Vst;
   c.on = on;
   return c;
-}
-
-// Issue this wave's share of the copy of tile t's K and V rows at once.
-template <int D>
-__device__ __forceinline__ void kv_issue(const KvMap<D>& m, bf16* Kst, bf16* Vst, int t,
-                                         int n_ct, const KvSrc<D>& s, int wave, int lane) {
-  kv_copy<D>(s, Kst, Vst, t, n_ct, true).all(m, wave, lane);
 }
 
 }  // namespace cartattn
