@@ -218,8 +218,17 @@ def train_bench(C, W, shape, steps, warmup):
         g = {k: v.to(dev) for k, v in x.items()}
         q0, k0 = g["q"], g["k_tok"]
         B, n, Hq, d = q0.shape
-        shp = C.attn_shape(q0, k0, shape.p, shape.frozen_rows, 0.0, g["k_cart"].dtype)
+        # f32 master rows with bf16 tokens: the step rounds them to bf16 once
+        # per layer (cart_rows_to_bf16) and gives the copy to the forward and
+        # the backward, which would otherwise each round them as they load
+        # them (the same values, so the same results)
+        cast = g["k_cart"].dtype == torch.float32 and q0.dtype == torch.bfloat16
+        rows_dt = torch.bfloat16 if cast else g["k_cart"].dtype
+        shp = C.attn_shape(q0, k0, shape.p, shape.frozen_rows, 0.0, rows_dt)
+        kcb = torch.empty(g["k_cart"].shape, dtype=torch.bfloat16, device=dev) if cast else None
+        vcb = torch.empty(g["v_cart"].shape, dtype=torch.bfloat16, device=dev) if cast else None
         st = dict(g=g, q0=q0, k0=k0, q=torch.empty_like(q0), k=torch.empty_like(k0), shp=shp,
+                  cast=cast, kc=kcb if cast else g["k_cart"], vc=vcb if cast else g["v_cart"],
                   o=torch.empty_like(q0),
                   lse=torch.empty(B, Hq, n, dtype=torch.float32, device=dev),
                   dq=torch.empty_like(q0), dkt=torch.empty_like(k0),
@@ -240,12 +249,14 @@ def train_bench(C, W, shape, steps, warmup):
             s["q"].copy_(s["q0"])
             s["k"].copy_(s["k0"])
             C.cart_rope_tokens(s["q"], s["k"], pos_base=p, theta=W.THETA)
-            C.cart_attn_fwd(s["shp"], s["q"], s["k"], g["v_tok"], g["k_cart"], g["v_cart"],
+            if s["cast"]:
+                C.cart_rows_to_bf16(g["k_cart"], g["v_cart"], s["kc"], s["vc"])
+            C.cart_attn_fwd(s["shp"], s["q"], s["k"], g["v_tok"], s["kc"], s["vc"],
                             s["o"], s["lse"], s["wsf"])
         for s in reversed(L):
             g = s["g"]
-            C.cart_attn_bwd(s["shp"], s["q"], s["k"], g["v_tok"], g["k_cart"],
-                            g["v_cart"], s["o"], s["lse"], g["dout"], s["dq"], s["dkt"],
+            C.cart_attn_bwd(s["shp"], s["q"], s["k"], g["v_tok"], s["kc"], s["vc"],
+                            s["o"], s["lse"], g["dout"], s["dq"], s["dkt"],
                             s["dvt"], s["dkc"], s["dvc"], False, s["wsb"])
             C.cart_rope_tokens(s["dq"], s["dkt"], pos_base=p, theta=W.THETA, inverse=True)
 
@@ -402,13 +413,15 @@ def variants_bench(C, W, shape, steps, warmup):
         return dict(qw=torch.empty_like(q), kw=torch.empty_like(k), o=torch.empty_like(q),
                     dq=torch.empty_like(q), dkt=torch.empty_like(k), dvt=torch.empty_like(k),
                     dkc=torch.empty(g["k_cart"].shape, dtype=torch.float32, device=dev),
-                    dvc=torch.empty(g["v_cart"].shape, dtype=torch.float32, device=dev))
+                    dvc=torch.empty(g["v_cart"].shape, dtype=torch.float32, device=dev),
+                    kcb=torch.empty(g["k_cart"].shape, dtype=torch.bfloat16, device=dev),
+                    vcb=torch.empty(g["v_cart"].shape, dtype=torch.bfloat16, device=dev))
 
     # sliding window of 4096 positions: every query sees exactly 4096 rows
     W_ = 4096
     def window_step():
         b = buffers(g["q"], g["k_tok"])
-        shp = C.attn_shape(g["q"], g["k_tok"], p, 1, 0.0, torch.float32, window=W_)
+        shp = C.attn_shape(g["q"], g["k_tok"], p, 1, 0.0, torch.bfloat16, window=W_)
         lse = torch.empty(1, Hq, n, dtype=torch.float32, device=dev)
         wsf = C.workspace(C.cart_attn_workspace_size(shp, False), dev)
         wsb = C.workspace(C.cart_attn_workspace_size(shp, True), dev)
@@ -416,9 +429,10 @@ def variants_bench(C, W, shape, steps, warmup):
         def step():
             b["qw"].copy_(g["q"]); b["kw"].copy_(g["k_tok"])
             C.cart_rope_tokens(b["qw"], b["kw"], pos_base=p, theta=W.THETA)
-            C.cart_attn_fwd(shp, b["qw"], b["kw"], g["v_tok"], g["k_cart"], g["v_cart"], b["o"],
+            C.cart_rows_to_bf16(g["k_cart"], g["v_cart"], b["kcb"], b["vcb"])
+            C.cart_attn_fwd(shp, b["qw"], b["kw"], g["v_tok"], b["kcb"], b["vcb"], b["o"],
                             lse, wsf)
-            C.cart_attn_bwd(shp, b["qw"], b["kw"], g["v_tok"], g["k_cart"], g["v_cart"], b["o"],
+            C.cart_attn_bwd(shp, b["qw"], b["kw"], g["v_tok"], b["kcb"], b["vcb"], b["o"],
                             lse, g["dout"], b["dq"], b["dkt"], b["dvt"], b["dkc"], b["dvc"],
                             False, wsb)
             C.cart_rope_tokens(b["dq"], b["dkt"], pos_base=p, theta=W.THETA, inverse=True)
@@ -431,7 +445,7 @@ def variants_bench(C, W, shape, steps, warmup):
     def packed_step():
         q, k, v, do = (g[t][0] for t in ("q", "k_tok", "v_tok", "dout"))
         b = buffers(q, k)
-        shp = C.attn_shape(q, k, p, 1, 0.0, torch.float32, seg_lens=seg)
+        shp = C.attn_shape(q, k, p, 1, 0.0, torch.bfloat16, seg_lens=seg)
         lse = torch.empty(len(seg), Hq, max(seg), dtype=torch.float32, device=dev)
         wsf = C.workspace(C.cart_attn_workspace_size(shp, False), dev)
         wsb = C.workspace(C.cart_attn_workspace_size(shp, True), dev)
@@ -439,8 +453,9 @@ def variants_bench(C, W, shape, steps, warmup):
         def step():
             b["qw"].copy_(q); b["kw"].copy_(k)
             C.cart_rope_tokens_packed(b["qw"], b["kw"], seg, pos_base=p, theta=W.THETA)
-            C.cart_attn_fwd(shp, b["qw"], b["kw"], v, g["k_cart"], g["v_cart"], b["o"], lse, wsf)
-            C.cart_attn_bwd(shp, b["qw"], b["kw"], v, g["k_cart"], g["v_cart"], b["o"], lse, do,
+            C.cart_rows_to_bf16(g["k_cart"], g["v_cart"], b["kcb"], b["vcb"])
+            C.cart_attn_fwd(shp, b["qw"], b["kw"], v, b["kcb"], b["vcb"], b["o"], lse, wsf)
+            C.cart_attn_bwd(shp, b["qw"], b["kw"], v, b["kcb"], b["vcb"], b["o"], lse, do,
                             b["dq"], b["dkt"], b["dvt"], b["dkc"], b["dvc"], False, wsb)
             C.cart_rope_tokens_packed(b["dq"], b["dkt"], seg, pos_base=p, theta=W.THETA,
                                       inverse=True)

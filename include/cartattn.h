@@ -200,6 +200,24 @@ int cart_adam_rows(float* rows, const float* grad, float* m, float* v, void* row
                    double lr, double beta1, double beta2, double eps, void* stream);
 
 /*
+ * cart_rows_to_bf16 -- the bf16 operands of f32 cartridge rows, made once.
+ *   Source: Cartridges guide, "Semantics" (parameterization): the trainable
+ *   rows are float32; the attention's products read them as bf16 operands.
+ *
+ * k_bf16[i] = bf16(k[i]) and v_bf16[i] = bf16(v[i]) (nearest even) for the
+ * n_rows x row_elems elements of k and v (float32; for a cartridge tensor
+ * n_rows = p, row_elems = n_kv_heads * head_dim). This is the rounding that
+ * cart_attn_fwd and cart_attn_bwd apply to f32 rows as they load them, so
+ * passing the outputs as bf16 cartridge rows gives the same results as
+ * passing k and v; a step that runs the forward and the backward on the same
+ * rows converts them once instead of in each call. The outputs must not
+ * overlap the inputs. row_elems % 4 == 0; every pointer 16-byte aligned and
+ * non-NULL unless n_rows = 0.
+ */
+int cart_rows_to_bf16(const float* k, const float* v, void* k_bf16, void* v_bf16,
+                      int64_t n_rows, int32_t row_elems, void* stream);
+
+/*
  * Workspace bytes that cart_attn_fwd (for_backward = 0) or cart_attn_bwd
  * (for_backward = 1) needs for shape `s` (host pointer). Returns 0 for an
  * invalid shape. The workspace is caller-owned device memory, 256-byte

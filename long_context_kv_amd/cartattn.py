@@ -43,6 +43,7 @@ _DTYPES = {torch.float32: CART_F32, torch.bfloat16: CART_BF16}
 
 EXPORTS = [
     "cart_rope_tokens", "cart_rope_tokens_packed", "cart_qk_norm_rope", "cart_qk_norm_rope_bwd", "cart_adam_rows",
+    "cart_rows_to_bf16",
     "cart_attn_workspace_size", "cart_parts_rows", "cart_compose_rows",
     "cart_attn_bwd_composed", "cart_write_composed_cache", "cart_attn_fwd", "cart_attn_bwd",
     "cart_cache_create", "cart_cache_destroy", "cart_cache_reset", "cart_cache_seq_len",
@@ -103,6 +104,7 @@ _lib.cart_qk_norm_rope_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, c
 _lib.cart_adam_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _i32, _i32, _i32,
                                 ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                 ctypes.c_double, _vp]
+_lib.cart_rows_to_bf16.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int64, _i32, _vp]
 _lib.cart_attn_workspace_size.argtypes = [_P(AttnShape), _i32]
 _lib.cart_parts_rows.argtypes = [_P(Parts)]
 _lib.cart_parts_rows.restype = _i32
@@ -258,6 +260,23 @@ def cart_adam_rows(rows: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: t
     _check(_lib.cart_adam_rows(_ptr(rows), _ptr(grad), _ptr(m), _ptr(v), _ptr(rows_bf16),
                                n_rows, row_elems, frozen_rows, step, lr, beta1, beta2, eps,
                                _stream(stream)), "cart_adam_rows")
+
+
+def cart_rows_to_bf16(k: torch.Tensor, v: torch.Tensor, k_out: torch.Tensor, v_out: torch.Tensor,
+                      stream=None) -> None:
+    """bf16 copies (nearest even) of f32 cartridge rows k, v [p, ...] into k_out, v_out."""
+    n_rows = k.shape[0]
+    row_elems = k.numel() // max(n_rows, 1)
+    _check(_lib.cart_rows_to_bf16(_ptr(k), _ptr(v), _ptr(k_out), _ptr(v_out), n_rows, row_elems,
+                                  _stream(stream)), "cart_rows_to_bf16")
+
+
+def rows_to_bf16(k: torch.Tensor, v: torch.Tensor, stream=None):
+    """Allocate and return the bf16 copies of f32 cartridge rows k, v."""
+    k_out = torch.empty(k.shape, dtype=torch.bfloat16, device=k.device)
+    v_out = torch.empty(v.shape, dtype=torch.bfloat16, device=v.device)
+    cart_rows_to_bf16(k, v, k_out, v_out, stream)
+    return k_out, v_out
 
 
 def cart_attn_workspace_size(shape: AttnShape, for_backward: bool) -> int:

@@ -416,6 +416,33 @@ int cart_adam_rows(float* rows, const float* grad, float* m, float* v, void* row
                     st, "cart_adam_rows");
 }
 
+int cart_rows_to_bf16(const float* k, const float* v, void* k_bf16, void* v_bf16,
+                      int64_t n_rows, int32_t row_elems, void* stream) {
+  if (n_rows < 0 || row_elems < 1)
+    return fail(CART_ERR_INVALID_ARG, "n_rows must be >= 0 and row_elems >= 1");
+  if (row_elems % 4 != 0)
+    return fail(CART_ERR_UNSUPPORTED, "row_elems (%d) must be a multiple of 4", row_elems);
+  const long long n = (long long)n_rows * row_elems;
+  if (n > (1LL << 40)) return fail(CART_ERR_UNSUPPORTED, "tensor too large");
+  if (n == 0) { g_err[0] = '\0'; return CART_OK; }
+  CHECK(need_ptr(k, "k"));
+  CHECK(need_ptr(v, "v"));
+  CHECK(need_ptr(k_bf16, "k_bf16"));
+  CHECK(need_ptr(v_bf16, "v_bf16"));
+  const auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  const size_t fb = (size_t)n * 4, hb = (size_t)n * 2;
+  if (overlap(k_bf16, hb, k, fb) || overlap(k_bf16, hb, v, fb) || overlap(v_bf16, hb, k, fb) ||
+      overlap(v_bf16, hb, v, fb) || overlap(k_bf16, hb, v_bf16, hb))
+    return fail(CART_ERR_INVALID_ARG, "cart_rows_to_bf16: outputs overlap the inputs or each other");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  return hip_result(launch_rows_to_bf16(k, v, reinterpret_cast<__bf16*>(k_bf16),
+                                        reinterpret_cast<__bf16*>(v_bf16), (size_t)n, st),
+                    st, "cart_rows_to_bf16");
+}
+
 size_t cart_attn_workspace_size(const cart_attn_shape* s, int32_t for_backward) {
   if (check_shape(s) != CART_OK) return 0;
   const AttnDims d = dims_of(s);

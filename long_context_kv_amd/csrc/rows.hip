@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void rows_to_bf16_kernel(const float4* __restr
 
 hipError_t launch_rows_to_bf16(const float* k, const float* v, bf16* kb, bf16* vb, size_t n,
                                hipStream_t st) {
-  const size_t n4 = n / 4;   // n = p * Hkv * D, a multiple of 64
+  const size_t n4 = n / 4;   // n = rows x row elements, a multiple of 4
   if (n4 == 0) return hipSuccess;
   size_t blocks = (n4 + 255) / 256;
   if (blocks > 4096) blocks = 4096;

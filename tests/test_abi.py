@@ -322,6 +322,24 @@ def test_adam_rows_validation():
     assert call(rows=None, n=0, fr=0) == C.CART_OK         # empty: nothing launched
 
 
+def test_rows_to_bf16_validation():
+    f = L.cart_rows_to_bf16
+
+    def call(k=FAKE, v=FAKE + 4096, kb=FAKE + 8192, vb=FAKE + 12288, n=8, e=64):
+        return f(k, v, kb, vb, n, e, None)
+
+    assert call(e=6) == C.CART_ERR_UNSUPPORTED
+    assert call(n=-1) == C.CART_ERR_INVALID_ARG
+    assert call(e=0) == C.CART_ERR_INVALID_ARG
+    assert call(k=None) == C.CART_ERR_INVALID_ARG
+    assert call(vb=None) == C.CART_ERR_INVALID_ARG
+    assert call(kb=MIS) == C.CART_ERR_ALIGNMENT
+    assert call(kb=FAKE + 1024) == C.CART_ERR_INVALID_ARG      # k_bf16 inside k
+    assert call(vb=FAKE + 8192 + 512) == C.CART_ERR_INVALID_ARG  # outputs overlap
+    assert b"overlap" in L.cart_last_error()
+    assert call(k=None, v=None, kb=None, vb=None, n=0) == C.CART_OK   # empty: nothing launched
+
+
 def _parts(rows, frozen, ptr=FAKE):
     n = len(rows)
     kp = (ctypes.c_void_p * n)(*[ptr if r else None for r in rows])

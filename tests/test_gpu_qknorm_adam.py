@@ -3,8 +3,10 @@ RMSNorm + RoPE (forward and input gradient) and Adam on the cartridge rows --
 through the C ABI against the CPU float64 oracle on the same seeded inputs.
 
 Tolerances: 1e-5 (normwise) for float32 tensors, 2e-2 for bfloat16 ones;
-frozen rows bit for bit unchanged; the bf16 copy written by Adam equal bit
-for bit to the nearest-even rounding of the f32 rows it wrote.
+frozen rows bit for bit unchanged; the bf16 copy written by Adam, and the
+one made by cart_rows_to_bf16, equal bit for bit to the nearest-even
+rounding of the f32 rows; attention on that copy equal bit for bit to
+attention on the f32 rows.
 """
 
 import numpy as np
@@ -130,3 +132,36 @@ def test_adam_rows(C, rows, hkv, d, frozen, lr):
         assert not bool(m[:frozen].any()) and not bool(v[:frozen].any())
         assert np.array_equal(f64(xb), O.round_bf16(xd.cpu().numpy()))
         xr = f64(xd)            # follow the GPU's f32 rows from here on
+
+
+def test_rows_to_bf16(C):
+    g = torch.Generator().manual_seed(91)
+    k = torch.randn(37, 2, 64, generator=g) * 3
+    v = torch.randn(37, 2, 64, generator=g)
+    # ties (halfway between two bf16 values, both parities), subnormals,
+    # the largest finite values and signed zeros
+    special = torch.tensor([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8),
+                            2.0 ** -130, -(2.0 ** -133), 3.0e38, -3.3e38, 0.0, -0.0,
+                            65504.0, 1.0e-40, 7.0 + 2.0 ** -6], dtype=torch.float32)
+    k.view(-1)[: special.numel()] = special
+    kb, vb = C.rows_to_bf16(k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(kb), O.round_bf16(k.numpy()))
+    assert np.array_equal(f64(vb), O.round_bf16(v.numpy()))
+    # signs of zeros and every bit of the rest
+    assert torch.equal(kb.cpu().view(torch.int16), k.to(torch.bfloat16).view(torch.int16))
+
+
+def test_attention_on_cast_rows_equals_f32_rows(C):
+    x = W.train_inputs(W.TrainShape("cast", 2, 40, 70, 8, 2, 128, torch.bfloat16,
+                                    torch.float32, 92))
+    d = {k_: t.cuda() for k_, t in x.items()}
+    kb, vb = C.rows_to_bf16(d["k_cart"], d["v_cart"])
+    o32, l32 = C.attn_fwd(d["q"], d["k_tok"], d["v_tok"], d["k_cart"], d["v_cart"])
+    ob, lb = C.attn_fwd(d["q"], d["k_tok"], d["v_tok"], kb, vb)
+    g32 = C.attn_bwd(d["q"], d["k_tok"], d["v_tok"], d["k_cart"], d["v_cart"], o32, l32, d["dout"])
+    gb = C.attn_bwd(d["q"], d["k_tok"], d["v_tok"], kb, vb, ob, lb, d["dout"])
+    torch.cuda.synchronize()
+    assert torch.equal(o32, ob) and torch.equal(l32, lb)
+    for a, b in zip(g32, gb):
+        assert torch.equal(a, b)
