@@ -50,11 +50,11 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "long-cartridge-28l"): (405.9e6, "44d49fd6f15bd83d"),
-    ("attn_bwd", "qwen3-8b-layer"): (1022.1e6, "44d49fd6f15bd83d"),
-    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "44d49fd6f15bd83d"),
-    ("attn_fwd", "long-cartridge-28l"): (117.9e6, "e191b37929fb7589"),
-    ("decode", "serving-decode"): (1225.6e6, "a8c53139c4f98b52"),
+    ("attn_bwd", "long-cartridge-28l"): (405.9e6, "a8362bc7b4830d10"),
+    ("attn_bwd", "qwen3-8b-layer"): (1022.1e6, "a8362bc7b4830d10"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "a8362bc7b4830d10"),
+    ("attn_fwd", "long-cartridge-28l"): (117.9e6, "b205611fb2e52afe"),
+    ("decode", "serving-decode"): (1225.6e6, "305af045842f1e10"),
 }
 
 

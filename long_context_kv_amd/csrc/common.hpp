@@ -288,6 +288,17 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+// The same from values read from lane 0: where the compiler cannot see that
+// the base and size are wave-uniform (values carried across branches, or
+// formed by vector instructions), a descriptor left in vector registers
+// turns every load through it into a loop over distinct descriptors.
+__device__ __forceinline__ buf_rsrc uniform_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return make_rsrc((const void*)(uintptr_t)((uint64_t)hi << 32 | lo),
+                   __builtin_amdgcn_readfirstlane(bytes));
+}
 // Cache-policy operand of a buffer load coherent at device scope on gfx950
 // (the SC1 bit: the load is served from beyond the XCD's L2).
 constexpr int kCpolDevice = 16;

@@ -229,18 +229,25 @@ void decode_mma_kernel(DecArgs a) {
   // buffer range ends there), so no stale or non-finite bytes enter the
   // products. Returns the tile's page-validity bits.
   const int n_tiles = (n_pg + 1) / 2;
-  auto issue = [&](int t) {
+  // The page ids of tile t (its two table entries, -1 past the split), as
+  // loaded values: the ids of tile t + 1 are loaded while tile t's copies
+  // are in flight, so the table read adds no latency of its own.
+  auto ids_of = [&](int t, int (&ids)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) ids[h] = 2 * t + h < n_pg ? bt[2 * t + h] : -1;
+  };
+  auto issue = [&](int t, const int (&ids)[2]) {
     int okb = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * t + h;
-      int page = i < n_pg ? bt[i] : -1;
+      int page = __builtin_amdgcn_readfirstlane(ids[h]);
       if (page >= a.c.n_pages) page = -1;
       okb |= (page >= 0) << h;
       const int rows = page >= 0 ? min(kPage, max(0, row_end - (row_begin + i * kPage))) : 0;
       const size_t base = ((size_t)max(page, 0) * a.c.Hkv + kv) * kPage * D;
-      const buf_rsrc rk = make_rsrc(kpool + base, (uint32_t)(rows * D * 2));
-      const buf_rsrc rv = make_rsrc(vpool + base, (uint32_t)(rows * D * 2));
+      const buf_rsrc rk = uniform_rsrc(kpool + base, (uint32_t)(rows * D * 2));
+      const buf_rsrc rv = uniform_rsrc(vpool + base, (uint32_t)(rows * D * 2));
 #pragma unroll
       for (int k = 0; k < NB; ++k) {
         if (k < NB - 1 || lane < LASTL) {
@@ -343,10 +350,15 @@ void decode_mma_kernel(DecArgs a) {
 
   // one tile at a time: the other resident workgroups' copies keep HBM busy
   // while this one computes
+  int ids[2], nxt[2];
+  ids_of(0, ids);
   for (int t = 0; t < n_tiles; ++t) {
-    const int okb = issue(t);
+    const int okb = issue(t, ids);
+    ids_of(t + 1, nxt);
     CART_WAIT_VMCNT(0);
     compute(t, okb);
+    ids[0] = nxt[0];
+    ids[1] = nxt[1];
   }
   CART_WAIT_VMCNT(0);
   l_run = wave_sum_halves(l_run);

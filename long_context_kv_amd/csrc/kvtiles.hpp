@@ -78,8 +78,7 @@ __device__ __forceinline__ KvMap<D, NWAVE> kv_map(int Hkv, int wave, int lane) {
 // With `on` false (no tile left to copy) every issue is a no-op.
 // The buffer descriptors are built at the copy from wave-uniform values read
 // from lane 0 (a descriptor carried across the branch around a tile's
-// compute was otherwise taken for divergent, and every copy became a loop
-// over distinct descriptors).
+// compute was otherwise taken for divergent).
 template <int D, int NWAVE = 4>
 struct KvCopy {
   using Map = KvMap<D, NWAVE>;
@@ -90,21 +89,14 @@ struct KvCopy {
   bf16 *kd, *vd;
   bool on;
 
-  __device__ __forceinline__ static buf_rsrc rsrc(const bf16* p, uint32_t n) {
-    const uint64_t a = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    return make_rsrc((const void*)(uintptr_t)((uint64_t)hi << 32 | lo),
-                     __builtin_amdgcn_readfirstlane(n));
-  }
   template <int J>
   __device__ __forceinline__ void issue(const Map& m, int wave, int lane) const {
     static_assert(J >= 0 && J < N, "copy index");
     if (!on) return;
     if constexpr (J < NK)
-      dma_block<D, kKvTile, NWAVE>(m, J, kd, rsrc(ks, bytes), wave, lane);
+      dma_block<D, kKvTile, NWAVE>(m, J, kd, uniform_rsrc(ks, bytes), wave, lane);
     else
-      dma_block<D, kKvTile, NWAVE>(m, J - NK, vd, rsrc(vs, bytes), wave, lane);
+      dma_block<D, kKvTile, NWAVE>(m, J - NK, vd, uniform_rsrc(vs, bytes), wave, lane);
   }
   // Copies LO .. HI-1.
   template <int LO, int HI>
