@@ -114,32 +114,62 @@ struct DecArgs {
 };
 
 // out[s, h] = sum over the sequence's splits, weighted by exp2(m_split - M).
+// Every split of the decode grid writes its partial (one with no pages of
+// its sequence: m = -inf, l = 0, O = 0, which weighs nothing), so the merge
+// reads all max_splits of them without looking up the sequence's length;
+// up to kMergeCap splits are loaded in one round.
+constexpr int kMergeCap = 8;
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   const int sh = blockIdx.x;          // (s * kq + t) * Hq + h
-  const int s = sh / (a.Hq * a.kq);
   const int lane = threadIdx.x;
-  const int len = min(a.c.seq_lens[s], a.c.max_pages * kPage);
-  const int pages = (len + kPage - 1) / kPage;
-  const int ns = min(a.max_splits, (pages + a.pps - 1) / a.pps);
   constexpr int PS = kPartHead + D;   // floats per partial
+  constexpr int NE = D / 64;
   const float* pp = a.part + (size_t)sh * a.max_splits * PS;
-  float mx = -INFINITY;
-  for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * PS]);
-  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  const int ns = a.max_splits;
+  float o[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) o[e] = 0.f;
   float lt = 0.f;
-  float o[D / 64];
+  if (ns <= kMergeCap) {
+    float m[kMergeCap], l[kMergeCap], x[kMergeCap][NE];
+    // (slots past ns re-read the last one, weighted zero below)
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) o[e] = 0.f;
-  for (int t = 0; t < ns; ++t) {
-    const float w = exp2f(pp[t * PS] - mu);
-    lt += w * pp[t * PS + 1];
+    for (int t = 0; t < kMergeCap; ++t) {
+      const float* q = pp + min(t, ns - 1) * PS;
+      m[t] = q[0];
+      l[t] = q[1];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) o[e] += w * pp[t * PS + kPartHead + lane + 64 * e];
+      for (int e = 0; e < NE; ++e) x[t][e] = q[kPartHead + lane + 64 * e];
+    }
+#pragma unroll
+    for (int t = 0; t < kMergeCap; ++t)
+      if (t >= ns) m[t] = -INFINITY;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kMergeCap; ++t) mx = fmaxf(mx, m[t]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+#pragma unroll
+    for (int t = 0; t < kMergeCap; ++t) {
+      const float w = exp2f(m[t] - mu);
+      lt += w * l[t];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) o[e] += w * x[t][e];
+    }
+  } else {
+    float mx = -INFINITY;
+    for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * PS]);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    for (int t = 0; t < ns; ++t) {
+      const float w = exp2f(pp[t * PS] - mu);
+      lt += w * pp[t * PS + 1];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) o[e] += w * pp[t * PS + kPartHead + lane + 64 * e];
+    }
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) a.out[(size_t)sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
+  for (int e = 0; e < NE; ++e) a.out[(size_t)sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
 }
 
 // ---- the decode / verify kernel --------------------------------------------
