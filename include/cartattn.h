@@ -420,7 +420,8 @@ int cart_write_composed_cache(cart_cache* c, int32_t seq, const cart_parts* part
  * The GQA group n_q_heads / n_kv_heads must be 1, 2, 4 or 8
  * (else CART_ERR_UNSUPPORTED; not a multiple of the cache's kv heads:
  * CART_ERR_GEOMETRY). The workspace size depends only on the cache geometry
- * and n_q_heads.
+ * and n_q_heads; it is 0 (workspace may be NULL) when the splits of every
+ * sequence are merged on chip, which cart_decode_schedule_query reports.
  */
 int cart_decode(cart_cache* c, const void* q, const void* k_new, const void* v_new,
                 int32_t n_q_heads, float scale, void* out, void* workspace,
@@ -450,6 +451,28 @@ int cart_decode_verify(cart_cache* c, const void* q, const void* k_new, const vo
 size_t cart_decode_verify_workspace_size(const cart_cache* c, int32_t n_tokens,
                                          int32_t n_q_heads);
 
+/*
+ * cart_decode_schedule_query -- how cart_decode (n_tokens = 1),
+ * cart_decode_verify and cart_decode_noalloc will split the pages of cache
+ * `c` for n_q_heads query heads over the GPU. Host-only (no HIP call, no
+ * device memory); the same plan the launches use, so a caller or a test can
+ * see which path a geometry takes. Not one of the method's operations: a
+ * diagnostic of this library's schedule. CART_ERR_INVALID_ARG for a NULL
+ * handle or out, n_tokens outside [1, 64], or n_q_heads not a positive
+ * multiple of the cache's kv heads.
+ */
+typedef struct {
+  int32_t pages_per_split;   /* 16-row pages a split streams at most */
+  int32_t max_splits;        /* splits of a sequence at full capacity */
+  int32_t waves_per_group;   /* > 0: a sequence's splits are the waves of one workgroup,
+                                merged on chip; 0: one workgroup per split, partials
+                                merged by a second kernel through the workspace */
+  int32_t grid;              /* decode workgroups */
+  int64_t workspace_bytes;   /* the workspace the call needs (0: none) */
+} cart_decode_schedule;
+int cart_decode_schedule_query(const cart_cache* c, int32_t n_tokens, int32_t n_q_heads,
+                               cart_decode_schedule* out);
+
 /* Shorten one sequence to new_len rows (0 <= new_len <= its length), e.g. to
    drop the rejected drafts of a verify step; cart_cache_reset is new_len 0. */
 int cart_cache_truncate(cart_cache* c, int32_t seq, int32_t new_len, void* stream);
@@ -459,8 +482,9 @@ int cart_cache_truncate(cart_cache* c, int32_t seq, int32_t new_len, void* strea
  * any device allocation, for callers that cannot allocate: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Same arguments, checks, kernels and results as cart_decode; the split
- * partials go to a scratch array that the library holds in device memory
- * (one per GPU, kept until the process ends), of at most
+ * partials (when they are not merged on chip) go to a scratch array that
+ * the library holds in device memory (one per GPU, kept until the process
+ * ends), of at most
  * cart_decode_noalloc_max_bytes() bytes: a cache/head geometry whose
  * cart_decode_workspace_size() exceeds it is refused with CART_ERR_WORKSPACE.
  * Every call on one GPU shares that GPU's scratch, so calls that overlap on
@@ -480,7 +504,8 @@ size_t cart_decode_noalloc_max_bytes(void);
  * "attn_bwd" (dK/dV, including the reduction of key tiles cut into pieces,
  * for bf16 tokens), "attn_bwd_dq" (dQ of bf16 tokens), "bwd_dq_combine",
  * "bwd_dq_finalize" (dQ of f32 tokens), "bwd_cart_reduce" (f32 tokens),
- * "cache_append", "decode_append", "decode", "decode_merge", "qk_norm_rope",
+ * "cache_append", "decode_append", "decode", "decode_merge" (past 8 splits per
+ * sequence), "qk_norm_rope",
  * "qk_norm_rope_bwd", "adam_rows", "compose_rows", "zero_frozen" (the
  * per-part frozen rows of cart_attn_bwd_composed). cart_timing_enable clears earlier records (after
  * waiting for them). cart_timing_query waits for the recorded events of one

@@ -50,6 +50,7 @@ EXPORTS = [
     "cart_append_cache", "cart_write_cache", "cart_decode", "cart_decode_workspace_size",
     "cart_decode_verify", "cart_decode_verify_workspace_size", "cart_cache_truncate",
     "cart_decode_noalloc", "cart_decode_noalloc_max_bytes", "cart_attn_schedule_query",
+    "cart_decode_schedule_query",
     "cart_timing_enable", "cart_timing_only", "cart_timing_query", "cart_status_string", "cart_last_error",
 ]
 
@@ -69,6 +70,12 @@ class AttnSchedule(ctypes.Structure):
         "fwd_grid", "fwd_key_splits", "bwd_cart_tiles", "bwd_tok_tiles", "bwd_units_per_piece",
         "bwd_cart_pieces", "bwd_tok_pieces_max", "bwd_kv_grid", "bwd_dq_grid",
         "bwd_dq_key_splits")]
+
+
+class DecodeSchedule(ctypes.Structure):
+    _fields_ = [("pages_per_split", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("waves_per_group", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -135,6 +142,7 @@ _lib.cart_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i32, ctypes.c_float, _
 _lib.cart_decode_noalloc_max_bytes.argtypes = []
 _lib.cart_decode_noalloc_max_bytes.restype = _sz
 _lib.cart_attn_schedule_query.argtypes = [_P(AttnShape), _P(AttnSchedule)]
+_lib.cart_decode_schedule_query.argtypes = [_vp, _i32, _i32, _P(DecodeSchedule)]
 _lib.cart_timing_enable.argtypes = [_i32]
 _lib.cart_timing_only.argtypes = [ctypes.c_char_p]
 _lib.cart_timing_query.argtypes = [ctypes.c_char_p, _P(ctypes.c_double), _P(_i32)]
@@ -465,6 +473,13 @@ class PagedCache:
 
     def decode_workspace_size(self, n_q_heads: int) -> int:
         return int(_lib.cart_decode_workspace_size(self.handle, n_q_heads))
+
+    def decode_schedule(self, n_q_heads: int, n_tokens: int = 1) -> DecodeSchedule:
+        """The split plan of a decode (n_tokens = 1) or verify step (host-only)."""
+        out = DecodeSchedule()
+        _check(_lib.cart_decode_schedule_query(self.handle, n_tokens, n_q_heads,
+                                               ctypes.byref(out)), "cart_decode_schedule_query")
+        return out
 
     def decode(self, q: torch.Tensor, out: torch.Tensor, workspace_t: Optional[torch.Tensor],
                k_new: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None,

@@ -744,6 +744,26 @@ int cart_decode_verify(cart_cache* c, const void* q, const void* k_new, const vo
                     "cart_decode_verify");
 }
 
+int cart_decode_schedule_query(const cart_cache* c, int32_t n_tokens, int32_t n_q_heads,
+                               cart_decode_schedule* out) {
+  if (!c) return fail(CART_ERR_INVALID_ARG, "cache handle is NULL");
+  if (!out) return fail(CART_ERR_INVALID_ARG, "out is NULL");
+  if (n_tokens < 1 || n_tokens > 64)
+    return fail(CART_ERR_INVALID_ARG, "tokens per sequence (%d) outside [1, 64]", n_tokens);
+  if (n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0)
+    return fail(CART_ERR_INVALID_ARG, "n_q_heads %d is not a multiple of the cache's %d kv heads",
+                n_q_heads, c->d.n_kv_heads);
+  const DecodePlan pl = plan_decode(cache_dims(c), n_q_heads, n_tokens);
+  cart_decode_schedule r{};
+  r.pages_per_split = pl.pages_per_split;
+  r.max_splits = pl.max_splits;
+  r.waves_per_group = pl.waves;
+  r.grid = (int32_t)pl.grid;
+  r.workspace_bytes = (int64_t)pl.part_bytes;
+  *out = r;
+  return CART_OK;
+}
+
 size_t cart_decode_verify_workspace_size(const cart_cache* c, int32_t n_tokens,
                                          int32_t n_q_heads) {
   if (!c || n_tokens < 1 || n_tokens > 64 || n_q_heads < 1 || n_q_heads % c->d.n_kv_heads != 0)

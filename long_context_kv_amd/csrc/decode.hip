@@ -23,8 +23,11 @@
 // of bf16 MFMAs, so each K/V byte is read once for all of them; the MFMA
 // work is idle most of the time, but it costs the wave almost no issue slots,
 // where per-row dot products on the VALU did (an earlier VALU kernel reached
-// 5.3 TB/s at 4 rows per kv head and a third less at 8). A second kernel
-// merges the splits of a sequence by log-sum-exp.
+// 5.3 TB/s at 4 rows per kv head and a third less at 8). The splits of a
+// sequence are merged by log-sum-exp: on chip, when a launch has at most 8
+// splits per sequence (one workgroup per (sequence, kv head, chunk), one
+// wave per split, the partials exchanged through LDS), else by a second
+// kernel over partials in the workspace.
 #include <math.h>
 
 #include <mutex>
@@ -186,8 +189,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 // resident. A second tile in flight per wave, which needs twice the LDS and
 // so halves the resident workgroups, was 13% slower; one-page tiles with two
 // stages, or three waves per SIMD, were no faster.
-template <int D, bool MASKED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+// W = 0: one wave per workgroup and split, its partial written to a.part for
+// decode_merge_kernel. W > 0 (a power of two, at least max_splits): W waves
+// per workgroup, wave w streams split w; each wave then leaves its partial
+// in its own LDS tile and, after one barrier, the waves merge the chunk's
+// rows and write the output (a wave past max_splits has no pages and a
+// partial that weighs nothing). The LDS per workgroup is W tiles, so a CU
+// still holds eight waves for every W.
+template <int D, bool MASKED, int W>
+__global__ __launch_bounds__(64 * (W > 0 ? W : 1)) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_mma_kernel(DecArgs a) {
   using M = Mfma<bf16>;
   using TL = Tile<D>;
@@ -198,19 +208,25 @@ void decode_mma_kernel(DecArgs a) {
   constexpr int NB = (CH + 63) / 64;            // 1 KiB copies per page tile
   constexpr int LASTL = CH - 64 * (NB - 1);     // lanes of the last, partial copy
   static_assert(2 * PT == tile_elems<D, 2 * kPage>(), "two page tiles form one 32-row tile");
-  // [K, V][two page tiles]
-  __shared__ __align__(16) bf16 tile[2][2 * PT];
+  constexpr int NW = W > 0 ? W : 1;   // waves per workgroup
+  constexpr int PS = kPartHead + D;   // floats of one row's split partial
+  // per wave: [K, V][two page tiles]
+  __shared__ __align__(16) bf16 tiles[NW][2][2 * PT];
+  static_assert(32 * PS * sizeof(float) <= sizeof(tiles[0]), "a wave's partials fit its tile");
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = NW > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l32 = lane & 31;
   const int hl = lane >> 5;
+  bf16 (&tile)[2][2 * PT] = tiles[wave];
 
   const int nb = a.max_splits;
   const int lg = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = lg % nb;
-  const int chunk_id = (lg / nb) % a.n_chunks;
-  const int kv = (lg / (nb * a.n_chunks)) % a.c.Hkv;
-  const int s = lg / (nb * a.n_chunks * a.c.Hkv);
+  const int split = W > 0 ? wave : lg % nb;
+  const int rest = W > 0 ? lg : lg / nb;   // (sequence, kv head, chunk)
+  const int chunk_id = rest % a.n_chunks;
+  const int kv = (rest / a.n_chunks) % a.c.Hkv;
+  const int s = rest / (a.n_chunks * a.c.Hkv);
   const int len = a.c.seq_lens[s];
   const int n_rows = a.kq * a.g;
   const int len_c = min(len, a.c.max_pages * kPage);
@@ -396,33 +412,100 @@ void decode_mma_kernel(DecArgs a) {
   // The split partial of this lane's row: m, l (lane half 0) and the
   // unnormalised O, whose d = 32 db + d_row(r, hl) elements the lane holds
   // in 4-element runs.
-  if (!row_ok) return;
-  const int tok = my_row / a.g;
-  float* pp = a.part + ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + my_row % a.g) * a.max_splits +
-                        split) * (kPartHead + D);
-  if (hl == 0) { pp[0] = m_ref; pp[1] = l_run; }
+  if constexpr (W == 0) {
+    if (!row_ok) return;
+    const int tok = my_row / a.g;
+    float* pp = a.part + ((((size_t)s * a.kq + tok) * a.Hq + kv * a.g + my_row % a.g) *
+                              a.max_splits + split) * PS;
+    if (hl == 0) { pp[0] = m_ref; pp[1] = l_run; }
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-      *reinterpret_cast<f32x4*>(pp + kPartHead + 32 * db + 8 * cc + 4 * hl) =
-          f32x4{acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2], acc[db][4 * cc + 3]};
+      for (int cc = 0; cc < 4; ++cc)
+        *reinterpret_cast<f32x4*>(pp + kPartHead + 32 * db + 8 * cc + 4 * hl) =
+            f32x4{acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2], acc[db][4 * cc + 3]};
+  } else {
+    // Into this wave's own tile, [32 rows][PS]: its copies have landed and
+    // its reads have returned (the last tile's waits), and no other wave
+    // touches it before the barrier.
+    asm volatile("" ::: "memory");
+    float* mine = reinterpret_cast<float*>(&tile[0][0]) + l32 * PS;
+    if (hl == 0) { mine[0] = m_ref; mine[1] = l_run; }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        *reinterpret_cast<f32x4*>(mine + kPartHead + 32 * db + 8 * cc + 4 * hl) =
+            f32x4{acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2], acc[db][4 * cc + 3]};
+    __syncthreads();
+    // Row r of the chunk is merged by wave r % W, lane l holding elements
+    // l + 64 e: the same sum as decode_merge_kernel (splits past max_splits
+    // add exact zeros there).
+    constexpr int NE = D / 64;
+    constexpr int TS = sizeof(tiles[0]) / sizeof(float);   // floats between waves' tiles
+    const float* p0 = reinterpret_cast<const float*>(&tiles[0][0][0]);
+    const int rows_here = min(32, n_rows - chunk_id * 32);
+    for (int r = wave; r < rows_here; r += W) {
+      float m[W], l[W], x[W][NE];
+#pragma unroll
+      for (int t = 0; t < W; ++t) {
+        const float* q = p0 + t * TS + r * PS;
+        m[t] = q[0];
+        l[t] = q[1];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) x[t][e] = q[kPartHead + lane + 64 * e];
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < W; ++t) mx = fmaxf(mx, m[t]);
+      const float mu = (mx == -INFINITY) ? 0.f : mx;
+      float lt = 0.f, o[NE];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int t = 0; t < W; ++t) {
+        const float w = exp2f(m[t] - mu);
+        lt += w * l[t];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o[e] += w * x[t][e];
+      }
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const int row = chunk_id * 32 + r;
+      const size_t sh = ((size_t)s * a.kq + row / a.g) * a.Hq + kv * a.g + row % a.g;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) a.out[sh * D + lane + 64 * e] = (bf16)(o[e] * inv);
+    }
+  }
+}
+
+template <int D, bool MASKED, int W>
+hipError_t launch_dec_mma(DecArgs a, const DecodePlan& pl, hipStream_t st) {
+  if constexpr (W > 0) {
+    CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED, W>), (unsigned)pl.grid, 64 * W, 0, st, a);
+    return hipGetLastError();
+  } else {
+    CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED, 0>), (unsigned)pl.grid, 64, 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
+    return hipGetLastError();
+  }
 }
 
 template <int D, bool MASKED>
-hipError_t launch_dec_mma(DecArgs a, hipStream_t st) {
-  a.n_chunks = (a.g * a.kq + 31) / 32;
-  const int grid = a.c.n_seqs * a.c.Hkv * a.n_chunks * a.max_splits;
-  CART_LAUNCH("decode", (decode_mma_kernel<D, MASKED>), grid, 64, 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  CART_LAUNCH("decode_merge", (decode_merge_kernel<D>), a.c.n_seqs * a.kq * a.Hq, 64, 0, st, a);
-  return hipGetLastError();
+hipError_t launch_dec_w(DecArgs a, const DecodePlan& pl, hipStream_t st) {
+  switch (pl.waves) {
+    case 1: return launch_dec_mma<D, MASKED, 1>(a, pl, st);
+    case 2: return launch_dec_mma<D, MASKED, 2>(a, pl, st);
+    case 4: return launch_dec_mma<D, MASKED, 4>(a, pl, st);
+    case 8: return launch_dec_mma<D, MASKED, 8>(a, pl, st);
+    default: return launch_dec_mma<D, MASKED, 0>(a, pl, st);
+  }
 }
 
 template <int D>
-hipError_t launch_dec_d(DecArgs a, hipStream_t st) {
-  return a.kq == 1 ? launch_dec_mma<D, false>(a, st) : launch_dec_mma<D, true>(a, st);
+hipError_t launch_dec_d(DecArgs a, const DecodePlan& pl, hipStream_t st) {
+  return a.kq == 1 ? launch_dec_w<D, false>(a, pl, st) : launch_dec_w<D, true>(a, pl, st);
 }
 
 }  // namespace
@@ -482,6 +565,8 @@ hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_
 // round: 6 or 8 splits per sequence instead of 4 measured 11% and 3% slower
 // on the 64-sequence serving cache), between 8 and kMaxPps pages.
 constexpr long long kResidentWgs = 256 * 8;
+// Most splits per sequence merged on chip (eight waves' LDS tiles fill a CU).
+constexpr int kOnChipSplits = 8;
 
 DecodePlan plan_decode(const CacheDims& c, int Hq, int kq) {
   DecodePlan pl{};
@@ -492,7 +577,19 @@ DecodePlan plan_decode(const CacheDims& c, int Hq, int kq) {
   pps = (pps + 3) / 4 * 4;
   pl.pages_per_split = (int)pps;
   pl.max_splits = (int)((c.max_pages + pps - 1) / pps);
-  pl.part_bytes = (size_t)c.n_seqs * kq * Hq * pl.max_splits * (kPartHead + c.D) * sizeof(float);
+  pl.chunks = (Hq / c.Hkv * kq + 31) / 32;
+  const long long wgs = (long long)c.n_seqs * c.Hkv * pl.chunks;
+  if (pl.max_splits <= kOnChipSplits) {
+    // splits merged on chip: one wave per split, the next power of two
+    pl.waves = 1;
+    while (pl.waves < pl.max_splits) pl.waves *= 2;
+    pl.grid = wgs;
+    pl.part_bytes = 0;
+  } else {
+    pl.waves = 0;
+    pl.grid = wgs * pl.max_splits;
+    pl.part_bytes = (size_t)c.n_seqs * kq * Hq * pl.max_splits * (kPartHead + c.D) * sizeof(float);
+  }
   return pl;
 }
 
@@ -516,8 +613,9 @@ hipError_t launch_decode(const CacheDims& c, int Hq, int kq, float scale, const 
   a.pps = pl.pages_per_split;
   a.max_splits = pl.max_splits;
   a.kq = kq;
+  a.n_chunks = pl.chunks;
   a.scale_log2 = scale * kLog2e;
-  return c.D == 128 ? launch_dec_d<128>(a, st) : launch_dec_d<64>(a, st);
+  return c.D == 128 ? launch_dec_d<128>(a, pl, st) : launch_dec_d<64>(a, pl, st);
 }
 
 }  // namespace cartattn

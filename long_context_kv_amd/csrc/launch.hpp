@@ -121,7 +121,10 @@ hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_
 
 struct DecodePlan {
   int pages_per_split, max_splits;
-  size_t part_bytes;
+  int chunks;          // workgroups per (sequence, kv head): query rows / 32
+  int waves;           // > 0: waves per workgroup, splits merged on chip; 0: merge kernel
+  long long grid;      // decode workgroups
+  size_t part_bytes;   // workspace for split partials (0 when merged on chip)
 };
 // kq query tokens per sequence: 1 for a decode step, more for a verify step
 // (whose k_new/v_new rows, kq per sequence, are appended first).

@@ -170,8 +170,9 @@ def test_cache_host_rules():
             C.CART_ERR_INVALID_ARG
         assert L.cart_append_cache(h, 0, FAKE, FAKE, 9, 8, 2, 64, None) == C.CART_ERR_INVALID_ARG
         # nothing stored yet: an attend-only decode has no rows to attend over
+        # (a geometry whose splits are merged on chip needs no workspace)
         ws = L.cart_decode_workspace_size(h, 4)
-        assert ws > 0
+        assert ws == 0
         assert L.cart_decode(h, FAKE, None, None, 4, 0.0, FAKE, FAKE, ws, None) == \
             C.CART_ERR_INVALID_ARG
         assert L.cart_decode(h, FAKE, FAKE, None, 4, 0.0, FAKE, FAKE, ws, None) == \
@@ -392,20 +393,80 @@ def test_write_composed_cache_refusals():
         L.cart_cache_destroy(h)
 
 
+def _decode_schedule(h, n_tokens, n_q_heads):
+    out = C.DecodeSchedule()
+    assert L.cart_decode_schedule_query(h, n_tokens, n_q_heads, ctypes.byref(out)) == C.CART_OK
+    return out
+
+
+@pytest.mark.parametrize("n_seqs,hkv,max_pages,hq", [
+    (2, 2, 4, 4), (5, 2, 40, 8), (3, 2, 24, 4), (64, 8, 320, 32), (1, 8, 100, 64),
+    (6, 8, 81, 32), (5, 2, 80, 16), (64, 8, 16384, 64), (1, 1, 1, 8)])
+def test_decode_schedule_query(n_seqs, hkv, max_pages, hq):
+    """The decode plan: a sequence's splits are merged on chip (one
+    workgroup of a power-of-two count of waves, no workspace) when there are
+    at most 8 of them, else by a merge kernel through the workspace; the
+    workspace sizes the entry points report are the plan's."""
+    d = _desc(n_seqs=n_seqs, n_kv_heads=hkv, head_dim=128, max_pages_per_seq=max_pages,
+              n_pages=n_seqs * max_pages)
+    h = ctypes.c_void_p()
+    assert L.cart_cache_create(ctypes.byref(d), ctypes.byref(h)) == C.CART_OK
+    try:
+        for k in (1, 4, 64):
+            sc = _decode_schedule(h, k, hq)
+            pps, ms = sc.pages_per_split, sc.max_splits
+            assert pps % 4 == 0 and 8 <= pps <= 256
+            assert ms == -(-max_pages // pps) and (ms - 1) * pps < max_pages
+            chunks = -(-(hq // hkv) * k // 32)
+            if ms <= 8:
+                w = sc.waves_per_group
+                assert w in (1, 2, 4, 8) and w >= ms and (w == 1 or w < 2 * ms)
+                assert sc.grid == n_seqs * hkv * chunks and sc.workspace_bytes == 0
+            else:
+                assert sc.waves_per_group == 0
+                assert sc.grid == n_seqs * hkv * chunks * ms
+                assert sc.workspace_bytes == n_seqs * k * hq * ms * (4 + 128) * 4
+            want = (L.cart_decode_workspace_size(h, hq) if k == 1 else
+                    L.cart_decode_verify_workspace_size(h, k, hq))
+            assert sc.workspace_bytes == want
+        bad = C.DecodeSchedule()
+        assert L.cart_decode_schedule_query(None, 1, hq, ctypes.byref(bad)) == C.CART_ERR_INVALID_ARG
+        assert L.cart_decode_schedule_query(h, 1, hq, None) == C.CART_ERR_INVALID_ARG
+        assert L.cart_decode_schedule_query(h, 0, hq, ctypes.byref(bad)) == C.CART_ERR_INVALID_ARG
+        assert L.cart_decode_schedule_query(h, 65, hq, ctypes.byref(bad)) == C.CART_ERR_INVALID_ARG
+        assert L.cart_decode_schedule_query(h, 1, hkv + 1 if hkv > 1 else 0,
+                                            ctypes.byref(bad)) == C.CART_ERR_INVALID_ARG
+    finally:
+        L.cart_cache_destroy(h)
+
+
 def test_verify_and_truncate_host_rules():
     h = ctypes.c_void_p()
     assert L.cart_cache_create(ctypes.byref(_desc()), ctypes.byref(h)) == C.CART_OK
     try:
         ws = L.cart_decode_verify_workspace_size(h, 4, 4)
-        assert ws == 4 * L.cart_decode_workspace_size(h, 4)   # 4 tokens: 4x the partials
+        assert ws == 0 == L.cart_decode_workspace_size(h, 4)   # merged on chip
         assert L.cart_decode_verify_workspace_size(h, 0, 4) == 0
         assert L.cart_decode_verify_workspace_size(h, 65, 4) == 0
+        # with more than 8 splits per sequence the partials go through the
+        # workspace: 4 tokens, 4x the partials of one
+        h2 = ctypes.c_void_p()
+        assert L.cart_cache_create(ctypes.byref(_desc(max_pages_per_seq=100, n_pages=200)),
+                                   ctypes.byref(h2)) == C.CART_OK
+        try:
+            ws2 = L.cart_decode_verify_workspace_size(h2, 4, 4)
+            assert ws2 == 4 * L.cart_decode_workspace_size(h2, 4) > 0
+            assert L.cart_decode_verify(h2, FAKE, FAKE, FAKE, 4, 4, 0.0, FAKE, FAKE, ws2 - 1,
+                                        None) == C.CART_ERR_WORKSPACE
+            assert L.cart_decode_verify(h2, FAKE, FAKE, FAKE, 4, 4, 0.0, FAKE, None, ws2,
+                                        None) == C.CART_ERR_WORKSPACE
+        finally:
+            L.cart_cache_destroy(h2)
         v = L.cart_decode_verify
         # drafts are appended: k_new / v_new are required
         assert v(h, FAKE, None, None, 4, 4, 0.0, FAKE, FAKE, ws, None) == C.CART_ERR_INVALID_ARG
         assert v(h, FAKE, FAKE, FAKE, 0, 4, 0.0, FAKE, FAKE, ws, None) == C.CART_ERR_INVALID_ARG
         assert v(h, FAKE, FAKE, FAKE, 4, 3, 0.0, FAKE, FAKE, ws, None) == C.CART_ERR_GEOMETRY
-        assert v(h, FAKE, FAKE, FAKE, 4, 4, 0.0, FAKE, FAKE, ws - 1, None) == C.CART_ERR_WORKSPACE
         # capacity is 64 rows: 65 drafts at once do not fit (refused as too many)
         assert v(h, FAKE, FAKE, FAKE, 65, 4, 0.0, FAKE, FAKE, 1 << 30, None) == \
             C.CART_ERR_INVALID_ARG

@@ -496,16 +496,20 @@ def test_config_serving_decode(C):
 # GQA groups 1, 2, 4, 8 at head_dim 64 and 128, with sequences of very
 # different lengths in one cache: 1 row, a few pages, a mid length and the
 # full capacity, so that some sequences have fewer splits than the launch's
-# maximum (idle split workgroups) and the merge counts them per sequence.
-DECODE_VARIANTS = [(g, d) for d in (64, 128) for g in (1, 2, 4, 8)]
+# maximum (idle splits, whose partials weigh nothing). At 40 pages per
+# sequence (5 splits) the splits are the waves of one workgroup, merged on
+# chip (three of its 8 waves always idle); at 80 (10 splits) one workgroup
+# per split, merged by the second kernel.
+DECODE_VARIANTS = [(g, d, mp) for mp in (40, 80) for d in (64, 128) for g in (1, 2, 4, 8)]
 
 
-@pytest.mark.parametrize("g,d", DECODE_VARIANTS, ids=[f"g{g}-d{d}" for g, d in DECODE_VARIANTS])
-def test_decode_variants_ragged(C, g, d):
+@pytest.mark.parametrize("g,d,max_pages", DECODE_VARIANTS,
+                         ids=[f"g{g}-d{d}-mp{mp}" for g, d, mp in DECODE_VARIANTS])
+def test_decode_variants_ragged(C, g, d, max_pages):
     Hkv = 2
     Hq = g * Hkv
-    max_pages = 40                                   # 640 rows per sequence
-    prefix = [1, 20, 257, 600, 100]
+    full = 16 * max_pages                            # rows per sequence at capacity
+    prefix = [1, 20, 257, full - 40, 100]
     gen = [0, 13, 50, 40, 0]
     di = W.decode_inputs_ragged(prefix, gen, Hq, Hkv, d, max_pages, seed=300 + 10 * g + d)
     n_seqs = len(prefix)
@@ -520,15 +524,18 @@ def test_decode_variants_ragged(C, g, d):
             cache.append(s, di.k_gen[s].cuda(), di.v_gen[s].cuda())
             oc.append(s, f64(di.k_gen[s]), f64(di.v_gen[s]))
     lens = [cache.seq_len(s) for s in range(n_seqs)]
-    assert lens == [a + b for a, b in zip(prefix, gen)] and max(lens) == 640
+    assert lens == [a + b for a, b in zip(prefix, gen)] and max(lens) == full
+    sc = cache.decode_schedule(Hq)
+    # at least 3 splits for the longest sequence: the merge really merges
+    assert sc.max_splits == max_pages // 8 >= 3
+    assert (sc.waves_per_group == 8) == (max_pages == 40)
+    assert (sc.waves_per_group == 0) == (max_pages == 80)
     nbytes = cache.decode_workspace_size(Hq)
     ws = C.workspace(nbytes, "cuda")
     out = torch.empty(n_seqs, Hq, d, dtype=torch.bfloat16, device="cuda")
     cache.decode(di.q.cuda(), out, ws)
     torch.cuda.synchronize()
     assert rel(f64(out), O.decode_step(oc, f64(di.q))) <= TOL_BF16
-    # at least 3 splits for the longest sequence: the merge really merges
-    assert nbytes >= n_seqs * Hq * 3 * (d + 2) * 4
     # then a step that appends one row to every sequence: the full one is
     # first reset and given its prefix alone again (in the oracle too)
     cache.reset(3)

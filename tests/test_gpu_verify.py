@@ -70,17 +70,21 @@ def test_one_token_verify_is_the_decode_step(C):
 # rows per kv head = g * k: up to 4 take the per-row VALU kernel, more the
 # MFMA kernel (32 rows per workgroup: 72 rows are three chunks, the last
 # ragged; 64 drafts is the largest verify step)
-CASES = [(g, k, d) for g, k in ((1, 3), (2, 2), (1, 8), (2, 3), (4, 2), (4, 4), (8, 4), (4, 16),
-                                (8, 9), (1, 64)) for d in (128,)]
-CASES += [(4, 4, 64), (2, 2, 64)]
+# At 40 pages per sequence (5 splits) the splits are merged on chip; the
+# cases at 80 (10 splits) take the merge kernel.
+CASES = [(g, k, d, 40) for g, k in ((1, 3), (2, 2), (1, 8), (2, 3), (4, 2), (4, 4), (8, 4),
+                                    (4, 16), (8, 9), (1, 64)) for d in (128,)]
+CASES += [(4, 4, 64, 40), (2, 2, 64, 40)]
+CASES += [(4, 4, 128, 80), (8, 9, 128, 80), (1, 64, 128, 80), (2, 3, 64, 80)]
 
 
-@pytest.mark.parametrize("g,k,d", CASES, ids=[f"g{g}-k{k}-d{d}" for g, k, d in CASES])
-def test_verify_against_oracle(C, g, k, d):
+@pytest.mark.parametrize("g,k,d,mp", CASES, ids=[f"g{g}-k{k}-d{d}-mp{mp}" for g, k, d, mp in CASES])
+def test_verify_against_oracle(C, g, k, d, mp):
     Hkv = 2
     Hq = g * Hkv
     prefix, gen = [1, 90, 400, 33], [0, 7, 100, 16]
-    cache, oc = _filled(C, prefix, gen, Hq, Hkv, d, 40, 100 + g + k)
+    cache, oc = _filled(C, prefix, gen, Hq, Hkv, d, mp, 100 + g + k)
+    assert (cache.decode_schedule(Hq, k).waves_per_group > 0) == (mp == 40)
     q, kn, vn = _drafts(4, k, Hq, Hkv, d, 200 + g + k)
     out = torch.empty(4, k, Hq, d, dtype=torch.bfloat16, device="cuda")
     ws = C.workspace(cache.verify_workspace_size(k, Hq), "cuda")

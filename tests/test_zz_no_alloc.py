@@ -24,8 +24,9 @@ L = C.lib()
 def test_noalloc_host_checks():
     assert L.cart_decode_noalloc_max_bytes() == 16 << 20
     # a geometry whose split partials exceed the scratch is refused before any
-    # HIP call (the appended row gives every sequence one row to attend over)
-    desc = C.CacheDesc(256, 8, 128, 16, 400, 256 * 400, C.CART_BF16, FAKE, FAKE, FAKE, FAKE)
+    # HIP call (the appended row gives every sequence one row to attend over);
+    # 64 splits per sequence, so they are merged through the scratch
+    desc = C.CacheDesc(64, 8, 128, 16, 16384, 64 * 16384, C.CART_BF16, FAKE, FAKE, FAKE, FAKE)
     h = ctypes.c_void_p()
     assert L.cart_cache_create(ctypes.byref(desc), ctypes.byref(h)) == C.CART_OK
     try:
@@ -70,7 +71,7 @@ def test_noalloc_matches_workspace_decode_twice():
         # (prefix lengths, generated lengths, Hq, Hkv, d, max_pages, seed): the
         # second is smaller (fewer sequences, shorter, fewer heads)
         ([700, 33, 1200, 5, 64, 980], [50, 0, 80, 3, 200, 0], 32, 8, 128, 81, 71),
-        ([40, 300, 9], [7, 0, 1], 8, 2, 64, 24, 72),
+        ([40, 300, 9], [7, 0, 1], 8, 2, 64, 72, 72),
     ]
     for i, (prefix, gen, Hq, Hkv, d, mp, seed) in enumerate(cases):
         say("noalloc call", i, "seqs", len(prefix), "Hq", Hq, "d", d)
@@ -80,7 +81,9 @@ def test_noalloc_matches_workspace_decode_twice():
         out_ws = torch.empty(n, Hq, d, dtype=torch.bfloat16, device="cuda")
         out_na = torch.full_like(out_ws, float("nan"))
         ws = C.workspace(cache.decode_workspace_size(Hq), "cuda")
-        assert cache.decode_workspace_size(Hq) <= C.decode_noalloc_max_bytes()
+        # more than 8 splits per sequence: the partials go through the scratch
+        assert cache.decode_schedule(Hq).waves_per_group == 0
+        assert 0 < cache.decode_workspace_size(Hq) <= C.decode_noalloc_max_bytes()
         cache.decode(q, out_ws, ws)
         cache.decode_noalloc(q, out_na)
         torch.cuda.synchronize()
@@ -98,3 +101,25 @@ def test_noalloc_matches_workspace_decode_twice():
         torch.cuda.synchronize()
         assert torch.equal(out_na, out_ws), i
         cache.close()
+
+
+@pytest.mark.gpu
+def test_noalloc_with_splits_merged_on_chip():
+    """A geometry of at most 8 splits per sequence needs no partials at all:
+    the allocation-free call takes the same kernel, without the scratch."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    prefix, gen, Hq, Hkv, d = [200, 1, 90], [9, 0, 30], 16, 4, 128
+    say("noalloc on-chip merge")
+    cache, oc, di = _filled_cache(prefix, gen, Hq, Hkv, d, 24, 73)
+    assert cache.decode_schedule(Hq).waves_per_group > 0
+    assert cache.decode_workspace_size(Hq) == 0
+    out_ws = torch.empty(3, Hq, d, dtype=torch.bfloat16, device="cuda")
+    out_na = torch.full_like(out_ws, float("nan"))
+    q = di.q.cuda()
+    cache.decode(q, out_ws, None)
+    cache.decode_noalloc(q, out_na)
+    torch.cuda.synchronize()
+    assert torch.equal(out_na, out_ws)
+    assert rel(f64(out_na), O.decode_step(oc, f64(di.q))) <= 2e-2
+    cache.close()
