@@ -499,8 +499,11 @@ def test_config_serving_decode(C):
 # maximum (idle splits, whose partials weigh nothing). At 40 pages per
 # sequence (5 splits) the splits are the waves of one workgroup, merged on
 # chip (three of its 8 waves always idle); at 80 (10 splits) one workgroup
-# per split, merged by the second kernel.
+# per split, merged by the second kernel; 16 and 24 pages give workgroups of
+# 2 and 4 waves (2 and 3 splits).
 DECODE_VARIANTS = [(g, d, mp) for mp in (40, 80) for d in (64, 128) for g in (1, 2, 4, 8)]
+DECODE_VARIANTS += [(4, 128, 16), (8, 64, 16), (2, 128, 24), (4, 64, 24)]
+WAVES_OF_PAGES = {16: 2, 24: 4, 40: 8, 80: 0}
 
 
 @pytest.mark.parametrize("g,d,max_pages", DECODE_VARIANTS,
@@ -509,7 +512,7 @@ def test_decode_variants_ragged(C, g, d, max_pages):
     Hkv = 2
     Hq = g * Hkv
     full = 16 * max_pages                            # rows per sequence at capacity
-    prefix = [1, 20, 257, full - 40, 100]
+    prefix = [1, 20, min(257, full // 2), full - 40, 100]
     gen = [0, 13, 50, 40, 0]
     di = W.decode_inputs_ragged(prefix, gen, Hq, Hkv, d, max_pages, seed=300 + 10 * g + d)
     n_seqs = len(prefix)
@@ -526,10 +529,9 @@ def test_decode_variants_ragged(C, g, d, max_pages):
     lens = [cache.seq_len(s) for s in range(n_seqs)]
     assert lens == [a + b for a, b in zip(prefix, gen)] and max(lens) == full
     sc = cache.decode_schedule(Hq)
-    # at least 3 splits for the longest sequence: the merge really merges
-    assert sc.max_splits == max_pages // 8 >= 3
-    assert (sc.waves_per_group == 8) == (max_pages == 40)
-    assert (sc.waves_per_group == 0) == (max_pages == 80)
+    # at least 2 splits for the longest sequence: the merge really merges
+    assert sc.max_splits == max_pages // 8 >= 2
+    assert sc.waves_per_group == WAVES_OF_PAGES[max_pages]
     nbytes = cache.decode_workspace_size(Hq)
     ws = C.workspace(nbytes, "cuda")
     out = torch.empty(n_seqs, Hq, d, dtype=torch.bfloat16, device="cuda")
