@@ -90,6 +90,7 @@ struct BwdArgs {
   int kv_tok_pieces;          // dK/dV pieces of one kv head's token tiles (all sequences)
   Segs seg;                   // token rows of each sequence; n is the longest
   float scale, scale_log2;
+  int q_pair;                 // dQ grid resident at once: blocks dealt in pairs
 };
 
 template <typename T> struct BLds;
@@ -1100,7 +1101,12 @@ __global__ __launch_bounds__(64 * kDqWaves, 8 / kDqWaves) void attn_bwd_dq_kerne
 
   int lg = xcd_remap(blockIdx.x, gridDim.x);
   const int split = lg % a.q_splits; lg /= a.q_splits;
-  const int qb = a.n_qb - 1 - (lg % a.n_qb); lg /= a.n_qb;
+  // Longest query blocks first. When the whole grid is resident at once
+  // (q_pair), the second half of the blocks is dealt shortest first, so a
+  // CU's two workgroups tend to pair a long block with a short one.
+  const int qr = lg % a.n_qb; lg /= a.n_qb;
+  const int qhalf = (a.n_qb + 1) / 2;
+  const int qb = (a.q_pair && qr >= qhalf) ? qr - qhalf : a.n_qb - 1 - qr;
   const int hg = lg % a.n_hg; lg /= a.n_hg;
   const int b = lg % a.B; lg /= a.B;
   const int kv = lg;
@@ -1623,6 +1629,10 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
       while (base * qs < 512 * 4 / kDqWaves && (qs * 2) * 4 <= min_tiles) qs *= 2;
     pl.q_splits = qs;
     pl.grid_q = (int)(base * qs);
+    // two workgroups per CU: a grid of at most 512 runs in one round
+    // (long-cartridge layer: dQ 1-2% faster with the blocks paired; grids of
+    // several rounds ran faster longest-first, and key-split grids no faster)
+    pl.q_pair = pl.grid_q <= 256 * (8 / kDqWaves) && qs == 1;
     if (qs > 1) pl.dq_part_bytes = (size_t)qs * d.B * d.n * d.Hq * d.D * sizeof(float);
   }
   pl.delta_bytes = (size_t)d.B * d.Hq * d.n * sizeof(float);   // and as much for lse2
@@ -1744,7 +1754,7 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.accumulate = accumulate ? 1 : 0;
   a.scale = d.scale;
   a.scale_log2 = d.scale * kLog2e;
-  a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb;
+  a.hpw = pl.hpw; a.wph = pl.wph; a.n_hg = pl.n_hg; a.n_qb = pl.n_qb; a.q_pair = pl.q_pair;
   a.zero_dq = d.tok_bf16 ? 0 : 1;
   if (d.tok_bf16) return d.D == 128 ? launch_bwd_bf16<128>(a, pl, st) : launch_bwd_bf16<64>(a, pl, st);
   return d.D == 128 ? launch_bwd_f32<128>(a, pl, st) : launch_bwd_f32<64>(a, pl, st);

@@ -53,6 +53,7 @@ struct BwdPlan {
   int kv_cart_pieces;   // dK/dV pieces of one kv head's cartridge tiles
   int kv_tok_pieces;    // dK/dV pieces of one kv head's token tiles (all sequences)
   int hpw, wph, n_hg, n_qb, q_splits, grid_q;     // query-major dQ kernel
+  int q_pair;           // 1: the dQ grid is resident at once (query blocks dealt in pairs)
   size_t shadow_bytes, dq_bytes, delta_bytes, part_bytes, tok_part_bytes, dq_part_bytes, cnt_bytes;
 };
 BwdPlan plan_bwd(const AttnDims& a);
