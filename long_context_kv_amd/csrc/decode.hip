@@ -116,12 +116,12 @@ struct DecArgs {
   float scale_log2;
 };
 
-// out[s, h] = sum over the sequence's splits, weighted by exp2(m_split - M).
-// Every split of the decode grid writes its partial (one with no pages of
-// its sequence: m = -inf, l = 0, O = 0, which weighs nothing), so the merge
-// reads all max_splits of them without looking up the sequence's length;
-// up to kMergeCap splits are loaded in one round.
-constexpr int kMergeCap = 8;
+// out[s, h] = sum over the sequence's splits, weighted by exp2(m_split - M),
+// for launches of more than 8 splits per sequence (fewer are merged inside
+// the decode kernel). Every split of the decode grid writes its partial (one
+// with no pages of its sequence: m = -inf, l = 0, O = 0, which weighs
+// nothing), so the merge reads all max_splits of them without looking up the
+// sequence's length.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
   const int sh = blockIdx.x;          // (s * kq + t) * Hq + h
@@ -134,41 +134,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) o[e] = 0.f;
   float lt = 0.f;
-  if (ns <= kMergeCap) {
-    float m[kMergeCap], l[kMergeCap], x[kMergeCap][NE];
-    // (slots past ns re-read the last one, weighted zero below)
+  float mx = -INFINITY;
+  for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * PS]);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  for (int t = 0; t < ns; ++t) {
+    const float w = exp2f(pp[t * PS] - mu);
+    lt += w * pp[t * PS + 1];
 #pragma unroll
-    for (int t = 0; t < kMergeCap; ++t) {
-      const float* q = pp + min(t, ns - 1) * PS;
-      m[t] = q[0];
-      l[t] = q[1];
-#pragma unroll
-      for (int e = 0; e < NE; ++e) x[t][e] = q[kPartHead + lane + 64 * e];
-    }
-#pragma unroll
-    for (int t = 0; t < kMergeCap; ++t)
-      if (t >= ns) m[t] = -INFINITY;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < kMergeCap; ++t) mx = fmaxf(mx, m[t]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-#pragma unroll
-    for (int t = 0; t < kMergeCap; ++t) {
-      const float w = exp2f(m[t] - mu);
-      lt += w * l[t];
-#pragma unroll
-      for (int e = 0; e < NE; ++e) o[e] += w * x[t][e];
-    }
-  } else {
-    float mx = -INFINITY;
-    for (int t = 0; t < ns; ++t) mx = fmaxf(mx, pp[t * PS]);
-    const float mu = (mx == -INFINITY) ? 0.f : mx;
-    for (int t = 0; t < ns; ++t) {
-      const float w = exp2f(pp[t * PS] - mu);
-      lt += w * pp[t * PS + 1];
-#pragma unroll
-      for (int e = 0; e < NE; ++e) o[e] += w * pp[t * PS + kPartHead + lane + 64 * e];
-    }
+    for (int e = 0; e < NE; ++e) o[e] += w * pp[t * PS + kPartHead + lane + 64 * e];
   }
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
@@ -439,8 +412,8 @@ void decode_mma_kernel(DecArgs a) {
             f32x4{acc[db][4 * cc], acc[db][4 * cc + 1], acc[db][4 * cc + 2], acc[db][4 * cc + 3]};
     __syncthreads();
     // Row r of the chunk is merged by wave r % W, lane l holding elements
-    // l + 64 e: the same sum as decode_merge_kernel (splits past max_splits
-    // add exact zeros there).
+    // l + 64 e, as decode_merge_kernel merges a row (waves past max_splits
+    // add exact zeros).
     constexpr int NE = D / 64;
     constexpr int TS = sizeof(tiles[0]) / sizeof(float);   // floats between waves' tiles
     const float* p0 = reinterpret_cast<const float*>(&tiles[0][0][0]);
