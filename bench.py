@@ -54,7 +54,7 @@ MEASURED_TRAFFIC = {
     ("attn_bwd", "qwen3-8b-layer"): (1026.9e6, "603a5a8d7d24e55e"),
     ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "603a5a8d7d24e55e"),
     ("attn_fwd", "long-cartridge-28l"): (118.0e6, "b205611fb2e52afe"),
-    ("decode", "serving-decode"): (1221.7e6, "6073aa58dde97c20"),
+    ("decode", "serving-decode"): (1221.7e6, "bcf3cfc869502111"),
 }
 
 

@@ -152,16 +152,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecArgs a) {
 // Up to 32 query rows (tokens x q-heads of one kv head) are the columns of
 // 32x32x16 bf16 MFMAs: over tiles of two pages (32 keys), S^T = K Q^T, an
 // online softmax per row (the forward's, lazily rescaled), then
-// O^T += V^T P^T with V^T taken by LDS transpose reads. One wave per
-// workgroup streams the split's tiles through one LDS tile (19 KiB at
-// D = 128) filled by direct global->LDS loads, a 16-row tile per page, so no
-// barrier orders the page stream. With 188 registers or fewer (two waves
-// per SIMD) a CU holds eight of these workgroups, and the splits of a step
-// (kResidentWgs) stream at once: measured on the 64-sequence serving cache,
-// HBM streams at full rate only while most of the step's workgroups are
-// resident. A second tile in flight per wave, which needs twice the LDS and
-// so halves the resident workgroups, was 13% slower; one-page tiles with two
-// stages, or three waves per SIMD, were no faster.
+// O^T += V^T P^T with V^T taken by LDS transpose reads. One wave per split
+// streams the split's tiles through its own LDS tile (19 KiB at D = 128)
+// filled by direct global->LDS loads, a 16-row tile per page, so no barrier
+// orders the page stream. With 188 registers or fewer (two waves per SIMD)
+// a CU holds eight of these waves, and the splits of a step (kResidentWgs)
+// stream at once: measured on the 64-sequence serving cache, HBM streams at
+// full rate only while most of the step's splits are resident. A second
+// tile in flight per wave, which needs twice the LDS and so halves the
+// resident splits, was 13% slower; one-page tiles with two stages, or three
+// waves per SIMD, were no faster.
 // W = 0: one wave per workgroup and split, its partial written to a.part for
 // decode_merge_kernel. W > 0 (a power of two, at least max_splits): W waves
 // per workgroup, wave w streams split w; each wave then leaves its partial
@@ -532,11 +532,11 @@ hipError_t launch_cache_set_len(const CacheDims& c, int seq, int len, hipStream_
   return hipGetLastError();
 }
 
-// Pages per split: about as many (sequence, kv head, split) workgroups as
-// the GPU holds at once when every sequence is full (256 CUs x 8 one-wave
-// workgroups; fewer splits leave CUs short of streams, more run in a second
-// round: 6 or 8 splits per sequence instead of 4 measured 11% and 3% slower
-// on the 64-sequence serving cache), between 8 and kMaxPps pages.
+// Pages per split: about as many (sequence, kv head, split) waves as the
+// GPU holds at once when every sequence is full (256 CUs x 8 waves; fewer
+// splits leave CUs short of streams, more run in a second round: 6 or 8
+// splits per sequence instead of 4 measured 11% and 3% slower on the
+// 64-sequence serving cache), between 8 and kMaxPps pages.
 constexpr long long kResidentWgs = 256 * 8;
 // Most splits per sequence merged on chip (eight waves' LDS tiles fill a CU).
 constexpr int kOnChipSplits = 8;
