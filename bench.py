@@ -50,10 +50,10 @@ KERNEL_SOURCES = {"attn_bwd": ("attn_bwd.hip", "common.hpp", "kvtiles.hpp"),
                   "attn_fwd": ("attn_fwd.hip", "common.hpp", "kvtiles.hpp"),
                   "decode": ("decode.hip", "common.hpp")}
 MEASURED_TRAFFIC = {
-    ("attn_bwd", "long-cartridge-28l"): (405.9e6, "603a5a8d7d24e55e"),
-    ("attn_bwd", "qwen3-8b-layer"): (1026.9e6, "603a5a8d7d24e55e"),
-    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "603a5a8d7d24e55e"),
-    ("attn_fwd", "long-cartridge-28l"): (118.0e6, "b205611fb2e52afe"),
+    ("attn_bwd", "long-cartridge-28l"): (518.4e6, "6abb81700c80d4ce"),
+    ("attn_bwd", "qwen3-8b-layer"): (1021.9e6, "6abb81700c80d4ce"),
+    ("attn_bwd", "qwen3-0.6b-layer"): (42.7e6, "6abb81700c80d4ce"),
+    ("attn_fwd", "long-cartridge-28l"): (117.9e6, "b205611fb2e52afe"),
     ("decode", "serving-decode"): (1221.7e6, "bcf3cfc869502111"),
 }
 

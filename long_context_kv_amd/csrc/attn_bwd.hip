@@ -91,6 +91,7 @@ struct BwdArgs {
   Segs seg;                   // token rows of each sequence; n is the longest
   float scale, scale_log2;
   int q_pair;                 // dQ grid resident at once: blocks dealt in pairs
+  int kv_ttok;                // dK/dV token tiles: pieces of at most this many units
 };
 
 template <typename T> struct BLds;
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
     for (tile = 0; tile < a.n_tt; ++tile) {
       if (!packed) {
         ut = a.g * (qt_hi_of(false, tile, 0) - tile * (kBNB / kBQ));
-        n_split = (ut + a.kv_target - 1) / a.kv_target;
+        n_split = (ut + a.kv_ttok - 1) / a.kv_ttok;
         if (r0 < a.B * n_split) { b = r0 / n_split; r0 %= n_split; break; }
         r0 -= a.B * n_split;
         continue;
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_kv_kernel(BwdArgs a) {
       for (b = 0; b < a.B; ++b) {
         if (tile * kBNB >= len_of(b)) continue;
         ut = a.g * (qt_hi_of(false, tile, b) - tile * (kBNB / kBQ));
-        n_split = (ut + a.kv_target - 1) / a.kv_target;
+        n_split = (ut + a.kv_ttok - 1) / a.kv_ttok;
         if (r0 < n_split) { found = true; break; }
         r0 -= n_split;
       }
@@ -1535,9 +1536,9 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
         if (has_tile(t, b)) t_max = std::max(t_max, tok_units_w(t, b));
     t_max = std::max(t_max, 1LL);
     const int slots = 32;   // one dK/dV workgroup per CU
-    auto finish = [&](long long T) {
+    auto finish = [&](long long T, long long Tt) {
       std::vector<std::pair<long long, long long>> pieces;   // (units, pieces of its tile)
-      auto tile = [&](long long u, bool at_least_one) {
+      auto tile = [&](long long u, bool at_least_one, long long T) {
         long long ns = (u + T - 1) / T;
         if (at_least_one && ns < 1) ns = 1;
         for (long long i = 0; i < ns; ++i) pieces.emplace_back((i + 1) * u / ns - i * u / ns, ns);
@@ -1550,11 +1551,11 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
             for (int c = 0; c < pl.n_ct; ++c)
               pieces.emplace_back((i + 1) * Uc / ns - i * Uc / ns, ns);
         } else {
-          for (int c = 0; c < pl.n_ct; ++c) tile(cart_units(c), true);
+          for (int c = 0; c < pl.n_ct; ++c) tile(cart_units(c), true, T);
         }
         for (int t = 0; t < pl.n_tt; ++t)
           for (int b = 0; b < d.B; ++b)
-            if (has_tile(t, b)) tile(tok_units_w(t, b), false);
+            if (has_tile(t, b)) tile(tok_units_w(t, b), false, Tt);
       }
       const size_t G = pieces.size(), q = G / 8, r = G % 8;
       double worst = 0.0;
@@ -1574,15 +1575,22 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
       }
       return worst;
     };
-    long long T = t_max;
-    double best = finish(T);
-    for (int k = 2; k <= 8; ++k) {
-      const long long c = std::max(4LL, (t_max + k - 1) / k);
-      if (c >= T) continue;
-      const double f = finish(c);
-      if (f < best - 1e-9) { best = f; T = c; }
+    // Token tiles may be cut finer than cartridge tiles (Tt <= T): the
+    // causal token tiles come last in each XCD's range, and smaller pieces
+    // there even out the finish when the cartridge tiles are dealt whole.
+    long long T = t_max, Tt = t_max;
+    double best = finish(T, Tt);
+    for (int k = 1; k <= 8; ++k) {
+      const long long c = k == 1 ? t_max : std::max(4LL, (t_max + k - 1) / k);
+      for (int kt = k; kt <= 8; ++kt) {
+        const long long ct = kt == 1 ? t_max : std::max(4LL, (t_max + kt - 1) / kt);
+        if (ct > c || (c == T && ct == Tt)) continue;
+        const double f = finish(c, ct);
+        if (f < best - 1e-9) { best = f; T = c; Tt = ct; }
+      }
     }
     pl.kv_target = (int)T;
+    pl.kv_ttok = (int)Tt;
     if (!windowed) {
       pl.kv_splits_c = pl.n_ct > 0 ? (int)((Uc + T - 1) / T) : 1;
       pl.kv_cart_pieces = pl.n_ct * pl.kv_splits_c;
@@ -1599,7 +1607,7 @@ static BwdPlan make_plan_bwd(const AttnDims& d) {
     for (int t = 0; t < pl.n_tt; ++t)
       for (int b = 0; b < d.B; ++b) {
         if (!has_tile(t, b)) continue;
-        const int ns = (int)((tok_units_w(t, b) + T - 1) / T);
+        const int ns = (int)((tok_units_w(t, b) + Tt - 1) / Tt);
         ptok += ns;
         stmax = std::max(stmax, ns);
       }
@@ -1745,6 +1753,7 @@ hipError_t launch_bwd(const AttnDims& d, const void* q, const void* k_tok, const
   a.n_ct = pl.n_ct; a.n_tt = pl.n_tt; a.nqt = pl.nqt;
   a.splits_c = d.tok_bf16 ? pl.kv_splits_c : pl.splits_c;
   a.kv_target = pl.kv_target; a.kv_ptok = pl.kv_ptok; a.kv_stmax = pl.kv_stmax;
+  a.kv_ttok = pl.kv_ttok;
   a.q_splits = pl.q_splits;
   a.kv_cart_pieces = pl.kv_cart_pieces;
   a.kv_tok_pieces = pl.kv_tok_pieces;

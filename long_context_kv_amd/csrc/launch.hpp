@@ -50,6 +50,7 @@ struct BwdPlan {
   // into ceil(units_t / kv_target)); kv_ptok pieces per (kv head, batch) of
   // token tiles, at most kv_stmax per token tile.
   int kv_target, kv_splits_c, kv_ptok, kv_stmax, grid_kv;
+  int kv_ttok;          // token tiles: pieces of at most this many units (<= kv_target)
   int kv_cart_pieces;   // dK/dV pieces of one kv head's cartridge tiles
   int kv_tok_pieces;    // dK/dV pieces of one kv head's token tiles (all sequences)
   int hpw, wph, n_hg, n_qb, q_splits, grid_q;     // query-major dQ kernel

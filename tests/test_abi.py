@@ -478,15 +478,28 @@ def test_verify_and_truncate_host_rules():
         L.cart_cache_destroy(h)
 
 
+def test_long_cartridge_schedule_cuts_token_tiles_only():
+    """On the long-cartridge layer the dK/dV plan deals every cartridge tile
+    whole (256 units: four rounds of 256 CUs) and cuts the larger causal
+    token tiles, which come last, into up to three pieces, so that the last
+    round evens out; the tiles' pieces are reduced in the kernel."""
+    s = _sched(1, 4096, 16384, 16, 8, 128)
+    assert s.bwd_cart_pieces == 1 and s.bwd_units_per_piece == 256
+    assert s.bwd_tok_pieces_max == 3
+    assert s.bwd_kv_grid > (s.bwd_cart_tiles + s.bwd_tok_tiles) * 8
+
+
 def test_window_schedule_and_validation():
     assert _fwd(_shape(window=-1)) == C.CART_ERR_INVALID_ARG
     full = _sched(1, 4096, 16384, 16, 8, 128)
     s = C.cart_attn_schedule_query(_shape(batch=1, q_seq=4096, p=16384, n_q_heads=16,
                                           n_kv_heads=8, head_dim=128, window=1024))
-    # a 1024-row window leaves most of the cartridge unseen: every key tile
-    # keeps its piece, but with far fewer (batch, head, query-tile) units
-    assert s.bwd_kv_grid == full.bwd_kv_grid and s.bwd_cart_tiles == full.bwd_cart_tiles
+    # a 1024-row window leaves most of the cartridge unseen: one piece per
+    # key tile, with far fewer (batch, head, query-tile) units
+    tiles = (s.bwd_cart_tiles + s.bwd_tok_tiles) * 8
+    assert s.bwd_kv_grid == tiles and s.bwd_cart_tiles == full.bwd_cart_tiles
     assert 3 * s.bwd_units_per_piece < full.bwd_units_per_piece
+    assert full.bwd_kv_grid >= tiles
     wide = C.cart_attn_schedule_query(_shape(batch=1, q_seq=4096, p=16384, n_q_heads=16,
                                              n_kv_heads=8, head_dim=128, window=20480))
     assert wide.bwd_kv_grid == full.bwd_kv_grid     # a window reaching every row is none
