@@ -290,6 +290,8 @@ typedef struct {
   int32_t bwd_kv_grid;            /* dK/dV workgroups */
   int32_t bwd_dq_grid;            /* dQ workgroups */
   int32_t bwd_dq_key_splits;      /* > 1: dQ key range split, pieces summed after */
+  int32_t bwd_tok_units_per_piece; /* token tiles: pieces of at most this many units
+                                      (bf16 tokens; 0 in the float32 mode) */
 } cart_attn_schedule;
 int cart_attn_schedule_query(const cart_attn_shape* s, cart_attn_schedule* out);
 

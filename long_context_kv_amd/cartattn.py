@@ -69,7 +69,7 @@ class AttnSchedule(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "fwd_grid", "fwd_key_splits", "bwd_cart_tiles", "bwd_tok_tiles", "bwd_units_per_piece",
         "bwd_cart_pieces", "bwd_tok_pieces_max", "bwd_kv_grid", "bwd_dq_grid",
-        "bwd_dq_key_splits")]
+        "bwd_dq_key_splits", "bwd_tok_units_per_piece")]
 
 
 class DecodeSchedule(ctypes.Structure):

@@ -516,6 +516,7 @@ int cart_attn_schedule_query(const cart_attn_shape* s, cart_attn_schedule* out) 
     r.bwd_kv_grid = bp.grid_kv;
     r.bwd_dq_grid = bp.grid_q;
     r.bwd_dq_key_splits = bp.q_splits;
+    r.bwd_tok_units_per_piece = bp.kv_ttok;
   } else {
     // float32 reference mode: one kernel, cartridge tiles split over units,
     // dQ accumulated in the same kernel

@@ -489,6 +489,29 @@ def test_long_cartridge_schedule_cuts_token_tiles_only():
     assert s.bwd_kv_grid > (s.bwd_cart_tiles + s.bwd_tok_tiles) * 8
 
 
+@pytest.mark.parametrize("B,n,p,Hq,Hkv,d", [
+    (1, 4096, 16384, 16, 8, 128), (4, 2048, 4096, 32, 8, 128), (1, 1024, 2048, 16, 8, 128),
+    (2, 200, 600, 8, 2, 128), (1, 500, 16, 4, 2, 128), (3, 77, 0, 6, 3, 64),
+    (1, 8192, 1024, 8, 1, 128), (2, 3000, 500, 12, 4, 64), (1, 1, 9, 4, 2, 64)])
+def test_dkdv_grid_follows_the_piece_rule(B, n, p, Hq, Hkv, d):
+    """The dK/dV grid is the sum of the pieces the kernel derives for its
+    block ids: every cartridge tile in the same number of pieces, token tile
+    t (units g * (query tiles from 4 t on) per sequence) in
+    ceil(units / token target) pieces, the token target at most the
+    cartridge one."""
+    s = _sched(B, n, p, Hq, Hkv, d)
+    g, nqt, n_tt = Hq // Hkv, -(-n // 32), -(-n // 128)
+    tt, tc = s.bwd_tok_units_per_piece, s.bwd_units_per_piece
+    assert 1 <= tt and (p == 0 or tt <= tc)
+    tok = [-(-(g * (nqt - 4 * t)) // tt) for t in range(n_tt)]
+    n_ct = -(-p // 128)
+    assert s.bwd_cart_tiles == n_ct and s.bwd_tok_tiles == n_tt
+    if n_ct:
+        assert s.bwd_cart_pieces == -(-(B * g * nqt) // tc)
+    assert s.bwd_tok_pieces_max == max(tok + [1])
+    assert s.bwd_kv_grid == Hkv * (n_ct * s.bwd_cart_pieces + B * sum(tok))
+
+
 def test_window_schedule_and_validation():
     assert _fwd(_shape(window=-1)) == C.CART_ERR_INVALID_ARG
     full = _sched(1, 4096, 16384, 16, 8, 128)
